@@ -1,0 +1,186 @@
+"""CPU oracle for the fused W4A16 / W8A16 linear layer (ctypes over oracle.c).
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, ``__graft_entry__.smoke()``
+and the CPU-baseline leg of ``bench.py``; never by the product package.  It
+shares no code with the HIP library.
+
+The arithmetic lives in ``oracle.c`` (plain C, fp32 dequant, fp64 sums in k
+order); this module only marshals numpy arrays.  See that file's header for
+what each step computes and which passage of the TileFuse summary it
+follows.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+CFLAGS = ["-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math", "-std=c11", "-Wall", "-shared", "-fPIC"]
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c into liboracle.so with gcc (host only)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + f".tmp{os.getpid()}"
+        subprocess.check_call(["gcc", *CFLAGS, _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build(force=True)
+        L = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        I64 = ctypes.c_int64
+        L.oracle_unpack_w4.argtypes = [P, I64, I64, P]
+        L.oracle_pack_w4.argtypes = [P, I64, I64, P]
+        L.oracle_bf16_to_f32.argtypes = [ctypes.c_uint16]
+        L.oracle_bf16_to_f32.restype = ctypes.c_float
+        L.oracle_f64_to_bf16.argtypes = [ctypes.c_double]
+        L.oracle_f64_to_bf16.restype = ctypes.c_uint16
+        L.oracle_round_bf16.argtypes = [P, I64, P]
+        L.oracle_dequant_w4.argtypes = [P, P, P, I64, I64, I64, P, I64, P]
+        L.oracle_dequant_w8.argtypes = [P, P, P, I64, I64, I64, P, I64, P]
+        L.oracle_linear.argtypes = [P, I64, I64, P, I64, P]
+        L.oracle_num_threads.restype = ctypes.c_int
+        L.oracle_packed_bytes.argtypes = [ctypes.c_int, I64, I64, I64]
+        L.oracle_packed_bytes.restype = ctypes.c_size_t
+        L.oracle_repack.argtypes = [ctypes.c_int, P, P, P, I64, I64, I64, P]
+        L.oracle_repack.restype = ctypes.c_int
+        L.oracle_unrepack.argtypes = [ctypes.c_int, P, I64, I64, I64, P, P, P]
+        L.oracle_unrepack.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _p(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def num_threads() -> int:
+    return int(lib().oracle_num_threads())
+
+
+def unpack_w4(words) -> np.ndarray:
+    """AWQ words [R][C/8] -> 4-bit codes [R][C] (uint8)."""
+    words = _c(words, np.uint32)
+    R, C8 = words.shape
+    out = np.empty((R, C8 * 8), dtype=np.uint8)
+    lib().oracle_unpack_w4(_p(words), R, C8 * 8, _p(out))
+    return out
+
+
+def pack_w4(codes) -> np.ndarray:
+    """4-bit codes [R][C] -> AWQ words [R][C/8] (the oracle's own packer)."""
+    codes = _c(codes, np.uint8)
+    R, C = codes.shape
+    out = np.empty((R, C // 8), dtype=np.uint32)
+    lib().oracle_pack_w4(_p(codes), R, C, _p(out))
+    return out
+
+
+def bf16_to_f32(bits) -> np.ndarray:
+    bits = _c(bits, np.uint16)
+    f = np.vectorize(lambda b: lib().oracle_bf16_to_f32(int(b)), otypes=[np.float32])
+    return f(bits) if bits.size else bits.astype(np.float32)
+
+
+def f64_to_bf16(y) -> np.ndarray:
+    """Round fp64 values to bf16 bits (nearest, ties to even) in one step."""
+    y = _c(y, np.float64)
+    out = np.empty(y.shape, dtype=np.uint16)
+    lib().oracle_round_bf16(_p(y), y.size, _p(out))
+    return out
+
+
+def dequant(bits, qweight, qzeros, scales, K, N, G, cols=None) -> np.ndarray:
+    """Dequantized fp32 weights w[K][len(cols)] (all N columns when cols is None)."""
+    sc = _c(scales, np.uint16)
+    if cols is None:
+        cp, ncols = None, N
+    else:
+        cols = _c(cols, np.int64)
+        if cols.size and (cols.min() < 0 or cols.max() >= N):
+            raise ValueError("column index out of range")
+        cp, ncols = _p(cols), cols.size
+    w = np.empty((K, ncols), dtype=np.float32)
+    if bits == 4:
+        qw, qz = _c(qweight, np.uint32), _c(qzeros, np.uint32)
+        assert qw.shape == (K, N // 8) and qz.shape == (K // G, N // 8)
+        lib().oracle_dequant_w4(_p(qw), _p(qz), _p(sc), K, N, G, cp, ncols, _p(w))
+    elif bits == 8:
+        qw, qz = _c(qweight, np.uint8), _c(qzeros, np.uint8)
+        assert qw.shape == (K, N) and qz.shape == (K // G, N)
+        lib().oracle_dequant_w8(_p(qw), _p(qz), _p(sc), K, N, G, cp, ncols, _p(w))
+    else:
+        raise ValueError("bits must be 4 or 8")
+    assert sc.shape == (K // G, N)
+    return w
+
+
+def linear(x_bits, w) -> np.ndarray:
+    """y64[M][N] = sum_k x[m][k] * w[k][n] in fp64, k ascending."""
+    x = _c(x_bits, np.uint16)
+    w = _c(w, np.float32)
+    M, K = x.shape
+    assert w.shape[0] == K
+    N = w.shape[1]
+    y = np.empty((M, N), dtype=np.float64)
+    lib().oracle_linear(_p(x), M, K, _p(w), N, _p(y))
+    return y
+
+
+def awq_linear(case, cols=None, rows=None) -> np.ndarray:
+    """Reference output of a synth.Case: fp64 y for the chosen rows/columns."""
+    w = dequant(case.bits, case.qweight, case.qzeros, case.scales, case.K, case.N, case.G, cols)
+    x = case.x if rows is None else case.x[np.asarray(rows)]
+    return linear(x, w)
+
+
+def packed_bytes(bits, K, N, G) -> int:
+    return int(lib().oracle_packed_bytes(bits, K, N, G))
+
+
+def repack(bits, qweight, qzeros, scales, K, N, G) -> np.ndarray:
+    """Reference interleaved pre-tiled buffer (uint8) for the checkpoint inputs."""
+    nbytes = packed_bytes(bits, K, N, G)
+    if nbytes == 0:
+        raise ValueError("invalid (bits, K, N, G)")
+    dt = np.uint32 if bits == 4 else np.uint8
+    qw, qz, sc = _c(qweight, dt), _c(qzeros, dt), _c(scales, np.uint16)
+    out = np.empty(nbytes, dtype=np.uint8)
+    rc = lib().oracle_repack(bits, _p(qw), _p(qz), _p(sc), K, N, G, _p(out))
+    if rc:
+        raise ValueError("oracle_repack rejected the shape")
+    return out
+
+
+def unrepack(bits, packed, K, N, G):
+    """Inverse of :func:`repack`: (codes [K][N], zeros [K/G][N], scale bits [K/G][N])."""
+    packed = _c(packed, np.uint8)
+    if packed.size < packed_bytes(bits, K, N, G):
+        raise ValueError("packed buffer too small")
+    codes = np.empty((K, N), dtype=np.uint8)
+    zeros = np.empty((K // G, N), dtype=np.uint8)
+    scales = np.empty((K // G, N), dtype=np.uint16)
+    rc = lib().oracle_unrepack(bits, _p(packed), K, N, G, _p(codes), _p(zeros), _p(scales))
+    if rc:
+        raise ValueError("oracle_unrepack rejected the shape")
+    return codes, zeros, scales

@@ -1,0 +1,369 @@
+/*
+ * CPU oracle for the fused W4A16 / W8A16 linear layer.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may call, link or
+ * load this file; only the tests, the smoke check and the benchmark's CPU
+ * baseline leg use it.  It shares no code, header or constant with the HIP
+ * library: every constant below is written out here on its own.
+ *
+ * What it computes (TileFuse technical summary, Methodology section 1,
+ * "Fused mixed-precision microkernels"): unpack the INT4/INT8 weights,
+ * dequantize them with per-group or per-channel scales and zero points, then
+ * run the matrix product.  Contribution 1 of the same summary says the
+ * weights are AWQ-style W4A16/W8A16 checkpoints.  Written out:
+ *
+ *   q[k][n]  = code of row k, column n              (unpack)
+ *   w[k][n]  = (q[k][n] - z[g][n]) * s[g][n],  g = floor(k / G)  (dequant)
+ *   y[m][n]  = sum_k x[m][k] * w[k][n]              (GEMM / GEMV)
+ *
+ * Precision: dequant in fp32 (exact: |q - z| <= 255 has at most 8 significant
+ * bits and a bf16 scale has 8, so the product has at most 16 < 24), products
+ * and the k-ascending sum in fp64, one rounding to bf16 at the end, straight
+ * from fp64 (round to nearest, ties to even).
+ *
+ * The repack/unrepack routines implement the interleaved pre-tiled layout
+ * (TileFuse summary, Methodology section 2, "Interleaved pre-tiling":
+ * scales and zero points packed into the weight tiles, tiles one consumer
+ * reads laid out contiguously).  The layout itself is this library's own
+ * (the pages fix no geometry); it is spelled out next to oracle_repack.
+ *
+ * Pins: every function here is checked against something other than itself
+ * by the host-only tests (exact rationals, integer GEMM special case,
+ * exhaustive dequant exactness, library fp64 matmul, golden word fixtures,
+ * round trips).  No function here is "parity unpinned".
+ *
+ * Build: gcc -O2 -fopenmp -ffp-contract=off -fno-fast-math -shared -fPIC
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* ------------------------------------------------------------------ */
+/* AWQ 4-bit word layout: word (r, c) holds columns 8c..8c+7 of row r; */
+/* column 8c+j sits in nibble NIBBLE_OF_COLUMN[j] (bits 4p..4p+3).     */
+/* ------------------------------------------------------------------ */
+static const int NIBBLE_OF_COLUMN[8] = {0, 4, 1, 5, 2, 6, 3, 7};
+
+static inline unsigned awq_code(const uint32_t *words, int64_t C, int64_t r, int64_t c)
+{
+    uint32_t wd = words[r * (C / 8) + c / 8];
+    return (wd >> (4 * NIBBLE_OF_COLUMN[c % 8])) & 0xFu;
+}
+
+void oracle_unpack_w4(const uint32_t *words, int64_t R, int64_t C, uint8_t *codes)
+{
+    for (int64_t r = 0; r < R; ++r)
+        for (int64_t c = 0; c < C; ++c)
+            codes[r * C + c] = (uint8_t)awq_code(words, C, r, c);
+}
+
+void oracle_pack_w4(const uint8_t *codes, int64_t R, int64_t C, uint32_t *words)
+{
+    for (int64_t r = 0; r < R; ++r)
+        for (int64_t cw = 0; cw < C / 8; ++cw) {
+            uint32_t wd = 0;
+            for (int j = 0; j < 8; ++j)
+                wd |= (uint32_t)(codes[r * C + 8 * cw + j] & 0xF) << (4 * NIBBLE_OF_COLUMN[j]);
+            words[r * (C / 8) + cw] = wd;
+        }
+}
+
+/* ------------------------------------------------------------------ */
+/* bf16 <-> binary floating point                                      */
+/* ------------------------------------------------------------------ */
+float oracle_bf16_to_f32(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+/* Round a double to the nearest bf16 value, ties to even, in one step.
+ * bf16 has 8 significant bits, exponents -126..127, subnormal quantum 2^-133. */
+uint16_t oracle_f64_to_bf16(double v)
+{
+    if (isnan(v))
+        return 0x7FC0;
+    uint16_t sign = signbit(v) ? 0x8000 : 0;
+    double a = fabs(v);
+    if (isinf(a))
+        return sign | 0x7F80;
+    if (a == 0.0)
+        return sign;
+    int e;
+    (void)frexp(a, &e);              /* a = f * 2^e, f in [0.5, 1): 2^(e-1) <= a < 2^e */
+    int quantum_exp = (e - 1) - 7;   /* spacing of 8-significant-bit values in that binade */
+    if (quantum_exp < -133)
+        quantum_exp = -133;          /* subnormal range */
+    double n = nearbyint(ldexp(a, -quantum_exp)); /* default mode: nearest, ties to even */
+    double r = ldexp(n, quantum_exp);
+    if (r >= 0x1p128)
+        return sign | 0x7F80;        /* rounds past the largest finite bf16 */
+    float rf = (float)r;             /* exact: r has <= 8 significant bits */
+    uint32_t u;
+    memcpy(&u, &rf, sizeof u);
+    return sign | (uint16_t)(u >> 16);
+}
+
+void oracle_round_bf16(const double *y, int64_t n, uint16_t *out)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = oracle_f64_to_bf16(y[i]);
+}
+
+/* ------------------------------------------------------------------ */
+/* Dequantization: w[k][j] = (q - z) * s for output column cols[j]     */
+/* (all columns when cols == NULL).  fp32, exact.                      */
+/* ------------------------------------------------------------------ */
+static inline int64_t col_of(const int64_t *cols, int64_t j) { return cols ? cols[j] : j; }
+
+void oracle_dequant_w4(const uint32_t *qweight, const uint32_t *qzeros, const uint16_t *scales,
+                       int64_t K, int64_t N, int64_t G, const int64_t *cols, int64_t ncols, float *w)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t k = 0; k < K; ++k) {
+        int64_t g = k / G;
+        for (int64_t j = 0; j < ncols; ++j) {
+            int64_t n = col_of(cols, j);
+            int q = (int)awq_code(qweight, N, k, n);
+            int z = (int)awq_code(qzeros, N, g, n);
+            float s = oracle_bf16_to_f32(scales[g * N + n]);
+            w[k * ncols + j] = (float)(q - z) * s;
+        }
+    }
+}
+
+void oracle_dequant_w8(const uint8_t *qweight, const uint8_t *zeros, const uint16_t *scales,
+                       int64_t K, int64_t N, int64_t G, const int64_t *cols, int64_t ncols, float *w)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t k = 0; k < K; ++k) {
+        int64_t g = k / G;
+        for (int64_t j = 0; j < ncols; ++j) {
+            int64_t n = col_of(cols, j);
+            int q = qweight[k * N + n];
+            int z = zeros[g * N + n];
+            float s = oracle_bf16_to_f32(scales[g * N + n]);
+            w[k * ncols + j] = (float)(q - z) * s;
+        }
+    }
+}
+
+/* ------------------------------------------------------------------ */
+/* Linear: y[m][n] = sum_{k ascending} x[m][k] * w[k][n], in fp64.     */
+/* Each thread owns a (row, column range) block and walks k outermost, */
+/* so every output element still sums in k order.                     */
+/* ------------------------------------------------------------------ */
+#define ORACLE_COL_CHUNK 512
+
+void oracle_linear(const uint16_t *x, int64_t M, int64_t K, const float *w, int64_t N, double *y)
+{
+    int64_t nchunks = (N + ORACLE_COL_CHUNK - 1) / ORACLE_COL_CHUNK;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t job = 0; job < M * nchunks; ++job) {
+        int64_t m = job / nchunks;
+        int64_t n0 = (job % nchunks) * ORACLE_COL_CHUNK;
+        int64_t n1 = n0 + ORACLE_COL_CHUNK < N ? n0 + ORACLE_COL_CHUNK : N;
+        double *yr = y + m * N;
+        for (int64_t n = n0; n < n1; ++n)
+            yr[n] = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            double xv = (double)oracle_bf16_to_f32(x[m * K + k]);
+            const float *wr = w + k * N;
+            for (int64_t n = n0; n < n1; ++n)
+                yr[n] += xv * (double)wr[n];
+        }
+    }
+}
+
+int oracle_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* ------------------------------------------------------------------ */
+/* Interleaved pre-tiled layout (format version 1).                    */
+/*                                                                    */
+/*   Column blocks of 64 output columns, block-major; ceil(N/64)       */
+/*   blocks, columns past N are padding (code 0, zero 0, scale 0).     */
+/*   Inside a block, groups in ascending k; each group is a header     */
+/*   followed by its G/32 chunks, one chunk per 32 rows ("k-step").   */
+/*   Header (bytes): 128 of scales, then zeros (W4: 32, W8: 64).       */
+/*     column c of the block, t = c / 16, r = c % 16:                  */
+/*       scale bits   at 2*(4r + t)                                    */
+/*       W4 zero      nibble t of the 16-bit little-endian value at    */
+/*                    128 + 2r                                         */
+/*       W8 zero      byte 128 + 4r + t                                */
+/*   Chunk (W4 1024 bytes, W8 2048), rows 32s + 8o + i, o < 4, i < 8:  */
+/*       W4  word at 16*(16o + r) + 4t; row i in nibble i/2 + 4*(i%2)  */
+/*       W8  byte at 1024*(t/2) + 16*(16o + r) + 8*(t%2) + i           */
+/* ------------------------------------------------------------------ */
+#define BLK_COLS 64
+#define STEP_ROWS 32
+
+static int layout_ok(int bits, int64_t K, int64_t N, int64_t G)
+{
+    if (bits != 4 && bits != 8)
+        return 0;
+    if (K <= 0 || N <= 0 || G <= 0)
+        return 0;
+    if (K % STEP_ROWS || G % STEP_ROWS || K % G)
+        return 0;
+    if (bits == 4 && N % 8)
+        return 0;
+    return 1;
+}
+
+static int64_t chunk_bytes(int bits) { return bits == 4 ? 1024 : 2048; }
+static int64_t header_bytes(int bits) { return bits == 4 ? 160 : 192; }
+static int64_t group_bytes(int bits, int64_t G) { return header_bytes(bits) + (G / STEP_ROWS) * chunk_bytes(bits); }
+static int64_t block_bytes(int bits, int64_t K, int64_t G) { return (K / G) * group_bytes(bits, G); }
+
+size_t oracle_packed_bytes(int bits, int64_t K, int64_t N, int64_t G)
+{
+    if (!layout_ok(bits, K, N, G))
+        return 0;
+    int64_t nblk = (N + BLK_COLS - 1) / BLK_COLS;
+    return (size_t)(nblk * block_bytes(bits, K, G));
+}
+
+/* byte offset of the header of (block j, group g) */
+static int64_t header_at(int bits, int64_t K, int64_t G, int64_t j, int64_t g)
+{
+    return j * block_bytes(bits, K, G) + g * group_bytes(bits, G);
+}
+
+/* byte offset of the chunk of global k-step s in block j */
+static int64_t chunk_at(int bits, int64_t K, int64_t G, int64_t j, int64_t s)
+{
+    int64_t per_group = G / STEP_ROWS;
+    return header_at(bits, K, G, j, s / per_group) + header_bytes(bits) + (s % per_group) * chunk_bytes(bits);
+}
+
+/* position of (row-in-step o*8+i, column c of the block) inside a chunk:   */
+/* byte offset, and for W4 the bit shift inside the little-endian word.   */
+static int64_t w4_word_in_chunk(int o, int c) { return 16 * (16 * o + c % 16) + 4 * (c / 16); }
+static int w4_shift_of_row(int i) { return 4 * (i / 2 + 4 * (i % 2)); }
+static int64_t w8_byte_in_chunk(int o, int i, int c)
+{
+    int t = c / 16, r = c % 16;
+    return 1024 * (t / 2) + 16 * (16 * o + r) + 8 * (t % 2) + i;
+}
+
+static void put_u32(uint8_t *p, uint32_t v) { p[0] = v; p[1] = v >> 8; p[2] = v >> 16; p[3] = v >> 24; }
+static uint32_t get_u32(const uint8_t *p) { return p[0] | (p[1] << 8) | (p[2] << 16) | ((uint32_t)p[3] << 24); }
+
+/* Codes and zeros are read through these accessors so one repack serves   */
+/* both widths.                                                           */
+static unsigned code_at(int bits, const void *qweight, int64_t N, int64_t k, int64_t n)
+{
+    return bits == 4 ? awq_code((const uint32_t *)qweight, N, k, n) : ((const uint8_t *)qweight)[k * N + n];
+}
+
+int oracle_repack(int bits, const void *qweight, const void *qzeros, const uint16_t *scales,
+                  int64_t K, int64_t N, int64_t G, uint8_t *packed)
+{
+    if (!layout_ok(bits, K, N, G))
+        return -1;
+    memset(packed, 0, oracle_packed_bytes(bits, K, N, G));
+    int64_t nblk = (N + BLK_COLS - 1) / BLK_COLS;
+#pragma omp parallel for schedule(static)
+    for (int64_t j = 0; j < nblk; ++j) {
+        for (int64_t g = 0; g < K / G; ++g) {
+            uint8_t *h = packed + header_at(bits, K, G, j, g);
+            for (int c = 0; c < BLK_COLS; ++c) {
+                int64_t n = j * BLK_COLS + c;
+                if (n >= N)
+                    continue;
+                int t = c / 16, r = c % 16;
+                uint16_t sb = scales[g * N + n];
+                h[2 * (4 * r + t)] = sb & 0xFF;
+                h[2 * (4 * r + t) + 1] = sb >> 8;
+                unsigned z = code_at(bits, qzeros, N, g, n);
+                if (bits == 4) {
+                    int bit = 4 * t; /* inside the 16-bit value at 128 + 2r */
+                    h[128 + 2 * r + bit / 8] |= (uint8_t)(z << (bit % 8));
+                } else {
+                    h[128 + 4 * r + t] = (uint8_t)z;
+                }
+            }
+        }
+        for (int64_t s = 0; s < K / STEP_ROWS; ++s) {
+            uint8_t *ch = packed + chunk_at(bits, K, G, j, s);
+            for (int o = 0; o < 4; ++o)
+                for (int c = 0; c < BLK_COLS; ++c) {
+                    int64_t n = j * BLK_COLS + c;
+                    if (n >= N)
+                        continue;
+                    for (int i = 0; i < 8; ++i) {
+                        int64_t k = s * STEP_ROWS + 8 * o + i;
+                        unsigned q = code_at(bits, qweight, N, k, n);
+                        if (bits == 4) {
+                            uint8_t *wp = ch + w4_word_in_chunk(o, c);
+                            put_u32(wp, get_u32(wp) | ((uint32_t)q << w4_shift_of_row(i)));
+                        } else {
+                            ch[w8_byte_in_chunk(o, i, c)] = (uint8_t)q;
+                        }
+                    }
+                }
+        }
+    }
+    return 0;
+}
+
+/* Inverse of oracle_repack: recover the codes [K][N], zeros [K/G][N] (one  */
+/* byte per value, unpacked) and the scale bits [K/G][N].  W4 callers can   */
+/* rebuild checkpoint words with oracle_pack_w4.                            */
+int oracle_unrepack(int bits, const uint8_t *packed, int64_t K, int64_t N, int64_t G,
+                    uint8_t *codes, uint8_t *zeros, uint16_t *scales)
+{
+    if (!layout_ok(bits, K, N, G))
+        return -1;
+    int64_t nblk = (N + BLK_COLS - 1) / BLK_COLS;
+#pragma omp parallel for schedule(static)
+    for (int64_t j = 0; j < nblk; ++j) {
+        for (int64_t g = 0; g < K / G; ++g) {
+            const uint8_t *h = packed + header_at(bits, K, G, j, g);
+            for (int c = 0; c < BLK_COLS; ++c) {
+                int64_t n = j * BLK_COLS + c;
+                if (n >= N)
+                    continue;
+                int t = c / 16, r = c % 16;
+                scales[g * N + n] = (uint16_t)(h[2 * (4 * r + t)] | (h[2 * (4 * r + t) + 1] << 8));
+                if (bits == 4) {
+                    int bit = 4 * t;
+                    zeros[g * N + n] = (h[128 + 2 * r + bit / 8] >> (bit % 8)) & 0xF;
+                } else {
+                    zeros[g * N + n] = h[128 + 4 * r + t];
+                }
+            }
+        }
+        for (int64_t s = 0; s < K / STEP_ROWS; ++s) {
+            const uint8_t *ch = packed + chunk_at(bits, K, G, j, s);
+            for (int o = 0; o < 4; ++o)
+                for (int c = 0; c < BLK_COLS; ++c) {
+                    int64_t n = j * BLK_COLS + c;
+                    if (n >= N)
+                        continue;
+                    for (int i = 0; i < 8; ++i) {
+                        int64_t k = s * STEP_ROWS + 8 * o + i;
+                        if (bits == 4)
+                            codes[k * N + n] = (get_u32(ch + w4_word_in_chunk(o, c)) >> w4_shift_of_row(i)) & 0xF;
+                        else
+                            codes[k * N + n] = ch[w8_byte_in_chunk(o, i, c)];
+                    }
+                }
+        }
+    }
+    return 0;
+}
