@@ -1,0 +1,304 @@
+"""Benchmark of the fused W4A16 / W8A16 linear layer on one MI355X.
+
+Headline (value): W4A16 GEMV at M=1 over one Llama-style decoder layer's seven
+linears (q/o 4096x4096, k/v 4096x1024, gate/up 4096x14336, down 14336x4096,
+group 128), as effective HBM GB/s = algorithmic bytes / time.  A step is one
+pass over the seven GEMVs, replayed as a HIP graph; steps rotate over weight
+replicas whose total (5 x 113 MB) exceeds twice the 256 MB Infinity Cache, so
+every step streams its weights from HBM.  Inputs are resident in HBM before
+the timed region starts.
+
+Also reported: the dominant kernel against its roofline (per-launch durations
+from HIP events on the launch stream), the W4A16 prefill GEMM at M=2048
+(TFLOP/s against the dense bf16 MFMA peak), and the CPU oracle on a bounded
+sample of the headline workload.
+
+Algorithmic bytes of one linear: K*N*b/8 codes + (K/G)*N*(b/8 + 2) metadata
++ 2*M*(K + N) activations in and outputs out.  Flops: 2*M*K*N.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
+BF16_DENSE_PEAK_TFS = 2500.0  # MI355X dense bf16 MFMA, published
+INFINITY_CACHE_BYTES = 256 * 2**20
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "gemv_w4a16_layer_m1_counters.json")
+
+
+def algorithmic_bytes(bits, M, K, N, G):
+    return K * N * bits // 8 + (K // G) * N * (bits // 8 if bits == 8 else 0.5) + (K // G) * N * 2 + 2 * M * (K + N)
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "quantized_linear_layers_awq_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--replicas", type=int, default=0, help="weight replicas to rotate (0: enough to beat the cache)")
+    p.add_argument("--only", choices=["all", "gemv", "gemm"], default="all",
+                   help="restrict the run (profiling passes)")
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--gemm-iters", type=int, default=20)
+    return p.parse_args()
+
+
+def stage_layer(torch, q, synth, M):
+    """Seven linears of the decoder layer: packed weights, x and y on the GPU."""
+    import numpy as np
+
+    lins = []
+    for sid in range(7):
+        c = synth.make_case(1, sid, M, keep_codes=False)
+        dev = "cuda:0"
+        qw = torch.from_numpy(c.qweight.view(np.int32)).to(dev)
+        qz = torch.from_numpy(c.qzeros.view(np.int32)).to(dev)
+        sc = torch.from_numpy(c.scales.view(np.int16)).to(dev)
+        packed = q.tf_repack_w4(qw, qz, sc, c.K, c.N, c.G)
+        del qw, qz, sc
+        x = torch.from_numpy(c.x.view(np.int16)).to(dev).view(torch.bfloat16)
+        y = torch.empty((M, c.N), dtype=torch.bfloat16, device=dev)
+        lins.append(dict(name=c.name, K=c.K, N=c.N, G=c.G, M=M, packed=packed, x=x, y=y,
+                         bytes=algorithmic_bytes(4, M, c.K, c.N, c.G)))
+    torch.cuda.synchronize()
+    return lins
+
+
+def cpu_baseline(synth, oracle, M, budget_s=12.0):
+    """The oracle, untuned, on the headline workload: whole passes over the
+    seven linears (dequant + fp64 linear), as many as fit the time budget."""
+    cases = [synth.make_case(1, sid, M, keep_codes=False) for sid in range(7)]
+    total_bytes = sum(algorithmic_bytes(4, M, c.K, c.N, c.G) for c in cases)
+    passes, t0 = 0, time.perf_counter()
+    while True:
+        for c in cases:
+            oracle.awq_linear(c)
+        passes += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    return dict(value=round(passes * total_bytes / el / 1e9, 3), unit="GB/s", cores=oracle.num_threads(),
+                kind="oracle",
+                sample=f"{passes} full pass(es) over the 7 layer linears at M=1 "
+                       f"({passes * total_bytes / 1e6:.0f} MB of algorithmic bytes, {el:.1f} s)")
+
+
+def queue_filler(torch, ms):
+    """Enqueue ~ms of GPU work so the launches queued after it run back to back."""
+    n = 8192
+    a = torch.randn((n, n), dtype=torch.bfloat16, device="cuda:0")
+    reps = max(1, int(ms / 0.6))
+    for _ in range(reps):
+        a = (a @ a).clamp_(-1, 1)
+    return a
+
+
+def bench_gemv(torch, q, args):
+    import synth
+
+    lins = stage_layer(torch, q, synth, M=1)
+    layer_bytes = sum(l["bytes"] for l in lins)
+    packed_bytes = sum(l["packed"].numel() for l in lins)
+    R = args.replicas or max(2, -(-2 * INFINITY_CACHE_BYTES // packed_bytes) + 1)
+    replicas = [[l["packed"] for l in lins]]
+    for _ in range(R - 1):
+        replicas.append([p.clone() for p in replicas[0]])
+    torch.cuda.synchronize()
+
+    def layer_pass(r):
+        for l, p in zip(lins, replicas[r]):
+            q.tf_gemv_w4a16(l["x"], p, l["K"], l["N"], l["G"], y=l["y"])
+
+    # eager reference results, then one graph per replica
+    layer_pass(0)
+    torch.cuda.synchronize()
+    ref = [l["y"].clone() for l in lins]
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    graphs = []
+    with torch.cuda.stream(stream):
+        for r in range(R):
+            layer_pass(r)  # warm the capture stream before capturing
+        torch.cuda.synchronize()
+        for r in range(R):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                layer_pass(r)
+            graphs.append(g)
+    torch.cuda.synchronize()
+    for r in range(R):
+        graphs[r].replay()
+        torch.cuda.synchronize()
+        for l, y0 in zip(lins, ref):
+            assert torch.equal(l["y"], y0), "graph replay differs from the eager result"
+
+    for i in range(args.warmup):
+        graphs[i % R].replay()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(args.steps):
+        graphs[i % R].replay()
+    t1.record()
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / args.steps
+
+    # eager step time for reference (host launch overhead included)
+    torch.cuda.synchronize()
+    h0 = time.perf_counter()
+    n_eager = min(args.steps, 50)
+    for i in range(n_eager):
+        layer_pass(i % R)
+    torch.cuda.synchronize()
+    eager_ms = (time.perf_counter() - h0) * 1e3 / n_eager
+
+    # per-launch kernel durations: event pairs around eager launches queued
+    # behind filler work, so no host gap lands inside a pair
+    n_prof = min(args.steps, 40)
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in lins]
+           for _ in range(n_prof)]
+    keep = queue_filler(torch, ms=0.05 * n_prof * len(lins) + 5)
+    for i in range(n_prof):
+        r = i % R
+        for (e0, e1), l, p in zip(evs[i], lins, replicas[r]):
+            e0.record()
+            q.tf_gemv_w4a16(l["x"], p, l["K"], l["N"], l["G"], y=l["y"])
+            e1.record()
+    torch.cuda.synchronize()
+    del keep
+    per_lin = [[evs[i][j][0].elapsed_time(evs[i][j][1]) for i in range(n_prof)] for j in range(len(lins))]
+    mean_us = [1e3 * sum(v) / len(v) for v in per_lin]
+    dur_total_us = sum(mean_us)
+    achieved = layer_bytes / (dur_total_us * 1e-6) / 1e9
+
+    traffic = None
+    if os.path.exists(COUNTERS_FILE):
+        with open(COUNTERS_FILE) as f:
+            cnt = json.load(f)
+        if cnt.get("kernel_source_hash") == kernel_source_hash():
+            traffic = cnt.get("hbm_bytes_per_launch")
+
+    value = layer_bytes / (ms_step * 1e-3) / 1e9
+    return dict(
+        value=value, ms_step=ms_step, eager_ms=eager_ms, replicas=R, layer_bytes=layer_bytes,
+        per_linear=[dict(name=l["name"].replace("c1_layer_", "").replace("_M1", ""), K=l["K"], N=l["N"],
+                         us=round(u, 3), gbs=round(l["bytes"] / (u * 1e-6) / 1e9, 1))
+                    for l, u in zip(lins, mean_us)],
+        roofline=dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                      frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic,
+                      kernel="gemv_kernel (tf_gemv_w4a16, W4, one k-tile per group)",
+                      bytes_per_launch=round(layer_bytes / len(lins)),
+                      avg_launch_us=round(dur_total_us / len(lins), 3)),
+    )
+
+
+def bench_gemm(torch, q, args):
+    import numpy as np
+
+    import synth
+
+    shapes = []
+    for sid in (0, 1):
+        c = synth.make_case(3, sid, 2048, keep_codes=False)
+        dev = "cuda:0"
+        qw = torch.from_numpy(c.qweight.view(np.int32)).to(dev)
+        qz = torch.from_numpy(c.qzeros.view(np.int32)).to(dev)
+        sc = torch.from_numpy(c.scales.view(np.int16)).to(dev)
+        packed = q.tf_repack_w4(qw, qz, sc, c.K, c.N, c.G)
+        x = torch.from_numpy(c.x.view(np.int16)).to(dev).view(torch.bfloat16)
+        y = torch.empty((c.M, c.N), dtype=torch.bfloat16, device=dev)
+        shapes.append(dict(M=c.M, K=c.K, N=c.N, G=c.G, packed=packed, x=x, y=y))
+    for s in shapes:
+        for _ in range(3):
+            q.tf_gemm_w4a16(s["x"], s["packed"], s["K"], s["N"], s["G"], y=s["y"])
+    torch.cuda.synchronize()
+    out = []
+    for s in shapes:
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.gemm_iters)]
+        for e0, e1 in evs:
+            e0.record()
+            q.tf_gemm_w4a16(s["x"], s["packed"], s["K"], s["N"], s["G"], y=s["y"])
+            e1.record()
+        torch.cuda.synchronize()
+        us = 1e3 * sum(e0.elapsed_time(e1) for e0, e1 in evs) / len(evs)
+        fl = 2.0 * s["M"] * s["K"] * s["N"]
+        out.append(dict(M=s["M"], K=s["K"], N=s["N"], us=round(us, 2), tflops=round(fl / (us * 1e-6) / 1e12, 1)))
+    tot_fl = sum(2.0 * o["M"] * o["K"] * o["N"] for o in out)
+    tot_us = sum(o["us"] for o in out)
+    tfs = tot_fl / (tot_us * 1e-6) / 1e12
+    return dict(
+        metric="W4A16 GEMM M=2048 TFLOP/s", value=round(tfs, 1), unit="TFLOP/s",
+        frac_of_peak=round(tfs / BF16_DENSE_PEAK_TFS, 4), shapes=out,
+        roofline=dict(bound="mfma", achieved=round(tfs, 1), peak=BF16_DENSE_PEAK_TFS, unit="TFLOP/s",
+                      frac=round(tfs / BF16_DENSE_PEAK_TFS, 4), traffic=None,
+                      kernel="gemm_kernel (tf_gemm_w4a16)"),
+    )
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this build has no multi-GPU path.",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import quantized_linear_layers_awq_amd as q
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU (MI355X)", file=sys.stderr)
+        sys.exit(1)
+    q.load_library()
+    torch.cuda.set_device(0)
+
+    line = {
+        "metric": "W4A16 GEMV M=1 effective HBM GB/s; W4A16 GEMM M=2048 TFLOP/s (% of peak)",
+        "value": None, "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": None, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "W4A16 GEMV, M=1, one Llama-style decoder layer (q/o 4096x4096, k/v 4096x1024, "
+                               "gate/up 4096x14336, down 14336x4096), group 128, HIP-graph replay, "
+                               "weights rotating over replicas larger than twice the Infinity Cache",
+                   "global_batch": 1, "parallelism": "none (1 GPU)"},
+    }
+    if args.only in ("all", "gemv"):
+        gv = bench_gemv(torch, q, args)
+        line["value"] = round(gv["value"], 1)
+        line["ms_per_step"] = round(gv["ms_step"], 5)
+        line["config"].update(replicas=gv["replicas"], layer_bytes=int(gv["layer_bytes"]))
+        line["roofline"] = gv["roofline"]
+        line["gemv_detail"] = dict(eager_ms_per_step=round(gv["eager_ms"], 4), per_linear=gv["per_linear"],
+                                   frac_of_hbm_peak=round(gv["value"] / HBM_PEAK_GBS, 4))
+    if args.only in ("all", "gemm"):
+        line["gemm"] = bench_gemm(torch, q, args)
+    if args.only == "all" and not args.no_cpu:
+        import oracle
+        import synth
+
+        line["cpu_baseline"] = cpu_baseline(synth, oracle, M=1)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

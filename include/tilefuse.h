@@ -1,0 +1,152 @@
+/*
+ * tilefuse.h -- C ABI of the fused W4A16 / W8A16 linear layer for AMD MI355X
+ * (gfx950).
+ *
+ * The operation (TileFuse technical summary, Methodology section 1, "Fused
+ * mixed-precision microkernels"): unpack INT4/INT8 weights, dequantize them
+ * as (q - zero) * scale with per-group or per-channel metadata, and run the
+ * GEMM (prefill) or GEMV (token generation, Methodology section 3) in one
+ * kernel flow, never writing full-precision weights to global memory.  The
+ * weights are AWQ-style checkpoints (Contribution 1).  An offline step
+ * re-lays them out as interleaved pre-tiled blocks with the metadata packed
+ * next to the codes (Methodology section 2, "Interleaved pre-tiling").
+ *
+ *   y[m][n] = sum_k x[m][k] * (q[k][n] - z[g][n]) * s[g][n],  g = k / G
+ *
+ * Conventions shared by every call:
+ *  - All data pointers are HIP device pointers owned by the caller; the
+ *    library allocates nothing and keeps no pointer after a call returns.
+ *  - Arrays are row-major and contiguous.  bf16 values travel as uint16_t
+ *    bit patterns.
+ *  - `stream` is a hipStream_t (NULL = the legacy default stream).  Calls are
+ *    asynchronous on it; faults inside kernels surface at the caller's next
+ *    synchronisation, as usual for HIP.
+ *  - Arguments are validated on the host before any HIP call.  A call that
+ *    returns anything but TF_OK has launched nothing and written nothing.
+ *  - M == 0 is a valid empty problem: TF_OK, nothing launched.
+ *  - Outputs must not alias inputs, the packed buffer or the workspace.
+ *
+ * Shape rules (TF_ERR_SHAPE / TF_ERR_GROUP when broken):
+ *  - K > 0, N > 0, K % 32 == 0; W4 also needs N % 8 == 0 (eight columns per
+ *    packed word).
+ *  - G > 0, G % 32 == 0, K % G == 0, and G divides 128, is a multiple of
+ *    128, or equals K.  Per-channel metadata is G == K.
+ *  - GEMV: 1 <= M <= 16.  GEMM: 1 <= M <= 2^30.
+ *  - Sizes are 64-bit; every dimension must be below 2^31.
+ */
+#ifndef TILEFUSE_H
+#define TILEFUSE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    TF_OK = 0,
+    TF_ERR_NULL = 1,              /* a required pointer is NULL */
+    TF_ERR_SHAPE = 2,             /* M, K or N outside the rules above */
+    TF_ERR_GROUP = 3,             /* G outside the rules above */
+    TF_ERR_ALIGN = 4,             /* a pointer misses its required alignment */
+    TF_ERR_BUFFER_TOO_SMALL = 5,  /* packed_bytes or ws_bytes below the size query */
+    TF_ERR_UNSUPPORTED = 6,       /* valid request this build does not implement */
+    TF_ERR_HIP = 7                /* the HIP runtime reported a launch error */
+} tf_status;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *tf_status_string(int status);
+
+/* Version of the packed (pre-tiled) layout written by tf_repack_*.  A packed
+ * buffer is only valid for the version that wrote it. */
+int tf_format_version(void);
+
+/* ------------------------------------------------------------------------ */
+/* Offline interleaved pre-tiling (Methodology section 2).                   */
+/*                                                                           */
+/* Layout, version 2 (the pages fix no geometry; this is the library's):     */
+/*  - Output columns in blocks of 16, block-major; ceil(N/16) blocks, padding */
+/*    columns carry code 0, zero 0, scale 0.  A block is one contiguous       */
+/*    range: its metadata, then its codes.                                   */
+/*  - Metadata: one record per group in ascending k -- W4 40 bytes (16 bf16   */
+/*    scales, then 16 zero-point nibbles), W8 48 bytes (16 scales, 16 zero   */
+/*    bytes) -- the region zero-padded to a multiple of 16 bytes.  Column c: */
+/*    scale bits at byte 2c; W4 zero in nibble c%2 of byte 32 + c/2; W8     */
+/*    zero at byte 32 + c.                                                   */
+/*  - Codes: ceil(K/128) k-tiles of 128 rows (W4 1024 bytes, W8 2048); rows  */
+/*    past K are padding.  Row 32u + 8o + i of a k-tile (u, o < 4, i < 8),   */
+/*    column r: W4 in the 32-bit word at byte 16(16o + r) + 4u, nibble       */
+/*    i/2 + 4(i%2); W8 at byte 1024(u/2) + 16(16o + r) + 8(u%2) + i.         */
+/*  So lane L = 16o + r of a 64-lane wavefront reading 16 bytes at 16L (W4)   */
+/*  receives, for each of the k-tile's four 32-row steps, eight consecutive  */
+/*  rows of column r: the B operand of a 16x16x32 bf16 MFMA after unpacking. */
+/*  Group sizes must keep every 128-row k-tile inside one group or made of   */
+/*  whole groups: G in {32, 64}, G a multiple of 128, or G == K.             */
+/* ------------------------------------------------------------------------ */
+
+/* Bytes of the packed buffer for (K, N, G); 0 if the shape is invalid. */
+size_t tf_packed_bytes_w4(int64_t K, int64_t N, int64_t G);
+size_t tf_packed_bytes_w8(int64_t K, int64_t N, int64_t G);
+
+/* Re-lay out an AWQ W4 checkpoint.
+ *   qweight  uint32 [K][N/8]: word (k, c) holds columns 8c..8c+7 of row k,
+ *            column 8c + j in nibble p(j), p = (0, 4, 1, 5, 2, 6, 3, 7).
+ *            4-byte aligned.
+ *   qzeros   uint32 [K/G][N/8], same packing.  4-byte aligned.
+ *   scales   bf16 [K/G][N].  2-byte aligned.
+ *   packed   output, packed_bytes >= tf_packed_bytes_w4(K, N, G); 16-byte
+ *            aligned.  Every byte of the layout is written. */
+int tf_repack_w4(const uint32_t *qweight, const uint32_t *qzeros, const uint16_t *scales,
+                 int64_t K, int64_t N, int64_t G, void *packed, size_t packed_bytes, void *stream);
+
+/* Re-lay out a W8 checkpoint: qweight uint8 [K][N], zeros uint8 [K/G][N]
+ * (unsigned codes, zero points stored as bytes), scales bf16 [K/G][N]. */
+int tf_repack_w8(const uint8_t *qweight, const uint8_t *zeros, const uint16_t *scales,
+                 int64_t K, int64_t N, int64_t G, void *packed, size_t packed_bytes, void *stream);
+
+/* ------------------------------------------------------------------------ */
+/* Fused linear layer.                                                       */
+/*   x          bf16 [M][K], 16-byte aligned                                 */
+/*   packed     a buffer written by tf_repack_w4 / _w8 with the same K, N, G  */
+/*   y          bf16 [M][N] output (fp32 accumulation, one rounding to bf16, */
+/*              nearest-even), 2-byte aligned                                */
+/*   workspace  device scratch of ws_bytes >= tf_workspace_bytes(...), 256-  */
+/*              byte aligned.  NULL is fine when the size query returns 0,   */
+/*              which it does for every shape in this version (kept in the   */
+/*              signature for split-K variants).                             */
+/* ------------------------------------------------------------------------ */
+size_t tf_workspace_bytes(int bits, int is_gemm, int64_t M, int64_t K, int64_t N, int64_t G);
+
+/* Token-generation GEMV, 1 <= M <= 16 (Methodology section 3). */
+int tf_gemv_w4a16(const uint16_t *x, const void *packed, size_t packed_bytes, uint16_t *y,
+                  int64_t M, int64_t K, int64_t N, int64_t G,
+                  void *workspace, size_t ws_bytes, void *stream);
+int tf_gemv_w8a16(const uint16_t *x, const void *packed, size_t packed_bytes, uint16_t *y,
+                  int64_t M, int64_t K, int64_t N, int64_t G,
+                  void *workspace, size_t ws_bytes, void *stream);
+
+/* Prefill GEMM, any M >= 1: each weight tile is unpacked once into LDS as the
+ * exact bf16 values q - z and reused by every row of the tile; each group's
+ * scale is applied once per (group, column) to its fp32 partial sum
+ * (Methodology section 1). */
+int tf_gemm_w4a16(const uint16_t *x, const void *packed, size_t packed_bytes, uint16_t *y,
+                  int64_t M, int64_t K, int64_t N, int64_t G,
+                  void *workspace, size_t ws_bytes, void *stream);
+int tf_gemm_w8a16(const uint16_t *x, const void *packed, size_t packed_bytes, uint16_t *y,
+                  int64_t M, int64_t K, int64_t N, int64_t G,
+                  void *workspace, size_t ws_bytes, void *stream);
+
+/* Test hook, not on the hot path: the dequantized weights w[K][N] as fp32
+ * ((q - z) * s is exact in fp32), produced by the same unpack and dequant
+ * code the GEMM uses.  w is 4-byte aligned. */
+int tf_dequant_w4_f32(const void *packed, size_t packed_bytes, float *w,
+                      int64_t K, int64_t N, int64_t G, void *stream);
+int tf_dequant_w8_f32(const void *packed, size_t packed_bytes, float *w,
+                      int64_t K, int64_t N, int64_t G, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TILEFUSE_H */

@@ -192,24 +192,28 @@ int oracle_num_threads(void)
 }
 
 /* ------------------------------------------------------------------ */
-/* Interleaved pre-tiled layout (format version 1).                    */
+/* Interleaved pre-tiled layout (format version 2).                    */
 /*                                                                    */
-/*   Column blocks of 64 output columns, block-major; ceil(N/64)       */
+/*   Column blocks of 16 output columns, block-major; ceil(N/16)       */
 /*   blocks, columns past N are padding (code 0, zero 0, scale 0).     */
-/*   Inside a block, groups in ascending k; each group is a header     */
-/*   followed by its G/32 chunks, one chunk per 32 rows ("k-step").   */
-/*   Header (bytes): 128 of scales, then zeros (W4: 32, W8: 64).       */
-/*     column c of the block, t = c / 16, r = c % 16:                  */
-/*       scale bits   at 2*(4r + t)                                    */
-/*       W4 zero      nibble t of the 16-bit little-endian value at    */
-/*                    128 + 2r                                         */
-/*       W8 zero      byte 128 + 4r + t                                */
-/*   Chunk (W4 1024 bytes, W8 2048), rows 32s + 8o + i, o < 4, i < 8:  */
-/*       W4  word at 16*(16o + r) + 4t; row i in nibble i/2 + 4*(i%2)  */
-/*       W8  byte at 1024*(t/2) + 16*(16o + r) + 8*(t%2) + i           */
+/*   A block is its metadata followed by its codes:                    */
+/*     metadata: one record per group in ascending k, W4 40 bytes      */
+/*       (16 bf16 scales, then 16 zero nibbles), W8 48 bytes (16       */
+/*       scales, 16 zero bytes); the region is zero-padded to a        */
+/*       multiple of 16 bytes.  Column c of the block:                 */
+/*         scale bits at 2c; W4 zero in byte 32 + c/2 (low nibble for  */
+/*         even c); W8 zero at byte 32 + c.                            */
+/*     codes: ceil(K/128) k-tiles of 128 rows (W4 1024 bytes, W8      */
+/*       2048); rows past K are padding (code 0).  Row 32u + 8o + i    */
+/*       of a k-tile (u, o < 4, i < 8), column r:                      */
+/*         W4  word at 16*(16o + r) + 4u; row i in nibble i/2 + 4*(i%2)*/
+/*         W8  byte at 1024*(u/2) + 16*(16o + r) + 8*(u%2) + i         */
+/*   Group sizes: multiples of 32 dividing K that divide 128, are a    */
+/*   multiple of 128, or equal K -- so a k-tile either lies inside one */
+/*   group or holds whole groups.                                      */
 /* ------------------------------------------------------------------ */
-#define BLK_COLS 64
-#define STEP_ROWS 32
+#define BLK_COLS 16
+#define TILE_ROWS 128
 
 static int layout_ok(int bits, int64_t K, int64_t N, int64_t G)
 {
@@ -217,17 +221,24 @@ static int layout_ok(int bits, int64_t K, int64_t N, int64_t G)
         return 0;
     if (K <= 0 || N <= 0 || G <= 0)
         return 0;
-    if (K % STEP_ROWS || G % STEP_ROWS || K % G)
+    if (K % 32 || G % 32 || K % G)
+        return 0;
+    if (!(TILE_ROWS % G == 0 || G % TILE_ROWS == 0 || G == K))
         return 0;
     if (bits == 4 && N % 8)
         return 0;
     return 1;
 }
 
-static int64_t chunk_bytes(int bits) { return bits == 4 ? 1024 : 2048; }
-static int64_t header_bytes(int bits) { return bits == 4 ? 160 : 192; }
-static int64_t group_bytes(int bits, int64_t G) { return header_bytes(bits) + (G / STEP_ROWS) * chunk_bytes(bits); }
-static int64_t block_bytes(int bits, int64_t K, int64_t G) { return (K / G) * group_bytes(bits, G); }
+static int64_t tile_bytes(int bits) { return bits == 4 ? 1024 : 2048; }
+static int64_t record_bytes(int bits) { return bits == 4 ? 40 : 48; }
+static int64_t meta_bytes(int bits, int64_t K, int64_t G)
+{
+    int64_t m = (K / G) * record_bytes(bits);
+    return (m + 15) / 16 * 16;
+}
+static int64_t ktiles(int64_t K) { return (K + TILE_ROWS - 1) / TILE_ROWS; }
+static int64_t block_bytes(int bits, int64_t K, int64_t G) { return meta_bytes(bits, K, G) + ktiles(K) * tile_bytes(bits); }
 
 size_t oracle_packed_bytes(int bits, int64_t K, int64_t N, int64_t G)
 {
@@ -237,35 +248,34 @@ size_t oracle_packed_bytes(int bits, int64_t K, int64_t N, int64_t G)
     return (size_t)(nblk * block_bytes(bits, K, G));
 }
 
-/* byte offset of the header of (block j, group g) */
-static int64_t header_at(int bits, int64_t K, int64_t G, int64_t j, int64_t g)
+/* byte offset of the metadata record of (block j, group g) */
+static int64_t record_at(int bits, int64_t K, int64_t G, int64_t j, int64_t g)
 {
-    return j * block_bytes(bits, K, G) + g * group_bytes(bits, G);
+    return j * block_bytes(bits, K, G) + g * record_bytes(bits);
 }
 
-/* byte offset of the chunk of global k-step s in block j */
-static int64_t chunk_at(int bits, int64_t K, int64_t G, int64_t j, int64_t s)
+/* byte offset of (row k, block column r) inside the code region of block j;  */
+/* for W4 also the bit shift inside the little-endian 32-bit word there.      */
+static int64_t code_at(int bits, int64_t K, int64_t G, int64_t j, int64_t k, int r, int *shift)
 {
-    int64_t per_group = G / STEP_ROWS;
-    return header_at(bits, K, G, j, s / per_group) + header_bytes(bits) + (s % per_group) * chunk_bytes(bits);
-}
-
-/* position of (row-in-step o*8+i, column c of the block) inside a chunk:   */
-/* byte offset, and for W4 the bit shift inside the little-endian word.   */
-static int64_t w4_word_in_chunk(int o, int c) { return 16 * (16 * o + c % 16) + 4 * (c / 16); }
-static int w4_shift_of_row(int i) { return 4 * (i / 2 + 4 * (i % 2)); }
-static int64_t w8_byte_in_chunk(int o, int i, int c)
-{
-    int t = c / 16, r = c % 16;
-    return 1024 * (t / 2) + 16 * (16 * o + r) + 8 * (t % 2) + i;
+    int64_t t = k / TILE_ROWS;
+    int kr = (int)(k % TILE_ROWS);
+    int u = kr / 32, o = (kr % 32) / 8, i = kr % 8;
+    int64_t base = j * block_bytes(bits, K, G) + meta_bytes(bits, K, G) + t * tile_bytes(bits);
+    if (bits == 4) {
+        *shift = 4 * (i / 2 + 4 * (i % 2));
+        return base + 16 * (16 * o + r) + 4 * u;
+    }
+    *shift = 0;
+    return base + 1024 * (u / 2) + 16 * (16 * o + r) + 8 * (u % 2) + i;
 }
 
 static void put_u32(uint8_t *p, uint32_t v) { p[0] = v; p[1] = v >> 8; p[2] = v >> 16; p[3] = v >> 24; }
 static uint32_t get_u32(const uint8_t *p) { return p[0] | (p[1] << 8) | (p[2] << 16) | ((uint32_t)p[3] << 24); }
 
-/* Codes and zeros are read through these accessors so one repack serves   */
-/* both widths.                                                           */
-static unsigned code_at(int bits, const void *qweight, int64_t N, int64_t k, int64_t n)
+/* Codes and zeros are read through this accessor so one repack serves both  */
+/* widths.                                                                   */
+static unsigned ckpt_code(int bits, const void *qweight, int64_t N, int64_t k, int64_t n)
 {
     return bits == 4 ? awq_code((const uint32_t *)qweight, N, k, n) : ((const uint8_t *)qweight)[k * N + n];
 }
@@ -279,43 +289,30 @@ int oracle_repack(int bits, const void *qweight, const void *qzeros, const uint1
     int64_t nblk = (N + BLK_COLS - 1) / BLK_COLS;
 #pragma omp parallel for schedule(static)
     for (int64_t j = 0; j < nblk; ++j) {
-        for (int64_t g = 0; g < K / G; ++g) {
-            uint8_t *h = packed + header_at(bits, K, G, j, g);
-            for (int c = 0; c < BLK_COLS; ++c) {
-                int64_t n = j * BLK_COLS + c;
-                if (n >= N)
-                    continue;
-                int t = c / 16, r = c % 16;
+        for (int r = 0; r < BLK_COLS; ++r) {
+            int64_t n = j * BLK_COLS + r;
+            if (n >= N)
+                continue;
+            for (int64_t g = 0; g < K / G; ++g) {
+                uint8_t *rec = packed + record_at(bits, K, G, j, g);
                 uint16_t sb = scales[g * N + n];
-                h[2 * (4 * r + t)] = sb & 0xFF;
-                h[2 * (4 * r + t) + 1] = sb >> 8;
-                unsigned z = code_at(bits, qzeros, N, g, n);
-                if (bits == 4) {
-                    int bit = 4 * t; /* inside the 16-bit value at 128 + 2r */
-                    h[128 + 2 * r + bit / 8] |= (uint8_t)(z << (bit % 8));
-                } else {
-                    h[128 + 4 * r + t] = (uint8_t)z;
-                }
+                rec[2 * r] = sb & 0xFF;
+                rec[2 * r + 1] = sb >> 8;
+                unsigned z = ckpt_code(bits, qzeros, N, g, n);
+                if (bits == 4)
+                    rec[32 + r / 2] |= (uint8_t)(z << (4 * (r % 2)));
+                else
+                    rec[32 + r] = (uint8_t)z;
             }
-        }
-        for (int64_t s = 0; s < K / STEP_ROWS; ++s) {
-            uint8_t *ch = packed + chunk_at(bits, K, G, j, s);
-            for (int o = 0; o < 4; ++o)
-                for (int c = 0; c < BLK_COLS; ++c) {
-                    int64_t n = j * BLK_COLS + c;
-                    if (n >= N)
-                        continue;
-                    for (int i = 0; i < 8; ++i) {
-                        int64_t k = s * STEP_ROWS + 8 * o + i;
-                        unsigned q = code_at(bits, qweight, N, k, n);
-                        if (bits == 4) {
-                            uint8_t *wp = ch + w4_word_in_chunk(o, c);
-                            put_u32(wp, get_u32(wp) | ((uint32_t)q << w4_shift_of_row(i)));
-                        } else {
-                            ch[w8_byte_in_chunk(o, i, c)] = (uint8_t)q;
-                        }
-                    }
-                }
+            for (int64_t k = 0; k < K; ++k) {
+                int shift;
+                int64_t at = code_at(bits, K, G, j, k, r, &shift);
+                unsigned q = ckpt_code(bits, qweight, N, k, n);
+                if (bits == 4)
+                    put_u32(packed + at, get_u32(packed + at) | ((uint32_t)q << shift));
+                else
+                    packed[at] = (uint8_t)q;
+            }
         }
     }
     return 0;
@@ -332,37 +329,20 @@ int oracle_unrepack(int bits, const uint8_t *packed, int64_t K, int64_t N, int64
     int64_t nblk = (N + BLK_COLS - 1) / BLK_COLS;
 #pragma omp parallel for schedule(static)
     for (int64_t j = 0; j < nblk; ++j) {
-        for (int64_t g = 0; g < K / G; ++g) {
-            const uint8_t *h = packed + header_at(bits, K, G, j, g);
-            for (int c = 0; c < BLK_COLS; ++c) {
-                int64_t n = j * BLK_COLS + c;
-                if (n >= N)
-                    continue;
-                int t = c / 16, r = c % 16;
-                scales[g * N + n] = (uint16_t)(h[2 * (4 * r + t)] | (h[2 * (4 * r + t) + 1] << 8));
-                if (bits == 4) {
-                    int bit = 4 * t;
-                    zeros[g * N + n] = (h[128 + 2 * r + bit / 8] >> (bit % 8)) & 0xF;
-                } else {
-                    zeros[g * N + n] = h[128 + 4 * r + t];
-                }
+        for (int r = 0; r < BLK_COLS; ++r) {
+            int64_t n = j * BLK_COLS + r;
+            if (n >= N)
+                continue;
+            for (int64_t g = 0; g < K / G; ++g) {
+                const uint8_t *rec = packed + record_at(bits, K, G, j, g);
+                scales[g * N + n] = (uint16_t)(rec[2 * r] | (rec[2 * r + 1] << 8));
+                zeros[g * N + n] = bits == 4 ? (rec[32 + r / 2] >> (4 * (r % 2))) & 0xF : rec[32 + r];
             }
-        }
-        for (int64_t s = 0; s < K / STEP_ROWS; ++s) {
-            const uint8_t *ch = packed + chunk_at(bits, K, G, j, s);
-            for (int o = 0; o < 4; ++o)
-                for (int c = 0; c < BLK_COLS; ++c) {
-                    int64_t n = j * BLK_COLS + c;
-                    if (n >= N)
-                        continue;
-                    for (int i = 0; i < 8; ++i) {
-                        int64_t k = s * STEP_ROWS + 8 * o + i;
-                        if (bits == 4)
-                            codes[k * N + n] = (get_u32(ch + w4_word_in_chunk(o, c)) >> w4_shift_of_row(i)) & 0xF;
-                        else
-                            codes[k * N + n] = ch[w8_byte_in_chunk(o, i, c)];
-                    }
-                }
+            for (int64_t k = 0; k < K; ++k) {
+                int shift;
+                int64_t at = code_at(bits, K, G, j, k, r, &shift);
+                codes[k * N + n] = bits == 4 ? (get_u32(packed + at) >> shift) & 0xF : packed[at];
+            }
         }
     }
     return 0;

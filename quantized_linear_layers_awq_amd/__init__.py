@@ -1,0 +1,32 @@
+"""Fused W4A16 / W8A16 linear layer for AMD MI355X (gfx950).
+
+Thin binding over ``libtilefuse.so`` (C ABI declared in ``include/tilefuse.h``).
+Each ``tf_*`` function here has the name of the C entry point it calls and
+only marshals arguments: torch supplies device memory and the current
+stream, every step of the computation runs in the HIP kernels.  There is no
+CPU fallback: without the built library every call raises.
+"""
+
+from __future__ import annotations
+
+from ._binding import (  # noqa: F401
+    TF_ERRORS,
+    TileFuseError,
+    library_path,
+    load_library,
+    tf_dequant_w4_f32,
+    tf_dequant_w8_f32,
+    tf_format_version,
+    tf_gemm_w4a16,
+    tf_gemm_w8a16,
+    tf_gemv_w4a16,
+    tf_gemv_w8a16,
+    tf_packed_bytes_w4,
+    tf_packed_bytes_w8,
+    tf_repack_w4,
+    tf_repack_w8,
+    tf_status_string,
+    tf_workspace_bytes,
+)
+
+__all__ = [n for n in dir() if n.startswith("tf_")] + ["TileFuseError", "load_library"]

@@ -1,0 +1,219 @@
+"""ctypes marshalling for libtilefuse.so (argument handling only).
+
+Torch tensors are passed as raw device pointers plus sizes; the stream is
+torch's current stream on the tensor's device.  Outputs and the split-K
+workspace are allocated with torch.  The C library validates every argument
+before touching the GPU and returns a status; a non-zero status raises
+:class:`TileFuseError`.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libtilefuse.so")
+
+TF_ERRORS = {
+    0: "TF_OK", 1: "TF_ERR_NULL", 2: "TF_ERR_SHAPE", 3: "TF_ERR_GROUP", 4: "TF_ERR_ALIGN",
+    5: "TF_ERR_BUFFER_TOO_SMALL", 6: "TF_ERR_UNSUPPORTED", 7: "TF_ERR_HIP",
+}
+
+
+class TileFuseError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        self.name = TF_ERRORS.get(status, f"status {status}")
+        super().__init__(f"{where}: {tf_status_string(status)}")
+
+
+_lib = None
+_lock = threading.Lock()
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libtilefuse.so (built in-tree); raise if it was never built."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(_LIB_PATH):
+            raise ImportError(f"{_LIB_PATH} is missing: build it with quantized_linear_layers_awq_amd.build.build()")
+        L = ctypes.CDLL(_LIB_PATH)
+        P, I64, SZ, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t, ctypes.c_int
+        L.tf_status_string.argtypes = [I]
+        L.tf_status_string.restype = ctypes.c_char_p
+        L.tf_format_version.restype = I
+        for n in ("tf_packed_bytes_w4", "tf_packed_bytes_w8"):
+            getattr(L, n).argtypes = [I64, I64, I64]
+            getattr(L, n).restype = SZ
+        for n in ("tf_repack_w4", "tf_repack_w8"):
+            getattr(L, n).argtypes = [P, P, P, I64, I64, I64, P, SZ, P]
+            getattr(L, n).restype = I
+        L.tf_workspace_bytes.argtypes = [I, I, I64, I64, I64, I64]
+        L.tf_workspace_bytes.restype = SZ
+        for n in ("tf_gemv_w4a16", "tf_gemv_w8a16", "tf_gemm_w4a16", "tf_gemm_w8a16"):
+            getattr(L, n).argtypes = [P, P, SZ, P, I64, I64, I64, I64, P, SZ, P]
+            getattr(L, n).restype = I
+        for n in ("tf_dequant_w4_f32", "tf_dequant_w8_f32"):
+            getattr(L, n).argtypes = [P, SZ, P, I64, I64, I64, P]
+            getattr(L, n).restype = I
+        _lib = L
+        return _lib
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise TileFuseError(status, where)
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(t: torch.Tensor, stream) -> int:
+    if stream is not None:
+        return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _need(t: torch.Tensor, name: str, nbytes_per_elem: int | None = None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor (got {t.device})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if nbytes_per_elem is not None and t.element_size() != nbytes_per_elem:
+        raise ValueError(f"{name} must have {nbytes_per_elem}-byte elements (got {t.dtype})")
+
+
+def tf_status_string(status: int) -> str:
+    return load_library().tf_status_string(int(status)).decode()
+
+
+def tf_format_version() -> int:
+    return int(load_library().tf_format_version())
+
+
+def tf_packed_bytes_w4(K: int, N: int, G: int) -> int:
+    return int(load_library().tf_packed_bytes_w4(K, N, G))
+
+
+def tf_packed_bytes_w8(K: int, N: int, G: int) -> int:
+    return int(load_library().tf_packed_bytes_w8(K, N, G))
+
+
+def tf_workspace_bytes(bits: int, is_gemm: bool, M: int, K: int, N: int, G: int) -> int:
+    return int(load_library().tf_workspace_bytes(bits, int(bool(is_gemm)), M, K, N, G))
+
+
+def _repack(bits, fn, qweight, qzeros, scales, K, N, G, packed, stream):
+    L = load_library()
+    elem = 4 if bits == 4 else 1
+    _need(qweight, "qweight", elem)
+    _need(qzeros, "qzeros", elem)
+    _need(scales, "scales", 2)
+    nbytes = (L.tf_packed_bytes_w4 if bits == 4 else L.tf_packed_bytes_w8)(K, N, G)
+    if packed is None:
+        packed = torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=qweight.device)
+    _need(packed, "packed", 1)
+    if qweight.numel() * elem < (K * N * bits) // 8 or scales.numel() * G < K * N:
+        raise ValueError(f"{fn}: qweight/scales hold fewer elements than (K, N, G) need")
+    _check(getattr(L, fn)(_ptr(qweight), _ptr(qzeros), _ptr(scales), K, N, G, _ptr(packed),
+                          packed.numel(), _stream(packed, stream)), fn)
+    return packed
+
+
+def tf_repack_w4(qweight, qzeros, scales, K, N, G, packed=None, stream=None):
+    """AWQ W4 checkpoint (int32 [K][N/8], int32 [K/G][N/8], bf16 [K/G][N]) -> packed uint8."""
+    return _repack(4, "tf_repack_w4", qweight, qzeros, scales, K, N, G, packed, stream)
+
+
+def tf_repack_w8(qweight, zeros, scales, K, N, G, packed=None, stream=None):
+    """W8 checkpoint (uint8 [K][N], uint8 [K/G][N], bf16 [K/G][N]) -> packed uint8."""
+    return _repack(8, "tf_repack_w8", qweight, zeros, scales, K, N, G, packed, stream)
+
+
+# Split-K workspaces, one per (device, stream); zero-filled at allocation and
+# left zero-filled by every successful call, so they are reused as they are.
+_workspaces: dict = {}
+
+
+def _workspace(device: torch.device, stream_handle: int, nbytes: int):
+    if nbytes == 0:
+        return None
+    key = (device.index, stream_handle)
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+        _workspaces[key] = ws
+    return ws
+
+
+def _linear(bits, is_gemm, fn, x, packed, K, N, G, y, workspace, stream):
+    L = load_library()
+    _need(x, "x", 2)
+    _need(packed, "packed", 1)
+    if x.dim() != 2 or x.shape[1] != K:
+        raise ValueError(f"{fn}: x must be [M][K] with K={K}")
+    M = x.shape[0]
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    _need(y, "y", 2)
+    if y.numel() < M * N:
+        raise ValueError(f"{fn}: y holds fewer than M*N elements")
+    sh = _stream(x, stream)
+    need = int(L.tf_workspace_bytes(bits, int(is_gemm), M, K, N, G))
+    if workspace is None:
+        workspace = _workspace(x.device, sh, need)
+    ws_ptr, ws_bytes = (None, 0) if workspace is None else (_ptr(workspace), workspace.numel() * workspace.element_size())
+    _check(getattr(L, fn)(_ptr(x), _ptr(packed), packed.numel(), _ptr(y), M, K, N, G, ws_ptr, ws_bytes, sh), fn)
+    return y
+
+
+def tf_gemv_w4a16(x, packed, K, N, G, y=None, workspace=None, stream=None):
+    """y[M][N] (bf16) for x [M][K] bf16, 1 <= M <= 16, W4 packed weights."""
+    return _linear(4, False, "tf_gemv_w4a16", x, packed, K, N, G, y, workspace, stream)
+
+
+def tf_gemv_w8a16(x, packed, K, N, G, y=None, workspace=None, stream=None):
+    return _linear(8, False, "tf_gemv_w8a16", x, packed, K, N, G, y, workspace, stream)
+
+
+def tf_gemm_w4a16(x, packed, K, N, G, y=None, workspace=None, stream=None):
+    """y[M][N] (bf16) for x [M][K] bf16, any M, W4 packed weights."""
+    return _linear(4, True, "tf_gemm_w4a16", x, packed, K, N, G, y, workspace, stream)
+
+
+def tf_gemm_w8a16(x, packed, K, N, G, y=None, workspace=None, stream=None):
+    return _linear(8, True, "tf_gemm_w8a16", x, packed, K, N, G, y, workspace, stream)
+
+
+def _dequant(fn, packed, K, N, G, w, stream):
+    L = load_library()
+    _need(packed, "packed", 1)
+    if w is None:
+        w = torch.empty((K, N), dtype=torch.float32, device=packed.device)
+    _need(w, "w", 4)
+    if w.numel() < K * N:
+        raise ValueError(f"{fn}: w holds fewer than K*N elements")
+    _check(getattr(L, fn)(_ptr(packed), packed.numel(), _ptr(w), K, N, G, _stream(packed, stream)), fn)
+    return w
+
+
+def tf_dequant_w4_f32(packed, K, N, G, w=None, stream=None):
+    """Test hook: fp32 dequantized weights [K][N] from a W4 packed buffer."""
+    return _dequant("tf_dequant_w4_f32", packed, K, N, G, w, stream)
+
+
+def tf_dequant_w8_f32(packed, K, N, G, w=None, stream=None):
+    return _dequant("tf_dequant_w8_f32", packed, K, N, G, w, stream)

@@ -1,0 +1,187 @@
+// C ABI of the fused W4A16 / W8A16 linear layer: argument validation on the
+// host (before any HIP call), then one launch sequence on the caller's stream.
+// The declarations and their documentation live in include/tilefuse.h.
+#include "tilefuse.h"
+
+#include "tf_launch.h"
+
+namespace {
+
+using tf::Layout;
+
+constexpr int64_t kDimLimit = int64_t(1) << 31;
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// Shape rules shared by every entry point; returns TF_OK or the error.
+int check_kng(int bits, int64_t K, int64_t N, int64_t G)
+{
+    if (K <= 0 || N <= 0 || K >= kDimLimit || N >= kDimLimit || K % tf::kStepRows)
+        return TF_ERR_SHAPE;
+    if (bits == 4 && N % 8)
+        return TF_ERR_SHAPE;
+    if (G <= 0 || G % tf::kStepRows || K % G)
+        return TF_ERR_GROUP;
+    // a 128-row k-tile must lie inside one group or hold whole groups
+    if (!(tf::kTileRows % G == 0 || G % tf::kTileRows == 0 || G == K))
+        return TF_ERR_GROUP;
+    return TF_OK;
+}
+
+size_t packed_bytes(int bits, int64_t K, int64_t N, int64_t G)
+{
+    if (check_kng(bits, K, N, G) != TF_OK)
+        return 0;
+    return (size_t)Layout::make(bits, K, N, G).total_bytes();
+}
+
+int repack(int bits, const void *qweight, const void *qzeros, const uint16_t *scales, int64_t K, int64_t N, int64_t G,
+           void *packed, size_t nbytes, void *stream)
+{
+    if (!qweight || !qzeros || !scales || !packed)
+        return TF_ERR_NULL;
+    if (int st = check_kng(bits, K, N, G))
+        return st;
+    if (!aligned(packed, 16) || !aligned(scales, 2) || (bits == 4 && (!aligned(qweight, 4) || !aligned(qzeros, 4))))
+        return TF_ERR_ALIGN;
+    const Layout lay = Layout::make(bits, K, N, G);
+    if (nbytes < (size_t)lay.total_bytes())
+        return TF_ERR_BUFFER_TOO_SMALL;
+    if (tf::launch_repack(bits, qweight, qzeros, scales, lay, packed, static_cast<hipStream_t>(stream)) != hipSuccess)
+        return TF_ERR_HIP;
+    return TF_OK;
+}
+
+// No kernel of this build needs scratch memory: the GEMV combines its K
+// split inside a workgroup and the GEMM owns whole output tiles.
+size_t workspace_bytes(int, int, int64_t, int64_t, int64_t, int64_t) { return 0; }
+
+int linear(int bits, bool is_gemm, const uint16_t *x, const void *packed, size_t nbytes, uint16_t *y, int64_t M,
+           int64_t K, int64_t N, int64_t G, void *ws, size_t ws_bytes, void *stream)
+{
+    if (M < 0)
+        return TF_ERR_SHAPE;
+    if (int st = check_kng(bits, K, N, G))
+        return st;
+    if (is_gemm ? M > (int64_t(1) << 30) : M > 16)
+        return TF_ERR_SHAPE;
+    if (M == 0)
+        return TF_OK;
+    if (!x || !packed || !y)
+        return TF_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(packed, 16) || !aligned(y, 2))
+        return TF_ERR_ALIGN;
+    const Layout lay = Layout::make(bits, K, N, G);
+    if (nbytes < (size_t)lay.total_bytes())
+        return TF_ERR_BUFFER_TOO_SMALL;
+    const size_t need = workspace_bytes(bits, is_gemm, M, K, N, G);
+    if (need) {
+        if (!ws)
+            return TF_ERR_NULL;
+        if (!aligned(ws, 256))
+            return TF_ERR_ALIGN;
+        if (ws_bytes < need)
+            return TF_ERR_BUFFER_TOO_SMALL;
+    }
+    hipError_t e;
+    if (is_gemm)
+        e = tf::launch_gemm(bits, x, packed, y, M, lay, static_cast<hipStream_t>(stream));
+    else
+        e = tf::launch_gemv(bits, x, packed, y, M, lay, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? TF_OK : TF_ERR_HIP;
+}
+
+int dequant(int bits, const void *packed, size_t nbytes, float *w, int64_t K, int64_t N, int64_t G, void *stream)
+{
+    if (!packed || !w)
+        return TF_ERR_NULL;
+    if (int st = check_kng(bits, K, N, G))
+        return st;
+    if (!aligned(packed, 16) || !aligned(w, 4))
+        return TF_ERR_ALIGN;
+    const Layout lay = Layout::make(bits, K, N, G);
+    if (nbytes < (size_t)lay.total_bytes())
+        return TF_ERR_BUFFER_TOO_SMALL;
+    if (tf::launch_dequant_f32(bits, packed, lay, w, static_cast<hipStream_t>(stream)) != hipSuccess)
+        return TF_ERR_HIP;
+    return TF_OK;
+}
+
+} // namespace
+
+extern "C" {
+
+const char *tf_status_string(int s)
+{
+    switch (s) {
+    case TF_OK: return "TF_OK";
+    case TF_ERR_NULL: return "TF_ERR_NULL: a required pointer is NULL";
+    case TF_ERR_SHAPE: return "TF_ERR_SHAPE: M, K or N outside the supported shapes";
+    case TF_ERR_GROUP: return "TF_ERR_GROUP: group size must be a multiple of 32 dividing K that divides 128, is a multiple of 128, or equals K";
+    case TF_ERR_ALIGN: return "TF_ERR_ALIGN: a pointer misses its required alignment";
+    case TF_ERR_BUFFER_TOO_SMALL: return "TF_ERR_BUFFER_TOO_SMALL: packed or workspace buffer too small";
+    case TF_ERR_UNSUPPORTED: return "TF_ERR_UNSUPPORTED";
+    case TF_ERR_HIP: return "TF_ERR_HIP: the HIP runtime reported a launch error";
+    default: return "unknown tf_status";
+    }
+}
+
+int tf_format_version(void) { return tf::kFormatVersion; }
+
+size_t tf_packed_bytes_w4(int64_t K, int64_t N, int64_t G) { return packed_bytes(4, K, N, G); }
+size_t tf_packed_bytes_w8(int64_t K, int64_t N, int64_t G) { return packed_bytes(8, K, N, G); }
+
+int tf_repack_w4(const uint32_t *qweight, const uint32_t *qzeros, const uint16_t *scales, int64_t K, int64_t N,
+                 int64_t G, void *packed, size_t nbytes, void *stream)
+{
+    return repack(4, qweight, qzeros, scales, K, N, G, packed, nbytes, stream);
+}
+
+int tf_repack_w8(const uint8_t *qweight, const uint8_t *zeros, const uint16_t *scales, int64_t K, int64_t N,
+                 int64_t G, void *packed, size_t nbytes, void *stream)
+{
+    return repack(8, qweight, zeros, scales, K, N, G, packed, nbytes, stream);
+}
+
+size_t tf_workspace_bytes(int bits, int is_gemm, int64_t M, int64_t K, int64_t N, int64_t G)
+{
+    if (bits != 4 && bits != 8)
+        return 0;
+    return workspace_bytes(bits, is_gemm, M, K, N, G);
+}
+
+int tf_gemv_w4a16(const uint16_t *x, const void *packed, size_t nbytes, uint16_t *y, int64_t M, int64_t K, int64_t N,
+                  int64_t G, void *ws, size_t ws_bytes, void *stream)
+{
+    return linear(4, false, x, packed, nbytes, y, M, K, N, G, ws, ws_bytes, stream);
+}
+
+int tf_gemv_w8a16(const uint16_t *x, const void *packed, size_t nbytes, uint16_t *y, int64_t M, int64_t K, int64_t N,
+                  int64_t G, void *ws, size_t ws_bytes, void *stream)
+{
+    return linear(8, false, x, packed, nbytes, y, M, K, N, G, ws, ws_bytes, stream);
+}
+
+int tf_gemm_w4a16(const uint16_t *x, const void *packed, size_t nbytes, uint16_t *y, int64_t M, int64_t K, int64_t N,
+                  int64_t G, void *ws, size_t ws_bytes, void *stream)
+{
+    return linear(4, true, x, packed, nbytes, y, M, K, N, G, ws, ws_bytes, stream);
+}
+
+int tf_gemm_w8a16(const uint16_t *x, const void *packed, size_t nbytes, uint16_t *y, int64_t M, int64_t K, int64_t N,
+                  int64_t G, void *ws, size_t ws_bytes, void *stream)
+{
+    return linear(8, true, x, packed, nbytes, y, M, K, N, G, ws, ws_bytes, stream);
+}
+
+int tf_dequant_w4_f32(const void *packed, size_t nbytes, float *w, int64_t K, int64_t N, int64_t G, void *stream)
+{
+    return dequant(4, packed, nbytes, w, K, N, G, stream);
+}
+
+int tf_dequant_w8_f32(const void *packed, size_t nbytes, float *w, int64_t K, int64_t N, int64_t G, void *stream)
+{
+    return dequant(8, packed, nbytes, w, K, N, G, stream);
+}
+
+} // extern "C"

@@ -1,0 +1,363 @@
+// Token-generation GEMV, M = 1..16 (TileFuse summary, Methodology section 3:
+// batch-1 GEMV, memory-bound at full precision; spread the weight stream over
+// the whole machine instead of a slice of it).
+//
+// MI355X design.  One workgroup owns one 16-column block of the packed buffer
+// -- a single contiguous byte range -- and its waves split K between them, so
+// partial sums combine in LDS and no cross-workgroup reduction, workspace,
+// atomic or device-wide fence is needed.  The waves per workgroup are chosen
+// so the grid holds about 16 waves per CU (up to 16 per workgroup for narrow
+// layers).  The chunk of activations and metadata a workgroup needs is staged
+// in LDS; a wave then streams its k-tiles with one 16-byte non-temporal load
+// per lane per 128 rows (W8: two), a fixed number of k-tiles ahead.
+//
+// Unpack happens in registers: for W4 a single and/or per pair of codes turns
+// nibbles into the bf16 values 128 + q (exact), which feed a 16x16x32 bf16
+// MFMA as the B operand with the activations as A (rows >= M are zero).  The
+// zero point goes through the same MFMA: a B operand holding bf16(128 + z) in
+// every row gives sum_k x * (128 + z).  At each group end the group's scale is
+// folded in once per (group, column):
+//     y += s * (sum_k x * (128 + q)  -  sum_k x * (128 + z))
+// which is sum_k x * (q - z) * s rearranged.  Both sums see the same
+// activations in the same order, so where q == z they are bitwise equal and
+// the contribution is exactly zero.  W8 uses bf16(q) and bf16(z) (exact).  No
+// bf16 weight is formed, none is written anywhere.  The waves of a workgroup
+// combine in a fixed order, so results are deterministic.
+#include "tf_common.h"
+#include "tf_launch.h"
+
+namespace tf {
+
+constexpr int kGemvMaxWaves = 16;
+constexpr int kGemvTargetWaves = 4096; // about 16 per CU
+
+// Eight W4 codes (one column, rows 0..7 of an octet) -> B operand of bf16
+// values 128 + q: OR-ing a nibble into the mantissa of bf16 128.0 (0x4300).
+// `magic` is 0x43004300 held in a vector register, so each pair costs one
+// v_and_or_b32 (the mask comes from a scalar register).
+__device__ __forceinline__ u32x4 w4_operand(uint32_t w, uint32_t magic)
+{
+    u32x4 b;
+    b[0] = (w & 0x000F000Fu) | magic;
+    b[1] = ((w >> 4) & 0x000F000Fu) | magic;
+    b[2] = ((w >> 8) & 0x000F000Fu) | magic;
+    b[3] = ((w >> 12) & 0x000F000Fu) | magic;
+    return b;
+}
+
+__device__ __forceinline__ uint32_t magic_in_vgpr()
+{
+    uint32_t m;
+    asm volatile("v_mov_b32 %0, 0x43004300" : "=v"(m));
+    return m;
+}
+
+// Eight W8 codes (bytes of w0, w1) -> B operand of the bf16 values q (exact).
+__device__ __forceinline__ u32x4 w8_operand(uint32_t w0, uint32_t w1)
+{
+    u32x4 b;
+    b[0] = pack_bf16x2((float)(w0 & 0xFFu), (float)((w0 >> 8) & 0xFFu));
+    b[1] = pack_bf16x2((float)((w0 >> 16) & 0xFFu), (float)(w0 >> 24));
+    b[2] = pack_bf16x2((float)(w1 & 0xFFu), (float)((w1 >> 8) & 0xFFu));
+    b[3] = pack_bf16x2((float)((w1 >> 16) & 0xFFu), (float)(w1 >> 24));
+    return b;
+}
+
+// B operand whose eight rows all hold the zero point, in the same form as the
+// code operand: bf16(128 + z) for W4, bf16(z) for W8.
+template <int BITS> __device__ __forceinline__ u32x4 zero_operand(uint32_t z)
+{
+    uint32_t v;
+    if constexpr (BITS == 4) {
+        const uint32_t h = 0x4300u | z;
+        v = h | (h << 16);
+    } else {
+        v = pack_bf16x2((float)z, (float)z);
+    }
+    return u32x4{v, v, v, v};
+}
+
+// The codes of one k-tile held by one lane: W4 16 bytes, W8 32 bytes.
+template <int BITS> struct TileCodes {
+    u32x4 w[BITS == 4 ? 1 : 2];
+};
+
+template <int BITS> __device__ __forceinline__ u32x4 code_operand(const TileCodes<BITS> &c, int u, uint32_t magic)
+{
+    if constexpr (BITS == 4)
+        return w4_operand(c.w[0][u], magic);
+    else
+        return w8_operand(c.w[u >> 1][2 * (u & 1)], c.w[u >> 1][2 * (u & 1) + 1]);
+}
+
+template <int BITS>
+__device__ __forceinline__ void load_codes(TileCodes<BITS> &c, const uint8_t *tile_lane)
+{
+    c.w[0] = load16_stream(tile_lane);
+    if constexpr (BITS == 8)
+        c.w[1] = load16_stream(tile_lane + 1024);
+}
+
+__device__ __forceinline__ void fold(f32x4 &yacc, f32x4 &gacc, f32x4 &zacc, float s)
+{
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        yacc[i] = fmaf(s, gacc[i] - zacc[i], yacc[i]);
+    gacc = zacc = f32x4{0.f, 0.f, 0.f, 0.f};
+}
+
+// Launch-time geometry of the K chunks staged in LDS.
+struct GemvChunks {
+    int tiles;    // k-tiles per chunk
+    int xpitch;   // bf16 elements per staged activation row (chunk rows + 8)
+    int meta_cap; // bytes reserved for the chunk's metadata records
+    int lds;      // dynamic LDS bytes per workgroup
+};
+
+// How the k-tiles of a block map onto metadata groups.
+enum GroupMode {
+    kSplitTiles = 0, // G in {32, 64}: a k-tile holds several groups
+    kMultiTile = 1,  // a group spans several k-tiles (G a multiple of 256, or G == K)
+    kOneTile = 2     // every k-tile is exactly one group (G == 128, or G == K <= 128)
+};
+
+// A chunk of K is staged per workgroup: activations x[0:M][chunk] (zero past
+// K) and the metadata records of the groups the chunk touches.  The only
+// vector-memory loads in the main loop are then the code stream, issued in
+// the order it is consumed, a fixed D k-tiles ahead; vector-memory counters
+// retire in order, so waiting for tile t never waits for anything issued
+// after it.  Each ring slot is unpacked into MFMA operands before it is
+// refilled, so the slot keeps its registers and no wait drains the ring.
+template <int BITS, int kMode, int D>
+__global__ __launch_bounds__(1024) void gemv_kernel(const uint16_t *__restrict__ x, const uint8_t *__restrict__ packed,
+                                                    uint16_t *__restrict__ y, Layout lay, int M, GemvChunks ch)
+{
+    // D: k-tiles of codes in flight per wave
+    constexpr uint32_t TB = tile_bytes(BITS), RB = record_bytes(BITS);
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    uint8_t *smeta = smem;
+    uint16_t *sx = reinterpret_cast<uint16_t *>(smem + ch.meta_cap);
+    float *red = reinterpret_cast<float *>(smem); // reused after the last chunk
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int W = blockDim.x >> 6;
+    const int r = lane & 15, o = lane >> 4;
+    const int64_t blk = blockIdx.x;
+    const uint8_t *meta = packed + blk * lay.block_bytes;
+    const uint8_t *tiles = meta + lay.meta_bytes + 16 * lane;
+    // MFMA rows >= M are never stored, so their lanes read row 0 instead of
+    // being masked off.
+    const int xr = r < M ? r : 0;
+    const uint32_t magic = magic_in_vgpr();
+    const int ktiles = (int)lay.ktiles;
+    const f32x4 zf = {0.f, 0.f, 0.f, 0.f};
+
+    f32x4 yacc = zf, gacc = zf, zacc = zf;
+    TileCodes<BITS> ring[D];
+
+    for (int c0 = 0; c0 < ktiles; c0 += ch.tiles) {
+        const int c1 = c0 + ch.tiles < ktiles ? c0 + ch.tiles : ktiles;
+        const int nct = c1 - c0;
+        const int a = c0 + nct * wave / W, b = c0 + nct * (wave + 1) / W; // this wave's k-tiles
+        const int n = b - a;
+        // codes first: their latency overlaps the staging below.  Ring loads
+        // past the wave's range re-read its last tile (in bounds, never used).
+        if (n > 0) {
+#pragma unroll
+            for (int j = 0; j < D; ++j)
+                load_codes<BITS>(ring[j], tiles + (uint32_t)(a + (j < n ? j : n - 1)) * TB);
+        }
+
+        if (c0 > 0)
+            __syncthreads(); // the previous chunk's LDS is no longer read
+        // ---- stage activations x[m][k0 .. k0 + 128 nct), zero past K ----
+        const int64_t k0 = (int64_t)c0 * kTileRows;
+        const int units_per_row = nct * (kTileRows / 8);
+        for (int e = tid; e < M * units_per_row; e += blockDim.x) {
+            const int m = e / units_per_row, u8 = e - m * units_per_row;
+            const int64_t k = k0 + 8 * u8;
+            u32x4 v = {0u, 0u, 0u, 0u};
+            if (k < lay.K)
+                v = load16(x + (int64_t)m * lay.K + k);
+            *reinterpret_cast<u32x4 *>(sx + m * ch.xpitch + 8 * u8) = v;
+        }
+        // ---- stage the metadata records of groups g0 .. g1 ----
+        const int64_t k1 = (int64_t)c1 * kTileRows < lay.K ? (int64_t)c1 * kTileRows : lay.K;
+        const int64_t g0 = k0 / lay.G, g1 = (k1 - 1) / lay.G;
+        const int rec_words = (int)((g1 - g0 + 1) * RB / 8);
+        for (int e = tid; e < rec_words; e += blockDim.x)
+            *reinterpret_cast<u32x2 *>(smeta + 8 * e) = *reinterpret_cast<const u32x2 *>(meta + g0 * RB + 8 * e);
+        __syncthreads();
+        if (n <= 0)
+            continue;
+
+        const uint16_t *xl = sx + xr * ch.xpitch + 8 * o - c0 * kTileRows;
+        // kMultiTile: tiles left in the current group and the group's record
+        const int tpg = kMode == kMultiTile ? (int)lay.tiles_per_group : 1;
+        const int ga = a / tpg;
+        int tg_left = tpg - (a - ga * tpg);
+        const uint8_t *rec = smeta + (ga - (int)g0) * RB;
+        const int sh = lay.G == kStepRows ? 0 : 1; // kSplitTiles: G is 32 or 64
+
+        for (int i = 0; i < n; i += D) {
+#pragma unroll
+            for (int j = 0; j < D; ++j) {
+                const int ti = i + j;
+                const int t = a + ti;
+                // consume the slot, then refill it with the tile D ahead
+                u32x4 ops[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    ops[u] = code_operand<BITS>(ring[j], u, magic);
+                load_codes<BITS>(ring[j], tiles + (uint32_t)(ti + D < n ? t + D : b - 1) * TB);
+                if (ti < n) {
+                    u32x4 xa[4];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u)
+                        xa[u] = *reinterpret_cast<const u32x4 *>(xl + t * kTileRows + kStepRows * u);
+                    if constexpr (kMode == kOneTile) {
+                        const uint8_t *rg = smeta + (t - (int)g0) * RB;
+                        const u32x4 zop = zero_operand<BITS>(record_zero<BITS>(rg, r));
+                        f32x4 ga4 = mfma16x16x32(xa[0], ops[0], zf);
+                        f32x4 za4 = mfma16x16x32(xa[0], zop, zf);
+#pragma unroll
+                        for (int u = 1; u < 4; ++u) {
+                            ga4 = mfma16x16x32(xa[u], ops[u], ga4);
+                            za4 = mfma16x16x32(xa[u], zop, za4);
+                        }
+                        const float sc = record_scale<BITS>(rg, r);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            yacc[e] = fmaf(sc, ga4[e] - za4[e], yacc[e]);
+                    } else if constexpr (kMode == kMultiTile) {
+                        const u32x4 zop = zero_operand<BITS>(record_zero<BITS>(rec, r));
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) {
+                            gacc = mfma16x16x32(xa[u], ops[u], gacc);
+                            zacc = mfma16x16x32(xa[u], zop, zacc);
+                        }
+                        --tg_left;
+                        if (tg_left == 0 || ti + 1 == n)
+                            fold(yacc, gacc, zacc, record_scale<BITS>(rec, r));
+                        if (tg_left == 0) {
+                            tg_left = tpg;
+                            rec += RB;
+                        }
+                    } else {
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) {
+                            const int64_t st = 4 * (int64_t)t + u;
+                            if (st < lay.steps) {
+                                const uint8_t *rg = smeta + ((st >> sh) - g0) * RB;
+                                const f32x4 ga4 = mfma16x16x32(xa[u], ops[u], zf);
+                                const f32x4 za4 =
+                                    mfma16x16x32(xa[u], zero_operand<BITS>(record_zero<BITS>(rg, r)), zf);
+                                gacc += ga4;
+                                zacc += za4;
+                                if (((st + 1) & ((1 << sh) - 1)) == 0)
+                                    fold(yacc, gacc, zacc, record_scale<BITS>(rg, r));
+                            }
+                        }
+                    }
+                }
+            }
+        }
+    }
+
+    // ---- combine the waves (C layout: lane holds rows 4o + i of column r) ----
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        red[(wave * 16 + 4 * o + e) * kBlockCols + r] = yacc[e];
+    __syncthreads();
+    for (int e = tid; e < M * kBlockCols; e += blockDim.x) {
+        const int row = e >> 4, col = e & 15;
+        float v = 0.f;
+        for (int w = 0; w < W; ++w)
+            v += red[(w * 16 + row) * kBlockCols + col];
+        const int64_t nn = blk * kBlockCols + col;
+        if (nn < lay.N)
+            y[(int64_t)row * lay.N + nn] = f32_to_bf16_bits(v);
+    }
+}
+
+int gemv_waves(const Layout &lay)
+{
+    int64_t w = (kGemvTargetWaves + lay.nblocks - 1) / lay.nblocks;
+    if (w > kGemvMaxWaves)
+        w = kGemvMaxWaves;
+    if (w > lay.ktiles)
+        w = lay.ktiles;
+    return w < 1 ? 1 : (int)w;
+}
+
+// Chunk size: as many k-tiles as fit the LDS share of one workgroup when
+// 16 / W workgroups run per CU (at most 64 KiB).
+static GemvChunks plan_chunks(int bits, const Layout &lay, int64_t M, int W)
+{
+    const int RB = record_bytes(bits);
+    int wgs = kGemvMaxWaves / W;
+    wgs = wgs < 1 ? 1 : wgs;
+    int64_t budget = (160 * 1024) / wgs - 512;
+    if (budget > 64 * 1024)
+        budget = 64 * 1024;
+    const int64_t recs_per_tile = lay.whole_tiles() ? 1 : lay.groups_per_tile;
+    const int64_t per_tile = M * kTileRows * 2 + recs_per_tile * RB;
+    int64_t tiles = (budget - 2 * RB - 16 * M) / per_tile;
+    if (tiles > lay.ktiles)
+        tiles = lay.ktiles;
+    if (tiles < 1)
+        tiles = 1;
+    GemvChunks c;
+    c.tiles = (int)tiles;
+    c.xpitch = (int)(tiles * kTileRows + 8);
+    // records of a chunk: groups g0..g1 of its rows, at most tiles * recs_per_tile + 1
+    c.meta_cap = (int)(((tiles * recs_per_tile + 1) * RB + 15) / 16 * 16);
+    int64_t lds = c.meta_cap + M * c.xpitch * 2;
+    const int64_t red = (int64_t)W * 16 * kBlockCols * 4;
+    c.lds = (int)(lds > red ? lds : red);
+    return c;
+}
+
+template <int BITS, int D>
+static void launch_gemv_depth(const Layout &lay, dim3 grid, dim3 block, const GemvChunks &ch, hipStream_t stream,
+                              const uint16_t *x, const uint8_t *pk, uint16_t *y, int M)
+{
+    if (lay.tiles_per_group == 1)
+        gemv_kernel<BITS, kOneTile, D><<<grid, block, ch.lds, stream>>>(x, pk, y, lay, M, ch);
+    else if (lay.whole_tiles())
+        gemv_kernel<BITS, kMultiTile, D><<<grid, block, ch.lds, stream>>>(x, pk, y, lay, M, ch);
+    else
+        gemv_kernel<BITS, kSplitTiles, D><<<grid, block, ch.lds, stream>>>(x, pk, y, lay, M, ch);
+}
+
+// Prefetch depth: measured on MI355X, two k-tiles in flight per wave suit
+// short per-wave ranges (at most 3 tiles), four the longer ones; deeper rings
+// only add redundant loads and registers.
+template <int BITS>
+static void launch_gemv_bits(const Layout &lay, dim3 grid, dim3 block, const GemvChunks &ch, hipStream_t stream,
+                             const uint16_t *x, const uint8_t *pk, uint16_t *y, int M)
+{
+    const int64_t per_wave = lay.ktiles / (block.x / 64);
+    if (per_wave <= 3)
+        launch_gemv_depth<BITS, 2>(lay, grid, block, ch, stream, x, pk, y, M);
+    else
+        launch_gemv_depth<BITS, 4>(lay, grid, block, ch, stream, x, pk, y, M);
+}
+
+hipError_t launch_gemv(int bits, const uint16_t *x, const void *packed, uint16_t *y, int64_t M, const Layout &lay,
+                       hipStream_t stream)
+{
+    const int W = gemv_waves(lay);
+    const GemvChunks ch = plan_chunks(bits, lay, M, W);
+    const dim3 grid((unsigned)lay.nblocks), block(64 * W);
+    const uint8_t *pk = static_cast<const uint8_t *>(packed);
+    if (bits == 4)
+        launch_gemv_bits<4>(lay, grid, block, ch, stream, x, pk, y, (int)M);
+    else
+        launch_gemv_bits<8>(lay, grid, block, ch, stream, x, pk, y, (int)M);
+    return hipGetLastError();
+}
+
+} // namespace tf

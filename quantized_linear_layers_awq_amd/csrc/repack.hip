@@ -1,0 +1,196 @@
+// Offline interleaved pre-tiling (TileFuse summary, Methodology section 2) and
+// the fp32 dequantization test hook.
+//
+// Repack is a copy-class gather: every thread writes one 16-byte unit of the
+// packed layout (or one metadata record), so stores are coalesced and every
+// byte of the layout, padding included, is written exactly once.  The
+// checkpoint reads are gathers the caches absorb; this runs once per weight.
+#include "tf_common.h"
+#include "tf_launch.h"
+
+namespace tf {
+
+// ---------------------------------------------------------------------------
+// Codes.  W4: 64 units of 16 bytes per k-tile (lane L = 16o + r: word u holds
+// rows 32u + 8o .. +7 of column r).  W8: 128 units (half h = u / 2 at 1024h).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void repack_w4_codes(const uint32_t *__restrict__ qweight, Layout lay,
+                                                       uint8_t *__restrict__ packed, int64_t units)
+{
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= units)
+        return;
+    const int L = (int)(idx & 63);
+    const int64_t bt = idx >> 6; // blk * ktiles + t
+    const int64_t blk = bt / lay.ktiles, t = bt - blk * lay.ktiles;
+    const int o = L >> 4, r = L & 15;
+    const int64_t n = blk * kBlockCols + r;
+    const int64_t words_per_row = lay.N / 8;
+    u32x4 out = {0u, 0u, 0u, 0u};
+    if (n < lay.N) {
+        const uint32_t sh = awq_nibble_shift((int)(n & 7));
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            uint32_t wd = 0;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int64_t k = t * kTileRows + kStepRows * u + 8 * o + i;
+                if (k < lay.K)
+                    wd |= ((qweight[k * words_per_row + (n >> 3)] >> sh) & 0xFu) << w4_row_shift(i);
+            }
+            out[u] = wd;
+        }
+    }
+    *reinterpret_cast<u32x4 *>(packed + lay.tile(4, blk, t) + 16 * L) = out;
+}
+
+__global__ __launch_bounds__(256) void repack_w8_codes(const uint8_t *__restrict__ qweight, Layout lay,
+                                                       uint8_t *__restrict__ packed, int64_t units)
+{
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= units)
+        return;
+    const int L = (int)(idx & 63);
+    const int h = (int)((idx >> 6) & 1);
+    const int64_t bt = idx >> 7;
+    const int64_t blk = bt / lay.ktiles, t = bt - blk * lay.ktiles;
+    const int o = L >> 4, r = L & 15;
+    const int64_t n = blk * kBlockCols + r;
+    u32x4 out = {0u, 0u, 0u, 0u};
+    if (n < lay.N) {
+#pragma unroll
+        for (int uu = 0; uu < 2; ++uu) {
+            const int u = 2 * h + uu;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int64_t k = t * kTileRows + kStepRows * u + 8 * o + i;
+                if (k < lay.K)
+                    out[2 * uu + (i >> 2)] |= (uint32_t)qweight[k * lay.N + n] << (8 * (i & 3));
+            }
+        }
+    }
+    *reinterpret_cast<u32x4 *>(packed + lay.tile(8, blk, t) + 1024 * h + 16 * L) = out;
+}
+
+// ---------------------------------------------------------------------------
+// Metadata: one thread per (block, group) writes the whole record (16 scales,
+// 16 zero points); the thread of a block's last group also zeroes the
+// record region's padding.
+// ---------------------------------------------------------------------------
+template <int BITS>
+__global__ __launch_bounds__(256) void repack_records(const void *__restrict__ qzeros,
+                                                      const uint16_t *__restrict__ scales, Layout lay,
+                                                      uint8_t *__restrict__ packed, int64_t units)
+{
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= units)
+        return;
+    const int64_t blk = idx / lay.ngroups, g = idx - blk * lay.ngroups;
+    uint32_t sc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    uint32_t zz[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (int c = 0; c < kBlockCols; ++c) {
+        const int64_t n = blk * kBlockCols + c;
+        if (n >= lay.N)
+            continue;
+        sc[c >> 1] |= (uint32_t)scales[g * lay.N + n] << (16 * (c & 1));
+        if constexpr (BITS == 4) {
+            const uint32_t *qz = static_cast<const uint32_t *>(qzeros);
+            const uint32_t z = (qz[g * (lay.N / 8) + (n >> 3)] >> awq_nibble_shift((int)(n & 7))) & 0xFu;
+            zz[c >> 3] |= z << (4 * (c & 7));
+        } else {
+            const uint32_t z = static_cast<const uint8_t *>(qzeros)[g * lay.N + n];
+            zz[c >> 2] |= z << (8 * (c & 3));
+        }
+    }
+    uint8_t *rec = packed + lay.record(BITS, blk, g);
+    // records start 8-byte aligned (W4, 40 bytes) or 16-byte aligned (W8, 48)
+    u32x2 *p2 = reinterpret_cast<u32x2 *>(rec);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        p2[i] = u32x2{sc[2 * i], sc[2 * i + 1]};
+    p2[4] = u32x2{zz[0], zz[1]};
+    if constexpr (BITS == 8)
+        p2[5] = u32x2{zz[2], zz[3]};
+    if (g == lay.ngroups - 1) {
+        uint8_t *end = rec + record_bytes(BITS);
+        uint8_t *meta_end = packed + blk * lay.block_bytes + lay.meta_bytes;
+        for (; end < meta_end; end += 8)
+            *reinterpret_cast<u32x2 *>(end) = u32x2{0u, 0u};
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Dequantization test hook: w[k][n] = (q - z) * s in fp32, through the same
+// unpack + dequant helpers the GEMM stages its tiles with.
+// ---------------------------------------------------------------------------
+template <int BITS>
+__global__ __launch_bounds__(256) void dequant_f32(const uint8_t *__restrict__ packed, Layout lay,
+                                                   float *__restrict__ w, int64_t units)
+{
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= units)
+        return;
+    constexpr int kUnitsPerTile = BITS == 4 ? 64 : 128;
+    const int L = (int)(idx & 63);
+    const int h = BITS == 4 ? 0 : (int)((idx >> 6) & 1);
+    const int64_t bt = idx / kUnitsPerTile;
+    const int64_t blk = bt / lay.ktiles, t = bt - blk * lay.ktiles;
+    const int o = L >> 4, r = L & 15;
+    const int64_t n = blk * kBlockCols + r;
+    if (n >= lay.N)
+        return;
+    const u32x4 cw = load16(packed + lay.tile(BITS, blk, t) + 1024 * h + 16 * L);
+    constexpr int kSteps = BITS == 4 ? 4 : 2;
+#pragma unroll
+    for (int uu = 0; uu < kSteps; ++uu) {
+        const int u = BITS == 4 ? uu : 2 * h + uu;
+        const int64_t k0 = t * kTileRows + kStepRows * u + 8 * o;
+        if (k0 >= lay.K)
+            continue;
+        const uint8_t *rec = packed + lay.record(BITS, blk, k0 / lay.G);
+        const float sv = record_scale<BITS>(rec, r);
+        const float zv = (float)record_zero<BITS>(rec, r);
+        float f[8];
+        if constexpr (BITS == 4)
+            dequant_w4_word(cw[u], sv, -zv * sv, f);
+        else
+            dequant_w8_pair(cw[2 * uu], cw[2 * uu + 1], sv, -zv * sv, f);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            w[(k0 + i) * lay.N + n] = f[i];
+    }
+}
+
+static inline unsigned grid_for(int64_t units) { return (unsigned)((units + 255) / 256); }
+
+hipError_t launch_repack(int bits, const void *qweight, const void *qzeros, const uint16_t *scales,
+                         const Layout &lay, void *packed, hipStream_t stream)
+{
+    uint8_t *out = static_cast<uint8_t *>(packed);
+    const int64_t code_units = lay.nblocks * lay.ktiles * (bits == 4 ? 64 : 128);
+    const int64_t rec_units = lay.nblocks * lay.ngroups;
+    if (bits == 4) {
+        repack_w4_codes<<<grid_for(code_units), 256, 0, stream>>>(static_cast<const uint32_t *>(qweight), lay, out,
+                                                                  code_units);
+        repack_records<4><<<grid_for(rec_units), 256, 0, stream>>>(qzeros, scales, lay, out, rec_units);
+    } else {
+        repack_w8_codes<<<grid_for(code_units), 256, 0, stream>>>(static_cast<const uint8_t *>(qweight), lay, out,
+                                                                  code_units);
+        repack_records<8><<<grid_for(rec_units), 256, 0, stream>>>(qzeros, scales, lay, out, rec_units);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_dequant_f32(int bits, const void *packed, const Layout &lay, float *w, hipStream_t stream)
+{
+    const uint8_t *in = static_cast<const uint8_t *>(packed);
+    const int64_t units = lay.nblocks * lay.ktiles * (bits == 4 ? 64 : 128);
+    if (bits == 4)
+        dequant_f32<4><<<grid_for(units), 256, 0, stream>>>(in, lay, w, units);
+    else
+        dequant_f32<8><<<grid_for(units), 256, 0, stream>>>(in, lay, w, units);
+    return hipGetLastError();
+}
+
+} // namespace tf

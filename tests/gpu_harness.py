@@ -1,0 +1,90 @@
+"""Helpers of the GPU parity tests: move a synth.Case to the device, run the
+HIP path through the binding, and compare with the oracle.
+
+Tolerance (fp32 accumulation, bf16 output):
+    |y - y_ref| <= 1e-2 * max(|y_ref|, rms(y_ref row))  for every element.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+
+
+def gpu_or_skip():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    import quantized_linear_layers_awq_amd as q
+
+    q.load_library()  # raises when the HIP library is missing: no silent fallback
+    return torch, q
+
+
+def to_device(case, torch, dev="cuda:0"):
+    qw = case.qweight.view(np.int32) if case.bits == 4 else case.qweight
+    qz = case.qzeros.view(np.int32) if case.bits == 4 else case.qzeros
+    return dict(
+        qweight=torch.from_numpy(np.ascontiguousarray(qw)).to(dev),
+        qzeros=torch.from_numpy(np.ascontiguousarray(qz)).to(dev),
+        scales=torch.from_numpy(case.scales.view(np.int16)).to(dev),
+        x=torch.from_numpy(case.x.view(np.int16)).to(dev).view(torch.bfloat16),
+    )
+
+
+def repack(case, d, q):
+    fn = q.tf_repack_w4 if case.bits == 4 else q.tf_repack_w8
+    return fn(d["qweight"], d["qzeros"], d["scales"], case.K, case.N, case.G)
+
+
+def linear_fn(q, bits, gemm):
+    return {(4, False): q.tf_gemv_w4a16, (8, False): q.tf_gemv_w8a16,
+            (4, True): q.tf_gemm_w4a16, (8, True): q.tf_gemm_w8a16}[(bits, gemm)]
+
+
+def bf16_to_f64(t):
+    """bf16 device tensor -> float64 numpy (exact)."""
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def bf16_bits(t):
+    """bf16 device tensor -> uint16 bit patterns (numpy)."""
+    import torch
+
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def within_tolerance(y, ref, rms=None):
+    """Elementwise bound; returns (ok, worst ratio of error to its bound)."""
+    if rms is None:
+        rms = np.sqrt(np.mean(ref**2, axis=1, keepdims=True))
+    bound = 1e-2 * np.maximum(np.abs(ref), rms)
+    err = np.abs(y - ref)
+    ratio = float(np.max(err / np.where(bound > 0, bound, np.inf))) if err.size else 0.0
+    ok = bool(np.all(err <= bound))
+    return ok, ratio
+
+
+def sample_indices(n, count, seed):
+    if n <= count:
+        return np.arange(n)
+    rng = np.random.default_rng(seed)
+    idx = np.sort(rng.choice(n, size=count, replace=False))
+    # always include both ends (first tile, ragged last tile)
+    return np.unique(np.concatenate([[0, n - 1], idx]))
+
+
+def check_linear(case, torch, q, gemm, rows=None, cols=None, packed=None, d=None):
+    """Run the HIP path on the whole case, compare the chosen rows/columns."""
+    d = d or to_device(case, torch)
+    packed = packed if packed is not None else repack(case, d, q)
+    y = linear_fn(q, case.bits, gemm)(d["x"], packed, case.K, case.N, case.G)
+    torch.cuda.synchronize()
+    yh = bf16_to_f64(y)
+    ref = oracle.awq_linear(case, cols=cols, rows=rows)
+    sub = yh if rows is None else yh[np.asarray(rows)]
+    sub = sub if cols is None else sub[:, np.asarray(cols)]
+    ok, ratio = within_tolerance(sub, ref)
+    return ok, ratio, y

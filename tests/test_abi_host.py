@@ -1,0 +1,161 @@
+"""Host-only checks of the C-ABI library: it loads, exports every symbol the
+header declares, agrees with the oracle on buffer sizes, and rejects bad
+arguments before any HIP call.
+
+The validation cases pass fake device addresses, so they only run where no
+GPU is visible: a validation bug there surfaces as TF_ERR_HIP (no device),
+never as a launch on a real device.
+"""
+
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = os.path.join(ROOT, "quantized_linear_layers_awq_amd", "libtilefuse.so")
+
+TF_OK, TF_ERR_NULL, TF_ERR_SHAPE, TF_ERR_GROUP, TF_ERR_ALIGN, TF_ERR_BUFFER_TOO_SMALL = 0, 1, 2, 3, 4, 5
+
+
+def _declared_symbols():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(tf_\w+)\s*\(", text))
+    return sorted(names)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail("libtilefuse.so is not built (run __graft_entry__.build())")
+    from quantized_linear_layers_awq_amd import load_library
+
+    return load_library()
+
+
+def _no_gpu():
+    try:
+        import torch
+
+        return not torch.cuda.is_available()
+    except Exception:
+        return True
+
+
+def test_header_declares_the_boundary():
+    names = _declared_symbols()
+    for n in ("tf_repack_w4", "tf_repack_w8", "tf_gemv_w4a16", "tf_gemv_w8a16", "tf_gemm_w4a16", "tf_gemm_w8a16"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    raw = ctypes.CDLL(LIB)
+    missing = [n for n in _declared_symbols() if not hasattr(raw, n)]
+    assert not missing, missing
+
+
+def test_binding_names_match_header(lib):
+    import quantized_linear_layers_awq_amd as q
+
+    for n in _declared_symbols():
+        assert hasattr(q, n), f"binding lacks {n}"
+
+
+def test_status_strings(lib):
+    assert lib.tf_status_string(0) == b"TF_OK"
+    assert lib.tf_status_string(3).startswith(b"TF_ERR_GROUP")
+    assert lib.tf_format_version() == 2
+
+
+@pytest.mark.parametrize("bits,K,N,G", [
+    (4, 4096, 4096, 128), (4, 14336, 4096, 128), (4, 28672, 8192, 128), (4, 64, 72, 32),
+    (8, 8192, 8192, 8192), (8, 96, 100, 32), (4, 384, 64, 384), (4, 160, 24, 160), (8, 1024, 40, 256),
+])
+def test_packed_bytes_match_oracle(lib, bits, K, N, G):
+    fn = lib.tf_packed_bytes_w4 if bits == 4 else lib.tf_packed_bytes_w8
+    assert fn(K, N, G) == oracle.packed_bytes(bits, K, N, G) > 0
+
+
+@pytest.mark.parametrize("K,N,G", [(100, 64, 100), (64, 12, 32), (64, 64, 48), (0, 64, 32), (64, 0, 32),
+                                   (64, 64, 0), (64, 64, 128), (2**31, 64, 32), (384, 64, 96)])
+def test_packed_bytes_invalid_shapes_are_zero(lib, K, N, G):
+    assert lib.tf_packed_bytes_w4(K, N, G) == 0
+
+
+@pytest.mark.parametrize("M,K,N,G", [(1, 4096, 4096, 128), (8, 14336, 4096, 128), (16, 4096, 1024, 128),
+                                     (1, 8192, 8192, 8192), (512, 8192, 8192, 8192), (2048, 4096, 14336, 128)])
+def test_workspace_cannot_hold_bf16_weights(lib, M, K, N, G):
+    # The layer never materialises full-precision weights: the only scratch it
+    # takes is far smaller than a bf16 copy of W.
+    for bits in (4, 8):
+        for gemm in (0, 1):
+            if not gemm and M > 16:
+                continue
+            assert lib.tf_workspace_bytes(bits, gemm, M, K, N, G) < K * N * 2 // 8
+
+
+def test_no_kernel_needs_a_workspace(lib):
+    for args in [(4, 0, 1, 4096, 4096, 128), (8, 1, 512, 8192, 8192, 8192), (5, 0, 1, 4096, 4096, 128)]:
+        assert lib.tf_workspace_bytes(*args) == 0
+
+
+FAKE = 0x10000  # a 64 KiB-aligned fake device address; never dereferenced
+
+
+@pytest.mark.skipif(not _no_gpu(), reason="fake-pointer validation cases run only where no GPU is visible")
+class TestValidation:
+    def _gemv(self, lib, M=1, K=256, N=128, G=128, x=FAKE, packed=FAKE, y=FAKE, nbytes=None, ws=FAKE,
+              ws_bytes=1 << 30, fn="tf_gemv_w4a16"):
+        if nbytes is None:
+            nbytes = 1 << 30
+        return getattr(lib, fn)(x, packed, nbytes, y, M, K, N, G, ws, ws_bytes, None)
+
+    def test_shape_errors(self, lib):
+        assert self._gemv(lib, K=33) == TF_ERR_SHAPE
+        assert self._gemv(lib, N=12) == TF_ERR_SHAPE
+        assert self._gemv(lib, M=17) == TF_ERR_SHAPE
+        assert self._gemv(lib, M=-1) == TF_ERR_SHAPE
+        assert self._gemv(lib, K=0) == TF_ERR_SHAPE
+        assert self._gemv(lib, M=2**30 + 1, fn="tf_gemm_w4a16") == TF_ERR_SHAPE
+
+    def test_group_errors(self, lib):
+        assert self._gemv(lib, G=48) == TF_ERR_GROUP
+        assert self._gemv(lib, G=512) == TF_ERR_GROUP
+        assert self._gemv(lib, G=0) == TF_ERR_GROUP
+        assert self._gemv(lib, K=384, G=96) == TF_ERR_GROUP   # neither divides 128 nor a multiple of it
+
+    def test_null_and_alignment(self, lib):
+        assert self._gemv(lib, x=None) == TF_ERR_NULL
+        assert self._gemv(lib, y=None) == TF_ERR_NULL
+        assert self._gemv(lib, packed=None) == TF_ERR_NULL
+        assert self._gemv(lib, x=FAKE + 2) == TF_ERR_ALIGN
+        assert self._gemv(lib, packed=FAKE + 8) == TF_ERR_ALIGN
+        assert self._gemv(lib, y=FAKE + 1) == TF_ERR_ALIGN
+
+    def test_buffer_sizes(self, lib):
+        need = lib.tf_packed_bytes_w4(256, 128, 128)
+        assert self._gemv(lib, nbytes=need - 1) == TF_ERR_BUFFER_TOO_SMALL
+        need8 = lib.tf_packed_bytes_w8(256, 100, 256)
+        assert self._gemv(lib, N=100, G=256, nbytes=need8 - 1, fn="tf_gemm_w8a16") == TF_ERR_BUFFER_TOO_SMALL
+
+    def test_empty_problem_is_ok_without_launch(self, lib):
+        assert self._gemv(lib, M=0, x=None, y=None, packed=None) == TF_OK
+        assert self._gemv(lib, M=0, x=None, y=None, packed=None, fn="tf_gemm_w8a16") == TF_OK
+
+    def test_repack_validation(self, lib):
+        f = lib.tf_repack_w4
+        assert f(FAKE, FAKE, FAKE, 256, 128, 128, FAKE, 10, None) == TF_ERR_BUFFER_TOO_SMALL
+        assert f(FAKE, None, FAKE, 256, 128, 128, FAKE, 1 << 30, None) == TF_ERR_NULL
+        assert f(FAKE, FAKE, FAKE + 1, 256, 128, 128, FAKE, 1 << 30, None) == TF_ERR_ALIGN
+        assert f(FAKE, FAKE, FAKE, 256, 128, 96, FAKE, 1 << 30, None) == TF_ERR_GROUP
+        assert lib.tf_repack_w8(FAKE, FAKE, FAKE, 256, 3, 33, FAKE, 1 << 30, None) == TF_ERR_GROUP
+
+    def test_dequant_validation(self, lib):
+        assert lib.tf_dequant_w4_f32(FAKE, 1, FAKE, 256, 128, 128, None) == TF_ERR_BUFFER_TOO_SMALL
+        assert lib.tf_dequant_w8_f32(FAKE, 1 << 30, FAKE + 2, 256, 128, 128, None) == TF_ERR_ALIGN

@@ -1,0 +1,148 @@
+"""GEMV and GEMM parity on small and ragged shapes, special cases that fix the
+result exactly, determinism and output guard bands."""
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_harness import bf16_bits, bf16_to_f64, check_linear, gpu_or_skip, linear_fn, repack, to_device
+
+pytestmark = pytest.mark.gpu
+
+# (bits, M, K, N, G): single and split-K plans, 128-row aligned and not,
+# per-group and per-channel, ragged N (partial 64-column block), ragged K.
+GEMV_SHAPES = [
+    (4, 1, 128, 64, 128), (4, 3, 512, 200, 128), (4, 16, 1024, 136, 64), (4, 5, 4096, 72, 32),
+    (4, 2, 384, 64, 384), (4, 1, 96, 64, 96), (4, 8, 4096, 128, 128), (4, 1, 8192, 256, 128),
+    (8, 1, 256, 100, 256), (8, 8, 2048, 260, 2048), (8, 4, 512, 64, 64), (8, 12, 4096, 64, 128),
+]
+
+GEMM_SHAPES = [
+    (4, 1, 256, 64, 128), (4, 33, 512, 200, 128), (4, 130, 1024, 136, 64), (4, 257, 384, 128, 384),
+    (4, 64, 96, 64, 32), (4, 300, 2048, 320, 128), (8, 77, 512, 100, 512), (8, 128, 256, 256, 32),
+    (8, 200, 1024, 192, 128),
+]
+
+
+def _case(bits, M, K, N, G, seed):
+    return synth.make_inputs(bits, M, K, N, G, seed=(51, seed, bits, M, K, N, G))
+
+
+@pytest.mark.parametrize("shape", GEMV_SHAPES)
+def test_gemv_within_tolerance(shape):
+    torch, q = gpu_or_skip()
+    print(f"gemv {shape}", flush=True)
+    c = _case(*shape, seed=1)
+    ok, ratio, _ = check_linear(c, torch, q, gemm=False)
+    assert ok, f"worst error / bound = {ratio:.3f}"
+
+
+@pytest.mark.parametrize("shape", GEMM_SHAPES)
+def test_gemm_within_tolerance(shape):
+    torch, q = gpu_or_skip()
+    print(f"gemm {shape}", flush=True)
+    c = _case(*shape, seed=2)
+    ok, ratio, _ = check_linear(c, torch, q, gemm=True)
+    assert ok, f"worst error / bound = {ratio:.3f}"
+
+
+def _integer_case(bits, M, K, N, G, seed):
+    """s = 1, z = 8 (W4) or 128 (W8), x in {-2..2}: y is an exact integer."""
+    rng = np.random.default_rng(seed)
+    codes = rng.integers(0, 1 << bits, size=(K, N), dtype=np.uint8)
+    zval = 8 if bits == 4 else 128
+    zeros = np.full((K // G, N), zval, np.uint8)
+    scales = np.full((K // G, N), 0x3F80, np.uint16)
+    xi = rng.integers(-2, 3, size=(M, K))
+    c = synth.gen.pack_case(bits, codes, zeros, scales, synth.f32_to_bf16_bits(xi.astype(np.float32)), G)
+    exact = xi.astype(np.int64) @ (codes.astype(np.int64) - zval)
+    return c, exact
+
+
+@pytest.mark.parametrize("gemm", [False, True])
+@pytest.mark.parametrize("bits,M,K,N,G", [(4, 1, 1024, 128, 128), (4, 7, 2048, 200, 64), (8, 4, 1024, 72, 1024),
+                                          (4, 16, 14336, 64, 128), (8, 3, 512, 64, 32)])
+def test_integer_case_is_bit_exact(gemm, bits, M, K, N, G):
+    torch, q = gpu_or_skip()
+    print(f"integer gemm={gemm} W{bits} M={M} K={K} N={N} G={G}", flush=True)
+    c, exact = _integer_case(bits, M, K, N, G, seed=K + N)
+    d = to_device(c, torch)
+    y = linear_fn(q, bits, gemm)(d["x"], repack(c, d, q), K, N, G)
+    torch.cuda.synchronize()
+    # every partial sum is an integer below 2^24, so fp32 holds it exactly and
+    # the only rounding is the final one to bf16
+    assert np.abs(exact).max() < 2**24
+    assert np.array_equal(bf16_bits(y), oracle.f64_to_bf16(exact.astype(np.float64)))
+
+
+@pytest.mark.parametrize("gemm", [False, True])
+@pytest.mark.parametrize("bits", [4, 8])
+def test_q_equal_zero_point_gives_zero(gemm, bits):
+    torch, q = gpu_or_skip()
+    c0 = _case(bits, 5, 1024, 136, 128, seed=3)
+    codes = c0.zeros[np.arange(c0.K) // c0.G]
+    c = synth.gen.pack_case(bits, codes, c0.zeros, c0.scales, c0.x, c0.G)
+    d = to_device(c, torch)
+    y = linear_fn(q, bits, gemm)(d["x"], repack(c, d, q), c.K, c.N, c.G)
+    torch.cuda.synchronize()
+    assert np.all(bf16_to_f64(y) == 0.0)
+
+
+@pytest.mark.parametrize("gemm,M", [(False, 1), (False, 8), (True, 64)])
+def test_runs_are_bitwise_deterministic(gemm, M):
+    torch, q = gpu_or_skip()
+    c = _case(4, M, 4096, 1024, 128, seed=4)
+    d = to_device(c, torch)
+    p = repack(c, d, q)
+    fn = linear_fn(q, 4, gemm)
+    a = bf16_bits(fn(d["x"], p, c.K, c.N, c.G))
+    b = bf16_bits(fn(d["x"], p, c.K, c.N, c.G))
+    assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("gemm,M", [(False, 3), (True, 40)])
+def test_output_guard_bands_untouched(gemm, M):
+    torch, q = gpu_or_skip()
+    c = _case(4, M, 2048, 200, 128, seed=5)
+    d = to_device(c, torch)
+    p = repack(c, d, q)
+    pad = 4096
+    big = torch.full((M * c.N + 2 * pad,), -7.25, dtype=torch.bfloat16, device="cuda:0")
+    y = big[pad:pad + M * c.N].view(M, c.N)
+    linear_fn(q, 4, gemm)(d["x"], p, c.K, c.N, c.G, y=y)
+    torch.cuda.synchronize()
+    host = big.float().cpu().numpy()
+    assert np.all(host[:pad] == -7.25) and np.all(host[-pad:] == -7.25)
+    ref = oracle.awq_linear(c)
+    yh = host[pad:pad + M * c.N].reshape(M, c.N).astype(np.float64)
+    rms = np.sqrt(np.mean(ref**2, axis=1, keepdims=True))
+    assert np.all(np.abs(yh - ref) <= 1e-2 * np.maximum(np.abs(ref), rms))
+
+
+def test_empty_batch_is_a_no_op():
+    torch, q = gpu_or_skip()
+    c = _case(4, 1, 256, 64, 128, seed=6)
+    d = to_device(c, torch)
+    p = repack(c, d, q)
+    x0 = torch.empty((0, c.K), dtype=torch.bfloat16, device="cuda:0")
+    for gemm in (False, True):
+        y = linear_fn(q, 4, gemm)(x0, p, c.K, c.N, c.G)
+        assert tuple(y.shape) == (0, c.N)
+
+
+def test_errors_raise_before_launch():
+    torch, q = gpu_or_skip()
+    c = _case(4, 2, 256, 64, 128, seed=7)
+    d = to_device(c, torch)
+    p = repack(c, d, q)
+    with pytest.raises(q.TileFuseError) as e:
+        q.tf_gemv_w4a16(d["x"], p[:100], c.K, c.N, c.G)
+    assert e.value.name == "TF_ERR_BUFFER_TOO_SMALL"
+    with pytest.raises(q.TileFuseError) as e:
+        q.tf_gemm_w4a16(d["x"], p, c.K, c.N, 96)
+    assert e.value.name == "TF_ERR_GROUP"
+    x17 = torch.zeros((17, c.K), dtype=torch.bfloat16, device="cuda:0")
+    with pytest.raises(q.TileFuseError) as e:
+        q.tf_gemv_w4a16(x17, p, c.K, c.N, c.G)
+    assert e.value.name == "TF_ERR_SHAPE"

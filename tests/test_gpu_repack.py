@@ -1,0 +1,60 @@
+"""GPU repack and dequant hook against the oracle: bit-exact."""
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_harness import gpu_or_skip, repack, to_device
+
+pytestmark = pytest.mark.gpu
+
+SMALL = [
+    (4, 64, 128, 32), (4, 256, 200, 128), (4, 384, 64, 384), (4, 192, 8, 64), (4, 96, 136, 96),
+    (8, 64, 128, 32), (8, 256, 100, 256), (8, 128, 4, 64), (8, 96, 72, 32), (8, 512, 130, 128),
+]
+
+
+@pytest.mark.parametrize("bits,K,N,G", SMALL)
+def test_repack_matches_oracle_bytes(bits, K, N, G):
+    torch, q = gpu_or_skip()
+    print(f"repack W{bits} K={K} N={N} G={G}", flush=True)
+    c = synth.make_inputs(bits, 1, K, N, G, seed=(41, bits, K, N))
+    packed = repack(c, to_device(c, torch), q)
+    torch.cuda.synchronize()
+    got = packed.cpu().numpy()
+    want = oracle.repack(bits, c.qweight, c.qzeros, c.scales, K, N, G)
+    assert got.size == want.size
+    assert np.array_equal(got, want)
+    codes, zeros, scales = oracle.unrepack(bits, got, K, N, G)
+    assert np.array_equal(codes, c.codes) and np.array_equal(zeros, c.zeros) and np.array_equal(scales, c.scales)
+
+
+@pytest.mark.parametrize("config,shape_id", [(0, 0), (1, 1), (2, 0), (3, 1), (4, 1)])
+def test_repack_matches_oracle_bytes_full_size(config, shape_id):
+    torch, q = gpu_or_skip()
+    c = synth.make_case(config, shape_id, 1, keep_codes=False)
+    print(f"repack full {c.name}", flush=True)
+    packed = repack(c, to_device(c, torch), q)
+    torch.cuda.synchronize()
+    want = oracle.repack(c.bits, c.qweight, c.qzeros, c.scales, c.K, c.N, c.G)
+    assert np.array_equal(packed.cpu().numpy(), want)
+
+
+@pytest.mark.parametrize("bits,K,N,G", SMALL + [(4, 4096, 4096, 128), (8, 8192, 512, 8192)])
+def test_dequant_f32_bit_exact(bits, K, N, G):
+    torch, q = gpu_or_skip()
+    print(f"dequant W{bits} K={K} N={N} G={G}", flush=True)
+    c = synth.make_inputs(bits, 1, K, N, G, seed=(42, bits, K, N))
+    packed = repack(c, to_device(c, torch), q)
+    fn = q.tf_dequant_w4_f32 if bits == 4 else q.tf_dequant_w8_f32
+    w = fn(packed, K, N, G)
+    torch.cuda.synchronize()
+    want = oracle.dequant(bits, c.qweight, c.qzeros, c.scales, K, N, G)
+    assert np.array_equal(w.cpu().numpy().view(np.uint32), want.view(np.uint32))
+
+
+def test_packed_size_and_version_agree():
+    torch, q = gpu_or_skip()
+    assert q.tf_format_version() == 2
+    assert q.tf_packed_bytes_w4(4096, 4096, 128) == oracle.packed_bytes(4, 4096, 4096, 128)

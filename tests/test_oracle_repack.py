@@ -38,15 +38,16 @@ def test_layout_positions_hand_worked(entry):
 
 
 @pytest.mark.parametrize("bits,K,N,G", [
-    (4, 64, 128, 32), (4, 256, 200, 128), (4, 384, 64, 384), (4, 192, 8, 64),
-    (8, 64, 128, 32), (8, 256, 100, 256), (8, 128, 4, 64), (8, 96, 72, 32),
+    (4, 64, 128, 32), (4, 256, 200, 128), (4, 384, 64, 384), (4, 192, 8, 64), (4, 160, 24, 160),
+    (8, 64, 128, 32), (8, 256, 100, 256), (8, 128, 4, 64), (8, 96, 72, 32), (8, 512, 40, 256),
 ])
 def test_repack_roundtrip_and_size(bits, K, N, G):
     c = synth.make_inputs(bits, 1, K, N, G, seed=(31, K, N))
     buf = oracle.repack(bits, c.qweight, c.qzeros, c.scales, K, N, G)
-    nblk = -(-N // 64)
-    hdr, chunk = (160, 1024) if bits == 4 else (192, 2048)
-    assert buf.size == nblk * (K // G) * (hdr + (G // 32) * chunk)
+    nblk = -(-N // 16)
+    rec, tile = (40, 1024) if bits == 4 else (48, 2048)
+    meta = -(-(K // G) * rec // 16) * 16
+    assert buf.size == nblk * (meta + -(-K // 128) * tile)
     codes, zeros, scales = oracle.unrepack(bits, buf, K, N, G)
     assert np.array_equal(codes, c.codes)
     assert np.array_equal(zeros, c.zeros)
@@ -56,14 +57,14 @@ def test_repack_roundtrip_and_size(bits, K, N, G):
 
 
 def test_repack_padding_columns_are_zero():
-    # N = 72 leaves 56 padding columns in the second block; their codes,
-    # zeros and scales must be 0 so a consumer can read whole blocks.
-    bits, K, N, G = 4, 64, 72, 32
+    # N = 72 leaves 8 padding columns in the last 16-column block; their
+    # codes, zeros and scales must be 0 so a consumer can read whole blocks.
+    bits, K, N, G = 4, 96, 72, 32
     c = synth.make_inputs(bits, 1, K, N, G, seed=(32,))
-    full = synth.gen.pack_case(bits, np.pad(c.codes, ((0, 0), (0, 56))), np.pad(c.zeros, ((0, 0), (0, 56))),
-                               np.pad(c.scales, ((0, 0), (0, 56))), c.x, G)
+    full = synth.gen.pack_case(bits, np.pad(c.codes, ((0, 0), (0, 8))), np.pad(c.zeros, ((0, 0), (0, 8))),
+                               np.pad(c.scales, ((0, 0), (0, 8))), c.x, G)
     a = oracle.repack(bits, c.qweight, c.qzeros, c.scales, K, N, G)
-    b = oracle.repack(bits, full.qweight, full.qzeros, full.scales, K, 128, G)
+    b = oracle.repack(bits, full.qweight, full.qzeros, full.scales, K, 80, G)
     assert np.array_equal(a, b)
 
 
@@ -81,6 +82,7 @@ def test_repack_is_a_bijection_on_code_positions():
             seen.add((pos, nib))
 
 
-@pytest.mark.parametrize("bits,K,N,G", [(4, 100, 64, 100), (4, 64, 12, 32), (8, 64, 64, 48), (4, 0, 64, 32)])
+@pytest.mark.parametrize("bits,K,N,G", [(4, 100, 64, 100), (4, 64, 12, 32), (8, 64, 64, 48), (4, 0, 64, 32),
+                                       (4, 384, 64, 96), (8, 640, 64, 320)])
 def test_layout_rejects_invalid_shapes(bits, K, N, G):
     assert oracle.packed_bytes(bits, K, N, G) == 0
