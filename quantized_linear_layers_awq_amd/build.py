@@ -26,8 +26,11 @@ def hipcc() -> str:
 
 
 def compile_flags() -> list[str]:
+    # -amdgpu-mfma-vgpr-form: MFMA accumulators in arch VGPRs, so the GEMM's
+    # per-group rescale is one multiply per accumulator (no AGPR round trips)
     return [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-mllvm", "-amdgpu-mfma-vgpr-form",
             "-I", INCLUDE, "-I", CSRC]
 
 

@@ -65,6 +65,8 @@ int linear(int bits, bool is_gemm, const uint16_t *x, const void *packed, size_t
         return st;
     if (is_gemm ? M > (int64_t(1) << 30) : M > 16)
         return TF_ERR_SHAPE;
+    if (is_gemm && K >= (int64_t(1) << 25)) // the GEMM's activation offsets are 32-bit
+        return TF_ERR_SHAPE;
     if (M == 0)
         return TF_OK;
     if (!x || !packed || !y)

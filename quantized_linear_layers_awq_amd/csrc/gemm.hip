@@ -2,198 +2,413 @@
 // section 1: unpack and dequantize each weight tile once, keep the result in
 // core-local memory and reuse it for the following matrix operations).
 //
-// MI355X design.  A workgroup owns a BM x BN output tile.  Per K-batch of 128
-// rows it stages the activation tile [BM][128] in LDS and unpacks the packed
-// weight tile once into LDS as bf16 (q - z) -- exact, since |q - z| <= 255 has
-// at most 8 significant bits -- laid out [BN][128] (k contiguous per column,
-// the 16x16x32 MFMA B operand a lane reads).  All BM rows reuse that tile
-// through bf16 MFMAs; each group's products accumulate in fp32 and the group's
-// bf16 scale is folded in once per (group, column):
-//     y += s[g][n] * sum_{k in g} x[m][k] * (q[k][n] - z[g][n])
-// i.e. the definition with the per-group factor taken out of the sum.  (A
-// bf16 copy of (q - z) * s would round every weight to 8 significant bits,
-// an error the elementwise output bound does not absorb.)  No dequantized
-// weight leaves LDS.
+// MI355X design.  A workgroup (4 waves) owns a 256 x 128 output tile; each
+// wave a 128 x 64 sub-tile of 8 x 4 bf16 16x16x32 MFMA tiles (128 fp32
+// accumulators per lane, all in arch VGPRs).  K advances in stages of 64 rows.
+// Every global load is an LDS-DMA load (global_load_lds_dwordx4 / _dword), so
+// nothing is staged through registers and the number of loads a stage issues
+// is fixed; the waits are explicit vmcnt values:
+//   - activations: a 3-deep ring of [256][64] bf16 stages, two stages ahead;
+//   - codes and metadata records: one k-tile (W4) or two stages (W8) ahead.
+// The packed codes of a stage are unpacked once into a [128][64] LDS tile as
+// the exact bf16 values q - z (|q - z| <= 255 has at most 8 significant
+// bits), double buffered, and all 256 rows of the tile reuse them.  All LDS
+// tiles use an XOR swizzle of their 16-byte units so that fragment reads and
+// writes are free of bank conflicts.
+//
+// The per-(group, column) scale is folded without a second accumulator set:
+// the accumulator holds y / s_g while group g accumulates, so at a group
+// boundary it is multiplied by s_g / s_{g+1} and at the end by the last s:
+//     y = s_G * (... (s_0/s_1 * P_0 + P_1) * s_1/s_2 + ... + P_G)
+// with P_g = sum_{k in g} x * (q - z) accumulated by the MFMAs in fp32.  A
+// zero scale keeps the previous one and its group's operands are written as
+// zeros, so its contribution vanishes as it should.  Consecutive scales must
+// keep s_g / s_{g+1} and the running sums inside the fp32 range (true for any
+// real checkpoint).
 #include "tf_common.h"
 #include "tf_launch.h"
 
 namespace tf {
 
-constexpr int kGemmBM = 128;
-constexpr int kGemmBN = 128;         // eight packed 16-column blocks
-constexpr int kGemmBK = kTileRows;   // one k-tile (four 32-row steps) per stage
-constexpr int kGemmLd = kGemmBK + 8; // LDS row pitch in bf16 (pad: spreads 16 rows over the banks)
+constexpr int kGBM = 256;                        // rows per workgroup tile
+constexpr int kGBN = 128;                        // columns per workgroup tile
+constexpr int kGBlocks = kGBN / kBlockCols;      // 8 packed blocks
+constexpr int kStage = 64;                       // k rows per pipeline stage
+constexpr int kAStages = 3;
+constexpr int kAStageBytes = kGBM * kStage * 2;  // 32 KiB
+constexpr int kBStageBytes = kGBN * kStage * 2;  // 16 KiB
+constexpr int kCodeBufBytes = kGBlocks * 1024;   // codes of one k-tile (W4) or stage (W8)
+constexpr int kMetaWaveBytes = 512;              // record bytes DMA'd per wave per k-tile
+constexpr int kMetaBufBytes = 4 * kMetaWaveBytes;
+constexpr int kOffB = kAStages * kAStageBytes;
+constexpr int kOffCodes = kOffB + 2 * kBStageBytes;
+constexpr int kOffMeta = kOffCodes + 2 * kCodeBufBytes;
+constexpr int kGemmLds = kOffMeta + 2 * kMetaBufBytes; // 148 KiB
 
-template <int BITS, bool kWhole>
-__global__ __launch_bounds__(256) void gemm_kernel(const uint16_t *__restrict__ x, const uint8_t *__restrict__ packed,
-                                                   uint16_t *__restrict__ y, Layout lay, int64_t M, int64_t m_tiles)
+// 16-byte unit (row, c) of a [rows][64] bf16 tile, c = 0..7.  Rows are 128
+// bytes, so two share a 256-byte bank line; the XOR with (row / 2) % 8 puts
+// the 16 rows a fragment read touches at one c into 16 distinct bank groups.
+__device__ __forceinline__ int swz(int row, int c) { return (row << 3) + (c ^ ((row >> 1) & 7)); }
+
+// s_waitcnt immediates (gfx9 encoding): vmcnt in bits 3:0 and 15:14, expcnt
+// 6:4, lgkmcnt 11:8; counters not named stay at their maximum (no wait).
+template <int N> __device__ __forceinline__ void wait_vmcnt()
 {
-    __shared__ __attribute__((aligned(16))) uint16_t sA[kGemmBM * kGemmLd];
-    __shared__ __attribute__((aligned(16))) uint16_t sB[kGemmBN * kGemmLd];
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4)); }
+
+// Workgroup barrier for LDS filled by LDS-DMA: each wave has already waited
+// for its own loads; the empty asm statements keep the compiler from moving
+// memory operations across the barrier.
+__device__ __forceinline__ void lds_barrier()
+{
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// LDS-DMA: lane i's 16 (or 4) bytes land at lds + 16 i (or 4 i).
+__device__ __forceinline__ void dma16(const void *g, void *lds)
+{
+    __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void *)lds, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void *g, void *lds)
+{
+    __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void *)lds, 4, 0, 0);
+}
+
+// kGOneTile: every k-tile is exactly one group (G == 128, or G == K <= 128);
+// kGWhole: every k-tile lies inside one group; kGSplit: G is 32 or 64.
+enum GemmGroups { kGSplit = 0, kGWhole = 1, kGOneTile = 2 };
+
+template <int BITS, int kMode>
+__global__ __launch_bounds__(256, 1) void gemm_kernel(const uint16_t *__restrict__ x, const uint8_t *__restrict__ packed,
+                                                      uint16_t *__restrict__ y, Layout lay, int64_t M, int m_tiles)
+{
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    constexpr int RB = record_bytes(BITS);
+    // records a k-tile can touch per block (split: up to four 32-row groups)
+    constexpr int kRecs = kMode == kGSplit ? 4 : 1;
+    constexpr int kBlockMeta = kRecs * RB;                   // <= 192 bytes
+    constexpr int kMetaDma = (2 * kBlockMeta / 4 + 63) / 64; // dword-DMA instructions per wave
+    constexpr bool kW8 = BITS == 8;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
-    const int o = lane >> 4, r = lane & 15;
-    // consecutive workgroups share a weight tile (column tile outer)
-    const int64_t nt = blockIdx.x / m_tiles;
-    const int64_t mt = blockIdx.x - nt * m_tiles;
-    const int64_t m0 = mt * kGemmBM;
-    const int64_t blk0 = nt * (kGemmBN / kBlockCols);
-    const uint32_t spg = (uint32_t)(lay.G / kStepRows);
-    constexpr int RB = record_bytes(BITS);
-    const u32x4 zero4 = {0u, 0u, 0u, 0u};
-    const f32x4 zf = {0.f, 0.f, 0.f, 0.f};
+    const int r = lane & 15, o = lane >> 4;
 
-    f32x4 yacc[4][4], gacc[4][4];
+    // ---- tile order: consecutive tiles on one XCD share a column tile ----
+    const int nwg = gridDim.x, bid = blockIdx.x;
+    const int xcd = bid & 7, local = bid >> 3, q8 = nwg >> 3, rem = nwg & 7;
+    const int tile = xcd < rem ? xcd * (q8 + 1) + local : rem * (q8 + 1) + (xcd - rem) * q8 + local;
+    const int nt = tile / m_tiles, mt = tile - nt * m_tiles;
+    const int64_t m0 = (int64_t)mt * kGBM;
+    const int64_t blk0 = (int64_t)nt * kGBlocks;
+
+    const int ktiles = (int)lay.ktiles;
+    const int nstages = 2 * ktiles;
+    const int steps = (int)lay.steps;
+    const int sg = (int)(lay.G / kStepRows); // 32-row steps per group
+    const int64_t K = lay.K;
+    const bool one_tile = kMode == kGOneTile;
+
+    uint8_t *const sA = lds;
+    uint8_t *const sB = lds + kOffB;
+    uint8_t *const sCodes = lds + kOffCodes;
+    uint8_t *const sMeta = lds + kOffMeta;
+
+    // ---- activations: wave w fills rows 64w .. 64w+63 of a stage, 8 rows per
+    //      instruction; lane p takes row 8j + p/8 and the 16-byte unit that the
+    //      swizzle places at slot p%8. ----
+    const int a_row_in = lane >> 3, a_slot = lane & 7;
+    // rows 64w + 8j + p/8 (j = 0..7), clamped at M - 1: the lane's base row
+    // and 32-bit element offsets of the other seven from it
+    const uint16_t *a_base;
+    int a_off[8];
+    {
+        const int64_t row0 = m0 + 64 * wave + a_row_in;
+        const int64_t g0 = row0 < M ? row0 : M - 1; // rows past M are computed on a copy, never stored
+        a_base = x + g0 * K;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+        for (int j = 0; j < 8; ++j) {
+            int64_t gm = row0 + 8 * j;
+            gm = gm < M ? gm : M - 1;
+            a_off[j] = (int)((gm - g0) * K);
+        }
+    }
+    // swizzle slot -> unit: (row / 2) % 8 is (4 (j % 2) + p / 16) % 8
+    const int a_c8e = 8 * (a_slot ^ ((a_row_in >> 1) & 7));
+    const int a_c8o = 8 * (a_slot ^ ((4 + (a_row_in >> 1)) & 7));
+    auto dma_a = [&](int s) {
+        uint8_t *dst = sA + (s % kAStages) * kAStageBytes + 64 * wave * 128;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            int64_t k = (int64_t)s * kStage + ((j & 1) ? a_c8o : a_c8e);
+            k = k < K ? k : 0; // rows past K meet zero weights
+            dma16(a_base + a_off[j] + k, dst + j * 1024);
+        }
+    };
+    // codes: wave w fetches blocks w and w + 4 (1 KiB each; W8: one half tile)
+    auto dma_codes = [&](int t, int half, int buf) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int bb = wave + 4 * i;
+            int64_t blk = blk0 + bb;
+            blk = blk < lay.nblocks ? blk : 0;
+            const uint8_t *src = packed + blk * lay.block_bytes + lay.meta_bytes + (int64_t)t * tile_bytes(BITS) +
+                                 1024 * half + 16 * lane;
+            dma16(src, sCodes + buf * kCodeBufBytes + bb * 1024);
+        }
+    };
+    // records of k-tile t for blocks 2w and 2w + 1, as dwords
+    auto first_group = [&](int t) -> int64_t { return one_tile ? t : ((int64_t)t * kTileRows) / lay.G; };
+    auto dma_meta = [&](int t, int buf) {
+        const int64_t g_first = first_group(t);
+#pragma unroll
+        for (int i = 0; i < kMetaDma; ++i) {
+            const int d = 64 * i + lane; // dword index within this wave's share
+            const int bsel = d / (kBlockMeta / 4), e = d - bsel * (kBlockMeta / 4);
+            const int64_t blk = blk0 + 2 * wave + bsel;
+            const int64_t g = g_first + (4 * e) / RB;
+            const bool ok = bsel < 2 && blk < lay.nblocks && g < lay.ngroups;
+            const uint8_t *src = ok ? packed + blk * lay.block_bytes + g_first * RB + 4 * e : packed;
+            dma4(src, sMeta + buf * kMetaBufBytes + wave * kMetaWaveBytes + 256 * i);
+        }
+    };
+    // the staged record of block bb (0..7) for group g, which k-tile t touches
+    auto meta_rec = [&](int bb, int t, int64_t g) -> const uint8_t * {
+        const uint8_t *rec = sMeta + (t & 1) * kMetaBufBytes + (bb >> 1) * kMetaWaveBytes + (bb & 1) * kBlockMeta;
+        return one_tile ? rec : rec + (int)(g - first_group(t)) * RB;
+    };
+    auto code_buf = [&](int s) { return kW8 ? (s & 1) : ((s >> 1) & 1); };
+
+    // ---- unpack stage sd into B buffer sd % 2: exact bf16 (q - z), zero where
+    //      the row is past K, the block past N, or the group's scale is 0 ----
+    auto fill_b = [&](int sd) {
+        const int td = sd >> 1, hd = sd & 1;
+        const uint8_t *codes = sCodes + code_buf(sd) * kCodeBufBytes;
+        uint8_t *dst = sB + (sd & 1) * kBStageBytes;
+#pragma unroll
+        for (int it = 0; it < 2; ++it) {
+            const int bb = wave + 4 * it;
+            const bool blk_ok = blk0 + bb < lay.nblocks;
+            // W4: words 2hd, 2hd+1 of the k-tile's 16 bytes; W8: the half's 16 bytes
+            u32x4 cw;
+            if constexpr (kW8) {
+                cw = *reinterpret_cast<const u32x4 *>(codes + bb * 1024 + 16 * lane);
+            } else {
+                const u32x2 c2 = *reinterpret_cast<const u32x2 *>(codes + bb * 1024 + 16 * lane + 8 * hd);
+                cw = u32x4{c2[0], c2[1], 0u, 0u};
+            }
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                const int step = 4 * td + 2 * hd + kk;
+                const int64_t g = one_tile ? td : (int64_t)step / sg;
+                const uint8_t *rec = meta_rec(bb, td, g);
+                const float sv = record_scale<BITS>(rec, r);
+                const uint32_t z = record_zero<BITS>(rec, r);
+                const bool live = blk_ok && step < steps && sv != 0.f;
+                float f[8];
+                if constexpr (kW8)
+                    dequant_w8_pair(cw[2 * kk], cw[2 * kk + 1], 1.f, -(float)z, f);
+                else
+                    dequant_w4_word(cw[kk], 1.f, -(float)z, f);
+                u32x4 v = {pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
+                           pack_bf16x2(f[6], f[7])};
+                if (!live)
+                    v = u32x4{0u, 0u, 0u, 0u};
+                *reinterpret_cast<u32x4 *>(dst + 16 * swz(16 * bb + r, 4 * kk + o)) = v;
+            }
+        }
+    };
+
+    // ---- scales of the lane's four columns (blocks 4 wn + j, column r) ----
+    auto scales_of = [&](int64_t g, int t, float (&s)[4]) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int bb = 4 * wn + j;
+            s[j] = blk0 + bb < lay.nblocks ? record_scale<BITS>(meta_rec(bb, t, g), r) : 0.f;
+        }
+    };
+
+    f32x4 acc[8][4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-            yacc[i][j] = gacc[i][j] = zf;
+            acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float seff[4];
 
-    for (int64_t t = 0; t < lay.ktiles; ++t) {
-        // ---- activations: 128 rows x 256 bytes, 16 bytes per thread x 8 ----
+    // ---- prologue: k-tile 0's codes and records, stages 0 and 1 of x ----
+    dma_codes(0, 0, 0);
+    dma_meta(0, 0);
+    dma_a(0);
+    if (nstages > 1) {
+        if (kW8)
+            dma_codes(0, 1, 1);
+        dma_a(1);
+        wait_vmcnt<8>();
+    } else {
+        wait_vmcnt<0>();
+    }
+    lds_barrier();
+    fill_b(0);
+    {
+        float s0[4];
+        scales_of(0, 0, s0);
 #pragma unroll
-        for (int it = 0; it < 8; ++it) {
-            const int idx = tid + 256 * it;
-            const int row = idx >> 4, c16 = idx & 15;
-            const int64_t gm = m0 + row;
-            const int64_t k = t * kTileRows + 8 * c16;
-            u32x4 v = zero4;
-            if (gm < M && k < lay.K)
-                v = load16(x + gm * lay.K + k);
-            *reinterpret_cast<u32x4 *>(&sA[row * kGemmLd + 8 * c16]) = v;
-        }
-        // ---- weights: unpack each 16-byte unit of codes once into LDS as the
-        //      exact bf16 values q - z.  Units map wave-uniformly to blocks. ----
-        constexpr int kUnitIters = BITS == 4 ? 2 : 4;
-#pragma unroll
-        for (int it = 0; it < kUnitIters; ++it) {
-            const int bb = BITS == 4 ? wave + 4 * it : (wave + 4 * it) >> 1;
-            const int h = BITS == 4 ? 0 : wave & 1;
-            const int64_t blk = blk0 + bb;
-            constexpr int kSteps = BITS == 4 ? 4 : 2;
-            const int nl = kBlockCols * bb + r;
-            if (blk < lay.nblocks) {
-                const uint8_t *meta = packed + blk * lay.block_bytes;
-                const u32x4 cw = load16(meta + lay.meta_bytes + t * tile_bytes(BITS) + 1024 * h + 16 * lane);
-                uint32_t zt = 0;
-                if constexpr (kWhole)
-                    zt = record_zero<BITS>(meta + (int64_t)((uint32_t)t / (uint32_t)lay.tiles_per_group) * RB, r);
-#pragma unroll
-                for (int uu = 0; uu < kSteps; ++uu) {
-                    const int u = BITS == 4 ? uu : 2 * h + uu;
-                    const int64_t s = 4 * t + u;
-                    u32x4 bf = zero4;
-                    if (s < lay.steps) {
-                        uint32_t z = zt;
-                        if constexpr (!kWhole)
-                            z = record_zero<BITS>(meta + (int64_t)((uint32_t)s / spg) * RB, r);
-                        float f[8];
-                        if constexpr (BITS == 4)
-                            dequant_w4_word(cw[u], 1.f, -(float)z, f);
-                        else
-                            dequant_w8_pair(cw[2 * uu], cw[2 * uu + 1], 1.f, -(float)z, f);
-                        bf = u32x4{pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
-                                   pack_bf16x2(f[6], f[7])};
-                    }
-                    *reinterpret_cast<u32x4 *>(&sB[nl * kGemmLd + kStepRows * u + 8 * o]) = bf;
-                }
-            } else {
-#pragma unroll
-                for (int uu = 0; uu < kSteps; ++uu) {
-                    const int u = BITS == 4 ? uu : 2 * h + uu;
-                    *reinterpret_cast<u32x4 *>(&sB[nl * kGemmLd + kStepRows * u + 8 * o]) = zero4;
-                }
-            }
-        }
-        // ---- scales of the groups that end inside this k-tile: this wave's
-        //      column j sits in block blk0 + 4 wn + j, column r ----
-        float scv[4][4];
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            const int64_t s = 4 * t + kk;
-            const bool ends = s < lay.steps && ((uint32_t)s + 1) % spg == 0;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int64_t blk = blk0 + 4 * wn + j;
-                scv[kk][j] = 0.f;
-                if (ends && blk < lay.nblocks)
-                    scv[kk][j] = record_scale<BITS>(
-                        packed + blk * lay.block_bytes + (int64_t)((uint32_t)s / spg) * RB, r);
-            }
-        }
-        __syncthreads();
+        for (int j = 0; j < 4; ++j)
+            seff[j] = s0[j] != 0.f ? s0[j] : 1.f;
+    }
+    wait_lgkmcnt0();
+    lds_barrier();
 
-        // ---- MFMA: each wave a 64 x 64 sub-tile, 4 x 4 MFMA tiles ----
+    for (int t = 0; t < ktiles; ++t)
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            const int64_t s = 4 * t + kk;
-            if (s >= lay.steps)
-                break;
-            u32x4 a[4], b[4];
-            const int kof = kStepRows * kk + 8 * o;
+    for (int h = 0; h < 2; ++h) {
+        const int s = 2 * t + h;
+        // ---- loads for later stages: codes and records first, x last.  Past
+        //      the end they re-read the last stage into slots nobody reads, so
+        //      every stage issues the same loads. ----
+        const int tn = t + 1 < ktiles ? t + 1 : ktiles - 1;
+        const int sa = s + 2 < nstages ? s + 2 : nstages - 1;
+        if (kW8)
+            dma_codes(sa >> 1, sa & 1, s & 1);
+        else if (h == 0)
+            dma_codes(tn, 0, (t + 1) & 1);
+        if (h == 0)
+            dma_meta(tn, (t + 1) & 1);
+        dma_a(sa);
+
+        // ---- MFMAs of stage s ----
+        const uint8_t *a_st = sA + (s % kAStages) * kAStageBytes;
+        const uint8_t *b_st = sB + h * kBStageBytes;
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                a[i] = *reinterpret_cast<const u32x4 *>(&sA[(64 * wm + 16 * i + r) * kGemmLd + kof]);
+        for (int kk = 0; kk < 2; ++kk) {
+            const int step = 4 * t + 2 * h + kk;
+            u32x4 bf[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                b[j] = *reinterpret_cast<const u32x4 *>(&sB[(64 * wn + 16 * j + r) * kGemmLd + kof]);
+                bf[j] = *reinterpret_cast<const u32x4 *>(b_st + 16 * swz(64 * wn + 16 * j + r, 4 * kk + o));
+            if (one_tile && h == 1 && kk == 1) {
+                // last step of k-tile t, which is group t: fold in s_t / s_{t+1}
+                // row tile by row tile, right after each one's MFMAs
+                float sn[4], ratio[4];
+                scales_of(tn, tn, sn);
+                const bool more = t + 1 < ktiles;
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+                for (int j = 0; j < 4; ++j) {
+                    const float se = sn[j] != 0.f ? sn[j] : seff[j];
+                    ratio[j] = more ? seff[j] * __builtin_amdgcn_rcpf(se) : 1.f;
+                    seff[j] = more ? se : seff[j];
+                }
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    gacc[i][j] = mfma16x16x32(a[i], b[j], gacc[i][j]);
-            if (((uint32_t)s + 1) % spg == 0) {
-                // group end: y += s[g][n] * (this group's sum), once per element
+                for (int i = 0; i < 8; ++i) {
+                    const u32x4 af =
+                        *reinterpret_cast<const u32x4 *>(a_st + 16 * swz(128 * wm + 16 * i + r, 4 * kk + o));
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
+                    for (int j = 0; j < 4; ++j) {
+                        acc[i][j] = mfma16x16x32(af, bf[j], acc[i][j]);
 #pragma unroll
                         for (int e = 0; e < 4; ++e)
-                            yacc[i][j][e] = fmaf(scv[kk][j], gacc[i][j][e], yacc[i][j][e]);
-                        gacc[i][j] = zf;
+                            acc[i][j][e] *= ratio[j];
                     }
+                }
+                continue;
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const u32x4 af =
+                    *reinterpret_cast<const u32x4 *>(a_st + 16 * swz(128 * wm + 16 * i + r, 4 * kk + o));
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    acc[i][j] = mfma16x16x32(af, bf[j], acc[i][j]);
+            }
+            // group boundary after this step: rescale by s_g / s_{g+1}
+            if (!one_tile && (step + 1) % sg == 0 && step + 1 < steps) {
+                const int64_t gn = (int64_t)(step + 1) / sg;
+                const int tg = (step + 1) >> 2; // k-tile holding the next group's first step
+                float sn[4], ratio[4];
+                scales_of(gn, tg, sn);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float se = sn[j] != 0.f ? sn[j] : seff[j];
+                    ratio[j] = seff[j] * __builtin_amdgcn_rcpf(se);
+                    seff[j] = se;
+                }
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            acc[i][j][e] *= ratio[j];
             }
         }
-        __syncthreads();
-    }
 
-    // ---- epilogue: fp32 -> bf16 (nearest even), masked to M x N ----
-    const int64_t n0 = nt * kGemmBN;
+        // ---- unpack the next stage's weights into the other B buffer (past
+        //      the last stage this writes a buffer nobody reads) ----
+        fill_b(s + 1);
+
+        // ---- stage s + 1's x (issued one stage ago) must have landed: only
+        //      this stage's eight x loads may still be in flight ----
+        wait_vmcnt<8>();
+        wait_lgkmcnt0();
+        lds_barrier();
+    }
+    wait_vmcnt<0>();
+
+    // ---- epilogue: y = acc * s_last, fp32 -> bf16 (nearest even) ----
+    const int64_t n0 = (int64_t)nt * kGBN;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int64_t row = m0 + 64 * wm + 16 * i + 4 * o + e;
+                const int64_t row = m0 + 128 * wm + 16 * i + 4 * o + e;
                 const int64_t col = n0 + 64 * wn + 16 * j + r;
                 if (row < M && col < lay.N)
-                    y[row * lay.N + col] = f32_to_bf16_bits(yacc[i][j][e]);
+                    y[row * lay.N + col] = f32_to_bf16_bits(acc[i][j][e] * seff[j]);
             }
+}
+
+// The kernel needs more than the default 64 KiB of dynamic LDS; raise the
+// limit once per instantiation.
+template <int BITS, int kMode> static void launch_mode(dim3 grid, hipStream_t stream, const uint16_t *x,
+                                                       const uint8_t *pk, uint16_t *y, const Layout &lay, int64_t M,
+                                                       int m_tiles)
+{
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(&gemm_kernel<BITS, kMode>),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, kGemmLds);
+    (void)attr;
+    gemm_kernel<BITS, kMode><<<grid, 256, kGemmLds, stream>>>(x, pk, y, lay, M, m_tiles);
 }
 
 hipError_t launch_gemm(int bits, const uint16_t *x, const void *packed, uint16_t *y, int64_t M, const Layout &lay,
                        hipStream_t stream)
 {
-    const int64_t m_tiles = (M + kGemmBM - 1) / kGemmBM;
-    const int64_t n_tiles = (lay.N + kGemmBN - 1) / kGemmBN;
+    const int64_t m_tiles = (M + kGBM - 1) / kGBM;
+    const int64_t n_tiles = (lay.N + kGBN - 1) / kGBN;
     const dim3 grid((unsigned)(m_tiles * n_tiles));
     const uint8_t *pk = static_cast<const uint8_t *>(packed);
-    const bool whole = lay.whole_tiles();
+    const int mode = lay.tiles_per_group == 1 ? kGOneTile : lay.whole_tiles() ? kGWhole : kGSplit;
     if (bits == 4) {
-        if (whole)
-            gemm_kernel<4, true><<<grid, 256, 0, stream>>>(x, pk, y, lay, M, m_tiles);
+        if (mode == kGOneTile)
+            launch_mode<4, kGOneTile>(grid, stream, x, pk, y, lay, M, (int)m_tiles);
+        else if (mode == kGWhole)
+            launch_mode<4, kGWhole>(grid, stream, x, pk, y, lay, M, (int)m_tiles);
         else
-            gemm_kernel<4, false><<<grid, 256, 0, stream>>>(x, pk, y, lay, M, m_tiles);
+            launch_mode<4, kGSplit>(grid, stream, x, pk, y, lay, M, (int)m_tiles);
     } else {
-        if (whole)
-            gemm_kernel<8, true><<<grid, 256, 0, stream>>>(x, pk, y, lay, M, m_tiles);
+        if (mode == kGOneTile)
+            launch_mode<8, kGOneTile>(grid, stream, x, pk, y, lay, M, (int)m_tiles);
+        else if (mode == kGWhole)
+            launch_mode<8, kGWhole>(grid, stream, x, pk, y, lay, M, (int)m_tiles);
         else
-            gemm_kernel<8, false><<<grid, 256, 0, stream>>>(x, pk, y, lay, M, m_tiles);
+            launch_mode<8, kGSplit>(grid, stream, x, pk, y, lay, M, (int)m_tiles);
     }
     return hipGetLastError();
 }
