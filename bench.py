@@ -55,8 +55,11 @@ def parse():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--replicas", type=int, default=0, help="weight replicas to rotate (0: enough to beat the cache)")
-    p.add_argument("--only", choices=["all", "gemv", "gemm"], default="all",
-                   help="restrict the run (profiling passes)")
+    p.add_argument("--only", choices=["all", "gemv", "gemm", "copy"], default="all",
+                   help="restrict the run (profiling passes); 'copy' runs the plain-copy calibration kernel")
+    p.add_argument("--counters-from", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
+                   help="no GPU: read four rocprofv3 --pmc output directories (FETCH_SIZE and WRITE_SIZE over "
+                        "'--only gemv', then over '--only copy') and write the per-launch HBM traffic file")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--gemm-iters", type=int, default=20)
     return p.parse_args()
@@ -100,6 +103,75 @@ def cpu_baseline(synth, oracle, M, budget_s=12.0):
                 kind="oracle",
                 sample=f"{passes} full pass(es) over the 7 layer linears at M=1 "
                        f"({passes * total_bytes / 1e6:.0f} MB of algorithmic bytes, {el:.1f} s)")
+
+
+COPY_BYTES = 1 << 30
+
+
+def bench_copy(torch):
+    """Plain device copy of COPY_BYTES, five times: the calibration kernel whose
+    FETCH_SIZE / WRITE_SIZE readings scale the GEMV's counters to bytes."""
+    src = torch.empty(COPY_BYTES // 2, dtype=torch.bfloat16, device="cuda:0").fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    return dict(copy_bytes=COPY_BYTES, launches=5)
+
+
+def _pmc_rows(path):
+    """(kernel name, counter name, value) rows of a rocprofv3 counter CSV
+    (a file, or a directory searched for *counter_collection.csv)."""
+    import csv
+    import glob
+
+    files = [path] if os.path.isfile(path) else sorted(
+        glob.glob(os.path.join(path, "**", "*counter_collection.csv"), recursive=True))
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {path}")
+    rows = []
+    for fn in files:
+        with open(fn, newline="") as f:
+            for r in csv.DictReader(f):
+                rows.append((r["Kernel_Name"], r["Counter_Name"], float(r["Counter_Value"]), r.get("Dispatch_Id")))
+    return rows
+
+
+def _per_dispatch_kib(path, counter, match):
+    """Mean over matching dispatches of one counter (summed over its
+    instances within a dispatch), in the counter's own unit (KiB)."""
+    per = {}
+    for name, cname, v, did in _pmc_rows(path):
+        if cname == counter and match(name):
+            per[did] = per.get(did, 0.0) + v
+    if not per:
+        raise SystemExit(f"no {counter} dispatches matched in {path}")
+    return sum(per.values()) / len(per), len(per)
+
+
+def write_counters(dirs):
+    """Per-launch HBM traffic of the GEMV layer from two --pmc passes, each
+    scaled by the same counter's reading on the plain copy kernel."""
+    fetch_dir, write_dir, cfetch_dir, cwrite_dir = dirs
+    is_gemv = lambda n: "gemv_kernel" in n
+    is_copy = lambda n: "copy" in n.lower() and "gemv" not in n
+    f_kib, nf = _per_dispatch_kib(fetch_dir, "FETCH_SIZE", is_gemv)
+    w_kib, nw = _per_dispatch_kib(write_dir, "WRITE_SIZE", is_gemv)
+    cf_kib, _ = _per_dispatch_kib(cfetch_dir, "FETCH_SIZE", is_copy)
+    cw_kib, _ = _per_dispatch_kib(cwrite_dir, "WRITE_SIZE", is_copy)
+    fetch_scale = COPY_BYTES / (cf_kib * 1024)
+    write_scale = COPY_BYTES / (cw_kib * 1024)
+    hbm = f_kib * 1024 * fetch_scale + w_kib * 1024 * write_scale
+    out = dict(kernel_source_hash=kernel_source_hash(), kernel="gemv_kernel (tf_gemv_w4a16), 7 layer linears",
+               fetch_kib_per_launch=round(f_kib, 1), write_kib_per_launch=round(w_kib, 1),
+               dispatches=dict(fetch=nf, write=nw),
+               copy_calibration=dict(bytes=COPY_BYTES, fetch_kib=round(cf_kib, 1), write_kib=round(cw_kib, 1),
+                                     fetch_scale=round(fetch_scale, 4), write_scale=round(write_scale, 4)),
+               hbm_bytes_per_launch=round(hbm))
+    with open(COUNTERS_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out))
 
 
 def queue_filler(torch, ms):
@@ -172,24 +244,26 @@ def bench_gemv(torch, q, args):
     torch.cuda.synchronize()
     eager_ms = (time.perf_counter() - h0) * 1e3 / n_eager
 
-    # per-launch kernel durations: event pairs around eager launches queued
-    # behind filler work, so no host gap lands inside a pair
+    # per-linear launch time: a batch of eager launches of one linear queued
+    # behind filler work (so they run back to back), one event pair per batch
     n_prof = min(args.steps, 40)
-    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in lins]
-           for _ in range(n_prof)]
-    keep = queue_filler(torch, ms=0.05 * n_prof * len(lins) + 5)
-    for i in range(n_prof):
-        r = i % R
-        for (e0, e1), l, p in zip(evs[i], lins, replicas[r]):
-            e0.record()
-            q.tf_gemv_w4a16(l["x"], p, l["K"], l["N"], l["G"], y=l["y"])
-            e1.record()
+    keep = queue_filler(torch, ms=0.02 * n_prof * len(lins) + 5)
+    evs = []
+    for j, l in enumerate(lins):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(n_prof):
+            q.tf_gemv_w4a16(l["x"], replicas[i % R][j], l["K"], l["N"], l["G"], y=l["y"])
+        e1.record()
+        evs.append((e0, e1))
     torch.cuda.synchronize()
     del keep
-    per_lin = [[evs[i][j][0].elapsed_time(evs[i][j][1]) for i in range(n_prof)] for j in range(len(lins))]
-    mean_us = [1e3 * sum(v) / len(v) for v in per_lin]
-    dur_total_us = sum(mean_us)
-    achieved = layer_bytes / (dur_total_us * 1e-6) / 1e9
+    mean_us = [1e3 * e0.elapsed_time(e1) / n_prof for e0, e1 in evs]
+
+    # the roofline's per-launch duration: the timed region (graph replays and
+    # the events around them share torch's current stream) over its launches
+    avg_launch_us = ms_step * 1e3 / len(lins)
+    achieved = layer_bytes / len(lins) / (avg_launch_us * 1e-6) / 1e9
 
     traffic = None
     if os.path.exists(COUNTERS_FILE):
@@ -208,7 +282,7 @@ def bench_gemv(torch, q, args):
                       frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic,
                       kernel="gemv_kernel (tf_gemv_w4a16, W4, one k-tile per group)",
                       bytes_per_launch=round(layer_bytes / len(lins)),
-                      avg_launch_us=round(dur_total_us / len(lins), 3)),
+                      avg_launch_us=round(avg_launch_us, 3)),
     )
 
 
@@ -258,6 +332,9 @@ def bench_gemm(torch, q, args):
 
 def main():
     args = parse()
+    if args.counters_from:
+        write_counters(args.counters_from)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this build has no multi-GPU path.",
               file=sys.stderr)
@@ -271,6 +348,9 @@ def main():
         sys.exit(1)
     q.load_library()
     torch.cuda.set_device(0)
+    if args.only == "copy":
+        print(json.dumps(bench_copy(torch)), flush=True)
+        return
 
     line = {
         "metric": "W4A16 GEMV M=1 effective HBM GB/s; W4A16 GEMM M=2048 TFLOP/s (% of peak)",
