@@ -2,12 +2,14 @@
 // section 1: unpack and dequantize each weight tile once, keep the result in
 // core-local memory and reuse it for the following matrix operations).
 //
-// MI355X design.  A workgroup (4 waves) owns a 256 x 128 output tile; each
-// wave a 128 x 64 sub-tile of 8 x 4 bf16 16x16x32 MFMA tiles (128 fp32
-// accumulators per lane, all in arch VGPRs).  K advances in stages of 64 rows.
-// Every global load is an LDS-DMA load (global_load_lds_dwordx4 / _dword), so
-// nothing is staged through registers and the number of loads a stage issues
-// is fixed; the waits are explicit vmcnt values:
+// MI355X design.  A workgroup (8 waves, two per SIMD) owns a 256 x 128 output
+// tile; each wave a 64 x 64 sub-tile of 4 x 4 bf16 16x16x32 MFMA tiles (64
+// fp32 accumulators per lane, in arch VGPRs).  Two waves per SIMD let one
+// wave's MFMAs run while the other waits on LDS or does vector work.  K
+// advances in stages of 64 rows.  Every global load is an LDS-DMA load
+// (global_load_lds_dwordx4 / _dword), so nothing is staged through registers
+// and the number of loads a stage issues is fixed; the waits are explicit
+// vmcnt values:
 //   - activations: a 3-deep ring of [256][64] bf16 stages, two stages ahead;
 //   - codes and metadata records: one k-tile (W4) or two stages (W8) ahead.
 // The packed codes of a stage are unpacked once into a [128][64] LDS tile as
@@ -38,12 +40,15 @@ constexpr int kAStages = 3;
 constexpr int kAStageBytes = kGBM * kStage * 2;  // 32 KiB
 constexpr int kBStageBytes = kGBN * kStage * 2;  // 16 KiB
 constexpr int kCodeBufBytes = kGBlocks * 1024;   // codes of one k-tile (W4) or stage (W8)
-constexpr int kMetaWaveBytes = 512;              // record bytes DMA'd per wave per k-tile
-constexpr int kMetaBufBytes = 4 * kMetaWaveBytes;
+constexpr int kGWaves = 8;                       // waves per workgroup (4 x 2 over the tile)
+constexpr int kGThreads = 64 * kGWaves;
+constexpr int kMetaWaveBytes = 256;              // record bytes DMA'd per wave (one block) per k-tile
+constexpr int kMetaBufBytes = kGWaves * kMetaWaveBytes;
 constexpr int kOffB = kAStages * kAStageBytes;
 constexpr int kOffCodes = kOffB + 2 * kBStageBytes;
 constexpr int kOffMeta = kOffCodes + 2 * kCodeBufBytes;
 constexpr int kGemmLds = kOffMeta + 2 * kMetaBufBytes; // 148 KiB
+static_assert(kGBlocks == kGWaves, "one packed block per wave");
 
 // 16-byte unit (row, c) of a [rows][64] bf16 tile, c = 0..7.  Rows are 128
 // bytes, so two share a 256-byte bank line; the XOR with (row / 2) % 8 puts
@@ -83,20 +88,22 @@ __device__ __forceinline__ void dma4(const void *g, void *lds)
 enum GemmGroups { kGSplit = 0, kGWhole = 1, kGOneTile = 2 };
 
 template <int BITS, int kMode>
-__global__ __launch_bounds__(256, 1) void gemm_kernel(const uint16_t *__restrict__ x, const uint8_t *__restrict__ packed,
-                                                      uint16_t *__restrict__ y, Layout lay, int64_t M, int m_tiles)
+__global__ __launch_bounds__(kGThreads, 1) void gemm_kernel(const uint16_t *__restrict__ x,
+                                                            const uint8_t *__restrict__ packed,
+                                                            uint16_t *__restrict__ y, Layout lay, int64_t M,
+                                                            int m_tiles)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     constexpr int RB = record_bytes(BITS);
     // records a k-tile can touch per block (split: up to four 32-row groups)
     constexpr int kRecs = kMode == kGSplit ? 4 : 1;
-    constexpr int kBlockMeta = kRecs * RB;                   // <= 192 bytes
-    constexpr int kMetaDma = (2 * kBlockMeta / 4 + 63) / 64; // dword-DMA instructions per wave
+    constexpr int kBlockMeta = kRecs * RB; // <= 192 bytes: one dword per lane
+    static_assert(kBlockMeta <= kMetaWaveBytes, "a block's records fit one dword DMA");
     constexpr bool kW8 = BITS == 8;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave >> 1, wn = wave & 1; // 64-row and 64-column slot of the wave
     const int r = lane & 15, o = lane >> 4;
 
     // ---- tile order: consecutive tiles on one XCD share a column tile ----
@@ -119,20 +126,20 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(const uint16_t *__restrict
     uint8_t *const sCodes = lds + kOffCodes;
     uint8_t *const sMeta = lds + kOffMeta;
 
-    // ---- activations: wave w fills rows 64w .. 64w+63 of a stage, 8 rows per
+    // ---- activations: wave w fills rows 32w .. 32w+31 of a stage, 8 rows per
     //      instruction; lane p takes row 8j + p/8 and the 16-byte unit that the
     //      swizzle places at slot p%8. ----
     const int a_row_in = lane >> 3, a_slot = lane & 7;
-    // rows 64w + 8j + p/8 (j = 0..7), clamped at M - 1: the lane's base row
-    // and 32-bit element offsets of the other seven from it
+    // rows 32w + 8j + p/8 (j = 0..3), clamped at M - 1: the lane's base row
+    // and 32-bit element offsets of the other three from it
     const uint16_t *a_base;
-    int a_off[8];
+    int a_off[4];
     {
-        const int64_t row0 = m0 + 64 * wave + a_row_in;
+        const int64_t row0 = m0 + 32 * wave + a_row_in;
         const int64_t g0 = row0 < M ? row0 : M - 1; // rows past M are computed on a copy, never stored
         a_base = x + g0 * K;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = 0; j < 4; ++j) {
             int64_t gm = row0 + 8 * j;
             gm = gm < M ? gm : M - 1;
             a_off[j] = (int)((gm - g0) * K);
@@ -142,100 +149,95 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(const uint16_t *__restrict
     const int a_c8e = 8 * (a_slot ^ ((a_row_in >> 1) & 7));
     const int a_c8o = 8 * (a_slot ^ ((4 + (a_row_in >> 1)) & 7));
     auto dma_a = [&](int s) {
-        uint8_t *dst = sA + (s % kAStages) * kAStageBytes + 64 * wave * 128;
+        uint8_t *dst = sA + (s % kAStages) * kAStageBytes + 32 * wave * 128;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = 0; j < 4; ++j) {
             int64_t k = (int64_t)s * kStage + ((j & 1) ? a_c8o : a_c8e);
             k = k < K ? k : 0; // rows past K meet zero weights
             dma16(a_base + a_off[j] + k, dst + j * 1024);
         }
     };
-    // codes: wave w fetches blocks w and w + 4 (1 KiB each; W8: one half tile)
+    // codes: wave w fetches block w (1 KiB; W8: one half tile)
+    const int64_t my_blk = blk0 + wave < lay.nblocks ? blk0 + wave : 0; // blocks past N: any valid block
     auto dma_codes = [&](int t, int half, int buf) {
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int bb = wave + 4 * i;
-            int64_t blk = blk0 + bb;
-            blk = blk < lay.nblocks ? blk : 0;
-            const uint8_t *src = packed + blk * lay.block_bytes + lay.meta_bytes + (int64_t)t * tile_bytes(BITS) +
-                                 1024 * half + 16 * lane;
-            dma16(src, sCodes + buf * kCodeBufBytes + bb * 1024);
-        }
+        const uint8_t *src =
+            packed + my_blk * lay.block_bytes + lay.meta_bytes + (int64_t)t * tile_bytes(BITS) + 1024 * half + 16 * lane;
+        dma16(src, sCodes + buf * kCodeBufBytes + wave * 1024);
     };
-    // records of k-tile t for blocks 2w and 2w + 1, as dwords
+    // records of k-tile t for block w, as dwords
     auto first_group = [&](int t) -> int64_t { return one_tile ? t : ((int64_t)t * kTileRows) / lay.G; };
     auto dma_meta = [&](int t, int buf) {
         const int64_t g_first = first_group(t);
-#pragma unroll
-        for (int i = 0; i < kMetaDma; ++i) {
-            const int d = 64 * i + lane; // dword index within this wave's share
-            const int bsel = d / (kBlockMeta / 4), e = d - bsel * (kBlockMeta / 4);
-            const int64_t blk = blk0 + 2 * wave + bsel;
-            const int64_t g = g_first + (4 * e) / RB;
-            const bool ok = bsel < 2 && blk < lay.nblocks && g < lay.ngroups;
-            const uint8_t *src = ok ? packed + blk * lay.block_bytes + g_first * RB + 4 * e : packed;
-            dma4(src, sMeta + buf * kMetaBufBytes + wave * kMetaWaveBytes + 256 * i);
-        }
+        const int64_t g = g_first + (4 * lane) / RB;
+        const bool ok = lane < kBlockMeta / 4 && g < lay.ngroups;
+        const uint8_t *src = ok ? packed + my_blk * lay.block_bytes + g_first * RB + 4 * lane : packed;
+        dma4(src, sMeta + buf * kMetaBufBytes + wave * kMetaWaveBytes);
     };
     // the staged record of block bb (0..7) for group g, which k-tile t touches
     auto meta_rec = [&](int bb, int t, int64_t g) -> const uint8_t * {
-        const uint8_t *rec = sMeta + (t & 1) * kMetaBufBytes + (bb >> 1) * kMetaWaveBytes + (bb & 1) * kBlockMeta;
+        const uint8_t *rec = sMeta + (t & 1) * kMetaBufBytes + bb * kMetaWaveBytes;
         return one_tile ? rec : rec + (int)(g - first_group(t)) * RB;
     };
     auto code_buf = [&](int s) { return kW8 ? (s & 1) : ((s >> 1) & 1); };
 
     // ---- unpack stage sd into B buffer sd % 2: exact bf16 (q - z), zero where
-    //      the row is past K, the block past N, or the group's scale is 0 ----
-    auto fill_b = [&](int sd) {
+    //      the row is past K or the group's scale is 0.  Columns past N need
+    //      no care: their outputs are never stored.  Wave w unpacks block w;
+    //      lane (o, r) column r, rows 32 kk + 8 o .. +7.  Split in two so the
+    //      LDS reads are issued early and the arithmetic overlaps MFMAs. ----
+    struct FillIn {
+        u32x4 cw;        // the lane's code words
+        float sv[2];     // scale per 32-row step
+        uint32_t z[2];   // zero point per 32-row step
+    };
+    auto fill_load = [&](int sd, FillIn &in) {
         const int td = sd >> 1, hd = sd & 1;
-        const uint8_t *codes = sCodes + code_buf(sd) * kCodeBufBytes;
+        const uint8_t *codes = sCodes + code_buf(sd) * kCodeBufBytes + wave * 1024 + 16 * lane;
+        if constexpr (kW8) {
+            in.cw = *reinterpret_cast<const u32x4 *>(codes);
+        } else {
+            const u32x2 c2 = *reinterpret_cast<const u32x2 *>(codes + 8 * hd);
+            in.cw = u32x4{c2[0], c2[1], 0u, 0u};
+        }
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            const int step = 4 * td + 2 * hd + kk;
+            const int64_t g = one_tile ? td : (int64_t)step / sg;
+            const uint8_t *rec = meta_rec(wave, td, g);
+            in.sv[kk] = record_scale<BITS>(rec, r);
+            in.z[kk] = record_zero<BITS>(rec, r);
+        }
+    };
+    auto fill_store = [&](int sd, const FillIn &in) {
+        const int td = sd >> 1, hd = sd & 1;
         uint8_t *dst = sB + (sd & 1) * kBStageBytes;
 #pragma unroll
-        for (int it = 0; it < 2; ++it) {
-            const int bb = wave + 4 * it;
-            const bool blk_ok = blk0 + bb < lay.nblocks;
-            // W4: words 2hd, 2hd+1 of the k-tile's 16 bytes; W8: the half's 16 bytes
-            u32x4 cw;
-            if constexpr (kW8) {
-                cw = *reinterpret_cast<const u32x4 *>(codes + bb * 1024 + 16 * lane);
-            } else {
-                const u32x2 c2 = *reinterpret_cast<const u32x2 *>(codes + bb * 1024 + 16 * lane + 8 * hd);
-                cw = u32x4{c2[0], c2[1], 0u, 0u};
-            }
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                const int step = 4 * td + 2 * hd + kk;
-                const int64_t g = one_tile ? td : (int64_t)step / sg;
-                const uint8_t *rec = meta_rec(bb, td, g);
-                const float sv = record_scale<BITS>(rec, r);
-                const uint32_t z = record_zero<BITS>(rec, r);
-                const bool live = blk_ok && step < steps && sv != 0.f;
-                float f[8];
-                if constexpr (kW8)
-                    dequant_w8_pair(cw[2 * kk], cw[2 * kk + 1], 1.f, -(float)z, f);
-                else
-                    dequant_w4_word(cw[kk], 1.f, -(float)z, f);
-                u32x4 v = {pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
-                           pack_bf16x2(f[6], f[7])};
-                if (!live)
-                    v = u32x4{0u, 0u, 0u, 0u};
-                *reinterpret_cast<u32x4 *>(dst + 16 * swz(16 * bb + r, 4 * kk + o)) = v;
-            }
+        for (int kk = 0; kk < 2; ++kk) {
+            const int step = 4 * td + 2 * hd + kk;
+            // (q - z) * live as fma(q, live, -z * live): the mask costs nothing
+            const float live = (step < steps && in.sv[kk] != 0.f) ? 1.f : 0.f;
+            const float nz = -(float)in.z[kk] * live;
+            float f[8];
+            if constexpr (kW8)
+                dequant_w8_pair(in.cw[2 * kk], in.cw[2 * kk + 1], live, nz, f);
+            else
+                dequant_w4_word(in.cw[kk], live, nz, f);
+            const u32x4 v = {pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
+                             pack_bf16x2(f[6], f[7])};
+            *reinterpret_cast<u32x4 *>(dst + 16 * swz(16 * wave + r, 4 * kk + o)) = v;
         }
     };
 
     // ---- scales of the lane's four columns (blocks 4 wn + j, column r) ----
     auto scales_of = [&](int64_t g, int t, float (&s)[4]) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int bb = 4 * wn + j;
-            s[j] = blk0 + bb < lay.nblocks ? record_scale<BITS>(meta_rec(bb, t, g), r) : 0.f;
-        }
+        for (int j = 0; j < 4; ++j)
+            s[j] = record_scale<BITS>(meta_rec(4 * wn + j, t, g), r);
     };
 
-    f32x4 acc[8][4];
+    f32x4 acc[4][4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
             acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -249,13 +251,15 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(const uint16_t *__restrict
         if (kW8)
             dma_codes(0, 1, 1);
         dma_a(1);
-        wait_vmcnt<8>();
+        wait_vmcnt<4>();
     } else {
         wait_vmcnt<0>();
     }
     lds_barrier();
-    fill_b(0);
     {
+        FillIn f0;
+        fill_load(0, f0);
+        fill_store(0, f0);
         float s0[4];
         scales_of(0, 0, s0);
 #pragma unroll
@@ -282,79 +286,83 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(const uint16_t *__restrict
             dma_meta(tn, (t + 1) & 1);
         dma_a(sa);
 
+        // ---- the next stage's codes and records (past the last stage this
+        //      reads and later writes buffers nobody reads) ----
+        FillIn fin;
+        fill_load(s + 1, fin);
+
         // ---- MFMAs of stage s ----
         const uint8_t *a_st = sA + (s % kAStages) * kAStageBytes;
         const uint8_t *b_st = sB + h * kBStageBytes;
+        // one-tile groups: the stage that ends k-tile t ends group t; fold in
+        // s_t / s_{t+1} row tile by row tile right after each one's MFMAs
+        const bool fold_here = one_tile && h == 1;
+        float ratio[4];
+        if (fold_here) {
+            float sn[4];
+            scales_of(tn, tn, sn);
+            const bool more = t + 1 < ktiles;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                // computed unconditionally (the asm pins it) so the last
+                // k-tile's select stays a select, not a branch
+                const float se = sn[j] != 0.f ? sn[j] : seff[j];
+                float rt = seff[j] * __builtin_amdgcn_rcpf(se);
+                asm volatile("" : "+v"(rt));
+                ratio[j] = more ? rt : 1.f;
+                seff[j] = more ? se : seff[j];
+            }
+        }
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
             const int step = 4 * t + 2 * h + kk;
-            u32x4 bf[4];
+            u32x4 bf[4], af[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j)
                 bf[j] = *reinterpret_cast<const u32x4 *>(b_st + 16 * swz(64 * wn + 16 * j + r, 4 * kk + o));
-            if (one_tile && h == 1 && kk == 1) {
-                // last step of k-tile t, which is group t: fold in s_t / s_{t+1}
-                // row tile by row tile, right after each one's MFMAs
-                float sn[4], ratio[4];
-                scales_of(tn, tn, sn);
-                const bool more = t + 1 < ktiles;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                af[i] = *reinterpret_cast<const u32x4 *>(a_st + 16 * swz(64 * wm + 16 * i + r, 4 * kk + o));
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const float se = sn[j] != 0.f ? sn[j] : seff[j];
-                    ratio[j] = more ? seff[j] * __builtin_amdgcn_rcpf(se) : 1.f;
-                    seff[j] = more ? se : seff[j];
-                }
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const u32x4 af =
-                        *reinterpret_cast<const u32x4 *>(a_st + 16 * swz(128 * wm + 16 * i + r, 4 * kk + o));
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        acc[i][j] = mfma16x16x32(af, bf[j], acc[i][j]);
+                    acc[i][j] = mfma16x16x32(af[i], bf[j], acc[i][j]);
+                    if (fold_here && kk == 1) {
 #pragma unroll
                         for (int e = 0; e < 4; ++e)
                             acc[i][j][e] *= ratio[j];
                     }
                 }
-                continue;
-            }
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const u32x4 af =
-                    *reinterpret_cast<const u32x4 *>(a_st + 16 * swz(128 * wm + 16 * i + r, 4 * kk + o));
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    acc[i][j] = mfma16x16x32(af, bf[j], acc[i][j]);
             }
             // group boundary after this step: rescale by s_g / s_{g+1}
             if (!one_tile && (step + 1) % sg == 0 && step + 1 < steps) {
                 const int64_t gn = (int64_t)(step + 1) / sg;
                 const int tg = (step + 1) >> 2; // k-tile holding the next group's first step
-                float sn[4], ratio[4];
+                float sn[4], rt[4];
                 scales_of(gn, tg, sn);
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const float se = sn[j] != 0.f ? sn[j] : seff[j];
-                    ratio[j] = seff[j] * __builtin_amdgcn_rcpf(se);
+                    rt[j] = seff[j] * __builtin_amdgcn_rcpf(se);
                     seff[j] = se;
                 }
 #pragma unroll
-                for (int i = 0; i < 8; ++i)
+                for (int i = 0; i < 4; ++i)
 #pragma unroll
                     for (int j = 0; j < 4; ++j)
 #pragma unroll
                         for (int e = 0; e < 4; ++e)
-                            acc[i][j][e] *= ratio[j];
+                            acc[i][j][e] *= rt[j];
             }
         }
 
-        // ---- unpack the next stage's weights into the other B buffer (past
-        //      the last stage this writes a buffer nobody reads) ----
-        fill_b(s + 1);
+        // ---- unpack the next stage's weights into the other B buffer ----
+        fill_store(s + 1, fin);
 
         // ---- stage s + 1's x (issued one stage ago) must have landed: only
-        //      this stage's eight x loads may still be in flight ----
-        wait_vmcnt<8>();
+        //      this stage's four x loads may still be in flight ----
+        wait_vmcnt<4>();
         wait_lgkmcnt0();
         lds_barrier();
     }
@@ -363,12 +371,12 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(const uint16_t *__restrict
     // ---- epilogue: y = acc * s_last, fp32 -> bf16 (nearest even) ----
     const int64_t n0 = (int64_t)nt * kGBN;
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int64_t row = m0 + 128 * wm + 16 * i + 4 * o + e;
+                const int64_t row = m0 + 64 * wm + 16 * i + 4 * o + e;
                 const int64_t col = n0 + 64 * wn + 16 * j + r;
                 if (row < M && col < lay.N)
                     y[row * lay.N + col] = f32_to_bf16_bits(acc[i][j][e] * seff[j]);
@@ -384,7 +392,7 @@ template <int BITS, int kMode> static void launch_mode(dim3 grid, hipStream_t st
     static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(&gemm_kernel<BITS, kMode>),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, kGemmLds);
     (void)attr;
-    gemm_kernel<BITS, kMode><<<grid, 256, kGemmLds, stream>>>(x, pk, y, lay, M, m_tiles);
+    gemm_kernel<BITS, kMode><<<grid, kGThreads, kGemmLds, stream>>>(x, pk, y, lay, M, m_tiles);
 }
 
 hipError_t launch_gemm(int bits, const uint16_t *x, const void *packed, uint16_t *y, int64_t M, const Layout &lay,
