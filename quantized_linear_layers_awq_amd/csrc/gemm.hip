@@ -2,14 +2,18 @@
 // section 1: unpack and dequantize each weight tile once, keep the result in
 // core-local memory and reuse it for the following matrix operations).
 //
-// MI355X design.  A workgroup (8 waves, two per SIMD) owns a 256 x 128 output
-// tile; each wave a 64 x 64 sub-tile of 4 x 4 bf16 16x16x32 MFMA tiles (64
-// fp32 accumulators per lane, in arch VGPRs).  Two waves per SIMD let one
-// wave's MFMAs run while the other waits on LDS or does vector work.  K
-// advances in stages of 64 rows.  Every global load is an LDS-DMA load
-// (global_load_lds_dwordx4 / _dword), so nothing is staged through registers
-// and the number of loads a stage issues is fixed; the waits are explicit
-// vmcnt values:
+// MI355X design.  A workgroup of 8 waves (two per SIMD) owns a 256 x 128
+// output tile; each wave a 64 x 64 sub-tile of 2 x 2 bf16 32x32x16 MFMA tiles
+// (64 fp32 accumulators per lane, in arch VGPRs).  The 32x32x16 form is used
+// because it keeps the matrix core busy for 32 cycles per instruction, long
+// enough for the unpack and rescale arithmetic of the same SIMD to issue in
+// its shadow; two waves per SIMD let one wave's MFMAs run while the other
+// waits.  K advances in stages of 64 rows, each consumed as four 16-row
+// slices whose A and B fragments are read from LDS one slice ahead.
+//
+// Every global load is an LDS-DMA load (global_load_lds_dwordx4 / _dword),
+// so nothing is staged through registers and the number of loads a stage
+// issues is fixed; the waits are explicit vmcnt values:
 //   - activations: a 3-deep ring of [256][64] bf16 stages, two stages ahead;
 //   - codes and metadata records: one k-tile (W4) or two stages (W8) ahead.
 // The packed codes of a stage are unpacked once into a [128][64] LDS tile as
@@ -18,24 +22,31 @@
 // tiles use an XOR swizzle of their 16-byte units so that fragment reads and
 // writes are free of bank conflicts.
 //
-// The per-(group, column) scale is folded without a second accumulator set:
-// the accumulator holds y / s_g while group g accumulates, so at a group
-// boundary it is multiplied by s_g / s_{g+1} and at the end by the last s:
-//     y = s_G * (... (s_0/s_1 * P_0 + P_1) * s_1/s_2 + ... + P_G)
-// with P_g = sum_{k in g} x * (q - z) accumulated by the MFMAs in fp32.  A
-// zero scale keeps the previous one and its group's operands are written as
-// zeros, so its contribution vanishes as it should.  Consecutive scales must
-// keep s_g / s_{g+1} and the running sums inside the fp32 range (true for any
-// real checkpoint).
+// The per-(group, column) scale is folded by ratio, in two accumulator
+// chains: even groups accumulate in chain 0, odd groups in chain 1.  A chain
+// holds its partial output divided by the scale of its latest group, so when
+// the chain moves from group g to group g + 2 it is multiplied by
+// s_g / s_{g+2}; the final output is chain_0 * s_0' + chain_1 * s_1' with the
+// chains' last scales.  That multiply runs while the other chain's group g + 1
+// is being accumulated, spread over its slices, so no fold ever sits between
+// two dependent MFMAs.  A zero scale keeps the chain's previous one and its
+// group's operands are written as zeros, so its contribution vanishes as it
+// should.  Consecutive scales of a chain must keep their ratios and the
+// running sums inside the fp32 range (true for any real checkpoint).
+#include <type_traits>
+
 #include "tf_common.h"
 #include "tf_launch.h"
 
 namespace tf {
 
+typedef float f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
+
 constexpr int kGBM = 256;                        // rows per workgroup tile
 constexpr int kGBN = 128;                        // columns per workgroup tile
 constexpr int kGBlocks = kGBN / kBlockCols;      // 8 packed blocks
 constexpr int kStage = 64;                       // k rows per pipeline stage
+constexpr int kSlice = 16;                       // k rows per 32x32x16 MFMA
 constexpr int kAStages = 3;
 constexpr int kAStageBytes = kGBM * kStage * 2;  // 32 KiB
 constexpr int kBStageBytes = kGBN * kStage * 2;  // 16 KiB
@@ -46,13 +57,19 @@ constexpr int kMetaWaveBytes = 256;              // record bytes DMA'd per wave 
 constexpr int kMetaBufBytes = kGWaves * kMetaWaveBytes;
 constexpr int kOffB = kAStages * kAStageBytes;
 constexpr int kOffCodes = kOffB + 2 * kBStageBytes;
-constexpr int kOffMeta = kOffCodes + 2 * kCodeBufBytes;
-constexpr int kGemmLds = kOffMeta + 2 * kMetaBufBytes; // 148 KiB
+// code buffers: W4 two k-tiles, W8 three stages (each fetched two stages
+// before it is unpacked)
+template <int BITS> constexpr int code_bufs() { return BITS == 8 ? 3 : 2; }
+constexpr int kMetaBufs = 3;                     // records are fetched two k-tiles ahead
+template <int BITS> constexpr int off_meta() { return kOffCodes + code_bufs<BITS>() * kCodeBufBytes; }
+template <int BITS> constexpr int gemm_lds() { return off_meta<BITS>() + kMetaBufs * kMetaBufBytes; } // 150 / 158 KiB
+static_assert(gemm_lds<8>() <= 160 * 1024, "LDS of one CU");
 static_assert(kGBlocks == kGWaves, "one packed block per wave");
 
 // 16-byte unit (row, c) of a [rows][64] bf16 tile, c = 0..7.  Rows are 128
 // bytes, so two share a 256-byte bank line; the XOR with (row / 2) % 8 puts
-// the 16 rows a fragment read touches at one c into 16 distinct bank groups.
+// the 16 rows that 16 consecutive lanes read at one c into 16 distinct bank
+// groups.
 __device__ __forceinline__ int swz(int row, int c) { return (row << 3) + (c ^ ((row >> 1) & 7)); }
 
 // s_waitcnt immediates (gfx9 encoding): vmcnt in bits 3:0 and 15:14, expcnt
@@ -83,9 +100,51 @@ __device__ __forceinline__ void dma4(const void *g, void *lds)
     __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void *)lds, 4, 0, 0);
 }
 
-// kGOneTile: every k-tile is exactly one group (G == 128, or G == K <= 128);
-// kGWhole: every k-tile lies inside one group; kGSplit: G is 32 or 64.
-enum GemmGroups { kGSplit = 0, kGWhole = 1, kGOneTile = 2 };
+__device__ __forceinline__ f32x16 mfma32x32x16(const u32x4 &a, const u32x4 &b, const f32x16 &c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                   0, 0, 0);
+}
+
+// Exact bf16 (q - z) * live of eight W4 codes (rows 0..7 of a column's
+// k-octet in one word).  `lo` / `hi` hold the even / odd nibbles as bytes;
+// the empty asm keeps the compiler from merging the masks into per-value
+// bit-field extracts, so each value is one v_cvt_f32_ubyteN and one fma.
+__device__ __forceinline__ u32x4 unpack_w4(uint32_t w, float live, float nz)
+{
+    uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+    asm volatile("" : "+v"(lo), "+v"(hi));
+    // nibble 2j holds row j/2... see w4_row_shift: rows 0,4,1,5 in lo, 2,6,3,7 in hi
+    const float r0 = fmaf((float)(lo & 0xFFu), live, nz), r4 = fmaf((float)((lo >> 8) & 0xFFu), live, nz);
+    const float r1 = fmaf((float)((lo >> 16) & 0xFFu), live, nz), r5 = fmaf((float)(lo >> 24), live, nz);
+    const float r2 = fmaf((float)(hi & 0xFFu), live, nz), r6 = fmaf((float)((hi >> 8) & 0xFFu), live, nz);
+    const float r3 = fmaf((float)((hi >> 16) & 0xFFu), live, nz), r7 = fmaf((float)(hi >> 24), live, nz);
+    return u32x4{pack_bf16x2(r0, r1), pack_bf16x2(r2, r3), pack_bf16x2(r4, r5), pack_bf16x2(r6, r7)};
+}
+
+// Same for eight W8 codes held in two words (row i in byte i).
+__device__ __forceinline__ u32x4 unpack_w8(uint32_t w0, uint32_t w1, float live, float nz)
+{
+    float f[8];
+    dequant_w8_pair(w0, w1, live, nz, f);
+    return u32x4{pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7])};
+}
+
+// How groups map onto the 16-row slices of the k loop.  kGSplit32/64 and
+// kGOneTile are the slices per group (G = 32, 64, 128); kGWhole covers groups
+// of whole k-tiles (G a multiple of 256, or G == K).
+enum GemmGroups { kGWhole = 0, kGSplit32 = 2, kGSplit64 = 4, kGOneTile = 8 };
+
+template <int V> using ic = std::integral_constant<int, V>;
+
+// f(ic<I>{}), ..., f(ic<N - 1>{}): loop indices usable as constants
+template <int I, int N, typename F> __device__ __forceinline__ void static_for(F &&f)
+{
+    if constexpr (I < N) {
+        f(ic<I>{});
+        static_for<I + 1, N>(f);
+    }
+}
 
 template <int BITS, int kMode>
 __global__ __launch_bounds__(kGThreads, 1) void gemm_kernel(const uint16_t *__restrict__ x,
@@ -95,16 +154,21 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_kernel(const uint16_t *__re
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     constexpr int RB = record_bytes(BITS);
+    constexpr int kSpg = kMode; // slices per group (0: whole k-tiles per group)
+    constexpr bool kSplit = kMode == kGSplit32 || kMode == kGSplit64;
+    constexpr bool one_tile = kMode == kGOneTile;
+    constexpr int kGpt = kSpg ? 8 / kSpg : 1; // groups per k-tile
     // records a k-tile can touch per block (split: up to four 32-row groups)
-    constexpr int kRecs = kMode == kGSplit ? 4 : 1;
+    constexpr int kRecs = kSplit ? 4 : 1;
     constexpr int kBlockMeta = kRecs * RB; // <= 192 bytes: one dword per lane
     static_assert(kBlockMeta <= kMetaWaveBytes, "a block's records fit one dword DMA");
     constexpr bool kW8 = BITS == 8;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave >> 1, wn = wave & 1; // 64-row and 64-column slot of the wave
-    const int r = lane & 15, o = lane >> 4;
+    const int wm = wave >> 1, wn = wave & 1;    // 64-row and 64-column slot of the wave
+    const int r = lane & 15, o = lane >> 4;     // fill: column r of the wave's block, k-octet o
+    const int l32 = lane & 31, h32 = lane >> 5; // MFMA fragments: row / column l32, k-octet h32
 
     // ---- tile order: consecutive tiles on one XCD share a column tile ----
     const int nwg = gridDim.x, bid = blockIdx.x;
@@ -117,270 +181,362 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_kernel(const uint16_t *__re
     const int ktiles = (int)lay.ktiles;
     const int nstages = 2 * ktiles;
     const int steps = (int)lay.steps;
-    const int sg = (int)(lay.G / kStepRows); // 32-row steps per group
     const int64_t K = lay.K;
-    const bool one_tile = kMode == kGOneTile;
 
     uint8_t *const sA = lds;
     uint8_t *const sB = lds + kOffB;
     uint8_t *const sCodes = lds + kOffCodes;
-    uint8_t *const sMeta = lds + kOffMeta;
+    uint8_t *const sMeta = lds + off_meta<BITS>();
 
-    // ---- activations: wave w fills rows 32w .. 32w+31 of a stage, 8 rows per
-    //      instruction; lane p takes row 8j + p/8 and the 16-byte unit that the
-    //      swizzle places at slot p%8. ----
-    const int a_row_in = lane >> 3, a_slot = lane & 7;
-    // rows 32w + 8j + p/8 (j = 0..3), clamped at M - 1: the lane's base row
-    // and 32-bit element offsets of the other three from it
-    const uint16_t *a_base;
-    int a_off[4];
-    {
-        const int64_t row0 = m0 + 32 * wave + a_row_in;
-        const int64_t g0 = row0 < M ? row0 : M - 1; // rows past M are computed on a copy, never stored
-        a_base = x + g0 * K;
+    // ---- activations.  Wave w fills rows 32w .. 32w+31 of a stage, 8 rows
+    //      per instruction j; lane p takes row 8j + p/8 and the 16-byte unit c
+    //      that the swizzle places at slot p%8.  The address is a wave-uniform
+    //      base (row 32w of the tile, clamped at M - 1, plus the stage's k) and
+    //      a 32-bit lane offset; rows past M read row M - 1 (computed, never
+    //      stored). ----
+    const int a_slot = lane & 7;
+    const int a_c[2] = {a_slot ^ ((lane >> 4) & 7), a_slot ^ ((4 + (lane >> 4)) & 7)}; // unit for even / odd j
+    const int64_t a_row_base = m0 + 32 * wave < M ? m0 + 32 * wave : M - 1;
+    const uint8_t *const a_gbase = reinterpret_cast<const uint8_t *>(x) + a_row_base * K * 2;
+    uint32_t a_voff[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            int64_t gm = row0 + 8 * j;
-            gm = gm < M ? gm : M - 1;
-            a_off[j] = (int)((gm - g0) * K);
-        }
+    for (int j = 0; j < 4; ++j) {
+        int64_t row = m0 + 32 * wave + 8 * j + (lane >> 3);
+        row = row < M ? row : M - 1;
+        a_voff[j] = (uint32_t)((row - a_row_base) * K * 2 + 16 * a_c[j & 1]);
     }
-    // swizzle slot -> unit: (row / 2) % 8 is (4 (j % 2) + p / 16) % 8
-    const int a_c8e = 8 * (a_slot ^ ((a_row_in >> 1) & 7));
-    const int a_c8o = 8 * (a_slot ^ ((4 + (a_row_in >> 1)) & 7));
-    auto dma_a = [&](int s) {
+    // instructions j0 .. j1 - 1 of the four that fill the wave's rows of stage s
+    auto dma_a = [&](int s, int j0, int j1) {
         uint8_t *dst = sA + (s % kAStages) * kAStageBytes + 32 * wave * 128;
+        const uint8_t *src = a_gbase + (int64_t)s * kStage * 2;
+        if (s * kStage + kStage <= (int)K) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            int64_t k = (int64_t)s * kStage + ((j & 1) ? a_c8o : a_c8e);
-            k = k < K ? k : 0; // rows past K meet zero weights
-            dma16(a_base + a_off[j] + k, dst + j * 1024);
+            for (int j = j0; j < j1; ++j)
+                dma16(src + a_voff[j], dst + j * 1024);
+        } else {
+            // a last stage that runs past K: those units read column 0 of
+            // their row instead (the rows past K meet zero weights).  The
+            // offsets are taken from the row base so none is negative.
+#pragma unroll
+            for (int j = j0; j < j1; ++j) {
+                const uint32_t col0 = a_voff[j] - 16 * a_c[j & 1]; // (row - row base) * 2K >= 0
+                const uint32_t v = s * kStage + 8 * a_c[j & 1] >= (int)K ? col0 : a_voff[j] + (uint32_t)s * kStage * 2;
+                dma16(a_gbase + v, dst + j * 1024);
+            }
         }
     };
-    // codes: wave w fetches block w (1 KiB; W8: one half tile)
+    // ---- codes: wave w fetches block w (1 KiB per k-tile; W8: per half) ----
     const int64_t my_blk = blk0 + wave < lay.nblocks ? blk0 + wave : 0; // blocks past N: any valid block
+    const uint8_t *const blk_base = packed + my_blk * lay.block_bytes;
     auto dma_codes = [&](int t, int half, int buf) {
-        const uint8_t *src =
-            packed + my_blk * lay.block_bytes + lay.meta_bytes + (int64_t)t * tile_bytes(BITS) + 1024 * half + 16 * lane;
-        dma16(src, sCodes + buf * kCodeBufBytes + wave * 1024);
+        const uint8_t *src = blk_base + lay.meta_bytes + (int64_t)t * tile_bytes(BITS) + 1024 * half;
+        dma16(src + 16 * lane, sCodes + buf * kCodeBufBytes + wave * 1024);
     };
-    // records of k-tile t for block w, as dwords
+    // ---- records of k-tile t for block w, as dwords, into the buffer of
+    //      k-tile tb (tb % 3); lanes past the records read the block's first
+    //      dword ----
     auto first_group = [&](int t) -> int64_t { return one_tile ? t : ((int64_t)t * kTileRows) / lay.G; };
-    auto dma_meta = [&](int t, int buf) {
+    auto dma_meta = [&](int t, int tb) {
         const int64_t g_first = first_group(t);
         const int64_t g = g_first + (4 * lane) / RB;
         const bool ok = lane < kBlockMeta / 4 && g < lay.ngroups;
-        const uint8_t *src = ok ? packed + my_blk * lay.block_bytes + g_first * RB + 4 * lane : packed;
-        dma4(src, sMeta + buf * kMetaBufBytes + wave * kMetaWaveBytes);
+        const uint32_t v = ok ? (uint32_t)(g_first * RB + 4 * lane) : 0u;
+        dma4(blk_base + v, sMeta + (tb % kMetaBufs) * kMetaBufBytes + wave * kMetaWaveBytes);
     };
     // the staged record of block bb (0..7) for group g, which k-tile t touches
     auto meta_rec = [&](int bb, int t, int64_t g) -> const uint8_t * {
-        const uint8_t *rec = sMeta + (t & 1) * kMetaBufBytes + bb * kMetaWaveBytes;
+        const uint8_t *rec = sMeta + (t % kMetaBufs) * kMetaBufBytes + bb * kMetaWaveBytes;
         return one_tile ? rec : rec + (int)(g - first_group(t)) * RB;
     };
-    auto code_buf = [&](int s) { return kW8 ? (s & 1) : ((s >> 1) & 1); };
-
-    // ---- unpack stage sd into B buffer sd % 2: exact bf16 (q - z), zero where
-    //      the row is past K or the group's scale is 0.  Columns past N need
-    //      no care: their outputs are never stored.  Wave w unpacks block w;
-    //      lane (o, r) column r, rows 32 kk + 8 o .. +7.  Split in two so the
-    //      LDS reads are issued early and the arithmetic overlaps MFMAs. ----
-    struct FillIn {
-        u32x4 cw;        // the lane's code words
-        float sv[2];     // scale per 32-row step
-        uint32_t z[2];   // zero point per 32-row step
+    auto code_buf = [&](int s) { return kW8 ? s % 3 : (s >> 1) & 1; };
+    // group of 32-row step `step`
+    auto group_of_step = [&](int step) -> int64_t {
+        return one_tile ? step >> 2 : ((int64_t)step * kStepRows) / lay.G;
     };
+
+    // ---- unpack stage sd into B buffer sd % 2 as exact bf16 (q - z), zero
+    //      where the row is past K or the group's scale is 0.  Columns past N
+    //      need no care: their outputs are never stored.  Wave w unpacks block
+    //      w; lane (o, r) column r, rows 32 kk + 8 o .. +7.  A B buffer is
+    //      k-octet major ([8][128] units of 16 bytes), so fragment reads and
+    //      these writes touch 256 contiguous bytes per 16 lanes and every
+    //      offset but the lane's own is an immediate. ----
+    struct FillIn {
+        u32x2 cw;      // the lane's code words for this stage (W8: 4 words in cw, cw8)
+        u32x2 cw8;
+        float sv[2];   // scale per 32-row step
+        uint32_t z[2]; // zero point per 32-row step
+    };
+    const uint8_t *const code_lane = sCodes + wave * 1024 + 16 * lane;
     auto fill_load = [&](int sd, FillIn &in) {
         const int td = sd >> 1, hd = sd & 1;
-        const uint8_t *codes = sCodes + code_buf(sd) * kCodeBufBytes + wave * 1024 + 16 * lane;
+        const uint8_t *codes = code_lane + code_buf(sd) * kCodeBufBytes;
         if constexpr (kW8) {
-            in.cw = *reinterpret_cast<const u32x4 *>(codes);
+            const u32x4 c4 = *reinterpret_cast<const u32x4 *>(codes);
+            in.cw = u32x2{c4[0], c4[1]};
+            in.cw8 = u32x2{c4[2], c4[3]};
         } else {
-            const u32x2 c2 = *reinterpret_cast<const u32x2 *>(codes + 8 * hd);
-            in.cw = u32x4{c2[0], c2[1], 0u, 0u};
+            in.cw = *reinterpret_cast<const u32x2 *>(codes + 8 * hd);
         }
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
             const int step = 4 * td + 2 * hd + kk;
-            const int64_t g = one_tile ? td : (int64_t)step / sg;
-            const uint8_t *rec = meta_rec(wave, td, g);
+            const uint8_t *rec = meta_rec(wave, td, group_of_step(step));
             in.sv[kk] = record_scale<BITS>(rec, r);
             in.z[kk] = record_zero<BITS>(rec, r);
         }
     };
-    auto fill_store = [&](int sd, const FillIn &in) {
-        const int td = sd >> 1, hd = sd & 1;
-        uint8_t *dst = sB + (sd & 1) * kBStageBytes;
+    uint8_t *const fill_lane = sB + o * 2048 + (16 * wave + r) * 16;
+    // 32-row step kk (0, 1) of stage sd
+    auto fill_store = [&](int sd, const FillIn &in, auto kk_c) {
+        constexpr int kk = decltype(kk_c)::value;
+        const int step = 4 * (sd >> 1) + 2 * (sd & 1) + kk;
+        // (q - z) * live as fma(q, live, -z * live): the mask costs nothing
+        const float live = (step < steps && in.sv[kk] != 0.f) ? 1.f : 0.f;
+        const float nz = -(float)in.z[kk] * live;
+        u32x4 v;
+        if constexpr (kW8)
+            v = kk == 0 ? unpack_w8(in.cw[0], in.cw[1], live, nz) : unpack_w8(in.cw8[0], in.cw8[1], live, nz);
+        else
+            v = unpack_w4(in.cw[kk], live, nz);
+        *reinterpret_cast<u32x4 *>(fill_lane + (sd & 1) * kBStageBytes + kk * 8192) = v;
+    };
+
+    // ---- scales of the lane's two columns: column l32 of the 32-column tiles
+    //      j = 0, 1 of the wave, i.e. column r of block 4 wn + 2 j + l32 / 16;
+    //      groups past K (slices after the last row) read as 0 ----
+    auto scales_of = [&](int64_t g, int t, float (&sc)[2]) {
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            const int step = 4 * td + 2 * hd + kk;
-            // (q - z) * live as fma(q, live, -z * live): the mask costs nothing
-            const float live = (step < steps && in.sv[kk] != 0.f) ? 1.f : 0.f;
-            const float nz = -(float)in.z[kk] * live;
-            float f[8];
-            if constexpr (kW8)
-                dequant_w8_pair(in.cw[2 * kk], in.cw[2 * kk + 1], live, nz, f);
-            else
-                dequant_w4_word(in.cw[kk], live, nz, f);
-            const u32x4 v = {pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
-                             pack_bf16x2(f[6], f[7])};
-            *reinterpret_cast<u32x4 *>(dst + 16 * swz(16 * wave + r, 4 * kk + o)) = v;
+        for (int j = 0; j < 2; ++j) {
+            const float v = record_scale<BITS>(meta_rec(4 * wn + 2 * j + (l32 >> 4), t, g), r);
+            sc[j] = g < lay.ngroups ? v : 0.f;
         }
     };
 
-    // ---- scales of the lane's four columns (blocks 4 wn + j, column r) ----
-    auto scales_of = [&](int64_t g, int t, float (&s)[4]) {
+    // ---- accumulator chains (even / odd groups) and their current scales ----
+    f32x16 acc[2][2][2];
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            s[j] = record_scale<BITS>(meta_rec(4 * wn + j, t, g), r);
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int e = 0; e < 16; ++e)
+                    acc[c][i][j][e] = 0.f;
+    float s_last[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
+    float ratio[2] = {1.f, 1.f}; // of the chain being folded
+    // chain C moves on to group g when `ok`: ratio s_last / s_g (a zero
+    // scale keeps s_last); otherwise the ratio is exactly 1.  The records are
+    // read either way (in bounds), so there is no branch.
+    auto start_fold = [&](auto c_c, int64_t g, int t, bool ok) {
+        constexpr int C = decltype(c_c)::value;
+        float sn[2];
+        scales_of(g, t, sn);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const float se = ok && sn[j] != 0.f ? sn[j] : s_last[C][j];
+            const float rt = s_last[C][j] * __builtin_amdgcn_rcpf(se);
+            ratio[j] = ok ? rt : 1.f;
+            s_last[C][j] = se;
+        }
+    };
+    // first group of chain C: its own scale (1 if zero: the chain stays 0)
+    auto start_chain = [&](auto c_c, int64_t g, int t) {
+        constexpr int C = decltype(c_c)::value;
+        float sn[2];
+        scales_of(g, t, sn);
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            s_last[C][j] = sn[j] != 0.f ? sn[j] : 1.f;
+    };
+    // chunk CH of NC of chain C times the ratio (element f = 16 (2 i + j) + e)
+    auto fold_chunk = [&](auto c_c, auto ch_c, auto nc_c) {
+        constexpr int C = decltype(c_c)::value, CH = decltype(ch_c)::value, NC = decltype(nc_c)::value;
+#pragma unroll
+        for (int f = CH * 64 / NC; f < (CH + 1) * 64 / NC; ++f) {
+            const int i = f >> 5, j = (f >> 4) & 1, e = f & 15;
+            acc[C][i][j][e] *= ratio[j];
+        }
     };
 
-    f32x4 acc[4][4];
+    // ---- fragment reads.  A: the swizzled unit (row, 2 sl + h32) of the
+    //      lane's row in sub-tile i, one offset per (slice, i) precomputed;
+    //      B: unit (2 sl + h32, column) of the k-octet major buffer. ----
+    int a_rd[4][2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int sl = 0; sl < 4; ++sl)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float seff[4];
+        for (int i = 0; i < 2; ++i)
+            a_rd[sl][i] = 16 * swz(64 * wm + 32 * i + l32, 2 * sl + h32);
+    const uint8_t *b_rd[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+        b_rd[j] = sB + h32 * 2048 + (64 * wn + 32 * j + l32) * 16;
+    auto read_frags = [&](const uint8_t *a_st, int hb, int sl, u32x4 (&af)[2], u32x4 (&bf)[2]) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            af[i] = *reinterpret_cast<const u32x4 *>(a_st + a_rd[sl][i]);
+            bf[i] = *reinterpret_cast<const u32x4 *>(b_rd[i] + hb * kBStageBytes + sl * 4096);
+        }
+    };
 
-    // ---- prologue: k-tile 0's codes and records, stages 0 and 1 of x ----
-    dma_codes(0, 0, 0);
+    // ---- prologue.  What stage 0 and the loop's first unpack need (records
+    //      of k-tiles 0 and 1, codes of k-tile 0, x of stage 0) is waited for
+    //      here; x of stage 1 and the next codes are waited for at the end of
+    //      stage 0, like every load the loop issues (nstages >= 2). ----
     dma_meta(0, 0);
-    dma_a(0);
-    if (nstages > 1) {
-        if (kW8)
-            dma_codes(0, 1, 1);
-        dma_a(1);
-        wait_vmcnt<4>();
-    } else {
-        wait_vmcnt<0>();
-    }
+    dma_meta(ktiles > 1 ? 1 : 0, 1);
+    dma_codes(0, 0, 0);
+    if (kW8)
+        dma_codes(0, 1, 1);
+    dma_a(0, 0, 4);
+    dma_a(1, 0, 4);
+    if (kW8)
+        dma_codes(ktiles > 1 ? 1 : 0, ktiles > 1 ? 0 : 1, 2); // stage 2
+    else
+        dma_codes(ktiles > 1 ? 1 : 0, 0, 1);
+    wait_vmcnt<5>();
     lds_barrier();
     {
         FillIn f0;
         fill_load(0, f0);
-        fill_store(0, f0);
-        float s0[4];
-        scales_of(0, 0, s0);
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            seff[j] = s0[j] != 0.f ? s0[j] : 1.f;
+        fill_store(0, f0, ic<0>{});
+        fill_store(0, f0, ic<1>{});
     }
+    // the chains' first groups: 0 and 1 (one-tile groups: k-tiles 0 and 1)
+    start_chain(ic<0>{}, 0, 0);
+    if constexpr (kMode != kGWhole)
+        start_chain(ic<1>{}, 1, one_tile ? 1 : 0);
     wait_lgkmcnt0();
     lds_barrier();
 
-    for (int t = 0; t < ktiles; ++t)
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const int s = 2 * t + h;
-        // ---- loads for later stages: codes and records first, x last.  Past
-        //      the end they re-read the last stage into slots nobody reads, so
-        //      every stage issues the same loads. ----
-        const int tn = t + 1 < ktiles ? t + 1 : ktiles - 1;
-        const int sa = s + 2 < nstages ? s + 2 : nstages - 1;
-        if (kW8)
-            dma_codes(sa >> 1, sa & 1, s & 1);
-        else if (h == 0)
-            dma_codes(tn, 0, (t + 1) & 1);
-        if (h == 0)
-            dma_meta(tn, (t + 1) & 1);
-        dma_a(sa);
+    // ---- one k-tile (two stages of four slices).  PAR is the chain of
+    //      one-tile groups (group t is chain t % 2). ----
+    auto ktile = [&](int t, auto par_c) {
+        constexpr int PAR = decltype(par_c)::value;
+        static_for<0, 2>([&](auto h_c) {
+            constexpr int h = decltype(h_c)::value;
+            const int s = 2 * t + h;
+            // ---- loads for later stages, each waited for at the end of the
+            //      next stage: x two stages ahead, then codes (W4: k-tile
+            //      t + 2 into the buffer of k-tile t, which stage 2t + 1 no
+            //      longer reads; W8: stage s + 3 into the buffer of stage s)
+            //      and records (k-tile t + 2 into the buffer of k-tile t - 1).
+            //      Past the end they re-read the last stage into buffers
+            //      nobody reads, so every stage issues the same loads.  They
+            //      and the unpack of the next stage are spread over the four
+            //      slices so that they issue between MFMAs. ----
+            const int sa = s + 2 < nstages ? s + 2 : nstages - 1;
+            const int t2 = t + 2 < ktiles ? t + 2 : ktiles - 1;
+            const uint8_t *a_st = sA + (s % kAStages) * kAStageBytes;
+            u32x4 af[2][2], bf[2][2]; // fragments of two slices in flight
+            FillIn fin;               // the next stage's codes and records
+            read_frags(a_st, h, 0, af[0], bf[0]);
 
-        // ---- the next stage's codes and records (past the last stage this
-        //      reads and later writes buffers nobody reads) ----
-        FillIn fin;
-        fill_load(s + 1, fin);
-
-        // ---- MFMAs of stage s ----
-        const uint8_t *a_st = sA + (s % kAStages) * kAStageBytes;
-        const uint8_t *b_st = sB + h * kBStageBytes;
-        // one-tile groups: the stage that ends k-tile t ends group t; fold in
-        // s_t / s_{t+1} row tile by row tile right after each one's MFMAs
-        const bool fold_here = one_tile && h == 1;
-        float ratio[4];
-        if (fold_here) {
-            float sn[4];
-            scales_of(tn, tn, sn);
-            const bool more = t + 1 < ktiles;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                // computed unconditionally (the asm pins it) so the last
-                // k-tile's select stays a select, not a branch
-                const float se = sn[j] != 0.f ? sn[j] : seff[j];
-                float rt = seff[j] * __builtin_amdgcn_rcpf(se);
-                asm volatile("" : "+v"(rt));
-                ratio[j] = more ? rt : 1.f;
-                seff[j] = more ? se : seff[j];
-            }
-        }
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            const int step = 4 * t + 2 * h + kk;
-            u32x4 bf[4], af[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                bf[j] = *reinterpret_cast<const u32x4 *>(b_st + 16 * swz(64 * wn + 16 * j + r, 4 * kk + o));
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                af[i] = *reinterpret_cast<const u32x4 *>(a_st + 16 * swz(64 * wm + 16 * i + r, 4 * kk + o));
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    acc[i][j] = mfma16x16x32(af[i], bf[j], acc[i][j]);
-                    if (fold_here && kk == 1) {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            acc[i][j][e] *= ratio[j];
+            static_for<0, 4>([&](auto sl_c) {
+                constexpr int sl = decltype(sl_c)::value;
+                constexpr int cur = sl & 1;
+                constexpr int sig = 4 * h + sl; // slice within the k-tile
+                if constexpr (sl + 1 < 4)
+                    read_frags(a_st, h, sl + 1, af[cur ^ 1], bf[cur ^ 1]);
+                if constexpr (sl == 0) {
+                    dma_a(sa, 0, 2);
+                } else if constexpr (sl == 1) {
+                    dma_a(sa, 2, 4);
+                    fill_load(s + 1, fin);
+                } else if constexpr (sl == 2) {
+                    if constexpr (kW8) {
+                        const int sc = s + 3 < nstages ? s + 3 : nstages - 1;
+                        dma_codes(sc >> 1, sc & 1, s % 3);
+                    } else if constexpr (h == 1) {
+                        dma_codes(t2, 0, t & 1);
                     }
+                    if constexpr (h == 0)
+                        dma_meta(t2, t + 2);
+                    fill_store(s + 1, fin, ic<0>{});
+                } else {
+                    fill_store(s + 1, fin, ic<1>{});
                 }
-            }
-            // group boundary after this step: rescale by s_g / s_{g+1}
-            if (!one_tile && (step + 1) % sg == 0 && step + 1 < steps) {
-                const int64_t gn = (int64_t)(step + 1) / sg;
-                const int tg = (step + 1) >> 2; // k-tile holding the next group's first step
-                float sn[4], rt[4];
-                scales_of(gn, tg, sn);
+                if constexpr (kMode == kGWhole) {
+                    // groups of whole k-tiles: chain 0 only, folded at the end
+                    // of each group (the next group's records are staged)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const float se = sn[j] != 0.f ? sn[j] : seff[j];
-                    rt[j] = seff[j] * __builtin_amdgcn_rcpf(se);
-                    seff[j] = se;
+                    for (int i = 0; i < 2; ++i)
+#pragma unroll
+                        for (int j = 0; j < 2; ++j)
+                            acc[0][i][j] = mfma32x32x16(af[cur][i], bf[cur][j], acc[0][i][j]);
+                    if (sig == 7 && (t + 1) % (int)lay.tiles_per_group == 0 && t + 1 < ktiles) {
+                        start_fold(ic<0>{}, (int64_t)(t + 1) / lay.tiles_per_group, t + 1, true);
+                        fold_chunk(ic<0>{}, ic<0>{}, ic<1>{});
+                    }
+                } else {
+                    constexpr int pos = sig % kSpg;               // slice within its group
+                    constexpr int gin = sig / kSpg;               // group within the k-tile
+                    constexpr int C = one_tile ? PAR : (gin & 1); // chain of this group
+                    constexpr int F = C ^ 1;                      // chain folded meanwhile
+                    // chain F (group g - 1) moves on to group g + 1, whose
+                    // records sit in this k-tile or the next one
+                    if constexpr (pos == 0) {
+                        const int64_t g = first_group(t) + gin;
+                        constexpr int tn_off = (gin + 1) / kGpt; // 0 or 1
+                        start_fold(ic<F>{}, g + 1, t + tn_off, g >= 1 && g + 1 < lay.ngroups);
+                    }
+#pragma unroll
+                    for (int i = 0; i < 2; ++i)
+#pragma unroll
+                        for (int j = 0; j < 2; ++j)
+                            acc[C][i][j] = mfma32x32x16(af[cur][i], bf[cur][j], acc[C][i][j]);
+                    fold_chunk(ic<F>{}, ic<pos>{}, ic<kSpg>{});
                 }
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j)
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            acc[i][j][e] *= rt[j];
-            }
+            });
+
+            // ---- everything issued before this stage has landed (stage
+            //      s + 1's x, the next codes and records); only this stage's
+            //      loads may still be in flight ----
+            if constexpr (kW8 && h == 0)
+                wait_vmcnt<6>();
+            else
+                wait_vmcnt<5>();
+            wait_lgkmcnt0();
+            lds_barrier();
+        });
+    };
+
+    if constexpr (one_tile) {
+        int t = 0;
+        for (; t + 1 < ktiles; t += 2) {
+            ktile(t, ic<0>{});
+            ktile(t + 1, ic<1>{});
         }
-
-        // ---- unpack the next stage's weights into the other B buffer ----
-        fill_store(s + 1, fin);
-
-        // ---- stage s + 1's x (issued one stage ago) must have landed: only
-        //      this stage's four x loads may still be in flight ----
-        wait_vmcnt<4>();
-        wait_lgkmcnt0();
-        lds_barrier();
+        if (t < ktiles)
+            ktile(t, ic<0>{});
+    } else {
+        for (int t = 0; t < ktiles; ++t)
+            ktile(t, ic<0>{});
     }
     wait_vmcnt<0>();
 
-    // ---- epilogue: y = acc * s_last, fp32 -> bf16 (nearest even) ----
+    // ---- epilogue: y = chain_0 * s_0' + chain_1 * s_1', fp32 -> bf16
+    //      (nearest even).  Element e of a 32x32 accumulator is row
+    //      8 (e / 4) + 4 h32 + e % 4, column l32. ----
     const int64_t n0 = (int64_t)nt * kGBN;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int j = 0; j < 2; ++j) {
+        const int64_t col = n0 + 64 * wn + 32 * j + l32;
+        if (col >= lay.N)
+            continue;
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int i = 0; i < 2; ++i)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int64_t row = m0 + 64 * wm + 16 * i + 4 * o + e;
-                const int64_t col = n0 + 64 * wn + 16 * j + r;
-                if (row < M && col < lay.N)
-                    y[row * lay.N + col] = f32_to_bf16_bits(acc[i][j][e] * seff[j]);
+            for (int e = 0; e < 16; ++e) {
+                const int64_t row = m0 + 64 * wm + 32 * i + 8 * (e >> 2) + 4 * h32 + (e & 3);
+                const float v = kMode == kGWhole ? acc[0][i][j][e] * s_last[0][j]
+                                                 : fmaf(acc[0][i][j][e], s_last[0][j], acc[1][i][j][e] * s_last[1][j]);
+                if (row < M)
+                    y[row * lay.N + col] = f32_to_bf16_bits(v);
             }
+    }
 }
 
 // The kernel needs more than the default 64 KiB of dynamic LDS; raise the
@@ -390,9 +546,9 @@ template <int BITS, int kMode> static void launch_mode(dim3 grid, hipStream_t st
                                                        int m_tiles)
 {
     static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(&gemm_kernel<BITS, kMode>),
-                                                       hipFuncAttributeMaxDynamicSharedMemorySize, kGemmLds);
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, gemm_lds<BITS>());
     (void)attr;
-    gemm_kernel<BITS, kMode><<<grid, kGThreads, kGemmLds, stream>>>(x, pk, y, lay, M, m_tiles);
+    gemm_kernel<BITS, kMode><<<grid, kGThreads, gemm_lds<BITS>(), stream>>>(x, pk, y, lay, M, m_tiles);
 }
 
 hipError_t launch_gemm(int bits, const uint16_t *x, const void *packed, uint16_t *y, int64_t M, const Layout &lay,
@@ -402,22 +558,23 @@ hipError_t launch_gemm(int bits, const uint16_t *x, const void *packed, uint16_t
     const int64_t n_tiles = (lay.N + kGBN - 1) / kGBN;
     const dim3 grid((unsigned)(m_tiles * n_tiles));
     const uint8_t *pk = static_cast<const uint8_t *>(packed);
-    const int mode = lay.tiles_per_group == 1 ? kGOneTile : lay.whole_tiles() ? kGWhole : kGSplit;
-    if (bits == 4) {
-        if (mode == kGOneTile)
-            launch_mode<4, kGOneTile>(grid, stream, x, pk, y, lay, M, (int)m_tiles);
-        else if (mode == kGWhole)
-            launch_mode<4, kGWhole>(grid, stream, x, pk, y, lay, M, (int)m_tiles);
-        else
-            launch_mode<4, kGSplit>(grid, stream, x, pk, y, lay, M, (int)m_tiles);
-    } else {
-        if (mode == kGOneTile)
-            launch_mode<8, kGOneTile>(grid, stream, x, pk, y, lay, M, (int)m_tiles);
-        else if (mode == kGWhole)
-            launch_mode<8, kGWhole>(grid, stream, x, pk, y, lay, M, (int)m_tiles);
-        else
-            launch_mode<8, kGSplit>(grid, stream, x, pk, y, lay, M, (int)m_tiles);
-    }
+    const int mode = lay.tiles_per_group == 1 ? kGOneTile
+                     : lay.whole_tiles()      ? kGWhole
+                     : lay.G == 32            ? kGSplit32
+                                              : kGSplit64;
+    auto go = [&](auto bits_c) {
+        constexpr int B = decltype(bits_c)::value;
+        switch (mode) {
+        case kGOneTile: launch_mode<B, kGOneTile>(grid, stream, x, pk, y, lay, M, (int)m_tiles); break;
+        case kGWhole: launch_mode<B, kGWhole>(grid, stream, x, pk, y, lay, M, (int)m_tiles); break;
+        case kGSplit32: launch_mode<B, kGSplit32>(grid, stream, x, pk, y, lay, M, (int)m_tiles); break;
+        default: launch_mode<B, kGSplit64>(grid, stream, x, pk, y, lay, M, (int)m_tiles); break;
+        }
+    };
+    if (bits == 4)
+        go(ic<4>{});
+    else
+        go(ic<8>{});
     return hipGetLastError();
 }
 
