@@ -3,7 +3,10 @@
 Headline (value): W4A16 GEMV at M=1 over one Llama-style decoder layer's seven
 linears (q/o 4096x4096, k/v 4096x1024, gate/up 4096x14336, down 14336x4096,
 group 128), as effective HBM GB/s = algorithmic bytes / time.  A step is one
-pass over the seven GEMVs, replayed as a HIP graph; steps rotate over weight
+pass over the layer's linears with q/k/v fused into one N=6144 GEMV and
+gate/up into one N=28672 GEMV, as serving engines store them (four launches),
+replayed as a HIP graph; the seven separate launches are timed beside it.
+Steps rotate over weight
 replicas whose total (5 x 113 MB) exceeds twice the 256 MB Infinity Cache, so
 every step streams its weights from HBM.  Inputs are resident in HBM before
 the timed region starts.
@@ -80,7 +83,7 @@ def stage_layer(torch, q, synth, M):
         del qw, qz, sc
         x = torch.from_numpy(c.x.view(np.int16)).to(dev).view(torch.bfloat16)
         y = torch.empty((M, c.N), dtype=torch.bfloat16, device=dev)
-        lins.append(dict(name=c.name, K=c.K, N=c.N, G=c.G, M=M, packed=packed, x=x, y=y,
+        lins.append(dict(name=c.name, sid=sid, K=c.K, N=c.N, G=c.G, M=M, packed=packed, x=x, y=y,
                          bytes=algorithmic_bytes(4, M, c.K, c.N, c.G)))
     torch.cuda.synchronize()
     return lins
@@ -184,13 +187,43 @@ def queue_filler(torch, ms):
     return a
 
 
-def bench_gemv(torch, q, args):
+def fuse_layer(torch, q, lins):
+    """The layer as serving engines lay it out: q, k, v fused into one N=6144
+    projection and gate, up into one N=28672 projection (the same weights and
+    bytes, four launches instead of seven).  The packed format is block-major
+    with self-contained 16-column blocks, so the fused buffer is the
+    concatenation of the per-linear buffers; that is checked here against a
+    repack of the concatenated AWQ checkpoint."""
+    import numpy as np
+
     import synth
 
-    lins = stage_layer(torch, q, synth, M=1)
-    layer_bytes = sum(l["bytes"] for l in lins)
-    packed_bytes = sum(l["packed"].numel() for l in lins)
-    R = args.replicas or max(2, -(-2 * INFINITY_CACHE_BYTES // packed_bytes) + 1)
+    by = {l["name"].split("_")[2]: l for l in lins}
+    groups = [("qkv", ["q", "k", "v"]), ("o", ["o"]), ("gate_up", ["gate", "up"]), ("down", ["down"])]
+    fused = []
+    for name, parts in groups:
+        ls = [by[p] for p in parts]
+        K, G, M = ls[0]["K"], ls[0]["G"], ls[0]["M"]
+        N = sum(l["N"] for l in ls)
+        packed = torch.cat([l["packed"] for l in ls]) if len(ls) > 1 else ls[0]["packed"]
+        if len(ls) > 1 and name == "qkv":
+            cs = [synth.make_case(1, l["sid"], M, keep_codes=False) for l in ls]
+            dev = "cuda:0"
+            qw = torch.from_numpy(np.concatenate([c.qweight for c in cs], axis=1).view(np.int32)).to(dev)
+            qz = torch.from_numpy(np.concatenate([c.qzeros for c in cs], axis=1).view(np.int32)).to(dev)
+            sc = torch.from_numpy(np.concatenate([c.scales for c in cs], axis=1).view(np.int16)).to(dev)
+            assert torch.equal(q.tf_repack_w4(qw, qz, sc, K, N, G), packed), "fused repack differs from concatenation"
+            del qw, qz, sc
+        y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda:0")
+        fused.append(dict(name=name, K=K, N=N, G=G, M=M, packed=packed, x=ls[0]["x"], y=y,
+                          bytes=algorithmic_bytes(4, M, K, N, G)))
+    torch.cuda.synchronize()
+    return fused
+
+
+def time_graphs(torch, q, lins, args, R):
+    """Graph replays of one pass over `lins`, rotating over R weight replicas;
+    returns (ms per pass, eager ms per pass, per-launch mean us)."""
     replicas = [[l["packed"] for l in lins]]
     for _ in range(R - 1):
         replicas.append([p.clone() for p in replicas[0]])
@@ -259,11 +292,28 @@ def bench_gemv(torch, q, args):
     torch.cuda.synchronize()
     del keep
     mean_us = [1e3 * e0.elapsed_time(e1) / n_prof for e0, e1 in evs]
+    del replicas, graphs
+    return ms_step, eager_ms, mean_us
+
+
+def bench_gemv(torch, q, args):
+    import synth
+
+    lins = stage_layer(torch, q, synth, M=1)
+    layer_bytes = sum(l["bytes"] for l in lins)
+    packed_bytes = sum(l["packed"].numel() for l in lins)
+    R = args.replicas or max(2, -(-2 * INFINITY_CACHE_BYTES // packed_bytes) + 1)
+
+    # headline: the fused four-launch layer; beside it the seven separate launches
+    fused = fuse_layer(torch, q, lins)
+    assert abs(sum(f["bytes"] for f in fused) - layer_bytes) < 2 * 2 * (4096 + 4096 + 14336), "fusion changed the bytes"
+    ms_f, eager_f, us_f = time_graphs(torch, q, fused, args, R)
+    ms_s, eager_s, us_s = time_graphs(torch, q, lins, args, R)
 
     # the roofline's per-launch duration: the timed region (graph replays and
     # the events around them share torch's current stream) over its launches
-    avg_launch_us = ms_step * 1e3 / len(lins)
-    achieved = layer_bytes / len(lins) / (avg_launch_us * 1e-6) / 1e9
+    avg_launch_us = ms_f * 1e3 / len(fused)
+    achieved = layer_bytes / len(fused) / (avg_launch_us * 1e-6) / 1e9
 
     traffic = None
     if os.path.exists(COUNTERS_FILE):
@@ -272,16 +322,20 @@ def bench_gemv(torch, q, args):
         if cnt.get("kernel_source_hash") == kernel_source_hash():
             traffic = cnt.get("hbm_bytes_per_launch")
 
-    value = layer_bytes / (ms_step * 1e-3) / 1e9
+    def rows(ls, us):
+        return [dict(name=l["name"].replace("c1_layer_", "").replace("_M1", ""), K=l["K"], N=l["N"],
+                     us=round(u, 3), gbs=round(l["bytes"] / (u * 1e-6) / 1e9, 1)) for l, u in zip(ls, us)]
+
+    value = layer_bytes / (ms_f * 1e-3) / 1e9
     return dict(
-        value=value, ms_step=ms_step, eager_ms=eager_ms, replicas=R, layer_bytes=layer_bytes,
-        per_linear=[dict(name=l["name"].replace("c1_layer_", "").replace("_M1", ""), K=l["K"], N=l["N"],
-                         us=round(u, 3), gbs=round(l["bytes"] / (u * 1e-6) / 1e9, 1))
-                    for l, u in zip(lins, mean_us)],
+        value=value, ms_step=ms_f, eager_ms=eager_f, replicas=R, layer_bytes=layer_bytes,
+        per_launch=rows(fused, us_f),
+        separate=dict(ms_per_step=round(ms_s, 5), gbs=round(layer_bytes / (ms_s * 1e-3) / 1e9, 1),
+                      eager_ms_per_step=round(eager_s, 4), per_linear=rows(lins, us_s)),
         roofline=dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                       frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic,
                       kernel="gemv_kernel (tf_gemv_w4a16, W4, one k-tile per group)",
-                      bytes_per_launch=round(layer_bytes / len(lins)),
+                      bytes_per_launch=round(layer_bytes / len(fused)),
                       avg_launch_us=round(avg_launch_us, 3)),
     )
 
@@ -308,14 +362,14 @@ def bench_gemm(torch, q, args):
     torch.cuda.synchronize()
     out = []
     for s in shapes:
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(args.gemm_iters)]
-        for e0, e1 in evs:
-            e0.record()
+        # back-to-back launches between one event pair: throughput per launch
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.gemm_iters):
             q.tf_gemm_w4a16(s["x"], s["packed"], s["K"], s["N"], s["G"], y=s["y"])
-            e1.record()
+        e1.record()
         torch.cuda.synchronize()
-        us = 1e3 * sum(e0.elapsed_time(e1) for e0, e1 in evs) / len(evs)
+        us = 1e3 * e0.elapsed_time(e1) / args.gemm_iters
         fl = 2.0 * s["M"] * s["K"] * s["N"]
         out.append(dict(M=s["M"], K=s["K"], N=s["N"], us=round(us, 2), tflops=round(fl / (us * 1e-6) / 1e12, 1)))
     tot_fl = sum(2.0 * o["M"] * o["K"] * o["N"] for o in out)
@@ -358,8 +412,9 @@ def main():
         "ms_per_step": None, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "W4A16 GEMV, M=1, one Llama-style decoder layer (q/o 4096x4096, k/v 4096x1024, "
-                               "gate/up 4096x14336, down 14336x4096), group 128, HIP-graph replay, "
-                               "weights rotating over replicas larger than twice the Infinity Cache",
+                               "gate/up 4096x14336, down 14336x4096), group 128; q/k/v fused into one N=6144 "
+                               "launch and gate/up into one N=28672 launch (four launches per step), HIP-graph "
+                               "replay, weights rotating over replicas larger than twice the Infinity Cache",
                    "global_batch": 1, "parallelism": "none (1 GPU)"},
     }
     if args.only in ("all", "gemv"):
@@ -368,8 +423,9 @@ def main():
         line["ms_per_step"] = round(gv["ms_step"], 5)
         line["config"].update(replicas=gv["replicas"], layer_bytes=int(gv["layer_bytes"]))
         line["roofline"] = gv["roofline"]
-        line["gemv_detail"] = dict(eager_ms_per_step=round(gv["eager_ms"], 4), per_linear=gv["per_linear"],
-                                   frac_of_hbm_peak=round(gv["value"] / HBM_PEAK_GBS, 4))
+        line["gemv_detail"] = dict(eager_ms_per_step=round(gv["eager_ms"], 4), per_launch=gv["per_launch"],
+                                   frac_of_hbm_peak=round(gv["value"] / HBM_PEAK_GBS, 4),
+                                   seven_separate_launches=gv["separate"])
     if args.only in ("all", "gemm"):
         line["gemm"] = bench_gemm(torch, q, args)
     if args.only == "all" and not args.no_cpu:
