@@ -43,10 +43,15 @@ def algorithmic_bytes(bits, M, K, N, G):
     return K * N * bits // 8 + (K // G) * N * (bits // 8 if bits == 8 else 0.5) + (K // G) * N * 2 + 2 * M * (K + N)
 
 
+GEMV_SOURCES = ("gemv.hip", "tf_common.h", "tf_launch.h")
+
+
 def kernel_source_hash():
+    """Hash of the GEMV kernel's sources: stored counters are used only while
+    the kernel they were taken on is unchanged."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "quantized_linear_layers_awq_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in GEMV_SOURCES:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
@@ -64,6 +69,9 @@ def parse():
                    help="no GPU: read four rocprofv3 --pmc output directories (FETCH_SIZE and WRITE_SIZE over "
                         "'--only gemv', then over '--only copy') and write the per-launch HBM traffic file")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--no-separate", action="store_true",
+                   help="time only the fused four-launch layer (counter passes: every GEMV dispatch is one "
+                        "of the four launches the roofline is computed over)")
     p.add_argument("--gemm-iters", type=int, default=20)
     return p.parse_args()
 
@@ -165,7 +173,8 @@ def write_counters(dirs):
     fetch_scale = COPY_BYTES / (cf_kib * 1024)
     write_scale = COPY_BYTES / (cw_kib * 1024)
     hbm = f_kib * 1024 * fetch_scale + w_kib * 1024 * write_scale
-    out = dict(kernel_source_hash=kernel_source_hash(), kernel="gemv_kernel (tf_gemv_w4a16), 7 layer linears",
+    out = dict(kernel_source_hash=kernel_source_hash(),
+               kernel="gemv_kernel (tf_gemv_w4a16), the four launches of the fused layer step",
                fetch_kib_per_launch=round(f_kib, 1), write_kib_per_launch=round(w_kib, 1),
                dispatches=dict(fetch=nf, write=nw),
                copy_calibration=dict(bytes=COPY_BYTES, fetch_kib=round(cf_kib, 1), write_kib=round(cw_kib, 1),
@@ -308,7 +317,8 @@ def bench_gemv(torch, q, args):
     fused = fuse_layer(torch, q, lins)
     assert abs(sum(f["bytes"] for f in fused) - layer_bytes) < 2 * 2 * (4096 + 4096 + 14336), "fusion changed the bytes"
     ms_f, eager_f, us_f = time_graphs(torch, q, fused, args, R)
-    ms_s, eager_s, us_s = time_graphs(torch, q, lins, args, R)
+    if not args.no_separate:
+        ms_s, eager_s, us_s = time_graphs(torch, q, lins, args, R)
 
     # the roofline's per-launch duration: the timed region (graph replays and
     # the events around them share torch's current stream) over its launches
@@ -330,8 +340,9 @@ def bench_gemv(torch, q, args):
     return dict(
         value=value, ms_step=ms_f, eager_ms=eager_f, replicas=R, layer_bytes=layer_bytes,
         per_launch=rows(fused, us_f),
-        separate=dict(ms_per_step=round(ms_s, 5), gbs=round(layer_bytes / (ms_s * 1e-3) / 1e9, 1),
-                      eager_ms_per_step=round(eager_s, 4), per_linear=rows(lins, us_s)),
+        separate=None if args.no_separate else dict(
+            ms_per_step=round(ms_s, 5), gbs=round(layer_bytes / (ms_s * 1e-3) / 1e9, 1),
+            eager_ms_per_step=round(eager_s, 4), per_linear=rows(lins, us_s)),
         roofline=dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                       frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic,
                       kernel="gemv_kernel (tf_gemv_w4a16, W4, one k-tile per group)",
