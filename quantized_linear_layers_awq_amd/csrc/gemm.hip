@@ -48,6 +48,10 @@ constexpr int kGBlocks = kGBN / kBlockCols;      // 8 packed blocks
 constexpr int kStage = 64;                       // k rows per pipeline stage
 constexpr int kSlice = 16;                       // k rows per 32x32x16 MFMA
 constexpr int kAStages = 3;
+// Row tiles per band of the tile order: with two, the 32 workgroups an XCD runs
+// at once cover 2 activation panels x 16 weight column tiles (measured best of
+// 1, 2, 4 and all).
+constexpr int kBand = 2;
 constexpr int kAStageBytes = kGBM * kStage * 2;  // 32 KiB
 constexpr int kBStageBytes = kGBN * kStage * 2;  // 16 KiB
 constexpr int kCodeBufBytes = kGBlocks * 1024;   // codes of one k-tile (W4) or stage (W8)
@@ -170,11 +174,19 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_kernel(const uint16_t *__re
     const int r = lane & 15, o = lane >> 4;     // fill: column r of the wave's block, k-octet o
     const int l32 = lane & 31, h32 = lane >> 5; // MFMA fragments: row / column l32, k-octet h32
 
-    // ---- tile order: consecutive tiles on one XCD share a column tile ----
+    // ---- tile order: each XCD (workgroups bid % 8) takes a contiguous range
+    //      of tiles, enumerated in bands of kBand row tiles: within a band,
+    //      consecutive tiles walk its rows first, then the columns, so the
+    //      workgroups an XCD runs at once share a few activation panels and
+    //      each weight column tile ----
     const int nwg = gridDim.x, bid = blockIdx.x;
     const int xcd = bid & 7, local = bid >> 3, q8 = nwg >> 3, rem = nwg & 7;
     const int tile = xcd < rem ? xcd * (q8 + 1) + local : rem * (q8 + 1) + (xcd - rem) * q8 + local;
-    const int nt = tile / m_tiles, mt = tile - nt * m_tiles;
+    const int n_tiles = nwg / m_tiles;
+    const int band_rows = kBand > 0 && kBand < m_tiles ? kBand : m_tiles;
+    const int band = tile / (band_rows * n_tiles), in_band = tile - band * band_rows * n_tiles;
+    const int rows_here = m_tiles - band * band_rows < band_rows ? m_tiles - band * band_rows : band_rows;
+    const int nt = in_band / rows_here, mt = band * band_rows + (in_band - (in_band / rows_here) * rows_here);
     const int64_t m0 = (int64_t)mt * kGBM;
     const int64_t blk0 = (int64_t)nt * kGBlocks;
 
