@@ -145,6 +145,20 @@ int tf_dequant_w4_f32(const void *packed, size_t packed_bytes, float *w,
 int tf_dequant_w8_f32(const void *packed, size_t packed_bytes, float *w,
                       int64_t K, int64_t N, int64_t G, void *stream);
 
+/* Test hooks of the GEMM's launch plan (host only, no GPU work).
+ * The GEMM covers y with 256-row x 128-column tiles and, when the tiles are
+ * not a whole number of rounds over the device's compute units, runs the
+ * columns of the last partial round as 256 x 64 tiles in a second launch.
+ * The plan never changes the result's bits.
+ *   tf_gemm_plan: writes out[0] = row tiles, out[1] = 128-column tiles,
+ *     out[2] = 64-column tiles for (M, N) on a device of `cus` compute
+ *     units.  TF_ERR_NULL / TF_ERR_SHAPE (M, N or cus < 1) on bad input.
+ *   tf_gemm_set_planning_cus: makes later GEMM calls of this process plan
+ *     for n compute units instead of the current device's (n <= 0 restores
+ *     the device's).  Process-wide; not meant to race with GEMM calls. */
+int tf_gemm_plan(int64_t M, int64_t N, int cus, int64_t *out);
+void tf_gemm_set_planning_cus(int n);
+
 #ifdef __cplusplus
 }
 #endif

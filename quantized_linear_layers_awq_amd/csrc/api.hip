@@ -186,4 +186,19 @@ int tf_dequant_w8_f32(const void *packed, size_t nbytes, float *w, int64_t K, in
     return dequant(8, packed, nbytes, w, K, N, G, stream);
 }
 
+int tf_gemm_plan(int64_t M, int64_t N, int cus, int64_t *out)
+{
+    if (!out)
+        return TF_ERR_NULL;
+    if (M < 1 || N < 1 || cus < 1 || M > (int64_t(1) << 30) || N >= kDimLimit)
+        return TF_ERR_SHAPE;
+    const tf::GemmPlan p = tf::plan_gemm(M, N, cus);
+    out[0] = p.m_tiles;
+    out[1] = p.wide_cols;
+    out[2] = p.narrow_cols;
+    return TF_OK;
+}
+
+void tf_gemm_set_planning_cus(int n) { tf::set_planning_cus(n); }
+
 } // extern "C"

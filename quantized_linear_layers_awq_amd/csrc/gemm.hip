@@ -33,6 +33,16 @@
 // group's operands are written as zeros, so its contribution vanishes as it
 // should.  Consecutive scales of a chain must keep their ratios and the
 // running sums inside the fp32 range (true for any real checkpoint).
+//
+// Launch plan.  A grid whose 256 x 128 tiles are not a whole number of
+// rounds over the compute units would end with a partial round in which the
+// other CUs idle.  When the columns of that last round fit one round as
+// 256 x 64 tiles, the launcher runs the whole rounds with wide tiles and those
+// columns with narrow tiles in a second launch (eight waves of 32 x 64; only
+// four of them fetch and unpack weights).  Every output element is still
+// computed by one workgroup with the same operations in the same order, so
+// the plan does not change a single bit of the result.
+#include <atomic>
 #include <type_traits>
 
 #include "tf_common.h"
@@ -43,8 +53,6 @@ namespace tf {
 typedef float f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
 
 constexpr int kGBM = 256;                        // rows per workgroup tile
-constexpr int kGBN = 128;                        // columns per workgroup tile
-constexpr int kGBlocks = kGBN / kBlockCols;      // 8 packed blocks
 constexpr int kStage = 64;                       // k rows per pipeline stage
 constexpr int kSlice = 16;                       // k rows per 32x32x16 MFMA
 constexpr int kAStages = 3;
@@ -53,22 +61,27 @@ constexpr int kAStages = 3;
 // 1, 2, 4 and all).
 constexpr int kBand = 2;
 constexpr int kAStageBytes = kGBM * kStage * 2;  // 32 KiB
-constexpr int kBStageBytes = kGBN * kStage * 2;  // 16 KiB
-constexpr int kCodeBufBytes = kGBlocks * 1024;   // codes of one k-tile (W4) or stage (W8)
-constexpr int kGWaves = 8;                       // waves per workgroup (4 x 2 over the tile)
+constexpr int kGWaves = 8;                       // waves per workgroup
 constexpr int kGThreads = 64 * kGWaves;
-constexpr int kMetaWaveBytes = 256;              // record bytes DMA'd per wave (one block) per k-tile
-constexpr int kMetaBufBytes = kGWaves * kMetaWaveBytes;
+constexpr int kMetaWaveBytes = 256;              // record bytes DMA'd per block per k-tile
 constexpr int kOffB = kAStages * kAStageBytes;
-constexpr int kOffCodes = kOffB + 2 * kBStageBytes;
+// Tile widths: WN = 2 is the 256 x 128 tile (waves 4 x 2, 64 x 64 each), WN =
+// 1 the 256 x 64 tile (waves 8 x 1, 32 x 64 each) that fills the last
+// partial round of a grid.  Per width: columns, packed blocks, bytes of one
+// dequantized B stage and of one buffer of codes.
+constexpr int tile_cols(int wn) { return 64 * wn; }
+constexpr int tile_blocks(int wn) { return 4 * wn; }
+constexpr int bstage_bytes(int wn) { return tile_cols(wn) * kStage * 2; } // 16 / 8 KiB
+constexpr int codebuf_bytes(int wn) { return tile_blocks(wn) * 1024; }    // one k-tile (W4) or stage (W8)
+constexpr int metabuf_bytes(int wn) { return tile_blocks(wn) * kMetaWaveBytes; }
+constexpr int off_codes(int wn) { return kOffB + 2 * bstage_bytes(wn); }
 // code buffers: W4 two k-tiles, W8 three stages (each fetched two stages
 // before it is unpacked)
-template <int BITS> constexpr int code_bufs() { return BITS == 8 ? 3 : 2; }
+constexpr int code_bufs(int bits) { return bits == 8 ? 3 : 2; }
 constexpr int kMetaBufs = 3;                     // records are fetched two k-tiles ahead
-template <int BITS> constexpr int off_meta() { return kOffCodes + code_bufs<BITS>() * kCodeBufBytes; }
-template <int BITS> constexpr int gemm_lds() { return off_meta<BITS>() + kMetaBufs * kMetaBufBytes; } // 150 / 158 KiB
-static_assert(gemm_lds<8>() <= 160 * 1024, "LDS of one CU");
-static_assert(kGBlocks == kGWaves, "one packed block per wave");
+constexpr int off_meta(int bits, int wn) { return off_codes(wn) + code_bufs(bits) * codebuf_bytes(wn); }
+constexpr int gemm_lds(int bits, int wn) { return off_meta(bits, wn) + kMetaBufs * metabuf_bytes(wn); } // <= 158 KiB
+static_assert(gemm_lds(8, 2) <= 160 * 1024, "LDS of one CU");
 
 // 16-byte unit (row, c) of a [rows][64] bf16 tile, c = 0..7.  Rows are 128
 // bytes, so two share a 256-byte bank line; the XOR with (row / 2) % 8 puts
@@ -150,12 +163,19 @@ template <int I, int N, typename F> __device__ __forceinline__ void static_for(F
     }
 }
 
-template <int BITS, int kMode>
+// The workgroup grid covers m_tiles row tiles x (gridDim.x / m_tiles) column
+// tiles of width 64 WN, starting at output column col0.
+template <int BITS, int kMode, int WN>
 __global__ __launch_bounds__(kGThreads, 1) void gemm_kernel(const uint16_t *__restrict__ x,
                                                             const uint8_t *__restrict__ packed,
                                                             uint16_t *__restrict__ y, Layout lay, int64_t M,
-                                                            int m_tiles)
+                                                            int m_tiles, int64_t col0)
 {
+    constexpr int kGBN = tile_cols(WN), kGBlocks = tile_blocks(WN);
+    constexpr int kBStageBytes = bstage_bytes(WN), kCodeBufBytes = codebuf_bytes(WN);
+    constexpr int kMetaBufBytes = metabuf_bytes(WN);
+    constexpr int kBOct = kGBN * 16; // bytes per k-octet row of a dequantized B stage
+    constexpr int MI = WN;           // 32-row MFMA tiles per wave (wave rows: 32 MI)
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     constexpr int RB = record_bytes(BITS);
     constexpr int kSpg = kMode; // slices per group (0: whole k-tiles per group)
@@ -170,7 +190,8 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_kernel(const uint16_t *__re
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave >> 1, wn = wave & 1;    // 64-row and 64-column slot of the wave
+    const int wm = wave / WN, wn = wave % WN;   // 32 MI-row and 64-column slot of the wave
+    const bool unpacker = WN == 2 || wave < kGBlocks; // waves that fetch and unpack a packed block
     const int r = lane & 15, o = lane >> 4;     // fill: column r of the wave's block, k-octet o
     const int l32 = lane & 31, h32 = lane >> 5; // MFMA fragments: row / column l32, k-octet h32
 
@@ -188,7 +209,7 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_kernel(const uint16_t *__re
     const int rows_here = m_tiles - band * band_rows < band_rows ? m_tiles - band * band_rows : band_rows;
     const int nt = in_band / rows_here, mt = band * band_rows + (in_band - (in_band / rows_here) * rows_here);
     const int64_t m0 = (int64_t)mt * kGBM;
-    const int64_t blk0 = (int64_t)nt * kGBlocks;
+    const int64_t blk0 = (col0 >> 4) + (int64_t)nt * kGBlocks;
 
     const int ktiles = (int)lay.ktiles;
     const int nstages = 2 * ktiles;
@@ -197,8 +218,8 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_kernel(const uint16_t *__re
 
     uint8_t *const sA = lds;
     uint8_t *const sB = lds + kOffB;
-    uint8_t *const sCodes = lds + kOffCodes;
-    uint8_t *const sMeta = lds + off_meta<BITS>();
+    uint8_t *const sCodes = lds + off_codes(WN);
+    uint8_t *const sMeta = lds + off_meta(BITS, WN);
 
     // ---- activations.  Wave w fills rows 32w .. 32w+31 of a stage, 8 rows
     //      per instruction j; lane p takes row 8j + p/8 and the 16-byte unit c
@@ -237,7 +258,9 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_kernel(const uint16_t *__re
             }
         }
     };
-    // ---- codes: wave w fetches block w (1 KiB per k-tile; W8: per half) ----
+    // ---- codes: wave w < kGBlocks fetches block w (1 KiB per k-tile; W8:
+    //      per half).  Only these waves fetch codes and records and unpack;
+    //      the others (the 64-column tile's waves 4 .. 7) load x only. ----
     const int64_t my_blk = blk0 + wave < lay.nblocks ? blk0 + wave : 0; // blocks past N: any valid block
     const uint8_t *const blk_base = packed + my_blk * lay.block_bytes;
     auto dma_codes = [&](int t, int half, int buf) {
@@ -298,7 +321,7 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_kernel(const uint16_t *__re
             in.z[kk] = record_zero<BITS>(rec, r);
         }
     };
-    uint8_t *const fill_lane = sB + o * 2048 + (16 * wave + r) * 16;
+    uint8_t *const fill_lane = sB + o * kBOct + (16 * wave + r) * 16;
     // 32-row step kk (0, 1) of stage sd
     auto fill_store = [&](int sd, const FillIn &in, auto kk_c) {
         constexpr int kk = decltype(kk_c)::value;
@@ -311,7 +334,7 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_kernel(const uint16_t *__re
             v = kk == 0 ? unpack_w8(in.cw[0], in.cw[1], live, nz) : unpack_w8(in.cw8[0], in.cw8[1], live, nz);
         else
             v = unpack_w4(in.cw[kk], live, nz);
-        *reinterpret_cast<u32x4 *>(fill_lane + (sd & 1) * kBStageBytes + kk * 8192) = v;
+        *reinterpret_cast<u32x4 *>(fill_lane + (sd & 1) * kBStageBytes + kk * 4 * kBOct) = v;
     };
 
     // ---- scales of the lane's two columns: column l32 of the 32-column tiles
@@ -326,11 +349,11 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_kernel(const uint16_t *__re
     };
 
     // ---- accumulator chains (even / odd groups) and their current scales ----
-    f32x16 acc[2][2][2];
+    f32x16 acc[2][MI][2];
 #pragma unroll
     for (int c = 0; c < 2; ++c)
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < MI; ++i)
 #pragma unroll
             for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -365,8 +388,9 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_kernel(const uint16_t *__re
     // chunk CH of NC of chain C times the ratio (element f = 16 (2 i + j) + e)
     auto fold_chunk = [&](auto c_c, auto ch_c, auto nc_c) {
         constexpr int C = decltype(c_c)::value, CH = decltype(ch_c)::value, NC = decltype(nc_c)::value;
+        constexpr int NE = 32 * MI; // accumulator elements per lane and chain
 #pragma unroll
-        for (int f = CH * 64 / NC; f < (CH + 1) * 64 / NC; ++f) {
+        for (int f = CH * NE / NC; f < (CH + 1) * NE / NC; ++f) {
             const int i = f >> 5, j = (f >> 4) & 1, e = f & 15;
             acc[C][i][j][e] *= ratio[j];
         }
@@ -375,42 +399,49 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_kernel(const uint16_t *__re
     // ---- fragment reads.  A: the swizzled unit (row, 2 sl + h32) of the
     //      lane's row in sub-tile i, one offset per (slice, i) precomputed;
     //      B: unit (2 sl + h32, column) of the k-octet major buffer. ----
-    int a_rd[4][2];
+    int a_rd[4][MI];
 #pragma unroll
     for (int sl = 0; sl < 4; ++sl)
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
-            a_rd[sl][i] = 16 * swz(64 * wm + 32 * i + l32, 2 * sl + h32);
+        for (int i = 0; i < MI; ++i)
+            a_rd[sl][i] = 16 * swz(32 * MI * wm + 32 * i + l32, 2 * sl + h32);
     const uint8_t *b_rd[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j)
-        b_rd[j] = sB + h32 * 2048 + (64 * wn + 32 * j + l32) * 16;
-    auto read_frags = [&](const uint8_t *a_st, int hb, int sl, u32x4 (&af)[2], u32x4 (&bf)[2]) {
+        b_rd[j] = sB + h32 * kBOct + (64 * wn + 32 * j + l32) * 16;
+    auto read_frags = [&](const uint8_t *a_st, int hb, int sl, u32x4 (&af)[MI], u32x4 (&bf)[2]) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
+        for (int i = 0; i < MI; ++i)
             af[i] = *reinterpret_cast<const u32x4 *>(a_st + a_rd[sl][i]);
-            bf[i] = *reinterpret_cast<const u32x4 *>(b_rd[i] + hb * kBStageBytes + sl * 4096);
-        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            bf[j] = *reinterpret_cast<const u32x4 *>(b_rd[j] + hb * kBStageBytes + sl * 2 * kBOct);
     };
 
     // ---- prologue.  What stage 0 and the loop's first unpack need (records
     //      of k-tiles 0 and 1, codes of k-tile 0, x of stage 0) is waited for
     //      here; x of stage 1 and the next codes are waited for at the end of
     //      stage 0, like every load the loop issues (nstages >= 2). ----
-    dma_meta(0, 0);
-    dma_meta(ktiles > 1 ? 1 : 0, 1);
-    dma_codes(0, 0, 0);
-    if (kW8)
-        dma_codes(0, 1, 1);
+    if (unpacker) {
+        dma_meta(0, 0);
+        dma_meta(ktiles > 1 ? 1 : 0, 1);
+        dma_codes(0, 0, 0);
+        if (kW8)
+            dma_codes(0, 1, 1);
+    }
     dma_a(0, 0, 4);
     dma_a(1, 0, 4);
-    if (kW8)
-        dma_codes(ktiles > 1 ? 1 : 0, ktiles > 1 ? 0 : 1, 2); // stage 2
-    else
-        dma_codes(ktiles > 1 ? 1 : 0, 0, 1);
-    wait_vmcnt<5>();
+    if (unpacker) {
+        if (kW8)
+            dma_codes(ktiles > 1 ? 1 : 0, ktiles > 1 ? 0 : 1, 2); // stage 2
+        else
+            dma_codes(ktiles > 1 ? 1 : 0, 0, 1);
+        wait_vmcnt<5>();
+    } else {
+        wait_vmcnt<4>();
+    }
     lds_barrier();
-    {
+    if (unpacker) {
         FillIn f0;
         fill_load(0, f0);
         fill_store(0, f0, ic<0>{});
@@ -442,7 +473,7 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_kernel(const uint16_t *__re
             const int sa = s + 2 < nstages ? s + 2 : nstages - 1;
             const int t2 = t + 2 < ktiles ? t + 2 : ktiles - 1;
             const uint8_t *a_st = sA + (s % kAStages) * kAStageBytes;
-            u32x4 af[2][2], bf[2][2]; // fragments of two slices in flight
+            u32x4 af[2][MI], bf[2][2]; // fragments of two slices in flight
             FillIn fin;               // the next stage's codes and records
             read_frags(a_st, h, 0, af[0], bf[0]);
 
@@ -456,25 +487,29 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_kernel(const uint16_t *__re
                     dma_a(sa, 0, 2);
                 } else if constexpr (sl == 1) {
                     dma_a(sa, 2, 4);
-                    fill_load(s + 1, fin);
+                    if (unpacker)
+                        fill_load(s + 1, fin);
                 } else if constexpr (sl == 2) {
-                    if constexpr (kW8) {
-                        const int sc = s + 3 < nstages ? s + 3 : nstages - 1;
-                        dma_codes(sc >> 1, sc & 1, s % 3);
-                    } else if constexpr (h == 1) {
-                        dma_codes(t2, 0, t & 1);
+                    if (unpacker) {
+                        if constexpr (kW8) {
+                            const int sc = s + 3 < nstages ? s + 3 : nstages - 1;
+                            dma_codes(sc >> 1, sc & 1, s % 3);
+                        } else if constexpr (h == 1) {
+                            dma_codes(t2, 0, t & 1);
+                        }
+                        if constexpr (h == 0)
+                            dma_meta(t2, t + 2);
+                        fill_store(s + 1, fin, ic<0>{});
                     }
-                    if constexpr (h == 0)
-                        dma_meta(t2, t + 2);
-                    fill_store(s + 1, fin, ic<0>{});
                 } else {
-                    fill_store(s + 1, fin, ic<1>{});
+                    if (unpacker)
+                        fill_store(s + 1, fin, ic<1>{});
                 }
                 if constexpr (kMode == kGWhole) {
                     // groups of whole k-tiles: chain 0 only, folded at the end
                     // of each group (the next group's records are staged)
 #pragma unroll
-                    for (int i = 0; i < 2; ++i)
+                    for (int i = 0; i < MI; ++i)
 #pragma unroll
                         for (int j = 0; j < 2; ++j)
                             acc[0][i][j] = mfma32x32x16(af[cur][i], bf[cur][j], acc[0][i][j]);
@@ -495,7 +530,7 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_kernel(const uint16_t *__re
                         start_fold(ic<F>{}, g + 1, t + tn_off, g >= 1 && g + 1 < lay.ngroups);
                     }
 #pragma unroll
-                    for (int i = 0; i < 2; ++i)
+                    for (int i = 0; i < MI; ++i)
 #pragma unroll
                         for (int j = 0; j < 2; ++j)
                             acc[C][i][j] = mfma32x32x16(af[cur][i], bf[cur][j], acc[C][i][j]);
@@ -505,8 +540,11 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_kernel(const uint16_t *__re
 
             // ---- everything issued before this stage has landed (stage
             //      s + 1's x, the next codes and records); only this stage's
-            //      loads may still be in flight ----
-            if constexpr (kW8 && h == 0)
+            //      loads may still be in flight (x: 4, codes and records: 1
+            //      or 2 on the unpacking waves) ----
+            if (!unpacker)
+                wait_vmcnt<4>();
+            else if constexpr (kW8 && h == 0)
                 wait_vmcnt<6>();
             else
                 wait_vmcnt<5>();
@@ -532,17 +570,17 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_kernel(const uint16_t *__re
     // ---- epilogue: y = chain_0 * s_0' + chain_1 * s_1', fp32 -> bf16
     //      (nearest even).  Element e of a 32x32 accumulator is row
     //      8 (e / 4) + 4 h32 + e % 4, column l32. ----
-    const int64_t n0 = (int64_t)nt * kGBN;
+    const int64_t n0 = col0 + (int64_t)nt * kGBN;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
         const int64_t col = n0 + 64 * wn + 32 * j + l32;
         if (col >= lay.N)
             continue;
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < MI; ++i)
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                const int64_t row = m0 + 64 * wm + 32 * i + 8 * (e >> 2) + 4 * h32 + (e & 3);
+                const int64_t row = m0 + 32 * MI * wm + 32 * i + 8 * (e >> 2) + 4 * h32 + (e & 3);
                 const float v = kMode == kGWhole ? acc[0][i][j][e] * s_last[0][j]
                                                  : fmaf(acc[0][i][j][e], s_last[0][j], acc[1][i][j][e] * s_last[1][j]);
                 if (row < M)
@@ -553,40 +591,96 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_kernel(const uint16_t *__re
 
 // The kernel needs more than the default 64 KiB of dynamic LDS; raise the
 // limit once per instantiation.
-template <int BITS, int kMode> static void launch_mode(dim3 grid, hipStream_t stream, const uint16_t *x,
-                                                       const uint8_t *pk, uint16_t *y, const Layout &lay, int64_t M,
-                                                       int m_tiles)
+template <int BITS, int kMode, int WN>
+static void launch_mode(int64_t tiles, int m_tiles, int64_t col0, hipStream_t stream, const uint16_t *x,
+                        const uint8_t *pk, uint16_t *y, const Layout &lay, int64_t M)
 {
-    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(&gemm_kernel<BITS, kMode>),
-                                                       hipFuncAttributeMaxDynamicSharedMemorySize, gemm_lds<BITS>());
+    auto kern = &gemm_kernel<BITS, kMode, WN>;
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, gemm_lds(BITS, WN));
     (void)attr;
-    gemm_kernel<BITS, kMode><<<grid, kGThreads, gemm_lds<BITS>(), stream>>>(x, pk, y, lay, M, m_tiles);
+    kern<<<dim3((unsigned)tiles), kGThreads, gemm_lds(BITS, WN), stream>>>(x, pk, y, lay, M, m_tiles, col0);
+}
+
+namespace {
+std::atomic<int> g_planning_cus{0};
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_device_cus[kMaxDevices];
+
+// compute units of the current device (queried once per device)
+int device_cus()
+{
+    if (const int forced = g_planning_cus.load(std::memory_order_relaxed))
+        return forced;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return 256;
+    int n = g_device_cus[dev].load(std::memory_order_relaxed);
+    if (n <= 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        g_device_cus[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+} // namespace
+
+void set_planning_cus(int n) { g_planning_cus.store(n > 0 ? n : 0, std::memory_order_relaxed); }
+
+GemmPlan plan_gemm(int64_t M, int64_t N, int cus)
+{
+    GemmPlan p;
+    p.m_tiles = (M + kGBM - 1) / kGBM;
+    const int64_t n_wide = (N + tile_cols(2) - 1) / tile_cols(2);
+    const int64_t tiles = p.m_tiles * n_wide;
+    p.wide_cols = n_wide; // default: one launch of 128-column tiles
+    p.narrow_cols = 0;
+    if (tiles % cus == 0)
+        return p;
+    // the whole rounds with 128-column tiles, the columns left over as
+    // 64-column tiles when they fit one round (a last partial round of wide
+    // tiles would otherwise leave CUs idle while it runs)
+    const int64_t full = (tiles / cus) * cus;
+    const int64_t wide = full / p.m_tiles < n_wide ? full / p.m_tiles : n_wide;
+    const int64_t rest = N - wide * tile_cols(2);
+    const int64_t narrow = (rest + tile_cols(1) - 1) / tile_cols(1);
+    if (rest > 0 && p.m_tiles * narrow <= cus) {
+        p.wide_cols = wide;
+        p.narrow_cols = narrow;
+    }
+    return p;
 }
 
 hipError_t launch_gemm(int bits, const uint16_t *x, const void *packed, uint16_t *y, int64_t M, const Layout &lay,
                        hipStream_t stream)
 {
-    const int64_t m_tiles = (M + kGBM - 1) / kGBM;
-    const int64_t n_tiles = (lay.N + kGBN - 1) / kGBN;
-    const dim3 grid((unsigned)(m_tiles * n_tiles));
+    const GemmPlan plan = plan_gemm(M, lay.N, device_cus());
     const uint8_t *pk = static_cast<const uint8_t *>(packed);
     const int mode = lay.tiles_per_group == 1 ? kGOneTile
                      : lay.whole_tiles()      ? kGWhole
                      : lay.G == 32            ? kGSplit32
                                               : kGSplit64;
-    auto go = [&](auto bits_c) {
-        constexpr int B = decltype(bits_c)::value;
+    const int mt = (int)plan.m_tiles;
+    auto go = [&](auto bits_c, auto wn_c, int64_t n_cols, int64_t col0) {
+        constexpr int B = decltype(bits_c)::value, WN = decltype(wn_c)::value;
+        const int64_t tiles = plan.m_tiles * n_cols;
         switch (mode) {
-        case kGOneTile: launch_mode<B, kGOneTile>(grid, stream, x, pk, y, lay, M, (int)m_tiles); break;
-        case kGWhole: launch_mode<B, kGWhole>(grid, stream, x, pk, y, lay, M, (int)m_tiles); break;
-        case kGSplit32: launch_mode<B, kGSplit32>(grid, stream, x, pk, y, lay, M, (int)m_tiles); break;
-        default: launch_mode<B, kGSplit64>(grid, stream, x, pk, y, lay, M, (int)m_tiles); break;
+        case kGOneTile: launch_mode<B, kGOneTile, WN>(tiles, mt, col0, stream, x, pk, y, lay, M); break;
+        case kGWhole: launch_mode<B, kGWhole, WN>(tiles, mt, col0, stream, x, pk, y, lay, M); break;
+        case kGSplit32: launch_mode<B, kGSplit32, WN>(tiles, mt, col0, stream, x, pk, y, lay, M); break;
+        default: launch_mode<B, kGSplit64, WN>(tiles, mt, col0, stream, x, pk, y, lay, M); break;
         }
     };
+    auto both = [&](auto bits_c) {
+        if (plan.wide_cols > 0)
+            go(bits_c, ic<2>{}, plan.wide_cols, 0);
+        if (plan.narrow_cols > 0)
+            go(bits_c, ic<1>{}, plan.narrow_cols, plan.wide_cols * tile_cols(2));
+    };
     if (bits == 4)
-        go(ic<4>{});
+        both(ic<4>{});
     else
-        go(ic<8>{});
+        both(ic<8>{});
     return hipGetLastError();
 }
 

@@ -13,6 +13,15 @@ hipError_t launch_dequant_f32(int bits, const void *packed, const Layout &lay, f
 int gemv_waves(const Layout &lay);
 hipError_t launch_gemv(int bits, const uint16_t *x, const void *packed, uint16_t *y, int64_t M, const Layout &lay,
                        hipStream_t stream);
+// How the GEMM covers the output: m_tiles row tiles of 256 rows, then
+// wide_cols column tiles of 128 columns from column 0 in one launch and
+// narrow_cols tiles of 64 columns after them in a second one.
+struct GemmPlan {
+    int64_t m_tiles, wide_cols, narrow_cols;
+};
+GemmPlan plan_gemm(int64_t M, int64_t N, int cus);
+// Compute units plan_gemm assumes (0: the current device's).
+void set_planning_cus(int n);
 hipError_t launch_gemm(int bits, const uint16_t *x, const void *packed, uint16_t *y, int64_t M, const Layout &lay,
                        hipStream_t stream);
 

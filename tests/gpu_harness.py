@@ -88,3 +88,29 @@ def check_linear(case, torch, q, gemm, rows=None, cols=None, packed=None, d=None
     sub = sub if cols is None else sub[:, np.asarray(cols)]
     ok, ratio = within_tolerance(sub, ref)
     return ok, ratio, y
+
+
+class planning_cus:
+    """Within the block, GEMM calls plan their launches for n compute units
+    (n = 1: one launch of 128-column tiles; see tf_gemm_plan)."""
+
+    def __init__(self, q, n):
+        self.q, self.n = q, n
+
+    def __enter__(self):
+        self.q.tf_gemm_set_planning_cus(self.n)
+
+    def __exit__(self, *exc):
+        self.q.tf_gemm_set_planning_cus(0)
+
+
+def split_cus(q, M, N):
+    """A compute-unit count for which the GEMM plan of (M, N) has both wide
+    and narrow tiles, or None if no count gives one."""
+    mt = -(-M // 256)
+    tiles = mt * -(-N // 128)
+    for cus in range(2, tiles + 1):
+        _, wide, narrow = q.tf_gemm_plan(M, N, cus)
+        if wide and narrow:
+            return cus
+    return None

@@ -105,6 +105,46 @@ def test_no_kernel_needs_a_workspace(lib):
         assert lib.tf_workspace_bytes(*args) == 0
 
 
+def _plan(lib, M, N, cus):
+    out = (ctypes.c_int64 * 3)()
+    st = lib.tf_gemm_plan(M, N, cus, out)
+    return st, tuple(out)
+
+
+def test_gemm_plan_covers_every_column_once(lib):
+    """The launch plan: 128-column tiles from column 0, then 64-column tiles,
+    covering [0, N) with no tile wholly past N; the narrow launch exists only
+    when the wide tiles miss a whole number of rounds and fits one round."""
+    rng = __import__("random").Random(7)
+    cases = [(2048, 14336, 256), (2048, 4096, 256), (512, 8192, 256), (1, 8192, 256), (4096, 32768, 256),
+             (1, 64, 256), (300, 24, 256), (513, 1048, 256), (4096, 28672, 304)]
+    cases += [(rng.randint(1, 9000), 8 * rng.randint(1, 5000), rng.choice([1, 2, 3, 7, 64, 80, 256, 304]))
+              for _ in range(400)]
+    for M, N, cus in cases:
+        st, (mt, wide, narrow) = _plan(lib, M, N, cus)
+        assert st == TF_OK
+        n_wide = -(-N // 128)
+        tiles = mt * n_wide
+        assert mt == -(-M // 256)
+        if narrow == 0:
+            assert wide == n_wide
+        else:
+            assert tiles % cus != 0
+            assert wide * 128 < N <= wide * 128 + narrow * 64 < N + 64
+            assert mt * narrow <= cus
+            assert mt * wide <= (tiles // cus) * cus
+    # the headline prefill shape: 3 whole rounds of wide tiles, one of narrow
+    assert _plan(lib, 2048, 14336, 256)[1] == (8, 96, 32)
+    assert _plan(lib, 2048, 4096, 256)[1] == (8, 32, 0)
+
+
+def test_gemm_plan_rejects_bad_input(lib):
+    assert _plan(lib, 0, 64, 256)[0] == TF_ERR_SHAPE
+    assert _plan(lib, 64, 0, 256)[0] == TF_ERR_SHAPE
+    assert _plan(lib, 64, 64, 0)[0] == TF_ERR_SHAPE
+    assert lib.tf_gemm_plan(64, 64, 256, None) == TF_ERR_NULL
+
+
 FAKE = 0x10000  # a 64 KiB-aligned fake device address; never dereferenced
 
 

@@ -6,7 +6,8 @@ import pytest
 
 import oracle
 import synth
-from gpu_harness import bf16_bits, bf16_to_f64, check_linear, gpu_or_skip, linear_fn, repack, to_device
+from gpu_harness import (bf16_bits, bf16_to_f64, check_linear, gpu_or_skip, linear_fn, planning_cus, repack,
+                         split_cus, to_device)
 
 pytestmark = pytest.mark.gpu
 
@@ -38,13 +39,51 @@ def test_gemv_within_tolerance(shape):
     assert ok, f"worst error / bound = {ratio:.3f}"
 
 
+def _plan_cus(q, plan, M, N):
+    """Compute units to plan for: the device's (auto), one (128-column tiles
+    only) or a count that splits the columns between both tile widths."""
+    if plan == "auto":
+        return 0
+    if plan == "wide":
+        return 1
+    cus = split_cus(q, M, N)
+    if cus is None:
+        pytest.skip("no compute-unit count splits this grid")
+    return cus
+
+
+@pytest.mark.parametrize("plan", ["auto", "wide", "split"])
 @pytest.mark.parametrize("shape", GEMM_SHAPES)
-def test_gemm_within_tolerance(shape):
+def test_gemm_within_tolerance(shape, plan):
     torch, q = gpu_or_skip()
-    print(f"gemm {shape}", flush=True)
+    cus = _plan_cus(q, plan, shape[1], shape[3])
+    print(f"gemm {shape} plan={plan} cus={cus} {q.tf_gemm_plan(shape[1], shape[3], cus or 256)}", flush=True)
     c = _case(*shape, seed=2)
-    ok, ratio, _ = check_linear(c, torch, q, gemm=True)
+    with planning_cus(q, cus):
+        ok, ratio, _ = check_linear(c, torch, q, gemm=True)
     assert ok, f"worst error / bound = {ratio:.3f}"
+
+
+@pytest.mark.parametrize("bits,M,K,N,G", [(4, 600, 1024, 1000, 128), (8, 300, 512, 456, 64), (4, 257, 256, 200, 32),
+                                          (8, 40, 1024, 328, 1024)])
+def test_gemm_plans_agree_bitwise(bits, M, K, N, G):
+    """Every tile width computes each output with the same operations in the
+    same order: all launch plans give identical bits."""
+    torch, q = gpu_or_skip()
+    c = _case(bits, M, K, N, G, seed=5)
+    d = to_device(c, torch)
+    pk = repack(c, d, q)
+    f = linear_fn(q, bits, True)
+    outs = {}
+    for cus in (1, split_cus(q, M, N), 10**6):
+        if cus is None:
+            continue
+        print(f"plans W{bits} M={M} K={K} N={N} G={G} cus={cus} {q.tf_gemm_plan(M, N, cus)}", flush=True)
+        with planning_cus(q, cus):
+            outs[cus] = bf16_bits(f(d["x"], pk, K, N, G))
+    ref = outs[1]
+    for cus, y in outs.items():
+        assert np.array_equal(y, ref), f"plan for {cus} CUs differs from the single wide launch"
 
 
 def _integer_case(bits, M, K, N, G, seed):
