@@ -108,13 +108,28 @@ __device__ __forceinline__ void lds_barrier()
 }
 
 // LDS-DMA: lane i's 16 (or 4) bytes land at lds + 16 i (or 4 i).
-__device__ __forceinline__ void dma16(const void *g, void *lds)
+// LDS-DMA loads go through buffer instructions (buffer_load_dword[x4] ...
+// lds) on a raw buffer resource whose base is wave-uniform: lane L's bytes
+// land at lds + size * L.  The buffer form matters: the compiler treats the
+// global-segment form as a flat access that may touch LDS and then drains
+// every outstanding LDS read before it and after it, which would serialise
+// the fragment reads with the MFMAs.
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+__device__ __forceinline__ Rsrc make_rsrc(const void *base)
 {
-    __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void *)lds, 16, 0, 0);
+    // stride 0, no range limit below 4 GiB (offsets are built in bounds),
+    // dword data format (required for the resource to be valid on gfx9)
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, -1, 0x00020000);
 }
-__device__ __forceinline__ void dma4(const void *g, void *lds)
+__device__ __forceinline__ void dma16(Rsrc r, uint32_t voff, uint32_t soff, void *lds)
 {
-    __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void *)lds, 4, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 16, (int)voff,
+                                             (int)soff, 0, 0);
+}
+__device__ __forceinline__ void dma4(Rsrc r, uint32_t voff, uint32_t soff, void *lds)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 4, (int)voff,
+                                             (int)soff, 0, 0);
 }
 
 __device__ __forceinline__ f32x16 mfma32x32x16(const u32x4 &a, const u32x4 &b, const f32x16 &c)
@@ -230,7 +245,7 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_kernel(const uint16_t *__re
     const int a_slot = lane & 7;
     const int a_c[2] = {a_slot ^ ((lane >> 4) & 7), a_slot ^ ((4 + (lane >> 4)) & 7)}; // unit for even / odd j
     const int64_t a_row_base = m0 + 32 * wave < M ? m0 + 32 * wave : M - 1;
-    const uint8_t *const a_gbase = reinterpret_cast<const uint8_t *>(x) + a_row_base * K * 2;
+    const Rsrc a_rsrc = make_rsrc(reinterpret_cast<const uint8_t *>(x) + a_row_base * K * 2);
     uint32_t a_voff[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -238,45 +253,42 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_kernel(const uint16_t *__re
         row = row < M ? row : M - 1;
         a_voff[j] = (uint32_t)((row - a_row_base) * K * 2 + 16 * a_c[j & 1]);
     }
+    // The lane's unit of stage s starts s * 128 bytes into the row; past
+    // a_lim it would leave the row (a last stage that runs past K), so the
+    // offset is clamped there and the unit re-reads the row's last 8 columns
+    // (finite values that meet zero weights).  Branch-free: two VALU per load.
+    const uint32_t a_lim[2] = {(uint32_t)(2 * K - 16 - 16 * a_c[0]), (uint32_t)(2 * K - 16 - 16 * a_c[1])};
     // instructions j0 .. j1 - 1 of the four that fill the wave's rows of stage s
     auto dma_a = [&](int s, int j0, int j1) {
         uint8_t *dst = sA + (s % kAStages) * kAStageBytes + 32 * wave * 128;
-        const uint8_t *src = a_gbase + (int64_t)s * kStage * 2;
-        if (s * kStage + kStage <= (int)K) {
+        const uint32_t ks = (uint32_t)s * kStage * 2;
 #pragma unroll
-            for (int j = j0; j < j1; ++j)
-                dma16(src + a_voff[j], dst + j * 1024);
-        } else {
-            // a last stage that runs past K: those units read column 0 of
-            // their row instead (the rows past K meet zero weights).  The
-            // offsets are taken from the row base so none is negative.
-#pragma unroll
-            for (int j = j0; j < j1; ++j) {
-                const uint32_t col0 = a_voff[j] - 16 * a_c[j & 1]; // (row - row base) * 2K >= 0
-                const uint32_t v = s * kStage + 8 * a_c[j & 1] >= (int)K ? col0 : a_voff[j] + (uint32_t)s * kStage * 2;
-                dma16(a_gbase + v, dst + j * 1024);
-            }
-        }
+        for (int j = j0; j < j1; ++j)
+            dma16(a_rsrc, a_voff[j] + __builtin_elementwise_min(ks, a_lim[j & 1]), 0, dst + j * 1024);
     };
     // ---- codes: wave w < kGBlocks fetches block w (1 KiB per k-tile; W8:
     //      per half).  Only these waves fetch codes and records and unpack;
     //      the others (the 64-column tile's waves 4 .. 7) load x only. ----
     const int64_t my_blk = blk0 + wave < lay.nblocks ? blk0 + wave : 0; // blocks past N: any valid block
-    const uint8_t *const blk_base = packed + my_blk * lay.block_bytes;
+    // one resource per block: a block (records and codes) is below 2^30 bytes
+    const Rsrc blk_rsrc = make_rsrc(packed + my_blk * lay.block_bytes);
     auto dma_codes = [&](int t, int half, int buf) {
-        const uint8_t *src = blk_base + lay.meta_bytes + (int64_t)t * tile_bytes(BITS) + 1024 * half;
-        dma16(src + 16 * lane, sCodes + buf * kCodeBufBytes + wave * 1024);
+        const uint32_t soff = (uint32_t)lay.meta_bytes + (uint32_t)t * tile_bytes(BITS) + 1024u * half;
+        dma16(blk_rsrc, 16 * lane, soff, sCodes + buf * kCodeBufBytes + wave * 1024);
     };
     // ---- records of k-tile t for block w, as dwords, into the buffer of
-    //      k-tile tb (tb % 3); lanes past the records read the block's first
-    //      dword ----
+    //      k-tile tb (tb % 3); lanes past the records, or past the last
+    //      group, read a dword of the block's first record instead ----
     auto first_group = [&](int t) -> int64_t { return one_tile ? t : ((int64_t)t * kTileRows) / lay.G; };
+    // (32-bit: a block's records are below 2^26 bytes; lanes past kBlockMeta
+    // re-read the first record's first dword)
+    const int m_lane = lane < kBlockMeta / 4 ? lane : 0;
+    const int m_grp = (4 * m_lane) / RB;
+    const int ngroups32 = (int)lay.ngroups;
     auto dma_meta = [&](int t, int tb) {
-        const int64_t g_first = first_group(t);
-        const int64_t g = g_first + (4 * lane) / RB;
-        const bool ok = lane < kBlockMeta / 4 && g < lay.ngroups;
-        const uint32_t v = ok ? (uint32_t)(g_first * RB + 4 * lane) : 0u;
-        dma4(blk_base + v, sMeta + (tb % kMetaBufs) * kMetaBufBytes + wave * kMetaWaveBytes);
+        const int g_first = (int)first_group(t);
+        const uint32_t v = g_first + m_grp < ngroups32 ? (uint32_t)(g_first * RB + 4 * m_lane) : 0u;
+        dma4(blk_rsrc, v, 0, sMeta + (tb % kMetaBufs) * kMetaBufBytes + wave * kMetaWaveBytes);
     };
     // the staged record of block bb (0..7) for group g, which k-tile t touches
     auto meta_rec = [&](int bb, int t, int64_t g) -> const uint8_t * {
@@ -297,11 +309,16 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_kernel(const uint16_t *__re
     //      these writes touch 256 contiguous bytes per 16 lanes and every
     //      offset but the lane's own is an immediate. ----
     struct FillIn {
-        u32x2 cw;      // the lane's code words for this stage (W8: 4 words in cw, cw8)
+        u32x2 cw;       // the lane's code words for this stage (W8: 4 words in cw, cw8)
         u32x2 cw8;
-        float sv[2];   // scale per 32-row step
-        uint32_t z[2]; // zero point per 32-row step
+        uint32_t sb[2]; // scale bits per 32-row step
+        uint32_t zb[2]; // byte holding the zero point per 32-row step
     };
+    // Raw loads only: the values are decoded where they are used, so that the
+    // loads can issue well before (the LDS counter is waited for in order).
+    auto scale_bits = [&](const uint8_t *rec) -> uint32_t { return *reinterpret_cast<const uint16_t *>(rec + 2 * r); };
+    auto zero_byte = [&](const uint8_t *rec) -> uint32_t { return rec[32 + (BITS == 4 ? (r >> 1) : r)]; };
+    auto zero_of = [&](uint32_t zb) -> uint32_t { return BITS == 4 ? (zb >> (4 * (r & 1))) & 0xFu : zb; };
     const uint8_t *const code_lane = sCodes + wave * 1024 + 16 * lane;
     auto fill_load = [&](int sd, FillIn &in) {
         const int td = sd >> 1, hd = sd & 1;
@@ -317,8 +334,8 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_kernel(const uint16_t *__re
         for (int kk = 0; kk < 2; ++kk) {
             const int step = 4 * td + 2 * hd + kk;
             const uint8_t *rec = meta_rec(wave, td, group_of_step(step));
-            in.sv[kk] = record_scale<BITS>(rec, r);
-            in.z[kk] = record_zero<BITS>(rec, r);
+            in.sb[kk] = scale_bits(rec);
+            in.zb[kk] = zero_byte(rec);
         }
     };
     uint8_t *const fill_lane = sB + o * kBOct + (16 * wave + r) * 16;
@@ -327,8 +344,8 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_kernel(const uint16_t *__re
         constexpr int kk = decltype(kk_c)::value;
         const int step = 4 * (sd >> 1) + 2 * (sd & 1) + kk;
         // (q - z) * live as fma(q, live, -z * live): the mask costs nothing
-        const float live = (step < steps && in.sv[kk] != 0.f) ? 1.f : 0.f;
-        const float nz = -(float)in.z[kk] * live;
+        const float live = (step < steps && (in.sb[kk] & 0x7FFFu) != 0) ? 1.f : 0.f;
+        const float nz = -(float)zero_of(in.zb[kk]) * live;
         u32x4 v;
         if constexpr (kW8)
             v = kk == 0 ? unpack_w8(in.cw[0], in.cw[1], live, nz) : unpack_w8(in.cw8[0], in.cw8[1], live, nz);
@@ -347,6 +364,17 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_kernel(const uint16_t *__re
             sc[j] = g < lay.ngroups ? v : 0.f;
         }
     };
+    // the same, split into the raw loads and their decoding
+    auto scales_load = [&](int64_t g, int t, uint32_t (&sb)[2]) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            sb[j] = scale_bits(meta_rec(4 * wn + 2 * j + (l32 >> 4), t, g));
+    };
+    auto scales_decode = [&](int64_t g, const uint32_t (&sb)[2], float (&sc)[2]) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            sc[j] = g < lay.ngroups ? __uint_as_float(sb[j] << 16) : 0.f;
+    };
 
     // ---- accumulator chains (even / odd groups) and their current scales ----
     f32x16 acc[2][MI][2];
@@ -364,10 +392,8 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_kernel(const uint16_t *__re
     // chain C moves on to group g when `ok`: ratio s_last / s_g (a zero
     // scale keeps s_last); otherwise the ratio is exactly 1.  The records are
     // read either way (in bounds), so there is no branch.
-    auto start_fold = [&](auto c_c, int64_t g, int t, bool ok) {
+    auto start_fold_with = [&](auto c_c, const float (&sn)[2], bool ok) {
         constexpr int C = decltype(c_c)::value;
-        float sn[2];
-        scales_of(g, t, sn);
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             const float se = ok && sn[j] != 0.f ? sn[j] : s_last[C][j];
@@ -375,6 +401,11 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_kernel(const uint16_t *__re
             ratio[j] = ok ? rt : 1.f;
             s_last[C][j] = se;
         }
+    };
+    auto start_fold = [&](auto c_c, int64_t g, int t, bool ok) {
+        float sn[2];
+        scales_of(g, t, sn);
+        start_fold_with(c_c, sn, ok);
     };
     // first group of chain C: its own scale (1 if zero: the chain stays 0)
     auto start_chain = [&](auto c_c, int64_t g, int t) {
@@ -481,14 +512,35 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_kernel(const uint16_t *__re
                 constexpr int sl = decltype(sl_c)::value;
                 constexpr int cur = sl & 1;
                 constexpr int sig = 4 * h + sl; // slice within the k-tile
+                // ---- LDS reads first, small ones before the fragments, then
+                //      a scheduling fence: the compiler may not sink them to
+                //      their uses, so the next slice's fragments load while
+                //      this slice's MFMAs run, and waiting for the small
+                //      reads never waits for the fragments ----
+                constexpr int spg = kSpg ? kSpg : 8;          // (whole k-tiles: unused)
+                constexpr int pos = sig % spg;                // slice within its group
+                constexpr int gin = sig / spg;                // group within the k-tile
+                constexpr bool fold_start = kMode != kGWhole && pos == 0;
+                uint32_t fold_sb[2];
+                int64_t fold_g = 0;
+                if constexpr (fold_start) {
+                    // chain F (group g - 1) moves on to group g + 1, whose
+                    // records sit in this k-tile or the next one
+                    constexpr int tn_off = (gin + 1) / kGpt; // 0 or 1
+                    fold_g = first_group(t) + gin + 1;
+                    scales_load(fold_g, t + tn_off, fold_sb);
+                }
+                if constexpr (sl == 1) {
+                    if (unpacker)
+                        fill_load(s + 1, fin);
+                }
                 if constexpr (sl + 1 < 4)
                     read_frags(a_st, h, sl + 1, af[cur ^ 1], bf[cur ^ 1]);
+                __builtin_amdgcn_sched_barrier(0);
                 if constexpr (sl == 0) {
                     dma_a(sa, 0, 2);
                 } else if constexpr (sl == 1) {
                     dma_a(sa, 2, 4);
-                    if (unpacker)
-                        fill_load(s + 1, fin);
                 } else if constexpr (sl == 2) {
                     if (unpacker) {
                         if constexpr (kW8) {
@@ -518,16 +570,12 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_kernel(const uint16_t *__re
                         fold_chunk(ic<0>{}, ic<0>{}, ic<1>{});
                     }
                 } else {
-                    constexpr int pos = sig % kSpg;               // slice within its group
-                    constexpr int gin = sig / kSpg;               // group within the k-tile
                     constexpr int C = one_tile ? PAR : (gin & 1); // chain of this group
                     constexpr int F = C ^ 1;                      // chain folded meanwhile
-                    // chain F (group g - 1) moves on to group g + 1, whose
-                    // records sit in this k-tile or the next one
-                    if constexpr (pos == 0) {
-                        const int64_t g = first_group(t) + gin;
-                        constexpr int tn_off = (gin + 1) / kGpt; // 0 or 1
-                        start_fold(ic<F>{}, g + 1, t + tn_off, g >= 1 && g + 1 < lay.ngroups);
+                    if constexpr (fold_start) {
+                        float sn[2];
+                        scales_decode(fold_g, fold_sb, sn);
+                        start_fold_with(ic<F>{}, sn, fold_g >= 2 && fold_g < lay.ngroups);
                     }
 #pragma unroll
                     for (int i = 0; i < MI; ++i)
