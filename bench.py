@@ -4,17 +4,22 @@ Headline (value): W4A16 GEMV at M=1 over one Llama-style decoder layer's seven
 linears (q/o 4096x4096, k/v 4096x1024, gate/up 4096x14336, down 14336x4096,
 group 128), as effective HBM GB/s = algorithmic bytes / time.  A step is one
 pass over the layer's linears with q/k/v fused into one N=6144 GEMV and
-gate/up into one N=28672 GEMV, as serving engines store them (four launches),
-replayed as a HIP graph; the seven separate launches are timed beside it.
-Steps rotate over weight
+gate/up into one N=28672 GEMV, as serving engines store them (four launches).
+The K timed steps are launched eagerly, queued behind filler work so that the
+GPU runs them back to back (kernels on one stream run one after another, so
+each launch sees its predecessor's results, as in a real decode step); HIP
+events on the launch stream bracket them.  HIP-graph replay of the same steps
+and the seven separate launches are timed beside it.  Steps rotate over weight
 replicas whose total (5 x 113 MB) exceeds twice the 256 MB Infinity Cache, so
 every step streams its weights from HBM.  Inputs are resident in HBM before
 the timed region starts.
 
 Also reported: the dominant kernel against its roofline (per-launch durations
 from HIP events on the launch stream), the W4A16 prefill GEMM at M=2048
-(TFLOP/s against the dense bf16 MFMA peak), and the CPU oracle on a bounded
-sample of the headline workload.
+(TFLOP/s against the dense bf16 MFMA peak), the CPU oracle on a bounded
+sample of the headline workload, and two measured practical roofs: a plain
+streaming-read kernel over the same packed buffers in the same launch
+pattern, and back-to-back bf16 MFMAs sustained for as long as the GEMM runs.
 
 Algorithmic bytes of one linear: K*N*b/8 codes + (K/G)*N*(b/8 + 2) metadata
 + 2*M*(K + N) activations in and outputs out.  Flops: 2*M*K*N.
@@ -301,8 +306,66 @@ def time_graphs(torch, q, lins, args, R):
     torch.cuda.synchronize()
     del keep
     mean_us = [1e3 * e0.elapsed_time(e1) / n_prof for e0, e1 in evs]
+
+    # the headline: K eager steps queued behind filler work, one event pair
+    queued_ms = time_queued(torch, lambda i: layer_pass(i % R), args.steps, enqueue_us=host_us_per_step(layer_pass, R))
+    for l, y0 in zip(lins, ref):
+        assert torch.equal(l["y"], y0), "queued eager launches differ from the first result"
+
+    # practical roof: a plain streaming read of the same packed buffers, one
+    # launch per linear, in the same queued pattern
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda:0")
+
+    def read_pass(r):
+        for p in replicas[r]:
+            q.tf_probe_stream_read(p, sink)
+
+    read_ms = time_queued(torch, lambda i: read_pass(i % R), args.steps, enqueue_us=host_us_per_step(read_pass, R))
     del replicas, graphs
-    return ms_step, eager_ms, mean_us
+    return dict(graph_ms=ms_step, host_eager_ms=eager_ms, queued_ms=queued_ms, read_roof_ms=read_ms,
+                mean_us=mean_us)
+
+
+def host_us_per_step(step, R, n=20):
+    """Host time to enqueue one step (for sizing the filler in front of a
+    queued run)."""
+    import torch
+
+    torch.cuda.synchronize()
+    h0 = time.perf_counter()
+    for i in range(n):
+        step(i % R)
+    us = (time.perf_counter() - h0) * 1e6 / n
+    torch.cuda.synchronize()
+    return us
+
+
+def time_queued(torch, step, steps, enqueue_us):
+    """ms per step of `steps` steps launched eagerly behind enough filler work
+    that the host has enqueued them all before the GPU reaches them; HIP
+    events on the launch stream bracket exactly the steps."""
+    torch.cuda.synchronize()
+    f0 = torch.cuda.Event(enable_timing=True)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    h0 = time.perf_counter()
+    f0.record()
+    keep = queue_filler(torch, ms=1.5 * steps * enqueue_us * 1e-3 + 2)
+    e0.record()
+    for i in range(steps):
+        step(i)
+    host_ms = (time.perf_counter() - h0) * 1e3
+    e1.record()
+    torch.cuda.synchronize()
+    del keep
+    ms = e0.elapsed_time(e1) / steps
+    # the GPU reached the steps after the filler; if the host was still
+    # enqueueing them then, the measurement includes host time (it can only
+    # err high)
+    filler_ms = f0.elapsed_time(e0)
+    if host_ms > filler_ms:
+        print(f"note: host enqueue ({host_ms:.2f} ms) outlasted the filler ({filler_ms:.2f} ms); the step time "
+              f"may include host waits", file=sys.stderr)
+    return ms
 
 
 def bench_gemv(torch, q, args):
@@ -316,14 +379,17 @@ def bench_gemv(torch, q, args):
     # headline: the fused four-launch layer; beside it the seven separate launches
     fused = fuse_layer(torch, q, lins)
     assert abs(sum(f["bytes"] for f in fused) - layer_bytes) < 2 * 2 * (4096 + 4096 + 14336), "fusion changed the bytes"
-    ms_f, eager_f, us_f = time_graphs(torch, q, fused, args, R)
+    tf_ = time_graphs(torch, q, fused, args, R)
+    ms_f, us_f = tf_["queued_ms"], tf_["mean_us"]
     if not args.no_separate:
-        ms_s, eager_s, us_s = time_graphs(torch, q, lins, args, R)
+        ts_ = time_graphs(torch, q, lins, args, R)
 
-    # the roofline's per-launch duration: the timed region (graph replays and
-    # the events around them share torch's current stream) over its launches
+    # the roofline's per-launch duration: the timed region (queued launches
+    # and the events around them share torch's current stream) over its
+    # launches
     avg_launch_us = ms_f * 1e3 / len(fused)
     achieved = layer_bytes / len(fused) / (avg_launch_us * 1e-6) / 1e9
+    read_roof = layer_bytes / (tf_["read_roof_ms"] * 1e-3) / 1e9
 
     traffic = None
     if os.path.exists(COUNTERS_FILE):
@@ -337,17 +403,24 @@ def bench_gemv(torch, q, args):
                      us=round(u, 3), gbs=round(l["bytes"] / (u * 1e-6) / 1e9, 1)) for l, u in zip(ls, us)]
 
     value = layer_bytes / (ms_f * 1e-3) / 1e9
+    gbs = lambda ms: round(layer_bytes / (ms * 1e-3) / 1e9, 1)
     return dict(
-        value=value, ms_step=ms_f, eager_ms=eager_f, replicas=R, layer_bytes=layer_bytes,
+        value=value, ms_step=ms_f, replicas=R, layer_bytes=layer_bytes,
+        graph_ms=tf_["graph_ms"], graph_gbs=gbs(tf_["graph_ms"]), host_eager_ms=tf_["host_eager_ms"],
+        read_roof_gbs=round(read_roof, 1),
         per_launch=rows(fused, us_f),
         separate=None if args.no_separate else dict(
-            ms_per_step=round(ms_s, 5), gbs=round(layer_bytes / (ms_s * 1e-3) / 1e9, 1),
-            eager_ms_per_step=round(eager_s, 4), per_linear=rows(lins, us_s)),
+            ms_per_step=round(ts_["queued_ms"], 5), gbs=gbs(ts_["queued_ms"]),
+            graph_ms_per_step=round(ts_["graph_ms"], 5), graph_gbs=gbs(ts_["graph_ms"]),
+            per_linear=rows(lins, ts_["mean_us"])),
         roofline=dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                       frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic,
                       kernel="gemv_kernel (tf_gemv_w4a16, W4, one k-tile per group)",
                       bytes_per_launch=round(layer_bytes / len(fused)),
-                      avg_launch_us=round(avg_launch_us, 3)),
+                      avg_launch_us=round(avg_launch_us, 3),
+                      measured_roof=round(read_roof, 1),
+                      frac_of_measured_roof=round(achieved / read_roof, 4),
+                      measured_roof_kind="plain streaming read of the same packed buffers, same queued launches"),
     )
 
 
@@ -386,12 +459,33 @@ def bench_gemm(torch, q, args):
     tot_fl = sum(2.0 * o["M"] * o["K"] * o["N"] for o in out)
     tot_us = sum(o["us"] for o in out)
     tfs = tot_fl / (tot_us * 1e-6) / 1e12
+
+    # practical roof: back-to-back bf16 MFMAs on every SIMD (two waves each),
+    # sustained for about as long as the GEMM launches above
+    props = torch.cuda.get_device_properties(0)
+    wgs = props.multi_processor_count
+    sink = torch.zeros(4, dtype=torch.float32, device="cuda:0")
+    iters = 2000
+    q.tf_probe_mfma(wgs, iters, sink)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n = max(1, int(tot_us * args.gemm_iters / 300.0))
+    e0.record()
+    fl = 0
+    for _ in range(n):
+        fl += q.tf_probe_mfma(wgs, iters, sink)
+    e1.record()
+    torch.cuda.synchronize()
+    mfma_roof = fl / (e0.elapsed_time(e1) * 1e-3) / 1e12
     return dict(
         metric="W4A16 GEMM M=2048 TFLOP/s", value=round(tfs, 1), unit="TFLOP/s",
         frac_of_peak=round(tfs / BF16_DENSE_PEAK_TFS, 4), shapes=out,
         roofline=dict(bound="mfma", achieved=round(tfs, 1), peak=BF16_DENSE_PEAK_TFS, unit="TFLOP/s",
                       frac=round(tfs / BF16_DENSE_PEAK_TFS, 4), traffic=None,
-                      kernel="gemm_kernel (tf_gemm_w4a16)"),
+                      kernel="gemm_kernel (tf_gemm_w4a16)",
+                      measured_roof=round(mfma_roof, 1), frac_of_measured_roof=round(tfs / mfma_roof, 4),
+                      measured_roof_kind="back-to-back bf16 32x32x16 MFMAs, 8 waves per CU, sustained "
+                                         "as long as the GEMM launches"),
     )
 
 
@@ -424,8 +518,9 @@ def main():
         "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "W4A16 GEMV, M=1, one Llama-style decoder layer (q/o 4096x4096, k/v 4096x1024, "
                                "gate/up 4096x14336, down 14336x4096), group 128; q/k/v fused into one N=6144 "
-                               "launch and gate/up into one N=28672 launch (four launches per step), HIP-graph "
-                               "replay, weights rotating over replicas larger than twice the Infinity Cache",
+                               "launch and gate/up into one N=28672 launch (four launches per step), launched "
+                               "back to back on one stream, weights rotating over replicas larger than twice the "
+                               "Infinity Cache",
                    "global_batch": 1, "parallelism": "none (1 GPU)"},
     }
     if args.only in ("all", "gemv"):
@@ -434,8 +529,12 @@ def main():
         line["ms_per_step"] = round(gv["ms_step"], 5)
         line["config"].update(replicas=gv["replicas"], layer_bytes=int(gv["layer_bytes"]))
         line["roofline"] = gv["roofline"]
-        line["gemv_detail"] = dict(eager_ms_per_step=round(gv["eager_ms"], 4), per_launch=gv["per_launch"],
+        line["gemv_detail"] = dict(per_launch=gv["per_launch"],
                                    frac_of_hbm_peak=round(gv["value"] / HBM_PEAK_GBS, 4),
+                                   read_roof_gbs=gv["read_roof_gbs"],
+                                   frac_of_read_roof=round(gv["value"] / gv["read_roof_gbs"], 4),
+                                   graph_replay=dict(ms_per_step=round(gv["graph_ms"], 5), gbs=gv["graph_gbs"]),
+                                   host_eager_ms_per_step=round(gv["host_eager_ms"], 4),
                                    seven_separate_launches=gv["separate"])
     if args.only in ("all", "gemm"):
         line["gemm"] = bench_gemm(torch, q, args)

@@ -159,6 +159,19 @@ int tf_dequant_w8_f32(const void *packed, size_t packed_bytes, float *w,
 int tf_gemm_plan(int64_t M, int64_t N, int cus, int64_t *out);
 void tf_gemm_set_planning_cus(int n);
 
+/* Measurement probes (not on the hot path): the practical roofs the fused
+ * kernels are measured against, on the same machine and launch pattern.
+ *   tf_probe_stream_read: one launch of a plain kernel that reads `bytes`
+ *     (a multiple of 16, buf 16-byte aligned) once with 16-byte non-temporal
+ *     loads and discards them; sink is a device uint32 it may write.
+ *   tf_probe_mfma: one launch of `workgroups` workgroups of 8 waves, each wave
+ *     issuing `iters` x 4 independent bf16 32x32x16 MFMAs; *flops (host) gets
+ *     the launch's flop count.  sink is a device float it may write.
+ * Both return TF_ERR_NULL / TF_ERR_SHAPE / TF_ERR_ALIGN on bad arguments,
+ * TF_ERR_HIP on a launch error. */
+int tf_probe_stream_read(const void *buf, size_t bytes, uint32_t *sink, void *stream);
+int tf_probe_mfma(int workgroups, int iters, float *sink, int64_t *flops, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

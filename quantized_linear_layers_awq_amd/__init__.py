@@ -25,6 +25,8 @@ from ._binding import (  # noqa: F401
     tf_gemv_w8a16,
     tf_packed_bytes_w4,
     tf_packed_bytes_w8,
+    tf_probe_mfma,
+    tf_probe_stream_read,
     tf_repack_w4,
     tf_repack_w8,
     tf_status_string,

@@ -70,6 +70,10 @@ def load_library():
         L.tf_gemm_plan.restype = I
         L.tf_gemm_set_planning_cus.argtypes = [I]
         L.tf_gemm_set_planning_cus.restype = None
+        L.tf_probe_stream_read.argtypes = [P, SZ, P, P]
+        L.tf_probe_stream_read.restype = I
+        L.tf_probe_mfma.argtypes = [I, I, P, ctypes.POINTER(I64), P]
+        L.tf_probe_mfma.restype = I
         _lib = L
         return _lib
 
@@ -236,3 +240,22 @@ def tf_gemm_set_planning_cus(n: int) -> None:
     """Test hook: later GEMM calls plan for n compute units (n <= 0: the
     device's own count).  Process-wide."""
     load_library().tf_gemm_set_planning_cus(int(n))
+
+
+def tf_probe_stream_read(buf, sink, stream=None):
+    """Measurement probe: one launch reading every byte of `buf` (a CUDA tensor
+    whose size is a multiple of 16 bytes) once; `sink` is a small int32 CUDA
+    tensor the kernel may write."""
+    L = load_library()
+    nbytes = buf.numel() * buf.element_size()
+    _check(L.tf_probe_stream_read(_ptr(buf), nbytes, _ptr(sink), _stream(buf, stream)), "tf_probe_stream_read")
+
+
+def tf_probe_mfma(workgroups, iters, sink, stream=None) -> int:
+    """Measurement probe: one launch of back-to-back bf16 MFMAs; returns its
+    flop count.  `sink` is a small float32 CUDA tensor the kernel may write."""
+    L = load_library()
+    flops = ctypes.c_int64(0)
+    _check(L.tf_probe_mfma(int(workgroups), int(iters), _ptr(sink), ctypes.byref(flops), _stream(sink, stream)),
+           "tf_probe_mfma")
+    return int(flops.value)

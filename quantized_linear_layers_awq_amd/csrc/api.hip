@@ -201,4 +201,30 @@ int tf_gemm_plan(int64_t M, int64_t N, int cus, int64_t *out)
 
 void tf_gemm_set_planning_cus(int n) { tf::set_planning_cus(n); }
 
+int tf_probe_stream_read(const void *buf, size_t bytes, uint32_t *sink, void *stream)
+{
+    if (!buf || !sink)
+        return TF_ERR_NULL;
+    if (bytes == 0 || bytes % 16 || bytes / 16 / 1024 >= (size_t(1) << 31))
+        return TF_ERR_SHAPE;
+    if (!aligned(buf, 16) || !aligned(sink, 4))
+        return TF_ERR_ALIGN;
+    return tf::launch_probe_read(buf, bytes, sink, static_cast<hipStream_t>(stream)) == hipSuccess ? TF_OK
+                                                                                                  : TF_ERR_HIP;
+}
+
+int tf_probe_mfma(int workgroups, int iters, float *sink, int64_t *flops, void *stream)
+{
+    if (!sink || !flops)
+        return TF_ERR_NULL;
+    if (workgroups < 1 || workgroups > (1 << 20) || iters < 1)
+        return TF_ERR_SHAPE;
+    if (!aligned(sink, 4))
+        return TF_ERR_ALIGN;
+    *flops = tf::probe_mfma_flops(workgroups, iters);
+    return tf::launch_probe_mfma(workgroups, iters, sink, static_cast<hipStream_t>(stream)) == hipSuccess
+               ? TF_OK
+               : TF_ERR_HIP;
+}
+
 } // extern "C"

@@ -25,4 +25,9 @@ void set_planning_cus(int n);
 hipError_t launch_gemm(int bits, const uint16_t *x, const void *packed, uint16_t *y, int64_t M, const Layout &lay,
                        hipStream_t stream);
 
+// Measurement probes (not on the hot path).
+hipError_t launch_probe_read(const void *buf, uint64_t bytes, uint32_t *sink, hipStream_t stream);
+hipError_t launch_probe_mfma(int workgroups, int iters, float *sink, hipStream_t stream);
+int64_t probe_mfma_flops(int workgroups, int iters);
+
 } // namespace tf

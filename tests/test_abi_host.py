@@ -196,6 +196,17 @@ class TestValidation:
         assert f(FAKE, FAKE, FAKE, 256, 128, 96, FAKE, 1 << 30, None) == TF_ERR_GROUP
         assert lib.tf_repack_w8(FAKE, FAKE, FAKE, 256, 3, 33, FAKE, 1 << 30, None) == TF_ERR_GROUP
 
+    def test_probe_validation(self, lib):
+        assert lib.tf_probe_stream_read(None, 1024, FAKE, None) == 1          # TF_ERR_NULL
+        assert lib.tf_probe_stream_read(FAKE, 1000, FAKE, None) == TF_ERR_SHAPE
+        assert lib.tf_probe_stream_read(FAKE, 0, FAKE, None) == TF_ERR_SHAPE
+        assert lib.tf_probe_stream_read(FAKE + 8, 1024, FAKE, None) == TF_ERR_ALIGN
+        flops = ctypes.c_int64(0)
+        assert lib.tf_probe_mfma(0, 10, FAKE, ctypes.byref(flops), None) == TF_ERR_SHAPE
+        assert lib.tf_probe_mfma(256, 0, FAKE, ctypes.byref(flops), None) == TF_ERR_SHAPE
+        assert lib.tf_probe_mfma(256, 10, None, ctypes.byref(flops), None) == TF_ERR_NULL
+        assert lib.tf_probe_mfma(256, 10, FAKE + 2, ctypes.byref(flops), None) == TF_ERR_ALIGN
+
     def test_dequant_validation(self, lib):
         assert lib.tf_dequant_w4_f32(FAKE, 1, FAKE, 256, 128, 128, None) == TF_ERR_BUFFER_TOO_SMALL
         assert lib.tf_dequant_w8_f32(FAKE, 1 << 30, FAKE + 2, 256, 128, 128, None) == TF_ERR_ALIGN
