@@ -68,12 +68,13 @@ def parse():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--replicas", type=int, default=0, help="weight replicas to rotate (0: enough to beat the cache)")
-    p.add_argument("--only", choices=["all", "gemv", "gemm", "copy"], default="all",
+    p.add_argument("--only", choices=["all", "gemv", "gemm", "copy", "configs"], default="all",
                    help="restrict the run (profiling passes); 'copy' runs the plain-copy calibration kernel")
     p.add_argument("--counters-from", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
                    help="no GPU: read four rocprofv3 --pmc output directories (FETCH_SIZE and WRITE_SIZE over "
                         "'--only gemv', then over '--only copy') and write the per-launch HBM traffic file")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--no-configs", action="store_true", help="skip the per-config throughput table")
     p.add_argument("--no-separate", action="store_true",
                    help="time only the fused four-launch layer (counter passes: every GEMV dispatch is one "
                         "of the four launches the roofline is computed over)")
@@ -489,6 +490,90 @@ def bench_gemm(torch, q, args):
     )
 
 
+def bench_configs(torch, q, args):
+    """Throughput of every workload configuration at every M it names: GEMV
+    launches queued back to back over weight replicas larger than twice the
+    Infinity Cache (GB/s of algorithmic bytes), GEMM launches back to back
+    (TFLOP/s).  Weights are the seeded synthetic ones; x for a second M of
+    the same weights is drawn on the GPU (timing does not depend on it)."""
+    import numpy as np
+
+    import synth
+
+    dev = "cuda:0"
+    out = []
+    for cfg in sorted(synth.CONFIGS):
+        spec = synth.CONFIGS[cfg]
+        if cfg == 1:
+            for M in spec["Ms"]:
+                lins = stage_layer(torch, q, synth, M=M)
+                fused = fuse_layer(torch, q, lins)
+                lb = sum(l["bytes"] for l in lins)
+                R = max(2, -(-2 * INFINITY_CACHE_BYTES // sum(f["packed"].numel() for f in fused)) + 1)
+                reps = [[f["packed"] for f in fused]] + [[f["packed"].clone() for f in fused] for _ in range(R - 1)]
+
+                def step(i, fused=fused, reps=reps, R=R):
+                    for f, p in zip(fused, reps[i % R]):
+                        q.tf_gemv_w4a16(f["x"], p, f["K"], f["N"], f["G"], y=f["y"])
+
+                step(0)
+                ms = time_queued(torch, step, 100, enqueue_us=host_us_per_step(lambda r: step(r), R))
+                out.append(dict(config=cfg, kernel="gemv", bits=4, M=M, shape="decoder layer, 4 launches", G=128,
+                                us=round(ms * 1e3, 2), gbs=round(lb / (ms * 1e-3) / 1e9, 1),
+                                frac_of_hbm_peak=round(lb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)))
+                del lins, fused, reps
+            continue
+        if cfg == 3:
+            continue  # the GEMM leg of the line
+        for sid, (name, bits, K, N, G) in enumerate(spec["shapes"]):
+            c = synth.make_case(cfg, sid, 1, keep_codes=False)
+            qw = torch.from_numpy(c.qweight.view(np.int32) if bits == 4 else c.qweight).to(dev)
+            qz = torch.from_numpy(c.qzeros.view(np.int32) if bits == 4 else c.qzeros).to(dev)
+            sc = torch.from_numpy(c.scales.view(np.int16)).to(dev)
+            repack = q.tf_repack_w4 if bits == 4 else q.tf_repack_w8
+            packed = repack(qw, qz, sc, K, N, G)
+            del qw, qz, sc, c
+            gemv = q.tf_gemv_w4a16 if bits == 4 else q.tf_gemv_w8a16
+            gemm = q.tf_gemm_w4a16 if bits == 4 else q.tf_gemm_w8a16
+            for M in spec["Ms"]:
+                x = torch.randn((M, K), device=dev).to(torch.bfloat16)
+                y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+                if M <= 16:
+                    R = max(2, -(-2 * INFINITY_CACHE_BYTES // packed.numel()) + 1)
+                    reps = [packed] + [packed.clone() for _ in range(R - 1)]
+
+                    def step(i, reps=reps, R=R, x=x, y=y, K=K, N=N, G=G, gemv=gemv):
+                        gemv(x, reps[i % R], K, N, G, y=y)
+
+                    step(0)
+                    ms = time_queued(torch, step, 100, enqueue_us=host_us_per_step(lambda r: step(r), R))
+                    b = algorithmic_bytes(bits, M, K, N, G)
+                    out.append(dict(config=cfg, kernel="gemv", bits=bits, M=M, shape=f"{K}x{N}", G=G,
+                                    us=round(ms * 1e3, 2), gbs=round(b / (ms * 1e-3) / 1e9, 1),
+                                    frac_of_hbm_peak=round(b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)))
+                    del reps
+                else:
+                    for _ in range(2):
+                        gemm(x, packed, K, N, G, y=y)
+                    torch.cuda.synchronize()
+                    n = max(3, min(args.gemm_iters, int(2e-2 / (2.0 * M * K * N / 1e15))))
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record()
+                    for _ in range(n):
+                        gemm(x, packed, K, N, G, y=y)
+                    e1.record()
+                    torch.cuda.synchronize()
+                    us = 1e3 * e0.elapsed_time(e1) / n
+                    tfs = 2.0 * M * K * N / (us * 1e-6) / 1e12
+                    out.append(dict(config=cfg, kernel="gemm", bits=bits, M=M, shape=f"{K}x{N}", G=G,
+                                    us=round(us, 2), tflops=round(tfs, 1),
+                                    frac_of_peak=round(tfs / BF16_DENSE_PEAK_TFS, 4)))
+                del x, y
+            del packed
+            torch.cuda.empty_cache()
+    return out
+
+
 def main():
     args = parse()
     if args.counters_from:
@@ -538,6 +623,8 @@ def main():
                                    seven_separate_launches=gv["separate"])
     if args.only in ("all", "gemm"):
         line["gemm"] = bench_gemm(torch, q, args)
+    if args.only == "configs" or (args.only == "all" and not args.no_configs):
+        line["configs"] = bench_configs(torch, q, args)
     if args.only == "all" and not args.no_cpu:
         import oracle
         import synth
