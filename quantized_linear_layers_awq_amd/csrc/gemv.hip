@@ -106,11 +106,13 @@ __device__ __forceinline__ void fold(f32x4 &yacc, f32x4 &gacc, f32x4 &zacc, floa
     gacc = zacc = f32x4{0.f, 0.f, 0.f, 0.f};
 }
 
-// Launch-time geometry of the K chunks staged in LDS.
+// Launch-time geometry: the blocks a workgroup covers and the K chunks it
+// stages in LDS.
 struct GemvChunks {
+    int bpw;      // 16-column blocks per workgroup (they share the staged x)
     int tiles;    // k-tiles per chunk
     int xpitch;   // bf16 elements per staged activation row (chunk rows + 8)
-    int meta_cap; // bytes reserved for the chunk's metadata records
+    int meta_cap; // bytes reserved per block for the chunk's metadata records
     int lds;      // dynamic LDS bytes per workgroup
 };
 
@@ -128,24 +130,29 @@ enum GroupMode {
 // retire in order, so waiting for tile t never waits for anything issued
 // after it.  Each ring slot is unpacked into MFMA operands before it is
 // refilled, so the slot keeps its registers and no wait drains the ring.
-template <int BITS, int kMode, int D>
+template <int BITS, int kMode, int D, int BPW>
 __global__ __launch_bounds__(1024) void gemv_kernel(const uint16_t *__restrict__ x, const uint8_t *__restrict__ packed,
                                                     uint16_t *__restrict__ y, Layout lay, int M, GemvChunks ch)
 {
     // D: k-tiles of codes in flight per wave
     constexpr uint32_t TB = tile_bytes(BITS), RB = record_bytes(BITS);
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-    uint8_t *smeta = smem;
-    uint16_t *sx = reinterpret_cast<uint16_t *>(smem + ch.meta_cap);
+    uint16_t *sx = reinterpret_cast<uint16_t *>(smem + BPW * ch.meta_cap);
     float *red = reinterpret_cast<float *>(smem); // reused after the last chunk
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int W = blockDim.x >> 6;
+    const int Wb = W / BPW;                               // waves per block
+    const int bi = BPW == 1 ? 0 : wave / Wb;              // this wave's block
+    const int ws = wave - bi * Wb;                        // and its share of K
     const int r = lane & 15, o = lane >> 4;
-    const int64_t blk = blockIdx.x;
-    const uint8_t *meta = packed + blk * lay.block_bytes;
+    const int64_t blk0 = (int64_t)blockIdx.x * BPW;       // first block of the workgroup
+    const int64_t blk = blk0 + bi;
+    const bool blk_ok = blk < lay.nblocks;                // a last workgroup may be partial
+    const uint8_t *meta = packed + (blk_ok ? blk : 0) * lay.block_bytes;
     const uint8_t *tiles = meta + lay.meta_bytes + 16 * lane;
+    uint8_t *smeta = smem + bi * ch.meta_cap;             // this block's staged records
     // MFMA rows >= M are never stored, so their lanes read row 0 instead of
     // being masked off.
     const int xr = r < M ? r : 0;
@@ -159,8 +166,8 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const uint16_t *__restrict__
     for (int c0 = 0; c0 < ktiles; c0 += ch.tiles) {
         const int c1 = c0 + ch.tiles < ktiles ? c0 + ch.tiles : ktiles;
         const int nct = c1 - c0;
-        const int a = c0 + nct * wave / W, b = c0 + nct * (wave + 1) / W; // this wave's k-tiles
-        const int n = b - a;
+        const int a = c0 + nct * ws / Wb, b = c0 + nct * (ws + 1) / Wb; // this wave's k-tiles
+        const int n = blk_ok ? b - a : 0;
         // codes first: their latency overlaps the staging below.  Ring loads
         // past the wave's range re-read its last tile (in bounds, never used).
         if (n > 0) {
@@ -182,12 +189,19 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const uint16_t *__restrict__
                 v = load16(x + (int64_t)m * lay.K + k);
             *reinterpret_cast<u32x4 *>(sx + m * ch.xpitch + 8 * u8) = v;
         }
-        // ---- stage the metadata records of groups g0 .. g1 ----
+        // ---- stage the metadata records of groups g0 .. g1, per block ----
         const int64_t k1 = (int64_t)c1 * kTileRows < lay.K ? (int64_t)c1 * kTileRows : lay.K;
         const int64_t g0 = k0 / lay.G, g1 = (k1 - 1) / lay.G;
         const int rec_words = (int)((g1 - g0 + 1) * RB / 8);
-        for (int e = tid; e < rec_words; e += blockDim.x)
-            *reinterpret_cast<u32x2 *>(smeta + 8 * e) = *reinterpret_cast<const u32x2 *>(meta + g0 * RB + 8 * e);
+#pragma unroll
+        for (int eb = 0; eb < BPW; ++eb) {
+            if (blk0 + eb < lay.nblocks) {
+                const uint8_t *src = packed + (blk0 + eb) * lay.block_bytes + g0 * RB;
+                for (int e = tid; e < rec_words; e += blockDim.x)
+                    *reinterpret_cast<u32x2 *>(smem + eb * ch.meta_cap + 8 * e) =
+                        *reinterpret_cast<const u32x2 *>(src + 8 * e);
+            }
+        }
         __syncthreads();
         if (n <= 0)
             continue;
@@ -271,65 +285,110 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const uint16_t *__restrict__
     for (int e = 0; e < 4; ++e)
         red[(wave * 16 + 4 * o + e) * kBlockCols + r] = yacc[e];
     __syncthreads();
-    for (int e = tid; e < M * kBlockCols; e += blockDim.x) {
-        const int row = e >> 4, col = e & 15;
-        float v = 0.f;
-        for (int w = 0; w < W; ++w)
-            v += red[(w * 16 + row) * kBlockCols + col];
-        const int64_t nn = blk * kBlockCols + col;
-        if (nn < lay.N)
-            y[(int64_t)row * lay.N + nn] = f32_to_bf16_bits(v);
+    // each block sums its own waves, in wave order
+#pragma unroll
+    for (int eb = 0; eb < BPW; ++eb) {
+        for (int e = tid; e < M * kBlockCols; e += blockDim.x) {
+            const int row = e >> 4, col = e & 15;
+            float v = 0.f;
+            for (int w = eb * Wb; w < (eb + 1) * Wb; ++w)
+                v += red[(w * 16 + row) * kBlockCols + col];
+            const int64_t nn = (blk0 + eb) * kBlockCols + col;
+            if (nn < lay.N)
+                y[(int64_t)row * lay.N + nn] = f32_to_bf16_bits(v);
+        }
     }
 }
 
-int gemv_waves(const Layout &lay)
+// Blocks per workgroup: one at M = 1 (x is small); with several activation
+// rows, x is M times larger and every workgroup stages all of it, so wide
+// layers give each workgroup up to four blocks (still at least 256
+// workgroups) and stage x once for all of them.
+static int gemv_bpw(const Layout &lay, int64_t M)
 {
-    int64_t w = (kGemvTargetWaves + lay.nblocks - 1) / lay.nblocks;
-    if (w > kGemvMaxWaves)
-        w = kGemvMaxWaves;
-    if (w > lay.ktiles)
-        w = lay.ktiles;
-    return w < 1 ? 1 : (int)w;
+    if (M < 2)
+        return 1;
+    int64_t b = lay.nblocks / 256;
+    return b >= 4 ? 4 : b >= 2 ? 2 : 1;
+}
+
+int gemv_waves(const Layout &lay, int64_t M)
+{
+    const int bpw = gemv_bpw(lay, M);
+    const int64_t wgs = (lay.nblocks + bpw - 1) / bpw;
+    int64_t wb = ((kGemvTargetWaves + wgs - 1) / wgs + bpw - 1) / bpw; // waves per block
+    if (wb * bpw > kGemvMaxWaves)
+        wb = kGemvMaxWaves / bpw;
+    if (wb > lay.ktiles)
+        wb = lay.ktiles;
+    return (int)(wb < 1 ? 1 : wb) * bpw;
 }
 
 // Chunk size: as many k-tiles as fit the LDS share of one workgroup when
-// 16 / W workgroups run per CU (at most 64 KiB).
-static GemvChunks plan_chunks(int bits, const Layout &lay, int64_t M, int W)
+// 16 / W workgroups run per CU (at most kGemvMaxLds).
+constexpr int kGemvMaxLds = 156 * 1024;
+static GemvChunks plan_chunks(int bits, const Layout &lay, int64_t M, int W, int bpw)
 {
     const int RB = record_bytes(bits);
     int wgs = kGemvMaxWaves / W;
     wgs = wgs < 1 ? 1 : wgs;
-    int64_t budget = (160 * 1024) / wgs - 512;
-    if (budget > 64 * 1024)
-        budget = 64 * 1024;
+    int64_t budget = (160 * 1024) / wgs - 1024;
+    if (budget > kGemvMaxLds)
+        budget = kGemvMaxLds;
     const int64_t recs_per_tile = lay.whole_tiles() ? 1 : lay.groups_per_tile;
-    const int64_t per_tile = M * kTileRows * 2 + recs_per_tile * RB;
-    int64_t tiles = (budget - 2 * RB - 16 * M) / per_tile;
+    const int64_t per_tile = M * kTileRows * 2 + bpw * recs_per_tile * RB;
+    int64_t tiles = (budget - bpw * (2 * RB + 16) - 16 * M) / per_tile;
     if (tiles > lay.ktiles)
         tiles = lay.ktiles;
     if (tiles < 1)
         tiles = 1;
     GemvChunks c;
+    c.bpw = bpw;
     c.tiles = (int)tiles;
     c.xpitch = (int)(tiles * kTileRows + 8);
     // records of a chunk: groups g0..g1 of its rows, at most tiles * recs_per_tile + 1
     c.meta_cap = (int)(((tiles * recs_per_tile + 1) * RB + 15) / 16 * 16);
-    int64_t lds = c.meta_cap + M * c.xpitch * 2;
+    int64_t lds = (int64_t)bpw * c.meta_cap + M * c.xpitch * 2;
     const int64_t red = (int64_t)W * 16 * kBlockCols * 4;
     c.lds = (int)(lds > red ? lds : red);
     return c;
+}
+
+// Dynamic LDS above the default 64 KiB needs the limit raised, once per
+// instantiation.
+template <int BITS, int kMode, int D, int BPW>
+static void launch_gemv_mode(const Layout &lay, dim3 grid, dim3 block, const GemvChunks &ch, hipStream_t stream,
+                             const uint16_t *x, const uint8_t *pk, uint16_t *y, int M)
+{
+    auto kern = &gemv_kernel<BITS, kMode, D, BPW>;
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, kGemvMaxLds);
+    (void)attr;
+    kern<<<grid, block, ch.lds, stream>>>(x, pk, y, lay, M, ch);
+}
+
+template <int BITS, int D, int BPW>
+static void launch_gemv_bpw(const Layout &lay, dim3 grid, dim3 block, const GemvChunks &ch, hipStream_t stream,
+                            const uint16_t *x, const uint8_t *pk, uint16_t *y, int M)
+{
+    if (lay.tiles_per_group == 1)
+        launch_gemv_mode<BITS, kOneTile, D, BPW>(lay, grid, block, ch, stream, x, pk, y, M);
+    else if (lay.whole_tiles())
+        launch_gemv_mode<BITS, kMultiTile, D, BPW>(lay, grid, block, ch, stream, x, pk, y, M);
+    else
+        launch_gemv_mode<BITS, kSplitTiles, D, BPW>(lay, grid, block, ch, stream, x, pk, y, M);
 }
 
 template <int BITS, int D>
 static void launch_gemv_depth(const Layout &lay, dim3 grid, dim3 block, const GemvChunks &ch, hipStream_t stream,
                               const uint16_t *x, const uint8_t *pk, uint16_t *y, int M)
 {
-    if (lay.tiles_per_group == 1)
-        gemv_kernel<BITS, kOneTile, D><<<grid, block, ch.lds, stream>>>(x, pk, y, lay, M, ch);
-    else if (lay.whole_tiles())
-        gemv_kernel<BITS, kMultiTile, D><<<grid, block, ch.lds, stream>>>(x, pk, y, lay, M, ch);
+    if (ch.bpw == 4)
+        launch_gemv_bpw<BITS, D, 4>(lay, grid, block, ch, stream, x, pk, y, M);
+    else if (ch.bpw == 2)
+        launch_gemv_bpw<BITS, D, 2>(lay, grid, block, ch, stream, x, pk, y, M);
     else
-        gemv_kernel<BITS, kSplitTiles, D><<<grid, block, ch.lds, stream>>>(x, pk, y, lay, M, ch);
+        launch_gemv_bpw<BITS, D, 1>(lay, grid, block, ch, stream, x, pk, y, M);
 }
 
 // Prefetch depth: measured on MI355X, two k-tiles in flight per wave suit
@@ -339,7 +398,7 @@ template <int BITS>
 static void launch_gemv_bits(const Layout &lay, dim3 grid, dim3 block, const GemvChunks &ch, hipStream_t stream,
                              const uint16_t *x, const uint8_t *pk, uint16_t *y, int M)
 {
-    const int64_t per_wave = lay.ktiles / (block.x / 64);
+    const int64_t per_wave = lay.ktiles / (block.x / 64 / ch.bpw);
     if (per_wave <= 3)
         launch_gemv_depth<BITS, 2>(lay, grid, block, ch, stream, x, pk, y, M);
     else
@@ -349,9 +408,10 @@ static void launch_gemv_bits(const Layout &lay, dim3 grid, dim3 block, const Gem
 hipError_t launch_gemv(int bits, const uint16_t *x, const void *packed, uint16_t *y, int64_t M, const Layout &lay,
                        hipStream_t stream)
 {
-    const int W = gemv_waves(lay);
-    const GemvChunks ch = plan_chunks(bits, lay, M, W);
-    const dim3 grid((unsigned)lay.nblocks), block(64 * W);
+    const int W = gemv_waves(lay, M);
+    const int bpw = gemv_bpw(lay, M);
+    const GemvChunks ch = plan_chunks(bits, lay, M, W, bpw);
+    const dim3 grid((unsigned)((lay.nblocks + bpw - 1) / bpw)), block(64 * W);
     const uint8_t *pk = static_cast<const uint8_t *>(packed);
     if (bits == 4)
         launch_gemv_bits<4>(lay, grid, block, ch, stream, x, pk, y, (int)M);

@@ -9,8 +9,9 @@ hipError_t launch_repack(int bits, const void *qweight, const void *qzeros, cons
                          const Layout &lay, void *packed, hipStream_t stream);
 hipError_t launch_dequant_f32(int bits, const void *packed, const Layout &lay, float *w, hipStream_t stream);
 
-// Waves per GEMV workgroup (one workgroup per 16-column block).
-int gemv_waves(const Layout &lay);
+// Waves per GEMV workgroup for M activation rows (one workgroup per 16-column
+// block, or per two or four blocks of a wide layer at M >= 2).
+int gemv_waves(const Layout &lay, int64_t M);
 hipError_t launch_gemv(int bits, const uint16_t *x, const void *packed, uint16_t *y, int64_t M, const Layout &lay,
                        hipStream_t stream);
 // How the GEMM covers the output: m_tiles row tiles of 256 rows, then

@@ -17,6 +17,10 @@ GEMV_SHAPES = [
     (4, 1, 128, 64, 128), (4, 3, 512, 200, 128), (4, 16, 1024, 136, 64), (4, 5, 4096, 72, 32),
     (4, 2, 384, 64, 384), (4, 1, 96, 64, 96), (4, 8, 4096, 128, 128), (4, 1, 8192, 256, 128),
     (8, 1, 256, 100, 256), (8, 8, 2048, 260, 2048), (8, 4, 512, 64, 64), (8, 12, 4096, 64, 128),
+    # wide layers at M >= 2: two or four blocks per workgroup, last workgroup partial
+    (4, 4, 512, 8240, 128), (4, 3, 1024, 16400, 64), (8, 8, 1024, 8208, 1024), (4, 2, 384, 16400, 384),
+    # M = 16 over K = 4096: 128 KiB of staged activations (dynamic LDS above 64 KiB)
+    (4, 16, 4096, 4096, 128),
 ]
 
 GEMM_SHAPES = [
