@@ -124,11 +124,12 @@ enum GroupMode {
 };
 
 // A chunk of K is staged per workgroup: activations x[0:M][chunk] (zero past
-// K) and the metadata records of the groups the chunk touches.  The only
-// vector-memory loads in the main loop are then the code stream, issued in
-// the order it is consumed, a fixed D k-tiles ahead; vector-memory counters
-// retire in order, so waiting for tile t never waits for anything issued
-// after it.  Each ring slot is unpacked into MFMA operands before it is
+// K) and the metadata records of the groups the chunk touches, loaded before
+// the chunk's first codes so that the staging barrier does not wait for the
+// codes.  The only vector-memory loads in the main loop are then the code
+// stream, issued in the order it is consumed, a fixed D k-tiles ahead;
+// vector-memory counters retire in order, so waiting for tile t never waits
+// for anything issued after it.  Each ring slot is unpacked into MFMA operands before it is
 // refilled, so the slot keeps its registers and no wait drains the ring.
 template <int BITS, int kMode, int D, int BPW>
 __global__ __launch_bounds__(1024) void gemv_kernel(const uint16_t *__restrict__ x, const uint8_t *__restrict__ packed,
@@ -168,8 +169,39 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const uint16_t *__restrict__
         const int nct = c1 - c0;
         const int a = c0 + nct * ws / Wb, b = c0 + nct * (ws + 1) / Wb; // this wave's k-tiles
         const int n = blk_ok ? b - a : 0;
-        // codes first: their latency overlaps the staging below.  Ring loads
-        // past the wave's range re-read its last tile (in bounds, never used).
+        // ---- x[m][k0 .. k0 + 128 nct) (zero past K) and the chunk's records
+        //      are loaded first, into registers: they come from L2 and are
+        //      stored to LDS before the barrier, and vector-memory loads
+        //      retire in order, so loads issued after the codes would wait for
+        //      the codes' HBM latency before the barrier ----
+        const int64_t k0 = (int64_t)c0 * kTileRows;
+        const int units_per_row = nct * (kTileRows / 8);
+        const int x_units = M * units_per_row;
+        constexpr int XR = 4; // x units per thread held in registers
+        u32x4 xv[XR];
+#pragma unroll
+        for (int i = 0; i < XR; ++i) {
+            const int e = tid + i * (int)blockDim.x;
+            xv[i] = u32x4{0u, 0u, 0u, 0u};
+            if (e < x_units) {
+                const int m = e / units_per_row, u8 = e - m * units_per_row;
+                const int64_t k = k0 + 8 * u8;
+                if (k < lay.K)
+                    xv[i] = load16(x + (int64_t)m * lay.K + k);
+            }
+        }
+        const int64_t k1 = (int64_t)c1 * kTileRows < lay.K ? (int64_t)c1 * kTileRows : lay.K;
+        const int64_t g0 = k0 / lay.G, g1 = (k1 - 1) / lay.G;
+        const int rec_words = (int)((g1 - g0 + 1) * RB / 8);
+        u32x2 mv[BPW];
+#pragma unroll
+        for (int eb = 0; eb < BPW; ++eb) {
+            mv[eb] = u32x2{0u, 0u};
+            if (tid < rec_words && blk0 + eb < lay.nblocks)
+                mv[eb] = *reinterpret_cast<const u32x2 *>(packed + (blk0 + eb) * lay.block_bytes + g0 * RB + 8 * tid);
+        }
+        // ---- then the codes.  Ring loads past the wave's range re-read its
+        //      last tile (in bounds, never used). ----
         if (n > 0) {
 #pragma unroll
             for (int j = 0; j < D; ++j)
@@ -178,10 +210,15 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const uint16_t *__restrict__
 
         if (c0 > 0)
             __syncthreads(); // the previous chunk's LDS is no longer read
-        // ---- stage activations x[m][k0 .. k0 + 128 nct), zero past K ----
-        const int64_t k0 = (int64_t)c0 * kTileRows;
-        const int units_per_row = nct * (kTileRows / 8);
-        for (int e = tid; e < M * units_per_row; e += blockDim.x) {
+#pragma unroll
+        for (int i = 0; i < XR; ++i) {
+            const int e = tid + i * (int)blockDim.x;
+            if (e < x_units) {
+                const int m = e / units_per_row, u8 = e - m * units_per_row;
+                *reinterpret_cast<u32x4 *>(sx + m * ch.xpitch + 8 * u8) = xv[i];
+            }
+        }
+        for (int e = tid + XR * (int)blockDim.x; e < x_units; e += blockDim.x) { // more than XR per thread
             const int m = e / units_per_row, u8 = e - m * units_per_row;
             const int64_t k = k0 + 8 * u8;
             u32x4 v = {0u, 0u, 0u, 0u};
@@ -189,15 +226,13 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const uint16_t *__restrict__
                 v = load16(x + (int64_t)m * lay.K + k);
             *reinterpret_cast<u32x4 *>(sx + m * ch.xpitch + 8 * u8) = v;
         }
-        // ---- stage the metadata records of groups g0 .. g1, per block ----
-        const int64_t k1 = (int64_t)c1 * kTileRows < lay.K ? (int64_t)c1 * kTileRows : lay.K;
-        const int64_t g0 = k0 / lay.G, g1 = (k1 - 1) / lay.G;
-        const int rec_words = (int)((g1 - g0 + 1) * RB / 8);
 #pragma unroll
         for (int eb = 0; eb < BPW; ++eb) {
             if (blk0 + eb < lay.nblocks) {
+                if (tid < rec_words)
+                    *reinterpret_cast<u32x2 *>(smem + eb * ch.meta_cap + 8 * tid) = mv[eb];
                 const uint8_t *src = packed + (blk0 + eb) * lay.block_bytes + g0 * RB;
-                for (int e = tid; e < rec_words; e += blockDim.x)
+                for (int e = tid + (int)blockDim.x; e < rec_words; e += blockDim.x) // more than one per thread
                     *reinterpret_cast<u32x2 *>(smem + eb * ch.meta_cap + 8 * e) =
                         *reinterpret_cast<const u32x2 *>(src + 8 * e);
             }
