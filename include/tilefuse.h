@@ -112,9 +112,11 @@ int tf_repack_w8(const uint8_t *qweight, const uint8_t *zeros, const uint16_t *s
 /*   y          bf16 [M][N] output (fp32 accumulation, one rounding to bf16, */
 /*              nearest-even), 2-byte aligned                                */
 /*   workspace  device scratch of ws_bytes >= tf_workspace_bytes(...), 256-  */
-/*              byte aligned.  NULL is fine when the size query returns 0,   */
-/*              which it does for every shape in this version (kept in the   */
-/*              signature for split-K variants).                             */
+/*              byte aligned.  NULL is fine when the size query returns 0:   */
+/*              always for the GEMV; for the GEMM unless it splits K (few    */
+/*              output tiles, i.e. small M).  The size depends on the device */
+/*              the query runs on (its compute-unit count): query on the     */
+/*              device the GEMM will run on.                                 */
 /* ------------------------------------------------------------------------ */
 size_t tf_workspace_bytes(int bits, int is_gemm, int64_t M, int64_t K, int64_t N, int64_t G);
 
@@ -146,17 +148,24 @@ int tf_dequant_w8_f32(const void *packed, size_t packed_bytes, float *w,
                       int64_t K, int64_t N, int64_t G, void *stream);
 
 /* Test hooks of the GEMM's launch plan (host only, no GPU work).
- * The GEMM covers y with 256-row x 128-column tiles and, when the tiles are
- * not a whole number of rounds over the device's compute units, runs the
+ * The GEMM covers y with 256-row x 128-column tiles.  When the tiles are not
+ * a whole number of rounds over the device's compute units, it runs the
  * columns of the last partial round as 256 x 64 tiles in a second launch.
- * The plan never changes the result's bits.
+ * When the tiles fill less than half the compute units (small M), it splits
+ * K into ranges that run in the same launch, each writing fp32 partial sums
+ * to the workspace, and a second kernel adds them in range order (so
+ * tf_workspace_bytes is non-zero for those shapes).  The plan never changes
+ * the result's bits except through that split: the order of the split sums.
  *   tf_gemm_plan: writes out[0] = row tiles, out[1] = 128-column tiles,
- *     out[2] = 64-column tiles for (M, N) on a device of `cus` compute
- *     units.  TF_ERR_NULL / TF_ERR_SHAPE (M, N or cus < 1) on bad input.
- *   tf_gemm_set_planning_cus: makes later GEMM calls of this process plan
- *     for n compute units instead of the current device's (n <= 0 restores
- *     the device's).  Process-wide; not meant to race with GEMM calls. */
-int tf_gemm_plan(int64_t M, int64_t N, int cus, int64_t *out);
+ *     out[2] = 64-column tiles, out[3] = K ranges, out[4] = k-tiles of 128
+ *     rows per range, for a GEMM of (bits, M, K, N, G) on a device of `cus`
+ *     compute units.  TF_ERR_NULL / TF_ERR_SHAPE / TF_ERR_GROUP /
+ *     TF_ERR_UNSUPPORTED on bad input.
+ *   tf_gemm_set_planning_cus: makes later GEMM calls and workspace queries
+ *     of this process plan for n compute units instead of the current
+ *     device's (n <= 0 restores the device's).  Process-wide; not meant to
+ *     race with GEMM calls. */
+int tf_gemm_plan(int bits, int64_t M, int64_t K, int64_t N, int64_t G, int cus, int64_t *out);
 void tf_gemm_set_planning_cus(int n);
 
 /* Measurement probes (not on the hot path): the practical roofs the fused

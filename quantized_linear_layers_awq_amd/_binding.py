@@ -66,7 +66,7 @@ def load_library():
         for n in ("tf_dequant_w4_f32", "tf_dequant_w8_f32"):
             getattr(L, n).argtypes = [P, SZ, P, I64, I64, I64, P]
             getattr(L, n).restype = I
-        L.tf_gemm_plan.argtypes = [I64, I64, I, ctypes.POINTER(I64)]
+        L.tf_gemm_plan.argtypes = [I, I64, I64, I64, I64, I, ctypes.POINTER(I64)]
         L.tf_gemm_plan.restype = I
         L.tf_gemm_set_planning_cus.argtypes = [I]
         L.tf_gemm_set_planning_cus.restype = None
@@ -227,13 +227,14 @@ def tf_dequant_w8_f32(packed, K, N, G, w=None, stream=None):
     return _dequant("tf_dequant_w8_f32", packed, K, N, G, w, stream)
 
 
-def tf_gemm_plan(M: int, N: int, cus: int) -> tuple[int, int, int]:
-    """Test hook: (row tiles, 128-column tiles, 64-column tiles) of the GEMM's
-    launch plan for (M, N) on a device of `cus` compute units (host only)."""
+def tf_gemm_plan(bits: int, M: int, K: int, N: int, G: int, cus: int) -> tuple[int, int, int, int, int]:
+    """Test hook: (row tiles, 128-column tiles, 64-column tiles, K ranges,
+    k-tiles per range) of the GEMM's launch plan on a device of `cus` compute
+    units (host only)."""
     L = load_library()
-    out = (ctypes.c_int64 * 3)()
-    _check(L.tf_gemm_plan(M, N, cus, out), "tf_gemm_plan")
-    return int(out[0]), int(out[1]), int(out[2])
+    out = (ctypes.c_int64 * 5)()
+    _check(L.tf_gemm_plan(bits, M, K, N, G, cus, out), "tf_gemm_plan")
+    return tuple(int(v) for v in out)
 
 
 def tf_gemm_set_planning_cus(n: int) -> None:

@@ -52,9 +52,15 @@ int repack(int bits, const void *qweight, const void *qzeros, const uint16_t *sc
     return TF_OK;
 }
 
-// No kernel of this build needs scratch memory: the GEMV combines its K
-// split inside a workgroup and the GEMM owns whole output tiles.
-size_t workspace_bytes(int, int, int64_t, int64_t, int64_t, int64_t) { return 0; }
+// The GEMV combines its K split inside a workgroup and needs no scratch
+// memory.  The GEMM needs fp32 partial sums when it splits K (few output
+// tiles: small M), S x M x N floats; otherwise none.
+size_t workspace_bytes(int bits, int is_gemm, int64_t M, int64_t K, int64_t N, int64_t G)
+{
+    if (!is_gemm || M < 1 || M > (int64_t(1) << 30) || check_kng(bits, K, N, G) != TF_OK)
+        return 0;
+    return (size_t)tf::gemm_workspace_bytes(M, N, K, G);
+}
 
 int linear(int bits, bool is_gemm, const uint16_t *x, const void *packed, size_t nbytes, uint16_t *y, int64_t M,
            int64_t K, int64_t N, int64_t G, void *ws, size_t ws_bytes, void *stream)
@@ -87,7 +93,7 @@ int linear(int bits, bool is_gemm, const uint16_t *x, const void *packed, size_t
     }
     hipError_t e;
     if (is_gemm)
-        e = tf::launch_gemm(bits, x, packed, y, M, lay, static_cast<hipStream_t>(stream));
+        e = tf::launch_gemm(bits, x, packed, y, M, lay, ws, static_cast<hipStream_t>(stream));
     else
         e = tf::launch_gemv(bits, x, packed, y, M, lay, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? TF_OK : TF_ERR_HIP;
@@ -186,16 +192,22 @@ int tf_dequant_w8_f32(const void *packed, size_t nbytes, float *w, int64_t K, in
     return dequant(8, packed, nbytes, w, K, N, G, stream);
 }
 
-int tf_gemm_plan(int64_t M, int64_t N, int cus, int64_t *out)
+int tf_gemm_plan(int bits, int64_t M, int64_t K, int64_t N, int64_t G, int cus, int64_t *out)
 {
     if (!out)
         return TF_ERR_NULL;
-    if (M < 1 || N < 1 || cus < 1 || M > (int64_t(1) << 30) || N >= kDimLimit)
+    if (bits != 4 && bits != 8)
+        return TF_ERR_UNSUPPORTED;
+    if (M < 1 || cus < 1 || M > (int64_t(1) << 30))
         return TF_ERR_SHAPE;
-    const tf::GemmPlan p = tf::plan_gemm(M, N, cus);
+    if (int st = check_kng(bits, K, N, G))
+        return st;
+    const tf::GemmPlan p = tf::plan_gemm(M, N, K, G, cus);
     out[0] = p.m_tiles;
     out[1] = p.wide_cols;
     out[2] = p.narrow_cols;
+    out[3] = p.splits;
+    out[4] = p.split_tiles;
     return TF_OK;
 }
 

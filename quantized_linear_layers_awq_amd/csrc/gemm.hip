@@ -178,13 +178,17 @@ template <int I, int N, typename F> __device__ __forceinline__ void static_for(F
     }
 }
 
-// The workgroup grid covers m_tiles row tiles x (gridDim.x / m_tiles) column
-// tiles of width 64 WN, starting at output column col0.
+// The workgroup grid covers `splits` ranges of split_tiles k-tiles each, and
+// per range m_tiles row tiles x (gridDim.x / splits / m_tiles) column tiles of
+// width 64 WN, starting at output column col0.  With one range the output is
+// y (bf16); with several, each range writes its fp32 partial sums to
+// ws[range][M][N] and a second kernel adds them.
 template <int BITS, int kMode, int WN>
 __global__ __launch_bounds__(kGThreads, 1) void gemm_kernel(const uint16_t *__restrict__ x,
                                                             const uint8_t *__restrict__ packed,
                                                             uint16_t *__restrict__ y, Layout lay, int64_t M,
-                                                            int m_tiles, int64_t col0)
+                                                            int m_tiles, int64_t col0, int splits,
+                                                            int split_tiles, float *__restrict__ ws)
 {
     constexpr int kGBN = tile_cols(WN), kGBlocks = tile_blocks(WN);
     constexpr int kBStageBytes = bstage_bytes(WN), kCodeBufBytes = codebuf_bytes(WN);
@@ -217,8 +221,10 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_kernel(const uint16_t *__re
     //      each weight column tile ----
     const int nwg = gridDim.x, bid = blockIdx.x;
     const int xcd = bid & 7, local = bid >> 3, q8 = nwg >> 3, rem = nwg & 7;
-    const int tile = xcd < rem ? xcd * (q8 + 1) + local : rem * (q8 + 1) + (xcd - rem) * q8 + local;
-    const int n_tiles = nwg / m_tiles;
+    const int tile_all = xcd < rem ? xcd * (q8 + 1) + local : rem * (q8 + 1) + (xcd - rem) * q8 + local;
+    const int per_split = nwg / splits;                    // output tiles of one k range
+    const int split = tile_all / per_split, tile = tile_all - split * per_split;
+    const int n_tiles = per_split / m_tiles;
     const int band_rows = kBand > 0 && kBand < m_tiles ? kBand : m_tiles;
     const int band = tile / (band_rows * n_tiles), in_band = tile - band * band_rows * n_tiles;
     const int rows_here = m_tiles - band * band_rows < band_rows ? m_tiles - band * band_rows : band_rows;
@@ -226,10 +232,38 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_kernel(const uint16_t *__re
     const int64_t m0 = (int64_t)mt * kGBM;
     const int64_t blk0 = (col0 >> 4) + (int64_t)nt * kGBlocks;
 
-    const int ktiles = (int)lay.ktiles;
+    // ---- the k range of this split as a layout of its own: its groups,
+    //      k-tiles and rows, with the packed block base moved to its first
+    //      record and the codes' offset moved to its first k-tile.  Ranges
+    //      start on group boundaries (a whole-k-tile group per range when one
+    //      group spans all of K). ----
+    const int64_t lda = lay.K; // elements per row of x
+    Layout L = lay;
+    int64_t k_begin = 0, g_begin = 0;
+    if (splits > 1) {
+        const int64_t kt0 = (int64_t)split * split_tiles;
+        const int64_t kt1 = kt0 + split_tiles < lay.ktiles ? kt0 + split_tiles : lay.ktiles;
+        k_begin = kt0 * kTileRows;
+        const int64_t k_end = kt1 * kTileRows < lay.K ? kt1 * kTileRows : lay.K;
+        g_begin = lay.G == lay.K ? 0 : k_begin / lay.G;
+        L.K = k_end - k_begin;
+        L.ktiles = kt1 - kt0;
+        L.steps = L.K / kStepRows;
+        if (lay.G == lay.K) {
+            L.G = L.K;
+            L.ngroups = 1;
+            L.tiles_per_group = L.ktiles;
+        } else {
+            L.ngroups = L.K / lay.G;
+        }
+        L.meta_bytes = lay.meta_bytes - g_begin * RB + kt0 * tile_bytes(BITS);
+    }
+    const uint8_t *const pk = packed + g_begin * RB; // a block's records of this range
+
+    const int ktiles = (int)L.ktiles;
     const int nstages = 2 * ktiles;
-    const int steps = (int)lay.steps;
-    const int64_t K = lay.K;
+    const int steps = (int)L.steps;
+    const int64_t K = L.K;
 
     uint8_t *const sA = lds;
     uint8_t *const sB = lds + kOffB;
@@ -245,13 +279,13 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_kernel(const uint16_t *__re
     const int a_slot = lane & 7;
     const int a_c[2] = {a_slot ^ ((lane >> 4) & 7), a_slot ^ ((4 + (lane >> 4)) & 7)}; // unit for even / odd j
     const int64_t a_row_base = m0 + 32 * wave < M ? m0 + 32 * wave : M - 1;
-    const Rsrc a_rsrc = make_rsrc(reinterpret_cast<const uint8_t *>(x) + a_row_base * K * 2);
+    const Rsrc a_rsrc = make_rsrc(reinterpret_cast<const uint8_t *>(x) + (a_row_base * lda + k_begin) * 2);
     uint32_t a_voff[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         int64_t row = m0 + 32 * wave + 8 * j + (lane >> 3);
         row = row < M ? row : M - 1;
-        a_voff[j] = (uint32_t)((row - a_row_base) * K * 2 + 16 * a_c[j & 1]);
+        a_voff[j] = (uint32_t)((row - a_row_base) * lda * 2 + 16 * a_c[j & 1]);
     }
     // The lane's unit of stage s starts s * 128 bytes into the row; past
     // a_lim it would leave the row (a last stage that runs past K), so the
@@ -269,22 +303,22 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_kernel(const uint16_t *__re
     // ---- codes: wave w < kGBlocks fetches block w (1 KiB per k-tile; W8:
     //      per half).  Only these waves fetch codes and records and unpack;
     //      the others (the 64-column tile's waves 4 .. 7) load x only. ----
-    const int64_t my_blk = blk0 + wave < lay.nblocks ? blk0 + wave : 0; // blocks past N: any valid block
+    const int64_t my_blk = blk0 + wave < L.nblocks ? blk0 + wave : 0; // blocks past N: any valid block
     // one resource per block: a block (records and codes) is below 2^30 bytes
-    const Rsrc blk_rsrc = make_rsrc(packed + my_blk * lay.block_bytes);
+    const Rsrc blk_rsrc = make_rsrc(pk + my_blk * L.block_bytes);
     auto dma_codes = [&](int t, int half, int buf) {
-        const uint32_t soff = (uint32_t)lay.meta_bytes + (uint32_t)t * tile_bytes(BITS) + 1024u * half;
+        const uint32_t soff = (uint32_t)L.meta_bytes + (uint32_t)t * tile_bytes(BITS) + 1024u * half;
         dma16(blk_rsrc, 16 * lane, soff, sCodes + buf * kCodeBufBytes + wave * 1024);
     };
     // ---- records of k-tile t for block w, as dwords, into the buffer of
     //      k-tile tb (tb % 3); lanes past the records, or past the last
     //      group, read a dword of the block's first record instead ----
-    auto first_group = [&](int t) -> int64_t { return one_tile ? t : ((int64_t)t * kTileRows) / lay.G; };
+    auto first_group = [&](int t) -> int64_t { return one_tile ? t : ((int64_t)t * kTileRows) / L.G; };
     // (32-bit: a block's records are below 2^26 bytes; lanes past kBlockMeta
     // re-read the first record's first dword)
     const int m_lane = lane < kBlockMeta / 4 ? lane : 0;
     const int m_grp = (4 * m_lane) / RB;
-    const int ngroups32 = (int)lay.ngroups;
+    const int ngroups32 = (int)L.ngroups;
     auto dma_meta = [&](int t, int tb) {
         const int g_first = (int)first_group(t);
         const uint32_t v = g_first + m_grp < ngroups32 ? (uint32_t)(g_first * RB + 4 * m_lane) : 0u;
@@ -298,7 +332,7 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_kernel(const uint16_t *__re
     auto code_buf = [&](int s) { return kW8 ? s % 3 : (s >> 1) & 1; };
     // group of 32-row step `step`
     auto group_of_step = [&](int step) -> int64_t {
-        return one_tile ? step >> 2 : ((int64_t)step * kStepRows) / lay.G;
+        return one_tile ? step >> 2 : ((int64_t)step * kStepRows) / L.G;
     };
 
     // ---- unpack stage sd into B buffer sd % 2 as exact bf16 (q - z), zero
@@ -361,7 +395,7 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_kernel(const uint16_t *__re
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             const float v = record_scale<BITS>(meta_rec(4 * wn + 2 * j + (l32 >> 4), t, g), r);
-            sc[j] = g < lay.ngroups ? v : 0.f;
+            sc[j] = g < L.ngroups ? v : 0.f;
         }
     };
     // the same, split into the raw loads and their decoding
@@ -373,7 +407,7 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_kernel(const uint16_t *__re
     auto scales_decode = [&](int64_t g, const uint32_t (&sb)[2], float (&sc)[2]) {
 #pragma unroll
         for (int j = 0; j < 2; ++j)
-            sc[j] = g < lay.ngroups ? __uint_as_float(sb[j] << 16) : 0.f;
+            sc[j] = g < L.ngroups ? __uint_as_float(sb[j] << 16) : 0.f;
     };
 
     // ---- accumulator chains (even / odd groups) and their current scales ----
@@ -565,8 +599,8 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_kernel(const uint16_t *__re
 #pragma unroll
                         for (int j = 0; j < 2; ++j)
                             acc[0][i][j] = mfma32x32x16(af[cur][i], bf[cur][j], acc[0][i][j]);
-                    if (sig == 7 && (t + 1) % (int)lay.tiles_per_group == 0 && t + 1 < ktiles) {
-                        start_fold(ic<0>{}, (int64_t)(t + 1) / lay.tiles_per_group, t + 1, true);
+                    if (sig == 7 && (t + 1) % (int)L.tiles_per_group == 0 && t + 1 < ktiles) {
+                        start_fold(ic<0>{}, (int64_t)(t + 1) / L.tiles_per_group, t + 1, true);
                         fold_chunk(ic<0>{}, ic<0>{}, ic<1>{});
                     }
                 } else {
@@ -575,7 +609,7 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_kernel(const uint16_t *__re
                     if constexpr (fold_start) {
                         float sn[2];
                         scales_decode(fold_g, fold_sb, sn);
-                        start_fold_with(ic<F>{}, sn, fold_g >= 2 && fold_g < lay.ngroups);
+                        start_fold_with(ic<F>{}, sn, fold_g >= 2 && fold_g < L.ngroups);
                     }
 #pragma unroll
                     for (int i = 0; i < MI; ++i)
@@ -622,7 +656,7 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_kernel(const uint16_t *__re
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
         const int64_t col = n0 + 64 * wn + 32 * j + l32;
-        if (col >= lay.N)
+        if (col >= L.N)
             continue;
 #pragma unroll
         for (int i = 0; i < MI; ++i)
@@ -631,8 +665,12 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_kernel(const uint16_t *__re
                 const int64_t row = m0 + 32 * MI * wm + 32 * i + 8 * (e >> 2) + 4 * h32 + (e & 3);
                 const float v = kMode == kGWhole ? acc[0][i][j][e] * s_last[0][j]
                                                  : fmaf(acc[0][i][j][e], s_last[0][j], acc[1][i][j][e] * s_last[1][j]);
-                if (row < M)
-                    y[row * lay.N + col] = f32_to_bf16_bits(v);
+                if (row < M) {
+                    if (splits > 1)
+                        ws[((int64_t)split * M + row) * L.N + col] = v;
+                    else
+                        y[row * L.N + col] = f32_to_bf16_bits(v);
+                }
             }
     }
 }
@@ -640,23 +678,53 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_kernel(const uint16_t *__re
 // The kernel needs more than the default 64 KiB of dynamic LDS; raise the
 // limit once per instantiation.
 template <int BITS, int kMode, int WN>
-static void launch_mode(int64_t tiles, int m_tiles, int64_t col0, hipStream_t stream, const uint16_t *x,
-                        const uint8_t *pk, uint16_t *y, const Layout &lay, int64_t M)
+static void launch_mode(int64_t wgs, int m_tiles, int64_t col0, const GemmPlan &plan, hipStream_t stream,
+                        const uint16_t *x, const uint8_t *pk, uint16_t *y, const Layout &lay, int64_t M, float *ws)
 {
     auto kern = &gemm_kernel<BITS, kMode, WN>;
     static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, gemm_lds(BITS, WN));
     (void)attr;
-    kern<<<dim3((unsigned)tiles), kGThreads, gemm_lds(BITS, WN), stream>>>(x, pk, y, lay, M, m_tiles, col0);
+    kern<<<dim3((unsigned)wgs), kGThreads, gemm_lds(BITS, WN), stream>>>(
+        x, pk, y, lay, M, m_tiles, col0, (int)plan.splits, (int)plan.split_tiles, ws);
+}
+
+// y = bf16(sum over s of ws[s]) for the M x N outputs, in split order.
+__global__ __launch_bounds__(256) void splitk_sum_kernel(const float *__restrict__ ws, int splits, int64_t mn,
+                                                         uint16_t *__restrict__ y)
+{
+    const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+    if (i >= mn)
+        return;
+    if (i + 4 <= mn) {
+        f32x4 v = *reinterpret_cast<const f32x4 *>(ws + i);
+        for (int s = 1; s < splits; ++s) {
+            const f32x4 w = *reinterpret_cast<const f32x4 *>(ws + s * mn + i);
+            v = v + w;
+        }
+        u32x2 o;
+        o[0] = pack_bf16x2(v[0], v[1]);
+        o[1] = pack_bf16x2(v[2], v[3]);
+        *reinterpret_cast<u32x2 *>(y + i) = o;
+    } else {
+        for (int64_t e = i; e < mn; ++e) {
+            float v = ws[e];
+            for (int s = 1; s < splits; ++s)
+                v += ws[s * mn + e];
+            y[e] = f32_to_bf16_bits(v);
+        }
+    }
 }
 
 namespace {
 std::atomic<int> g_planning_cus{0};
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_device_cus[kMaxDevices];
+} // namespace
 
-// compute units of the current device (queried once per device)
-int device_cus()
+// compute units the plan assumes: the forced count, else the current
+// device's (queried once per device)
+int planning_cus()
 {
     if (const int forced = g_planning_cus.load(std::memory_order_relaxed))
         return forced;
@@ -671,18 +739,39 @@ int device_cus()
     }
     return n;
 }
-} // namespace
 
 void set_planning_cus(int n) { g_planning_cus.store(n > 0 ? n : 0, std::memory_order_relaxed); }
 
-GemmPlan plan_gemm(int64_t M, int64_t N, int cus)
+GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, int64_t G, int cus)
 {
     GemmPlan p;
     p.m_tiles = (M + kGBM - 1) / kGBM;
     const int64_t n_wide = (N + tile_cols(2) - 1) / tile_cols(2);
     const int64_t tiles = p.m_tiles * n_wide;
-    p.wide_cols = n_wide; // default: one launch of 128-column tiles
+    const int64_t ktiles = (K + kTileRows - 1) / kTileRows;
+    p.wide_cols = n_wide; // default: one launch of 128-column tiles over all of K
     p.narrow_cols = 0;
+    p.splits = 1;
+    p.split_tiles = ktiles;
+    // Few output tiles (small M): split K so that the chip fills.  A range
+    // holds at least 4 k-tiles and starts on a group boundary; each range
+    // writes fp32 partial sums that a second kernel adds in range order.
+    if (2 * tiles <= cus && ktiles >= 8) {
+        const int64_t unit = (G % kTileRows == 0 && G != K) ? G / kTileRows : 1; // k-tiles per boundary step
+        int64_t s = cus / tiles;
+        s = s < 8 ? s : 8;
+        s = s < ktiles / 4 ? s : ktiles / 4;
+        if (s >= 2) {
+            int64_t st = (ktiles + s - 1) / s;
+            st = (st + unit - 1) / unit * unit;
+            s = (ktiles + st - 1) / st;
+            if (s >= 2) {
+                p.splits = s;
+                p.split_tiles = st;
+                return p;
+            }
+        }
+    }
     if (tiles % cus == 0)
         return p;
     // the whole rounds with 128-column tiles, the columns left over as
@@ -699,10 +788,17 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int cus)
     return p;
 }
 
-hipError_t launch_gemm(int bits, const uint16_t *x, const void *packed, uint16_t *y, int64_t M, const Layout &lay,
-                       hipStream_t stream)
+int64_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t G)
 {
-    const GemmPlan plan = plan_gemm(M, lay.N, device_cus());
+    const GemmPlan p = plan_gemm(M, N, K, G, planning_cus());
+    return p.splits > 1 ? p.splits * M * N * (int64_t)sizeof(float) : 0;
+}
+
+hipError_t launch_gemm(int bits, const uint16_t *x, const void *packed, uint16_t *y, int64_t M, const Layout &lay,
+                       void *workspace, hipStream_t stream)
+{
+    const GemmPlan plan = plan_gemm(M, lay.N, lay.K, lay.G, planning_cus());
+    float *ws = plan.splits > 1 ? static_cast<float *>(workspace) : nullptr;
     const uint8_t *pk = static_cast<const uint8_t *>(packed);
     const int mode = lay.tiles_per_group == 1 ? kGOneTile
                      : lay.whole_tiles()      ? kGWhole
@@ -711,12 +807,12 @@ hipError_t launch_gemm(int bits, const uint16_t *x, const void *packed, uint16_t
     const int mt = (int)plan.m_tiles;
     auto go = [&](auto bits_c, auto wn_c, int64_t n_cols, int64_t col0) {
         constexpr int B = decltype(bits_c)::value, WN = decltype(wn_c)::value;
-        const int64_t tiles = plan.m_tiles * n_cols;
+        const int64_t wgs = plan.m_tiles * n_cols * plan.splits;
         switch (mode) {
-        case kGOneTile: launch_mode<B, kGOneTile, WN>(tiles, mt, col0, stream, x, pk, y, lay, M); break;
-        case kGWhole: launch_mode<B, kGWhole, WN>(tiles, mt, col0, stream, x, pk, y, lay, M); break;
-        case kGSplit32: launch_mode<B, kGSplit32, WN>(tiles, mt, col0, stream, x, pk, y, lay, M); break;
-        default: launch_mode<B, kGSplit64, WN>(tiles, mt, col0, stream, x, pk, y, lay, M); break;
+        case kGOneTile: launch_mode<B, kGOneTile, WN>(wgs, mt, col0, plan, stream, x, pk, y, lay, M, ws); break;
+        case kGWhole: launch_mode<B, kGWhole, WN>(wgs, mt, col0, plan, stream, x, pk, y, lay, M, ws); break;
+        case kGSplit32: launch_mode<B, kGSplit32, WN>(wgs, mt, col0, plan, stream, x, pk, y, lay, M, ws); break;
+        default: launch_mode<B, kGSplit64, WN>(wgs, mt, col0, plan, stream, x, pk, y, lay, M, ws); break;
         }
     };
     auto both = [&](auto bits_c) {
@@ -729,6 +825,11 @@ hipError_t launch_gemm(int bits, const uint16_t *x, const void *packed, uint16_t
         both(ic<4>{});
     else
         both(ic<8>{});
+    if (plan.splits > 1) {
+        const int64_t mn = M * lay.N;
+        const int64_t grid = (mn + 4 * 256 - 1) / (4 * 256);
+        splitk_sum_kernel<<<dim3((unsigned)grid), 256, 0, stream>>>(ws, (int)plan.splits, mn, y);
+    }
     return hipGetLastError();
 }
 

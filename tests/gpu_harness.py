@@ -104,13 +104,21 @@ class planning_cus:
         self.q.tf_gemm_set_planning_cus(0)
 
 
-def split_cus(q, M, N):
-    """A compute-unit count for which the GEMM plan of (M, N) has both wide
-    and narrow tiles, or None if no count gives one."""
+def split_cus(q, bits, M, K, N, G):
+    """A compute-unit count for which the GEMM plan has both 128- and
+    64-column tiles and does not split K, or None if no count gives one."""
     mt = -(-M // 256)
     tiles = mt * -(-N // 128)
     for cus in range(2, tiles + 1):
-        _, wide, narrow = q.tf_gemm_plan(M, N, cus)
-        if wide and narrow:
+        _, wide, narrow, splits, _ = q.tf_gemm_plan(bits, M, K, N, G, cus)
+        if wide and narrow and splits == 1:
+            return cus
+    return None
+
+
+def splitk_cus(q, bits, M, K, N, G):
+    """A compute-unit count for which the GEMM plan splits K, or None."""
+    for cus in (256, 1024, 4096, 1 << 20):
+        if q.tf_gemm_plan(bits, M, K, N, G, cus)[3] > 1:
             return cus
     return None

@@ -91,41 +91,71 @@ def test_packed_bytes_invalid_shapes_are_zero(lib, K, N, G):
 @pytest.mark.parametrize("M,K,N,G", [(1, 4096, 4096, 128), (8, 14336, 4096, 128), (16, 4096, 1024, 128),
                                      (1, 8192, 8192, 8192), (512, 8192, 8192, 8192), (2048, 4096, 14336, 128)])
 def test_workspace_cannot_hold_bf16_weights(lib, M, K, N, G):
-    # The layer never materialises full-precision weights: the only scratch it
-    # takes is far smaller than a bf16 copy of W.
+    # The layer never materialises full-precision weights: its only scratch is
+    # fp32 partial outputs of a K split (at most 8 x M x N), smaller than a
+    # bf16 copy of W for every shape here.
     for bits in (4, 8):
         for gemm in (0, 1):
             if not gemm and M > 16:
                 continue
-            assert lib.tf_workspace_bytes(bits, gemm, M, K, N, G) < K * N * 2 // 8
+            ws = lib.tf_workspace_bytes(bits, gemm, M, K, N, G)
+            assert ws <= 8 * M * N * 4
+            assert ws < K * N * 2
 
 
-def test_no_kernel_needs_a_workspace(lib):
-    for args in [(4, 0, 1, 4096, 4096, 128), (8, 1, 512, 8192, 8192, 8192), (5, 0, 1, 4096, 4096, 128)]:
-        assert lib.tf_workspace_bytes(*args) == 0
-
-
-def _plan(lib, M, N, cus):
-    out = (ctypes.c_int64 * 3)()
-    st = lib.tf_gemm_plan(M, N, cus, out)
+def _plan(lib, M, N, cus, K=4096, G=128, bits=4):
+    out = (ctypes.c_int64 * 5)()
+    st = lib.tf_gemm_plan(bits, M, K, N, G, cus, out)
     return st, tuple(out)
+
+
+def test_workspace_only_for_split_k_gemm(lib):
+    """The GEMV never needs scratch memory; the GEMM needs S x M x N fp32
+    partial sums exactly when its plan splits K (this host has no GPU, so the
+    plan assumes the library's default of 256 compute units)."""
+    assert lib.tf_workspace_bytes(4, 0, 1, 4096, 4096, 128) == 0
+    assert lib.tf_workspace_bytes(8, 0, 16, 8192, 8192, 8192) == 0
+    assert lib.tf_workspace_bytes(5, 1, 1, 4096, 4096, 128) == 0
+    for bits, M, K, N, G in [(8, 512, 8192, 8192, 8192), (4, 1, 4096, 4096, 128), (4, 2048, 4096, 14336, 128),
+                             (4, 100, 1024, 200, 64), (4, 64, 384, 64, 128)]:
+        st, (_, _, _, splits, _) = _plan(lib, M, N, 256, K=K, G=G, bits=bits)
+        assert st == TF_OK
+        want = splits * M * N * 4 if splits > 1 else 0
+        assert lib.tf_workspace_bytes(bits, 1, M, K, N, G) == want
+    assert _plan(lib, 512, 8192, 256, K=8192, G=8192, bits=8)[1][3] == 2   # W8 M=512: two K ranges
+    assert _plan(lib, 2048, 14336, 256)[1][3] == 1                         # prefill: no split
 
 
 def test_gemm_plan_covers_every_column_once(lib):
     """The launch plan: 128-column tiles from column 0, then 64-column tiles,
     covering [0, N) with no tile wholly past N; the narrow launch exists only
-    when the wide tiles miss a whole number of rounds and fits one round."""
+    when the wide tiles miss a whole number of rounds and fits one round.
+    A K split uses wide tiles only, fits one round, and its ranges of whole
+    groups cover the k-tiles exactly once."""
     rng = __import__("random").Random(7)
-    cases = [(2048, 14336, 256), (2048, 4096, 256), (512, 8192, 256), (1, 8192, 256), (4096, 32768, 256),
-             (1, 64, 256), (300, 24, 256), (513, 1048, 256), (4096, 28672, 304)]
-    cases += [(rng.randint(1, 9000), 8 * rng.randint(1, 5000), rng.choice([1, 2, 3, 7, 64, 80, 256, 304]))
-              for _ in range(400)]
-    for M, N, cus in cases:
-        st, (mt, wide, narrow) = _plan(lib, M, N, cus)
-        assert st == TF_OK
+    cases = [(2048, 14336, 256, 4096, 128), (2048, 4096, 256, 14336, 128), (512, 8192, 256, 8192, 8192),
+             (1, 8192, 256, 4096, 128), (4096, 32768, 256, 8192, 128), (1, 64, 256, 256, 128), (300, 24, 256, 512, 64),
+             (513, 1048, 256, 4128, 32), (4096, 28672, 304, 8192, 128), (64, 4096, 256, 8192, 512)]
+    for _ in range(400):
+        G = rng.choice([32, 64, 128, 256, 512])
+        K = G * rng.randint(1, 40) if G >= 128 else 128 * rng.randint(1, 40)
+        cases.append((rng.randint(1, 9000), 8 * rng.randint(1, 5000), rng.choice([1, 2, 3, 7, 64, 80, 256, 304]),
+                      K, rng.choice([G, K])))
+    for M, N, cus, K, G in cases:
+        st, (mt, wide, narrow, splits, st_tiles) = _plan(lib, M, N, cus, K=K, G=G)
+        assert st == TF_OK, (M, N, cus, K, G)
         n_wide = -(-N // 128)
         tiles = mt * n_wide
+        ktiles = -(-K // 128)
         assert mt == -(-M // 256)
+        if splits > 1:
+            assert wide == n_wide and narrow == 0
+            assert splits * tiles <= cus
+            assert (splits - 1) * st_tiles < ktiles <= splits * st_tiles
+            unit = G // 128 if G % 128 == 0 and G != K else 1
+            assert st_tiles % unit == 0 and st_tiles >= 4
+            continue
+        assert st_tiles == ktiles
         if narrow == 0:
             assert wide == n_wide
         else:
@@ -134,15 +164,18 @@ def test_gemm_plan_covers_every_column_once(lib):
             assert mt * narrow <= cus
             assert mt * wide <= (tiles // cus) * cus
     # the headline prefill shape: 3 whole rounds of wide tiles, one of narrow
-    assert _plan(lib, 2048, 14336, 256)[1] == (8, 96, 32)
-    assert _plan(lib, 2048, 4096, 256)[1] == (8, 32, 0)
+    assert _plan(lib, 2048, 14336, 256)[1] == (8, 96, 32, 1, 32)
+    assert _plan(lib, 2048, 4096, 256, K=14336)[1] == (8, 32, 0, 1, 112)
 
 
 def test_gemm_plan_rejects_bad_input(lib):
     assert _plan(lib, 0, 64, 256)[0] == TF_ERR_SHAPE
     assert _plan(lib, 64, 0, 256)[0] == TF_ERR_SHAPE
     assert _plan(lib, 64, 64, 0)[0] == TF_ERR_SHAPE
-    assert lib.tf_gemm_plan(64, 64, 256, None) == TF_ERR_NULL
+    assert _plan(lib, 64, 64, 256, K=4096, G=96)[0] == TF_ERR_GROUP
+    out = (ctypes.c_int64 * 5)()
+    assert lib.tf_gemm_plan(4, 64, 4096, 64, 128, 256, None) == TF_ERR_NULL
+    assert lib.tf_gemm_plan(5, 64, 4096, 64, 128, 256, out) == 6  # TF_ERR_UNSUPPORTED
 
 
 FAKE = 0x10000  # a 64 KiB-aligned fake device address; never dereferenced

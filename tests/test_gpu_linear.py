@@ -7,7 +7,7 @@ import pytest
 import oracle
 import synth
 from gpu_harness import (bf16_bits, bf16_to_f64, check_linear, gpu_or_skip, linear_fn, planning_cus, repack,
-                         split_cus, to_device)
+                         split_cus, splitk_cus, to_device)
 
 pytestmark = pytest.mark.gpu
 
@@ -27,6 +27,9 @@ GEMM_SHAPES = [
     (4, 1, 256, 64, 128), (4, 33, 512, 200, 128), (4, 130, 1024, 136, 64), (4, 257, 384, 128, 384),
     (4, 64, 96, 64, 32), (4, 300, 2048, 320, 128), (8, 77, 512, 100, 512), (8, 128, 256, 256, 32),
     (8, 200, 1024, 192, 128),
+    # K splits: groups of four k-tiles (ranges on group boundaries), one group
+    # over all of K (each range a one-group layout), a ragged last k-tile
+    (4, 96, 4096, 256, 512), (8, 64, 3072, 128, 3072), (4, 40, 2080, 128, 32), (4, 16, 2048, 136, 64),
 ]
 
 
@@ -43,25 +46,26 @@ def test_gemv_within_tolerance(shape):
     assert ok, f"worst error / bound = {ratio:.3f}"
 
 
-def _plan_cus(q, plan, M, N):
+def _plan_cus(q, plan, shape):
     """Compute units to plan for: the device's (auto), one (128-column tiles
-    only) or a count that splits the columns between both tile widths."""
+    only), a count that splits the columns between both tile widths, or one
+    that splits K."""
     if plan == "auto":
         return 0
     if plan == "wide":
         return 1
-    cus = split_cus(q, M, N)
+    cus = split_cus(q, *shape) if plan == "split" else splitk_cus(q, *shape)
     if cus is None:
-        pytest.skip("no compute-unit count splits this grid")
+        pytest.skip(f"no compute-unit count gives a '{plan}' plan for this grid")
     return cus
 
 
-@pytest.mark.parametrize("plan", ["auto", "wide", "split"])
+@pytest.mark.parametrize("plan", ["auto", "wide", "split", "splitk"])
 @pytest.mark.parametrize("shape", GEMM_SHAPES)
 def test_gemm_within_tolerance(shape, plan):
     torch, q = gpu_or_skip()
-    cus = _plan_cus(q, plan, shape[1], shape[3])
-    print(f"gemm {shape} plan={plan} cus={cus} {q.tf_gemm_plan(shape[1], shape[3], cus or 256)}", flush=True)
+    cus = _plan_cus(q, plan, shape)
+    print(f"gemm {shape} plan={plan} cus={cus} {q.tf_gemm_plan(*shape, cus or 256)}", flush=True)
     c = _case(*shape, seed=2)
     with planning_cus(q, cus):
         ok, ratio, _ = check_linear(c, torch, q, gemm=True)
@@ -72,17 +76,17 @@ def test_gemm_within_tolerance(shape, plan):
                                           (8, 40, 1024, 328, 1024)])
 def test_gemm_plans_agree_bitwise(bits, M, K, N, G):
     """Every tile width computes each output with the same operations in the
-    same order: all launch plans give identical bits."""
+    same order: all launch plans that do not split K give identical bits."""
     torch, q = gpu_or_skip()
     c = _case(bits, M, K, N, G, seed=5)
     d = to_device(c, torch)
     pk = repack(c, d, q)
     f = linear_fn(q, bits, True)
     outs = {}
-    for cus in (1, split_cus(q, M, N), 10**6):
+    for cus in (1, split_cus(q, bits, M, K, N, G)):
         if cus is None:
             continue
-        print(f"plans W{bits} M={M} K={K} N={N} G={G} cus={cus} {q.tf_gemm_plan(M, N, cus)}", flush=True)
+        print(f"plans W{bits} M={M} K={K} N={N} G={G} cus={cus} {q.tf_gemm_plan(bits, M, K, N, G, cus)}", flush=True)
         with planning_cus(q, cus):
             outs[cus] = bf16_bits(f(d["x"], pk, K, N, G))
     ref = outs[1]
