@@ -68,7 +68,8 @@ def parse():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--replicas", type=int, default=0, help="weight replicas to rotate (0: enough to beat the cache)")
-    p.add_argument("--only", choices=["all", "gemv", "gemm", "copy", "configs"], default="all",
+    p.add_argument("--only", choices=["all", "gemv", "gemm", "copy", "configs", "crossover", "energy"],
+                   default="all",
                    help="restrict the run (profiling passes); 'copy' runs the plain-copy calibration kernel")
     p.add_argument("--counters-from", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
                    help="no GPU: read four rocprofv3 --pmc output directories (FETCH_SIZE and WRITE_SIZE over "
@@ -574,6 +575,127 @@ def bench_configs(torch, q, args):
     return out
 
 
+CROSSOVER_MS = (1, 2, 4, 8, 12, 16, 24, 32, 48, 64, 96, 128, 192, 256)
+
+
+def bench_crossover(torch, q, args):
+    """GEMV against GEMM on the decoder layer (four fused launches, W4, group
+    128) at M = 1 ... 256: microseconds per layer pass for each kernel that
+    accepts the M, queued back to back over weight replicas larger than
+    twice the Infinity Cache, and which of the two is faster."""
+    import synth
+
+    lins = stage_layer(torch, q, synth, M=1)
+    fused = fuse_layer(torch, q, lins)
+    del lins
+    R = max(2, -(-2 * INFINITY_CACHE_BYTES // sum(f["packed"].numel() for f in fused)) + 1)
+    reps = [[f["packed"] for f in fused]] + [[f["packed"].clone() for f in fused] for _ in range(R - 1)]
+    flops1 = sum(2.0 * f["K"] * f["N"] for f in fused)
+    out = []
+    for M in CROSSOVER_MS:
+        xs = [torch.randn((M, f["K"]), device="cuda:0").to(torch.bfloat16) for f in fused]
+        ys = [torch.empty((M, f["N"]), dtype=torch.bfloat16, device="cuda:0") for f in fused]
+        lb = sum(algorithmic_bytes(4, M, f["K"], f["N"], f["G"]) for f in fused)
+        row = dict(M=M, layer_bytes=int(lb))
+        kernels = [("gemv", q.tf_gemv_w4a16)] if M <= 16 else []
+        kernels.append(("gemm", q.tf_gemm_w4a16))
+        for name, fn in kernels:
+            def step(i, fn=fn, xs=xs, ys=ys):
+                for f, p, x, y in zip(fused, reps[i % R], xs, ys):
+                    fn(x, p, f["K"], f["N"], f["G"], y=y)
+
+            step(0)
+            ms = time_queued(torch, step, 40, enqueue_us=host_us_per_step(step, R))
+            row[name] = dict(us=round(ms * 1e3, 2), gbs=round(lb / (ms * 1e-3) / 1e9, 1),
+                             tflops=round(flops1 * M / (ms * 1e-3) / 1e12, 1))
+        row["faster"] = min((k for k in ("gemv", "gemm") if k in row), key=lambda k: row[k]["us"])
+        out.append(row)
+        del xs, ys
+    del reps, fused
+    torch.cuda.empty_cache()
+    return out
+
+
+def bench_energy(torch, q, args, seconds=2.0):
+    """Energy per call from the GPU's energy accumulator (amdsmi), read around
+    about `seconds` of back-to-back calls: the decoder layer's GEMV pass at
+    M=1 and the prefill GEMM at M=2048, beside the idle draw over the same
+    time.  The accumulator updates about once a millisecond, so each window
+    is long; the figures are board energy, idle included."""
+    try:
+        import amdsmi
+
+        amdsmi.amdsmi_init()
+        handle = amdsmi.amdsmi_get_processor_handles()[0]
+    except Exception as exc:  # no SMI access on this machine
+        return dict(available=False, reason=f"{type(exc).__name__}: {exc}")
+
+    import synth
+
+    def joules():
+        e = amdsmi.amdsmi_get_energy_count(handle)
+        return e["energy_accumulator"] * e["counter_resolution"] * 1e-6
+
+    def window(run_one, calls_per_run):
+        run_one(0)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        n = 0
+        while time.perf_counter() - t0 < 0.3:  # settle the clocks
+            run_one(n)
+            n += 1
+        torch.cuda.synchronize()
+        j0, t0 = joules(), time.perf_counter()
+        n = 0
+        while time.perf_counter() - t0 < seconds:
+            run_one(n)
+            n += 1
+            if n % 64 == 0:
+                torch.cuda.synchronize()
+        torch.cuda.synchronize()
+        j1, t1 = joules(), time.perf_counter()
+        calls = n * calls_per_run
+        return dict(calls=calls, seconds=round(t1 - t0, 3), joules=round(j1 - j0, 3),
+                    watts=round((j1 - j0) / (t1 - t0), 1), uj_per_call=round((j1 - j0) / calls * 1e6, 2))
+
+    torch.cuda.synchronize()
+    j0, t0 = joules(), time.perf_counter()
+    time.sleep(seconds)
+    idle_w = (joules() - j0) / (time.perf_counter() - t0)
+
+    lins = stage_layer(torch, q, synth, M=1)
+    fused = fuse_layer(torch, q, lins)
+    del lins
+    R = max(2, -(-2 * INFINITY_CACHE_BYTES // sum(f["packed"].numel() for f in fused)) + 1)
+    reps = [[f["packed"] for f in fused]] + [[f["packed"].clone() for f in fused] for _ in range(R - 1)]
+
+    def layer_pass(i):
+        for f, p in zip(fused, reps[i % R]):
+            q.tf_gemv_w4a16(f["x"], p, f["K"], f["N"], f["G"], y=f["y"])
+
+    gemv = window(layer_pass, 1)
+    gemv.update(kernel="gemv W4A16 M=1, decoder layer pass (four launches)")
+    del reps, fused
+
+    c = synth.make_case(3, 0, 2048, keep_codes=False)
+    import numpy as np
+
+    dev = "cuda:0"
+    packed = q.tf_repack_w4(torch.from_numpy(c.qweight.view(np.int32)).to(dev),
+                            torch.from_numpy(c.qzeros.view(np.int32)).to(dev),
+                            torch.from_numpy(c.scales.view(np.int16)).to(dev), c.K, c.N, c.G)
+    x = torch.from_numpy(c.x.view(np.int16)).to(dev).view(torch.bfloat16)
+    y = torch.empty((c.M, c.N), dtype=torch.bfloat16, device=dev)
+    gemm = window(lambda i: q.tf_gemm_w4a16(x, packed, c.K, c.N, c.G, y=y), 1)
+    gemm.update(kernel=f"gemm W4A16 M={c.M} K={c.K} N={c.N}",
+                tflop_per_joule=round(2.0 * c.M * c.K * c.N * gemm["calls"] / 1e12 / gemm["joules"], 3))
+    try:
+        amdsmi.amdsmi_shut_down()
+    except Exception:
+        pass
+    return dict(available=True, idle_watts=round(idle_w, 1), gemv=gemv, gemm=gemm)
+
+
 def main():
     args = parse()
     if args.counters_from:
@@ -625,6 +747,10 @@ def main():
         line["gemm"] = bench_gemm(torch, q, args)
     if args.only == "configs" or (args.only == "all" and not args.no_configs):
         line["configs"] = bench_configs(torch, q, args)
+    if args.only == "crossover":
+        line["crossover"] = bench_crossover(torch, q, args)
+    if args.only == "energy":
+        line["energy"] = bench_energy(torch, q, args)
     if args.only == "all" and not args.no_cpu:
         import oracle
         import synth
