@@ -80,6 +80,8 @@ def parse():
                    help="time only the fused four-launch layer (counter passes: every GEMV dispatch is one "
                         "of the four launches the roofline is computed over)")
     p.add_argument("--gemm-iters", type=int, default=20)
+    p.add_argument("--crossover-ms", default=None,
+                   help="comma-separated M values for '--only crossover' (default: 1 ... 256)")
     return p.parse_args()
 
 
@@ -580,9 +582,10 @@ CROSSOVER_MS = (1, 2, 4, 8, 12, 16, 24, 32, 48, 64, 96, 128, 192, 256)
 
 def bench_crossover(torch, q, args):
     """GEMV against GEMM on the decoder layer (four fused launches, W4, group
-    128) at M = 1 ... 256: microseconds per layer pass for each kernel that
-    accepts the M, queued back to back over weight replicas larger than
-    twice the Infinity Cache, and which of the two is faster."""
+    128) at M = 1 ... 256: microseconds per layer pass for each entry point
+    that accepts the M (tf_gemm as routed, and up to M = 64 also forced onto
+    the tiled GEMM), queued back to back over weight replicas larger than
+    twice the Infinity Cache, and which is fastest."""
     import synth
 
     lins = stage_layer(torch, q, synth, M=1)
@@ -592,14 +595,18 @@ def bench_crossover(torch, q, args):
     reps = [[f["packed"] for f in fused]] + [[f["packed"].clone() for f in fused] for _ in range(R - 1)]
     flops1 = sum(2.0 * f["K"] * f["N"] for f in fused)
     out = []
-    for M in CROSSOVER_MS:
+    ms_list = [int(v) for v in args.crossover_ms.split(",")] if args.crossover_ms else CROSSOVER_MS
+    for M in ms_list:
         xs = [torch.randn((M, f["K"]), device="cuda:0").to(torch.bfloat16) for f in fused]
         ys = [torch.empty((M, f["N"]), dtype=torch.bfloat16, device="cuda:0") for f in fused]
         lb = sum(algorithmic_bytes(4, M, f["K"], f["N"], f["G"]) for f in fused)
         row = dict(M=M, layer_bytes=int(lb))
-        kernels = [("gemv", q.tf_gemv_w4a16)] if M <= 16 else []
-        kernels.append(("gemm", q.tf_gemm_w4a16))
-        for name, fn in kernels:
+        kernels = [("gemv", q.tf_gemv_w4a16, 0)] if M <= 16 else []
+        kernels.append(("gemm", q.tf_gemm_w4a16, 0))
+        if M <= 64:  # the GEMM call runs the GEMV kernel; the tiled GEMM beside it
+            kernels.append(("gemm_tiled", q.tf_gemm_w4a16, 1))
+        for name, fn, route in kernels:
+            q.tf_gemm_set_route(route)
             def step(i, fn=fn, xs=xs, ys=ys):
                 for f, p, x, y in zip(fused, reps[i % R], xs, ys):
                     fn(x, p, f["K"], f["N"], f["G"], y=y)
@@ -608,7 +615,8 @@ def bench_crossover(torch, q, args):
             ms = time_queued(torch, step, 40, enqueue_us=host_us_per_step(step, R))
             row[name] = dict(us=round(ms * 1e3, 2), gbs=round(lb / (ms * 1e-3) / 1e9, 1),
                              tflops=round(flops1 * M / (ms * 1e-3) / 1e12, 1))
-        row["faster"] = min((k for k in ("gemv", "gemm") if k in row), key=lambda k: row[k]["us"])
+            q.tf_gemm_set_route(0)
+        row["faster"] = min((k for k in ("gemv", "gemm", "gemm_tiled") if k in row), key=lambda k: row[k]["us"])
         out.append(row)
         del xs, ys
     del reps, fused

@@ -113,10 +113,11 @@ int tf_repack_w8(const uint8_t *qweight, const uint8_t *zeros, const uint16_t *s
 /*              nearest-even), 2-byte aligned                                */
 /*   workspace  device scratch of ws_bytes >= tf_workspace_bytes(...), 256-  */
 /*              byte aligned.  NULL is fine when the size query returns 0:   */
-/*              always for the GEMV; for the GEMM unless it splits K (few    */
-/*              output tiles, i.e. small M).  The size depends on the device */
-/*              the query runs on (its compute-unit count): query on the     */
-/*              device the GEMM will run on.                                 */
+/*              always for tf_gemv_* (M <= 16); for tf_gemm_* unless it      */
+/*              splits K over workgroups (small M, or 17 <= M <= 64 on a     */
+/*              layer too narrow to fill the device).  The size depends on   */
+/*              the device the query runs on (its compute-unit count): query */
+/*              on the device the call will run on.                          */
 /* ------------------------------------------------------------------------ */
 size_t tf_workspace_bytes(int bits, int is_gemm, int64_t M, int64_t K, int64_t N, int64_t G);
 
@@ -128,10 +129,13 @@ int tf_gemv_w8a16(const uint16_t *x, const void *packed, size_t packed_bytes, ui
                   int64_t M, int64_t K, int64_t N, int64_t G,
                   void *workspace, size_t ws_bytes, void *stream);
 
-/* Prefill GEMM, any M >= 1: each weight tile is unpacked once into LDS as the
- * exact bf16 values q - z and reused by every row of the tile; each group's
- * scale is applied once per (group, column) to its fp32 partial sum
- * (Methodology section 1). */
+/* Prefill GEMM, any M >= 1 (Methodology section 1): each weight tile is
+ * unpacked once into LDS as the exact bf16 values q - z and reused by every
+ * row of a 256-row tile; each group's scale is applied once per (group,
+ * column) to its fp32 partial sum.  For M <= 64 a 256-row tile would mostly
+ * compute padding, so the call runs the GEMV kernel instead, with up to four
+ * 16-row chunks of x per wave (and K split over workgroups on narrow layers);
+ * the result meets the same tolerance, not the tiled kernel's bits. */
 int tf_gemm_w4a16(const uint16_t *x, const void *packed, size_t packed_bytes, uint16_t *y,
                   int64_t M, int64_t K, int64_t N, int64_t G,
                   void *workspace, size_t ws_bytes, void *stream);
@@ -156,17 +160,22 @@ int tf_dequant_w8_f32(const void *packed, size_t packed_bytes, float *w,
  * to the workspace, and a second kernel adds them in range order (so
  * tf_workspace_bytes is non-zero for those shapes).  The plan never changes
  * the result's bits except through that split: the order of the split sums.
- *   tf_gemm_plan: writes out[0] = row tiles, out[1] = 128-column tiles,
- *     out[2] = 64-column tiles, out[3] = K ranges, out[4] = k-tiles of 128
- *     rows per range, for a GEMM of (bits, M, K, N, G) on a device of `cus`
- *     compute units.  TF_ERR_NULL / TF_ERR_SHAPE / TF_ERR_GROUP /
- *     TF_ERR_UNSUPPORTED on bad input.
- *   tf_gemm_set_planning_cus: makes later GEMM calls and workspace queries
- *     of this process plan for n compute units instead of the current
- *     device's (n <= 0 restores the device's).  Process-wide; not meant to
- *     race with GEMM calls. */
+ *   tf_gemm_plan: writes six values for a GEMM of (bits, M, K, N, G) on a
+ *     device of `cus` compute units: out[5] = 1 when the call runs the GEMV
+ *     kernel (then out[0..2] = 0), 0 for the tiled GEMM; out[0] = row tiles,
+ *     out[1] = 128-column tiles, out[2] = 64-column tiles, out[3] = K ranges,
+ *     out[4] = k-tiles of 128 rows per range.  TF_ERR_NULL / TF_ERR_SHAPE /
+ *     TF_ERR_GROUP / TF_ERR_UNSUPPORTED on bad input.
+ *   tf_gemm_set_planning_cus: makes later GEMM and GEMV calls and workspace
+ *     queries of this process plan for n compute units instead of the
+ *     current device's (n <= 0 restores the device's).  Process-wide; not
+ *     meant to race with those calls.
+ *   tf_gemm_set_route: which kernel later tf_gemm_* calls with M <= 64 run:
+ *     0 (default) the GEMV kernel, 1 the tiled GEMM, 2 the GEMV kernel.
+ *     Other values act as 0.  Process-wide, like the above. */
 int tf_gemm_plan(int bits, int64_t M, int64_t K, int64_t N, int64_t G, int cus, int64_t *out);
 void tf_gemm_set_planning_cus(int n);
+void tf_gemm_set_route(int route);
 
 /* Measurement probes (not on the hot path): the practical roofs the fused
  * kernels are measured against, on the same machine and launch pattern.

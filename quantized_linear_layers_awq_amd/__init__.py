@@ -19,6 +19,7 @@ from ._binding import (  # noqa: F401
     tf_format_version,
     tf_gemm_plan,
     tf_gemm_set_planning_cus,
+    tf_gemm_set_route,
     tf_gemm_w4a16,
     tf_gemm_w8a16,
     tf_gemv_w4a16,

@@ -70,6 +70,8 @@ def load_library():
         L.tf_gemm_plan.restype = I
         L.tf_gemm_set_planning_cus.argtypes = [I]
         L.tf_gemm_set_planning_cus.restype = None
+        L.tf_gemm_set_route.argtypes = [I]
+        L.tf_gemm_set_route.restype = None
         L.tf_probe_stream_read.argtypes = [P, SZ, P, P]
         L.tf_probe_stream_read.restype = I
         L.tf_probe_mfma.argtypes = [I, I, P, ctypes.POINTER(I64), P]
@@ -227,12 +229,12 @@ def tf_dequant_w8_f32(packed, K, N, G, w=None, stream=None):
     return _dequant("tf_dequant_w8_f32", packed, K, N, G, w, stream)
 
 
-def tf_gemm_plan(bits: int, M: int, K: int, N: int, G: int, cus: int) -> tuple[int, int, int, int, int]:
+def tf_gemm_plan(bits: int, M: int, K: int, N: int, G: int, cus: int) -> tuple[int, int, int, int, int, int]:
     """Test hook: (row tiles, 128-column tiles, 64-column tiles, K ranges,
-    k-tiles per range) of the GEMM's launch plan on a device of `cus` compute
-    units (host only)."""
+    k-tiles per range, 1 if the call runs the GEMV kernel else 0) of a GEMM
+    call's launch plan on a device of `cus` compute units (host only)."""
     L = load_library()
-    out = (ctypes.c_int64 * 5)()
+    out = (ctypes.c_int64 * 6)()
     _check(L.tf_gemm_plan(bits, M, K, N, G, cus, out), "tf_gemm_plan")
     return tuple(int(v) for v in out)
 
@@ -241,6 +243,12 @@ def tf_gemm_set_planning_cus(n: int) -> None:
     """Test hook: later GEMM calls plan for n compute units (n <= 0: the
     device's own count).  Process-wide."""
     load_library().tf_gemm_set_planning_cus(int(n))
+
+
+def tf_gemm_set_route(route: int) -> None:
+    """Test hook: the kernel later GEMM calls with M <= 64 run (0 automatic,
+    1 the tiled GEMM, 2 the GEMV kernel).  Process-wide."""
+    load_library().tf_gemm_set_route(int(route))
 
 
 def tf_probe_stream_read(buf, sink, stream=None):

@@ -52,13 +52,17 @@ int repack(int bits, const void *qweight, const void *qzeros, const uint16_t *sc
     return TF_OK;
 }
 
-// The GEMV combines its K split inside a workgroup and needs no scratch
-// memory.  The GEMM needs fp32 partial sums when it splits K (few output
-// tiles: small M), S x M x N floats; otherwise none.
+// fp32 partial sums, S x M x N floats, when a call splits K over workgroups:
+// the tiled GEMM with few output tiles (small M), the GEMV kernel above 16
+// rows on a layer too narrow to fill the chip.  Otherwise none: the GEMV at
+// M <= 16 combines its K split inside a workgroup.
 size_t workspace_bytes(int bits, int is_gemm, int64_t M, int64_t K, int64_t N, int64_t G)
 {
-    if (!is_gemm || M < 1 || M > (int64_t(1) << 30) || check_kng(bits, K, N, G) != TF_OK)
+    if (M < 1 || M > (is_gemm ? (int64_t(1) << 30) : 16) || check_kng(bits, K, N, G) != TF_OK)
         return 0;
+    const Layout lay = Layout::make(bits, K, N, G);
+    if (!is_gemm || tf::gemm_uses_gemv(M))
+        return (size_t)tf::gemv_workspace_bytes(lay, M, tf::planning_cus());
     return (size_t)tf::gemm_workspace_bytes(M, N, K, G);
 }
 
@@ -92,10 +96,10 @@ int linear(int bits, bool is_gemm, const uint16_t *x, const void *packed, size_t
             return TF_ERR_BUFFER_TOO_SMALL;
     }
     hipError_t e;
-    if (is_gemm)
+    if (is_gemm && !tf::gemm_uses_gemv(M))
         e = tf::launch_gemm(bits, x, packed, y, M, lay, ws, static_cast<hipStream_t>(stream));
     else
-        e = tf::launch_gemv(bits, x, packed, y, M, lay, static_cast<hipStream_t>(stream));
+        e = tf::launch_gemv(bits, x, packed, y, M, lay, ws, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? TF_OK : TF_ERR_HIP;
 }
 
@@ -202,16 +206,30 @@ int tf_gemm_plan(int bits, int64_t M, int64_t K, int64_t N, int64_t G, int cus, 
         return TF_ERR_SHAPE;
     if (int st = check_kng(bits, K, N, G))
         return st;
+    if (tf::gemm_uses_gemv(M)) {
+        const Layout lay = Layout::make(bits, K, N, G);
+        int64_t st = 0;
+        out[0] = 0;
+        out[1] = 0;
+        out[2] = 0;
+        out[3] = tf::gemv_splits(lay, M, cus, &st);
+        out[4] = st;
+        out[5] = 1;
+        return TF_OK;
+    }
     const tf::GemmPlan p = tf::plan_gemm(M, N, K, G, cus);
     out[0] = p.m_tiles;
     out[1] = p.wide_cols;
     out[2] = p.narrow_cols;
     out[3] = p.splits;
     out[4] = p.split_tiles;
+    out[5] = 0;
     return TF_OK;
 }
 
 void tf_gemm_set_planning_cus(int n) { tf::set_planning_cus(n); }
+
+void tf_gemm_set_route(int route) { tf::set_gemm_route(route); }
 
 int tf_probe_stream_read(const void *buf, size_t bytes, uint32_t *sink, void *stream)
 {

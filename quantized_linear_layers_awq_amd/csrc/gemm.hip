@@ -689,19 +689,25 @@ static void launch_mode(int64_t wgs, int m_tiles, int64_t col0, const GemmPlan &
         x, pk, y, lay, M, m_tiles, col0, (int)plan.splits, (int)plan.split_tiles, ws);
 }
 
-// y = bf16(sum over s of ws[s]) for the M x N outputs, in split order.
-__global__ __launch_bounds__(256) void splitk_sum_kernel(const float *__restrict__ ws, int splits, int64_t mn,
+// y = bf16(sum over s of ws[s]) for the M x N outputs, in split order.  The
+// split count is a template parameter so that a thread issues all S loads
+// at once (one round trip) and then adds them in order.
+template <int S>
+__global__ __launch_bounds__(256) void splitk_sum_kernel(const float *__restrict__ ws, int64_t mn,
                                                          uint16_t *__restrict__ y)
 {
     const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
     if (i >= mn)
         return;
     if (i + 4 <= mn) {
-        f32x4 v = *reinterpret_cast<const f32x4 *>(ws + i);
-        for (int s = 1; s < splits; ++s) {
-            const f32x4 w = *reinterpret_cast<const f32x4 *>(ws + s * mn + i);
-            v = v + w;
-        }
+        f32x4 p[S];
+#pragma unroll
+        for (int s = 0; s < S; ++s)
+            p[s] = *reinterpret_cast<const f32x4 *>(ws + s * mn + i);
+        f32x4 v = p[0];
+#pragma unroll
+        for (int s = 1; s < S; ++s)
+            v = v + p[s];
         u32x2 o;
         o[0] = pack_bf16x2(v[0], v[1]);
         o[1] = pack_bf16x2(v[2], v[3]);
@@ -709,10 +715,38 @@ __global__ __launch_bounds__(256) void splitk_sum_kernel(const float *__restrict
     } else {
         for (int64_t e = i; e < mn; ++e) {
             float v = ws[e];
-            for (int s = 1; s < splits; ++s)
+#pragma unroll
+            for (int s = 1; s < S; ++s)
                 v += ws[s * mn + e];
             y[e] = f32_to_bf16_bits(v);
         }
+    }
+}
+
+template <int S> static void launch_sum(const float *ws, int64_t mn, uint16_t *y, hipStream_t stream)
+{
+    const int64_t grid = (mn + 4 * 256 - 1) / (4 * 256);
+    splitk_sum_kernel<S><<<dim3((unsigned)grid), 256, 0, stream>>>(ws, mn, y);
+}
+
+void launch_splitk_sum(const float *ws, int splits, int64_t mn, uint16_t *y, hipStream_t stream)
+{
+    switch (splits) {
+    case 2: launch_sum<2>(ws, mn, y, stream); break;
+    case 3: launch_sum<3>(ws, mn, y, stream); break;
+    case 4: launch_sum<4>(ws, mn, y, stream); break;
+    case 5: launch_sum<5>(ws, mn, y, stream); break;
+    case 6: launch_sum<6>(ws, mn, y, stream); break;
+    case 7: launch_sum<7>(ws, mn, y, stream); break;
+    case 8: launch_sum<8>(ws, mn, y, stream); break;
+    case 9: launch_sum<9>(ws, mn, y, stream); break;
+    case 10: launch_sum<10>(ws, mn, y, stream); break;
+    case 11: launch_sum<11>(ws, mn, y, stream); break;
+    case 12: launch_sum<12>(ws, mn, y, stream); break;
+    case 13: launch_sum<13>(ws, mn, y, stream); break;
+    case 14: launch_sum<14>(ws, mn, y, stream); break;
+    case 15: launch_sum<15>(ws, mn, y, stream); break;
+    default: launch_sum<16>(ws, mn, y, stream); break;
     }
 }
 
@@ -741,6 +775,18 @@ int planning_cus()
 }
 
 void set_planning_cus(int n) { g_planning_cus.store(n > 0 ? n : 0, std::memory_order_relaxed); }
+
+namespace {
+std::atomic<int> g_gemm_route{0};
+} // namespace
+
+bool gemm_uses_gemv(int64_t M)
+{
+    const int route = g_gemm_route.load(std::memory_order_relaxed);
+    return M <= kGemvKernelMaxM && route != 1;
+}
+
+void set_gemm_route(int route) { g_gemm_route.store(route == 1 || route == 2 ? route : 0, std::memory_order_relaxed); }
 
 GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, int64_t G, int cus)
 {
@@ -825,11 +871,8 @@ hipError_t launch_gemm(int bits, const uint16_t *x, const void *packed, uint16_t
         both(ic<4>{});
     else
         both(ic<8>{});
-    if (plan.splits > 1) {
-        const int64_t mn = M * lay.N;
-        const int64_t grid = (mn + 4 * 256 - 1) / (4 * 256);
-        splitk_sum_kernel<<<dim3((unsigned)grid), 256, 0, stream>>>(ws, (int)plan.splits, mn, y);
-    }
+    if (plan.splits > 1)
+        launch_splitk_sum(ws, (int)plan.splits, M * lay.N, y, stream);
     return hipGetLastError();
 }
 

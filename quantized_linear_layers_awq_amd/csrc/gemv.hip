@@ -1,6 +1,7 @@
 // Token-generation GEMV, M = 1..16 (TileFuse summary, Methodology section 3:
 // batch-1 GEMV, memory-bound at full precision; spread the weight stream over
-// the whole machine instead of a slice of it).
+// the whole machine instead of a slice of it), and the same dataflow for
+// 17..64 rows (gemv_mid_kernel below), which GEMM calls of that size run.
 //
 // MI355X design.  One workgroup owns one 16-column block of the packed buffer
 // -- a single contiguous byte range -- and its waves split K between them, so
@@ -30,6 +31,9 @@ namespace tf {
 
 constexpr int kGemvMaxWaves = 16;
 constexpr int kGemvTargetWaves = 4096; // about 16 per CU
+// K ranges of the 17..64-row GEMV: at least 2 k-tiles, at most 16 ranges
+constexpr int kGemvMinSplitTiles = 2;
+constexpr int kGemvMaxSplits = 16;
 
 // Eight W4 codes (one column, rows 0..7 of an octet) -> B operand of bf16
 // values 128 + q: OR-ing a nibble into the mantissa of bf16 128.0 (0x4300).
@@ -335,6 +339,293 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const uint16_t *__restrict__
     }
 }
 
+// ---- GEMV for 17..64 activation rows ----
+//
+// Above 16 rows every weight operand feeds MT = 2 or 4 row chunks of 16, so
+// one unpack serves up to 64 rows.  A workgroup is eight waves, one
+// 16-column block each (the activations staged in LDS serve 128 columns),
+// and K may be split over workgroups (gridDim.y ranges of split_tiles
+// k-tiles) whose fp32 partial sums a second kernel adds in range order.  Each
+// wave walks its range of k-tiles in one continuous ring of D code loads;
+// the range is staged in chunks of `tiles` k-tiles, double buffered: the
+// next chunk's activations and records are loaded into registers before the
+// current chunk's code refills are issued (vector-memory loads retire in
+// order, so storing them to LDS at the chunk's end never waits for codes in
+// flight), and one barrier per chunk separates the buffers' uses.
+constexpr int kMidWaves = 8;   // waves (blocks) per workgroup
+// activation units of 16 bytes staged per thread per chunk, by row chunks
+constexpr int mid_xregs(int mt) { return mt == 2 ? 8 : 8; }
+constexpr int kMidRecRegs = 4; // record words of 8 bytes per thread per chunk
+// k-tiles of codes in flight per wave: the chunk length, 8 or 4 (a chunk
+// holds 4096 / (16 M) k-tiles of activations: 8 up to 32 rows, 4 above)
+
+struct MidChunks {
+    int tiles;       // k-tiles per staged chunk (a multiple of the ring depth)
+    int xpitch;      // bf16 elements per staged activation row (chunk rows + 8)
+    int meta_cap;    // bytes per block of a chunk's records
+    int lds;         // dynamic LDS bytes: two record buffers, two x buffers
+    int split_tiles; // k-tiles per K range (gridDim.y ranges)
+};
+
+template <int BITS, int kMode, int MT, int D>
+__global__ __launch_bounds__(64 * kMidWaves) void gemv_mid_kernel(const uint16_t *__restrict__ x,
+                                                                 const uint8_t *__restrict__ packed,
+                                                                 uint16_t *__restrict__ y, Layout lay, int M,
+                                                                 MidChunks ch, float *__restrict__ ws)
+{
+    constexpr uint32_t TB = tile_bytes(BITS), RB = record_bytes(BITS);
+    constexpr int kThreads = 64 * kMidWaves;
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    const int meta_buf_bytes = kMidWaves * ch.meta_cap;
+    const int x_buf_bytes = M * ch.xpitch * 2;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int r = lane & 15, o = lane >> 4;
+    const int64_t blk0 = (int64_t)blockIdx.x * kMidWaves;
+    const int64_t blk = blk0 + wave;
+    const bool blk_ok = blk < lay.nblocks;
+    const uint8_t *tiles = packed + (blk_ok ? blk : 0) * lay.block_bytes + lay.meta_bytes + 16 * lane;
+    const int ktiles = (int)lay.ktiles;
+    const int split = blockIdx.y;
+    const int kt_begin = split * ch.split_tiles;
+    const int kt_end = kt_begin + ch.split_tiles < ktiles ? kt_begin + ch.split_tiles : ktiles;
+    const int nchunks = (kt_end - kt_begin + ch.tiles - 1) / ch.tiles;
+    // rows >= M are never stored; their lanes read row 0
+    const int xr = r < M ? r : 0;
+    int xoff[MT]; // row chunk c relative to chunk 0
+#pragma unroll
+    for (int c = 0; c < MT; ++c)
+        xoff[c] = c == 0 ? 0 : ((16 * c + r < M ? 16 * c + r : 0) - xr) * ch.xpitch;
+    const uint32_t magic = magic_in_vgpr();
+    const f32x4 zf = {0.f, 0.f, 0.f, 0.f};
+
+    // ---- staging of chunk cc: activations x[0:M][chunk] (zero past K) and
+    //      the records of the groups the chunk touches, for all eight blocks
+    constexpr int XR = mid_xregs(MT);
+    u32x4 xv[XR];
+    u32x2 mv[kMidRecRegs];
+    auto chunk_bounds = [&](int cc, int &c0, int &c1) {
+        c0 = kt_begin + cc * ch.tiles;
+        c1 = c0 + ch.tiles < kt_end ? c0 + ch.tiles : kt_end;
+    };
+    auto chunk_groups = [&](int c0, int c1, int64_t &g0, int &rec_words) {
+        const int64_t k0 = (int64_t)c0 * kTileRows;
+        const int64_t k1 = (int64_t)c1 * kTileRows < lay.K ? (int64_t)c1 * kTileRows : lay.K;
+        g0 = k0 / lay.G;
+        rec_words = (int)(((k1 - 1) / lay.G - g0 + 1) * RB / 8);
+    };
+    // Every thread issues the same loads on every path (addresses clamped
+    // into the buffers, unused values zeroed afterwards), so the
+    // vector-memory wait before the LDS stores counts exactly the loads
+    // issued after them and never drains the code ring.
+    auto stage_load = [&](int cc) {
+        int c0, c1;
+        chunk_bounds(cc, c0, c1);
+        const int64_t k0 = (int64_t)c0 * kTileRows;
+        const int upr = (c1 - c0) * (kTileRows / 8);
+        const int x_units = M * upr;
+#pragma unroll
+        for (int i = 0; i < XR; ++i) {
+            const int e = tid + i * kThreads;
+            const int ec = e < x_units ? e : x_units - 1;
+            const int m = ec / upr, u8 = ec - m * upr;
+            const int64_t k = k0 + 8 * u8;
+            xv[i] = load16(x + (int64_t)m * lay.K + (k < lay.K ? k : lay.K - 8));
+        }
+        int64_t g0;
+        int rw;
+        chunk_groups(c0, c1, g0, rw);
+#pragma unroll
+        for (int i = 0; i < kMidRecRegs; ++i) {
+            const int e = tid + i * kThreads;
+            const int eb = e / rw, w = e - eb * rw;
+            const bool ok = eb < kMidWaves && blk0 + eb < lay.nblocks;
+            const int64_t b = ok ? blk0 + eb : 0;
+            mv[i] = *reinterpret_cast<const u32x2 *>(packed + b * lay.block_bytes + g0 * RB + 8 * (ok ? w : 0));
+        }
+    };
+    auto stage_store = [&](int cc) {
+        int c0, c1;
+        chunk_bounds(cc, c0, c1);
+        uint8_t *mbuf = smem + (cc & 1) * meta_buf_bytes;
+        uint16_t *xbuf = reinterpret_cast<uint16_t *>(smem + 2 * meta_buf_bytes + (cc & 1) * x_buf_bytes);
+        const int upr = (c1 - c0) * (kTileRows / 8);
+        const int x_units = M * upr;
+        const int64_t k0 = (int64_t)c0 * kTileRows;
+#pragma unroll
+        for (int i = 0; i < XR; ++i) {
+            const int e = tid + i * kThreads;
+            if (e < x_units) {
+                const int m = e / upr, u8 = e - m * upr;
+                const bool in_k = k0 + 8 * u8 < lay.K; // columns past K stage as zero
+                *reinterpret_cast<u32x4 *>(xbuf + m * ch.xpitch + 8 * u8) = in_k ? xv[i] : u32x4{0u, 0u, 0u, 0u};
+            }
+        }
+        int64_t g0;
+        int rw;
+        chunk_groups(c0, c1, g0, rw);
+#pragma unroll
+        for (int i = 0; i < kMidRecRegs; ++i) {
+            const int e = tid + i * kThreads;
+            const int eb = e / rw, w = e - eb * rw;
+            if (eb < kMidWaves && blk0 + eb < lay.nblocks)
+                *reinterpret_cast<u32x2 *>(mbuf + eb * ch.meta_cap + 8 * w) = mv[i];
+        }
+    };
+
+    f32x4 yacc[MT], gacc[MT], zacc[MT];
+#pragma unroll
+    for (int c = 0; c < MT; ++c)
+        yacc[c] = gacc[c] = zacc[c] = zf;
+    TileCodes<BITS> ring[D];
+
+    // ---- prologue: chunk 0 staged, the ring filled with the first D tiles.
+    //      A wave past the last block streams block 0 and stores nothing.
+    stage_load(0);
+#pragma unroll
+    for (int j = 0; j < D; ++j)
+        load_codes<BITS>(ring[j], tiles + (uint32_t)(kt_begin + j < kt_end ? kt_begin + j : kt_end - 1) * TB);
+    stage_store(0);
+    __syncthreads();
+
+    // kMultiTile: tiles left in the current group, and the group
+    const int tpg = kMode == kMultiTile ? (int)lay.tiles_per_group : 1;
+    int64_t gcur = kt_begin / tpg;
+    int tg_left = tpg - (kt_begin - (int)gcur * tpg);
+    const int sh = lay.G == kStepRows ? 0 : 1; // kSplitTiles: G is 32 or 64
+
+    for (int cc = 0; cc < nchunks; ++cc) {
+        int c0, c1;
+        chunk_bounds(cc, c0, c1);
+        int64_t g0;
+        int rw;
+        chunk_groups(c0, c1, g0, rw);
+        const bool more = cc + 1 < nchunks;
+        const uint8_t *smeta = smem + (cc & 1) * meta_buf_bytes + wave * ch.meta_cap;
+        const uint16_t *xl = reinterpret_cast<const uint16_t *>(smem + 2 * meta_buf_bytes + (cc & 1) * x_buf_bytes) +
+                             xr * ch.xpitch + 8 * o - c0 * kTileRows;
+        // D k-tiles from tile i.  The next chunk's staging loads are issued
+        // after the chunk's first tile, ahead of its code refills: at that
+        // tile only codes are in flight, so its wait is exact, and storing
+        // the staged values at the chunk's end waits for none of the refills.
+        auto group = [&](int i, bool first) {
+#pragma unroll
+                for (int j = 0; j < D; ++j) {
+                    const int t = i + j;
+                    if (t < c1) {
+                        u32x4 ops[4];
+#pragma unroll
+                        for (int u = 0; u < 4; ++u)
+                            ops[u] = code_operand<BITS>(ring[j], u, magic);
+                        auto xfrag = [&](int c, int u) {
+                            return *reinterpret_cast<const u32x4 *>(xl + xoff[c] + t * kTileRows + kStepRows * u);
+                        };
+                        if constexpr (kMode == kOneTile) {
+                            const uint8_t *rg = smeta + (t - (int)g0) * RB;
+                            const u32x4 zop = zero_operand<BITS>(record_zero<BITS>(rg, r));
+#pragma unroll
+                            for (int c = 0; c < MT; ++c) {
+                                u32x4 xa[4];
+#pragma unroll
+                                for (int u = 0; u < 4; ++u)
+                                    xa[u] = xfrag(c, u);
+                                f32x4 ga4 = mfma16x16x32(xa[0], ops[0], zf);
+                                f32x4 za4 = mfma16x16x32(xa[0], zop, zf);
+#pragma unroll
+                                for (int u = 1; u < 4; ++u) {
+                                    ga4 = mfma16x16x32(xa[u], ops[u], ga4);
+                                    za4 = mfma16x16x32(xa[u], zop, za4);
+                                }
+                                const float sc = record_scale<BITS>(rg, r);
+#pragma unroll
+                                for (int e = 0; e < 4; ++e)
+                                    yacc[c][e] = fmaf(sc, ga4[e] - za4[e], yacc[c][e]);
+                            }
+                        } else if constexpr (kMode == kMultiTile) {
+                            const uint8_t *rec = smeta + (gcur - g0) * RB;
+                            const u32x4 zop = zero_operand<BITS>(record_zero<BITS>(rec, r));
+#pragma unroll
+                            for (int c = 0; c < MT; ++c) {
+#pragma unroll
+                                for (int u = 0; u < 4; ++u) {
+                                    const u32x4 xa = xfrag(c, u);
+                                    gacc[c] = mfma16x16x32(xa, ops[u], gacc[c]);
+                                    zacc[c] = mfma16x16x32(xa, zop, zacc[c]);
+                                }
+                            }
+                            --tg_left;
+                            if (tg_left == 0 || t + 1 == kt_end) {
+                                const float sc = record_scale<BITS>(rec, r);
+#pragma unroll
+                                for (int c = 0; c < MT; ++c)
+                                    fold(yacc[c], gacc[c], zacc[c], sc);
+                            }
+                            if (tg_left == 0) {
+                                tg_left = tpg;
+                                ++gcur;
+                            }
+                        } else {
+#pragma unroll
+                            for (int u = 0; u < 4; ++u) {
+                                const int64_t st = 4 * (int64_t)t + u;
+                                if (st < lay.steps) {
+                                    const uint8_t *rg = smeta + ((st >> sh) - g0) * RB;
+                                    const u32x4 zop = zero_operand<BITS>(record_zero<BITS>(rg, r));
+                                    const bool last = ((st + 1) & ((1 << sh) - 1)) == 0;
+#pragma unroll
+                                    for (int c = 0; c < MT; ++c) {
+                                        const u32x4 xa = xfrag(c, u);
+                                        gacc[c] += mfma16x16x32(xa, ops[u], zf);
+                                        zacc[c] += mfma16x16x32(xa, zop, zf);
+                                    }
+                                    if (last) {
+                                        const float sc = record_scale<BITS>(rg, r);
+#pragma unroll
+                                        for (int c = 0; c < MT; ++c)
+                                            fold(yacc[c], gacc[c], zacc[c], sc);
+                                    }
+                                }
+                            }
+                        }
+                    }
+                    if (first && j == 0 && more)
+                        stage_load(cc + 1);
+                    // refill the slot with the tile D ahead, across chunk
+                    // boundaries (past the range: its last tile again, never
+                    // used); issued on every path
+                    load_codes<BITS>(ring[j], tiles + (uint32_t)(t + D < kt_end ? t + D : kt_end - 1) * TB);
+                }
+        };
+        group(c0, true);
+        for (int i = c0 + D; i < c1; i += D)
+            group(i, false);
+        if (more)
+            stage_store(cc + 1); // the buffer was last read in chunk cc - 1
+        __syncthreads();
+    }
+
+    // ---- outputs straight from the accumulators (C layout: lane holds rows
+    //      16 c + 4 o + e of column r); with K split, fp32 partials
+    if (blk_ok) {
+        const int64_t nn = blk * kBlockCols + r;
+        if (nn < lay.N) {
+#pragma unroll
+            for (int c = 0; c < MT; ++c)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int row = 16 * c + 4 * o + e;
+                    if (row < M) {
+                        if (gridDim.y > 1)
+                            ws[((int64_t)split * M + row) * lay.N + nn] = yacc[c][e];
+                        else
+                            y[(int64_t)row * lay.N + nn] = f32_to_bf16_bits(yacc[c][e]);
+                    }
+                }
+        }
+    }
+}
+
 // Blocks per workgroup: one at M = 1 (x is small); with several activation
 // rows, x is M times larger and every workgroup stages all of it, so wide
 // layers give each workgroup up to four blocks (still at least 256
@@ -440,14 +731,141 @@ static void launch_gemv_bits(const Layout &lay, dim3 grid, dim3 block, const Gem
         launch_gemv_depth<BITS, 4>(lay, grid, block, ch, stream, x, pk, y, M);
 }
 
-hipError_t launch_gemv(int bits, const uint16_t *x, const void *packed, uint16_t *y, int64_t M, const Layout &lay,
-                       hipStream_t stream)
+// ---- launch of the 17..64-row GEMV ----
+
+static int mid_mt(int64_t M) { return M <= 32 ? 2 : 4; }
+
+// K ranges over workgroups (M > 16 only).  One workgroup runs per compute
+// unit (its LDS and registers), so a launch takes ceil(groups * s / cus)
+// rounds of ceil(ktiles / s) k-tiles each plus a fixed cost per round
+// (staging the first chunk, the outputs: about kMidRoundTiles k-tiles); a
+// split adds the summing launch, about as long as kMidSumTiles k-tiles.  The
+// split count minimises that, from 1 to kGemvMaxSplits ranges of at least
+// kGemvMinSplitTiles k-tiles.  (Measured on MI355X.)
+constexpr int64_t kMidRoundTiles = 4;
+constexpr int64_t kMidSumTiles = 8;
+int64_t gemv_splits(const Layout &lay, int64_t M, int cus, int64_t *split_tiles)
 {
+    int64_t best = 1;
+    if (M > 16) {
+        const int64_t groups = (lay.nblocks + kMidWaves - 1) / kMidWaves;
+        auto cost = [&](int64_t s) {
+            const int64_t st = (lay.ktiles + s - 1) / s;
+            return (groups * s + cus - 1) / cus * (st + kMidRoundTiles) + (s > 1 ? kMidSumTiles : 0);
+        };
+        for (int64_t s = 2; s <= kGemvMaxSplits && (lay.ktiles + s - 1) / s >= kGemvMinSplitTiles; ++s)
+            if (cost(s) < cost(best))
+                best = s;
+    }
+    const int64_t st = (lay.ktiles + best - 1) / best;
+    const int64_t s = (lay.ktiles + st - 1) / st;
+    if (split_tiles)
+        *split_tiles = st;
+    return s;
+}
+
+int64_t gemv_workspace_bytes(const Layout &lay, int64_t M, int cus)
+{
+    const int64_t s = gemv_splits(lay, M, cus, nullptr);
+    return s > 1 ? s * M * lay.N * (int64_t)sizeof(float) : 0;
+}
+
+// Chunk: as many k-tiles as the threads' staging registers hold for M rows
+// (16 M units of 16 bytes per k-tile), rounded down to a multiple of the
+// ring depth (8 when that leaves at least 8, else 4), and whose records fit
+// the record registers; two such chunks of activations take at most
+// 2 * 64 * 4 * 128 * 2 bytes = 130 KiB of LDS.
+static int64_t mid_xunits(int64_t M) { return (int64_t)mid_xregs(mid_mt(M)) * 64 * kMidWaves; }
+static int mid_depth(int64_t M) { return mid_xunits(M) / (16 * M) >= 8 ? 8 : 4; }
+
+static MidChunks plan_mid(int bits, const Layout &lay, int64_t M, int64_t split_tiles)
+{
+    const int RB = record_bytes(bits);
+    const int D = mid_depth(M);
+    const int64_t gpt = lay.whole_tiles() ? 1 : lay.groups_per_tile;
+    int64_t t = mid_xunits(M) / (16 * M);
+    t = t / D * D;
+    while (t > D && kMidWaves * ((t * gpt + 1) * RB / 8) > kMidRecRegs * 64 * kMidWaves)
+        t -= D;
+    const int64_t span = (split_tiles + D - 1) / D * D;
+    if (t > span)
+        t = span;
+    MidChunks c;
+    c.tiles = (int)t;
+    c.xpitch = (int)(t * kTileRows + 8);
+    c.meta_cap = (int)(((t * gpt + 1) * RB + 15) / 16 * 16);
+    c.lds = (int)(2 * (int64_t)kMidWaves * c.meta_cap + 2 * M * c.xpitch * 2);
+    c.split_tiles = (int)split_tiles;
+    return c;
+}
+
+template <int BITS, int kMode, int MT, int D>
+static void launch_mid_mode(dim3 grid, const MidChunks &ch, hipStream_t stream, const uint16_t *x,
+                            const uint8_t *pk, uint16_t *y, const Layout &lay, int M, float *ws)
+{
+    auto kern = &gemv_mid_kernel<BITS, kMode, MT, D>;
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, kGemvMaxLds);
+    (void)attr;
+    kern<<<grid, 64 * kMidWaves, ch.lds, stream>>>(x, pk, y, lay, M, ch, ws);
+}
+
+template <int BITS, int MT, int D>
+static void launch_mid_mt(dim3 grid, const MidChunks &ch, hipStream_t stream, const uint16_t *x, const uint8_t *pk,
+                          uint16_t *y, const Layout &lay, int M, float *ws)
+{
+    if (lay.tiles_per_group == 1)
+        launch_mid_mode<BITS, kOneTile, MT, D>(grid, ch, stream, x, pk, y, lay, M, ws);
+    else if (lay.whole_tiles())
+        launch_mid_mode<BITS, kMultiTile, MT, D>(grid, ch, stream, x, pk, y, lay, M, ws);
+    else
+        launch_mid_mode<BITS, kSplitTiles, MT, D>(grid, ch, stream, x, pk, y, lay, M, ws);
+}
+
+template <int BITS>
+static void launch_mid_bits(dim3 grid, const MidChunks &ch, hipStream_t stream, const uint16_t *x, const uint8_t *pk,
+                            uint16_t *y, const Layout &lay, int M, float *ws)
+{
+    // M <= 32: two row chunks, depth 8; above: four row chunks, depth 4
+    if (mid_mt(M) == 2)
+        launch_mid_mt<BITS, 2, 8>(grid, ch, stream, x, pk, y, lay, M, ws);
+    else
+        launch_mid_mt<BITS, 4, 4>(grid, ch, stream, x, pk, y, lay, M, ws);
+}
+
+static hipError_t launch_gemv_mid(int bits, const uint16_t *x, const uint8_t *pk, uint16_t *y, int64_t M,
+                                  const Layout &lay, void *workspace, hipStream_t stream)
+{
+    int64_t split_tiles = 0;
+    const int64_t splits = gemv_splits(lay, M, planning_cus(), &split_tiles);
+    const MidChunks ch = plan_mid(bits, lay, M, split_tiles);
+    // the kernel stages a chunk's activations with mid_xregs loads per
+    // thread, walks chunks of ch.tiles > 0 k-tiles, and needs its LDS
+    const int D = mid_depth(M);
+    if (ch.tiles < 1 || (ch.tiles % D != 0 && ch.tiles < split_tiles) ||
+        M * ch.tiles * (kTileRows / 8) > mid_xunits(M) || ch.lds > kGemvMaxLds)
+        return hipErrorInvalidValue;
+    const dim3 grid((unsigned)((lay.nblocks + kMidWaves - 1) / kMidWaves), (unsigned)splits);
+    float *ws = splits > 1 ? static_cast<float *>(workspace) : nullptr;
+    if (bits == 4)
+        launch_mid_bits<4>(grid, ch, stream, x, pk, y, lay, (int)M, ws);
+    else
+        launch_mid_bits<8>(grid, ch, stream, x, pk, y, lay, (int)M, ws);
+    if (splits > 1)
+        launch_splitk_sum(ws, (int)splits, M * lay.N, y, stream);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemv(int bits, const uint16_t *x, const void *packed, uint16_t *y, int64_t M, const Layout &lay,
+                       void *workspace, hipStream_t stream)
+{
+    const uint8_t *pk = static_cast<const uint8_t *>(packed);
+    if (M > 16)
+        return launch_gemv_mid(bits, x, pk, y, M, lay, workspace, stream);
     const int W = gemv_waves(lay, M);
     const int bpw = gemv_bpw(lay, M);
     const GemvChunks ch = plan_chunks(bits, lay, M, W, bpw);
     const dim3 grid((unsigned)((lay.nblocks + bpw - 1) / bpw)), block(64 * W);
-    const uint8_t *pk = static_cast<const uint8_t *>(packed);
     if (bits == 4)
         launch_gemv_bits<4>(lay, grid, block, ch, stream, x, pk, y, (int)M);
     else

@@ -9,11 +9,21 @@ hipError_t launch_repack(int bits, const void *qweight, const void *qzeros, cons
                          const Layout &lay, void *packed, hipStream_t stream);
 hipError_t launch_dequant_f32(int bits, const void *packed, const Layout &lay, float *w, hipStream_t stream);
 
-// Waves per GEMV workgroup for M activation rows (one workgroup per 16-column
-// block, or per two or four blocks of a wide layer at M >= 2).
+// Waves per GEMV workgroup for M <= 16 activation rows (one workgroup per
+// 16-column block, or per two or four blocks of a wide layer at M >= 2).
 int gemv_waves(const Layout &lay, int64_t M);
+// K ranges the GEMV splits over workgroups (17 <= M <= 64 on a layer too
+// narrow to fill `cus` compute units; 1 otherwise) and k-tiles per range.
+int64_t gemv_splits(const Layout &lay, int64_t M, int cus, int64_t *split_tiles);
+// Workspace bytes of a GEMV launch: fp32 partial sums when it splits K.
+int64_t gemv_workspace_bytes(const Layout &lay, int64_t M, int cus);
+// Largest M the GEMV kernel takes (16-row chunks, up to four per wave).
+constexpr int64_t kGemvKernelMaxM = 64;
 hipError_t launch_gemv(int bits, const uint16_t *x, const void *packed, uint16_t *y, int64_t M, const Layout &lay,
-                       hipStream_t stream);
+                       void *workspace, hipStream_t stream);
+// y = bf16(sum of the splits' fp32 partials ws[s][mn]), added in split order;
+// 2 <= splits <= 16 (both plans stay within that).
+void launch_splitk_sum(const float *ws, int splits, int64_t mn, uint16_t *y, hipStream_t stream);
 // How the GEMM covers the output: m_tiles row tiles of 256 rows, then
 // wide_cols column tiles of 128 columns from column 0 in one launch and
 // narrow_cols tiles of 64 columns after them in a second one.  With splits
@@ -27,8 +37,13 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, int64_t G, int cus);
 int planning_cus();
 // Force the compute units plan_gemm assumes (0: the current device's).
 void set_planning_cus(int n);
-// Workspace bytes of a GEMM call (0 unless it splits K).
+// Workspace bytes of the tiled GEMM (0 unless it splits K).
 int64_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t G);
+// Which kernel a GEMM call of M rows runs: the GEMV kernel (M <= 64: the
+// tiled GEMM would compute 256-row tiles) or the tiled GEMM.  The route can
+// be forced for tests: 0 automatic, 1 tiled GEMM, 2 GEMV kernel where M <= 64.
+bool gemm_uses_gemv(int64_t M);
+void set_gemm_route(int route);
 hipError_t launch_gemm(int bits, const uint16_t *x, const void *packed, uint16_t *y, int64_t M, const Layout &lay,
                        void *workspace, hipStream_t stream);
 

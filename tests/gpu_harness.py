@@ -104,13 +104,27 @@ class planning_cus:
         self.q.tf_gemm_set_planning_cus(0)
 
 
+class gemm_route:
+    """Within the block, GEMM calls with M <= 64 run the given kernel
+    (1 the tiled GEMM, 2 the GEMV kernel; see tf_gemm_set_route)."""
+
+    def __init__(self, q, route):
+        self.q, self.route = q, route
+
+    def __enter__(self):
+        self.q.tf_gemm_set_route(self.route)
+
+    def __exit__(self, *exc):
+        self.q.tf_gemm_set_route(0)
+
+
 def split_cus(q, bits, M, K, N, G):
     """A compute-unit count for which the GEMM plan has both 128- and
     64-column tiles and does not split K, or None if no count gives one."""
     mt = -(-M // 256)
     tiles = mt * -(-N // 128)
     for cus in range(2, tiles + 1):
-        _, wide, narrow, splits, _ = q.tf_gemm_plan(bits, M, K, N, G, cus)
+        _, wide, narrow, splits, _, _ = q.tf_gemm_plan(bits, M, K, N, G, cus)
         if wide and narrow and splits == 1:
             return cus
     return None

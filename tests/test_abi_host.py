@@ -88,45 +88,124 @@ def test_packed_bytes_invalid_shapes_are_zero(lib, K, N, G):
     assert lib.tf_packed_bytes_w4(K, N, G) == 0
 
 
+@pytest.fixture
+def tiled_route(lib):
+    """GEMM calls and plans with M <= 64 use the tiled GEMM within the test."""
+    lib.tf_gemm_set_route(1)
+    yield
+    lib.tf_gemm_set_route(0)
+
+
+@pytest.mark.parametrize("route", [0, 1])
 @pytest.mark.parametrize("M,K,N,G", [(1, 4096, 4096, 128), (8, 14336, 4096, 128), (16, 4096, 1024, 128),
-                                     (1, 8192, 8192, 8192), (512, 8192, 8192, 8192), (2048, 4096, 14336, 128)])
-def test_workspace_cannot_hold_bf16_weights(lib, M, K, N, G):
+                                     (1, 8192, 8192, 8192), (512, 8192, 8192, 8192), (2048, 4096, 14336, 128),
+                                     (64, 4096, 4096, 128), (33, 14336, 4096, 128), (64, 256, 1024, 128)])
+def test_workspace_cannot_hold_bf16_weights(lib, route, M, K, N, G):
     # The layer never materialises full-precision weights: its only scratch is
-    # fp32 partial outputs of a K split (at most 8 x M x N), smaller than a
-    # bf16 copy of W for every shape here.
-    for bits in (4, 8):
-        for gemm in (0, 1):
-            if not gemm and M > 16:
-                continue
-            ws = lib.tf_workspace_bytes(bits, gemm, M, K, N, G)
-            assert ws <= 8 * M * N * 4
-            assert ws < K * N * 2
+    # fp32 partial outputs of a K split (at most 16 x M x N, and at most one
+    # range per two k-tiles), smaller than a bf16 copy of W for every shape.
+    lib.tf_gemm_set_route(route)
+    try:
+        for bits in (4, 8):
+            for gemm in (0, 1):
+                if not gemm and M > 16:
+                    continue
+                ws = lib.tf_workspace_bytes(bits, gemm, M, K, N, G)
+                assert ws <= 16 * M * N * 4
+                assert ws < K * N * 2
+    finally:
+        lib.tf_gemm_set_route(0)
 
 
 def _plan(lib, M, N, cus, K=4096, G=128, bits=4):
-    out = (ctypes.c_int64 * 5)()
+    out = (ctypes.c_int64 * 6)()
     st = lib.tf_gemm_plan(bits, M, K, N, G, cus, out)
     return st, tuple(out)
 
 
-def test_workspace_only_for_split_k_gemm(lib):
-    """The GEMV never needs scratch memory; the GEMM needs S x M x N fp32
-    partial sums exactly when its plan splits K (this host has no GPU, so the
-    plan assumes the library's default of 256 compute units)."""
-    assert lib.tf_workspace_bytes(4, 0, 1, 4096, 4096, 128) == 0
-    assert lib.tf_workspace_bytes(8, 0, 16, 8192, 8192, 8192) == 0
-    assert lib.tf_workspace_bytes(5, 1, 1, 4096, 4096, 128) == 0
-    for bits, M, K, N, G in [(8, 512, 8192, 8192, 8192), (4, 1, 4096, 4096, 128), (4, 2048, 4096, 14336, 128),
-                             (4, 100, 1024, 200, 64), (4, 64, 384, 64, 128)]:
-        st, (_, _, _, splits, _) = _plan(lib, M, N, 256, K=K, G=G, bits=bits)
-        assert st == TF_OK
-        want = splits * M * N * 4 if splits > 1 else 0
-        assert lib.tf_workspace_bytes(bits, 1, M, K, N, G) == want
-    assert _plan(lib, 512, 8192, 256, K=8192, G=8192, bits=8)[1][3] == 2   # W8 M=512: two K ranges
-    assert _plan(lib, 2048, 14336, 256)[1][3] == 1                         # prefill: no split
+@pytest.mark.parametrize("route", [0, 1])
+def test_workspace_only_for_split_k(lib, route):
+    """tf_gemv_* never needs scratch memory; a GEMM call needs S x M x N fp32
+    partial sums exactly when its plan splits K, whichever kernel it runs
+    (this host has no GPU, so plans assume the library's default of 256
+    compute units)."""
+    lib.tf_gemm_set_route(route)
+    try:
+        assert lib.tf_workspace_bytes(4, 0, 1, 4096, 4096, 128) == 0
+        assert lib.tf_workspace_bytes(8, 0, 16, 8192, 8192, 8192) == 0
+        assert lib.tf_workspace_bytes(4, 0, 17, 4096, 4096, 128) == 0  # beyond the GEMV's M
+        assert lib.tf_workspace_bytes(5, 1, 1, 4096, 4096, 128) == 0
+        for bits, M, K, N, G in [(8, 512, 8192, 8192, 8192), (4, 1, 4096, 4096, 128), (4, 2048, 4096, 14336, 128),
+                                 (4, 100, 1024, 200, 64), (4, 64, 384, 64, 128), (4, 48, 4096, 4096, 128),
+                                 (8, 20, 8192, 1024, 8192), (4, 64, 4096, 28672, 128)]:
+            st, (_, _, _, splits, _, _) = _plan(lib, M, N, 256, K=K, G=G, bits=bits)
+            assert st == TF_OK
+            want = splits * M * N * 4 if splits > 1 else 0
+            assert lib.tf_workspace_bytes(bits, 1, M, K, N, G) == want
+        assert _plan(lib, 512, 8192, 256, K=8192, G=8192, bits=8)[1][3] == 2   # W8 M=512: two K ranges
+        assert _plan(lib, 2048, 14336, 256)[1][3] == 1                         # prefill: no split
+    finally:
+        lib.tf_gemm_set_route(0)
 
 
-def test_gemm_plan_covers_every_column_once(lib):
+def test_gemm_route_by_m(lib):
+    """GEMM calls with M <= 64 run the GEMV kernel unless the tiled GEMM is
+    forced; larger M always run the tiled GEMM."""
+    for M in (1, 16, 17, 40, 64):
+        assert _plan(lib, M, 4096, 256)[1][5] == 1
+    for M in (65, 256, 2048):
+        assert _plan(lib, M, 4096, 256)[1][5] == 0
+    lib.tf_gemm_set_route(1)
+    try:
+        assert _plan(lib, 1, 4096, 256)[1][5] == 0
+        assert _plan(lib, 64, 4096, 256)[1][5] == 0
+    finally:
+        lib.tf_gemm_set_route(0)
+    lib.tf_gemm_set_route(2)
+    try:
+        assert _plan(lib, 64, 4096, 256)[1][5] == 1
+        assert _plan(lib, 65, 4096, 256)[1][5] == 0
+    finally:
+        lib.tf_gemm_set_route(0)
+
+
+def test_gemv_route_plan_covers_k_once(lib):
+    """The GEMV kernel's plan for a GEMM call: no K split at M <= 16;
+    otherwise at most 16 ranges of at least two k-tiles that cover the
+    k-tiles exactly once, their count minimising the launch's rounds of
+    128-column workgroups over the compute units times (the k-tiles per range
+    + 4 for the round's fixed cost), plus eight k-tiles' worth for the
+    summing launch when K is split."""
+    rng = __import__("random").Random(11)
+    cases = [(1, 4096, 256, 4096, 128), (16, 4096, 256, 14336, 128), (17, 4096, 256, 4096, 128),
+             (64, 28672, 256, 4096, 128), (64, 4096, 256, 14336, 128), (40, 64, 256, 256, 128),
+             (64, 8, 256, 128, 128), (33, 1000, 304, 8192, 8192)]
+    for _ in range(300):
+        G = rng.choice([32, 64, 128, 256, 512])
+        K = G * rng.randint(1, 40) if G >= 128 else 128 * rng.randint(1, 40)
+        cases.append((rng.randint(1, 64), 8 * rng.randint(1, 5000), rng.choice([1, 2, 3, 7, 64, 80, 256, 304]),
+                      K, rng.choice([G, K])))
+    for M, N, cus, K, G in cases:
+        st, (mt, wide, narrow, splits, st_tiles, route) = _plan(lib, M, N, cus, K=K, G=G)
+        assert st == TF_OK and route == 1 and mt == wide == narrow == 0, (M, N, cus, K, G)
+        ktiles = -(-K // 128)
+        groups = -(-N // 128)
+        assert (splits - 1) * st_tiles < ktiles <= splits * st_tiles
+        if M <= 16:
+            assert splits == 1
+            continue
+        if splits > 1:
+            assert splits <= 16 and st_tiles >= 2
+
+        def cost(s):
+            st = -(-ktiles // s)
+            return -(-(groups * s) // cus) * (st + 4) + (8 if s > 1 else 0)
+
+        valid = [s for s in range(1, 17) if s == 1 or -(-ktiles // s) >= 2]
+        assert cost(splits) == min(cost(s) for s in valid), (M, N, cus, K, G, splits)
+
+
+def test_gemm_plan_covers_every_column_once(lib, tiled_route):
     """The launch plan: 128-column tiles from column 0, then 64-column tiles,
     covering [0, N) with no tile wholly past N; the narrow launch exists only
     when the wide tiles miss a whole number of rounds and fits one round.
@@ -142,8 +221,8 @@ def test_gemm_plan_covers_every_column_once(lib):
         cases.append((rng.randint(1, 9000), 8 * rng.randint(1, 5000), rng.choice([1, 2, 3, 7, 64, 80, 256, 304]),
                       K, rng.choice([G, K])))
     for M, N, cus, K, G in cases:
-        st, (mt, wide, narrow, splits, st_tiles) = _plan(lib, M, N, cus, K=K, G=G)
-        assert st == TF_OK, (M, N, cus, K, G)
+        st, (mt, wide, narrow, splits, st_tiles, route) = _plan(lib, M, N, cus, K=K, G=G)
+        assert st == TF_OK and route == 0, (M, N, cus, K, G)
         n_wide = -(-N // 128)
         tiles = mt * n_wide
         ktiles = -(-K // 128)
@@ -164,8 +243,8 @@ def test_gemm_plan_covers_every_column_once(lib):
             assert mt * narrow <= cus
             assert mt * wide <= (tiles // cus) * cus
     # the headline prefill shape: 3 whole rounds of wide tiles, one of narrow
-    assert _plan(lib, 2048, 14336, 256)[1] == (8, 96, 32, 1, 32)
-    assert _plan(lib, 2048, 4096, 256, K=14336)[1] == (8, 32, 0, 1, 112)
+    assert _plan(lib, 2048, 14336, 256)[1] == (8, 96, 32, 1, 32, 0)
+    assert _plan(lib, 2048, 4096, 256, K=14336)[1] == (8, 32, 0, 1, 112, 0)
 
 
 def test_gemm_plan_rejects_bad_input(lib):
@@ -173,7 +252,7 @@ def test_gemm_plan_rejects_bad_input(lib):
     assert _plan(lib, 64, 0, 256)[0] == TF_ERR_SHAPE
     assert _plan(lib, 64, 64, 0)[0] == TF_ERR_SHAPE
     assert _plan(lib, 64, 64, 256, K=4096, G=96)[0] == TF_ERR_GROUP
-    out = (ctypes.c_int64 * 5)()
+    out = (ctypes.c_int64 * 6)()
     assert lib.tf_gemm_plan(4, 64, 4096, 64, 128, 256, None) == TF_ERR_NULL
     assert lib.tf_gemm_plan(5, 64, 4096, 64, 128, 256, out) == 6  # TF_ERR_UNSUPPORTED
 

@@ -6,8 +6,8 @@ import pytest
 
 import oracle
 import synth
-from gpu_harness import (bf16_bits, bf16_to_f64, check_linear, gpu_or_skip, linear_fn, planning_cus, repack,
-                         split_cus, splitk_cus, to_device)
+from gpu_harness import (bf16_bits, bf16_to_f64, check_linear, gemm_route, gpu_or_skip, linear_fn, planning_cus,
+                         repack, split_cus, splitk_cus, to_device)
 
 pytestmark = pytest.mark.gpu
 
@@ -32,6 +32,15 @@ GEMM_SHAPES = [
     (4, 96, 4096, 256, 512), (8, 64, 3072, 128, 3072), (4, 40, 2080, 128, 32), (4, 16, 2048, 136, 64),
 ]
 
+# GEMM calls with 17 <= M <= 64 run the GEMV kernel with two or four 16-row
+# chunks per wave: every group mode, ragged N (a partial last workgroup of
+# eight blocks), K over several staged chunks, a ragged last row chunk.
+MID_SHAPES = [
+    (4, 17, 512, 200, 128), (4, 32, 4096, 1024, 128), (4, 33, 1024, 136, 64), (4, 64, 2048, 4096, 128),
+    (4, 48, 4096, 72, 32), (4, 64, 768, 256, 256), (4, 20, 384, 64, 384), (4, 64, 14336, 512, 128),
+    (8, 24, 1024, 100, 1024), (8, 64, 2048, 260, 64), (8, 40, 4096, 520, 128), (8, 63, 512, 64, 32),
+]
+
 
 def _case(bits, M, K, N, G, seed):
     return synth.make_inputs(bits, M, K, N, G, seed=(51, seed, bits, M, K, N, G))
@@ -47,26 +56,47 @@ def test_gemv_within_tolerance(shape):
 
 
 def _plan_cus(q, plan, shape):
-    """Compute units to plan for: the device's (auto), one (128-column tiles
-    only), a count that splits the columns between both tile widths, or one
-    that splits K."""
-    if plan == "auto":
+    """Compute units to plan the tiled GEMM for: the device's (auto, tiled),
+    one (128-column tiles only), a count that splits the columns between both
+    tile widths, or one that splits K."""
+    if plan in ("auto", "tiled"):
         return 0
     if plan == "wide":
         return 1
-    cus = split_cus(q, *shape) if plan == "split" else splitk_cus(q, *shape)
+    with gemm_route(q, 1):
+        cus = split_cus(q, *shape) if plan == "split" else splitk_cus(q, *shape)
     if cus is None:
         pytest.skip(f"no compute-unit count gives a '{plan}' plan for this grid")
     return cus
 
 
-@pytest.mark.parametrize("plan", ["auto", "wide", "split", "splitk"])
+@pytest.mark.parametrize("plan", ["auto", "tiled", "wide", "split", "splitk"])
 @pytest.mark.parametrize("shape", GEMM_SHAPES)
 def test_gemm_within_tolerance(shape, plan):
+    """auto: the kernel the call picks (the GEMV kernel for M <= 64); the
+    other plans force the tiled GEMM."""
     torch, q = gpu_or_skip()
+    if plan == "tiled" and shape[1] > 64:
+        pytest.skip("above 64 rows the automatic route is the tiled GEMM")
     cus = _plan_cus(q, plan, shape)
-    print(f"gemm {shape} plan={plan} cus={cus} {q.tf_gemm_plan(*shape, cus or 256)}", flush=True)
-    c = _case(*shape, seed=2)
+    route = 0 if plan == "auto" else 1
+    with gemm_route(q, route):
+        print(f"gemm {shape} plan={plan} cus={cus} {q.tf_gemm_plan(*shape, cus or 256)}", flush=True)
+        c = _case(*shape, seed=2)
+        with planning_cus(q, cus):
+            ok, ratio, _ = check_linear(c, torch, q, gemm=True)
+    assert ok, f"worst error / bound = {ratio:.3f}"
+
+
+@pytest.mark.parametrize("cus", [0, 1, 4096])
+@pytest.mark.parametrize("shape", MID_SHAPES)
+def test_gemm_mid_m_gemv_kernel(shape, cus):
+    """GEMM calls of 17..64 rows through the GEMV kernel, planned for the
+    device (0), for one compute unit (K never split) and for 4096 (K split
+    into as many ranges as the plan allows, fp32 partials summed in order)."""
+    torch, q = gpu_or_skip()
+    print(f"mid {shape} cus={cus} {q.tf_gemm_plan(*shape, cus or 256)}", flush=True)
+    c = _case(*shape, seed=6)
     with planning_cus(q, cus):
         ok, ratio, _ = check_linear(c, torch, q, gemm=True)
     assert ok, f"worst error / bound = {ratio:.3f}"
@@ -83,12 +113,14 @@ def test_gemm_plans_agree_bitwise(bits, M, K, N, G):
     pk = repack(c, d, q)
     f = linear_fn(q, bits, True)
     outs = {}
-    for cus in (1, split_cus(q, bits, M, K, N, G)):
-        if cus is None:
-            continue
-        print(f"plans W{bits} M={M} K={K} N={N} G={G} cus={cus} {q.tf_gemm_plan(bits, M, K, N, G, cus)}", flush=True)
-        with planning_cus(q, cus):
-            outs[cus] = bf16_bits(f(d["x"], pk, K, N, G))
+    with gemm_route(q, 1):
+        for cus in (1, split_cus(q, bits, M, K, N, G)):
+            if cus is None:
+                continue
+            print(f"plans W{bits} M={M} K={K} N={N} G={G} cus={cus} {q.tf_gemm_plan(bits, M, K, N, G, cus)}",
+                  flush=True)
+            with planning_cus(q, cus):
+                outs[cus] = bf16_bits(f(d["x"], pk, K, N, G))
     ref = outs[1]
     for cus, y in outs.items():
         assert np.array_equal(y, ref), f"plan for {cus} CUs differs from the single wide launch"
@@ -107,15 +139,21 @@ def _integer_case(bits, M, K, N, G, seed):
     return c, exact
 
 
-@pytest.mark.parametrize("gemm", [False, True])
+# gemm: False tf_gemv_*, "auto" tf_gemm_* as routed, "tiled" tf_gemm_* forced
+# onto the tiled GEMM; cus 4096 makes the GEMV kernel split K at M > 16.
+@pytest.mark.parametrize("gemm", [False, "auto", "tiled"])
 @pytest.mark.parametrize("bits,M,K,N,G", [(4, 1, 1024, 128, 128), (4, 7, 2048, 200, 64), (8, 4, 1024, 72, 1024),
-                                          (4, 16, 14336, 64, 128), (8, 3, 512, 64, 32)])
+                                          (4, 16, 14336, 64, 128), (8, 3, 512, 64, 32), (4, 40, 2048, 200, 64),
+                                          (8, 64, 1024, 72, 1024), (4, 33, 4096, 128, 128)])
 def test_integer_case_is_bit_exact(gemm, bits, M, K, N, G):
     torch, q = gpu_or_skip()
+    if not gemm and M > 16:
+        pytest.skip("tf_gemv takes M <= 16")
     print(f"integer gemm={gemm} W{bits} M={M} K={K} N={N} G={G}", flush=True)
     c, exact = _integer_case(bits, M, K, N, G, seed=K + N)
     d = to_device(c, torch)
-    y = linear_fn(q, bits, gemm)(d["x"], repack(c, d, q), K, N, G)
+    with gemm_route(q, 1 if gemm == "tiled" else 0), planning_cus(q, 4096 if M > 16 else 0):
+        y = linear_fn(q, bits, bool(gemm))(d["x"], repack(c, d, q), K, N, G)
     torch.cuda.synchronize()
     # every partial sum is an integer below 2^24, so fp32 holds it exactly and
     # the only rounding is the final one to bf16
@@ -123,15 +161,16 @@ def test_integer_case_is_bit_exact(gemm, bits, M, K, N, G):
     assert np.array_equal(bf16_bits(y), oracle.f64_to_bf16(exact.astype(np.float64)))
 
 
-@pytest.mark.parametrize("gemm", [False, True])
+@pytest.mark.parametrize("gemm,M", [(False, 5), ("auto", 5), ("tiled", 5), ("auto", 40), ("tiled", 40)])
 @pytest.mark.parametrize("bits", [4, 8])
-def test_q_equal_zero_point_gives_zero(gemm, bits):
+def test_q_equal_zero_point_gives_zero(gemm, M, bits):
     torch, q = gpu_or_skip()
-    c0 = _case(bits, 5, 1024, 136, 128, seed=3)
+    c0 = _case(bits, M, 1024, 136, 128, seed=3)
     codes = c0.zeros[np.arange(c0.K) // c0.G]
     c = synth.gen.pack_case(bits, codes, c0.zeros, c0.scales, c0.x, c0.G)
     d = to_device(c, torch)
-    y = linear_fn(q, bits, gemm)(d["x"], repack(c, d, q), c.K, c.N, c.G)
+    with gemm_route(q, 1 if gemm == "tiled" else 0), planning_cus(q, 4096 if M > 16 else 0):
+        y = linear_fn(q, bits, bool(gemm))(d["x"], repack(c, d, q), c.K, c.N, c.G)
     torch.cuda.synchronize()
     assert np.all(bf16_to_f64(y) == 0.0)
 

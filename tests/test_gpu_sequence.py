@@ -16,7 +16,7 @@ def test_mixed_shapes_back_to_back():
     torch, q = gpu_or_skip()
     plan = [(4, False, 1, 4096, 1024, 128), (4, False, 8, 4096, 14336, 128), (8, False, 3, 8192, 512, 8192),
             (4, True, 130, 1024, 320, 64), (4, False, 16, 14336, 4096, 128), (8, True, 64, 512, 100, 512),
-            (4, False, 1, 4096, 1024, 128)]
+            (4, True, 40, 4096, 4096, 128), (8, True, 20, 2048, 8192, 2048), (4, False, 1, 4096, 1024, 128)]
     runs = []
     for it, (bits, gemm, M, K, N, G) in enumerate(plan):
         c = synth.make_inputs(bits, M, K, N, G, seed=(61, it))
