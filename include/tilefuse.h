@@ -112,16 +112,21 @@ int tf_repack_w8(const uint8_t *qweight, const uint8_t *zeros, const uint16_t *s
 /*   y          bf16 [M][N] output (fp32 accumulation, one rounding to bf16, */
 /*              nearest-even), 2-byte aligned                                */
 /*   workspace  device scratch of ws_bytes >= tf_workspace_bytes(...), 256-  */
-/*              byte aligned.  NULL is fine when the size query returns 0:   */
-/*              always for tf_gemv_* (M <= 16); for tf_gemm_* unless it      */
-/*              splits K over workgroups (small M, or 17 <= M <= 64 on a     */
-/*              layer too narrow to fill the device).  The size depends on   */
-/*              the device the query runs on (its compute-unit count): query */
-/*              on the device the call will run on.                          */
+/*              byte aligned.  NULL is fine when the size query returns 0, */
+/*              i.e. unless the call splits K over workgroups: the GEMM at   */
+/*              small M, or either call at 8 <= M <= 64 on a layer too      */
+/*              narrow to fill the device (the 16-row-chunk kernel).  Below  */
+/*              8 rows tf_gemv_* never needs one.  The size depends on the   */
+/*              device the query runs on (its compute-unit count): query on  */
+/*              the device the call will run on.                             */
 /* ------------------------------------------------------------------------ */
 size_t tf_workspace_bytes(int bits, int is_gemm, int64_t M, int64_t K, int64_t N, int64_t G);
 
-/* Token-generation GEMV, 1 <= M <= 16 (Methodology section 3). */
+/* Token-generation GEMV, 1 <= M <= 16 (Methodology section 3).  From 2
+ * rows, wide layers (and from 8 rows, layers whose K ranges stay long
+ * enough) run the kernel that serves 16-row chunks of x with one unpack
+ * (the one GEMM calls of up to 64 rows run), which may split K over
+ * workgroups and then needs the workspace. */
 int tf_gemv_w4a16(const uint16_t *x, const void *packed, size_t packed_bytes, uint16_t *y,
                   int64_t M, int64_t K, int64_t N, int64_t G,
                   void *workspace, size_t ws_bytes, void *stream);
@@ -133,9 +138,10 @@ int tf_gemv_w8a16(const uint16_t *x, const void *packed, size_t packed_bytes, ui
  * unpacked once into LDS as the exact bf16 values q - z and reused by every
  * row of a 256-row tile; each group's scale is applied once per (group,
  * column) to its fp32 partial sum.  For M <= 64 a 256-row tile would mostly
- * compute padding, so the call runs the GEMV kernel instead, with up to four
- * 16-row chunks of x per wave (and K split over workgroups on narrow layers);
- * the result meets the same tolerance, not the tiled kernel's bits. */
+ * compute padding, so the call runs the GEMV kernels instead (as tf_gemv_*
+ * does up to 16 rows; above, up to four 16-row chunks of x per wave, K split
+ * over workgroups on narrow layers); the result meets the same tolerance,
+ * not the tiled kernel's bits. */
 int tf_gemm_w4a16(const uint16_t *x, const void *packed, size_t packed_bytes, uint16_t *y,
                   int64_t M, int64_t K, int64_t N, int64_t G,
                   void *workspace, size_t ws_bytes, void *stream);

@@ -53,9 +53,10 @@ int repack(int bits, const void *qweight, const void *qzeros, const uint16_t *sc
 }
 
 // fp32 partial sums, S x M x N floats, when a call splits K over workgroups:
-// the tiled GEMM with few output tiles (small M), the GEMV kernel above 16
-// rows on a layer too narrow to fill the chip.  Otherwise none: the GEMV at
-// M <= 16 combines its K split inside a workgroup.
+// the tiled GEMM with few output tiles (small M), the 16-row-chunk GEMV
+// kernel (8..64 rows) on a layer too narrow to fill the chip.  Otherwise
+// none: the GEMV kernel for up to 16 rows combines its K split inside a
+// workgroup.
 size_t workspace_bytes(int bits, int is_gemm, int64_t M, int64_t K, int64_t N, int64_t G)
 {
     if (M < 1 || M > (is_gemm ? (int64_t(1) << 30) : 16) || check_kng(bits, K, N, G) != TF_OK)

@@ -1,7 +1,8 @@
 // Token-generation GEMV, M = 1..16 (TileFuse summary, Methodology section 3:
 // batch-1 GEMV, memory-bound at full precision; spread the weight stream over
-// the whole machine instead of a slice of it), and the same dataflow for
-// 17..64 rows (gemv_mid_kernel below), which GEMM calls of that size run.
+// the whole machine instead of a slice of it), and the same dataflow with
+// 16-row chunks of x (gemv_mid_kernel below) for up to 64 rows, which GEMM
+// calls of up to 64 rows run as well.
 //
 // MI355X design.  One workgroup owns one 16-column block of the packed buffer
 // -- a single contiguous byte range -- and its waves split K between them, so
@@ -31,7 +32,7 @@ namespace tf {
 
 constexpr int kGemvMaxWaves = 16;
 constexpr int kGemvTargetWaves = 4096; // about 16 per CU
-// K ranges of the 17..64-row GEMV: at least 2 k-tiles, at most 16 ranges
+// K ranges of the 16-row-chunk GEMV: at least 2 k-tiles, at most 16 ranges
 constexpr int kGemvMinSplitTiles = 2;
 constexpr int kGemvMaxSplits = 16;
 
@@ -339,10 +340,10 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const uint16_t *__restrict__
     }
 }
 
-// ---- GEMV for 17..64 activation rows ----
+// ---- GEMV for 2..64 activation rows, 16-row chunks ----
 //
-// Above 16 rows every weight operand feeds MT = 2 or 4 row chunks of 16, so
-// one unpack serves up to 64 rows.  A workgroup is eight waves, one
+// Every weight operand feeds MT = 1, 2 or 4 row chunks of 16, so one unpack
+// serves up to 64 rows.  A workgroup is eight waves, one
 // 16-column block each (the activations staged in LDS serve 128 columns),
 // and K may be split over workgroups (gridDim.y ranges of split_tiles
 // k-tiles) whose fp32 partial sums a second kernel adds in range order.  Each
@@ -354,7 +355,7 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const uint16_t *__restrict__
 // flight), and one barrier per chunk separates the buffers' uses.
 constexpr int kMidWaves = 8;   // waves (blocks) per workgroup
 // activation units of 16 bytes staged per thread per chunk, by row chunks
-constexpr int mid_xregs(int mt) { return mt == 2 ? 8 : 8; }
+constexpr int mid_xregs(int) { return 8; }
 constexpr int kMidRecRegs = 4; // record words of 8 bytes per thread per chunk
 // k-tiles of codes in flight per wave: the chunk length, 8 or 4 (a chunk
 // holds 4096 / (16 M) k-tiles of activations: 8 up to 32 rows, 4 above)
@@ -731,11 +732,11 @@ static void launch_gemv_bits(const Layout &lay, dim3 grid, dim3 block, const Gem
         launch_gemv_depth<BITS, 4>(lay, grid, block, ch, stream, x, pk, y, M);
 }
 
-// ---- launch of the 17..64-row GEMV ----
+// ---- launch of the 16-row-chunk GEMV ----
 
-static int mid_mt(int64_t M) { return M <= 32 ? 2 : 4; }
+static int mid_mt(int64_t M) { return M <= 16 ? 1 : M <= 32 ? 2 : 4; }
 
-// K ranges over workgroups (M > 16 only).  One workgroup runs per compute
+// K ranges over workgroups of the 16-row-chunk kernel.  One workgroup runs per compute
 // unit (its LDS and registers), so a launch takes ceil(groups * s / cus)
 // rounds of ceil(ktiles / s) k-tiles each plus a fixed cost per round
 // (staging the first chunk, the outputs: about kMidRoundTiles k-tiles); a
@@ -744,24 +745,54 @@ static int mid_mt(int64_t M) { return M <= 32 ? 2 : 4; }
 // kGemvMinSplitTiles k-tiles.  (Measured on MI355X.)
 constexpr int64_t kMidRoundTiles = 4;
 constexpr int64_t kMidSumTiles = 8;
-int64_t gemv_splits(const Layout &lay, int64_t M, int cus, int64_t *split_tiles)
+static int64_t mid_splits(const Layout &lay, int cus, int64_t *split_tiles)
 {
+    const int64_t groups = (lay.nblocks + kMidWaves - 1) / kMidWaves;
+    auto cost = [&](int64_t s) {
+        const int64_t st = (lay.ktiles + s - 1) / s;
+        return (groups * s + cus - 1) / cus * (st + kMidRoundTiles) + (s > 1 ? kMidSumTiles : 0);
+    };
     int64_t best = 1;
-    if (M > 16) {
-        const int64_t groups = (lay.nblocks + kMidWaves - 1) / kMidWaves;
-        auto cost = [&](int64_t s) {
-            const int64_t st = (lay.ktiles + s - 1) / s;
-            return (groups * s + cus - 1) / cus * (st + kMidRoundTiles) + (s > 1 ? kMidSumTiles : 0);
-        };
-        for (int64_t s = 2; s <= kGemvMaxSplits && (lay.ktiles + s - 1) / s >= kGemvMinSplitTiles; ++s)
-            if (cost(s) < cost(best))
-                best = s;
-    }
+    for (int64_t s = 2; s <= kGemvMaxSplits && (lay.ktiles + s - 1) / s >= kGemvMinSplitTiles; ++s)
+        if (cost(s) < cost(best))
+            best = s;
     const int64_t st = (lay.ktiles + best - 1) / best;
-    const int64_t s = (lay.ktiles + st - 1) / st;
     if (split_tiles)
         *split_tiles = st;
-    return s;
+    return (lay.ktiles + st - 1) / st;
+}
+
+// Which kernel a call of M rows runs.  Above 16 rows, the 16-row-chunk
+// kernel.  Below, it is faster where it needs no K split (a layer wide
+// enough to fill the chip) from 2 rows, and where it splits K from 8 rows
+// if its ranges hold at least kMidMinRangeTiles k-tiles; elsewhere the
+// summing launch outweighs the gain and the kernel for up to 16 rows, which
+// splits K inside a workgroup, is kept.  At M = 1 that kernel is always the
+// faster.  Measured on the decoder layer: gate_up (no split) 18.6 -> 17.3 us
+// at M = 2; down (8 ranges of 14 k-tiles) 16.2 -> 14.5 us at M = 8; q/k/v (5
+// ranges of 7) 12.3 -> 9.8 us at M = 10; o (8 ranges of 4) slower at every
+// M up to 16.
+constexpr int64_t kMidSplitFromRows = 8;
+constexpr int64_t kMidMinRangeTiles = 6;
+static bool use_mid(const Layout &lay, int64_t M, int cus)
+{
+    if (M > 16)
+        return true;
+    if (M < 2)
+        return false;
+    int64_t st = 0;
+    if (mid_splits(lay, cus, &st) == 1)
+        return true;
+    return M >= kMidSplitFromRows && st >= kMidMinRangeTiles;
+}
+
+int64_t gemv_splits(const Layout &lay, int64_t M, int cus, int64_t *split_tiles)
+{
+    if (use_mid(lay, M, cus))
+        return mid_splits(lay, cus, split_tiles);
+    if (split_tiles)
+        *split_tiles = lay.ktiles;
+    return 1;
 }
 
 int64_t gemv_workspace_bytes(const Layout &lay, int64_t M, int cus)
@@ -826,8 +857,10 @@ template <int BITS>
 static void launch_mid_bits(dim3 grid, const MidChunks &ch, hipStream_t stream, const uint16_t *x, const uint8_t *pk,
                             uint16_t *y, const Layout &lay, int M, float *ws)
 {
-    // M <= 32: two row chunks, depth 8; above: four row chunks, depth 4
-    if (mid_mt(M) == 2)
+    // M <= 16: one row chunk, M <= 32: two, depth 8; above: four, depth 4
+    if (mid_mt(M) == 1)
+        launch_mid_mt<BITS, 1, 8>(grid, ch, stream, x, pk, y, lay, M, ws);
+    else if (mid_mt(M) == 2)
         launch_mid_mt<BITS, 2, 8>(grid, ch, stream, x, pk, y, lay, M, ws);
     else
         launch_mid_mt<BITS, 4, 4>(grid, ch, stream, x, pk, y, lay, M, ws);
@@ -860,7 +893,7 @@ hipError_t launch_gemv(int bits, const uint16_t *x, const void *packed, uint16_t
                        void *workspace, hipStream_t stream)
 {
     const uint8_t *pk = static_cast<const uint8_t *>(packed);
-    if (M > 16)
+    if (use_mid(lay, M, planning_cus()))
         return launch_gemv_mid(bits, x, pk, y, M, lay, workspace, stream);
     const int W = gemv_waves(lay, M);
     const int bpw = gemv_bpw(lay, M);

@@ -12,8 +12,10 @@ hipError_t launch_dequant_f32(int bits, const void *packed, const Layout &lay, f
 // Waves per GEMV workgroup for M <= 16 activation rows (one workgroup per
 // 16-column block, or per two or four blocks of a wide layer at M >= 2).
 int gemv_waves(const Layout &lay, int64_t M);
-// K ranges the GEMV splits over workgroups (17 <= M <= 64 on a layer too
-// narrow to fill `cus` compute units; 1 otherwise) and k-tiles per range.
+// K ranges the GEMV splits over workgroups (the 16-row-chunk kernel, which
+// runs above 16 rows, from 2 rows where it needs no split and from 8 where
+// its K ranges are long enough, on a layer too narrow to fill `cus` compute
+// units; 1 otherwise) and k-tiles per range.
 int64_t gemv_splits(const Layout &lay, int64_t M, int cus, int64_t *split_tiles);
 // Workspace bytes of a GEMV launch: fp32 partial sums when it splits K.
 int64_t gemv_workspace_bytes(const Layout &lay, int64_t M, int cus);

@@ -13,6 +13,7 @@ pytestmark = pytest.mark.gpu
 
 
 @pytest.mark.parametrize("gemm,bits,M,K,N,G", [(False, 4, 1, 4096, 1024, 128), (False, 8, 8, 8192, 512, 8192),
+                                               (False, 4, 16, 14336, 1024, 128),
                                                (True, 4, 96, 1024, 320, 128), (True, 4, 48, 4096, 4096, 128)])
 def test_graph_replays_match_eager(gemm, bits, M, K, N, G):
     torch, q = gpu_or_skip()

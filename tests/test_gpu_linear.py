@@ -21,6 +21,11 @@ GEMV_SHAPES = [
     (4, 4, 512, 8240, 128), (4, 3, 1024, 16400, 64), (8, 8, 1024, 8208, 1024), (4, 2, 384, 16400, 384),
     # M = 16 over K = 4096: 128 KiB of staged activations (dynamic LDS above 64 KiB)
     (4, 16, 4096, 4096, 128),
+    # 12..16 rows on the 16-row-chunk kernel: K split into long ranges (one
+    # group per tile, per channel, G = 64), a wide layer split in three with
+    # a partial last workgroup, a wide layer not split
+    (4, 16, 14336, 1024, 128), (8, 14, 14336, 264, 14336), (4, 12, 8192, 4096, 64), (4, 13, 2048, 8200, 128),
+    (4, 14, 4096, 28672, 128),
 ]
 
 GEMM_SHAPES = [
@@ -91,7 +96,7 @@ def test_gemm_within_tolerance(shape, plan):
 @pytest.mark.parametrize("cus", [0, 1, 4096])
 @pytest.mark.parametrize("shape", MID_SHAPES)
 def test_gemm_mid_m_gemv_kernel(shape, cus):
-    """GEMM calls of 17..64 rows through the GEMV kernel, planned for the
+    """GEMM calls of 17..64 rows through the 16-row-chunk GEMV kernel, planned for the
     device (0), for one compute unit (K never split) and for 4096 (K split
     into as many ranges as the plan allows, fp32 partials summed in order)."""
     torch, q = gpu_or_skip()
