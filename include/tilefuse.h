@@ -93,7 +93,10 @@ size_t tf_packed_bytes_w8(int64_t K, int64_t N, int64_t G);
  *   qweight  uint32 [K][N/8]: word (k, c) holds columns 8c..8c+7 of row k,
  *            column 8c + j in nibble p(j), p = (0, 4, 1, 5, 2, 6, 3, 7).
  *            4-byte aligned.
- *   qzeros   uint32 [K/G][N/8], same packing.  4-byte aligned.
+ *   qzeros   uint32 [K/G][N/8], same packing.  4-byte aligned.  NULL for
+ *            symmetric quantization: every zero point is 8 (Methodology
+ *            section 1 names zero points; this is their common special
+ *            case), packed exactly as an explicit tensor of 8s would be.
  *   scales   bf16 [K/G][N].  2-byte aligned.
  *   packed   output, packed_bytes >= tf_packed_bytes_w4(K, N, G); 16-byte
  *            aligned.  Every byte of the layout is written. */
@@ -101,7 +104,8 @@ int tf_repack_w4(const uint32_t *qweight, const uint32_t *qzeros, const uint16_t
                  int64_t K, int64_t N, int64_t G, void *packed, size_t packed_bytes, void *stream);
 
 /* Re-lay out a W8 checkpoint: qweight uint8 [K][N], zeros uint8 [K/G][N]
- * (unsigned codes, zero points stored as bytes), scales bf16 [K/G][N]. */
+ * (unsigned codes, zero points stored as bytes), scales bf16 [K/G][N].
+ * zeros NULL: symmetric quantization, every zero point 128. */
 int tf_repack_w8(const uint8_t *qweight, const uint8_t *zeros, const uint16_t *scales,
                  int64_t K, int64_t N, int64_t G, void *packed, size_t packed_bytes, void *stream);
 

@@ -130,7 +130,8 @@ def _repack(bits, fn, qweight, qzeros, scales, K, N, G, packed, stream):
     L = load_library()
     elem = 4 if bits == 4 else 1
     _need(qweight, "qweight", elem)
-    _need(qzeros, "qzeros", elem)
+    if qzeros is not None:  # None: symmetric quantization (zero point 2^(bits-1))
+        _need(qzeros, "qzeros", elem)
     _need(scales, "scales", 2)
     nbytes = (L.tf_packed_bytes_w4 if bits == 4 else L.tf_packed_bytes_w8)(K, N, G)
     if packed is None:
@@ -144,12 +145,14 @@ def _repack(bits, fn, qweight, qzeros, scales, K, N, G, packed, stream):
 
 
 def tf_repack_w4(qweight, qzeros, scales, K, N, G, packed=None, stream=None):
-    """AWQ W4 checkpoint (int32 [K][N/8], int32 [K/G][N/8], bf16 [K/G][N]) -> packed uint8."""
+    """AWQ W4 checkpoint (int32 [K][N/8], int32 [K/G][N/8] or None for
+    symmetric zero points of 8, bf16 [K/G][N]) -> packed uint8."""
     return _repack(4, "tf_repack_w4", qweight, qzeros, scales, K, N, G, packed, stream)
 
 
 def tf_repack_w8(qweight, zeros, scales, K, N, G, packed=None, stream=None):
-    """W8 checkpoint (uint8 [K][N], uint8 [K/G][N], bf16 [K/G][N]) -> packed uint8."""
+    """W8 checkpoint (uint8 [K][N], uint8 [K/G][N] or None for symmetric
+    zero points of 128, bf16 [K/G][N]) -> packed uint8."""
     return _repack(8, "tf_repack_w8", qweight, zeros, scales, K, N, G, packed, stream)
 
 

@@ -38,7 +38,7 @@ size_t packed_bytes(int bits, int64_t K, int64_t N, int64_t G)
 int repack(int bits, const void *qweight, const void *qzeros, const uint16_t *scales, int64_t K, int64_t N, int64_t G,
            void *packed, size_t nbytes, void *stream)
 {
-    if (!qweight || !qzeros || !scales || !packed)
+    if (!qweight || !scales || !packed) // qzeros may be NULL: symmetric quantization
         return TF_ERR_NULL;
     if (int st = check_kng(bits, K, N, G))
         return st;

@@ -94,12 +94,14 @@ __global__ __launch_bounds__(256) void repack_records(const void *__restrict__ q
         if (n >= lay.N)
             continue;
         sc[c >> 1] |= (uint32_t)scales[g * lay.N + n] << (16 * (c & 1));
+        // no zero-point tensor: symmetric quantization, z = 2^(b-1)
         if constexpr (BITS == 4) {
             const uint32_t *qz = static_cast<const uint32_t *>(qzeros);
-            const uint32_t z = (qz[g * (lay.N / 8) + (n >> 3)] >> awq_nibble_shift((int)(n & 7))) & 0xFu;
+            const uint32_t z =
+                qz ? (qz[g * (lay.N / 8) + (n >> 3)] >> awq_nibble_shift((int)(n & 7))) & 0xFu : 8u;
             zz[c >> 3] |= z << (4 * (c & 7));
         } else {
-            const uint32_t z = static_cast<const uint8_t *>(qzeros)[g * lay.N + n];
+            const uint32_t z = qzeros ? static_cast<const uint8_t *>(qzeros)[g * lay.N + n] : 128u;
             zz[c >> 2] |= z << (8 * (c & 3));
         }
     }

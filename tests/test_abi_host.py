@@ -316,7 +316,12 @@ class TestValidation:
     def test_repack_validation(self, lib):
         f = lib.tf_repack_w4
         assert f(FAKE, FAKE, FAKE, 256, 128, 128, FAKE, 10, None) == TF_ERR_BUFFER_TOO_SMALL
-        assert f(FAKE, None, FAKE, 256, 128, 128, FAKE, 1 << 30, None) == TF_ERR_NULL
+        assert f(None, FAKE, FAKE, 256, 128, 128, FAKE, 1 << 30, None) == TF_ERR_NULL
+        assert f(FAKE, FAKE, None, 256, 128, 128, FAKE, 1 << 30, None) == TF_ERR_NULL
+        assert f(FAKE, FAKE, FAKE, 256, 128, 128, None, 1 << 30, None) == TF_ERR_NULL
+        # no zero-point tensor means symmetric quantization: validated, not rejected
+        assert f(FAKE, None, FAKE, 256, 128, 128, FAKE, 10, None) == TF_ERR_BUFFER_TOO_SMALL
+        assert lib.tf_repack_w8(FAKE, None, FAKE, 256, 100, 128, FAKE, 10, None) == TF_ERR_BUFFER_TOO_SMALL
         assert f(FAKE, FAKE, FAKE + 1, 256, 128, 128, FAKE, 1 << 30, None) == TF_ERR_ALIGN
         assert f(FAKE, FAKE, FAKE, 256, 128, 96, FAKE, 1 << 30, None) == TF_ERR_GROUP
         assert lib.tf_repack_w8(FAKE, FAKE, FAKE, 256, 3, 33, FAKE, 1 << 30, None) == TF_ERR_GROUP

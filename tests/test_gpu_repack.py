@@ -58,3 +58,44 @@ def test_packed_size_and_version_agree():
     torch, q = gpu_or_skip()
     assert q.tf_format_version() == 2
     assert q.tf_packed_bytes_w4(4096, 4096, 128) == oracle.packed_bytes(4, 4096, 4096, 128)
+
+
+def _symmetric(c):
+    """The case with every zero point 2^(bits-1): what a checkpoint without a
+    zero-point tensor means."""
+    zeros = np.full_like(c.zeros, 1 << (c.bits - 1))
+    return synth.gen.pack_case(c.bits, c.codes, zeros, c.scales, c.x, c.G)
+
+
+@pytest.mark.parametrize("bits,K,N,G", [(4, 256, 200, 128), (4, 384, 64, 384), (4, 192, 8, 64), (8, 256, 100, 256),
+                                        (8, 96, 72, 32), (4, 4096, 1024, 128)])
+def test_symmetric_repack_matches_oracle_bytes(bits, K, N, G):
+    """No zero-point tensor (NULL) packs exactly as an explicit tensor of
+    2^(bits-1), as the oracle packs it."""
+    torch, q = gpu_or_skip()
+    print(f"symmetric repack W{bits} K={K} N={N} G={G}", flush=True)
+    c = _symmetric(synth.make_inputs(bits, 1, K, N, G, seed=(43, bits, K, N)))
+    d = to_device(c, torch)
+    fn = q.tf_repack_w4 if bits == 4 else q.tf_repack_w8
+    packed = fn(d["qweight"], None, d["scales"], K, N, G)
+    torch.cuda.synchronize()
+    want = oracle.repack(bits, c.qweight, c.qzeros, c.scales, K, N, G)
+    assert np.array_equal(packed.cpu().numpy(), want)
+
+
+@pytest.mark.parametrize("gemm,M", [(False, 1), (False, 12), (True, 40), (True, 300)])
+@pytest.mark.parametrize("bits", [4, 8])
+def test_symmetric_linear_within_tolerance(gemm, M, bits):
+    torch, q = gpu_or_skip()
+    from gpu_harness import bf16_to_f64, linear_fn, within_tolerance
+
+    K, N, G = 2048, 264, 128
+    print(f"symmetric linear gemm={gemm} W{bits} M={M}", flush=True)
+    c = _symmetric(synth.make_inputs(bits, M, K, N, G, seed=(44, bits, M)))
+    d = to_device(c, torch)
+    fn = q.tf_repack_w4 if bits == 4 else q.tf_repack_w8
+    packed = fn(d["qweight"], None, d["scales"], K, N, G)
+    y = linear_fn(q, bits, gemm)(d["x"], packed, K, N, G)
+    torch.cuda.synchronize()
+    ok, ratio = within_tolerance(bf16_to_f64(y), oracle.awq_linear(c))
+    assert ok, f"worst error / bound = {ratio:.3f}"
