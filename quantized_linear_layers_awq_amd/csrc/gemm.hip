@@ -54,7 +54,6 @@ typedef float f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
 
 constexpr int kGBM = 256;                        // rows per workgroup tile
 constexpr int kStage = 64;                       // k rows per pipeline stage
-constexpr int kSlice = 16;                       // k rows per 32x32x16 MFMA
 constexpr int kAStages = 3;
 // Row tiles per band of the tile order: with two, the 32 workgroups an XCD runs
 // at once cover 2 activation panels x 16 weight column tiles (measured best of

@@ -402,74 +402,74 @@ __global__ __launch_bounds__(64 * kMidWaves) void gemv_mid_kernel(const uint16_t
     const f32x4 zf = {0.f, 0.f, 0.f, 0.f};
 
     // ---- staging of chunk cc: activations x[0:M][chunk] (zero past K) and
-    //      the records of the groups the chunk touches, for all eight blocks
+    //      the records of the groups the chunk touches, for all eight blocks.
+    //      A thread's units are split into (row, unit) and (block, word) by a
+    //      multiply-high with a per-chunk constant instead of a division:
+    //      floor(n / d) = umulhi(n, floor((2^32 - 1) / d) + 1) exactly for
+    //      2 <= d and n d < 2^32 (here n < 8192, d <= 2048). ----
     constexpr int XR = mid_xregs(MT);
     u32x4 xv[XR];
     u32x2 mv[kMidRecRegs];
-    auto chunk_bounds = [&](int cc, int &c0, int &c1) {
-        c0 = kt_begin + cc * ch.tiles;
-        c1 = c0 + ch.tiles < kt_end ? c0 + ch.tiles : kt_end;
+    struct Chunk {
+        int c0, c1, upr, rw;
+        uint32_t upr_m, rw_m;
+        uint32_t g0;
     };
-    auto chunk_groups = [&](int c0, int c1, int64_t &g0, int &rec_words) {
-        const int64_t k0 = (int64_t)c0 * kTileRows;
-        const int64_t k1 = (int64_t)c1 * kTileRows < lay.K ? (int64_t)c1 * kTileRows : lay.K;
-        g0 = k0 / lay.G;
-        rec_words = (int)(((k1 - 1) / lay.G - g0 + 1) * RB / 8);
+    auto chunk_info = [&](int cc) {
+        Chunk c;
+        c.c0 = kt_begin + cc * ch.tiles;
+        c.c1 = c.c0 + ch.tiles < kt_end ? c.c0 + ch.tiles : kt_end;
+        c.upr = (c.c1 - c.c0) * (kTileRows / 8);
+        const uint32_t k0 = (uint32_t)c.c0 * kTileRows;
+        const uint32_t k1 = (uint32_t)c.c1 * kTileRows < (uint32_t)lay.K ? (uint32_t)c.c1 * kTileRows : (uint32_t)lay.K;
+        c.g0 = k0 / (uint32_t)lay.G;
+        c.rw = (int)(((k1 - 1) / (uint32_t)lay.G - c.g0 + 1) * RB / 8);
+        c.upr_m = 0xFFFFFFFFu / (uint32_t)c.upr + 1u;
+        c.rw_m = 0xFFFFFFFFu / (uint32_t)c.rw + 1u;
+        return c;
     };
     // Every thread issues the same loads on every path (addresses clamped
     // into the buffers, unused values zeroed afterwards), so the
     // vector-memory wait before the LDS stores counts exactly the loads
     // issued after them and never drains the code ring.
-    auto stage_load = [&](int cc) {
-        int c0, c1;
-        chunk_bounds(cc, c0, c1);
-        const int64_t k0 = (int64_t)c0 * kTileRows;
-        const int upr = (c1 - c0) * (kTileRows / 8);
-        const int x_units = M * upr;
+    auto stage_load = [&](const Chunk &c) {
+        const int64_t k0 = (int64_t)c.c0 * kTileRows;
+        const int x_units = M * c.upr;
 #pragma unroll
         for (int i = 0; i < XR; ++i) {
             const int e = tid + i * kThreads;
             const int ec = e < x_units ? e : x_units - 1;
-            const int m = ec / upr, u8 = ec - m * upr;
+            const int m = (int)__umulhi((uint32_t)ec, c.upr_m), u8 = ec - m * c.upr;
             const int64_t k = k0 + 8 * u8;
             xv[i] = load16(x + (int64_t)m * lay.K + (k < lay.K ? k : lay.K - 8));
         }
-        int64_t g0;
-        int rw;
-        chunk_groups(c0, c1, g0, rw);
 #pragma unroll
         for (int i = 0; i < kMidRecRegs; ++i) {
             const int e = tid + i * kThreads;
-            const int eb = e / rw, w = e - eb * rw;
+            const int eb = (int)__umulhi((uint32_t)e, c.rw_m), w = e - eb * c.rw;
             const bool ok = eb < kMidWaves && blk0 + eb < lay.nblocks;
             const int64_t b = ok ? blk0 + eb : 0;
-            mv[i] = *reinterpret_cast<const u32x2 *>(packed + b * lay.block_bytes + g0 * RB + 8 * (ok ? w : 0));
+            mv[i] = *reinterpret_cast<const u32x2 *>(packed + b * lay.block_bytes + (int64_t)c.g0 * RB + 8 * (ok ? w : 0));
         }
     };
-    auto stage_store = [&](int cc) {
-        int c0, c1;
-        chunk_bounds(cc, c0, c1);
+    auto stage_store = [&](const Chunk &c, int cc) {
         uint8_t *mbuf = smem + (cc & 1) * meta_buf_bytes;
         uint16_t *xbuf = reinterpret_cast<uint16_t *>(smem + 2 * meta_buf_bytes + (cc & 1) * x_buf_bytes);
-        const int upr = (c1 - c0) * (kTileRows / 8);
-        const int x_units = M * upr;
-        const int64_t k0 = (int64_t)c0 * kTileRows;
+        const int x_units = M * c.upr;
+        const int64_t k0 = (int64_t)c.c0 * kTileRows;
 #pragma unroll
         for (int i = 0; i < XR; ++i) {
             const int e = tid + i * kThreads;
             if (e < x_units) {
-                const int m = e / upr, u8 = e - m * upr;
+                const int m = (int)__umulhi((uint32_t)e, c.upr_m), u8 = e - m * c.upr;
                 const bool in_k = k0 + 8 * u8 < lay.K; // columns past K stage as zero
                 *reinterpret_cast<u32x4 *>(xbuf + m * ch.xpitch + 8 * u8) = in_k ? xv[i] : u32x4{0u, 0u, 0u, 0u};
             }
         }
-        int64_t g0;
-        int rw;
-        chunk_groups(c0, c1, g0, rw);
 #pragma unroll
         for (int i = 0; i < kMidRecRegs; ++i) {
             const int e = tid + i * kThreads;
-            const int eb = e / rw, w = e - eb * rw;
+            const int eb = (int)__umulhi((uint32_t)e, c.rw_m), w = e - eb * c.rw;
             if (eb < kMidWaves && blk0 + eb < lay.nblocks)
                 *reinterpret_cast<u32x2 *>(mbuf + eb * ch.meta_cap + 8 * w) = mv[i];
         }
@@ -483,11 +483,12 @@ __global__ __launch_bounds__(64 * kMidWaves) void gemv_mid_kernel(const uint16_t
 
     // ---- prologue: chunk 0 staged, the ring filled with the first D tiles.
     //      A wave past the last block streams block 0 and stores nothing.
-    stage_load(0);
+    Chunk cur = chunk_info(0);
+    stage_load(cur);
 #pragma unroll
     for (int j = 0; j < D; ++j)
         load_codes<BITS>(ring[j], tiles + (uint32_t)(kt_begin + j < kt_end ? kt_begin + j : kt_end - 1) * TB);
-    stage_store(0);
+    stage_store(cur, 0);
     __syncthreads();
 
     // kMultiTile: tiles left in the current group, and the group
@@ -497,12 +498,10 @@ __global__ __launch_bounds__(64 * kMidWaves) void gemv_mid_kernel(const uint16_t
     const int sh = lay.G == kStepRows ? 0 : 1; // kSplitTiles: G is 32 or 64
 
     for (int cc = 0; cc < nchunks; ++cc) {
-        int c0, c1;
-        chunk_bounds(cc, c0, c1);
-        int64_t g0;
-        int rw;
-        chunk_groups(c0, c1, g0, rw);
+        const int c0 = cur.c0, c1 = cur.c1;
+        const int64_t g0 = cur.g0;
         const bool more = cc + 1 < nchunks;
+        const Chunk nxt = more ? chunk_info(cc + 1) : cur;
         const uint8_t *smeta = smem + (cc & 1) * meta_buf_bytes + wave * ch.meta_cap;
         const uint16_t *xl = reinterpret_cast<const uint16_t *>(smem + 2 * meta_buf_bytes + (cc & 1) * x_buf_bytes) +
                              xr * ch.xpitch + 8 * o - c0 * kTileRows;
@@ -591,7 +590,7 @@ __global__ __launch_bounds__(64 * kMidWaves) void gemv_mid_kernel(const uint16_t
                         }
                     }
                     if (first && j == 0 && more)
-                        stage_load(cc + 1);
+                        stage_load(nxt);
                     // refill the slot with the tile D ahead, across chunk
                     // boundaries (past the range: its last tile again, never
                     // used); issued on every path
@@ -602,8 +601,9 @@ __global__ __launch_bounds__(64 * kMidWaves) void gemv_mid_kernel(const uint16_t
         for (int i = c0 + D; i < c1; i += D)
             group(i, false);
         if (more)
-            stage_store(cc + 1); // the buffer was last read in chunk cc - 1
+            stage_store(nxt, cc + 1); // the buffer was last read in chunk cc - 1
         __syncthreads();
+        cur = nxt;
     }
 
     // ---- outputs straight from the accumulators (C layout: lane holds rows
