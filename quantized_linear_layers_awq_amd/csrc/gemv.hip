@@ -182,6 +182,10 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const uint16_t *__restrict__
         const int64_t k0 = (int64_t)c0 * kTileRows;
         const int units_per_row = nct * (kTileRows / 8);
         const int x_units = M * units_per_row;
+        // unit e is row e / units_per_row: a multiply-high by a per-chunk
+        // constant instead of a division, exact since e * units_per_row <
+        // 2^32 (the chunk fits LDS: units_per_row < 10^4, e < 16 of them)
+        const uint32_t upr_m = 0xFFFFFFFFu / (uint32_t)units_per_row + 1u;
         constexpr int XR = 4; // x units per thread held in registers
         u32x4 xv[XR];
 #pragma unroll
@@ -189,14 +193,14 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const uint16_t *__restrict__
             const int e = tid + i * (int)blockDim.x;
             xv[i] = u32x4{0u, 0u, 0u, 0u};
             if (e < x_units) {
-                const int m = e / units_per_row, u8 = e - m * units_per_row;
+                const int m = (int)__umulhi((uint32_t)e, upr_m), u8 = e - m * units_per_row;
                 const int64_t k = k0 + 8 * u8;
                 if (k < lay.K)
                     xv[i] = load16(x + (int64_t)m * lay.K + k);
             }
         }
         const int64_t k1 = (int64_t)c1 * kTileRows < lay.K ? (int64_t)c1 * kTileRows : lay.K;
-        const int64_t g0 = k0 / lay.G, g1 = (k1 - 1) / lay.G;
+        const int64_t g0 = (uint32_t)k0 / (uint32_t)lay.G, g1 = (uint32_t)(k1 - 1) / (uint32_t)lay.G;
         const int rec_words = (int)((g1 - g0 + 1) * RB / 8);
         u32x2 mv[BPW];
 #pragma unroll
@@ -219,12 +223,12 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const uint16_t *__restrict__
         for (int i = 0; i < XR; ++i) {
             const int e = tid + i * (int)blockDim.x;
             if (e < x_units) {
-                const int m = e / units_per_row, u8 = e - m * units_per_row;
+                const int m = (int)__umulhi((uint32_t)e, upr_m), u8 = e - m * units_per_row;
                 *reinterpret_cast<u32x4 *>(sx + m * ch.xpitch + 8 * u8) = xv[i];
             }
         }
         for (int e = tid + XR * (int)blockDim.x; e < x_units; e += blockDim.x) { // more than XR per thread
-            const int m = e / units_per_row, u8 = e - m * units_per_row;
+            const int m = (int)__umulhi((uint32_t)e, upr_m), u8 = e - m * units_per_row;
             const int64_t k = k0 + 8 * u8;
             u32x4 v = {0u, 0u, 0u, 0u};
             if (k < lay.K)
