@@ -312,7 +312,23 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_kernel(const uint16_t *__re
     // ---- records of k-tile t for block w, as dwords, into the buffer of
     //      k-tile tb (tb % 3); lanes past the records, or past the last
     //      group, read a dword of the block's first record instead ----
-    auto first_group = [&](int t) -> int64_t { return one_tile ? t : ((int64_t)t * kTileRows) / L.G; };
+    // (no division in the loop: G = 32 or 64 gives kGpt groups per k-tile;
+    // whole-k-tile groups are t / (k-tiles per group), a multiply-high by a
+    // per-launch constant, exact while t * tpg < 2^32, else a division; one
+    // group over all of K is group 0)
+    const uint32_t tpg = (uint32_t)(L.G == L.K ? 1 : L.G / kTileRows);
+    const bool tpg_fast = L.G == L.K || (uint64_t)L.ktiles * tpg < (1ull << 32);
+    const uint32_t tpg_m = 0xFFFFFFFFu / tpg + 1u; // unused when tpg == 1
+    auto first_group = [&](int t) -> int64_t {
+        if constexpr (one_tile)
+            return t;
+        else if constexpr (kSplit)
+            return (int64_t)t * kGpt;
+        else if (L.G == L.K)
+            return 0;
+        else
+            return tpg_fast ? (int64_t)__umulhi((uint32_t)t, tpg_m) : (int64_t)((uint32_t)t / tpg);
+    };
     // (32-bit: a block's records are below 2^26 bytes; lanes past kBlockMeta
     // re-read the first record's first dword)
     const int m_lane = lane < kBlockMeta / 4 ? lane : 0;
@@ -331,7 +347,12 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_kernel(const uint16_t *__re
     auto code_buf = [&](int s) { return kW8 ? s % 3 : (s >> 1) & 1; };
     // group of 32-row step `step`
     auto group_of_step = [&](int step) -> int64_t {
-        return one_tile ? step >> 2 : ((int64_t)step * kStepRows) / L.G;
+        if constexpr (one_tile)
+            return step >> 2;
+        else if constexpr (kSplit)
+            return kMode == kGSplit32 ? step : step >> 1; // G = 32 or 64: one or two steps per group
+        else
+            return first_group(step >> 2);
     };
 
     // ---- unpack stage sd into B buffer sd % 2 as exact bf16 (q - z), zero
