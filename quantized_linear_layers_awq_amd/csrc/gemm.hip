@@ -687,7 +687,7 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_kernel(const uint16_t *__re
                                                  : fmaf(acc[0][i][j][e], s_last[0][j], acc[1][i][j][e] * s_last[1][j]);
                 if (row < M) {
                     if (splits > 1)
-                        ws[((int64_t)split * M + row) * L.N + col] = v;
+                        __builtin_nontemporal_store(v, ws + ((int64_t)split * M + row) * L.N + col);
                     else
                         y[row * L.N + col] = f32_to_bf16_bits(v);
                 }
@@ -711,7 +711,8 @@ static void launch_mode(int64_t wgs, int m_tiles, int64_t col0, const GemmPlan &
 
 // y = bf16(sum over s of ws[s]) for the M x N outputs, in split order.  The
 // split count is a template parameter so that a thread issues all S loads
-// at once (one round trip) and then adds them in order.
+// at once (one round trip) and then adds them in order.  The partials were
+// stored non-temporally on other XCDs and are read the same way.
 template <int S>
 __global__ __launch_bounds__(256) void splitk_sum_kernel(const float *__restrict__ ws, int64_t mn,
                                                          uint16_t *__restrict__ y)
@@ -723,7 +724,7 @@ __global__ __launch_bounds__(256) void splitk_sum_kernel(const float *__restrict
         f32x4 p[S];
 #pragma unroll
         for (int s = 0; s < S; ++s)
-            p[s] = *reinterpret_cast<const f32x4 *>(ws + s * mn + i);
+            p[s] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(ws + s * mn + i));
         f32x4 v = p[0];
 #pragma unroll
         for (int s = 1; s < S; ++s)

@@ -611,7 +611,9 @@ __global__ __launch_bounds__(64 * kMidWaves) void gemv_mid_kernel(const uint16_t
     }
 
     // ---- outputs straight from the accumulators (C layout: lane holds rows
-    //      16 c + 4 o + e of column r); with K split, fp32 partials
+    //      16 c + 4 o + e of column r); with K split, fp32 partials, stored
+    //      non-temporally: the summing kernel reads them on other XCDs, so
+    //      they need not stay in this XCD's L2
     if (blk_ok) {
         const int64_t nn = blk * kBlockCols + r;
         if (nn < lay.N) {
@@ -622,7 +624,7 @@ __global__ __launch_bounds__(64 * kMidWaves) void gemv_mid_kernel(const uint16_t
                     const int row = 16 * c + 4 * o + e;
                     if (row < M) {
                         if (gridDim.y > 1)
-                            ws[((int64_t)split * M + row) * lay.N + nn] = yacc[c][e];
+                            __builtin_nontemporal_store(yacc[c][e], ws + ((int64_t)split * M + row) * lay.N + nn);
                         else
                             y[(int64_t)row * lay.N + nn] = f32_to_bf16_bits(yacc[c][e]);
                     }
