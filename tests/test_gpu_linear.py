@@ -35,6 +35,8 @@ GEMM_SHAPES = [
     # K splits: groups of four k-tiles (ranges on group boundaries), one group
     # over all of K (each range a one-group layout), a ragged last k-tile
     (4, 96, 4096, 256, 512), (8, 64, 3072, 128, 3072), (4, 40, 2080, 128, 32), (4, 16, 2048, 136, 64),
+    # between the GEMV kernels' 64 rows and one 256-row tile
+    (4, 100, 768, 136, 256), (8, 77, 2080, 40, 32), (8, 128, 512, 64, 32),
 ]
 
 # GEMM calls with 17 <= M <= 64 run the GEMV kernel with two or four 16-row
