@@ -162,20 +162,22 @@ int tf_dequant_w8_f32(const void *packed, size_t packed_bytes, float *w,
                       int64_t K, int64_t N, int64_t G, void *stream);
 
 /* Test hooks of the GEMM's launch plan (host only, no GPU work).
- * The GEMM covers y with 256-row x 128-column tiles.  When the tiles are not
- * a whole number of rounds over the device's compute units, it runs the
- * columns of the last partial round as 256 x 64 tiles in a second launch.
+ * The GEMM covers y with 256-row x 128-column tiles (128 x 128 up to 128
+ * rows).  When 256-row tiles are not a whole number of rounds over the
+ * device's compute units, it runs the columns of the last partial round as
+ * 256 x 64 tiles in a second launch.
  * When the tiles fill less than half the compute units (small M), it splits
  * K into ranges that run in the same launch, each writing fp32 partial sums
  * to the workspace, and a second kernel adds them in range order (so
  * tf_workspace_bytes is non-zero for those shapes).  The plan never changes
  * the result's bits except through that split: the order of the split sums.
- *   tf_gemm_plan: writes six values for a GEMM of (bits, M, K, N, G) on a
+ *   tf_gemm_plan: writes seven values for a GEMM of (bits, M, K, N, G) on a
  *     device of `cus` compute units: out[5] = 1 when the call runs the GEMV
- *     kernel (then out[0..2] = 0), 0 for the tiled GEMM; out[0] = row tiles,
- *     out[1] = 128-column tiles, out[2] = 64-column tiles, out[3] = K ranges,
- *     out[4] = k-tiles of 128 rows per range.  TF_ERR_NULL / TF_ERR_SHAPE /
- *     TF_ERR_GROUP / TF_ERR_UNSUPPORTED on bad input.
+ *     kernel (then out[0..2] = out[6] = 0), 0 for the tiled GEMM; out[0] =
+ *     row tiles of out[6] rows (256 or 128), out[1] = 128-column tiles,
+ *     out[2] = 64-column tiles, out[3] = K ranges, out[4] = k-tiles of 128
+ *     rows per range.  TF_ERR_NULL / TF_ERR_SHAPE / TF_ERR_GROUP /
+ *     TF_ERR_UNSUPPORTED on bad input.
  *   tf_gemm_set_planning_cus: makes later GEMM and GEMV calls and workspace
  *     queries of this process plan for n compute units instead of the
  *     current device's (n <= 0 restores the device's).  Process-wide; not

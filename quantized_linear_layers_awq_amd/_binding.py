@@ -232,12 +232,13 @@ def tf_dequant_w8_f32(packed, K, N, G, w=None, stream=None):
     return _dequant("tf_dequant_w8_f32", packed, K, N, G, w, stream)
 
 
-def tf_gemm_plan(bits: int, M: int, K: int, N: int, G: int, cus: int) -> tuple[int, int, int, int, int, int]:
+def tf_gemm_plan(bits: int, M: int, K: int, N: int, G: int, cus: int) -> tuple[int, ...]:
     """Test hook: (row tiles, 128-column tiles, 64-column tiles, K ranges,
-    k-tiles per range, 1 if the call runs the GEMV kernel else 0) of a GEMM
-    call's launch plan on a device of `cus` compute units (host only)."""
+    k-tiles per range, 1 if the call runs the GEMV kernel else 0, rows per
+    row tile) of a GEMM call's launch plan on a device of `cus` compute
+    units (host only)."""
     L = load_library()
-    out = (ctypes.c_int64 * 6)()
+    out = (ctypes.c_int64 * 7)()
     _check(L.tf_gemm_plan(bits, M, K, N, G, cus, out), "tf_gemm_plan")
     return tuple(int(v) for v in out)
 

@@ -216,6 +216,7 @@ int tf_gemm_plan(int bits, int64_t M, int64_t K, int64_t N, int64_t G, int cus, 
         out[3] = tf::gemv_splits(lay, M, cus, &st);
         out[4] = st;
         out[5] = 1;
+        out[6] = 0;
         return TF_OK;
     }
     const tf::GemmPlan p = tf::plan_gemm(M, N, K, G, cus);
@@ -225,6 +226,7 @@ int tf_gemm_plan(int bits, int64_t M, int64_t K, int64_t N, int64_t G, int cus, 
     out[3] = p.splits;
     out[4] = p.split_tiles;
     out[5] = 0;
+    out[6] = p.rows;
     return TF_OK;
 }
 

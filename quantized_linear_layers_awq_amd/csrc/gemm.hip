@@ -59,11 +59,11 @@ constexpr int kAStages = 3;
 // at once cover 2 activation panels x 16 weight column tiles (measured best of
 // 1, 2, 4 and all).
 constexpr int kBand = 2;
-constexpr int kAStageBytes = kGBM * kStage * 2;  // 32 KiB
+constexpr int a_stage_bytes(int bm) { return bm * kStage * 2; } // 32 / 16 KiB
 constexpr int kGWaves = 8;                       // waves per workgroup
 constexpr int kGThreads = 64 * kGWaves;
 constexpr int kMetaWaveBytes = 256;              // record bytes DMA'd per block per k-tile
-constexpr int kOffB = kAStages * kAStageBytes;
+constexpr int off_b(int bm) { return kAStages * a_stage_bytes(bm); }
 // Tile widths: WN = 2 is the 256 x 128 tile (waves 4 x 2, 64 x 64 each), WN =
 // 1 the 256 x 64 tile (waves 8 x 1, 32 x 64 each) that fills the last
 // partial round of a grid.  Per width: columns, packed blocks, bytes of one
@@ -73,14 +73,17 @@ constexpr int tile_blocks(int wn) { return 4 * wn; }
 constexpr int bstage_bytes(int wn) { return tile_cols(wn) * kStage * 2; } // 16 / 8 KiB
 constexpr int codebuf_bytes(int wn) { return tile_blocks(wn) * 1024; }    // one k-tile (W4) or stage (W8)
 constexpr int metabuf_bytes(int wn) { return tile_blocks(wn) * kMetaWaveBytes; }
-constexpr int off_codes(int wn) { return kOffB + 2 * bstage_bytes(wn); }
+constexpr int off_codes(int wn, int bm) { return off_b(bm) + 2 * bstage_bytes(wn); }
 // code buffers: W4 two k-tiles, W8 three stages (each fetched two stages
 // before it is unpacked)
 constexpr int code_bufs(int bits) { return bits == 8 ? 3 : 2; }
 constexpr int kMetaBufs = 3;                     // records are fetched two k-tiles ahead
-constexpr int off_meta(int bits, int wn) { return off_codes(wn) + code_bufs(bits) * codebuf_bytes(wn); }
-constexpr int gemm_lds(int bits, int wn) { return off_meta(bits, wn) + kMetaBufs * metabuf_bytes(wn); } // <= 158 KiB
-static_assert(gemm_lds(8, 2) <= 160 * 1024, "LDS of one CU");
+constexpr int off_meta(int bits, int wn, int bm) { return off_codes(wn, bm) + code_bufs(bits) * codebuf_bytes(wn); }
+constexpr int gemm_lds(int bits, int wn, int bm)
+{
+    return off_meta(bits, wn, bm) + kMetaBufs * metabuf_bytes(wn); // <= 158 KiB
+}
+static_assert(gemm_lds(8, 2, kGBM) <= 160 * 1024, "LDS of one CU");
 
 // 16-byte unit (row, c) of a [rows][64] bf16 tile, c = 0..7.  Rows are 128
 // bytes, so two share a 256-byte bank line; the XOR with (row / 2) % 8 puts
@@ -182,7 +185,7 @@ template <int I, int N, typename F> __device__ __forceinline__ void static_for(F
 // width 64 WN, starting at output column col0.  With one range the output is
 // y (bf16); with several, each range writes its fp32 partial sums to
 // ws[range][M][N] and a second kernel adds them.
-template <int BITS, int kMode, int WN>
+template <int BITS, int kMode, int WN, int BM>
 __global__ __launch_bounds__(kGThreads, 1) void gemm_kernel(const uint16_t *__restrict__ x,
                                                             const uint8_t *__restrict__ packed,
                                                             uint16_t *__restrict__ y, Layout lay, int64_t M,
@@ -193,7 +196,14 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_kernel(const uint16_t *__re
     constexpr int kBStageBytes = bstage_bytes(WN), kCodeBufBytes = codebuf_bytes(WN);
     constexpr int kMetaBufBytes = metabuf_bytes(WN);
     constexpr int kBOct = kGBN * 16; // bytes per k-octet row of a dequantized B stage
-    constexpr int MI = WN;           // 32-row MFMA tiles per wave (wave rows: 32 MI)
+    // 32-row MFMA tiles per wave (wave rows: 32 MI): a 256-row tile is 4 x 2
+    // waves of 64 x 64 (WN = 2) or 8 x 1 of 32 x 64 (WN = 1); a 128-row tile
+    // (128 columns only) 4 x 2 waves of 32 x 64
+    static_assert(BM == kGBM || (BM == 128 && WN == 2), "row tile");
+    constexpr int MI = BM == kGBM ? WN : 1;
+    constexpr int kAStageBytes = a_stage_bytes(BM);
+    constexpr int kAJ = BM / 64;     // x DMA instructions (8 rows each) per wave and stage
+    constexpr int kARows = BM / kGWaves; // rows of a stage each wave fetches
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     constexpr int RB = record_bytes(BITS);
     constexpr int kSpg = kMode; // slices per group (0: whole k-tiles per group)
@@ -228,7 +238,7 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_kernel(const uint16_t *__re
     const int band = tile / (band_rows * n_tiles), in_band = tile - band * band_rows * n_tiles;
     const int rows_here = m_tiles - band * band_rows < band_rows ? m_tiles - band * band_rows : band_rows;
     const int nt = in_band / rows_here, mt = band * band_rows + (in_band - (in_band / rows_here) * rows_here);
-    const int64_t m0 = (int64_t)mt * kGBM;
+    const int64_t m0 = (int64_t)mt * BM;
     const int64_t blk0 = (col0 >> 4) + (int64_t)nt * kGBlocks;
 
     // ---- the k range of this split as a layout of its own: its groups,
@@ -265,24 +275,25 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_kernel(const uint16_t *__re
     const int64_t K = L.K;
 
     uint8_t *const sA = lds;
-    uint8_t *const sB = lds + kOffB;
-    uint8_t *const sCodes = lds + off_codes(WN);
-    uint8_t *const sMeta = lds + off_meta(BITS, WN);
+    uint8_t *const sB = lds + off_b(BM);
+    uint8_t *const sCodes = lds + off_codes(WN, BM);
+    uint8_t *const sMeta = lds + off_meta(BITS, WN, BM);
 
-    // ---- activations.  Wave w fills rows 32w .. 32w+31 of a stage, 8 rows
-    //      per instruction j; lane p takes row 8j + p/8 and the 16-byte unit c
-    //      that the swizzle places at slot p%8.  The address is a wave-uniform
-    //      base (row 32w of the tile, clamped at M - 1, plus the stage's k) and
-    //      a 32-bit lane offset; rows past M read row M - 1 (computed, never
-    //      stored). ----
+    // ---- activations.  Wave w fills rows R w .. R w + R - 1 of a stage (R =
+    //      BM / 8), 8 rows per instruction j; lane p takes row 8j + p/8 and the
+    //      16-byte unit c that the swizzle places at slot p%8 (R w is a
+    //      multiple of 16, so the swizzle of those rows repeats every two j).
+    //      The address is a wave-uniform base (row R w of the tile, clamped at
+    //      M - 1, plus the stage's k) and a 32-bit lane offset; rows past M
+    //      read row M - 1 (computed, never stored). ----
     const int a_slot = lane & 7;
     const int a_c[2] = {a_slot ^ ((lane >> 4) & 7), a_slot ^ ((4 + (lane >> 4)) & 7)}; // unit for even / odd j
-    const int64_t a_row_base = m0 + 32 * wave < M ? m0 + 32 * wave : M - 1;
+    const int64_t a_row_base = m0 + kARows * wave < M ? m0 + kARows * wave : M - 1;
     const Rsrc a_rsrc = make_rsrc(reinterpret_cast<const uint8_t *>(x) + (a_row_base * lda + k_begin) * 2);
-    uint32_t a_voff[4];
+    uint32_t a_voff[kAJ];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        int64_t row = m0 + 32 * wave + 8 * j + (lane >> 3);
+    for (int j = 0; j < kAJ; ++j) {
+        int64_t row = m0 + kARows * wave + 8 * j + (lane >> 3);
         row = row < M ? row : M - 1;
         a_voff[j] = (uint32_t)((row - a_row_base) * lda * 2 + 16 * a_c[j & 1]);
     }
@@ -291,9 +302,9 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_kernel(const uint16_t *__re
     // offset is clamped there and the unit re-reads the row's last 8 columns
     // (finite values that meet zero weights).  Branch-free: two VALU per load.
     const uint32_t a_lim[2] = {(uint32_t)(2 * K - 16 - 16 * a_c[0]), (uint32_t)(2 * K - 16 - 16 * a_c[1])};
-    // instructions j0 .. j1 - 1 of the four that fill the wave's rows of stage s
+    // instructions j0 .. j1 - 1 of the kAJ that fill the wave's rows of stage s
     auto dma_a = [&](int s, int j0, int j1) {
-        uint8_t *dst = sA + (s % kAStages) * kAStageBytes + 32 * wave * 128;
+        uint8_t *dst = sA + (s % kAStages) * kAStageBytes + kARows * wave * 128;
         const uint32_t ks = (uint32_t)s * kStage * 2;
 #pragma unroll
         for (int j = j0; j < j1; ++j)
@@ -514,16 +525,16 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_kernel(const uint16_t *__re
         if (kW8)
             dma_codes(0, 1, 1);
     }
-    dma_a(0, 0, 4);
-    dma_a(1, 0, 4);
+    dma_a(0, 0, kAJ);
+    dma_a(1, 0, kAJ);
     if (unpacker) {
         if (kW8)
             dma_codes(ktiles > 1 ? 1 : 0, ktiles > 1 ? 0 : 1, 2); // stage 2
         else
             dma_codes(ktiles > 1 ? 1 : 0, 0, 1);
-        wait_vmcnt<5>();
+        wait_vmcnt<kAJ + 1>();
     } else {
-        wait_vmcnt<4>();
+        wait_vmcnt<kAJ>();
     }
     lds_barrier();
     if (unpacker) {
@@ -592,9 +603,9 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_kernel(const uint16_t *__re
                     read_frags(a_st, h, sl + 1, af[cur ^ 1], bf[cur ^ 1]);
                 __builtin_amdgcn_sched_barrier(0);
                 if constexpr (sl == 0) {
-                    dma_a(sa, 0, 2);
+                    dma_a(sa, 0, kAJ / 2);
                 } else if constexpr (sl == 1) {
-                    dma_a(sa, 2, 4);
+                    dma_a(sa, kAJ / 2, kAJ);
                 } else if constexpr (sl == 2) {
                     if (unpacker) {
                         if constexpr (kW8) {
@@ -642,14 +653,14 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_kernel(const uint16_t *__re
 
             // ---- everything issued before this stage has landed (stage
             //      s + 1's x, the next codes and records); only this stage's
-            //      loads may still be in flight (x: 4, codes and records: 1
+            //      loads may still be in flight (x: kAJ, codes and records: 1
             //      or 2 on the unpacking waves) ----
             if (!unpacker)
-                wait_vmcnt<4>();
+                wait_vmcnt<kAJ>();
             else if constexpr (kW8 && h == 0)
-                wait_vmcnt<6>();
+                wait_vmcnt<kAJ + 2>();
             else
-                wait_vmcnt<5>();
+                wait_vmcnt<kAJ + 1>();
             wait_lgkmcnt0();
             lds_barrier();
         });
@@ -697,15 +708,16 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_kernel(const uint16_t *__re
 
 // The kernel needs more than the default 64 KiB of dynamic LDS; raise the
 // limit once per instantiation.
-template <int BITS, int kMode, int WN>
+template <int BITS, int kMode, int WN, int BM>
 static void launch_mode(int64_t wgs, int m_tiles, int64_t col0, const GemmPlan &plan, hipStream_t stream,
                         const uint16_t *x, const uint8_t *pk, uint16_t *y, const Layout &lay, int64_t M, float *ws)
 {
-    auto kern = &gemm_kernel<BITS, kMode, WN>;
+    auto kern = &gemm_kernel<BITS, kMode, WN, BM>;
     static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                                       hipFuncAttributeMaxDynamicSharedMemorySize, gemm_lds(BITS, WN));
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                       gemm_lds(BITS, WN, BM));
     (void)attr;
-    kern<<<dim3((unsigned)wgs), kGThreads, gemm_lds(BITS, WN), stream>>>(
+    kern<<<dim3((unsigned)wgs), kGThreads, gemm_lds(BITS, WN, BM), stream>>>(
         x, pk, y, lay, M, m_tiles, col0, (int)plan.splits, (int)plan.split_tiles, ws);
 }
 
@@ -812,7 +824,10 @@ void set_gemm_route(int route) { g_gemm_route.store(route == 1 || route == 2 ? r
 GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, int64_t G, int cus)
 {
     GemmPlan p;
-    p.m_tiles = (M + kGBM - 1) / kGBM;
+    // up to 128 rows, 128-row tiles: a 256-row tile would compute at least
+    // as many padding rows as real ones
+    p.rows = M <= kShortTileMaxM ? kShortTileRows : kGBM;
+    p.m_tiles = (M + p.rows - 1) / p.rows;
     const int64_t n_wide = (N + tile_cols(2) - 1) / tile_cols(2);
     const int64_t tiles = p.m_tiles * n_wide;
     const int64_t ktiles = (K + kTileRows - 1) / kTileRows;
@@ -839,7 +854,7 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, int64_t G, int cus)
             }
         }
     }
-    if (tiles % cus == 0)
+    if (tiles % cus == 0 || p.rows != kGBM)
         return p;
     // the whole rounds with 128-column tiles, the columns left over as
     // 64-column tiles when they fit one round (a last partial round of wide
@@ -872,21 +887,25 @@ hipError_t launch_gemm(int bits, const uint16_t *x, const void *packed, uint16_t
                      : lay.G == 32            ? kGSplit32
                                               : kGSplit64;
     const int mt = (int)plan.m_tiles;
-    auto go = [&](auto bits_c, auto wn_c, int64_t n_cols, int64_t col0) {
-        constexpr int B = decltype(bits_c)::value, WN = decltype(wn_c)::value;
+    auto go = [&](auto bits_c, auto wn_c, auto bm_c, int64_t n_cols, int64_t col0) {
+        constexpr int B = decltype(bits_c)::value, WN = decltype(wn_c)::value, BM = decltype(bm_c)::value;
         const int64_t wgs = plan.m_tiles * n_cols * plan.splits;
         switch (mode) {
-        case kGOneTile: launch_mode<B, kGOneTile, WN>(wgs, mt, col0, plan, stream, x, pk, y, lay, M, ws); break;
-        case kGWhole: launch_mode<B, kGWhole, WN>(wgs, mt, col0, plan, stream, x, pk, y, lay, M, ws); break;
-        case kGSplit32: launch_mode<B, kGSplit32, WN>(wgs, mt, col0, plan, stream, x, pk, y, lay, M, ws); break;
-        default: launch_mode<B, kGSplit64, WN>(wgs, mt, col0, plan, stream, x, pk, y, lay, M, ws); break;
+        case kGOneTile: launch_mode<B, kGOneTile, WN, BM>(wgs, mt, col0, plan, stream, x, pk, y, lay, M, ws); break;
+        case kGWhole: launch_mode<B, kGWhole, WN, BM>(wgs, mt, col0, plan, stream, x, pk, y, lay, M, ws); break;
+        case kGSplit32: launch_mode<B, kGSplit32, WN, BM>(wgs, mt, col0, plan, stream, x, pk, y, lay, M, ws); break;
+        default: launch_mode<B, kGSplit64, WN, BM>(wgs, mt, col0, plan, stream, x, pk, y, lay, M, ws); break;
         }
     };
     auto both = [&](auto bits_c) {
+        if (plan.rows != kGBM) { // short tiles: 128 columns only
+            go(bits_c, ic<2>{}, ic<kShortTileRows>{}, plan.wide_cols, 0);
+            return;
+        }
         if (plan.wide_cols > 0)
-            go(bits_c, ic<2>{}, plan.wide_cols, 0);
+            go(bits_c, ic<2>{}, ic<kGBM>{}, plan.wide_cols, 0);
         if (plan.narrow_cols > 0)
-            go(bits_c, ic<1>{}, plan.narrow_cols, plan.wide_cols * tile_cols(2));
+            go(bits_c, ic<1>{}, ic<kGBM>{}, plan.narrow_cols, plan.wide_cols * tile_cols(2));
     };
     if (bits == 4)
         both(ic<4>{});

@@ -26,13 +26,16 @@ hipError_t launch_gemv(int bits, const uint16_t *x, const void *packed, uint16_t
 // y = bf16(sum of the splits' fp32 partials ws[s][mn]), added in split order;
 // 2 <= splits <= 16 (both plans stay within that).
 void launch_splitk_sum(const float *ws, int splits, int64_t mn, uint16_t *y, hipStream_t stream);
-// How the GEMM covers the output: m_tiles row tiles of 256 rows, then
-// wide_cols column tiles of 128 columns from column 0 in one launch and
-// narrow_cols tiles of 64 columns after them in a second one.  With splits
-// > 1 (small M), K is cut into ranges of split_tiles k-tiles that run in the
-// same launch and write fp32 partial sums to the workspace.
+// How the GEMM covers the output: m_tiles row tiles of `rows` rows (256, or
+// 128 up to kShortTileMaxM rows), then wide_cols column tiles of 128 columns
+// from column 0 in one launch and (256-row tiles only) narrow_cols tiles of
+// 64 columns after them in a second one.  With splits > 1 (small M), K is
+// cut into ranges of split_tiles k-tiles that run in the same launch and
+// write fp32 partial sums to the workspace.
+constexpr int64_t kShortTileRows = 128;
+constexpr int64_t kShortTileMaxM = 128;
 struct GemmPlan {
-    int64_t m_tiles, wide_cols, narrow_cols, splits, split_tiles;
+    int64_t m_tiles, wide_cols, narrow_cols, splits, split_tiles, rows;
 };
 GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, int64_t G, int cus);
 // Compute units plan_gemm assumes: the forced count, else the device's.

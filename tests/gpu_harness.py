@@ -124,7 +124,7 @@ def split_cus(q, bits, M, K, N, G):
     mt = -(-M // 256)
     tiles = mt * -(-N // 128)
     for cus in range(2, tiles + 1):
-        _, wide, narrow, splits, _, _ = q.tf_gemm_plan(bits, M, K, N, G, cus)
+        _, wide, narrow, splits, _, _, _ = q.tf_gemm_plan(bits, M, K, N, G, cus)
         if wide and narrow and splits == 1:
             return cus
     return None

@@ -118,7 +118,7 @@ def test_workspace_cannot_hold_bf16_weights(lib, route, M, K, N, G):
 
 
 def _plan(lib, M, N, cus, K=4096, G=128, bits=4):
-    out = (ctypes.c_int64 * 6)()
+    out = (ctypes.c_int64 * 7)()
     st = lib.tf_gemm_plan(bits, M, K, N, G, cus, out)
     return st, tuple(out)
 
@@ -135,13 +135,13 @@ def test_workspace_only_for_split_k(lib, route):
         assert lib.tf_workspace_bytes(8, 0, 7, 8192, 8192, 8192) == 0
         assert lib.tf_workspace_bytes(4, 0, 17, 4096, 4096, 128) == 0  # beyond the GEMV's M
         # 16 rows, per-channel W8 8192 x 8192: the 16-row-chunk kernel in four K ranges
-        st, (_, _, _, splits, _, _) = _plan(lib, 16, 8192, 256, K=8192, G=8192, bits=8)
+        st, (_, _, _, splits, _, _, _) = _plan(lib, 16, 8192, 256, K=8192, G=8192, bits=8)
         assert lib.tf_workspace_bytes(8, 0, 16, 8192, 8192, 8192) == (16 * 8192 * 4 * splits if splits > 1 else 0)
         assert lib.tf_workspace_bytes(5, 1, 1, 4096, 4096, 128) == 0
         for bits, M, K, N, G in [(8, 512, 8192, 8192, 8192), (4, 1, 4096, 4096, 128), (4, 2048, 4096, 14336, 128),
                                  (4, 100, 1024, 200, 64), (4, 64, 384, 64, 128), (4, 48, 4096, 4096, 128),
                                  (8, 20, 8192, 1024, 8192), (4, 64, 4096, 28672, 128)]:
-            st, (_, _, _, splits, _, _) = _plan(lib, M, N, 256, K=K, G=G, bits=bits)
+            st, (_, _, _, splits, _, _, _) = _plan(lib, M, N, 256, K=K, G=G, bits=bits)
             assert st == TF_OK
             want = splits * M * N * 4 if splits > 1 else 0
             assert lib.tf_workspace_bytes(bits, 1, M, K, N, G) == want
@@ -190,8 +190,8 @@ def test_gemv_route_plan_covers_k_once(lib):
         cases.append((rng.randint(1, 64), 8 * rng.randint(1, 5000), rng.choice([1, 2, 3, 7, 64, 80, 256, 304]),
                       K, rng.choice([G, K])))
     for M, N, cus, K, G in cases:
-        st, (mt, wide, narrow, splits, st_tiles, route) = _plan(lib, M, N, cus, K=K, G=G)
-        assert st == TF_OK and route == 1 and mt == wide == narrow == 0, (M, N, cus, K, G)
+        st, (mt, wide, narrow, splits, st_tiles, route, rows) = _plan(lib, M, N, cus, K=K, G=G)
+        assert st == TF_OK and route == 1 and mt == wide == narrow == rows == 0, (M, N, cus, K, G)
         ktiles = -(-K // 128)
         groups = -(-N // 128)
         assert (splits - 1) * st_tiles < ktiles <= splits * st_tiles
@@ -234,12 +234,15 @@ def test_gemm_plan_covers_every_column_once(lib, tiled_route):
         cases.append((rng.randint(1, 9000), 8 * rng.randint(1, 5000), rng.choice([1, 2, 3, 7, 64, 80, 256, 304]),
                       K, rng.choice([G, K])))
     for M, N, cus, K, G in cases:
-        st, (mt, wide, narrow, splits, st_tiles, route) = _plan(lib, M, N, cus, K=K, G=G)
+        st, (mt, wide, narrow, splits, st_tiles, route, rows) = _plan(lib, M, N, cus, K=K, G=G)
         assert st == TF_OK and route == 0, (M, N, cus, K, G)
         n_wide = -(-N // 128)
         tiles = mt * n_wide
         ktiles = -(-K // 128)
-        assert mt == -(-M // 256)
+        assert rows == (128 if M <= 128 else 256)
+        assert mt == -(-M // rows)
+        if rows == 128:
+            assert narrow == 0  # short tiles come in one width
         if splits > 1:
             assert wide == n_wide and narrow == 0
             assert splits * tiles <= cus
@@ -256,8 +259,10 @@ def test_gemm_plan_covers_every_column_once(lib, tiled_route):
             assert mt * narrow <= cus
             assert mt * wide <= (tiles // cus) * cus
     # the headline prefill shape: 3 whole rounds of wide tiles, one of narrow
-    assert _plan(lib, 2048, 14336, 256)[1] == (8, 96, 32, 1, 32, 0)
-    assert _plan(lib, 2048, 4096, 256, K=14336)[1] == (8, 32, 0, 1, 112, 0)
+    assert _plan(lib, 2048, 14336, 256)[1] == (8, 96, 32, 1, 32, 0, 256)
+    assert _plan(lib, 2048, 4096, 256, K=14336)[1] == (8, 32, 0, 1, 112, 0, 256)
+    # 65..128 rows: one 128-row tile per column tile
+    assert _plan(lib, 100, 28672, 256)[1] == (1, 224, 0, 1, 32, 0, 128)
 
 
 def test_gemm_plan_rejects_bad_input(lib):
@@ -265,7 +270,7 @@ def test_gemm_plan_rejects_bad_input(lib):
     assert _plan(lib, 64, 0, 256)[0] == TF_ERR_SHAPE
     assert _plan(lib, 64, 64, 0)[0] == TF_ERR_SHAPE
     assert _plan(lib, 64, 64, 256, K=4096, G=96)[0] == TF_ERR_GROUP
-    out = (ctypes.c_int64 * 6)()
+    out = (ctypes.c_int64 * 7)()
     assert lib.tf_gemm_plan(4, 64, 4096, 64, 128, 256, None) == TF_ERR_NULL
     assert lib.tf_gemm_plan(5, 64, 4096, 64, 128, 256, out) == 6  # TF_ERR_UNSUPPORTED
 
