@@ -31,7 +31,9 @@
  *    packed word).
  *  - G > 0, G % 32 == 0, K % G == 0, and G divides 128, is a multiple of
  *    128, or equals K.  Per-channel metadata is G == K.
- *  - GEMV: 1 <= M <= 16.  GEMM: 1 <= M <= 2^30 and K < 2^25.
+ *  - GEMV: 1 <= M <= 16.  GEMM: 1 <= M <= 2^30.  Both: K < 2^25 (the
+ *    kernels' offsets within a row of x and within a packed block are
+ *    32-bit; tf_packed_bytes_* and the repack take K up to 2^31).
  *  - Sizes are 64-bit; every dimension must be below 2^31.
  */
 #ifndef TILEFUSE_H

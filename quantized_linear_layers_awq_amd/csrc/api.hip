@@ -76,7 +76,9 @@ int linear(int bits, bool is_gemm, const uint16_t *x, const void *packed, size_t
         return st;
     if (is_gemm ? M > (int64_t(1) << 30) : M > 16)
         return TF_ERR_SHAPE;
-    if (is_gemm && K >= (int64_t(1) << 25)) // the GEMM's activation offsets are 32-bit
+    // 32-bit offsets: a row of x in the GEMM, and a code tile within a
+    // 16-column block (K / 128 tiles of up to 2 KiB) in the GEMV kernels
+    if (K >= (int64_t(1) << 25))
         return TF_ERR_SHAPE;
     if (M == 0)
         return TF_OK;

@@ -290,6 +290,10 @@ class TestValidation:
         assert self._gemv(lib, K=33) == TF_ERR_SHAPE
         assert self._gemv(lib, N=12) == TF_ERR_SHAPE
         assert self._gemv(lib, M=17) == TF_ERR_SHAPE
+        # K at the 32-bit offset limit of the kernels, for both entry points
+        assert self._gemv(lib, K=1 << 25, G=1 << 25) == TF_ERR_SHAPE
+        assert self._gemv(lib, M=64, K=1 << 25, G=128, fn="tf_gemm_w4a16") == TF_ERR_SHAPE
+        assert self._gemv(lib, K=(1 << 25) - 32, G=(1 << 25) - 32, nbytes=10) == TF_ERR_BUFFER_TOO_SMALL
         assert self._gemv(lib, M=-1) == TF_ERR_SHAPE
         assert self._gemv(lib, K=0) == TF_ERR_SHAPE
         assert self._gemv(lib, M=2**30 + 1, fn="tf_gemm_w4a16") == TF_ERR_SHAPE
