@@ -55,6 +55,7 @@ def lib():
         L.oracle_dequant_w4.argtypes = [P, P, P, I64, I64, I64, P, I64, P]
         L.oracle_dequant_w8.argtypes = [P, P, P, I64, I64, I64, P, I64, P]
         L.oracle_linear.argtypes = [P, I64, I64, P, I64, P]
+        L.oracle_silu_mul.argtypes = [P, P, I64, P]
         L.oracle_num_threads.restype = ctypes.c_int
         L.oracle_packed_bytes.argtypes = [ctypes.c_int, I64, I64, I64]
         L.oracle_packed_bytes.restype = ctypes.c_size_t
@@ -152,6 +153,26 @@ def awq_linear(case, cols=None, rows=None) -> np.ndarray:
     w = dequant(case.bits, case.qweight, case.qzeros, case.scales, case.K, case.N, case.G, cols)
     x = case.x if rows is None else case.x[np.asarray(rows)]
     return linear(x, w)
+
+
+def silu_mul(g, u) -> np.ndarray:
+    """silu(g) * u elementwise in fp64 (g and u fp64 arrays of one shape)."""
+    g = _c(g, np.float64)
+    u = _c(u, np.float64)
+    if g.shape != u.shape:
+        raise ValueError("g and u differ in shape")
+    out = np.empty(g.shape, dtype=np.float64)
+    lib().oracle_silu_mul(_p(g), _p(u), g.size, _p(out))
+    return out
+
+
+def awq_linear_silu_mul(case, cols=None, rows=None) -> np.ndarray:
+    """Reference output of a synth.Case holding a [gate | up] layer (N even):
+    fp64 silu(y[:, n]) * y[:, N/2 + n] for the chosen rows and n < N/2."""
+    half = case.N // 2
+    cols = np.arange(half) if cols is None else np.asarray(cols, dtype=np.int64)
+    y = awq_linear(case, cols=np.concatenate([cols, cols + half]), rows=rows)
+    return silu_mul(y[:, : cols.size], y[:, cols.size :])
 
 
 def packed_bytes(bits, K, N, G) -> int:

@@ -27,6 +27,9 @@
  * reads laid out contiguously).  The layout itself is this library's own
  * (the pages fix no geometry); it is spelled out next to oracle_repack.
  *
+ * oracle_silu_mul adds the SiLU product of a fused [gate | up] layer
+ * (a decode epilogue; see that function).
+ *
  * Pins: every function here is checked against something other than itself
  * by the host-only tests (exact rationals, integer GEMM special case,
  * exhaustive dequant exactness, library fp64 matmul, golden word fixtures,
@@ -180,6 +183,20 @@ void oracle_linear(const uint16_t *x, int64_t M, int64_t K, const float *w, int6
                 yr[n] += xv * (double)wr[n];
         }
     }
+}
+
+/* ------------------------------------------------------------------ */
+/* SiLU product of a fused [gate | up] layer: out = silu(g) * u with   */
+/* silu(v) = v * sigmoid(v) = v / (1 + e^-v), all in fp64.  The pages  */
+/* name no activation; this is the Llama-style MLP's, applied to the   */
+/* unrounded sums of the gate and up columns (the summary's Results    */
+/* section: token generation pays per-kernel dispatch, so the product   */
+/* runs in the GEMV's epilogue rather than a launch of its own).       */
+/* ------------------------------------------------------------------ */
+void oracle_silu_mul(const double *g, const double *u, int64_t n, double *out)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = g[i] / (1.0 + exp(-g[i])) * u[i];
 }
 
 int oracle_num_threads(void)

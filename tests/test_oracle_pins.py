@@ -259,3 +259,56 @@ def test_linear_sampled_rows_and_columns_match_full():
     y = oracle.awq_linear(c)
     rows, cols = np.array([5, 0, 3]), np.array([127, 1, 64, 9])
     assert np.array_equal(oracle.awq_linear(c, cols=cols, rows=rows), y[rows][:, cols])
+
+
+# ----------------------------------------------------------------------------
+# SiLU product of a fused [gate | up] layer
+# ----------------------------------------------------------------------------
+
+
+def test_silu_closed_forms():
+    # sigmoid(ln k) = k / (k + 1), so silu(ln k) = ln k * k / (k + 1)
+    ks = np.array([3.0, 1.0 / 3.0, 7.0, 1.0])
+    g = np.log(ks)
+    got = oracle.silu_mul(g, np.ones_like(g))
+    want = g * ks / (ks + 1.0)
+    assert np.all(np.abs(got - want) <= 4e-16 * np.abs(want) + 1e-300)
+    # the limits: silu(v) -> v as v -> +inf, -> -0 as v -> -inf, with no NaN
+    far = oracle.silu_mul(np.array([800.0, -800.0, 40.0]), np.ones(3))
+    assert far[0] == 800.0 and far[1] == 0.0 and np.signbit(far[1]) and far[2] == 40.0
+
+
+def test_silu_mul_scales_the_up_operand_only():
+    # silu(ln 3) * 2 is 1.5 ln 3; swapping the operands would give silu(2) ln 3
+    got = oracle.silu_mul(np.array([np.log(3.0)]), np.array([2.0]))
+    assert abs(got[0] - 1.5 * np.log(3.0)) <= 4e-16 * got[0]
+    rng = np.random.default_rng(41)
+    g, u = rng.normal(0, 4, 64), rng.normal(0, 4, 64)
+    assert np.array_equal(oracle.silu_mul(g, u), oracle.silu_mul(g, np.ones(64)) * u)
+
+
+def test_silu_matches_tanh_form():
+    # sigmoid(v) = (1 + tanh(v / 2)) / 2: a second route through a library routine
+    v = np.random.default_rng(42).uniform(-30, 30, 4096)
+    want = v * (1.0 + np.tanh(v / 2.0)) / 2.0
+    got = oracle.silu_mul(v, np.ones_like(v))
+    # at large negative v, 1 + tanh(v / 2) cancels: that form is good to
+    # about eps * |v| there, absolutely
+    assert np.all(np.abs(got - want) <= 1e-14 * np.abs(want) + 1e-15 * np.abs(v))
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_silu_mul_pairs_column_n_with_n_plus_half(bits):
+    # gate columns 0..7, up columns 8..15; exact sums from the definition
+    c = synth.make_inputs(bits, 2, 64, 16, 32, seed=(43, bits))
+    exact = _exact_y(c)
+    got = oracle.awq_linear_silu_mul(c)
+    assert got.shape == (2, 8)
+    for m in range(2):
+        for n in range(8):
+            g, u = float(exact[m][n]), float(exact[m][n + 8])
+            want = g * (1.0 + np.tanh(g / 2.0)) / 2.0 * u
+            assert abs(got[m, n] - want) <= 1e-13 * max(abs(want), 1e-30)
+    # sampled rows and columns agree with the full result
+    sub = oracle.awq_linear_silu_mul(c, cols=np.array([7, 0, 3]), rows=np.array([1]))
+    assert np.array_equal(sub, got[[1]][:, [7, 0, 3]])
