@@ -68,7 +68,7 @@ def parse():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--replicas", type=int, default=0, help="weight replicas to rotate (0: enough to beat the cache)")
-    p.add_argument("--only", choices=["all", "gemv", "gemm", "copy", "configs", "crossover", "energy"],
+    p.add_argument("--only", choices=["all", "gemv", "gemm", "copy", "configs", "crossover", "energy", "silu"],
                    default="all",
                    help="restrict the run (profiling passes); 'copy' runs the plain-copy calibration kernel")
     p.add_argument("--counters-from", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
@@ -624,6 +624,48 @@ def bench_crossover(torch, q, args):
     return out
 
 
+def bench_silu(torch, q, args):
+    """The decoder layer's fused gate/up projection (W4, K = 4096, N = 2 x
+    14336, group 128) followed by silu(gate) * up, at M = 1 ... 16: the GEMV
+    then torch's silu and multiply (three launches) against the GEMV with the
+    product in its epilogue (one launch), queued back to back over weight
+    replicas larger than twice the Infinity Cache; microseconds per call."""
+    import synth
+
+    lins = stage_layer(torch, q, synth, M=1)
+    gu = [f for f in fuse_layer(torch, q, lins) if f["name"] == "gate_up"][0]
+    del lins
+    K, N, G = gu["K"], gu["N"], gu["G"]
+    n2 = N // 2
+    R = max(2, -(-2 * INFINITY_CACHE_BYTES // gu["packed"].numel()) + 1)
+    reps = [gu["packed"]] + [gu["packed"].clone() for _ in range(R - 1)]
+    F = torch.nn.functional
+    out = []
+    for M in (1, 4, 8, 16):
+        x = torch.randn((M, K), device="cuda:0").to(torch.bfloat16)
+        yg = torch.empty((M, N), dtype=torch.bfloat16, device="cuda:0")
+        o = torch.empty((M, n2), dtype=torch.bfloat16, device="cuda:0")
+
+        def unfused(i):
+            q.tf_gemv_w4a16(x, reps[i % R], K, N, G, y=yg)
+            torch.mul(F.silu(yg[:, :n2]), yg[:, n2:], out=o)
+
+        def fused(i):
+            q.tf_gemv_w4a16_silu_mul(x, reps[i % R], K, N, G, y=o)
+
+        row = dict(M=M)
+        for name, step in (("gemv_then_torch_silu_mul", unfused), ("fused_epilogue", fused)):
+            step(0)
+            ms = time_queued(torch, step, 60, enqueue_us=host_us_per_step(step, R))
+            row[name] = dict(us=round(ms * 1e3, 2),
+                             gbs=round(algorithmic_bytes(4, M, K, N, G) / (ms * 1e-3) / 1e9, 1))
+        out.append(row)
+        del x, yg, o
+    del reps, gu
+    torch.cuda.empty_cache()
+    return out
+
+
 def bench_energy(torch, q, args, seconds=2.0):
     """Energy per call from the GPU's energy accumulator (amdsmi), read around
     about `seconds` of back-to-back calls: the decoder layer's GEMV pass at
@@ -759,6 +801,8 @@ def main():
         line["crossover"] = bench_crossover(torch, q, args)
     if args.only == "energy":
         line["energy"] = bench_energy(torch, q, args)
+    if args.only == "silu":
+        line["silu_mul"] = bench_silu(torch, q, args)
     if args.only == "all" and not args.no_cpu:
         import oracle
         import synth

@@ -140,6 +140,25 @@ int tf_gemv_w8a16(const uint16_t *x, const void *packed, size_t packed_bytes, ui
                   int64_t M, int64_t K, int64_t N, int64_t G,
                   void *workspace, size_t ws_bytes, void *stream);
 
+/* Token-generation GEMV over a fused [gate | up] layer with the SiLU product
+ * in its epilogue, so that a decode step needs no separate activation
+ * launch (the summary's Results section finds token generation dominated by
+ * per-kernel dispatch overhead, and Methodology section 4 amortises it).
+ * SiLU itself is not on the pages: silu(v) = v / (1 + e^-v), the activation
+ * of the Llama-style MLP whose gate and up projections this fuses.
+ *   packed  the layer repacked with N = 2 N' columns: gate in columns
+ *           0 .. N'-1, up in N' .. N-1.  N % 32 == 0, so each half is whole
+ *           16-column blocks.
+ *   y       bf16 [M][N']: y[m][n] = silu(g) * u, where g and u are the fp32
+ *           sums of columns n and N' + n, rounded once to bf16 (nearest-even).
+ *           Neither sum is rounded to bf16 first.
+ * 0 <= M <= 16 (M == 0 does nothing), K < 2^25; no workspace.  Other
+ * arguments and errors as tf_gemv_*; N % 32 != 0 is TF_ERR_SHAPE. */
+int tf_gemv_w4a16_silu_mul(const uint16_t *x, const void *packed, size_t packed_bytes, uint16_t *y,
+                           int64_t M, int64_t K, int64_t N, int64_t G, void *stream);
+int tf_gemv_w8a16_silu_mul(const uint16_t *x, const void *packed, size_t packed_bytes, uint16_t *y,
+                           int64_t M, int64_t K, int64_t N, int64_t G, void *stream);
+
 /* Prefill GEMM, any M >= 1 (Methodology section 1): each weight tile is
  * unpacked once into LDS as the exact bf16 values q - z and reused by every
  * row of a 256-row tile; each group's scale is applied once per (group,

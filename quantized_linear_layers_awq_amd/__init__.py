@@ -23,7 +23,9 @@ from ._binding import (  # noqa: F401
     tf_gemm_w4a16,
     tf_gemm_w8a16,
     tf_gemv_w4a16,
+    tf_gemv_w4a16_silu_mul,
     tf_gemv_w8a16,
+    tf_gemv_w8a16_silu_mul,
     tf_packed_bytes_w4,
     tf_packed_bytes_w8,
     tf_probe_mfma,

@@ -63,6 +63,9 @@ def load_library():
         for n in ("tf_gemv_w4a16", "tf_gemv_w8a16", "tf_gemm_w4a16", "tf_gemm_w8a16"):
             getattr(L, n).argtypes = [P, P, SZ, P, I64, I64, I64, I64, P, SZ, P]
             getattr(L, n).restype = I
+        for n in ("tf_gemv_w4a16_silu_mul", "tf_gemv_w8a16_silu_mul"):
+            getattr(L, n).argtypes = [P, P, SZ, P, I64, I64, I64, I64, P]
+            getattr(L, n).restype = I
         for n in ("tf_dequant_w4_f32", "tf_dequant_w8_f32"):
             getattr(L, n).argtypes = [P, SZ, P, I64, I64, I64, P]
             getattr(L, n).restype = I
@@ -209,6 +212,32 @@ def tf_gemm_w4a16(x, packed, K, N, G, y=None, workspace=None, stream=None):
 
 def tf_gemm_w8a16(x, packed, K, N, G, y=None, workspace=None, stream=None):
     return _linear(8, True, "tf_gemm_w8a16", x, packed, K, N, G, y, workspace, stream)
+
+
+def _silu_mul(fn, x, packed, K, N, G, y, stream):
+    L = load_library()
+    _need(x, "x", 2)
+    _need(packed, "packed", 1)
+    if x.dim() != 2 or x.shape[1] != K:
+        raise ValueError(f"{fn}: x must be [M][K] with K={K}")
+    M = x.shape[0]
+    if y is None:
+        y = torch.empty((M, N // 2), dtype=torch.bfloat16, device=x.device)
+    _need(y, "y", 2)
+    if y.numel() < M * (N // 2):
+        raise ValueError(f"{fn}: y holds fewer than M*N/2 elements")
+    _check(getattr(L, fn)(_ptr(x), _ptr(packed), packed.numel(), _ptr(y), M, K, N, G, _stream(x, stream)), fn)
+    return y
+
+
+def tf_gemv_w4a16_silu_mul(x, packed, K, N, G, y=None, stream=None):
+    """y[M][N/2] = silu(x Wg) * (x Wu) (bf16) for a W4 [gate | up] layer of N
+    columns, x [M][K] bf16, 1 <= M <= 16."""
+    return _silu_mul("tf_gemv_w4a16_silu_mul", x, packed, K, N, G, y, stream)
+
+
+def tf_gemv_w8a16_silu_mul(x, packed, K, N, G, y=None, stream=None):
+    return _silu_mul("tf_gemv_w8a16_silu_mul", x, packed, K, N, G, y, stream)
 
 
 def _dequant(fn, packed, K, N, G, w, stream):

@@ -106,6 +106,31 @@ int linear(int bits, bool is_gemm, const uint16_t *x, const void *packed, size_t
     return e == hipSuccess ? TF_OK : TF_ERR_HIP;
 }
 
+// [gate | up] GEMV with the SiLU product (the kernel for up to 16 rows only).
+int linear_silu_mul(int bits, const uint16_t *x, const void *packed, size_t nbytes, uint16_t *y, int64_t M, int64_t K,
+                    int64_t N, int64_t G, void *stream)
+{
+    if (M < 0 || M > 16)
+        return TF_ERR_SHAPE;
+    if (int st = check_kng(bits, K, N, G))
+        return st;
+    // both halves whole 16-column blocks; 32-bit code-tile offsets as in linear()
+    if (N % (2 * tf::kBlockCols) || K >= (int64_t(1) << 25))
+        return TF_ERR_SHAPE;
+    if (M == 0)
+        return TF_OK;
+    if (!x || !packed || !y)
+        return TF_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(packed, 16) || !aligned(y, 2))
+        return TF_ERR_ALIGN;
+    const Layout lay = Layout::make(bits, K, N, G);
+    if (nbytes < (size_t)lay.total_bytes())
+        return TF_ERR_BUFFER_TOO_SMALL;
+    return tf::launch_gemv_silu_mul(bits, x, packed, y, M, lay, static_cast<hipStream_t>(stream)) == hipSuccess
+               ? TF_OK
+               : TF_ERR_HIP;
+}
+
 int dequant(int bits, const void *packed, size_t nbytes, float *w, int64_t K, int64_t N, int64_t G, void *stream)
 {
     if (!packed || !w)
@@ -187,6 +212,18 @@ int tf_gemm_w8a16(const uint16_t *x, const void *packed, size_t nbytes, uint16_t
                   int64_t G, void *ws, size_t ws_bytes, void *stream)
 {
     return linear(8, true, x, packed, nbytes, y, M, K, N, G, ws, ws_bytes, stream);
+}
+
+int tf_gemv_w4a16_silu_mul(const uint16_t *x, const void *packed, size_t nbytes, uint16_t *y, int64_t M, int64_t K,
+                           int64_t N, int64_t G, void *stream)
+{
+    return linear_silu_mul(4, x, packed, nbytes, y, M, K, N, G, stream);
+}
+
+int tf_gemv_w8a16_silu_mul(const uint16_t *x, const void *packed, size_t nbytes, uint16_t *y, int64_t M, int64_t K,
+                           int64_t N, int64_t G, void *stream)
+{
+    return linear_silu_mul(8, x, packed, nbytes, y, M, K, N, G, stream);
 }
 
 int tf_dequant_w4_f32(const void *packed, size_t nbytes, float *w, int64_t K, int64_t N, int64_t G, void *stream)

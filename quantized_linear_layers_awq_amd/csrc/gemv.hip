@@ -36,6 +36,10 @@ constexpr int kGemvTargetWaves = 4096; // about 16 per CU
 constexpr int kGemvMinSplitTiles = 2;
 constexpr int kGemvMaxSplits = 16;
 
+// SiLU, x * sigmoid(x) = x / (1 + e^-x); at large negative x the
+// exponential overflows to +inf and the quotient is -0, the limit.
+__device__ __forceinline__ float silu(float v) { return v / (1.f + expf(-v)); }
+
 // Eight W4 codes (one column, rows 0..7 of an octet) -> B operand of bf16
 // values 128 + q: OR-ing a nibble into the mantissa of bf16 128.0 (0x4300).
 // `magic` is 0x43004300 held in a vector register, so each pair costs one
@@ -136,7 +140,12 @@ enum GroupMode {
 // vector-memory counters retire in order, so waiting for tile t never waits
 // for anything issued after it.  Each ring slot is unpacked into MFMA operands before it is
 // refilled, so the slot keeps its registers and no wait drains the ring.
-template <int BITS, int kMode, int D, int BPW>
+//
+// ACT = kActSiluMul: the layer is [gate | up] along N (N = 2 N', both halves
+// whole 16-column blocks).  A workgroup owns P = BPW / 2 consecutive gate
+// blocks and the up blocks N' / 16 further on, and writes
+// y[m][n] = silu(g) * u (n < N') from the fp32 sums, rounded once.
+template <int BITS, int kMode, int D, int BPW, int ACT = kActNone>
 __global__ __launch_bounds__(1024) void gemv_kernel(const uint16_t *__restrict__ x, const uint8_t *__restrict__ packed,
                                                     uint16_t *__restrict__ y, Layout lay, int M, GemvChunks ch)
 {
@@ -154,7 +163,16 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const uint16_t *__restrict__
     const int ws = wave - bi * Wb;                        // and its share of K
     const int r = lane & 15, o = lane >> 4;
     const int64_t blk0 = (int64_t)blockIdx.x * BPW;       // first block of the workgroup
-    const int64_t blk = blk0 + bi;
+    static_assert(ACT == kActNone || BPW % 2 == 0, "gate and up blocks come in pairs");
+    constexpr int P = BPW / 2;                            // gate blocks of a workgroup (ACT)
+    // block of the workgroup's eb-th slot
+    auto block_of = [&](int eb) -> int64_t {
+        if constexpr (ACT == kActNone)
+            return blk0 + eb;
+        const int64_t j = (int64_t)blockIdx.x * P + (eb < P ? eb : eb - P);
+        return eb < P ? j : (lay.nblocks >> 1) + j;
+    };
+    const int64_t blk = block_of(bi);
     const bool blk_ok = blk < lay.nblocks;                // a last workgroup may be partial
     const uint8_t *meta = packed + (blk_ok ? blk : 0) * lay.block_bytes;
     const uint8_t *tiles = meta + lay.meta_bytes + 16 * lane;
@@ -206,8 +224,8 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const uint16_t *__restrict__
 #pragma unroll
         for (int eb = 0; eb < BPW; ++eb) {
             mv[eb] = u32x2{0u, 0u};
-            if (tid < rec_words && blk0 + eb < lay.nblocks)
-                mv[eb] = *reinterpret_cast<const u32x2 *>(packed + (blk0 + eb) * lay.block_bytes + g0 * RB + 8 * tid);
+            if (tid < rec_words && block_of(eb) < lay.nblocks)
+                mv[eb] = *reinterpret_cast<const u32x2 *>(packed + block_of(eb) * lay.block_bytes + g0 * RB + 8 * tid);
         }
         // ---- then the codes.  Ring loads past the wave's range re-read its
         //      last tile (in bounds, never used). ----
@@ -237,10 +255,10 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const uint16_t *__restrict__
         }
 #pragma unroll
         for (int eb = 0; eb < BPW; ++eb) {
-            if (blk0 + eb < lay.nblocks) {
+            if (block_of(eb) < lay.nblocks) {
                 if (tid < rec_words)
                     *reinterpret_cast<u32x2 *>(smem + eb * ch.meta_cap + 8 * tid) = mv[eb];
-                const uint8_t *src = packed + (blk0 + eb) * lay.block_bytes + g0 * RB;
+                const uint8_t *src = packed + block_of(eb) * lay.block_bytes + g0 * RB;
                 for (int e = tid + (int)blockDim.x; e < rec_words; e += blockDim.x) // more than one per thread
                     *reinterpret_cast<u32x2 *>(smem + eb * ch.meta_cap + 8 * e) =
                         *reinterpret_cast<const u32x2 *>(src + 8 * e);
@@ -330,16 +348,32 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const uint16_t *__restrict__
         red[(wave * 16 + 4 * o + e) * kBlockCols + r] = yacc[e];
     __syncthreads();
     // each block sums its own waves, in wave order
+    auto block_sum = [&](int eb, int row, int col) {
+        float v = 0.f;
+        for (int w = eb * Wb; w < (eb + 1) * Wb; ++w)
+            v += red[(w * 16 + row) * kBlockCols + col];
+        return v;
+    };
+    if constexpr (ACT == kActNone) {
 #pragma unroll
-    for (int eb = 0; eb < BPW; ++eb) {
-        for (int e = tid; e < M * kBlockCols; e += blockDim.x) {
-            const int row = e >> 4, col = e & 15;
-            float v = 0.f;
-            for (int w = eb * Wb; w < (eb + 1) * Wb; ++w)
-                v += red[(w * 16 + row) * kBlockCols + col];
-            const int64_t nn = (blk0 + eb) * kBlockCols + col;
-            if (nn < lay.N)
-                y[(int64_t)row * lay.N + nn] = f32_to_bf16_bits(v);
+        for (int eb = 0; eb < BPW; ++eb) {
+            for (int e = tid; e < M * kBlockCols; e += blockDim.x) {
+                const int row = e >> 4, col = e & 15;
+                const float v = block_sum(eb, row, col);
+                const int64_t nn = (blk0 + eb) * kBlockCols + col;
+                if (nn < lay.N)
+                    y[(int64_t)row * lay.N + nn] = f32_to_bf16_bits(v);
+            }
+        }
+    } else {
+        const int64_t n2 = lay.N >> 1;
+        for (int eb = 0; eb < P; ++eb) {
+            for (int e = tid; e < M * kBlockCols; e += blockDim.x) {
+                const int row = e >> 4, col = e & 15;
+                const float g = block_sum(eb, row, col), u = block_sum(eb + P, row, col);
+                const int64_t nn = block_of(eb) * kBlockCols + col;
+                y[(int64_t)row * n2 + nn] = f32_to_bf16_bits(silu(g) * u);
+            }
         }
     }
 }
@@ -645,9 +679,8 @@ static int gemv_bpw(const Layout &lay, int64_t M)
     return b >= 4 ? 4 : b >= 2 ? 2 : 1;
 }
 
-int gemv_waves(const Layout &lay, int64_t M)
+static int gemv_waves_bpw(const Layout &lay, int bpw)
 {
-    const int bpw = gemv_bpw(lay, M);
     const int64_t wgs = (lay.nblocks + bpw - 1) / bpw;
     int64_t wb = ((kGemvTargetWaves + wgs - 1) / wgs + bpw - 1) / bpw; // waves per block
     if (wb * bpw > kGemvMaxWaves)
@@ -656,6 +689,8 @@ int gemv_waves(const Layout &lay, int64_t M)
         wb = lay.ktiles;
     return (int)(wb < 1 ? 1 : wb) * bpw;
 }
+
+int gemv_waves(const Layout &lay, int64_t M) { return gemv_waves_bpw(lay, gemv_bpw(lay, M)); }
 
 // Chunk size: as many k-tiles as fit the LDS share of one workgroup when
 // 16 / W workgroups run per CU (at most kGemvMaxLds).
@@ -689,53 +724,53 @@ static GemvChunks plan_chunks(int bits, const Layout &lay, int64_t M, int W, int
 
 // Dynamic LDS above the default 64 KiB needs the limit raised, once per
 // instantiation.
-template <int BITS, int kMode, int D, int BPW>
+template <int BITS, int kMode, int D, int BPW, int ACT>
 static void launch_gemv_mode(const Layout &lay, dim3 grid, dim3 block, const GemvChunks &ch, hipStream_t stream,
                              const uint16_t *x, const uint8_t *pk, uint16_t *y, int M)
 {
-    auto kern = &gemv_kernel<BITS, kMode, D, BPW>;
+    auto kern = &gemv_kernel<BITS, kMode, D, BPW, ACT>;
     static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, kGemvMaxLds);
     (void)attr;
     kern<<<grid, block, ch.lds, stream>>>(x, pk, y, lay, M, ch);
 }
 
-template <int BITS, int D, int BPW>
+template <int BITS, int D, int BPW, int ACT>
 static void launch_gemv_bpw(const Layout &lay, dim3 grid, dim3 block, const GemvChunks &ch, hipStream_t stream,
                             const uint16_t *x, const uint8_t *pk, uint16_t *y, int M)
 {
     if (lay.tiles_per_group == 1)
-        launch_gemv_mode<BITS, kOneTile, D, BPW>(lay, grid, block, ch, stream, x, pk, y, M);
+        launch_gemv_mode<BITS, kOneTile, D, BPW, ACT>(lay, grid, block, ch, stream, x, pk, y, M);
     else if (lay.whole_tiles())
-        launch_gemv_mode<BITS, kMultiTile, D, BPW>(lay, grid, block, ch, stream, x, pk, y, M);
+        launch_gemv_mode<BITS, kMultiTile, D, BPW, ACT>(lay, grid, block, ch, stream, x, pk, y, M);
     else
-        launch_gemv_mode<BITS, kSplitTiles, D, BPW>(lay, grid, block, ch, stream, x, pk, y, M);
+        launch_gemv_mode<BITS, kSplitTiles, D, BPW, ACT>(lay, grid, block, ch, stream, x, pk, y, M);
 }
 
-template <int BITS, int D>
+template <int BITS, int D, int ACT>
 static void launch_gemv_depth(const Layout &lay, dim3 grid, dim3 block, const GemvChunks &ch, hipStream_t stream,
                               const uint16_t *x, const uint8_t *pk, uint16_t *y, int M)
 {
     if (ch.bpw == 4)
-        launch_gemv_bpw<BITS, D, 4>(lay, grid, block, ch, stream, x, pk, y, M);
+        launch_gemv_bpw<BITS, D, 4, ACT>(lay, grid, block, ch, stream, x, pk, y, M);
     else if (ch.bpw == 2)
-        launch_gemv_bpw<BITS, D, 2>(lay, grid, block, ch, stream, x, pk, y, M);
-    else
-        launch_gemv_bpw<BITS, D, 1>(lay, grid, block, ch, stream, x, pk, y, M);
+        launch_gemv_bpw<BITS, D, 2, ACT>(lay, grid, block, ch, stream, x, pk, y, M);
+    else if constexpr (ACT == kActNone) // pairs of gate and up blocks need an even count
+        launch_gemv_bpw<BITS, D, 1, ACT>(lay, grid, block, ch, stream, x, pk, y, M);
 }
 
 // Prefetch depth: measured on MI355X, two k-tiles in flight per wave suit
 // short per-wave ranges (at most 3 tiles), four the longer ones; deeper rings
 // only add redundant loads and registers.
-template <int BITS>
+template <int BITS, int ACT = kActNone>
 static void launch_gemv_bits(const Layout &lay, dim3 grid, dim3 block, const GemvChunks &ch, hipStream_t stream,
                              const uint16_t *x, const uint8_t *pk, uint16_t *y, int M)
 {
     const int64_t per_wave = lay.ktiles / (block.x / 64 / ch.bpw);
     if (per_wave <= 3)
-        launch_gemv_depth<BITS, 2>(lay, grid, block, ch, stream, x, pk, y, M);
+        launch_gemv_depth<BITS, 2, ACT>(lay, grid, block, ch, stream, x, pk, y, M);
     else
-        launch_gemv_depth<BITS, 4>(lay, grid, block, ch, stream, x, pk, y, M);
+        launch_gemv_depth<BITS, 4, ACT>(lay, grid, block, ch, stream, x, pk, y, M);
 }
 
 // ---- launch of the 16-row-chunk GEMV ----
@@ -909,6 +944,29 @@ hipError_t launch_gemv(int bits, const uint16_t *x, const void *packed, uint16_t
         launch_gemv_bits<4>(lay, grid, block, ch, stream, x, pk, y, (int)M);
     else
         launch_gemv_bits<8>(lay, grid, block, ch, stream, x, pk, y, (int)M);
+    return hipGetLastError();
+}
+
+// The fused gate/up GEMV with the SiLU product: the kernel for up to 16 rows
+// with gate block j and up block N/32 + j in one workgroup (two or four
+// blocks per workgroup, so one or two pairs).
+hipError_t launch_gemv_silu_mul(int bits, const uint16_t *x, const void *packed, uint16_t *y, int64_t M,
+                                const Layout &lay, hipStream_t stream)
+{
+    const int64_t half = lay.nblocks / 2;
+    if (lay.nblocks % 2 || M < 1 || M > 16)
+        return hipErrorInvalidValue;
+    int bpw = gemv_bpw(lay, M) < 2 ? 2 : gemv_bpw(lay, M);
+    if ((half * 2) % bpw)
+        bpw = 2;
+    const int W = gemv_waves_bpw(lay, bpw);
+    const GemvChunks ch = plan_chunks(bits, lay, M, W, bpw);
+    const dim3 grid((unsigned)(half / (bpw / 2))), block(64 * W);
+    const uint8_t *pk = static_cast<const uint8_t *>(packed);
+    if (bits == 4)
+        launch_gemv_bits<4, kActSiluMul>(lay, grid, block, ch, stream, x, pk, y, (int)M);
+    else
+        launch_gemv_bits<8, kActSiluMul>(lay, grid, block, ch, stream, x, pk, y, (int)M);
     return hipGetLastError();
 }
 

@@ -23,6 +23,13 @@ int64_t gemv_workspace_bytes(const Layout &lay, int64_t M, int cus);
 constexpr int64_t kGemvKernelMaxM = 64;
 hipError_t launch_gemv(int bits, const uint16_t *x, const void *packed, uint16_t *y, int64_t M, const Layout &lay,
                        void *workspace, hipStream_t stream);
+// Epilogue of the GEMV kernel: none, or silu(gate) * up over a [gate | up]
+// layer (launch_gemv_silu_mul).
+constexpr int kActNone = 0, kActSiluMul = 1;
+// y[m][n] = silu(g) * u with g, u the fp32 sums of columns n and N/2 + n of a
+// [gate | up] layer (N % 32 == 0), 1 <= M <= 16; y is [M][N/2].  No workspace.
+hipError_t launch_gemv_silu_mul(int bits, const uint16_t *x, const void *packed, uint16_t *y, int64_t M,
+                                const Layout &lay, hipStream_t stream);
 // y = bf16(sum of the splits' fp32 partials ws[s][mn]), added in split order;
 // 2 <= splits <= 16 (both plans stay within that).
 void launch_splitk_sum(const float *ws, int splits, int64_t mn, uint16_t *y, hipStream_t stream);

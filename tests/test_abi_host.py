@@ -322,6 +322,25 @@ class TestValidation:
         assert self._gemv(lib, M=0, x=None, y=None, packed=None) == TF_OK
         assert self._gemv(lib, M=0, x=None, y=None, packed=None, fn="tf_gemm_w8a16") == TF_OK
 
+    def _silu(self, lib, M=1, K=256, N=128, G=128, x=FAKE, packed=FAKE, y=FAKE, nbytes=1 << 30,
+              fn="tf_gemv_w4a16_silu_mul"):
+        return getattr(lib, fn)(x, packed, nbytes, y, M, K, N, G, None)
+
+    def test_silu_mul_validation(self, lib):
+        assert self._silu(lib, N=112) == TF_ERR_SHAPE          # halves of 56 columns: not whole blocks
+        assert self._silu(lib, N=100, fn="tf_gemv_w8a16_silu_mul") == TF_ERR_SHAPE
+        assert self._silu(lib, M=17) == TF_ERR_SHAPE
+        assert self._silu(lib, M=-1) == TF_ERR_SHAPE
+        assert self._silu(lib, K=1 << 25, G=1 << 25) == TF_ERR_SHAPE
+        assert self._silu(lib, G=48) == TF_ERR_GROUP
+        assert self._silu(lib, x=None) == TF_ERR_NULL
+        assert self._silu(lib, packed=None) == TF_ERR_NULL
+        assert self._silu(lib, y=FAKE + 1) == TF_ERR_ALIGN
+        assert self._silu(lib, x=FAKE + 8) == TF_ERR_ALIGN
+        need = lib.tf_packed_bytes_w4(256, 128, 128)
+        assert self._silu(lib, nbytes=need - 1) == TF_ERR_BUFFER_TOO_SMALL
+        assert self._silu(lib, M=0, x=None, y=None, packed=None) == TF_OK
+
     def test_repack_validation(self, lib):
         f = lib.tf_repack_w4
         assert f(FAKE, FAKE, FAKE, 256, 128, 128, FAKE, 10, None) == TF_ERR_BUFFER_TOO_SMALL
