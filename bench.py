@@ -630,15 +630,26 @@ def bench_silu(torch, q, args):
     then torch's silu and multiply (three launches) against the GEMV with the
     product in its epilogue (one launch), queued back to back over weight
     replicas larger than twice the Infinity Cache; microseconds per call."""
+    import numpy as np
+
     import synth
 
-    lins = stage_layer(torch, q, synth, M=1)
-    gu = [f for f in fuse_layer(torch, q, lins) if f["name"] == "gate_up"][0]
-    del lins
-    K, N, G = gu["K"], gu["N"], gu["G"]
+    # the layer's gate and up checkpoints side by side, packed both ways: plain
+    # (for the GEMV) and with the halves interleaved (for the fused call)
+    cs = [synth.make_case(1, sid, 1, keep_codes=False) for sid in (4, 5)]
+    assert [c.name.split("_")[2] for c in cs] == ["gate", "up"]
+    K, G, N = cs[0].K, cs[0].G, cs[0].N + cs[1].N
     n2 = N // 2
-    R = max(2, -(-2 * INFINITY_CACHE_BYTES // gu["packed"].numel()) + 1)
-    reps = [gu["packed"]] + [gu["packed"].clone() for _ in range(R - 1)]
+    dev = "cuda:0"
+    qw = torch.from_numpy(np.concatenate([c.qweight for c in cs], axis=1).view(np.int32)).to(dev)
+    qz = torch.from_numpy(np.concatenate([c.qzeros for c in cs], axis=1).view(np.int32)).to(dev)
+    sc = torch.from_numpy(np.concatenate([c.scales for c in cs], axis=1).view(np.int16)).to(dev)
+    plain = q.tf_repack_w4(qw, qz, sc, K, N, G)
+    paired = q.tf_repack_w4_gate_up(qw, qz, sc, K, N, G)
+    del qw, qz, sc, cs
+    R = max(2, -(-2 * INFINITY_CACHE_BYTES // plain.numel()) + 1)
+    reps = [plain] + [plain.clone() for _ in range(R - 1)]
+    preps = [paired] + [paired.clone() for _ in range(R - 1)]
     F = torch.nn.functional
     out = []
     for M in (1, 4, 8, 16):
@@ -651,7 +662,7 @@ def bench_silu(torch, q, args):
             torch.mul(F.silu(yg[:, :n2]), yg[:, n2:], out=o)
 
         def fused(i):
-            q.tf_gemv_w4a16_silu_mul(x, reps[i % R], K, N, G, y=o)
+            q.tf_gemv_w4a16_silu_mul(x, preps[i % R], K, N, G, y=o)
 
         row = dict(M=M)
         for name, step in (("gemv_then_torch_silu_mul", unfused), ("fused_epilogue", fused)):
@@ -661,7 +672,7 @@ def bench_silu(torch, q, args):
                              gbs=round(algorithmic_bytes(4, M, K, N, G) / (ms * 1e-3) / 1e9, 1))
         out.append(row)
         del x, yg, o
-    del reps, gu
+    del reps, preps, plain, paired
     torch.cuda.empty_cache()
     return out
 

@@ -111,6 +111,17 @@ int tf_repack_w4(const uint32_t *qweight, const uint32_t *qzeros, const uint16_t
 int tf_repack_w8(const uint8_t *qweight, const uint8_t *zeros, const uint16_t *scales,
                  int64_t K, int64_t N, int64_t G, void *packed, size_t packed_bytes, void *stream);
 
+/* Re-lay out a fused [gate | up] checkpoint (N = 2 N' columns, gate first,
+ * N % 16 == 0) for tf_gemv_*_silu_mul: arguments, size and errors as
+ * tf_repack_w4 / _w8, but column c of 16-column block j holds gate column
+ * 8 j + c (c < 8) or up column 8 j + c - 8 (c >= 8), so that every block
+ * holds matching gate and up columns.  The result is the plain layout of the
+ * checkpoint with its columns so permuted; N % 16 != 0 is TF_ERR_SHAPE. */
+int tf_repack_w4_gate_up(const uint32_t *qweight, const uint32_t *qzeros, const uint16_t *scales,
+                         int64_t K, int64_t N, int64_t G, void *packed, size_t packed_bytes, void *stream);
+int tf_repack_w8_gate_up(const uint8_t *qweight, const uint8_t *zeros, const uint16_t *scales,
+                         int64_t K, int64_t N, int64_t G, void *packed, size_t packed_bytes, void *stream);
+
 /* ------------------------------------------------------------------------ */
 /* Fused linear layer.                                                       */
 /*   x          bf16 [M][K], 16-byte aligned                                 */
@@ -146,18 +157,23 @@ int tf_gemv_w8a16(const uint16_t *x, const void *packed, size_t packed_bytes, ui
  * per-kernel dispatch overhead, and Methodology section 4 amortises it).
  * SiLU itself is not on the pages: silu(v) = v / (1 + e^-v), the activation
  * of the Llama-style MLP whose gate and up projections this fuses.
- *   packed  the layer repacked with N = 2 N' columns: gate in columns
- *           0 .. N'-1, up in N' .. N-1.  N % 32 == 0, so each half is whole
- *           16-column blocks.
+ *   packed  written by tf_repack_w4_gate_up / _w8_gate_up for the layer of
+ *           N = 2 N' columns (gate in checkpoint columns 0 .. N'-1, up in
+ *           N' .. N-1), N % 16 == 0.
  *   y       bf16 [M][N']: y[m][n] = silu(g) * u, where g and u are the fp32
- *           sums of columns n and N' + n, rounded once to bf16 (nearest-even).
- *           Neither sum is rounded to bf16 first.
- * 0 <= M <= 16 (M == 0 does nothing), K < 2^25; no workspace.  Other
- * arguments and errors as tf_gemv_*; N % 32 != 0 is TF_ERR_SHAPE. */
+ *           sums of checkpoint columns n and N' + n, rounded once to bf16
+ *           (nearest-even).  Neither sum is rounded to bf16 first.
+ * 0 <= M <= 16 (M == 0 does nothing), K < 2^25.  The call runs the kernel
+ * tf_gemv_* runs for the same (M, K, N, G), so it needs the workspace that
+ * tf_workspace_bytes(bits, 0, M, K, N, G) reports (none below 8 rows).
+ * Other arguments and errors as tf_gemv_*; N % 16 != 0 is TF_ERR_SHAPE.  A
+ * buffer from plain tf_repack_* gives wrong results here (not detectable). */
 int tf_gemv_w4a16_silu_mul(const uint16_t *x, const void *packed, size_t packed_bytes, uint16_t *y,
-                           int64_t M, int64_t K, int64_t N, int64_t G, void *stream);
+                           int64_t M, int64_t K, int64_t N, int64_t G,
+                           void *workspace, size_t ws_bytes, void *stream);
 int tf_gemv_w8a16_silu_mul(const uint16_t *x, const void *packed, size_t packed_bytes, uint16_t *y,
-                           int64_t M, int64_t K, int64_t N, int64_t G, void *stream);
+                           int64_t M, int64_t K, int64_t N, int64_t G,
+                           void *workspace, size_t ws_bytes, void *stream);
 
 /* Prefill GEMM, any M >= 1 (Methodology section 1): each weight tile is
  * unpacked once into LDS as the exact bf16 values q - z and reused by every

@@ -193,6 +193,34 @@ def repack(bits, qweight, qzeros, scales, K, N, G) -> np.ndarray:
     return out
 
 
+def gate_up_order(N) -> np.ndarray:
+    """Checkpoint column of each packed column of a [gate | up] layer (N / 2
+    a multiple of 8) packed for the SiLU-product GEMV: in 16-column block j,
+    columns 0..7 take gate columns 8j..8j+7 and columns 8..15 take up columns
+    N/2 + 8j .. N/2 + 8j + 7."""
+    if N % 16:
+        raise ValueError("N / 2 must be a multiple of 8")
+    order = []
+    for j in range(N // 16):
+        order += [8 * j + c for c in range(8)]
+        order += [N // 2 + 8 * j + c for c in range(8)]
+    return np.array(order, dtype=np.int64)
+
+
+def repack_gate_up(bits, qweight, qzeros, scales, K, N, G) -> np.ndarray:
+    """Reference buffer for a [gate | up] checkpoint packed for the
+    SiLU-product GEMV: the plain layout of the checkpoint with its columns in
+    :func:`gate_up_order`.  W4 words hold runs of 8 columns, and the order
+    moves whole runs, so whole words move."""
+    order = gate_up_order(N)
+    if bits == 4:
+        words = order[::8] // 8
+        qw, qz = np.asarray(qweight)[:, words], np.asarray(qzeros)[:, words]
+    else:
+        qw, qz = np.asarray(qweight)[:, order], np.asarray(qzeros)[:, order]
+    return repack(bits, qw, qz, np.asarray(scales)[:, order], K, N, G)
+
+
 def unrepack(bits, packed, K, N, G):
     """Inverse of :func:`repack`: (codes [K][N], zeros [K/G][N], scale bits [K/G][N])."""
     packed = _c(packed, np.uint8)

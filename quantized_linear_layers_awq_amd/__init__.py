@@ -31,7 +31,9 @@ from ._binding import (  # noqa: F401
     tf_probe_mfma,
     tf_probe_stream_read,
     tf_repack_w4,
+    tf_repack_w4_gate_up,
     tf_repack_w8,
+    tf_repack_w8_gate_up,
     tf_status_string,
     tf_workspace_bytes,
 )

@@ -55,7 +55,7 @@ def load_library():
         for n in ("tf_packed_bytes_w4", "tf_packed_bytes_w8"):
             getattr(L, n).argtypes = [I64, I64, I64]
             getattr(L, n).restype = SZ
-        for n in ("tf_repack_w4", "tf_repack_w8"):
+        for n in ("tf_repack_w4", "tf_repack_w8", "tf_repack_w4_gate_up", "tf_repack_w8_gate_up"):
             getattr(L, n).argtypes = [P, P, P, I64, I64, I64, P, SZ, P]
             getattr(L, n).restype = I
         L.tf_workspace_bytes.argtypes = [I, I, I64, I64, I64, I64]
@@ -64,7 +64,7 @@ def load_library():
             getattr(L, n).argtypes = [P, P, SZ, P, I64, I64, I64, I64, P, SZ, P]
             getattr(L, n).restype = I
         for n in ("tf_gemv_w4a16_silu_mul", "tf_gemv_w8a16_silu_mul"):
-            getattr(L, n).argtypes = [P, P, SZ, P, I64, I64, I64, I64, P]
+            getattr(L, n).argtypes = [P, P, SZ, P, I64, I64, I64, I64, P, SZ, P]
             getattr(L, n).restype = I
         for n in ("tf_dequant_w4_f32", "tf_dequant_w8_f32"):
             getattr(L, n).argtypes = [P, SZ, P, I64, I64, I64, P]
@@ -153,6 +153,16 @@ def tf_repack_w4(qweight, qzeros, scales, K, N, G, packed=None, stream=None):
     return _repack(4, "tf_repack_w4", qweight, qzeros, scales, K, N, G, packed, stream)
 
 
+def tf_repack_w4_gate_up(qweight, qzeros, scales, K, N, G, packed=None, stream=None):
+    """AWQ W4 checkpoint of a [gate | up] layer (N columns, gate first) ->
+    packed uint8 for tf_gemv_w4a16_silu_mul."""
+    return _repack(4, "tf_repack_w4_gate_up", qweight, qzeros, scales, K, N, G, packed, stream)
+
+
+def tf_repack_w8_gate_up(qweight, zeros, scales, K, N, G, packed=None, stream=None):
+    return _repack(8, "tf_repack_w8_gate_up", qweight, zeros, scales, K, N, G, packed, stream)
+
+
 def tf_repack_w8(qweight, zeros, scales, K, N, G, packed=None, stream=None):
     """W8 checkpoint (uint8 [K][N], uint8 [K/G][N] or None for symmetric
     zero points of 128, bf16 [K/G][N]) -> packed uint8."""
@@ -214,7 +224,7 @@ def tf_gemm_w8a16(x, packed, K, N, G, y=None, workspace=None, stream=None):
     return _linear(8, True, "tf_gemm_w8a16", x, packed, K, N, G, y, workspace, stream)
 
 
-def _silu_mul(fn, x, packed, K, N, G, y, stream):
+def _silu_mul(bits, fn, x, packed, K, N, G, y, workspace, stream):
     L = load_library()
     _need(x, "x", 2)
     _need(packed, "packed", 1)
@@ -226,18 +236,23 @@ def _silu_mul(fn, x, packed, K, N, G, y, stream):
     _need(y, "y", 2)
     if y.numel() < M * (N // 2):
         raise ValueError(f"{fn}: y holds fewer than M*N/2 elements")
-    _check(getattr(L, fn)(_ptr(x), _ptr(packed), packed.numel(), _ptr(y), M, K, N, G, _stream(x, stream)), fn)
+    sh = _stream(x, stream)
+    need = int(L.tf_workspace_bytes(bits, 0, M, K, N, G))
+    if workspace is None:
+        workspace = _workspace(x.device, sh, need)
+    ws_ptr, ws_bytes = (None, 0) if workspace is None else (_ptr(workspace), workspace.numel() * workspace.element_size())
+    _check(getattr(L, fn)(_ptr(x), _ptr(packed), packed.numel(), _ptr(y), M, K, N, G, ws_ptr, ws_bytes, sh), fn)
     return y
 
 
-def tf_gemv_w4a16_silu_mul(x, packed, K, N, G, y=None, stream=None):
+def tf_gemv_w4a16_silu_mul(x, packed, K, N, G, y=None, workspace=None, stream=None):
     """y[M][N/2] = silu(x Wg) * (x Wu) (bf16) for a W4 [gate | up] layer of N
-    columns, x [M][K] bf16, 1 <= M <= 16."""
-    return _silu_mul("tf_gemv_w4a16_silu_mul", x, packed, K, N, G, y, stream)
+    columns packed by tf_repack_w4_gate_up, x [M][K] bf16, 1 <= M <= 16."""
+    return _silu_mul(4, "tf_gemv_w4a16_silu_mul", x, packed, K, N, G, y, workspace, stream)
 
 
-def tf_gemv_w8a16_silu_mul(x, packed, K, N, G, y=None, stream=None):
-    return _silu_mul("tf_gemv_w8a16_silu_mul", x, packed, K, N, G, y, stream)
+def tf_gemv_w8a16_silu_mul(x, packed, K, N, G, y=None, workspace=None, stream=None):
+    return _silu_mul(8, "tf_gemv_w8a16_silu_mul", x, packed, K, N, G, y, workspace, stream)
 
 
 def _dequant(fn, packed, K, N, G, w, stream):

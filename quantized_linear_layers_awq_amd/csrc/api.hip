@@ -35,19 +35,24 @@ size_t packed_bytes(int bits, int64_t K, int64_t N, int64_t G)
     return (size_t)Layout::make(bits, K, N, G).total_bytes();
 }
 
+// gate_up: a [gate | up] checkpoint (N / 2 a multiple of 8), packed for the
+// SiLU-product GEMV with the two halves interleaved in runs of 8 columns.
 int repack(int bits, const void *qweight, const void *qzeros, const uint16_t *scales, int64_t K, int64_t N, int64_t G,
-           void *packed, size_t nbytes, void *stream)
+           void *packed, size_t nbytes, void *stream, bool gate_up = false)
 {
     if (!qweight || !scales || !packed) // qzeros may be NULL: symmetric quantization
         return TF_ERR_NULL;
     if (int st = check_kng(bits, K, N, G))
         return st;
+    if (gate_up && N % (2 * 8))
+        return TF_ERR_SHAPE;
     if (!aligned(packed, 16) || !aligned(scales, 2) || (bits == 4 && (!aligned(qweight, 4) || !aligned(qzeros, 4))))
         return TF_ERR_ALIGN;
     const Layout lay = Layout::make(bits, K, N, G);
     if (nbytes < (size_t)lay.total_bytes())
         return TF_ERR_BUFFER_TOO_SMALL;
-    if (tf::launch_repack(bits, qweight, qzeros, scales, lay, packed, static_cast<hipStream_t>(stream)) != hipSuccess)
+    if (tf::launch_repack(bits, qweight, qzeros, scales, lay, packed, static_cast<hipStream_t>(stream),
+                          gate_up ? N / 2 : 0) != hipSuccess)
         return TF_ERR_HIP;
     return TF_OK;
 }
@@ -106,16 +111,17 @@ int linear(int bits, bool is_gemm, const uint16_t *x, const void *packed, size_t
     return e == hipSuccess ? TF_OK : TF_ERR_HIP;
 }
 
-// [gate | up] GEMV with the SiLU product (the kernel for up to 16 rows only).
+// [gate | up] GEMV with the SiLU product over a buffer from repack(gate_up)
+// (the kernel for up to 16 rows only).
 int linear_silu_mul(int bits, const uint16_t *x, const void *packed, size_t nbytes, uint16_t *y, int64_t M, int64_t K,
-                    int64_t N, int64_t G, void *stream)
+                    int64_t N, int64_t G, void *ws, size_t ws_bytes, void *stream)
 {
     if (M < 0 || M > 16)
         return TF_ERR_SHAPE;
     if (int st = check_kng(bits, K, N, G))
         return st;
-    // both halves whole 16-column blocks; 32-bit code-tile offsets as in linear()
-    if (N % (2 * tf::kBlockCols) || K >= (int64_t(1) << 25))
+    // halves of whole 8-column runs; 32-bit code-tile offsets as in linear()
+    if (N % (2 * 8) || K >= (int64_t(1) << 25))
         return TF_ERR_SHAPE;
     if (M == 0)
         return TF_OK;
@@ -126,7 +132,17 @@ int linear_silu_mul(int bits, const uint16_t *x, const void *packed, size_t nbyt
     const Layout lay = Layout::make(bits, K, N, G);
     if (nbytes < (size_t)lay.total_bytes())
         return TF_ERR_BUFFER_TOO_SMALL;
-    return tf::launch_gemv_silu_mul(bits, x, packed, y, M, lay, static_cast<hipStream_t>(stream)) == hipSuccess
+    // the kernel and its K split are the plain GEMV's for this shape
+    const size_t need = workspace_bytes(bits, 0, M, K, N, G);
+    if (need) {
+        if (!ws)
+            return TF_ERR_NULL;
+        if (!aligned(ws, 256))
+            return TF_ERR_ALIGN;
+        if (ws_bytes < need)
+            return TF_ERR_BUFFER_TOO_SMALL;
+    }
+    return tf::launch_gemv_silu_mul(bits, x, packed, y, M, lay, ws, static_cast<hipStream_t>(stream)) == hipSuccess
                ? TF_OK
                : TF_ERR_HIP;
 }
@@ -183,6 +199,18 @@ int tf_repack_w8(const uint8_t *qweight, const uint8_t *zeros, const uint16_t *s
     return repack(8, qweight, zeros, scales, K, N, G, packed, nbytes, stream);
 }
 
+int tf_repack_w4_gate_up(const uint32_t *qweight, const uint32_t *qzeros, const uint16_t *scales, int64_t K,
+                         int64_t N, int64_t G, void *packed, size_t nbytes, void *stream)
+{
+    return repack(4, qweight, qzeros, scales, K, N, G, packed, nbytes, stream, true);
+}
+
+int tf_repack_w8_gate_up(const uint8_t *qweight, const uint8_t *zeros, const uint16_t *scales, int64_t K, int64_t N,
+                         int64_t G, void *packed, size_t nbytes, void *stream)
+{
+    return repack(8, qweight, zeros, scales, K, N, G, packed, nbytes, stream, true);
+}
+
 size_t tf_workspace_bytes(int bits, int is_gemm, int64_t M, int64_t K, int64_t N, int64_t G)
 {
     if (bits != 4 && bits != 8)
@@ -215,15 +243,15 @@ int tf_gemm_w8a16(const uint16_t *x, const void *packed, size_t nbytes, uint16_t
 }
 
 int tf_gemv_w4a16_silu_mul(const uint16_t *x, const void *packed, size_t nbytes, uint16_t *y, int64_t M, int64_t K,
-                           int64_t N, int64_t G, void *stream)
+                           int64_t N, int64_t G, void *ws, size_t ws_bytes, void *stream)
 {
-    return linear_silu_mul(4, x, packed, nbytes, y, M, K, N, G, stream);
+    return linear_silu_mul(4, x, packed, nbytes, y, M, K, N, G, ws, ws_bytes, stream);
 }
 
 int tf_gemv_w8a16_silu_mul(const uint16_t *x, const void *packed, size_t nbytes, uint16_t *y, int64_t M, int64_t K,
-                           int64_t N, int64_t G, void *stream)
+                           int64_t N, int64_t G, void *ws, size_t ws_bytes, void *stream)
 {
-    return linear_silu_mul(8, x, packed, nbytes, y, M, K, N, G, stream);
+    return linear_silu_mul(8, x, packed, nbytes, y, M, K, N, G, ws, ws_bytes, stream);
 }
 
 int tf_dequant_w4_f32(const void *packed, size_t nbytes, float *w, int64_t K, int64_t N, int64_t G, void *stream)

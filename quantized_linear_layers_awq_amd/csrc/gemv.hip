@@ -141,10 +141,10 @@ enum GroupMode {
 // for anything issued after it.  Each ring slot is unpacked into MFMA operands before it is
 // refilled, so the slot keeps its registers and no wait drains the ring.
 //
-// ACT = kActSiluMul: the layer is [gate | up] along N (N = 2 N', both halves
-// whole 16-column blocks).  A workgroup owns P = BPW / 2 consecutive gate
-// blocks and the up blocks N' / 16 further on, and writes
-// y[m][n] = silu(g) * u (n < N') from the fp32 sums, rounded once.
+// ACT = kActSiluMul: a [gate | up] layer of N = 2 N' columns packed by
+// tf_repack_*_gate_up, so that columns c and c + 8 of block j are gate and up
+// column 8 j + c; the kernel writes y[m][8 j + c] = silu(g) * u from the fp32
+// sums, rounded once.
 template <int BITS, int kMode, int D, int BPW, int ACT = kActNone>
 __global__ __launch_bounds__(1024) void gemv_kernel(const uint16_t *__restrict__ x, const uint8_t *__restrict__ packed,
                                                     uint16_t *__restrict__ y, Layout lay, int M, GemvChunks ch)
@@ -163,16 +163,7 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const uint16_t *__restrict__
     const int ws = wave - bi * Wb;                        // and its share of K
     const int r = lane & 15, o = lane >> 4;
     const int64_t blk0 = (int64_t)blockIdx.x * BPW;       // first block of the workgroup
-    static_assert(ACT == kActNone || BPW % 2 == 0, "gate and up blocks come in pairs");
-    constexpr int P = BPW / 2;                            // gate blocks of a workgroup (ACT)
-    // block of the workgroup's eb-th slot
-    auto block_of = [&](int eb) -> int64_t {
-        if constexpr (ACT == kActNone)
-            return blk0 + eb;
-        const int64_t j = (int64_t)blockIdx.x * P + (eb < P ? eb : eb - P);
-        return eb < P ? j : (lay.nblocks >> 1) + j;
-    };
-    const int64_t blk = block_of(bi);
+    const int64_t blk = blk0 + bi;
     const bool blk_ok = blk < lay.nblocks;                // a last workgroup may be partial
     const uint8_t *meta = packed + (blk_ok ? blk : 0) * lay.block_bytes;
     const uint8_t *tiles = meta + lay.meta_bytes + 16 * lane;
@@ -224,8 +215,8 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const uint16_t *__restrict__
 #pragma unroll
         for (int eb = 0; eb < BPW; ++eb) {
             mv[eb] = u32x2{0u, 0u};
-            if (tid < rec_words && block_of(eb) < lay.nblocks)
-                mv[eb] = *reinterpret_cast<const u32x2 *>(packed + block_of(eb) * lay.block_bytes + g0 * RB + 8 * tid);
+            if (tid < rec_words && blk0 + eb < lay.nblocks)
+                mv[eb] = *reinterpret_cast<const u32x2 *>(packed + (blk0 + eb) * lay.block_bytes + g0 * RB + 8 * tid);
         }
         // ---- then the codes.  Ring loads past the wave's range re-read its
         //      last tile (in bounds, never used). ----
@@ -255,10 +246,10 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const uint16_t *__restrict__
         }
 #pragma unroll
         for (int eb = 0; eb < BPW; ++eb) {
-            if (block_of(eb) < lay.nblocks) {
+            if (blk0 + eb < lay.nblocks) {
                 if (tid < rec_words)
                     *reinterpret_cast<u32x2 *>(smem + eb * ch.meta_cap + 8 * tid) = mv[eb];
-                const uint8_t *src = packed + block_of(eb) * lay.block_bytes + g0 * RB;
+                const uint8_t *src = packed + (blk0 + eb) * lay.block_bytes + g0 * RB;
                 for (int e = tid + (int)blockDim.x; e < rec_words; e += blockDim.x) // more than one per thread
                     *reinterpret_cast<u32x2 *>(smem + eb * ch.meta_cap + 8 * e) =
                         *reinterpret_cast<const u32x2 *>(src + 8 * e);
@@ -348,31 +339,36 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const uint16_t *__restrict__
         red[(wave * 16 + 4 * o + e) * kBlockCols + r] = yacc[e];
     __syncthreads();
     // each block sums its own waves, in wave order
-    auto block_sum = [&](int eb, int row, int col) {
-        float v = 0.f;
-        for (int w = eb * Wb; w < (eb + 1) * Wb; ++w)
-            v += red[(w * 16 + row) * kBlockCols + col];
-        return v;
-    };
     if constexpr (ACT == kActNone) {
 #pragma unroll
         for (int eb = 0; eb < BPW; ++eb) {
             for (int e = tid; e < M * kBlockCols; e += blockDim.x) {
                 const int row = e >> 4, col = e & 15;
-                const float v = block_sum(eb, row, col);
+                float v = 0.f;
+                for (int w = eb * Wb; w < (eb + 1) * Wb; ++w)
+                    v += red[(w * 16 + row) * kBlockCols + col];
                 const int64_t nn = (blk0 + eb) * kBlockCols + col;
                 if (nn < lay.N)
                     y[(int64_t)row * lay.N + nn] = f32_to_bf16_bits(v);
             }
         }
     } else {
+        auto block_sum = [&](int eb, int row, int col) {
+            float v = 0.f;
+            for (int w = eb * Wb; w < (eb + 1) * Wb; ++w)
+                v += red[(w * 16 + row) * kBlockCols + col];
+            return v;
+        };
         const int64_t n2 = lay.N >> 1;
-        for (int eb = 0; eb < P; ++eb) {
-            for (int e = tid; e < M * kBlockCols; e += blockDim.x) {
-                const int row = e >> 4, col = e & 15;
-                const float g = block_sum(eb, row, col), u = block_sum(eb + P, row, col);
-                const int64_t nn = block_of(eb) * kBlockCols + col;
-                y[(int64_t)row * n2 + nn] = f32_to_bf16_bits(silu(g) * u);
+        constexpr int kHalf = kBlockCols / 2;
+#pragma unroll
+        for (int eb = 0; eb < BPW; ++eb) {
+            if (blk0 + eb >= lay.nblocks)
+                break;
+            for (int e = tid; e < M * kHalf; e += blockDim.x) {
+                const int row = e >> 3, c = e & 7;
+                const float g = block_sum(eb, row, c), u = block_sum(eb, row, c + kHalf);
+                y[(int64_t)row * n2 + (blk0 + eb) * kHalf + c] = f32_to_bf16_bits(silu(g) * u);
             }
         }
     }
@@ -406,7 +402,11 @@ struct MidChunks {
     int split_tiles; // k-tiles per K range (gridDim.y ranges)
 };
 
-template <int BITS, int kMode, int MT, int D>
+// ACT = kActSiluMul: as in gemv_kernel, a [gate | up] layer packed by
+// tf_repack_*_gate_up; lanes r and r + 8 hold gate and up column 8 blk + r.
+// With K split, the partials are the plain ones and the summing kernel
+// applies the product.
+template <int BITS, int kMode, int MT, int D, int ACT = kActNone>
 __global__ __launch_bounds__(64 * kMidWaves) void gemv_mid_kernel(const uint16_t *__restrict__ x,
                                                                  const uint8_t *__restrict__ packed,
                                                                  uint16_t *__restrict__ y, Layout lay, int M,
@@ -648,23 +648,61 @@ __global__ __launch_bounds__(64 * kMidWaves) void gemv_mid_kernel(const uint16_t
     //      16 c + 4 o + e of column r); with K split, fp32 partials, stored
     //      non-temporally: the summing kernel reads them on other XCDs, so
     //      they need not stay in this XCD's L2
-    if (blk_ok) {
-        const int64_t nn = blk * kBlockCols + r;
-        if (nn < lay.N) {
+    if constexpr (ACT == kActNone) {
+        if (blk_ok) {
+            const int64_t nn = blk * kBlockCols + r;
+            if (nn < lay.N) {
 #pragma unroll
-            for (int c = 0; c < MT; ++c)
+                for (int c = 0; c < MT; ++c)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int row = 16 * c + 4 * o + e;
-                    if (row < M) {
-                        if (gridDim.y > 1)
-                            __builtin_nontemporal_store(yacc[c][e], ws + ((int64_t)split * M + row) * lay.N + nn);
-                        else
-                            y[(int64_t)row * lay.N + nn] = f32_to_bf16_bits(yacc[c][e]);
+                    for (int e = 0; e < 4; ++e) {
+                        const int row = 16 * c + 4 * o + e;
+                        if (row < M) {
+                            if (gridDim.y > 1)
+                                __builtin_nontemporal_store(yacc[c][e], ws + ((int64_t)split * M + row) * lay.N + nn);
+                            else
+                                y[(int64_t)row * lay.N + nn] = f32_to_bf16_bits(yacc[c][e]);
+                        }
                     }
-                }
+            }
         }
+    } else if (blk_ok) { // blk_ok is uniform over the wave; N % 16 == 0: every column exists
+        const int64_t nn = blk * kBlockCols + r, n2 = lay.N >> 1;
+#pragma unroll
+        for (int c = 0; c < MT; ++c)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int row = 16 * c + 4 * o + e;
+                const float u = __shfl_xor(yacc[c][e], kBlockCols / 2); // lane r + 8: the up column
+                if (row < M) {
+                    if (gridDim.y > 1)
+                        __builtin_nontemporal_store(yacc[c][e], ws + ((int64_t)split * M + row) * lay.N + nn);
+                    else if (r < kBlockCols / 2)
+                        y[(int64_t)row * n2 + blk * (kBlockCols / 2) + r] = f32_to_bf16_bits(silu(yacc[c][e]) * u);
+                }
+            }
     }
+}
+
+// Sum of a SiLU-product launch's K ranges: y[m][8 j + c] = silu(g) * u, g
+// and u the in-order sums of the ranges' partials of columns 16 j + c and
+// 16 j + c + 8.  One thread per output.
+__global__ __launch_bounds__(256) void splitk_sum_silu_kernel(const float *__restrict__ ws, int splits, int64_t M,
+                                                              int64_t N, uint16_t *__restrict__ y)
+{
+    const int64_t n2 = N >> 1;
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= M * n2)
+        return;
+    const int64_t m = i / n2, h = i - m * n2;
+    const int64_t col = (h >> 3) * kBlockCols + (h & 7);
+    float g = 0.f, u = 0.f;
+    for (int s = 0; s < splits; ++s) {
+        const float *row = ws + ((int64_t)s * M + m) * N;
+        g += __builtin_nontemporal_load(row + col);
+        u += __builtin_nontemporal_load(row + col + kBlockCols / 2);
+    }
+    y[i] = f32_to_bf16_bits(silu(g) * u);
 }
 
 // Blocks per workgroup: one at M = 1 (x is small); with several activation
@@ -679,8 +717,9 @@ static int gemv_bpw(const Layout &lay, int64_t M)
     return b >= 4 ? 4 : b >= 2 ? 2 : 1;
 }
 
-static int gemv_waves_bpw(const Layout &lay, int bpw)
+int gemv_waves(const Layout &lay, int64_t M)
 {
+    const int bpw = gemv_bpw(lay, M);
     const int64_t wgs = (lay.nblocks + bpw - 1) / bpw;
     int64_t wb = ((kGemvTargetWaves + wgs - 1) / wgs + bpw - 1) / bpw; // waves per block
     if (wb * bpw > kGemvMaxWaves)
@@ -689,8 +728,6 @@ static int gemv_waves_bpw(const Layout &lay, int bpw)
         wb = lay.ktiles;
     return (int)(wb < 1 ? 1 : wb) * bpw;
 }
-
-int gemv_waves(const Layout &lay, int64_t M) { return gemv_waves_bpw(lay, gemv_bpw(lay, M)); }
 
 // Chunk size: as many k-tiles as fit the LDS share of one workgroup when
 // 16 / W workgroups run per CU (at most kGemvMaxLds).
@@ -755,7 +792,7 @@ static void launch_gemv_depth(const Layout &lay, dim3 grid, dim3 block, const Ge
         launch_gemv_bpw<BITS, D, 4, ACT>(lay, grid, block, ch, stream, x, pk, y, M);
     else if (ch.bpw == 2)
         launch_gemv_bpw<BITS, D, 2, ACT>(lay, grid, block, ch, stream, x, pk, y, M);
-    else if constexpr (ACT == kActNone) // pairs of gate and up blocks need an even count
+    else
         launch_gemv_bpw<BITS, D, 1, ACT>(lay, grid, block, ch, stream, x, pk, y, M);
 }
 
@@ -871,45 +908,51 @@ static MidChunks plan_mid(int bits, const Layout &lay, int64_t M, int64_t split_
     return c;
 }
 
-template <int BITS, int kMode, int MT, int D>
+template <int BITS, int kMode, int MT, int D, int ACT>
 static void launch_mid_mode(dim3 grid, const MidChunks &ch, hipStream_t stream, const uint16_t *x,
                             const uint8_t *pk, uint16_t *y, const Layout &lay, int M, float *ws)
 {
-    auto kern = &gemv_mid_kernel<BITS, kMode, MT, D>;
+    auto kern = &gemv_mid_kernel<BITS, kMode, MT, D, ACT>;
     static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, kGemvMaxLds);
     (void)attr;
     kern<<<grid, 64 * kMidWaves, ch.lds, stream>>>(x, pk, y, lay, M, ch, ws);
 }
 
-template <int BITS, int MT, int D>
+template <int BITS, int MT, int D, int ACT>
 static void launch_mid_mt(dim3 grid, const MidChunks &ch, hipStream_t stream, const uint16_t *x, const uint8_t *pk,
                           uint16_t *y, const Layout &lay, int M, float *ws)
 {
     if (lay.tiles_per_group == 1)
-        launch_mid_mode<BITS, kOneTile, MT, D>(grid, ch, stream, x, pk, y, lay, M, ws);
+        launch_mid_mode<BITS, kOneTile, MT, D, ACT>(grid, ch, stream, x, pk, y, lay, M, ws);
     else if (lay.whole_tiles())
-        launch_mid_mode<BITS, kMultiTile, MT, D>(grid, ch, stream, x, pk, y, lay, M, ws);
+        launch_mid_mode<BITS, kMultiTile, MT, D, ACT>(grid, ch, stream, x, pk, y, lay, M, ws);
     else
-        launch_mid_mode<BITS, kSplitTiles, MT, D>(grid, ch, stream, x, pk, y, lay, M, ws);
+        launch_mid_mode<BITS, kSplitTiles, MT, D, ACT>(grid, ch, stream, x, pk, y, lay, M, ws);
 }
 
-template <int BITS>
+template <int BITS, int ACT>
 static void launch_mid_bits(dim3 grid, const MidChunks &ch, hipStream_t stream, const uint16_t *x, const uint8_t *pk,
                             uint16_t *y, const Layout &lay, int M, float *ws)
 {
     // M <= 16: one row chunk, M <= 32: two, depth 8; above: four, depth 4
+    // (the SiLU product is a decode epilogue: at most 16 rows)
     if (mid_mt(M) == 1)
-        launch_mid_mt<BITS, 1, 8>(grid, ch, stream, x, pk, y, lay, M, ws);
-    else if (mid_mt(M) == 2)
-        launch_mid_mt<BITS, 2, 8>(grid, ch, stream, x, pk, y, lay, M, ws);
-    else
-        launch_mid_mt<BITS, 4, 4>(grid, ch, stream, x, pk, y, lay, M, ws);
+        launch_mid_mt<BITS, 1, 8, ACT>(grid, ch, stream, x, pk, y, lay, M, ws);
+    else if constexpr (ACT == kActNone) {
+        if (mid_mt(M) == 2)
+            launch_mid_mt<BITS, 2, 8, ACT>(grid, ch, stream, x, pk, y, lay, M, ws);
+        else
+            launch_mid_mt<BITS, 4, 4, ACT>(grid, ch, stream, x, pk, y, lay, M, ws);
+    }
 }
 
+template <int ACT = kActNone>
 static hipError_t launch_gemv_mid(int bits, const uint16_t *x, const uint8_t *pk, uint16_t *y, int64_t M,
                                   const Layout &lay, void *workspace, hipStream_t stream)
 {
+    if (ACT != kActNone && M > 16)
+        return hipErrorInvalidValue;
     int64_t split_tiles = 0;
     const int64_t splits = gemv_splits(lay, M, planning_cus(), &split_tiles);
     const MidChunks ch = plan_mid(bits, lay, M, split_tiles);
@@ -922,11 +965,16 @@ static hipError_t launch_gemv_mid(int bits, const uint16_t *x, const uint8_t *pk
     const dim3 grid((unsigned)((lay.nblocks + kMidWaves - 1) / kMidWaves), (unsigned)splits);
     float *ws = splits > 1 ? static_cast<float *>(workspace) : nullptr;
     if (bits == 4)
-        launch_mid_bits<4>(grid, ch, stream, x, pk, y, lay, (int)M, ws);
+        launch_mid_bits<4, ACT>(grid, ch, stream, x, pk, y, lay, (int)M, ws);
     else
-        launch_mid_bits<8>(grid, ch, stream, x, pk, y, lay, (int)M, ws);
-    if (splits > 1)
-        launch_splitk_sum(ws, (int)splits, M * lay.N, y, stream);
+        launch_mid_bits<8, ACT>(grid, ch, stream, x, pk, y, lay, (int)M, ws);
+    if (splits > 1) {
+        if constexpr (ACT == kActNone)
+            launch_splitk_sum(ws, (int)splits, M * lay.N, y, stream);
+        else
+            splitk_sum_silu_kernel<<<(unsigned)((M * (lay.N / 2) + 255) / 256), 256, 0, stream>>>(ws, (int)splits, M,
+                                                                                                lay.N, y);
+    }
     return hipGetLastError();
 }
 
@@ -947,21 +995,20 @@ hipError_t launch_gemv(int bits, const uint16_t *x, const void *packed, uint16_t
     return hipGetLastError();
 }
 
-// The fused gate/up GEMV with the SiLU product: the kernel for up to 16 rows
-// with gate block j and up block N/32 + j in one workgroup (two or four
-// blocks per workgroup, so one or two pairs).
+// The gate/up GEMV with the SiLU product: the kernel the plain GEMV of the
+// same shape runs, on its grid (each block pairs its own columns).
 hipError_t launch_gemv_silu_mul(int bits, const uint16_t *x, const void *packed, uint16_t *y, int64_t M,
-                                const Layout &lay, hipStream_t stream)
+                                const Layout &lay, void *workspace, hipStream_t stream)
 {
-    const int64_t half = lay.nblocks / 2;
-    if (lay.nblocks % 2 || M < 1 || M > 16)
+    if (lay.N % kBlockCols || M < 1 || M > 16)
         return hipErrorInvalidValue;
-    int bpw = gemv_bpw(lay, M) < 2 ? 2 : gemv_bpw(lay, M);
-    if ((half * 2) % bpw)
-        bpw = 2;
-    const int W = gemv_waves_bpw(lay, bpw);
+    if (use_mid(lay, M, planning_cus()))
+        return launch_gemv_mid<kActSiluMul>(bits, x, static_cast<const uint8_t *>(packed), y, M, lay, workspace,
+                                            stream);
+    const int W = gemv_waves(lay, M);
+    const int bpw = gemv_bpw(lay, M);
     const GemvChunks ch = plan_chunks(bits, lay, M, W, bpw);
-    const dim3 grid((unsigned)(half / (bpw / 2))), block(64 * W);
+    const dim3 grid((unsigned)((lay.nblocks + bpw - 1) / bpw)), block(64 * W);
     const uint8_t *pk = static_cast<const uint8_t *>(packed);
     if (bits == 4)
         launch_gemv_bits<4, kActSiluMul>(lay, grid, block, ch, stream, x, pk, y, (int)M);

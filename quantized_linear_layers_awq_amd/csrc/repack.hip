@@ -10,12 +10,22 @@
 
 namespace tf {
 
+// Checkpoint column of packed column n: n itself, or, for a [gate | up]
+// checkpoint packed for the SiLU-product GEMV (half = N/2, a multiple of 8),
+// gate column 8 j + c for c = n % 16 < 8 of block j = n / 16 and up column
+// 8 j + c - 8 for c >= 8.  Runs of eight columns stay runs of eight, so
+// n % 8 (an AWQ word's nibble) is unchanged.
+__device__ __forceinline__ int64_t source_col(int64_t n, int64_t half)
+{
+    return half == 0 ? n : ((n & 8) ? half : 0) + ((n >> 4) << 3) + (n & 7);
+}
+
 // ---------------------------------------------------------------------------
 // Codes.  W4: 64 units of 16 bytes per k-tile (lane L = 16o + r: word u holds
 // rows 32u + 8o .. +7 of column r).  W8: 128 units (half h = u / 2 at 1024h).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void repack_w4_codes(const uint32_t *__restrict__ qweight, Layout lay,
-                                                       uint8_t *__restrict__ packed, int64_t units)
+                                                       uint8_t *__restrict__ packed, int64_t units, int64_t half)
 {
     const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (idx >= units)
@@ -24,11 +34,11 @@ __global__ __launch_bounds__(256) void repack_w4_codes(const uint32_t *__restric
     const int64_t bt = idx >> 6; // blk * ktiles + t
     const int64_t blk = bt / lay.ktiles, t = bt - blk * lay.ktiles;
     const int o = L >> 4, r = L & 15;
-    const int64_t n = blk * kBlockCols + r;
+    const int64_t n = blk * kBlockCols + r, sn = source_col(n, half);
     const int64_t words_per_row = lay.N / 8;
     u32x4 out = {0u, 0u, 0u, 0u};
     if (n < lay.N) {
-        const uint32_t sh = awq_nibble_shift((int)(n & 7));
+        const uint32_t sh = awq_nibble_shift((int)(sn & 7));
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             uint32_t wd = 0;
@@ -36,7 +46,7 @@ __global__ __launch_bounds__(256) void repack_w4_codes(const uint32_t *__restric
             for (int i = 0; i < 8; ++i) {
                 const int64_t k = t * kTileRows + kStepRows * u + 8 * o + i;
                 if (k < lay.K)
-                    wd |= ((qweight[k * words_per_row + (n >> 3)] >> sh) & 0xFu) << w4_row_shift(i);
+                    wd |= ((qweight[k * words_per_row + (sn >> 3)] >> sh) & 0xFu) << w4_row_shift(i);
             }
             out[u] = wd;
         }
@@ -45,7 +55,7 @@ __global__ __launch_bounds__(256) void repack_w4_codes(const uint32_t *__restric
 }
 
 __global__ __launch_bounds__(256) void repack_w8_codes(const uint8_t *__restrict__ qweight, Layout lay,
-                                                       uint8_t *__restrict__ packed, int64_t units)
+                                                       uint8_t *__restrict__ packed, int64_t units, int64_t half)
 {
     const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (idx >= units)
@@ -55,7 +65,7 @@ __global__ __launch_bounds__(256) void repack_w8_codes(const uint8_t *__restrict
     const int64_t bt = idx >> 7;
     const int64_t blk = bt / lay.ktiles, t = bt - blk * lay.ktiles;
     const int o = L >> 4, r = L & 15;
-    const int64_t n = blk * kBlockCols + r;
+    const int64_t n = blk * kBlockCols + r, sn = source_col(n, half);
     u32x4 out = {0u, 0u, 0u, 0u};
     if (n < lay.N) {
 #pragma unroll
@@ -65,7 +75,7 @@ __global__ __launch_bounds__(256) void repack_w8_codes(const uint8_t *__restrict
             for (int i = 0; i < 8; ++i) {
                 const int64_t k = t * kTileRows + kStepRows * u + 8 * o + i;
                 if (k < lay.K)
-                    out[2 * uu + (i >> 2)] |= (uint32_t)qweight[k * lay.N + n] << (8 * (i & 3));
+                    out[2 * uu + (i >> 2)] |= (uint32_t)qweight[k * lay.N + sn] << (8 * (i & 3));
             }
         }
     }
@@ -80,7 +90,7 @@ __global__ __launch_bounds__(256) void repack_w8_codes(const uint8_t *__restrict
 template <int BITS>
 __global__ __launch_bounds__(256) void repack_records(const void *__restrict__ qzeros,
                                                       const uint16_t *__restrict__ scales, Layout lay,
-                                                      uint8_t *__restrict__ packed, int64_t units)
+                                                      uint8_t *__restrict__ packed, int64_t units, int64_t half)
 {
     const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (idx >= units)
@@ -93,15 +103,16 @@ __global__ __launch_bounds__(256) void repack_records(const void *__restrict__ q
         const int64_t n = blk * kBlockCols + c;
         if (n >= lay.N)
             continue;
-        sc[c >> 1] |= (uint32_t)scales[g * lay.N + n] << (16 * (c & 1));
+        const int64_t sn = source_col(n, half);
+        sc[c >> 1] |= (uint32_t)scales[g * lay.N + sn] << (16 * (c & 1));
         // no zero-point tensor: symmetric quantization, z = 2^(b-1)
         if constexpr (BITS == 4) {
             const uint32_t *qz = static_cast<const uint32_t *>(qzeros);
             const uint32_t z =
-                qz ? (qz[g * (lay.N / 8) + (n >> 3)] >> awq_nibble_shift((int)(n & 7))) & 0xFu : 8u;
+                qz ? (qz[g * (lay.N / 8) + (sn >> 3)] >> awq_nibble_shift((int)(sn & 7))) & 0xFu : 8u;
             zz[c >> 3] |= z << (4 * (c & 7));
         } else {
-            const uint32_t z = qzeros ? static_cast<const uint8_t *>(qzeros)[g * lay.N + n] : 128u;
+            const uint32_t z = qzeros ? static_cast<const uint8_t *>(qzeros)[g * lay.N + sn] : 128u;
             zz[c >> 2] |= z << (8 * (c & 3));
         }
     }
@@ -167,19 +178,21 @@ __global__ __launch_bounds__(256) void dequant_f32(const uint8_t *__restrict__ p
 static inline unsigned grid_for(int64_t units) { return (unsigned)((units + 255) / 256); }
 
 hipError_t launch_repack(int bits, const void *qweight, const void *qzeros, const uint16_t *scales,
-                         const Layout &lay, void *packed, hipStream_t stream)
+                         const Layout &lay, void *packed, hipStream_t stream, int64_t pair_half)
 {
+    if (pair_half && (pair_half % 8 || 2 * pair_half != lay.N))
+        return hipErrorInvalidValue;
     uint8_t *out = static_cast<uint8_t *>(packed);
     const int64_t code_units = lay.nblocks * lay.ktiles * (bits == 4 ? 64 : 128);
     const int64_t rec_units = lay.nblocks * lay.ngroups;
     if (bits == 4) {
         repack_w4_codes<<<grid_for(code_units), 256, 0, stream>>>(static_cast<const uint32_t *>(qweight), lay, out,
-                                                                  code_units);
-        repack_records<4><<<grid_for(rec_units), 256, 0, stream>>>(qzeros, scales, lay, out, rec_units);
+                                                                  code_units, pair_half);
+        repack_records<4><<<grid_for(rec_units), 256, 0, stream>>>(qzeros, scales, lay, out, rec_units, pair_half);
     } else {
         repack_w8_codes<<<grid_for(code_units), 256, 0, stream>>>(static_cast<const uint8_t *>(qweight), lay, out,
-                                                                  code_units);
-        repack_records<8><<<grid_for(rec_units), 256, 0, stream>>>(qzeros, scales, lay, out, rec_units);
+                                                                  code_units, pair_half);
+        repack_records<8><<<grid_for(rec_units), 256, 0, stream>>>(qzeros, scales, lay, out, rec_units, pair_half);
     }
     return hipGetLastError();
 }

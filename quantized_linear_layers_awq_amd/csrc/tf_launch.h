@@ -5,8 +5,11 @@
 
 namespace tf {
 
+// pair_half = 0: the checkpoint's columns in order.  pair_half = N/2 (a
+// multiple of 8): a [gate | up] checkpoint, packed so that column c of block
+// j is gate column 8 j + c (c < 8) or up column 8 j + c - 8 (c >= 8).
 hipError_t launch_repack(int bits, const void *qweight, const void *qzeros, const uint16_t *scales,
-                         const Layout &lay, void *packed, hipStream_t stream);
+                         const Layout &lay, void *packed, hipStream_t stream, int64_t pair_half = 0);
 hipError_t launch_dequant_f32(int bits, const void *packed, const Layout &lay, float *w, hipStream_t stream);
 
 // Waves per GEMV workgroup for M <= 16 activation rows (one workgroup per
@@ -26,10 +29,12 @@ hipError_t launch_gemv(int bits, const uint16_t *x, const void *packed, uint16_t
 // Epilogue of the GEMV kernel: none, or silu(gate) * up over a [gate | up]
 // layer (launch_gemv_silu_mul).
 constexpr int kActNone = 0, kActSiluMul = 1;
-// y[m][n] = silu(g) * u with g, u the fp32 sums of columns n and N/2 + n of a
-// [gate | up] layer (N % 32 == 0), 1 <= M <= 16; y is [M][N/2].  No workspace.
+// y[m][8 j + c] = silu(g) * u with g, u the fp32 sums of columns c and c + 8
+// of block j of a [gate | up] layer packed with pair_half = N/2 (N % 16 ==
+// 0), 1 <= M <= 16; y is [M][N/2].  Same kernel choice, and so the same
+// workspace (gemv_workspace_bytes), as launch_gemv of that shape.
 hipError_t launch_gemv_silu_mul(int bits, const uint16_t *x, const void *packed, uint16_t *y, int64_t M,
-                                const Layout &lay, hipStream_t stream);
+                                const Layout &lay, void *workspace, hipStream_t stream);
 // y = bf16(sum of the splits' fp32 partials ws[s][mn]), added in split order;
 // 2 <= splits <= 16 (both plans stay within that).
 void launch_splitk_sum(const float *ws, int splits, int64_t mn, uint16_t *y, hipStream_t stream);

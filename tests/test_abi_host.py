@@ -322,13 +322,16 @@ class TestValidation:
         assert self._gemv(lib, M=0, x=None, y=None, packed=None) == TF_OK
         assert self._gemv(lib, M=0, x=None, y=None, packed=None, fn="tf_gemm_w8a16") == TF_OK
 
-    def _silu(self, lib, M=1, K=256, N=128, G=128, x=FAKE, packed=FAKE, y=FAKE, nbytes=1 << 30,
-              fn="tf_gemv_w4a16_silu_mul"):
-        return getattr(lib, fn)(x, packed, nbytes, y, M, K, N, G, None)
+    def _silu(self, lib, M=1, K=256, N=128, G=128, x=FAKE, packed=FAKE, y=FAKE, nbytes=1 << 30, ws=FAKE,
+              ws_bytes=1 << 30, fn="tf_gemv_w4a16_silu_mul"):
+        return getattr(lib, fn)(x, packed, nbytes, y, M, K, N, G, ws, ws_bytes, None)
 
     def test_silu_mul_validation(self, lib):
-        assert self._silu(lib, N=112) == TF_ERR_SHAPE          # halves of 56 columns: not whole blocks
+        assert self._silu(lib, N=104) == TF_ERR_SHAPE          # halves of 52 columns: not runs of 8
         assert self._silu(lib, N=100, fn="tf_gemv_w8a16_silu_mul") == TF_ERR_SHAPE
+        assert lib.tf_repack_w4_gate_up(FAKE, FAKE, FAKE, 256, 104, 128, FAKE, 1 << 30, None) == TF_ERR_SHAPE
+        assert lib.tf_repack_w8_gate_up(FAKE, FAKE, FAKE, 256, 100, 128, FAKE, 1 << 30, None) == TF_ERR_SHAPE
+        assert lib.tf_repack_w4_gate_up(FAKE, None, FAKE, 256, 112, 128, FAKE, 10, None) == TF_ERR_BUFFER_TOO_SMALL
         assert self._silu(lib, M=17) == TF_ERR_SHAPE
         assert self._silu(lib, M=-1) == TF_ERR_SHAPE
         assert self._silu(lib, K=1 << 25, G=1 << 25) == TF_ERR_SHAPE
@@ -340,6 +343,15 @@ class TestValidation:
         need = lib.tf_packed_bytes_w4(256, 128, 128)
         assert self._silu(lib, nbytes=need - 1) == TF_ERR_BUFFER_TOO_SMALL
         assert self._silu(lib, M=0, x=None, y=None, packed=None) == TF_OK
+        # a shape the plain GEMV splits over K: the same workspace rules
+        shape = dict(M=16, K=8192, N=8192, G=8192, fn="tf_gemv_w8a16_silu_mul")
+        need = lib.tf_workspace_bytes(8, 0, 16, 8192, 8192, 8192)
+        assert need > 0
+        assert self._silu(lib, ws=None, **shape) == TF_ERR_NULL
+        assert self._silu(lib, ws=FAKE + 64, **shape) == TF_ERR_ALIGN
+        assert self._silu(lib, ws_bytes=need - 1, **shape) == TF_ERR_BUFFER_TOO_SMALL
+        assert self._silu(lib, ws=None, ws_bytes=0, nbytes=10, M=4, K=8192, N=8192, G=8192,
+                          fn="tf_gemv_w8a16_silu_mul") == TF_ERR_BUFFER_TOO_SMALL  # no workspace needed below 8 rows
 
     def test_repack_validation(self, lib):
         f = lib.tf_repack_w4

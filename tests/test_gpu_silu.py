@@ -1,23 +1,24 @@
 """Fused [gate | up] GEMV with the SiLU product (tf_gemv_*_silu_mul) against
 the oracle: y[m][n] = silu(g) * u from the unrounded sums of columns n and
-N/2 + n, one rounding to bf16."""
+N/2 + n, one rounding to bf16; the gate/up repack bit for bit."""
 
 import numpy as np
 import pytest
 
 import oracle
 import synth
-from gpu_harness import bf16_bits, bf16_to_f64, gpu_or_skip, repack, sample_indices, to_device, within_tolerance
+from gpu_harness import (bf16_bits, bf16_to_f64, gpu_or_skip, planning_cus, sample_indices, to_device,
+                         within_tolerance)
 
 pytestmark = pytest.mark.gpu
 
-# (bits, M, K, N, G), N the fused width: one or two gate/up pairs per
-# workgroup, an odd number of pairs where two per workgroup would not
-# divide them, ragged K, G = 32 / 64 / 128 / per channel, up to 16 rows
+# (bits, M, K, N, G), N the fused width: halves of whole and half blocks
+# (N/2 = 56, 40), one, two and four blocks per workgroup with a partial last
+# workgroup, ragged K, G = 32 / 64 / 128 / per channel, up to 16 rows
 SHAPES = [
     (4, 1, 512, 320, 128), (4, 3, 352, 64, 32), (4, 8, 1024, 4096, 64), (4, 16, 4096, 4096, 128),
-    (4, 2, 256, 16384, 128), (4, 5, 128, 32800, 128), (4, 1, 384, 96, 384),
-    (8, 1, 256, 96, 256), (8, 4, 2048, 8192, 128), (8, 12, 1024, 16384, 1024), (8, 16, 512, 64, 32),
+    (4, 2, 256, 16384, 128), (4, 5, 128, 32784, 128), (4, 1, 384, 112, 384), (4, 4, 512, 8208, 128),
+    (8, 1, 256, 80, 256), (8, 4, 2048, 8192, 128), (8, 12, 1024, 16400, 1024), (8, 16, 512, 64, 32),
 ]
 
 
@@ -25,9 +26,14 @@ def _fn(q, bits):
     return q.tf_gemv_w4a16_silu_mul if bits == 4 else q.tf_gemv_w8a16_silu_mul
 
 
+def repack_gate_up(case, d, q):
+    fn = q.tf_repack_w4_gate_up if case.bits == 4 else q.tf_repack_w8_gate_up
+    return fn(d["qweight"], d["qzeros"], d["scales"], case.K, case.N, case.G)
+
+
 def _run(case, torch, q, d=None, p=None, y=None):
     d = d or to_device(case, torch)
-    p = p if p is not None else repack(case, d, q)
+    p = p if p is not None else repack_gate_up(case, d, q)
     out = _fn(q, case.bits)(d["x"], p, case.K, case.N, case.G, y=y)
     torch.cuda.synchronize()
     return out
@@ -43,6 +49,35 @@ def test_silu_mul_within_tolerance(shape):
     assert tuple(y.shape) == (M, N // 2)
     ref = oracle.awq_linear_silu_mul(c)
     ok, ratio = within_tolerance(bf16_to_f64(y), ref)
+    assert ok, f"worst error / bound = {ratio:.3f}"
+
+
+# The kernel and K split the plain GEMV of the shape would run, forced by
+# the compute units the plan assumes (1: never a split; 256, 4096: long-K
+# layers split into 4..16 ranges from 8 rows, partials summed by the SiLU
+# sum kernel; wide layers from 2 rows run the 16-row-chunk kernel unsplit).
+# (bits, M, K, N, G) -> K ranges at 1 / 256 / 4096 compute units
+ROUTE_SHAPES = {
+    (4, 8, 14336, 4096, 128): (1, 8, 16), (8, 16, 8192, 8192, 8192): (1, 4, 1),
+    (4, 12, 14336, 1024, 64): (1, 16, 16), (8, 8, 8192, 4112, 2048): (1, 7, 1),
+    (4, 10, 28672, 528, 32): (1, 16, 16), (4, 16, 4096, 28672, 128): (1, 1, 1),
+    (4, 2, 1024, 8192, 128): (1, 1, 1), (4, 5, 2048, 1040, 32): (1, 1, 1),
+}
+
+
+@pytest.mark.parametrize("cus", [1, 256, 4096])
+@pytest.mark.parametrize("shape", list(ROUTE_SHAPES), ids=[str(s) for s in ROUTE_SHAPES])
+def test_silu_mul_routes(shape, cus):
+    torch, q = gpu_or_skip()
+    bits, M, K, N, G = shape
+    print(f"silu_mul route shape={shape} cus={cus}", flush=True)
+    c = synth.make_inputs(bits, M, K, N, G, seed=(69, bits, M, K), keep_codes=False)
+    with planning_cus(q, cus):
+        splits = ROUTE_SHAPES[shape][(1, 256, 4096).index(cus)]
+        assert q.tf_workspace_bytes(bits, False, M, K, N, G) == (4 * splits * M * N if splits > 1 else 0)
+        y = _run(c, torch, q)
+    cols = sample_indices(N // 2, 512, seed=70)
+    ok, ratio = within_tolerance(bf16_to_f64(y)[:, cols], oracle.awq_linear_silu_mul(c, cols=cols))
     assert ok, f"worst error / bound = {ratio:.3f}"
 
 
@@ -62,18 +97,21 @@ def test_silu_mul_decoder_gate_up(bits, M):
 
 
 @pytest.mark.parametrize("half", ["gate", "up"])
-@pytest.mark.parametrize("bits,M", [(4, 1), (4, 6), (8, 3)])
-def test_zero_half_gives_exact_zero(bits, M, half):
+@pytest.mark.parametrize("bits,M,cus", [(4, 1, 0), (4, 6, 0), (8, 3, 0), (4, 8, 256), (4, 12, 1)])
+def test_zero_half_gives_exact_zero(bits, M, cus, half):
     """q == z on the gate half makes g exactly 0 and silu(0) = 0; on the up
     half u is exactly 0.  Either way every output is exactly zero."""
     torch, q = gpu_or_skip()
-    K, N, G = 1024, 2 * 1056, 128
+    # a long-K layer where the plan splits K: partials summed by the SiLU sum kernel
+    K, N, G = (14336, 1024, 128) if cus == 256 else (1024, 2 * 1056, 128)
     c0 = synth.make_inputs(bits, M, K, N, G, seed=(64, bits, M))
     codes = c0.codes.copy()
     cols = slice(0, N // 2) if half == "gate" else slice(N // 2, N)
     codes[:, cols] = c0.zeros[np.arange(K) // G][:, cols]
     c = synth.gen.pack_case(bits, codes, c0.zeros, c0.scales, c0.x, G)
-    y = _run(c, torch, q)
+    with planning_cus(q, cus):
+        assert (q.tf_workspace_bytes(bits, False, M, K, N, G) > 0) == (cus == 256)
+        y = _run(c, torch, q)
     assert np.all(bf16_to_f64(y) == 0.0)
 
 
@@ -81,7 +119,7 @@ def test_silu_mul_deterministic_and_guard_bands():
     torch, q = gpu_or_skip()
     c = synth.make_inputs(4, 7, 2048, 2 * 1040, 128, seed=(65,))
     d = to_device(c, torch)
-    p = repack(c, d, q)
+    p = repack_gate_up(c, d, q)
     a = bf16_bits(_run(c, torch, q, d, p))
     pad, n = 4096, c.M * (c.N // 2)
     big = torch.full((n + 2 * pad,), -7.25, dtype=torch.bfloat16, device="cuda:0")
@@ -91,15 +129,28 @@ def test_silu_mul_deterministic_and_guard_bands():
     assert np.array_equal(bf16_bits(big[pad:pad + n]).reshape(c.M, -1), a)
 
 
+@pytest.mark.parametrize("bits,K,N,G", [(4, 256, 48, 128), (4, 4096, 28672, 128), (4, 352, 112, 32),
+                                         (8, 384, 80, 384), (8, 1024, 4112, 64)])
+def test_gate_up_repack_matches_oracle(bits, K, N, G):
+    torch, q = gpu_or_skip()
+    c = synth.make_inputs(bits, 1, K, N, G, seed=(68, bits, N), keep_codes=False)
+    d = to_device(c, torch)
+    got = repack_gate_up(c, d, q).cpu().numpy()
+    want = oracle.repack_gate_up(bits, c.qweight, c.qzeros, c.scales, K, N, G)
+    assert np.array_equal(got, want)
+
+
 def test_silu_mul_rejects_bad_shapes_before_launch():
     torch, q = gpu_or_skip()
-    c = synth.make_inputs(4, 2, 256, 80, 128, seed=(66,))
+    c = synth.make_inputs(4, 2, 256, 72, 128, seed=(66,))
     d = to_device(c, torch)
-    p = repack(c, d, q)
+    p = q.tf_repack_w4(d["qweight"], d["qzeros"], d["scales"], c.K, c.N, c.G)
     with pytest.raises(q.TileFuseError):
-        q.tf_gemv_w4a16_silu_mul(d["x"], p, c.K, c.N, c.G)  # 40-column halves: not whole blocks
+        q.tf_gemv_w4a16_silu_mul(d["x"], p, c.K, c.N, c.G)  # halves of 36 columns
+    with pytest.raises(q.TileFuseError):
+        repack_gate_up(c, d, q)
     x17 = torch.zeros((17, 256), dtype=torch.bfloat16, device="cuda:0")
     c2 = synth.make_inputs(4, 1, 256, 128, 128, seed=(67,))
     d2 = to_device(c2, torch)
     with pytest.raises(q.TileFuseError):
-        q.tf_gemv_w4a16_silu_mul(x17, repack(c2, d2, q), 256, 128, 128)
+        q.tf_gemv_w4a16_silu_mul(x17, repack_gate_up(c2, d2, q), 256, 128, 128)

@@ -86,3 +86,27 @@ def test_repack_is_a_bijection_on_code_positions():
                                        (4, 384, 64, 96), (8, 640, 64, 320)])
 def test_layout_rejects_invalid_shapes(bits, K, N, G):
     assert oracle.packed_bytes(bits, K, N, G) == 0
+
+
+def test_gate_up_order_hand_derived():
+    # N = 32: two blocks of (8 gate, 8 up); N = 48: halves of 24, three blocks
+    assert oracle.gate_up_order(32).tolist() == (list(range(0, 8)) + list(range(16, 24))
+                                                 + list(range(8, 16)) + list(range(24, 32)))
+    assert oracle.gate_up_order(48).tolist() == (list(range(0, 8)) + list(range(24, 32)) + list(range(8, 16))
+                                                 + list(range(32, 40)) + list(range(16, 24)) + list(range(40, 48)))
+    o = oracle.gate_up_order(14336 * 2)
+    assert sorted(o.tolist()) == list(range(28672))          # a permutation
+    with pytest.raises(ValueError):
+        oracle.gate_up_order(40)
+
+
+@pytest.mark.parametrize("bits,K,N,G", [(4, 256, 48, 128), (4, 160, 112, 32), (8, 384, 32, 384), (8, 128, 80, 64)])
+def test_gate_up_repack_roundtrip(bits, K, N, G):
+    c = synth.make_inputs(bits, 1, K, N, G, seed=(71, bits, N))
+    packed = oracle.repack_gate_up(bits, c.qweight, c.qzeros, c.scales, K, N, G)
+    assert packed.size == oracle.packed_bytes(bits, K, N, G)
+    codes, zeros, scales = oracle.unrepack(bits, packed, K, N, G)
+    order = oracle.gate_up_order(N)
+    assert np.array_equal(codes, c.codes[:, order])
+    assert np.array_equal(zeros, c.zeros[:, order])
+    assert np.array_equal(scales, c.scales[:, order])
