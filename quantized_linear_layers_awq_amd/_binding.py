@@ -169,8 +169,10 @@ def tf_repack_w8(qweight, zeros, scales, K, N, G, packed=None, stream=None):
     return _repack(8, "tf_repack_w8", qweight, zeros, scales, K, N, G, packed, stream)
 
 
-# Split-K workspaces, one per (device, stream); zero-filled at allocation and
-# left zero-filled by every successful call, so they are reused as they are.
+# Split-K workspaces, one per (device, stream), grown on demand.  A split
+# launch writes every partial sum it later adds up, so what a buffer holds
+# between calls does not matter; calls on one stream run in order, so one
+# buffer per stream is never used by two calls at once.
 _workspaces: dict = {}
 
 
@@ -180,7 +182,11 @@ def _workspace(device: torch.device, stream_handle: int, nbytes: int):
     key = (device.index, stream_handle)
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+        # allocated on the launch stream: when a larger buffer replaces this
+        # one, torch's allocator reuses the old memory only for work ordered
+        # after the launches still reading it
+        with torch.cuda.stream(torch.cuda.ExternalStream(stream_handle, device=device)):
+            ws = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
         _workspaces[key] = ws
     return ws
 

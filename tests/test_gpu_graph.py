@@ -1,7 +1,8 @@
-"""The layer under HIP-graph capture: the kernels use no memset and keep their
-split-K counters self-resetting, so a captured graph replays correctly.  Each
-replay is checked bitwise against the eager result, with eager work and
-synchronisations between replays."""
+"""The layer under HIP-graph capture: the kernels use no memset and no
+counters (a split launch writes its partial sums and a second kernel adds
+them), so a captured graph replays correctly.  Each replay is checked bitwise
+against the eager result, with eager work and synchronisations between
+replays."""
 
 import numpy as np
 import pytest
