@@ -34,6 +34,8 @@
  *  - GEMV: 1 <= M <= 16.  GEMM: 1 <= M <= 2^30.  Both: K < 2^25 (the
  *    kernels' offsets within a row of x and within a packed block are
  *    32-bit; tf_packed_bytes_* and the repack take K up to 2^31).
+ *  - The [gate | up] calls (tf_repack_*_gate_up, tf_gemv_*_silu_mul) also
+ *    need N % 16 == 0: each half a whole number of 8-column runs.
  *  - Sizes are 64-bit; every dimension must be below 2^31.
  */
 #ifndef TILEFUSE_H
