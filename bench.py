@@ -312,9 +312,12 @@ def time_graphs(torch, q, lins, args, R):
     mean_us = [1e3 * e0.elapsed_time(e1) / n_prof for e0, e1 in evs]
 
     # the headline: K eager steps queued behind filler work, one event pair
-    queued_ms = time_queued(torch, lambda i: layer_pass(i % R), args.steps, enqueue_us=host_us_per_step(layer_pass, R))
+    enq_us = host_us_per_step(layer_pass, R)
+    queued_ms = time_queued(torch, lambda i: layer_pass(i % R), args.steps, enqueue_us=enq_us)
     for l, y0 in zip(lins, ref):
         assert torch.equal(l["y"], y0), "queued eager launches differ from the first result"
+    # spread: the same queued steps with an event between consecutive steps
+    step_pct = percentiles_us(time_queued_steps(torch, lambda i: layer_pass(i % R), args.steps, enq_us))
 
     # practical roof: a plain streaming read of the same packed buffers, one
     # launch per linear, in the same queued pattern
@@ -327,7 +330,7 @@ def time_graphs(torch, q, lins, args, R):
     read_ms = time_queued(torch, lambda i: read_pass(i % R), args.steps, enqueue_us=host_us_per_step(read_pass, R))
     del replicas, graphs
     return dict(graph_ms=ms_step, host_eager_ms=eager_ms, queued_ms=queued_ms, read_roof_ms=read_ms,
-                mean_us=mean_us)
+                mean_us=mean_us, step_pct_us=step_pct)
 
 
 def host_us_per_step(step, R, n=20):
@@ -372,6 +375,32 @@ def time_queued(torch, step, steps, enqueue_us):
     return ms
 
 
+def percentiles_us(ms_list):
+    """p10, p50 (median) and p90 of per-step times given in ms, in us."""
+    import numpy as np
+
+    a = np.asarray(ms_list) * 1e3
+    return dict(p10=round(float(np.percentile(a, 10)), 3), p50=round(float(np.percentile(a, 50)), 3),
+                p90=round(float(np.percentile(a, 90)), 3), n=int(a.size))
+
+
+def time_queued_steps(torch, step, steps, enqueue_us):
+    """Per-step times (ms) of `steps` steps queued as in time_queued, with a
+    HIP event on the launch stream between consecutive steps.  The events
+    add a little work of their own, so this gives the spread, while
+    time_queued (one event pair) gives the mean."""
+    torch.cuda.synchronize()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    keep = queue_filler(torch, ms=1.5 * steps * enqueue_us * 1e-3 + 2)
+    evs[0].record()
+    for i in range(steps):
+        step(i)
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    del keep
+    return [a.elapsed_time(b) for a, b in zip(evs[:-1], evs[1:])]
+
+
 def bench_gemv(torch, q, args):
     import synth
 
@@ -411,6 +440,7 @@ def bench_gemv(torch, q, args):
     return dict(
         value=value, ms_step=ms_f, replicas=R, layer_bytes=layer_bytes,
         graph_ms=tf_["graph_ms"], graph_gbs=gbs(tf_["graph_ms"]), host_eager_ms=tf_["host_eager_ms"],
+        step_pct_us=tf_["step_pct_us"],
         read_roof_gbs=round(read_roof, 1),
         per_launch=rows(fused, us_f),
         separate=None if args.no_separate else dict(
@@ -459,7 +489,16 @@ def bench_gemm(torch, q, args):
         torch.cuda.synchronize()
         us = 1e3 * e0.elapsed_time(e1) / args.gemm_iters
         fl = 2.0 * s["M"] * s["K"] * s["N"]
-        out.append(dict(M=s["M"], K=s["K"], N=s["N"], us=round(us, 2), tflops=round(fl / (us * 1e-6) / 1e12, 1)))
+        # spread: the same back-to-back launches with an event between them
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.gemm_iters + 1)]
+        evs[0].record()
+        for i in range(args.gemm_iters):
+            q.tf_gemm_w4a16(s["x"], s["packed"], s["K"], s["N"], s["G"], y=s["y"])
+            evs[i + 1].record()
+        torch.cuda.synchronize()
+        pct = percentiles_us([a.elapsed_time(b) for a, b in zip(evs[:-1], evs[1:])])
+        out.append(dict(M=s["M"], K=s["K"], N=s["N"], us=round(us, 2), tflops=round(fl / (us * 1e-6) / 1e12, 1),
+                        launch_pct_us=pct))
     tot_fl = sum(2.0 * o["M"] * o["K"] * o["N"] for o in out)
     tot_us = sum(o["us"] for o in out)
     tfs = tot_fl / (tot_us * 1e-6) / 1e12
@@ -803,6 +842,7 @@ def main():
                                    frac_of_read_roof=round(gv["value"] / gv["read_roof_gbs"], 4),
                                    graph_replay=dict(ms_per_step=round(gv["graph_ms"], 5), gbs=gv["graph_gbs"]),
                                    host_eager_ms_per_step=round(gv["host_eager_ms"], 4),
+                                   step_percentiles_us=gv["step_pct_us"],
                                    seven_separate_launches=gv["separate"])
     if args.only in ("all", "gemm"):
         line["gemm"] = bench_gemm(torch, q, args)
