@@ -119,10 +119,25 @@ def cpu_baseline(synth, oracle, M, budget_s=12.0):
         el = time.perf_counter() - t0
         if el >= budget_s:
             break
-    return dict(value=round(passes * total_bytes / el / 1e9, 3), unit="GB/s", cores=oracle.num_threads(),
+    cores = oracle.num_threads()
+    # per core: the 4096 x 4096 linear (config 0) on one thread, about 2 s
+    c0 = synth.make_case(0, 0, 1, keep_codes=False)
+    c0_bytes = algorithmic_bytes(4, 1, c0.K, c0.N, c0.G)
+    oracle.set_num_threads(1)
+    try:
+        n1, t1 = 0, time.perf_counter()
+        while time.perf_counter() - t1 < 2.0:
+            oracle.awq_linear(c0)
+            n1 += 1
+        el1 = time.perf_counter() - t1
+    finally:
+        oracle.set_num_threads(cores)
+    return dict(value=round(passes * total_bytes / el / 1e9, 3), unit="GB/s", cores=cores,
                 kind="oracle",
                 sample=f"{passes} full pass(es) over the 7 layer linears at M=1 "
-                       f"({passes * total_bytes / 1e6:.0f} MB of algorithmic bytes, {el:.1f} s)")
+                       f"({passes * total_bytes / 1e6:.0f} MB of algorithmic bytes, {el:.1f} s)",
+                per_core=dict(value=round(n1 * c0_bytes / el1 / 1e9, 4), unit="GB/s", cores=1,
+                              sample=f"{n1} pass(es) of the 4096x4096 W4 linear at M=1 on one thread ({el1:.1f} s)"))
 
 
 COPY_BYTES = 1 << 30

@@ -57,6 +57,8 @@ def lib():
         L.oracle_linear.argtypes = [P, I64, I64, P, I64, P]
         L.oracle_silu_mul.argtypes = [P, P, I64, P]
         L.oracle_num_threads.restype = ctypes.c_int
+        L.oracle_set_num_threads.argtypes = [ctypes.c_int]
+        L.oracle_set_num_threads.restype = None
         L.oracle_packed_bytes.argtypes = [ctypes.c_int, I64, I64, I64]
         L.oracle_packed_bytes.restype = ctypes.c_size_t
         L.oracle_repack.argtypes = [ctypes.c_int, P, P, P, I64, I64, I64, P]
@@ -73,6 +75,11 @@ def _p(a: np.ndarray):
 
 def _c(a, dtype):
     return np.ascontiguousarray(a, dtype=dtype)
+
+
+def set_num_threads(n: int) -> None:
+    """Threads the oracle's later parallel loops use."""
+    lib().oracle_set_num_threads(int(n))
 
 
 def num_threads() -> int:

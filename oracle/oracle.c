@@ -208,6 +208,17 @@ int oracle_num_threads(void)
 #endif
 }
 
+/* Threads later parallel loops use (the CPU baseline's per-core figure). */
+void oracle_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    if (n > 0)
+        omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /* ------------------------------------------------------------------ */
 /* Interleaved pre-tiled layout (format version 2).                    */
 /*                                                                    */
