@@ -55,7 +55,7 @@ typedef enum {
     TF_ERR_GROUP = 3,             /* G outside the rules above */
     TF_ERR_ALIGN = 4,             /* a pointer misses its required alignment */
     TF_ERR_BUFFER_TOO_SMALL = 5,  /* packed_bytes or ws_bytes below the size query */
-    TF_ERR_UNSUPPORTED = 6,       /* valid request this build does not implement */
+    TF_ERR_UNSUPPORTED = 6,       /* valid request the library does not implement */
     TF_ERR_HIP = 7                /* the HIP runtime reported a launch error */
 } tf_status;
 
