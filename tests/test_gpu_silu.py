@@ -154,3 +154,20 @@ def test_silu_mul_rejects_bad_shapes_before_launch():
     d2 = to_device(c2, torch)
     with pytest.raises(q.TileFuseError):
         q.tf_gemv_w4a16_silu_mul(x17, repack_gate_up(c2, d2, q), 256, 128, 128)
+
+
+@pytest.mark.parametrize("bits,M", [(4, 1), (4, 8), (8, 3)])
+def test_silu_mul_large_sums(bits, M):
+    """Scales raised by 2^12 put the sums in the thousands, so e^-g
+    overflows fp32 wherever g < -89: silu there is -0, never NaN."""
+    torch, q = gpu_or_skip()
+    c0 = synth.make_inputs(bits, M, 1024, 2 * 528, 128, seed=(72, bits, M))
+    scales = (c0.scales.astype(np.uint32) + (12 << 7)).astype(np.uint16)  # x 2^12, exact in bf16
+    c = synth.gen.pack_case(bits, c0.codes, c0.zeros, scales, c0.x, c0.G)
+    y = bf16_to_f64(_run(c, torch, q))
+    assert not np.any(np.isnan(y))
+    ref = oracle.awq_linear_silu_mul(c)
+    gate = oracle.awq_linear(c, cols=np.arange(c.N // 2))
+    assert np.any(gate < -89.0), "expected sums past the fp32 exponent range"
+    ok, ratio = within_tolerance(y, ref)
+    assert ok, f"worst error / bound = {ratio:.3f}"
