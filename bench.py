@@ -683,7 +683,8 @@ def bench_silu(torch, q, args):
     14336, group 128) followed by silu(gate) * up, at M = 1 ... 16: the GEMV
     then torch's silu and multiply (three launches) against the GEMV with the
     product in its epilogue (one launch), queued back to back over weight
-    replicas larger than twice the Infinity Cache; microseconds per call."""
+    replicas larger than twice the Infinity Cache; then the same at 2048 rows
+    with the GEMM, launched back to back; microseconds per call."""
     import numpy as np
 
     import synth
@@ -726,7 +727,29 @@ def bench_silu(torch, q, args):
                              gbs=round(algorithmic_bytes(4, M, K, N, G) / (ms * 1e-3) / 1e9, 1))
         out.append(row)
         del x, yg, o
-    del reps, preps, plain, paired
+    # prefill: 2048 rows, launches back to back (MFMA-bound, no replicas needed)
+    M = 2048
+    x = torch.randn((M, K), device="cuda:0").to(torch.bfloat16)
+    yg = torch.empty((M, N), dtype=torch.bfloat16, device="cuda:0")
+    o = torch.empty((M, n2), dtype=torch.bfloat16, device="cuda:0")
+    steps = (("gemm_then_torch_silu_mul", lambda: (q.tf_gemm_w4a16(x, plain, K, N, G, y=yg),
+                                                   torch.mul(F.silu(yg[:, :n2]), yg[:, n2:], out=o))),
+             ("fused_epilogue", lambda: q.tf_gemm_w4a16_silu_mul(x, paired, K, N, G, y=o)))
+    row = dict(M=M)
+    for name, step in steps:
+        for _ in range(3):
+            step()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            step()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / 10 * 1e3
+        row[name] = dict(us=round(us, 2), tflops=round(2.0 * M * K * N / (us * 1e-6) / 1e12, 1))
+    out.append(row)
+    del x, yg, o, reps, preps, plain, paired
     torch.cuda.empty_cache()
     return out
 

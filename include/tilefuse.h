@@ -34,8 +34,9 @@
  *  - GEMV: 1 <= M <= 16.  GEMM: 1 <= M <= 2^30.  Both: K < 2^25 (the
  *    kernels' offsets within a row of x and within a packed block are
  *    32-bit; tf_packed_bytes_* and the repack take K up to 2^31).
- *  - The [gate | up] calls (tf_repack_*_gate_up, tf_gemv_*_silu_mul) also
- *    need N % 16 == 0: each half a whole number of 8-column runs.
+ *  - The [gate | up] calls (tf_repack_*_gate_up, tf_gemv_*_silu_mul,
+ *    tf_gemm_*_silu_mul) also need N % 16 == 0: each half a whole number of
+ *    8-column runs.
  *  - Sizes are 64-bit; every dimension must be below 2^31.
  */
 #ifndef TILEFUSE_H
@@ -174,6 +175,20 @@ int tf_gemv_w4a16_silu_mul(const uint16_t *x, const void *packed, size_t packed_
                            int64_t M, int64_t K, int64_t N, int64_t G,
                            void *workspace, size_t ws_bytes, void *stream);
 int tf_gemv_w8a16_silu_mul(const uint16_t *x, const void *packed, size_t packed_bytes, uint16_t *y,
+                           int64_t M, int64_t K, int64_t N, int64_t G,
+                           void *workspace, size_t ws_bytes, void *stream);
+
+/* Prefill GEMM over the same fused [gate | up] layer with the SiLU product in
+ * its epilogue: arguments, output and errors as tf_gemv_*_silu_mul, for any
+ * 1 <= M <= 2^30.  The call runs the kernels and launch plan tf_gemm_* runs
+ * for the same (M, K, N, G), so it needs the workspace
+ * tf_workspace_bytes(bits, 1, M, K, N, G) reports; with K split, the
+ * product is applied after the ranges are added.  The [M][N] gate/up
+ * output is never written to memory. */
+int tf_gemm_w4a16_silu_mul(const uint16_t *x, const void *packed, size_t packed_bytes, uint16_t *y,
+                           int64_t M, int64_t K, int64_t N, int64_t G,
+                           void *workspace, size_t ws_bytes, void *stream);
+int tf_gemm_w8a16_silu_mul(const uint16_t *x, const void *packed, size_t packed_bytes, uint16_t *y,
                            int64_t M, int64_t K, int64_t N, int64_t G,
                            void *workspace, size_t ws_bytes, void *stream);
 

@@ -21,7 +21,9 @@ from ._binding import (  # noqa: F401
     tf_gemm_set_planning_cus,
     tf_gemm_set_route,
     tf_gemm_w4a16,
+    tf_gemm_w4a16_silu_mul,
     tf_gemm_w8a16,
+    tf_gemm_w8a16_silu_mul,
     tf_gemv_w4a16,
     tf_gemv_w4a16_silu_mul,
     tf_gemv_w8a16,

@@ -63,7 +63,7 @@ def load_library():
         for n in ("tf_gemv_w4a16", "tf_gemv_w8a16", "tf_gemm_w4a16", "tf_gemm_w8a16"):
             getattr(L, n).argtypes = [P, P, SZ, P, I64, I64, I64, I64, P, SZ, P]
             getattr(L, n).restype = I
-        for n in ("tf_gemv_w4a16_silu_mul", "tf_gemv_w8a16_silu_mul"):
+        for n in ("tf_gemv_w4a16_silu_mul", "tf_gemv_w8a16_silu_mul", "tf_gemm_w4a16_silu_mul", "tf_gemm_w8a16_silu_mul"):
             getattr(L, n).argtypes = [P, P, SZ, P, I64, I64, I64, I64, P, SZ, P]
             getattr(L, n).restype = I
         for n in ("tf_dequant_w4_f32", "tf_dequant_w8_f32"):
@@ -230,7 +230,7 @@ def tf_gemm_w8a16(x, packed, K, N, G, y=None, workspace=None, stream=None):
     return _linear(8, True, "tf_gemm_w8a16", x, packed, K, N, G, y, workspace, stream)
 
 
-def _silu_mul(bits, fn, x, packed, K, N, G, y, workspace, stream):
+def _silu_mul(bits, fn, x, packed, K, N, G, y, workspace, stream, is_gemm=False):
     L = load_library()
     _need(x, "x", 2)
     _need(packed, "packed", 1)
@@ -243,12 +243,22 @@ def _silu_mul(bits, fn, x, packed, K, N, G, y, workspace, stream):
     if y.numel() < M * (N // 2):
         raise ValueError(f"{fn}: y holds fewer than M*N/2 elements")
     sh = _stream(x, stream)
-    need = int(L.tf_workspace_bytes(bits, 0, M, K, N, G))
+    need = int(L.tf_workspace_bytes(bits, int(is_gemm), M, K, N, G))
     if workspace is None:
         workspace = _workspace(x.device, sh, need)
     ws_ptr, ws_bytes = (None, 0) if workspace is None else (_ptr(workspace), workspace.numel() * workspace.element_size())
     _check(getattr(L, fn)(_ptr(x), _ptr(packed), packed.numel(), _ptr(y), M, K, N, G, ws_ptr, ws_bytes, sh), fn)
     return y
+
+
+def tf_gemm_w4a16_silu_mul(x, packed, K, N, G, y=None, workspace=None, stream=None):
+    """y[M][N/2] = silu(x Wg) * (x Wu) (bf16) for a W4 [gate | up] layer of N
+    columns packed by tf_repack_w4_gate_up, x [M][K] bf16, any M."""
+    return _silu_mul(4, "tf_gemm_w4a16_silu_mul", x, packed, K, N, G, y, workspace, stream, is_gemm=True)
+
+
+def tf_gemm_w8a16_silu_mul(x, packed, K, N, G, y=None, workspace=None, stream=None):
+    return _silu_mul(8, "tf_gemm_w8a16_silu_mul", x, packed, K, N, G, y, workspace, stream, is_gemm=True)
 
 
 def tf_gemv_w4a16_silu_mul(x, packed, K, N, G, y=None, workspace=None, stream=None):

@@ -111,12 +111,13 @@ int linear(int bits, bool is_gemm, const uint16_t *x, const void *packed, size_t
     return e == hipSuccess ? TF_OK : TF_ERR_HIP;
 }
 
-// [gate | up] GEMV with the SiLU product over a buffer from repack(gate_up)
-// (the kernel for up to 16 rows only).
-int linear_silu_mul(int bits, const uint16_t *x, const void *packed, size_t nbytes, uint16_t *y, int64_t M, int64_t K,
-                    int64_t N, int64_t G, void *ws, size_t ws_bytes, void *stream)
+// [gate | up] GEMV or GEMM with the SiLU product over a buffer from
+// repack(gate_up): the kernels, plans and workspace of the plain call of the
+// same shape, with the product in the epilogue (or in the split sum).
+int linear_silu_mul(int bits, bool is_gemm, const uint16_t *x, const void *packed, size_t nbytes, uint16_t *y,
+                    int64_t M, int64_t K, int64_t N, int64_t G, void *ws, size_t ws_bytes, void *stream)
 {
-    if (M < 0 || M > 16)
+    if (M < 0 || M > (is_gemm ? (int64_t(1) << 30) : 16))
         return TF_ERR_SHAPE;
     if (int st = check_kng(bits, K, N, G))
         return st;
@@ -132,8 +133,8 @@ int linear_silu_mul(int bits, const uint16_t *x, const void *packed, size_t nbyt
     const Layout lay = Layout::make(bits, K, N, G);
     if (nbytes < (size_t)lay.total_bytes())
         return TF_ERR_BUFFER_TOO_SMALL;
-    // the kernel and its K split are the plain GEMV's for this shape
-    const size_t need = workspace_bytes(bits, 0, M, K, N, G);
+    // the kernel and its K split are the plain call's for this shape
+    const size_t need = workspace_bytes(bits, is_gemm, M, K, N, G);
     if (need) {
         if (!ws)
             return TF_ERR_NULL;
@@ -142,9 +143,12 @@ int linear_silu_mul(int bits, const uint16_t *x, const void *packed, size_t nbyt
         if (ws_bytes < need)
             return TF_ERR_BUFFER_TOO_SMALL;
     }
-    return tf::launch_gemv_silu_mul(bits, x, packed, y, M, lay, ws, static_cast<hipStream_t>(stream)) == hipSuccess
-               ? TF_OK
-               : TF_ERR_HIP;
+    hipError_t e;
+    if (is_gemm && !tf::gemm_uses_gemv(M))
+        e = tf::launch_gemm(bits, x, packed, y, M, lay, ws, static_cast<hipStream_t>(stream), tf::kActSiluMul);
+    else
+        e = tf::launch_gemv_silu_mul(bits, x, packed, y, M, lay, ws, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? TF_OK : TF_ERR_HIP;
 }
 
 int dequant(int bits, const void *packed, size_t nbytes, float *w, int64_t K, int64_t N, int64_t G, void *stream)
@@ -245,13 +249,25 @@ int tf_gemm_w8a16(const uint16_t *x, const void *packed, size_t nbytes, uint16_t
 int tf_gemv_w4a16_silu_mul(const uint16_t *x, const void *packed, size_t nbytes, uint16_t *y, int64_t M, int64_t K,
                            int64_t N, int64_t G, void *ws, size_t ws_bytes, void *stream)
 {
-    return linear_silu_mul(4, x, packed, nbytes, y, M, K, N, G, ws, ws_bytes, stream);
+    return linear_silu_mul(4, false, x, packed, nbytes, y, M, K, N, G, ws, ws_bytes, stream);
 }
 
 int tf_gemv_w8a16_silu_mul(const uint16_t *x, const void *packed, size_t nbytes, uint16_t *y, int64_t M, int64_t K,
                            int64_t N, int64_t G, void *ws, size_t ws_bytes, void *stream)
 {
-    return linear_silu_mul(8, x, packed, nbytes, y, M, K, N, G, ws, ws_bytes, stream);
+    return linear_silu_mul(8, false, x, packed, nbytes, y, M, K, N, G, ws, ws_bytes, stream);
+}
+
+int tf_gemm_w4a16_silu_mul(const uint16_t *x, const void *packed, size_t nbytes, uint16_t *y, int64_t M, int64_t K,
+                           int64_t N, int64_t G, void *ws, size_t ws_bytes, void *stream)
+{
+    return linear_silu_mul(4, true, x, packed, nbytes, y, M, K, N, G, ws, ws_bytes, stream);
+}
+
+int tf_gemm_w8a16_silu_mul(const uint16_t *x, const void *packed, size_t nbytes, uint16_t *y, int64_t M, int64_t K,
+                           int64_t N, int64_t G, void *ws, size_t ws_bytes, void *stream)
+{
+    return linear_silu_mul(8, true, x, packed, nbytes, y, M, K, N, G, ws, ws_bytes, stream);
 }
 
 int tf_dequant_w4_f32(const void *packed, size_t nbytes, float *w, int64_t K, int64_t N, int64_t G, void *stream)

@@ -185,7 +185,7 @@ template <int I, int N, typename F> __device__ __forceinline__ void static_for(F
 // width 64 WN, starting at output column col0.  With one range the output is
 // y (bf16); with several, each range writes its fp32 partial sums to
 // ws[range][M][N] and a second kernel adds them.
-template <int BITS, int kMode, int WN, int BM>
+template <int BITS, int kMode, int WN, int BM, int ACT = kActNone>
 __global__ __launch_bounds__(kGThreads, 1) void gemm_kernel(const uint16_t *__restrict__ x,
                                                             const uint8_t *__restrict__ packed,
                                                             uint16_t *__restrict__ y, Layout lay, int64_t M,
@@ -696,11 +696,26 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_kernel(const uint16_t *__re
                 const int64_t row = m0 + 32 * MI * wm + 32 * i + 8 * (e >> 2) + 4 * h32 + (e & 3);
                 const float v = kMode == kGWhole ? acc[0][i][j][e] * s_last[0][j]
                                                  : fmaf(acc[0][i][j][e], s_last[0][j], acc[1][i][j][e] * s_last[1][j]);
-                if (row < M) {
-                    if (splits > 1)
-                        __builtin_nontemporal_store(v, ws + ((int64_t)split * M + row) * L.N + col);
-                    else
-                        y[row * L.N + col] = f32_to_bf16_bits(v);
+                if constexpr (ACT == kActNone) {
+                    if (row < M) {
+                        if (splits > 1)
+                            __builtin_nontemporal_store(v, ws + ((int64_t)split * M + row) * L.N + col);
+                        else
+                            y[row * L.N + col] = f32_to_bf16_bits(v);
+                    }
+                } else {
+                    // [gate | up] packed by tf_repack_*_gate_up (N % 16 == 0):
+                    // column c < 8 of a 16-column block is gate, c + 8 (lane
+                    // l32 ^ 8, same rows) the matching up column.  Lanes of
+                    // columns past N skip in whole 16-column groups.
+                    const float u = __shfl_xor(v, 8);
+                    if (row < M) {
+                        if (splits > 1)
+                            __builtin_nontemporal_store(v, ws + ((int64_t)split * M + row) * L.N + col);
+                        else if ((col & 8) == 0)
+                            y[row * (L.N >> 1) + ((col >> 4) << 3) + (col & 7)] =
+                                f32_to_bf16_bits(v / (1.f + expf(-v)) * u);
+                    }
                 }
             }
     }
@@ -708,11 +723,11 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_kernel(const uint16_t *__re
 
 // The kernel needs more than the default 64 KiB of dynamic LDS; raise the
 // limit once per instantiation.
-template <int BITS, int kMode, int WN, int BM>
+template <int BITS, int kMode, int WN, int BM, int ACT>
 static void launch_mode(int64_t wgs, int m_tiles, int64_t col0, const GemmPlan &plan, hipStream_t stream,
                         const uint16_t *x, const uint8_t *pk, uint16_t *y, const Layout &lay, int64_t M, float *ws)
 {
-    auto kern = &gemm_kernel<BITS, kMode, WN, BM>;
+    auto kern = &gemm_kernel<BITS, kMode, WN, BM, ACT>;
     static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize,
                                                        gemm_lds(BITS, WN, BM));
@@ -877,8 +892,10 @@ int64_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t G)
 }
 
 hipError_t launch_gemm(int bits, const uint16_t *x, const void *packed, uint16_t *y, int64_t M, const Layout &lay,
-                       void *workspace, hipStream_t stream)
+                       void *workspace, hipStream_t stream, int act)
 {
+    if (act != kActNone && lay.N % kBlockCols)
+        return hipErrorInvalidValue;
     const GemmPlan plan = plan_gemm(M, lay.N, lay.K, lay.G, planning_cus());
     float *ws = plan.splits > 1 ? static_cast<float *>(workspace) : nullptr;
     const uint8_t *pk = static_cast<const uint8_t *>(packed);
@@ -887,15 +904,22 @@ hipError_t launch_gemm(int bits, const uint16_t *x, const void *packed, uint16_t
                      : lay.G == 32            ? kGSplit32
                                               : kGSplit64;
     const int mt = (int)plan.m_tiles;
-    auto go = [&](auto bits_c, auto wn_c, auto bm_c, int64_t n_cols, int64_t col0) {
+    auto go_act = [&](auto bits_c, auto wn_c, auto bm_c, auto act_c, int64_t n_cols, int64_t col0) {
         constexpr int B = decltype(bits_c)::value, WN = decltype(wn_c)::value, BM = decltype(bm_c)::value;
+        constexpr int A = decltype(act_c)::value;
         const int64_t wgs = plan.m_tiles * n_cols * plan.splits;
         switch (mode) {
-        case kGOneTile: launch_mode<B, kGOneTile, WN, BM>(wgs, mt, col0, plan, stream, x, pk, y, lay, M, ws); break;
-        case kGWhole: launch_mode<B, kGWhole, WN, BM>(wgs, mt, col0, plan, stream, x, pk, y, lay, M, ws); break;
-        case kGSplit32: launch_mode<B, kGSplit32, WN, BM>(wgs, mt, col0, plan, stream, x, pk, y, lay, M, ws); break;
-        default: launch_mode<B, kGSplit64, WN, BM>(wgs, mt, col0, plan, stream, x, pk, y, lay, M, ws); break;
+        case kGOneTile: launch_mode<B, kGOneTile, WN, BM, A>(wgs, mt, col0, plan, stream, x, pk, y, lay, M, ws); break;
+        case kGWhole: launch_mode<B, kGWhole, WN, BM, A>(wgs, mt, col0, plan, stream, x, pk, y, lay, M, ws); break;
+        case kGSplit32: launch_mode<B, kGSplit32, WN, BM, A>(wgs, mt, col0, plan, stream, x, pk, y, lay, M, ws); break;
+        default: launch_mode<B, kGSplit64, WN, BM, A>(wgs, mt, col0, plan, stream, x, pk, y, lay, M, ws); break;
         }
+    };
+    auto go = [&](auto bits_c, auto wn_c, auto bm_c, int64_t n_cols, int64_t col0) {
+        if (act == kActSiluMul)
+            go_act(bits_c, wn_c, bm_c, ic<kActSiluMul>{}, n_cols, col0);
+        else
+            go_act(bits_c, wn_c, bm_c, ic<kActNone>{}, n_cols, col0);
     };
     auto both = [&](auto bits_c) {
         if (plan.rows != kGBM) { // short tiles: 128 columns only
@@ -911,8 +935,12 @@ hipError_t launch_gemm(int bits, const uint16_t *x, const void *packed, uint16_t
         both(ic<4>{});
     else
         both(ic<8>{});
-    if (plan.splits > 1)
-        launch_splitk_sum(ws, (int)plan.splits, M * lay.N, y, stream);
+    if (plan.splits > 1) {
+        if (act == kActSiluMul)
+            launch_splitk_sum_silu(ws, (int)plan.splits, M, lay.N, y, stream);
+        else
+            launch_splitk_sum(ws, (int)plan.splits, M * lay.N, y, stream);
+    }
     return hipGetLastError();
 }
 

@@ -936,23 +936,18 @@ static void launch_mid_bits(dim3 grid, const MidChunks &ch, hipStream_t stream, 
                             uint16_t *y, const Layout &lay, int M, float *ws)
 {
     // M <= 16: one row chunk, M <= 32: two, depth 8; above: four, depth 4
-    // (the SiLU product is a decode epilogue: at most 16 rows)
     if (mid_mt(M) == 1)
         launch_mid_mt<BITS, 1, 8, ACT>(grid, ch, stream, x, pk, y, lay, M, ws);
-    else if constexpr (ACT == kActNone) {
-        if (mid_mt(M) == 2)
-            launch_mid_mt<BITS, 2, 8, ACT>(grid, ch, stream, x, pk, y, lay, M, ws);
-        else
-            launch_mid_mt<BITS, 4, 4, ACT>(grid, ch, stream, x, pk, y, lay, M, ws);
-    }
+    else if (mid_mt(M) == 2)
+        launch_mid_mt<BITS, 2, 8, ACT>(grid, ch, stream, x, pk, y, lay, M, ws);
+    else
+        launch_mid_mt<BITS, 4, 4, ACT>(grid, ch, stream, x, pk, y, lay, M, ws);
 }
 
 template <int ACT = kActNone>
 static hipError_t launch_gemv_mid(int bits, const uint16_t *x, const uint8_t *pk, uint16_t *y, int64_t M,
                                   const Layout &lay, void *workspace, hipStream_t stream)
 {
-    if (ACT != kActNone && M > 16)
-        return hipErrorInvalidValue;
     int64_t split_tiles = 0;
     const int64_t splits = gemv_splits(lay, M, planning_cus(), &split_tiles);
     const MidChunks ch = plan_mid(bits, lay, M, split_tiles);
@@ -972,8 +967,7 @@ static hipError_t launch_gemv_mid(int bits, const uint16_t *x, const uint8_t *pk
         if constexpr (ACT == kActNone)
             launch_splitk_sum(ws, (int)splits, M * lay.N, y, stream);
         else
-            splitk_sum_silu_kernel<<<(unsigned)((M * (lay.N / 2) + 255) / 256), 256, 0, stream>>>(ws, (int)splits, M,
-                                                                                                lay.N, y);
+            launch_splitk_sum_silu(ws, (int)splits, M, lay.N, y, stream);
     }
     return hipGetLastError();
 }
@@ -995,12 +989,17 @@ hipError_t launch_gemv(int bits, const uint16_t *x, const void *packed, uint16_t
     return hipGetLastError();
 }
 
+void launch_splitk_sum_silu(const float *ws, int splits, int64_t M, int64_t N, uint16_t *y, hipStream_t stream)
+{
+    splitk_sum_silu_kernel<<<(unsigned)((M * (N / 2) + 255) / 256), 256, 0, stream>>>(ws, splits, M, N, y);
+}
+
 // The gate/up GEMV with the SiLU product: the kernel the plain GEMV of the
 // same shape runs, on its grid (each block pairs its own columns).
 hipError_t launch_gemv_silu_mul(int bits, const uint16_t *x, const void *packed, uint16_t *y, int64_t M,
                                 const Layout &lay, void *workspace, hipStream_t stream)
 {
-    if (lay.N % kBlockCols || M < 1 || M > 16)
+    if (lay.N % kBlockCols || M < 1 || M > kGemvKernelMaxM)
         return hipErrorInvalidValue;
     if (use_mid(lay, M, planning_cus()))
         return launch_gemv_mid<kActSiluMul>(bits, x, static_cast<const uint8_t *>(packed), y, M, lay, workspace,

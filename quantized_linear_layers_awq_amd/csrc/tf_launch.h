@@ -31,10 +31,13 @@ hipError_t launch_gemv(int bits, const uint16_t *x, const void *packed, uint16_t
 constexpr int kActNone = 0, kActSiluMul = 1;
 // y[m][8 j + c] = silu(g) * u with g, u the fp32 sums of columns c and c + 8
 // of block j of a [gate | up] layer packed with pair_half = N/2 (N % 16 ==
-// 0), 1 <= M <= 16; y is [M][N/2].  Same kernel choice, and so the same
-// workspace (gemv_workspace_bytes), as launch_gemv of that shape.
+// 0), 1 <= M <= kGemvKernelMaxM; y is [M][N/2].  Same kernel choice, and so
+// the same workspace (gemv_workspace_bytes), as launch_gemv of that shape.
 hipError_t launch_gemv_silu_mul(int bits, const uint16_t *x, const void *packed, uint16_t *y, int64_t M,
                                 const Layout &lay, void *workspace, hipStream_t stream);
+// Sum of a SiLU-product launch's K ranges: y[m][8 j + c] = silu(g) * u from
+// the in-order sums of the partials ws[s][m][16 j + c] and ws[s][m][16 j + c + 8].
+void launch_splitk_sum_silu(const float *ws, int splits, int64_t M, int64_t N, uint16_t *y, hipStream_t stream);
 // y = bf16(sum of the splits' fp32 partials ws[s][mn]), added in split order;
 // 2 <= splits <= 16 (both plans stay within that).
 void launch_splitk_sum(const float *ws, int splits, int64_t mn, uint16_t *y, hipStream_t stream);
@@ -61,8 +64,10 @@ int64_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t G);
 // be forced for tests: 0 automatic, 1 tiled GEMM, 2 GEMV kernel where M <= 64.
 bool gemm_uses_gemv(int64_t M);
 void set_gemm_route(int route);
+// act = kActSiluMul: a [gate | up] layer packed with pair_half = N/2, y is
+// [M][N/2] = silu(gate) * up (as launch_gemv_silu_mul).
 hipError_t launch_gemm(int bits, const uint16_t *x, const void *packed, uint16_t *y, int64_t M, const Layout &lay,
-                       void *workspace, hipStream_t stream);
+                       void *workspace, hipStream_t stream, int act = kActNone);
 
 // Measurement probes (not on the hot path).
 hipError_t launch_probe_read(const void *buf, uint64_t bytes, uint32_t *sink, hipStream_t stream);

@@ -343,6 +343,11 @@ class TestValidation:
         need = lib.tf_packed_bytes_w4(256, 128, 128)
         assert self._silu(lib, nbytes=need - 1) == TF_ERR_BUFFER_TOO_SMALL
         assert self._silu(lib, M=0, x=None, y=None, packed=None) == TF_OK
+        # the prefill entry point: any M, same shape rules
+        assert self._silu(lib, M=17, fn="tf_gemm_w4a16_silu_mul", nbytes=10) == TF_ERR_BUFFER_TOO_SMALL
+        assert self._silu(lib, M=17) == TF_ERR_SHAPE                      # the GEMV call stops at 16 rows
+        assert self._silu(lib, M=2048, N=104, fn="tf_gemm_w4a16_silu_mul") == TF_ERR_SHAPE
+        assert self._silu(lib, M=2**30 + 1, fn="tf_gemm_w8a16_silu_mul") == TF_ERR_SHAPE
         # a shape the plain GEMV splits over K: the same workspace rules
         shape = dict(M=16, K=8192, N=8192, G=8192, fn="tf_gemv_w8a16_silu_mul")
         need = lib.tf_workspace_bytes(8, 0, 16, 8192, 8192, 8192)

@@ -171,3 +171,78 @@ def test_silu_mul_large_sums(bits, M):
     assert np.any(gate < -89.0), "expected sums past the fp32 exponent range"
     ok, ratio = within_tolerance(y, ref)
     assert ok, f"worst error / bound = {ratio:.3f}"
+
+
+# tf_gemm_*_silu_mul: every route of the plain GEMM call of the same shape.
+# (bits, M, K, N, G, cus, route): the 16-row-chunk kernel at 17..64 rows (one
+# to four row chunks, K split or not), 128-row tiles (forced at 64 rows, and
+# at 96 and 100) with K split, 256-row tiles with K split, as wide + narrow
+# launches, and as narrow tiles only
+GEMM_SILU = [
+    (4, 17, 1024, 1056, 128, 0, 0), (4, 40, 2048, 2080, 64, 0, 0), (8, 64, 1024, 528, 1024, 0, 0),
+    (4, 64, 1024, 1056, 128, 0, 1), (4, 100, 4096, 1024, 128, 0, 0), (4, 96, 4096, 256, 512, 4096, 0),
+    (4, 300, 1024, 2080, 128, 0, 0), (4, 520, 512, 4096, 32, 40, 0), (8, 257, 384, 1040, 384, 0, 0),
+]
+
+
+@pytest.mark.parametrize("shape", GEMM_SILU, ids=[str(s) for s in GEMM_SILU])
+def test_gemm_silu_mul_routes(shape):
+    torch, q = gpu_or_skip()
+    from gpu_harness import gemm_route
+
+    bits, M, K, N, G, cus, route = shape
+    print(f"gemm silu_mul shape={shape}", flush=True)
+    c = synth.make_inputs(bits, M, K, N, G, seed=(73, bits, M, K), keep_codes=False)
+    d = to_device(c, torch)
+    p = repack_gate_up(c, d, q)
+    fn = q.tf_gemm_w4a16_silu_mul if bits == 4 else q.tf_gemm_w8a16_silu_mul
+    with planning_cus(q, cus), gemm_route(q, route):
+        y = fn(d["x"], p, K, N, G)
+    torch.cuda.synchronize()
+    assert tuple(y.shape) == (M, N // 2)
+    rows = sample_indices(M, 48, seed=74)
+    cols = sample_indices(N // 2, 384, seed=75)
+    ref = oracle.awq_linear_silu_mul(c, cols=cols, rows=rows)
+    ok, ratio = within_tolerance(bf16_to_f64(y)[rows][:, cols], ref)
+    assert ok, f"worst error / bound = {ratio:.3f}"
+
+
+def test_gemm_silu_mul_plans_cover_the_routes():
+    """The shapes above reach the plans they are meant to (host-side plan)."""
+    torch, q = gpu_or_skip()
+    assert q.tf_gemm_plan(4, 96, 4096, 256, 512, 4096)[3] > 1               # K split
+    assert q.tf_gemm_plan(4, 300, 1024, 2080, 128, 256)[3] > 1              # K split, 256-row tiles
+    wide, narrow = q.tf_gemm_plan(4, 520, 512, 4096, 32, 40)[1:3]
+    assert wide > 0 and narrow > 0                                          # wide + narrow launches
+    assert q.tf_gemm_plan(8, 257, 384, 1040, 384, 256)[1:3] == (0, 17)      # narrow tiles only
+    assert q.tf_gemm_plan(4, 100, 4096, 1024, 128, 256)[6] == 128           # 128-row tiles
+    assert q.tf_gemm_plan(4, 40, 2048, 2080, 64, 256)[5] == 1               # the GEMV kernel
+
+
+def test_gemm_silu_mul_decoder_prefill():
+    """The decoder layer's gate/up at 2048 rows (K = 4096, 2 x 14336 columns:
+    seven rounds of 256 x 128 tiles), on sampled rows and columns."""
+    torch, q = gpu_or_skip()
+    c = synth.make_inputs(4, 2048, 4096, 28672, 128, seed=(76,), keep_codes=False)
+    d = to_device(c, torch)
+    y = q.tf_gemm_w4a16_silu_mul(d["x"], repack_gate_up(c, d, q), 4096, 28672, 128)
+    torch.cuda.synchronize()
+    rows = sample_indices(2048, 24, seed=77)
+    cols = sample_indices(14336, 256, seed=78)
+    ok, ratio = within_tolerance(bf16_to_f64(y)[rows][:, cols], oracle.awq_linear_silu_mul(c, cols=cols, rows=rows))
+    assert ok, f"worst error / bound = {ratio:.3f}"
+
+
+@pytest.mark.parametrize("M,cus", [(300, 0), (96, 4096), (40, 0)])
+def test_gemm_silu_mul_zero_gate_gives_zero(M, cus):
+    torch, q = gpu_or_skip()
+    K, N, G = 4096, 1056, 512
+    c0 = synth.make_inputs(4, M, K, N, G, seed=(79, M))
+    codes = c0.codes.copy()
+    codes[:, : N // 2] = c0.zeros[np.arange(K) // G][:, : N // 2]
+    c = synth.gen.pack_case(4, codes, c0.zeros, c0.scales, c0.x, G)
+    d = to_device(c, torch)
+    with planning_cus(q, cus):
+        y = q.tf_gemm_w4a16_silu_mul(d["x"], repack_gate_up(c, d, q), K, N, G)
+    torch.cuda.synchronize()
+    assert np.all(bf16_to_f64(y) == 0.0)
