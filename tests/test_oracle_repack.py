@@ -110,3 +110,14 @@ def test_gate_up_repack_roundtrip(bits, K, N, G):
     assert np.array_equal(codes, c.codes[:, order])
     assert np.array_equal(zeros, c.zeros[:, order])
     assert np.array_equal(scales, c.scales[:, order])
+
+
+@pytest.mark.parametrize("bits,K,N,G", [(4, 256, 48, 128), (8, 128, 80, 64), (4, 96, 112, 32)])
+def test_gate_up_repack_equals_repack_of_permuted_codes(bits, K, N, G):
+    """The word shortcut of repack_gate_up against a checkpoint rebuilt from
+    column-permuted codes, zeros and scales by the generator's own packer."""
+    c = synth.make_inputs(bits, 1, K, N, G, seed=(81, bits, N))
+    order = oracle.gate_up_order(N)
+    cp = synth.gen.pack_case(bits, c.codes[:, order], c.zeros[:, order], c.scales[:, order], c.x, G)
+    want = oracle.repack(bits, cp.qweight, cp.qzeros, cp.scales, K, N, G)
+    assert np.array_equal(oracle.repack_gate_up(bits, c.qweight, c.qzeros, c.scales, K, N, G), want)
