@@ -707,7 +707,9 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_kernel(const uint16_t *__re
                     // [gate | up] packed by tf_repack_*_gate_up (N % 16 == 0):
                     // column c < 8 of a 16-column block is gate, c + 8 (lane
                     // l32 ^ 8, same rows) the matching up column.  Lanes of
-                    // columns past N skip in whole 16-column groups.
+                    // columns past N skip in whole 16-column groups.  SiLU as
+                    // in the GEMV epilogue: v / (1 + e^-v), -0 where e^-v
+                    // overflows.
                     const float u = __shfl_xor(v, 8);
                     if (row < M) {
                         if (splits > 1)
