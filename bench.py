@@ -48,7 +48,11 @@ def algorithmic_bytes(bits, M, K, N, G):
     return K * N * bits // 8 + (K // G) * N * (bits // 8 if bits == 8 else 0.5) + (K // G) * N * 2 + 2 * M * (K + N)
 
 
-GEMV_SOURCES = ("gemv.hip", "tf_common.h", "tf_launch.h")
+GEMV_SOURCES = ("gemv.hip", "tf_common.h", "tf_launch.h", "tf_operands.h")
+# the dominant kernel of the headline step as a kernel trace names it: the
+# GEMV kernel for W4, one k-tile per group (mode 2), ring depth D, BPW blocks
+# per workgroup, plain bf16 store (epilogue 0)
+GEMV_TRACE_NAME = "gemv_kernel<4, 2, {depth}, {bpw}, 0>"
 
 
 def kernel_source_hash():
@@ -71,10 +75,13 @@ def parse():
     p.add_argument("--only", choices=["all", "gemv", "gemm", "copy", "configs", "crossover", "energy", "silu"],
                    default="all",
                    help="restrict the run (profiling passes); 'copy' runs the plain-copy calibration kernel")
+    p.add_argument("--counters-kernel", default=GEMV_TRACE_NAME.format(depth=4, bpw=1),
+                   help="kernel name (as traced) whose dispatches --counters-from averages")
     p.add_argument("--counters-from", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
                    help="no GPU: read four rocprofv3 --pmc output directories (FETCH_SIZE and WRITE_SIZE over "
                         "'--only gemv', then over '--only copy') and write the per-launch HBM traffic file")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--no-energy", action="store_true", help="skip the energy-per-call leg")
     p.add_argument("--no-configs", action="store_true", help="skip the per-config throughput table")
     p.add_argument("--no-separate", action="store_true",
                    help="time only the fused four-launch layer (counter passes: every GEMV dispatch is one "
@@ -184,11 +191,12 @@ def _per_dispatch_kib(path, counter, match):
     return sum(per.values()) / len(per), len(per)
 
 
-def write_counters(dirs):
-    """Per-launch HBM traffic of the GEMV layer from two --pmc passes, each
-    scaled by the same counter's reading on the plain copy kernel."""
+def write_counters(dirs, kernel):
+    """Per-launch HBM traffic of the dominant GEMV kernel (its dispatches in
+    the layer step) from two --pmc passes, each scaled by the same counter's
+    reading on the plain copy kernel."""
     fetch_dir, write_dir, cfetch_dir, cwrite_dir = dirs
-    is_gemv = lambda n: "gemv_kernel" in n
+    is_gemv = lambda n: kernel in n
     is_copy = lambda n: "copy" in n.lower() and "gemv" not in n
     f_kib, nf = _per_dispatch_kib(fetch_dir, "FETCH_SIZE", is_gemv)
     w_kib, nw = _per_dispatch_kib(write_dir, "WRITE_SIZE", is_gemv)
@@ -197,8 +205,8 @@ def write_counters(dirs):
     fetch_scale = COPY_BYTES / (cf_kib * 1024)
     write_scale = COPY_BYTES / (cw_kib * 1024)
     hbm = f_kib * 1024 * fetch_scale + w_kib * 1024 * write_scale
-    out = dict(kernel_source_hash=kernel_source_hash(),
-               kernel="gemv_kernel (tf_gemv_w4a16), the four launches of the fused layer step",
+    out = dict(kernel_source_hash=kernel_source_hash(), kernel_trace_name=kernel,
+               kernel=f"{kernel} (tf_gemv_w4a16): its dispatches in the fused layer step",
                fetch_kib_per_launch=round(f_kib, 1), write_kib_per_launch=round(w_kib, 1),
                dispatches=dict(fetch=nf, write=nw),
                copy_calibration=dict(bytes=COPY_BYTES, fetch_kib=round(cf_kib, 1), write_kib=round(cw_kib, 1),
@@ -432,18 +440,35 @@ def bench_gemv(torch, q, args):
     if not args.no_separate:
         ts_ = time_graphs(torch, q, lins, args, R)
 
-    # the roofline's per-launch duration: the timed region (queued launches
-    # and the events around them share torch's current stream) over its
-    # launches
-    avg_launch_us = ms_f * 1e3 / len(fused)
-    achieved = layer_bytes / len(fused) / (avg_launch_us * 1e-6) / 1e9
+    # The roofline's dominant kernel: launches are grouped by the kernel
+    # instance they run (the GEMV kernel, its ring depth and blocks per
+    # workgroup, from the library's plan), as a kernel trace's statistics
+    # group them; the group with the most time per step is the dominant
+    # kernel.  Its per-launch durations are the back-to-back batches of one
+    # launch each, timed with HIP events on the launch stream (torch's
+    # current stream, which the binding launches on).
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    groups = {}
+    for f, us in zip(fused, us_f):
+        pl = q.tf_gemv_plan(4, 1, f["K"], f["N"], f["G"], cus)
+        key = (pl["kernel"], pl["depth"], pl["bpw"])
+        g = groups.setdefault(key, dict(names=[], bytes=0.0, us=0.0, n=0))
+        g["names"].append(f["name"])
+        g["bytes"] += f["bytes"]
+        g["us"] += us
+        g["n"] += 1
+    dom_key, dom = max(groups.items(), key=lambda kv: kv[1]["us"])
+    avg_launch_us = dom["us"] / dom["n"]
+    achieved = dom["bytes"] / (dom["us"] * 1e-6) / 1e9
+    step_achieved = layer_bytes / (ms_f * 1e-3) / 1e9
     read_roof = layer_bytes / (tf_["read_roof_ms"] * 1e-3) / 1e9
 
+    trace_name = GEMV_TRACE_NAME.format(depth=dom_key[1], bpw=dom_key[2])
     traffic = None
     if os.path.exists(COUNTERS_FILE):
         with open(COUNTERS_FILE) as f:
             cnt = json.load(f)
-        if cnt.get("kernel_source_hash") == kernel_source_hash():
+        if cnt.get("kernel_source_hash") == kernel_source_hash() and cnt.get("kernel_trace_name") == trace_name:
             traffic = cnt.get("hbm_bytes_per_launch")
 
     def rows(ls, us):
@@ -464,12 +489,17 @@ def bench_gemv(torch, q, args):
             per_linear=rows(lins, ts_["mean_us"])),
         roofline=dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                       frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic,
-                      kernel="gemv_kernel (tf_gemv_w4a16, W4, one k-tile per group)",
-                      bytes_per_launch=round(layer_bytes / len(fused)),
+                      kernel=f"{trace_name} ({' and '.join(dom['names'])} launches)",
+                      launches=dom["names"],
+                      bytes_per_launch=round(dom["bytes"] / dom["n"]),
                       avg_launch_us=round(avg_launch_us, 3),
+                      step_average=dict(achieved=round(step_achieved, 1),
+                                        frac=round(step_achieved / HBM_PEAK_GBS, 4),
+                                        what="all four launches of the step: layer bytes over step time"),
                       measured_roof=round(read_roof, 1),
-                      frac_of_measured_roof=round(achieved / read_roof, 4),
-                      measured_roof_kind="plain streaming read of the same packed buffers, same queued launches"),
+                      frac_of_measured_roof=round(step_achieved / read_roof, 4),
+                      measured_roof_kind="plain streaming read of the same packed buffers, same queued launches "
+                                         "(compared with the step average)"),
     )
 
 
@@ -655,12 +685,16 @@ def bench_crossover(torch, q, args):
         ys = [torch.empty((M, f["N"]), dtype=torch.bfloat16, device="cuda:0") for f in fused]
         lb = sum(algorithmic_bytes(4, M, f["K"], f["N"], f["G"]) for f in fused)
         row = dict(M=M, layer_bytes=int(lb))
-        kernels = [("gemv", q.tf_gemv_w4a16, 0)] if M <= 16 else []
-        kernels.append(("gemm", q.tf_gemm_w4a16, 0))
+        cus = torch.cuda.get_device_properties(0).multi_processor_count
+
+        def tiled(x, p, K, N, G, y):  # the same GEMM call forced onto the tiled GEMM
+            return q.tf_linear_planned(4, q.TF_OP_GEMM, x, p, K, N, G, cus, q.TF_ROUTE_TILED, y=y)
+
+        kernels = [("gemv", q.tf_gemv_w4a16)] if M <= 16 else []
+        kernels.append(("gemm", q.tf_gemm_w4a16))
         if M <= 64:  # the GEMM call runs the GEMV kernel; the tiled GEMM beside it
-            kernels.append(("gemm_tiled", q.tf_gemm_w4a16, 1))
-        for name, fn, route in kernels:
-            q.tf_gemm_set_route(route)
+            kernels.append(("gemm_tiled", tiled))
+        for name, fn in kernels:
             def step(i, fn=fn, xs=xs, ys=ys):
                 for f, p, x, y in zip(fused, reps[i % R], xs, ys):
                     fn(x, p, f["K"], f["N"], f["G"], y=y)
@@ -669,7 +703,6 @@ def bench_crossover(torch, q, args):
             ms = time_queued(torch, step, 40, enqueue_us=host_us_per_step(step, R))
             row[name] = dict(us=round(ms * 1e3, 2), gbs=round(lb / (ms * 1e-3) / 1e9, 1),
                              tflops=round(flops1 * M / (ms * 1e-3) / 1e12, 1))
-            q.tf_gemm_set_route(0)
         row["faster"] = min((k for k in ("gemv", "gemm", "gemm_tiled") if k in row), key=lambda k: row[k]["us"])
         out.append(row)
         del xs, ys
@@ -754,12 +787,16 @@ def bench_silu(torch, q, args):
     return out
 
 
-def bench_energy(torch, q, args, seconds=2.0):
+def bench_energy(torch, q, args, seconds=1.0):
     """Energy per call from the GPU's energy accumulator (amdsmi), read around
-    about `seconds` of back-to-back calls: the decoder layer's GEMV pass at
-    M=1 and the prefill GEMM at M=2048, beside the idle draw over the same
-    time.  The accumulator updates about once a millisecond, so each window
-    is long; the figures are board energy, idle included."""
+    about `seconds` of calls that keep the GPU busy the whole window: the
+    decoder layer's GEMV pass at M=1 as HIP-graph replays of 32 passes each
+    (over weight replicas larger than twice the Infinity Cache; eager
+    launches from the host would leave the GPU idle between them), and the
+    prefill GEMM at M=2048 launched back to back.  HIP events around the
+    window give the GPU-busy fraction.  Beside them the idle draw over the
+    same time.  The accumulator updates about once a millisecond, so each
+    window is long; the figures are board energy, idle included."""
     try:
         import amdsmi
 
@@ -774,7 +811,7 @@ def bench_energy(torch, q, args, seconds=2.0):
         e = amdsmi.amdsmi_get_energy_count(handle)
         return e["energy_accumulator"] * e["counter_resolution"] * 1e-6
 
-    def window(run_one, calls_per_run):
+    def window(run_one, calls_per_run, gpu_ms_per_run):
         run_one(0)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
@@ -783,18 +820,29 @@ def bench_energy(torch, q, args, seconds=2.0):
             run_one(n)
             n += 1
         torch.cuda.synchronize()
+        # keep about 20 ms of work queued: the host never lets the GPU drain
+        ahead = max(2, int(20.0 / gpu_ms_per_run))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        marks = []
         j0, t0 = joules(), time.perf_counter()
+        e0.record()
         n = 0
         while time.perf_counter() - t0 < seconds:
             run_one(n)
             n += 1
-            if n % 64 == 0:
-                torch.cuda.synchronize()
+            ev = torch.cuda.Event()
+            ev.record()
+            marks.append(ev)
+            if len(marks) > ahead:
+                marks.pop(0).synchronize()
+        e1.record()
         torch.cuda.synchronize()
         j1, t1 = joules(), time.perf_counter()
         calls = n * calls_per_run
+        busy = e0.elapsed_time(e1) * 1e-3 / (t1 - t0)
         return dict(calls=calls, seconds=round(t1 - t0, 3), joules=round(j1 - j0, 3),
-                    watts=round((j1 - j0) / (t1 - t0), 1), uj_per_call=round((j1 - j0) / calls * 1e6, 2))
+                    watts=round((j1 - j0) / (t1 - t0), 1), mj_per_call=round((j1 - j0) / calls * 1e3, 4),
+                    gpu_busy_frac=round(min(busy, 1.0), 3))
 
     torch.cuda.synchronize()
     j0, t0 = joules(), time.perf_counter()
@@ -806,14 +854,32 @@ def bench_energy(torch, q, args, seconds=2.0):
     del lins
     R = max(2, -(-2 * INFINITY_CACHE_BYTES // sum(f["packed"].numel() for f in fused)) + 1)
     reps = [[f["packed"] for f in fused]] + [[f["packed"].clone() for f in fused] for _ in range(R - 1)]
+    passes = 32
 
     def layer_pass(i):
         for f, p in zip(fused, reps[i % R]):
             q.tf_gemv_w4a16(f["x"], p, f["K"], f["N"], f["G"], y=f["y"])
 
-    gemv = window(layer_pass, 1)
-    gemv.update(kernel="gemv W4A16 M=1, decoder layer pass (four launches)")
-    del reps, fused
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        layer_pass(0)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            for i in range(passes):
+                layer_pass(i)
+    torch.cuda.synchronize()
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    graph.replay()
+    g0.record()
+    graph.replay()
+    g1.record()
+    torch.cuda.synchronize()
+    gemv = window(lambda i: graph.replay(), passes, g0.elapsed_time(g1))
+    gemv.update(kernel="gemv W4A16 M=1, decoder layer pass (four launches), HIP-graph replays of "
+                       f"{passes} passes", unit="mJ per layer pass")
+    del reps, fused, graph
 
     c = synth.make_case(3, 0, 2048, keep_codes=False)
     import numpy as np
@@ -824,20 +890,21 @@ def bench_energy(torch, q, args, seconds=2.0):
                             torch.from_numpy(c.scales.view(np.int16)).to(dev), c.K, c.N, c.G)
     x = torch.from_numpy(c.x.view(np.int16)).to(dev).view(torch.bfloat16)
     y = torch.empty((c.M, c.N), dtype=torch.bfloat16, device=dev)
-    gemm = window(lambda i: q.tf_gemm_w4a16(x, packed, c.K, c.N, c.G, y=y), 1)
-    gemm.update(kernel=f"gemm W4A16 M={c.M} K={c.K} N={c.N}",
+    gemm = window(lambda i: q.tf_gemm_w4a16(x, packed, c.K, c.N, c.G, y=y), 1, 0.3)
+    gemm.update(kernel=f"gemm W4A16 M={c.M} K={c.K} N={c.N}", unit="mJ per GEMM call",
                 tflop_per_joule=round(2.0 * c.M * c.K * c.N * gemm["calls"] / 1e12 / gemm["joules"], 3))
     try:
         amdsmi.amdsmi_shut_down()
     except Exception:
         pass
-    return dict(available=True, idle_watts=round(idle_w, 1), gemv=gemv, gemm=gemm)
+    return dict(available=True, idle_watts=round(idle_w, 1), gemv=gemv, gemm=gemm,
+                note="board energy from the amdsmi accumulator, idle draw included")
 
 
 def main():
     args = parse()
     if args.counters_from:
-        write_counters(args.counters_from)
+        write_counters(args.counters_from, args.counters_kernel)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the library has no multi-GPU path.",
@@ -888,7 +955,7 @@ def main():
         line["configs"] = bench_configs(torch, q, args)
     if args.only == "crossover":
         line["crossover"] = bench_crossover(torch, q, args)
-    if args.only == "energy":
+    if args.only == "energy" or (args.only == "all" and not args.no_energy):
         line["energy"] = bench_energy(torch, q, args)
     if args.only == "silu":
         line["silu_mul"] = bench_silu(torch, q, args)

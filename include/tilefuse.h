@@ -207,41 +207,83 @@ int tf_gemm_w8a16(const uint16_t *x, const void *packed, size_t packed_bytes, ui
                   int64_t M, int64_t K, int64_t N, int64_t G,
                   void *workspace, size_t ws_bytes, void *stream);
 
-/* Test hook, not on the hot path: the dequantized weights w[K][N] as fp32
- * ((q - z) * s is exact in fp32), produced by the same unpack and dequant
- * code the GEMM uses.  w is 4-byte aligned. */
+/* Test hooks, not on the hot path: the dequantized weights w[K][N] as fp32
+ * ((q - z) * s is exact in fp32), decoded from a packed buffer by the
+ * kernels' own operand builders, so that comparing w with the plain
+ * definition bit for bit checks the code the kernels run:
+ *   tf_dequant_w4_f32 / _w8_f32: the GEMM's -- the exact bf16 values q - z it
+ *     stores in its LDS weight tile -- times s;
+ *   tf_dequant_gemv_w4_f32 / _w8_f32: the GEMV kernels' -- bf16 128 + q and
+ *     the zero-point operand 128 + z (W8: q and z) -- their difference times
+ *     s.
+ * w is 4-byte aligned; other arguments and errors as tf_gemv_*. */
 int tf_dequant_w4_f32(const void *packed, size_t packed_bytes, float *w,
                       int64_t K, int64_t N, int64_t G, void *stream);
 int tf_dequant_w8_f32(const void *packed, size_t packed_bytes, float *w,
                       int64_t K, int64_t N, int64_t G, void *stream);
+int tf_dequant_gemv_w4_f32(const void *packed, size_t packed_bytes, float *w,
+                           int64_t K, int64_t N, int64_t G, void *stream);
+int tf_dequant_gemv_w8_f32(const void *packed, size_t packed_bytes, float *w,
+                           int64_t K, int64_t N, int64_t G, void *stream);
 
-/* Test hooks of the GEMM's launch plan (host only, no GPU work).
+/* ------------------------------------------------------------------------ */
+/* Test hooks with explicit plan inputs.  A product call plans its launches */
+/* for the current device's compute units and picks its kernel by M (the    */
+/* GEMV kernels up to 64 rows).  These hooks take both as arguments, per    */
+/* call; the library keeps no setting between calls (its only process-wide */
+/* state is the per-device compute-unit count, queried once).               */
+/*                                                                          */
+/*   op     TF_OP_GEMV (tf_gemv_*), TF_OP_GEMM (tf_gemm_*),                 */
+/*          TF_OP_GEMV_SILU_MUL, TF_OP_GEMM_SILU_MUL (the *_silu_mul calls)  */
+/*   cus    compute units to plan for, 1 .. 2^20                            */
+/*   route  TF_ROUTE_AUTO (the product calls' choice), TF_ROUTE_TILED (GEMM */
+/*          calls run the tiled GEMM at any M), TF_ROUTE_GEMV (the GEMV     */
+/*          kernels up to 64 rows, as AUTO)                                 */
+/* Other values: TF_ERR_UNSUPPORTED (the size query returns 0).             */
+/* ------------------------------------------------------------------------ */
+enum { TF_OP_GEMV = 0, TF_OP_GEMM = 1, TF_OP_GEMV_SILU_MUL = 2, TF_OP_GEMM_SILU_MUL = 3 };
+enum { TF_ROUTE_AUTO = 0, TF_ROUTE_TILED = 1, TF_ROUTE_GEMV = 2 };
+
+/* The call `op` on (bits, M, K, N, G) as planned for (cus, route): the same
+ * validation, kernels and results as the product entry point it names when
+ * cus is the device's count and route is TF_ROUTE_AUTO.  The workspace is
+ * the one tf_workspace_bytes_planned reports for the same inputs. */
+int tf_linear_planned(int bits, int op, const uint16_t *x, const void *packed, size_t packed_bytes,
+                      uint16_t *y, int64_t M, int64_t K, int64_t N, int64_t G,
+                      void *workspace, size_t ws_bytes, int cus, int route, void *stream);
+size_t tf_workspace_bytes_planned(int bits, int op, int64_t M, int64_t K, int64_t N, int64_t G,
+                                  int cus, int route);
+
+/* Launch plan of a GEMM call (host only, no GPU work).
  * The GEMM covers y with 256-row x 128-column tiles (128 x 128 up to 128
  * rows).  When 256-row tiles are not a whole number of rounds over the
- * device's compute units, it runs the columns of the last partial round as
- * 256 x 64 tiles in a second launch.
- * When the tiles fill less than half the compute units (small M), it splits
- * K into ranges that run in the same launch, each writing fp32 partial sums
- * to the workspace, and a second kernel adds them in range order (so
- * tf_workspace_bytes is non-zero for those shapes).  The plan never changes
- * the result's bits except through that split: the order of the split sums.
- *   tf_gemm_plan: writes seven values for a GEMM of (bits, M, K, N, G) on a
- *     device of `cus` compute units: out[5] = 1 when the call runs the GEMV
- *     kernel (then out[0..2] = out[6] = 0), 0 for the tiled GEMM; out[0] =
- *     row tiles of out[6] rows (256 or 128), out[1] = 128-column tiles,
- *     out[2] = 64-column tiles, out[3] = K ranges, out[4] = k-tiles of 128
- *     rows per range.  TF_ERR_NULL / TF_ERR_SHAPE / TF_ERR_GROUP /
- *     TF_ERR_UNSUPPORTED on bad input.
- *   tf_gemm_set_planning_cus: makes later GEMM and GEMV calls and workspace
- *     queries of this process plan for n compute units instead of the
- *     current device's (n <= 0 restores the device's).  Process-wide; not
- *     meant to race with those calls.
- *   tf_gemm_set_route: which kernel later tf_gemm_* calls with M <= 64 run:
- *     0 (default) the GEMV kernel, 1 the tiled GEMM, 2 the GEMV kernel.
- *     Other values act as 0.  Process-wide, like the above. */
-int tf_gemm_plan(int bits, int64_t M, int64_t K, int64_t N, int64_t G, int cus, int64_t *out);
-void tf_gemm_set_planning_cus(int n);
-void tf_gemm_set_route(int route);
+ * compute units, it runs the columns of the last partial round as 256 x 64
+ * tiles in a second launch.  When the tiles fill less than half the compute
+ * units (small M), it splits K into ranges that run in the same launch, each
+ * writing fp32 partial sums to the workspace, and a second kernel adds them
+ * in range order.  The plan never changes the result's bits except through
+ * that split (the order of the split sums).
+ * Writes seven values: out[5] = 1 when the call runs the GEMV kernels (then
+ * out[0..2] = out[6] = 0 and out[3], out[4] are their K split), 0 for the
+ * tiled GEMM; out[0] = row tiles of out[6] rows (256 or 128), out[1] =
+ * 128-column tiles, out[2] = 64-column tiles, out[3] = K ranges, out[4] =
+ * k-tiles of 128 rows per range.  TF_ERR_NULL / TF_ERR_SHAPE / TF_ERR_GROUP /
+ * TF_ERR_UNSUPPORTED on bad input. */
+int tf_gemm_plan(int bits, int64_t M, int64_t K, int64_t N, int64_t G, int cus, int route, int64_t *out);
+
+/* Launch plan of the GEMV kernels for M <= 64 rows (host only), for checks of
+ * the limits the kernels rely on.  Writes fourteen values: out[0] kernel (0:
+ * the kernel for up to 16 rows, 1: the 16-row-chunk kernel), out[1] waves
+ * per workgroup, out[2] 16-column blocks per workgroup, out[3] K ranges over
+ * workgroups, out[4] k-tiles per range, out[5] k-tiles per staged chunk,
+ * out[6] k-tiles of codes in flight per wave, out[7] 16-row chunks per wave,
+ * out[8] LDS bytes per workgroup, out[9] the launcher's LDS limit, out[10]
+ * 16-byte activation units one staging pass holds (kernel 1; 0: staged by a
+ * loop), out[11] 8-byte record words one staging pass holds over all blocks
+ * (kernel 1; 0: a loop), out[12] record bytes reserved per block per chunk,
+ * out[13] bf16 elements per staged activation row.  Errors as tf_gemm_plan;
+ * M outside 1..64 is TF_ERR_SHAPE. */
+int tf_gemv_plan(int bits, int64_t M, int64_t K, int64_t N, int64_t G, int cus, int64_t *out);
 
 /* Measurement probes (not on the hot path): the practical roofs the fused
  * kernels are measured against, on the same machine and launch pattern.

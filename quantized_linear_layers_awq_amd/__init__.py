@@ -14,12 +14,20 @@ from ._binding import (  # noqa: F401
     TileFuseError,
     library_path,
     load_library,
+    TF_OP_GEMM,
+    TF_OP_GEMM_SILU_MUL,
+    TF_OP_GEMV,
+    TF_OP_GEMV_SILU_MUL,
+    TF_ROUTE_AUTO,
+    TF_ROUTE_GEMV,
+    TF_ROUTE_TILED,
+    tf_dequant_gemv_w4_f32,
+    tf_dequant_gemv_w8_f32,
     tf_dequant_w4_f32,
     tf_dequant_w8_f32,
     tf_format_version,
     tf_gemm_plan,
-    tf_gemm_set_planning_cus,
-    tf_gemm_set_route,
+    tf_gemv_plan,
     tf_gemm_w4a16,
     tf_gemm_w4a16_silu_mul,
     tf_gemm_w8a16,
@@ -28,6 +36,7 @@ from ._binding import (  # noqa: F401
     tf_gemv_w4a16_silu_mul,
     tf_gemv_w8a16,
     tf_gemv_w8a16_silu_mul,
+    tf_linear_planned,
     tf_packed_bytes_w4,
     tf_packed_bytes_w8,
     tf_probe_mfma,
@@ -38,6 +47,7 @@ from ._binding import (  # noqa: F401
     tf_repack_w8_gate_up,
     tf_status_string,
     tf_workspace_bytes,
+    tf_workspace_bytes_planned,
 )
 
-__all__ = [n for n in dir() if n.startswith("tf_")] + ["TileFuseError", "load_library"]
+__all__ = [n for n in dir() if n.startswith(("tf_", "TF_"))] + ["TileFuseError", "load_library"]

@@ -66,15 +66,17 @@ def load_library():
         for n in ("tf_gemv_w4a16_silu_mul", "tf_gemv_w8a16_silu_mul", "tf_gemm_w4a16_silu_mul", "tf_gemm_w8a16_silu_mul"):
             getattr(L, n).argtypes = [P, P, SZ, P, I64, I64, I64, I64, P, SZ, P]
             getattr(L, n).restype = I
-        for n in ("tf_dequant_w4_f32", "tf_dequant_w8_f32"):
+        for n in ("tf_dequant_w4_f32", "tf_dequant_w8_f32", "tf_dequant_gemv_w4_f32", "tf_dequant_gemv_w8_f32"):
             getattr(L, n).argtypes = [P, SZ, P, I64, I64, I64, P]
             getattr(L, n).restype = I
-        L.tf_gemm_plan.argtypes = [I, I64, I64, I64, I64, I, ctypes.POINTER(I64)]
+        L.tf_linear_planned.argtypes = [I, I, P, P, SZ, P, I64, I64, I64, I64, P, SZ, I, I, P]
+        L.tf_linear_planned.restype = I
+        L.tf_workspace_bytes_planned.argtypes = [I, I, I64, I64, I64, I64, I, I]
+        L.tf_workspace_bytes_planned.restype = SZ
+        L.tf_gemm_plan.argtypes = [I, I64, I64, I64, I64, I, I, ctypes.POINTER(I64)]
         L.tf_gemm_plan.restype = I
-        L.tf_gemm_set_planning_cus.argtypes = [I]
-        L.tf_gemm_set_planning_cus.restype = None
-        L.tf_gemm_set_route.argtypes = [I]
-        L.tf_gemm_set_route.restype = None
+        L.tf_gemv_plan.argtypes = [I, I64, I64, I64, I64, I, ctypes.POINTER(I64)]
+        L.tf_gemv_plan.restype = I
         L.tf_probe_stream_read.argtypes = [P, SZ, P, P]
         L.tf_probe_stream_read.restype = I
         L.tf_probe_mfma.argtypes = [I, I, P, ctypes.POINTER(I64), P]
@@ -172,8 +174,11 @@ def tf_repack_w8(qweight, zeros, scales, K, N, G, packed=None, stream=None):
 # Split-K workspaces, one per (device, stream), grown on demand.  A split
 # launch writes every partial sum it later adds up, so what a buffer holds
 # between calls does not matter; calls on one stream run in order, so one
-# buffer per stream is never used by two calls at once.
+# buffer per stream is never used by two calls at once.  A buffer that a
+# larger one replaces is kept, never freed: a HIP graph captured on that
+# stream still writes and reads it on every replay.
 _workspaces: dict = {}
+_retired: list = []
 
 
 def _workspace(device: torch.device, stream_handle: int, nbytes: int):
@@ -182,34 +187,54 @@ def _workspace(device: torch.device, stream_handle: int, nbytes: int):
     key = (device.index, stream_handle)
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
-        # allocated on the launch stream: when a larger buffer replaces this
-        # one, torch's allocator reuses the old memory only for work ordered
-        # after the launches still reading it
+        if ws is not None:
+            _retired.append(ws)
+        # allocated on the launch stream, so that torch orders the memory's
+        # first use after the work already queued there
         with torch.cuda.stream(torch.cuda.ExternalStream(stream_handle, device=device)):
             ws = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
         _workspaces[key] = ws
     return ws
 
 
-def _linear(bits, is_gemm, fn, x, packed, K, N, G, y, workspace, stream):
+TF_OP_GEMV, TF_OP_GEMM, TF_OP_GEMV_SILU_MUL, TF_OP_GEMM_SILU_MUL = 0, 1, 2, 3
+TF_ROUTE_AUTO, TF_ROUTE_TILED, TF_ROUTE_GEMV = 0, 1, 2
+
+
+def _call(bits, op, fn, x, packed, K, N, G, y, workspace, stream, plan=None):
+    """One linear call through entry point `fn`; plan = (cus, route) calls
+    tf_linear_planned with those plan inputs instead."""
     L = load_library()
     _need(x, "x", 2)
     _need(packed, "packed", 1)
     if x.dim() != 2 or x.shape[1] != K:
         raise ValueError(f"{fn}: x must be [M][K] with K={K}")
     M = x.shape[0]
+    n_out = N // 2 if op in (TF_OP_GEMV_SILU_MUL, TF_OP_GEMM_SILU_MUL) else N
     if y is None:
-        y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+        y = torch.empty((M, n_out), dtype=torch.bfloat16, device=x.device)
     _need(y, "y", 2)
-    if y.numel() < M * N:
-        raise ValueError(f"{fn}: y holds fewer than M*N elements")
+    if y.numel() < M * n_out:
+        raise ValueError(f"{fn}: y holds fewer than {M * n_out} elements")
     sh = _stream(x, stream)
-    need = int(L.tf_workspace_bytes(bits, int(is_gemm), M, K, N, G))
+    if plan is None:
+        need = int(L.tf_workspace_bytes(bits, int(op in (TF_OP_GEMM, TF_OP_GEMM_SILU_MUL)), M, K, N, G))
+    else:
+        need = int(L.tf_workspace_bytes_planned(bits, op, M, K, N, G, int(plan[0]), int(plan[1])))
     if workspace is None:
         workspace = _workspace(x.device, sh, need)
     ws_ptr, ws_bytes = (None, 0) if workspace is None else (_ptr(workspace), workspace.numel() * workspace.element_size())
-    _check(getattr(L, fn)(_ptr(x), _ptr(packed), packed.numel(), _ptr(y), M, K, N, G, ws_ptr, ws_bytes, sh), fn)
+    if plan is None:
+        st = getattr(L, fn)(_ptr(x), _ptr(packed), packed.numel(), _ptr(y), M, K, N, G, ws_ptr, ws_bytes, sh)
+    else:
+        st = L.tf_linear_planned(bits, op, _ptr(x), _ptr(packed), packed.numel(), _ptr(y), M, K, N, G, ws_ptr,
+                                 ws_bytes, int(plan[0]), int(plan[1]), sh)
+    _check(st, fn if plan is None else f"tf_linear_planned({fn})")
     return y
+
+
+def _linear(bits, is_gemm, fn, x, packed, K, N, G, y, workspace, stream):
+    return _call(bits, TF_OP_GEMM if is_gemm else TF_OP_GEMV, fn, x, packed, K, N, G, y, workspace, stream)
 
 
 def tf_gemv_w4a16(x, packed, K, N, G, y=None, workspace=None, stream=None):
@@ -231,24 +256,8 @@ def tf_gemm_w8a16(x, packed, K, N, G, y=None, workspace=None, stream=None):
 
 
 def _silu_mul(bits, fn, x, packed, K, N, G, y, workspace, stream, is_gemm=False):
-    L = load_library()
-    _need(x, "x", 2)
-    _need(packed, "packed", 1)
-    if x.dim() != 2 or x.shape[1] != K:
-        raise ValueError(f"{fn}: x must be [M][K] with K={K}")
-    M = x.shape[0]
-    if y is None:
-        y = torch.empty((M, N // 2), dtype=torch.bfloat16, device=x.device)
-    _need(y, "y", 2)
-    if y.numel() < M * (N // 2):
-        raise ValueError(f"{fn}: y holds fewer than M*N/2 elements")
-    sh = _stream(x, stream)
-    need = int(L.tf_workspace_bytes(bits, int(is_gemm), M, K, N, G))
-    if workspace is None:
-        workspace = _workspace(x.device, sh, need)
-    ws_ptr, ws_bytes = (None, 0) if workspace is None else (_ptr(workspace), workspace.numel() * workspace.element_size())
-    _check(getattr(L, fn)(_ptr(x), _ptr(packed), packed.numel(), _ptr(y), M, K, N, G, ws_ptr, ws_bytes, sh), fn)
-    return y
+    op = TF_OP_GEMM_SILU_MUL if is_gemm else TF_OP_GEMV_SILU_MUL
+    return _call(bits, op, fn, x, packed, K, N, G, y, workspace, stream)
 
 
 def tf_gemm_w4a16_silu_mul(x, packed, K, N, G, y=None, workspace=None, stream=None):
@@ -284,7 +293,8 @@ def _dequant(fn, packed, K, N, G, w, stream):
 
 
 def tf_dequant_w4_f32(packed, K, N, G, w=None, stream=None):
-    """Test hook: fp32 dequantized weights [K][N] from a W4 packed buffer."""
+    """Test hook: fp32 dequantized weights [K][N] from a W4 packed buffer,
+    decoded by the GEMM's operand builder."""
     return _dequant("tf_dequant_w4_f32", packed, K, N, G, w, stream)
 
 
@@ -292,27 +302,55 @@ def tf_dequant_w8_f32(packed, K, N, G, w=None, stream=None):
     return _dequant("tf_dequant_w8_f32", packed, K, N, G, w, stream)
 
 
-def tf_gemm_plan(bits: int, M: int, K: int, N: int, G: int, cus: int) -> tuple[int, ...]:
+def tf_dequant_gemv_w4_f32(packed, K, N, G, w=None, stream=None):
+    """Test hook: the same weights decoded by the GEMV kernels' operand
+    builders (128 + q and 128 + z, their difference times s)."""
+    return _dequant("tf_dequant_gemv_w4_f32", packed, K, N, G, w, stream)
+
+
+def tf_dequant_gemv_w8_f32(packed, K, N, G, w=None, stream=None):
+    return _dequant("tf_dequant_gemv_w8_f32", packed, K, N, G, w, stream)
+
+
+_OP_FN = {(4, TF_OP_GEMV): "tf_gemv_w4a16", (8, TF_OP_GEMV): "tf_gemv_w8a16", (4, TF_OP_GEMM): "tf_gemm_w4a16",
+          (8, TF_OP_GEMM): "tf_gemm_w8a16", (4, TF_OP_GEMV_SILU_MUL): "tf_gemv_w4a16_silu_mul",
+          (8, TF_OP_GEMV_SILU_MUL): "tf_gemv_w8a16_silu_mul", (4, TF_OP_GEMM_SILU_MUL): "tf_gemm_w4a16_silu_mul",
+          (8, TF_OP_GEMM_SILU_MUL): "tf_gemm_w8a16_silu_mul"}
+
+
+def tf_linear_planned(bits, op, x, packed, K, N, G, cus, route=TF_ROUTE_AUTO, y=None, workspace=None, stream=None):
+    """Test hook: the linear call `op` (TF_OP_*) planned for `cus` compute
+    units and kernel route `route` (TF_ROUTE_*), with the workspace that plan
+    needs; same validation and kernels as the product entry point."""
+    return _call(bits, op, _OP_FN[(bits, op)], x, packed, K, N, G, y, workspace, stream, plan=(cus, route))
+
+
+def tf_workspace_bytes_planned(bits, op, M, K, N, G, cus, route=TF_ROUTE_AUTO) -> int:
+    return int(load_library().tf_workspace_bytes_planned(bits, op, M, K, N, G, cus, route))
+
+
+def tf_gemm_plan(bits: int, M: int, K: int, N: int, G: int, cus: int, route: int = TF_ROUTE_AUTO) -> tuple[int, ...]:
     """Test hook: (row tiles, 128-column tiles, 64-column tiles, K ranges,
-    k-tiles per range, 1 if the call runs the GEMV kernel else 0, rows per
+    k-tiles per range, 1 if the call runs the GEMV kernels else 0, rows per
     row tile) of a GEMM call's launch plan on a device of `cus` compute
-    units (host only)."""
+    units with kernel route `route` (host only)."""
     L = load_library()
     out = (ctypes.c_int64 * 7)()
-    _check(L.tf_gemm_plan(bits, M, K, N, G, cus, out), "tf_gemm_plan")
+    _check(L.tf_gemm_plan(bits, M, K, N, G, cus, route, out), "tf_gemm_plan")
     return tuple(int(v) for v in out)
 
 
-def tf_gemm_set_planning_cus(n: int) -> None:
-    """Test hook: later GEMM calls plan for n compute units (n <= 0: the
-    device's own count).  Process-wide."""
-    load_library().tf_gemm_set_planning_cus(int(n))
+GEMV_PLAN_FIELDS = ("kernel", "waves", "bpw", "splits", "split_tiles", "chunk_tiles", "depth", "row_chunks", "lds",
+                    "lds_limit", "x_capacity", "rec_capacity", "meta_cap", "xpitch")
 
 
-def tf_gemm_set_route(route: int) -> None:
-    """Test hook: the kernel later GEMM calls with M <= 64 run (0 automatic,
-    1 the tiled GEMM, 2 the GEMV kernel).  Process-wide."""
-    load_library().tf_gemm_set_route(int(route))
+def tf_gemv_plan(bits: int, M: int, K: int, N: int, G: int, cus: int) -> dict:
+    """Test hook: the GEMV kernels' launch plan for M <= 64 rows on `cus`
+    compute units (host only), as a dict over GEMV_PLAN_FIELDS."""
+    L = load_library()
+    out = (ctypes.c_int64 * 14)()
+    _check(L.tf_gemv_plan(bits, M, K, N, G, cus, out), "tf_gemv_plan")
+    return dict(zip(GEMV_PLAN_FIELDS, (int(v) for v in out)))
 
 
 def tf_probe_stream_read(buf, sink, stream=None):

@@ -57,29 +57,40 @@ int repack(int bits, const void *qweight, const void *qzeros, const uint16_t *sc
     return TF_OK;
 }
 
+// The four kinds of linear call (the TF_OP_* values of the header).
+constexpr int kOpGemv = 0, kOpGemm = 1, kOpGemvSiluMul = 2, kOpGemmSiluMul = 3;
+bool op_is_gemm(int op) { return op == kOpGemm || op == kOpGemmSiluMul; }
+bool op_is_silu(int op) { return op == kOpGemvSiluMul || op == kOpGemmSiluMul; }
+int64_t op_max_m(int op) { return op_is_gemm(op) ? (int64_t(1) << 30) : 16; }
+
 // fp32 partial sums, S x M x N floats, when a call splits K over workgroups:
 // the tiled GEMM with few output tiles (small M), the 16-row-chunk GEMV
 // kernel (8..64 rows) on a layer too narrow to fill the chip.  Otherwise
 // none: the GEMV kernel for up to 16 rows combines its K split inside a
-// workgroup.
-size_t workspace_bytes(int bits, int is_gemm, int64_t M, int64_t K, int64_t N, int64_t G)
+// workgroup.  A SiLU-product call needs what the plain call of its shape
+// needs.
+size_t workspace_bytes(int bits, int op, int64_t M, int64_t K, int64_t N, int64_t G, int cus, int route)
 {
-    if (M < 1 || M > (is_gemm ? (int64_t(1) << 30) : 16) || check_kng(bits, K, N, G) != TF_OK)
+    if (M < 1 || M > op_max_m(op) || check_kng(bits, K, N, G) != TF_OK)
         return 0;
     const Layout lay = Layout::make(bits, K, N, G);
-    if (!is_gemm || tf::gemm_uses_gemv(M))
-        return (size_t)tf::gemv_workspace_bytes(lay, M, tf::planning_cus());
-    return (size_t)tf::gemm_workspace_bytes(M, N, K, G);
+    if (!op_is_gemm(op) || tf::gemm_uses_gemv(M, route))
+        return (size_t)tf::gemv_workspace_bytes(lay, M, cus);
+    return (size_t)tf::gemm_workspace_bytes(M, N, K, G, cus);
 }
 
-int linear(int bits, bool is_gemm, const uint16_t *x, const void *packed, size_t nbytes, uint16_t *y, int64_t M,
-           int64_t K, int64_t N, int64_t G, void *ws, size_t ws_bytes, void *stream)
+// One linear call: validation on the host, then the launches.  cus and
+// route are the plan's inputs: the device's compute units and the automatic
+// route for every product entry point.
+int linear(int bits, int op, const uint16_t *x, const void *packed, size_t nbytes, uint16_t *y, int64_t M, int64_t K,
+           int64_t N, int64_t G, void *ws, size_t ws_bytes, int cus, int route, void *stream)
 {
-    if (M < 0)
+    if (M < 0 || M > op_max_m(op))
         return TF_ERR_SHAPE;
     if (int st = check_kng(bits, K, N, G))
         return st;
-    if (is_gemm ? M > (int64_t(1) << 30) : M > 16)
+    // the [gate | up] halves are whole 8-column runs
+    if (op_is_silu(op) && N % (2 * 8))
         return TF_ERR_SHAPE;
     // 32-bit offsets: a row of x in the GEMM, and a code tile within a
     // 16-column block (K / 128 tiles of up to 2 KiB) in the GEMV kernels
@@ -94,7 +105,7 @@ int linear(int bits, bool is_gemm, const uint16_t *x, const void *packed, size_t
     const Layout lay = Layout::make(bits, K, N, G);
     if (nbytes < (size_t)lay.total_bytes())
         return TF_ERR_BUFFER_TOO_SMALL;
-    const size_t need = workspace_bytes(bits, is_gemm, M, K, N, G);
+    const size_t need = workspace_bytes(bits, op, M, K, N, G, cus, route);
     if (need) {
         if (!ws)
             return TF_ERR_NULL;
@@ -103,55 +114,20 @@ int linear(int bits, bool is_gemm, const uint16_t *x, const void *packed, size_t
         if (ws_bytes < need)
             return TF_ERR_BUFFER_TOO_SMALL;
     }
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    const bool tiled = op_is_gemm(op) && !tf::gemm_uses_gemv(M, route);
     hipError_t e;
-    if (is_gemm && !tf::gemm_uses_gemv(M))
-        e = tf::launch_gemm(bits, x, packed, y, M, lay, ws, static_cast<hipStream_t>(stream));
+    if (tiled)
+        e = tf::launch_gemm(bits, x, packed, y, M, lay, ws, st, cus, op_is_silu(op) ? tf::kActSiluMul : tf::kActNone);
+    else if (op_is_silu(op))
+        e = tf::launch_gemv_silu_mul(bits, x, packed, y, M, lay, ws, st, cus);
     else
-        e = tf::launch_gemv(bits, x, packed, y, M, lay, ws, static_cast<hipStream_t>(stream));
+        e = tf::launch_gemv(bits, x, packed, y, M, lay, ws, st, cus);
     return e == hipSuccess ? TF_OK : TF_ERR_HIP;
 }
 
-// [gate | up] GEMV or GEMM with the SiLU product over a buffer from
-// repack(gate_up): the kernels, plans and workspace of the plain call of the
-// same shape, with the product in the epilogue (or in the split sum).
-int linear_silu_mul(int bits, bool is_gemm, const uint16_t *x, const void *packed, size_t nbytes, uint16_t *y,
-                    int64_t M, int64_t K, int64_t N, int64_t G, void *ws, size_t ws_bytes, void *stream)
-{
-    if (M < 0 || M > (is_gemm ? (int64_t(1) << 30) : 16))
-        return TF_ERR_SHAPE;
-    if (int st = check_kng(bits, K, N, G))
-        return st;
-    // halves of whole 8-column runs; 32-bit code-tile offsets as in linear()
-    if (N % (2 * 8) || K >= (int64_t(1) << 25))
-        return TF_ERR_SHAPE;
-    if (M == 0)
-        return TF_OK;
-    if (!x || !packed || !y)
-        return TF_ERR_NULL;
-    if (!aligned(x, 16) || !aligned(packed, 16) || !aligned(y, 2))
-        return TF_ERR_ALIGN;
-    const Layout lay = Layout::make(bits, K, N, G);
-    if (nbytes < (size_t)lay.total_bytes())
-        return TF_ERR_BUFFER_TOO_SMALL;
-    // the kernel and its K split are the plain call's for this shape
-    const size_t need = workspace_bytes(bits, is_gemm, M, K, N, G);
-    if (need) {
-        if (!ws)
-            return TF_ERR_NULL;
-        if (!aligned(ws, 256))
-            return TF_ERR_ALIGN;
-        if (ws_bytes < need)
-            return TF_ERR_BUFFER_TOO_SMALL;
-    }
-    hipError_t e;
-    if (is_gemm && !tf::gemm_uses_gemv(M))
-        e = tf::launch_gemm(bits, x, packed, y, M, lay, ws, static_cast<hipStream_t>(stream), tf::kActSiluMul);
-    else
-        e = tf::launch_gemv_silu_mul(bits, x, packed, y, M, lay, ws, static_cast<hipStream_t>(stream));
-    return e == hipSuccess ? TF_OK : TF_ERR_HIP;
-}
-
-int dequant(int bits, const void *packed, size_t nbytes, float *w, int64_t K, int64_t N, int64_t G, void *stream)
+int dequant(int bits, const void *packed, size_t nbytes, float *w, int64_t K, int64_t N, int64_t G, void *stream,
+            bool gemv)
 {
     if (!packed || !w)
         return TF_ERR_NULL;
@@ -162,9 +138,15 @@ int dequant(int bits, const void *packed, size_t nbytes, float *w, int64_t K, in
     const Layout lay = Layout::make(bits, K, N, G);
     if (nbytes < (size_t)lay.total_bytes())
         return TF_ERR_BUFFER_TOO_SMALL;
-    if (tf::launch_dequant_f32(bits, packed, lay, w, static_cast<hipStream_t>(stream)) != hipSuccess)
+    if (tf::launch_dequant_f32(bits, packed, lay, w, static_cast<hipStream_t>(stream), gemv) != hipSuccess)
         return TF_ERR_HIP;
     return TF_OK;
+}
+
+bool plan_inputs_ok(int bits, int op, int cus, int route)
+{
+    return (bits == 4 || bits == 8) && op >= kOpGemv && op <= kOpGemmSiluMul && cus >= 1 && cus <= (1 << 20) &&
+           (route == tf::kRouteAuto || route == tf::kRouteTiled || route == tf::kRouteGemv);
 }
 
 } // namespace
@@ -219,78 +201,74 @@ size_t tf_workspace_bytes(int bits, int is_gemm, int64_t M, int64_t K, int64_t N
 {
     if (bits != 4 && bits != 8)
         return 0;
-    return workspace_bytes(bits, is_gemm, M, K, N, G);
+    return workspace_bytes(bits, is_gemm ? kOpGemm : kOpGemv, M, K, N, G, tf::device_cus(), tf::kRouteAuto);
 }
 
-int tf_gemv_w4a16(const uint16_t *x, const void *packed, size_t nbytes, uint16_t *y, int64_t M, int64_t K, int64_t N,
-                  int64_t G, void *ws, size_t ws_bytes, void *stream)
-{
-    return linear(4, false, x, packed, nbytes, y, M, K, N, G, ws, ws_bytes, stream);
-}
-
-int tf_gemv_w8a16(const uint16_t *x, const void *packed, size_t nbytes, uint16_t *y, int64_t M, int64_t K, int64_t N,
-                  int64_t G, void *ws, size_t ws_bytes, void *stream)
-{
-    return linear(8, false, x, packed, nbytes, y, M, K, N, G, ws, ws_bytes, stream);
-}
-
-int tf_gemm_w4a16(const uint16_t *x, const void *packed, size_t nbytes, uint16_t *y, int64_t M, int64_t K, int64_t N,
-                  int64_t G, void *ws, size_t ws_bytes, void *stream)
-{
-    return linear(4, true, x, packed, nbytes, y, M, K, N, G, ws, ws_bytes, stream);
-}
-
-int tf_gemm_w8a16(const uint16_t *x, const void *packed, size_t nbytes, uint16_t *y, int64_t M, int64_t K, int64_t N,
-                  int64_t G, void *ws, size_t ws_bytes, void *stream)
-{
-    return linear(8, true, x, packed, nbytes, y, M, K, N, G, ws, ws_bytes, stream);
-}
-
-int tf_gemv_w4a16_silu_mul(const uint16_t *x, const void *packed, size_t nbytes, uint16_t *y, int64_t M, int64_t K,
-                           int64_t N, int64_t G, void *ws, size_t ws_bytes, void *stream)
-{
-    return linear_silu_mul(4, false, x, packed, nbytes, y, M, K, N, G, ws, ws_bytes, stream);
-}
-
-int tf_gemv_w8a16_silu_mul(const uint16_t *x, const void *packed, size_t nbytes, uint16_t *y, int64_t M, int64_t K,
-                           int64_t N, int64_t G, void *ws, size_t ws_bytes, void *stream)
-{
-    return linear_silu_mul(8, false, x, packed, nbytes, y, M, K, N, G, ws, ws_bytes, stream);
-}
-
-int tf_gemm_w4a16_silu_mul(const uint16_t *x, const void *packed, size_t nbytes, uint16_t *y, int64_t M, int64_t K,
-                           int64_t N, int64_t G, void *ws, size_t ws_bytes, void *stream)
-{
-    return linear_silu_mul(4, true, x, packed, nbytes, y, M, K, N, G, ws, ws_bytes, stream);
-}
-
-int tf_gemm_w8a16_silu_mul(const uint16_t *x, const void *packed, size_t nbytes, uint16_t *y, int64_t M, int64_t K,
-                           int64_t N, int64_t G, void *ws, size_t ws_bytes, void *stream)
-{
-    return linear_silu_mul(8, true, x, packed, nbytes, y, M, K, N, G, ws, ws_bytes, stream);
-}
+#define TF_LINEAR(name, bits, op)                                                                                     \
+    int name(const uint16_t *x, const void *packed, size_t nbytes, uint16_t *y, int64_t M, int64_t K, int64_t N,      \
+             int64_t G, void *ws, size_t ws_bytes, void *stream)                                                      \
+    {                                                                                                                 \
+        return linear(bits, op, x, packed, nbytes, y, M, K, N, G, ws, ws_bytes, tf::device_cus(), tf::kRouteAuto,   \
+                      stream);                                                                                        \
+    }
+TF_LINEAR(tf_gemv_w4a16, 4, kOpGemv)
+TF_LINEAR(tf_gemv_w8a16, 8, kOpGemv)
+TF_LINEAR(tf_gemm_w4a16, 4, kOpGemm)
+TF_LINEAR(tf_gemm_w8a16, 8, kOpGemm)
+TF_LINEAR(tf_gemv_w4a16_silu_mul, 4, kOpGemvSiluMul)
+TF_LINEAR(tf_gemv_w8a16_silu_mul, 8, kOpGemvSiluMul)
+TF_LINEAR(tf_gemm_w4a16_silu_mul, 4, kOpGemmSiluMul)
+TF_LINEAR(tf_gemm_w8a16_silu_mul, 8, kOpGemmSiluMul)
+#undef TF_LINEAR
 
 int tf_dequant_w4_f32(const void *packed, size_t nbytes, float *w, int64_t K, int64_t N, int64_t G, void *stream)
 {
-    return dequant(4, packed, nbytes, w, K, N, G, stream);
+    return dequant(4, packed, nbytes, w, K, N, G, stream, false);
 }
 
 int tf_dequant_w8_f32(const void *packed, size_t nbytes, float *w, int64_t K, int64_t N, int64_t G, void *stream)
 {
-    return dequant(8, packed, nbytes, w, K, N, G, stream);
+    return dequant(8, packed, nbytes, w, K, N, G, stream, false);
 }
 
-int tf_gemm_plan(int bits, int64_t M, int64_t K, int64_t N, int64_t G, int cus, int64_t *out)
+int tf_dequant_gemv_w4_f32(const void *packed, size_t nbytes, float *w, int64_t K, int64_t N, int64_t G,
+                           void *stream)
+{
+    return dequant(4, packed, nbytes, w, K, N, G, stream, true);
+}
+
+int tf_dequant_gemv_w8_f32(const void *packed, size_t nbytes, float *w, int64_t K, int64_t N, int64_t G,
+                           void *stream)
+{
+    return dequant(8, packed, nbytes, w, K, N, G, stream, true);
+}
+
+size_t tf_workspace_bytes_planned(int bits, int op, int64_t M, int64_t K, int64_t N, int64_t G, int cus, int route)
+{
+    if (!plan_inputs_ok(bits, op, cus, route))
+        return 0;
+    return workspace_bytes(bits, op, M, K, N, G, cus, route);
+}
+
+int tf_linear_planned(int bits, int op, const uint16_t *x, const void *packed, size_t nbytes, uint16_t *y, int64_t M,
+                      int64_t K, int64_t N, int64_t G, void *ws, size_t ws_bytes, int cus, int route, void *stream)
+{
+    if (!plan_inputs_ok(bits, op, cus, route))
+        return TF_ERR_UNSUPPORTED;
+    return linear(bits, op, x, packed, nbytes, y, M, K, N, G, ws, ws_bytes, cus, route, stream);
+}
+
+int tf_gemm_plan(int bits, int64_t M, int64_t K, int64_t N, int64_t G, int cus, int route, int64_t *out)
 {
     if (!out)
         return TF_ERR_NULL;
-    if (bits != 4 && bits != 8)
+    if (!plan_inputs_ok(bits, kOpGemm, cus < 1 ? 1 : cus, route))
         return TF_ERR_UNSUPPORTED;
     if (M < 1 || cus < 1 || M > (int64_t(1) << 30))
         return TF_ERR_SHAPE;
     if (int st = check_kng(bits, K, N, G))
         return st;
-    if (tf::gemm_uses_gemv(M)) {
+    if (tf::gemm_uses_gemv(M, route)) {
         const Layout lay = Layout::make(bits, K, N, G);
         int64_t st = 0;
         out[0] = 0;
@@ -313,9 +291,23 @@ int tf_gemm_plan(int bits, int64_t M, int64_t K, int64_t N, int64_t G, int cus, 
     return TF_OK;
 }
 
-void tf_gemm_set_planning_cus(int n) { tf::set_planning_cus(n); }
-
-void tf_gemm_set_route(int route) { tf::set_gemm_route(route); }
+int tf_gemv_plan(int bits, int64_t M, int64_t K, int64_t N, int64_t G, int cus, int64_t *out)
+{
+    if (!out)
+        return TF_ERR_NULL;
+    if (bits != 4 && bits != 8)
+        return TF_ERR_UNSUPPORTED;
+    if (M < 1 || M > tf::kGemvKernelMaxM || cus < 1 || cus > (1 << 20))
+        return TF_ERR_SHAPE;
+    if (int st = check_kng(bits, K, N, G))
+        return st;
+    const tf::GemvPlanInfo p = tf::gemv_plan_info(bits, Layout::make(bits, K, N, G), M, cus);
+    const int64_t v[14] = {p.kernel, p.waves,  p.bpw,        p.splits,       p.split_tiles, p.chunk_tiles, p.depth,
+                           p.row_chunks, p.lds, p.lds_limit, p.x_capacity, p.rec_capacity, p.meta_cap,  p.xpitch};
+    for (int i = 0; i < 14; ++i)
+        out[i] = v[i];
+    return TF_OK;
+}
 
 int tf_probe_stream_read(const void *buf, size_t bytes, uint32_t *sink, void *stream)
 {

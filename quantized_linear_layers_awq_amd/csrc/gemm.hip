@@ -47,6 +47,7 @@
 
 #include "tf_common.h"
 #include "tf_launch.h"
+#include "tf_operands.h"
 
 namespace tf {
 
@@ -138,30 +139,6 @@ __device__ __forceinline__ f32x16 mfma32x32x16(const u32x4 &a, const u32x4 &b, c
 {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
                                                    0, 0, 0);
-}
-
-// Exact bf16 (q - z) * live of eight W4 codes (rows 0..7 of a column's
-// k-octet in one word).  `lo` / `hi` hold the even / odd nibbles as bytes;
-// the empty asm keeps the compiler from merging the masks into per-value
-// bit-field extracts, so each value is one v_cvt_f32_ubyteN and one fma.
-__device__ __forceinline__ u32x4 unpack_w4(uint32_t w, float live, float nz)
-{
-    uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
-    asm volatile("" : "+v"(lo), "+v"(hi));
-    // nibble 2j holds row j/2... see w4_row_shift: rows 0,4,1,5 in lo, 2,6,3,7 in hi
-    const float r0 = fmaf((float)(lo & 0xFFu), live, nz), r4 = fmaf((float)((lo >> 8) & 0xFFu), live, nz);
-    const float r1 = fmaf((float)((lo >> 16) & 0xFFu), live, nz), r5 = fmaf((float)(lo >> 24), live, nz);
-    const float r2 = fmaf((float)(hi & 0xFFu), live, nz), r6 = fmaf((float)((hi >> 8) & 0xFFu), live, nz);
-    const float r3 = fmaf((float)((hi >> 16) & 0xFFu), live, nz), r7 = fmaf((float)(hi >> 24), live, nz);
-    return u32x4{pack_bf16x2(r0, r1), pack_bf16x2(r2, r3), pack_bf16x2(r4, r5), pack_bf16x2(r6, r7)};
-}
-
-// Same for eight W8 codes held in two words (row i in byte i).
-__device__ __forceinline__ u32x4 unpack_w8(uint32_t w0, uint32_t w1, float live, float nz)
-{
-    float f[8];
-    dequant_w8_pair(w0, w1, live, nz, f);
-    return u32x4{pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7])};
 }
 
 // How groups map onto the 16-row slices of the k loop.  kGSplit32/64 and
@@ -295,20 +272,23 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_kernel(const uint16_t *__re
     for (int j = 0; j < kAJ; ++j) {
         int64_t row = m0 + kARows * wave + 8 * j + (lane >> 3);
         row = row < M ? row : M - 1;
-        a_voff[j] = (uint32_t)((row - a_row_base) * lda * 2 + 16 * a_c[j & 1]);
+        a_voff[j] = (uint32_t)((row - a_row_base) * lda * 2);
     }
-    // The lane's unit of stage s starts s * 128 bytes into the row; past
-    // a_lim it would leave the row (a last stage that runs past K), so the
-    // offset is clamped there and the unit re-reads the row's last 8 columns
-    // (finite values that meet zero weights).  Branch-free: two VALU per load.
-    const uint32_t a_lim[2] = {(uint32_t)(2 * K - 16 - 16 * a_c[0]), (uint32_t)(2 * K - 16 - 16 * a_c[1])};
+    // The lane's unit of stage s starts s * 128 + 16 c bytes into the row
+    // (c its swizzled unit); a unit that would end past the range's last
+    // column (a last stage that runs past K, or a range shorter than a
+    // stage) is clamped to the row's last 16 bytes and re-reads its last 8
+    // columns (finite values that meet zero weights).  The clamp is on the
+    // whole offset, so it holds for every K >= 32 (a row of 64 bytes).
+    const uint32_t a_c16[2] = {16u * (uint32_t)a_c[0], 16u * (uint32_t)a_c[1]};
+    const uint32_t a_last = (uint32_t)(2 * K - 16);
     // instructions j0 .. j1 - 1 of the kAJ that fill the wave's rows of stage s
     auto dma_a = [&](int s, int j0, int j1) {
         uint8_t *dst = sA + (s % kAStages) * kAStageBytes + kARows * wave * 128;
         const uint32_t ks = (uint32_t)s * kStage * 2;
 #pragma unroll
         for (int j = j0; j < j1; ++j)
-            dma16(a_rsrc, a_voff[j] + __builtin_elementwise_min(ks, a_lim[j & 1]), 0, dst + j * 1024);
+            dma16(a_rsrc, a_voff[j] + __builtin_elementwise_min(ks + a_c16[j & 1], a_last), 0, dst + j * 1024);
     };
     // ---- codes: wave w < kGBlocks fetches block w (1 KiB per k-tile; W8:
     //      per half).  Only these waves fetch codes and records and unpack;
@@ -801,17 +781,14 @@ void launch_splitk_sum(const float *ws, int splits, int64_t mn, uint16_t *y, hip
 }
 
 namespace {
-std::atomic<int> g_planning_cus{0};
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_device_cus[kMaxDevices];
 } // namespace
 
-// compute units the plan assumes: the forced count, else the current
-// device's (queried once per device)
-int planning_cus()
+// compute units of the current device, queried once per device (the value
+// never changes, so concurrent first queries store the same number)
+int device_cus()
 {
-    if (const int forced = g_planning_cus.load(std::memory_order_relaxed))
-        return forced;
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
         return 256;
@@ -824,19 +801,7 @@ int planning_cus()
     return n;
 }
 
-void set_planning_cus(int n) { g_planning_cus.store(n > 0 ? n : 0, std::memory_order_relaxed); }
-
-namespace {
-std::atomic<int> g_gemm_route{0};
-} // namespace
-
-bool gemm_uses_gemv(int64_t M)
-{
-    const int route = g_gemm_route.load(std::memory_order_relaxed);
-    return M <= kGemvKernelMaxM && route != 1;
-}
-
-void set_gemm_route(int route) { g_gemm_route.store(route == 1 || route == 2 ? route : 0, std::memory_order_relaxed); }
+bool gemm_uses_gemv(int64_t M, int route) { return M <= kGemvKernelMaxM && route != kRouteTiled; }
 
 GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, int64_t G, int cus)
 {
@@ -887,18 +852,18 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, int64_t G, int cus)
     return p;
 }
 
-int64_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t G)
+int64_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t G, int cus)
 {
-    const GemmPlan p = plan_gemm(M, N, K, G, planning_cus());
+    const GemmPlan p = plan_gemm(M, N, K, G, cus);
     return p.splits > 1 ? p.splits * M * N * (int64_t)sizeof(float) : 0;
 }
 
 hipError_t launch_gemm(int bits, const uint16_t *x, const void *packed, uint16_t *y, int64_t M, const Layout &lay,
-                       void *workspace, hipStream_t stream, int act)
+                       void *workspace, hipStream_t stream, int cus, int act)
 {
     if (act != kActNone && lay.N % kBlockCols)
         return hipErrorInvalidValue;
-    const GemmPlan plan = plan_gemm(M, lay.N, lay.K, lay.G, planning_cus());
+    const GemmPlan plan = plan_gemm(M, lay.N, lay.K, lay.G, cus);
     float *ws = plan.splits > 1 ? static_cast<float *>(workspace) : nullptr;
     const uint8_t *pk = static_cast<const uint8_t *>(packed);
     const int mode = lay.tiles_per_group == 1 ? kGOneTile

@@ -27,6 +27,7 @@
 // combine in a fixed order, so results are deterministic.
 #include "tf_common.h"
 #include "tf_launch.h"
+#include "tf_operands.h"
 
 namespace tf {
 
@@ -39,52 +40,6 @@ constexpr int kGemvMaxSplits = 16;
 // SiLU, x * sigmoid(x) = x / (1 + e^-x); at large negative x the
 // exponential overflows to +inf and the quotient is -0, the limit.
 __device__ __forceinline__ float silu(float v) { return v / (1.f + expf(-v)); }
-
-// Eight W4 codes (one column, rows 0..7 of an octet) -> B operand of bf16
-// values 128 + q: OR-ing a nibble into the mantissa of bf16 128.0 (0x4300).
-// `magic` is 0x43004300 held in a vector register, so each pair costs one
-// v_and_or_b32 (the mask comes from a scalar register).
-__device__ __forceinline__ u32x4 w4_operand(uint32_t w, uint32_t magic)
-{
-    u32x4 b;
-    b[0] = (w & 0x000F000Fu) | magic;
-    b[1] = ((w >> 4) & 0x000F000Fu) | magic;
-    b[2] = ((w >> 8) & 0x000F000Fu) | magic;
-    b[3] = ((w >> 12) & 0x000F000Fu) | magic;
-    return b;
-}
-
-__device__ __forceinline__ uint32_t magic_in_vgpr()
-{
-    uint32_t m;
-    asm volatile("v_mov_b32 %0, 0x43004300" : "=v"(m));
-    return m;
-}
-
-// Eight W8 codes (bytes of w0, w1) -> B operand of the bf16 values q (exact).
-__device__ __forceinline__ u32x4 w8_operand(uint32_t w0, uint32_t w1)
-{
-    u32x4 b;
-    b[0] = pack_bf16x2((float)(w0 & 0xFFu), (float)((w0 >> 8) & 0xFFu));
-    b[1] = pack_bf16x2((float)((w0 >> 16) & 0xFFu), (float)(w0 >> 24));
-    b[2] = pack_bf16x2((float)(w1 & 0xFFu), (float)((w1 >> 8) & 0xFFu));
-    b[3] = pack_bf16x2((float)((w1 >> 16) & 0xFFu), (float)(w1 >> 24));
-    return b;
-}
-
-// B operand whose eight rows all hold the zero point, in the same form as the
-// code operand: bf16(128 + z) for W4, bf16(z) for W8.
-template <int BITS> __device__ __forceinline__ u32x4 zero_operand(uint32_t z)
-{
-    uint32_t v;
-    if constexpr (BITS == 4) {
-        const uint32_t h = 0x4300u | z;
-        v = h | (h << 16);
-    } else {
-        v = pack_bf16x2((float)z, (float)z);
-    }
-    return u32x4{v, v, v, v};
-}
 
 // The codes of one k-tile held by one lane: W4 16 bytes, W8 32 bytes.
 template <int BITS> struct TileCodes {
@@ -944,18 +899,35 @@ static void launch_mid_bits(dim3 grid, const MidChunks &ch, hipStream_t stream, 
         launch_mid_mt<BITS, 4, 4, ACT>(grid, ch, stream, x, pk, y, lay, M, ws);
 }
 
+// Most 8-byte record words one chunk of `tiles` k-tiles touches in a block:
+// the groups from the chunk's first row to its last.  A chunk starting
+// mid-group touches one group more than its k-tiles alone would hold.
+static int64_t mid_max_rec_words(int bits, const Layout &lay, int64_t tiles)
+{
+    const int64_t gpt = lay.whole_tiles() ? 1 : lay.groups_per_tile;
+    return (tiles * gpt + 1) * record_bytes(bits) / 8;
+}
+
+// The staging registers of gemv_mid_kernel hold kMidRecRegs words per
+// thread: kMidRecRegs * 64 * kMidWaves over the workgroup's blocks.
+constexpr int64_t kMidRecCapacity = (int64_t)kMidRecRegs * 64 * kMidWaves;
+
 template <int ACT = kActNone>
 static hipError_t launch_gemv_mid(int bits, const uint16_t *x, const uint8_t *pk, uint16_t *y, int64_t M,
-                                  const Layout &lay, void *workspace, hipStream_t stream)
+                                  const Layout &lay, void *workspace, hipStream_t stream, int cus)
 {
     int64_t split_tiles = 0;
-    const int64_t splits = gemv_splits(lay, M, planning_cus(), &split_tiles);
+    const int64_t splits = gemv_splits(lay, M, cus, &split_tiles);
     const MidChunks ch = plan_mid(bits, lay, M, split_tiles);
     // the kernel stages a chunk's activations with mid_xregs loads per
-    // thread, walks chunks of ch.tiles > 0 k-tiles, and needs its LDS
+    // thread and its records with kMidRecRegs loads per thread, walks chunks
+    // of ch.tiles > 0 k-tiles, and needs its LDS; a plan outside those
+    // limits is refused rather than launched
     const int D = mid_depth(M);
+    const int64_t rec_words = mid_max_rec_words(bits, lay, ch.tiles);
     if (ch.tiles < 1 || (ch.tiles % D != 0 && ch.tiles < split_tiles) ||
-        M * ch.tiles * (kTileRows / 8) > mid_xunits(M) || ch.lds > kGemvMaxLds)
+        M * ch.tiles * (kTileRows / 8) > mid_xunits(M) || ch.lds > kGemvMaxLds ||
+        kMidWaves * rec_words > kMidRecCapacity || 8 * rec_words > ch.meta_cap)
         return hipErrorInvalidValue;
     const dim3 grid((unsigned)((lay.nblocks + kMidWaves - 1) / kMidWaves), (unsigned)splits);
     float *ws = splits > 1 ? static_cast<float *>(workspace) : nullptr;
@@ -972,15 +944,58 @@ static hipError_t launch_gemv_mid(int bits, const uint16_t *x, const uint8_t *pk
     return hipGetLastError();
 }
 
-hipError_t launch_gemv(int bits, const uint16_t *x, const void *packed, uint16_t *y, int64_t M, const Layout &lay,
-                       void *workspace, hipStream_t stream)
+GemvPlanInfo gemv_plan_info(int bits, const Layout &lay, int64_t M, int cus)
 {
-    const uint8_t *pk = static_cast<const uint8_t *>(packed);
-    if (use_mid(lay, M, planning_cus()))
-        return launch_gemv_mid(bits, x, pk, y, M, lay, workspace, stream);
+    GemvPlanInfo p{};
+    p.lds_limit = kGemvMaxLds;
+    if (use_mid(lay, M, cus)) {
+        int64_t st = 0;
+        p.kernel = 1;
+        p.splits = gemv_splits(lay, M, cus, &st);
+        p.split_tiles = st;
+        const MidChunks ch = plan_mid(bits, lay, M, st);
+        p.waves = kMidWaves;
+        p.bpw = kMidWaves;
+        p.chunk_tiles = ch.tiles;
+        p.depth = mid_depth(M);
+        p.row_chunks = mid_mt(M);
+        p.lds = ch.lds;
+        p.x_capacity = mid_xunits(M);
+        p.rec_capacity = kMidRecCapacity;
+        p.meta_cap = ch.meta_cap;
+        p.xpitch = ch.xpitch;
+        return p;
+    }
     const int W = gemv_waves(lay, M);
     const int bpw = gemv_bpw(lay, M);
     const GemvChunks ch = plan_chunks(bits, lay, M, W, bpw);
+    p.kernel = 0;
+    p.waves = W;
+    p.bpw = bpw;
+    p.splits = 1;
+    p.split_tiles = lay.ktiles;
+    p.chunk_tiles = ch.tiles;
+    p.depth = lay.ktiles / (W / bpw) <= 3 ? 2 : 4;
+    p.row_chunks = 1;
+    p.lds = ch.lds;
+    p.x_capacity = 0; // staged by a loop: no fixed capacity
+    p.rec_capacity = 0;
+    p.meta_cap = ch.meta_cap;
+    p.xpitch = ch.xpitch;
+    return p;
+}
+
+hipError_t launch_gemv(int bits, const uint16_t *x, const void *packed, uint16_t *y, int64_t M, const Layout &lay,
+                       void *workspace, hipStream_t stream, int cus)
+{
+    const uint8_t *pk = static_cast<const uint8_t *>(packed);
+    if (use_mid(lay, M, cus))
+        return launch_gemv_mid(bits, x, pk, y, M, lay, workspace, stream, cus);
+    const int W = gemv_waves(lay, M);
+    const int bpw = gemv_bpw(lay, M);
+    const GemvChunks ch = plan_chunks(bits, lay, M, W, bpw);
+    if (ch.tiles < 1 || ch.lds > kGemvMaxLds)
+        return hipErrorInvalidValue;
     const dim3 grid((unsigned)((lay.nblocks + bpw - 1) / bpw)), block(64 * W);
     if (bits == 4)
         launch_gemv_bits<4>(lay, grid, block, ch, stream, x, pk, y, (int)M);
@@ -997,16 +1012,18 @@ void launch_splitk_sum_silu(const float *ws, int splits, int64_t M, int64_t N, u
 // The gate/up GEMV with the SiLU product: the kernel the plain GEMV of the
 // same shape runs, on its grid (each block pairs its own columns).
 hipError_t launch_gemv_silu_mul(int bits, const uint16_t *x, const void *packed, uint16_t *y, int64_t M,
-                                const Layout &lay, void *workspace, hipStream_t stream)
+                                const Layout &lay, void *workspace, hipStream_t stream, int cus)
 {
     if (lay.N % kBlockCols || M < 1 || M > kGemvKernelMaxM)
         return hipErrorInvalidValue;
-    if (use_mid(lay, M, planning_cus()))
+    if (use_mid(lay, M, cus))
         return launch_gemv_mid<kActSiluMul>(bits, x, static_cast<const uint8_t *>(packed), y, M, lay, workspace,
-                                            stream);
+                                            stream, cus);
     const int W = gemv_waves(lay, M);
     const int bpw = gemv_bpw(lay, M);
     const GemvChunks ch = plan_chunks(bits, lay, M, W, bpw);
+    if (ch.tiles < 1 || ch.lds > kGemvMaxLds)
+        return hipErrorInvalidValue;
     const dim3 grid((unsigned)((lay.nblocks + bpw - 1) / bpw)), block(64 * W);
     const uint8_t *pk = static_cast<const uint8_t *>(packed);
     if (bits == 4)

@@ -7,6 +7,7 @@
 // checkpoint reads are gathers the caches absorb; this runs once per weight.
 #include "tf_common.h"
 #include "tf_launch.h"
+#include "tf_operands.h"
 
 namespace tf {
 
@@ -134,10 +135,16 @@ __global__ __launch_bounds__(256) void repack_records(const void *__restrict__ q
 }
 
 // ---------------------------------------------------------------------------
-// Dequantization test hook: w[k][n] = (q - z) * s in fp32, through the same
-// unpack + dequant helpers the GEMM stages its tiles with.
+// Dequantization test hooks: w[k][n] = (q - z) * s in fp32, decoded by the
+// kernels' own operand builders (tf_operands.h), so that a bit-exact match
+// with the oracle pins the code the kernels run:
+//   GEMV = false: the GEMM's unpack_w4 / unpack_w8, the exact bf16 q - z of
+//                 its LDS weight tile, times s;
+//   GEMV = true:  the GEMV's w4_operand / w8_operand and zero_operand (bf16
+//                 128 + q and 128 + z, or q and z), their difference times s.
+// Both products are exact in fp32 (at most 8 significant bits each).
 // ---------------------------------------------------------------------------
-template <int BITS>
+template <int BITS, bool GEMV>
 __global__ __launch_bounds__(256) void dequant_f32(const uint8_t *__restrict__ packed, Layout lay,
                                                    float *__restrict__ w, int64_t units)
 {
@@ -154,6 +161,7 @@ __global__ __launch_bounds__(256) void dequant_f32(const uint8_t *__restrict__ p
     if (n >= lay.N)
         return;
     const u32x4 cw = load16(packed + lay.tile(BITS, blk, t) + 1024 * h + 16 * L);
+    const uint32_t magic = magic_in_vgpr();
     constexpr int kSteps = BITS == 4 ? 4 : 2;
 #pragma unroll
     for (int uu = 0; uu < kSteps; ++uu) {
@@ -163,15 +171,28 @@ __global__ __launch_bounds__(256) void dequant_f32(const uint8_t *__restrict__ p
             continue;
         const uint8_t *rec = packed + lay.record(BITS, blk, k0 / lay.G);
         const float sv = record_scale<BITS>(rec, r);
-        const float zv = (float)record_zero<BITS>(rec, r);
-        float f[8];
-        if constexpr (BITS == 4)
-            dequant_w4_word(cw[u], sv, -zv * sv, f);
-        else
-            dequant_w8_pair(cw[2 * uu], cw[2 * uu + 1], sv, -zv * sv, f);
+        const uint32_t zq = record_zero<BITS>(rec, r);
+        // eight rows of column n as bf16 pairs (rows 2i, 2i + 1 in word i)
+        u32x4 op, zop = {0u, 0u, 0u, 0u};
+        if constexpr (GEMV) {
+            if constexpr (BITS == 4)
+                op = w4_operand(cw[u], magic);
+            else
+                op = w8_operand(cw[2 * uu], cw[2 * uu + 1]);
+            zop = zero_operand<BITS>(zq);
+        } else {
+            if constexpr (BITS == 4)
+                op = unpack_w4(cw[u], 1.f, -(float)zq);
+            else
+                op = unpack_w8(cw[2 * uu], cw[2 * uu + 1], 1.f, -(float)zq);
+        }
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-            w[(k0 + i) * lay.N + n] = f[i];
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t sh = 16u * (uint32_t)(i & 1);
+            const float b = bf16_bits_to_f32((op[i >> 1] >> sh) & 0xFFFFu);
+            const float d = GEMV ? b - bf16_bits_to_f32((zop[i >> 1] >> sh) & 0xFFFFu) : b;
+            w[(k0 + i) * lay.N + n] = d * sv;
+        }
     }
 }
 
@@ -197,14 +218,22 @@ hipError_t launch_repack(int bits, const void *qweight, const void *qzeros, cons
     return hipGetLastError();
 }
 
-hipError_t launch_dequant_f32(int bits, const void *packed, const Layout &lay, float *w, hipStream_t stream)
+hipError_t launch_dequant_f32(int bits, const void *packed, const Layout &lay, float *w, hipStream_t stream,
+                              bool gemv)
 {
     const uint8_t *in = static_cast<const uint8_t *>(packed);
     const int64_t units = lay.nblocks * lay.ktiles * (bits == 4 ? 64 : 128);
-    if (bits == 4)
-        dequant_f32<4><<<grid_for(units), 256, 0, stream>>>(in, lay, w, units);
-    else
-        dequant_f32<8><<<grid_for(units), 256, 0, stream>>>(in, lay, w, units);
+    if (bits == 4) {
+        if (gemv)
+            dequant_f32<4, true><<<grid_for(units), 256, 0, stream>>>(in, lay, w, units);
+        else
+            dequant_f32<4, false><<<grid_for(units), 256, 0, stream>>>(in, lay, w, units);
+    } else {
+        if (gemv)
+            dequant_f32<8, true><<<grid_for(units), 256, 0, stream>>>(in, lay, w, units);
+        else
+            dequant_f32<8, false><<<grid_for(units), 256, 0, stream>>>(in, lay, w, units);
+    }
     return hipGetLastError();
 }
 

@@ -120,36 +120,6 @@ __device__ __forceinline__ f32x4 mfma16x16x32(const u32x4 &a, const u32x4 &b, co
                                                    0, 0, 0);
 }
 
-// Exact fp32 dequantization of eight W4 codes (rows 0..7 of one column's
-// k-octet) packed in one word: w = q * s + c with c = -z * s, which equals
-// (q - z) * s exactly (both products and their difference fit in 24 bits).
-__device__ __forceinline__ void dequant_w4_word(uint32_t wd, float s, float c, float out[8])
-{
-    const uint32_t lo = wd & 0x0F0F0F0Fu;        // nibbles 0,2,4,6 -> rows 0,4,1,5
-    const uint32_t hi = (wd >> 4) & 0x0F0F0F0Fu; // nibbles 1,3,5,7 -> rows 2,6,3,7
-    out[0] = fmaf((float)(lo & 0xFFu), s, c);
-    out[4] = fmaf((float)((lo >> 8) & 0xFFu), s, c);
-    out[1] = fmaf((float)((lo >> 16) & 0xFFu), s, c);
-    out[5] = fmaf((float)(lo >> 24), s, c);
-    out[2] = fmaf((float)(hi & 0xFFu), s, c);
-    out[6] = fmaf((float)((hi >> 8) & 0xFFu), s, c);
-    out[3] = fmaf((float)((hi >> 16) & 0xFFu), s, c);
-    out[7] = fmaf((float)(hi >> 24), s, c);
-}
-
-// Same for eight W8 codes held in two words (row i in byte i).
-__device__ __forceinline__ void dequant_w8_pair(uint32_t w0, uint32_t w1, float s, float c, float out[8])
-{
-    out[0] = fmaf((float)(w0 & 0xFFu), s, c);
-    out[1] = fmaf((float)((w0 >> 8) & 0xFFu), s, c);
-    out[2] = fmaf((float)((w0 >> 16) & 0xFFu), s, c);
-    out[3] = fmaf((float)(w0 >> 24), s, c);
-    out[4] = fmaf((float)(w1 & 0xFFu), s, c);
-    out[5] = fmaf((float)((w1 >> 8) & 0xFFu), s, c);
-    out[6] = fmaf((float)((w1 >> 16) & 0xFFu), s, c);
-    out[7] = fmaf((float)(w1 >> 24), s, c);
-}
-
 __device__ __forceinline__ u32x4 load16(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
 
 // Streamed once per call: hint the memory system not to keep the lines.

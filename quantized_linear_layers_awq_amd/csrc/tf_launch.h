@@ -10,7 +10,12 @@ namespace tf {
 // j is gate column 8 j + c (c < 8) or up column 8 j + c - 8 (c >= 8).
 hipError_t launch_repack(int bits, const void *qweight, const void *qzeros, const uint16_t *scales,
                          const Layout &lay, void *packed, hipStream_t stream, int64_t pair_half = 0);
-hipError_t launch_dequant_f32(int bits, const void *packed, const Layout &lay, float *w, hipStream_t stream);
+// The fp32 weights (q - z) * s decoded from a packed buffer by the GEMM's
+// operand builder (gemv = false: exact bf16 q - z, times s) or the GEMV's
+// (gemv = true: bf16 128 + q and 128 + z for W4, q and z for W8, their
+// difference times s).
+hipError_t launch_dequant_f32(int bits, const void *packed, const Layout &lay, float *w, hipStream_t stream,
+                              bool gemv);
 
 // Waves per GEMV workgroup for M <= 16 activation rows (one workgroup per
 // 16-column block, or per two or four blocks of a wide layer at M >= 2).
@@ -20,12 +25,31 @@ int gemv_waves(const Layout &lay, int64_t M);
 // its K ranges are long enough, on a layer too narrow to fill `cus` compute
 // units; 1 otherwise) and k-tiles per range.
 int64_t gemv_splits(const Layout &lay, int64_t M, int cus, int64_t *split_tiles);
+// The GEMV launch plan a call of (bits, M) rows would run on `cus` compute
+// units, for host-side checks of its invariants (no GPU work):
+struct GemvPlanInfo {
+    int64_t kernel;       // 0: the kernel for up to 16 rows, 1: the 16-row-chunk kernel
+    int64_t waves;        // waves per workgroup
+    int64_t bpw;          // 16-column blocks per workgroup
+    int64_t splits;       // K ranges over workgroups
+    int64_t split_tiles;  // k-tiles per range
+    int64_t chunk_tiles;  // k-tiles per staged chunk
+    int64_t depth;        // code loads in flight per wave (k-tiles)
+    int64_t row_chunks;   // 16-row chunks per wave (kernel 1)
+    int64_t lds;          // dynamic LDS bytes per workgroup
+    int64_t lds_limit;    // the most the launcher allows
+    int64_t x_capacity;   // 16-byte activation units one staging pass holds (kernel 1)
+    int64_t rec_capacity; // 8-byte record words one staging pass holds over all blocks (kernel 1)
+    int64_t meta_cap;     // bytes reserved per block for a chunk's records
+    int64_t xpitch;       // bf16 elements per staged activation row
+};
+GemvPlanInfo gemv_plan_info(int bits, const Layout &lay, int64_t M, int cus);
 // Workspace bytes of a GEMV launch: fp32 partial sums when it splits K.
 int64_t gemv_workspace_bytes(const Layout &lay, int64_t M, int cus);
 // Largest M the GEMV kernel takes (16-row chunks, up to four per wave).
 constexpr int64_t kGemvKernelMaxM = 64;
 hipError_t launch_gemv(int bits, const uint16_t *x, const void *packed, uint16_t *y, int64_t M, const Layout &lay,
-                       void *workspace, hipStream_t stream);
+                       void *workspace, hipStream_t stream, int cus);
 // Epilogue of the GEMV kernel: none, or silu(gate) * up over a [gate | up]
 // layer (launch_gemv_silu_mul).
 constexpr int kActNone = 0, kActSiluMul = 1;
@@ -34,7 +58,7 @@ constexpr int kActNone = 0, kActSiluMul = 1;
 // 0), 1 <= M <= kGemvKernelMaxM; y is [M][N/2].  Same kernel choice, and so
 // the same workspace (gemv_workspace_bytes), as launch_gemv of that shape.
 hipError_t launch_gemv_silu_mul(int bits, const uint16_t *x, const void *packed, uint16_t *y, int64_t M,
-                                const Layout &lay, void *workspace, hipStream_t stream);
+                                const Layout &lay, void *workspace, hipStream_t stream, int cus);
 // Sum of a SiLU-product launch's K ranges: y[m][8 j + c] = silu(g) * u from
 // the in-order sums of the partials ws[s][m][16 j + c] and ws[s][m][16 j + c + 8].
 void launch_splitk_sum_silu(const float *ws, int splits, int64_t M, int64_t N, uint16_t *y, hipStream_t stream);
@@ -53,21 +77,23 @@ struct GemmPlan {
     int64_t m_tiles, wide_cols, narrow_cols, splits, split_tiles, rows;
 };
 GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, int64_t G, int cus);
-// Compute units plan_gemm assumes: the forced count, else the device's.
-int planning_cus();
-// Force the compute units plan_gemm assumes (0: the current device's).
-void set_planning_cus(int n);
-// Workspace bytes of the tiled GEMM (0 unless it splits K).
-int64_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t G);
-// Which kernel a GEMM call of M rows runs: the GEMV kernel (M <= 64: the
-// tiled GEMM would compute 256-row tiles) or the tiled GEMM.  The route can
-// be forced for tests: 0 automatic, 1 tiled GEMM, 2 GEMV kernel where M <= 64.
-bool gemm_uses_gemv(int64_t M);
-void set_gemm_route(int route);
+// Compute units of the current device (queried once per device and kept:
+// the library's only process-wide state).
+int device_cus();
+// Workspace bytes of the tiled GEMM planned for `cus` compute units (0
+// unless it splits K).
+int64_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t G, int cus);
+// Which kernel a GEMM call of M rows runs: the GEMV kernels (M <= 64: the
+// tiled GEMM would compute 128- or 256-row tiles) or the tiled GEMM.  The
+// route is an argument: kRouteAuto in every product call; the test hooks
+// may pass kRouteTiled (the tiled GEMM at any M) or kRouteGemv (the GEMV
+// kernels up to 64 rows).
+constexpr int kRouteAuto = 0, kRouteTiled = 1, kRouteGemv = 2;
+bool gemm_uses_gemv(int64_t M, int route);
 // act = kActSiluMul: a [gate | up] layer packed with pair_half = N/2, y is
 // [M][N/2] = silu(gate) * up (as launch_gemv_silu_mul).
 hipError_t launch_gemm(int bits, const uint16_t *x, const void *packed, uint16_t *y, int64_t M, const Layout &lay,
-                       void *workspace, hipStream_t stream, int act = kActNone);
+                       void *workspace, hipStream_t stream, int cus, int act = kActNone);
 
 // Measurement probes (not on the hot path).
 hipError_t launch_probe_read(const void *buf, uint64_t bytes, uint32_t *sink, hipStream_t stream);

@@ -76,11 +76,33 @@ def sample_indices(n, count, seed):
     return np.unique(np.concatenate([[0, n - 1], idx]))
 
 
-def check_linear(case, torch, q, gemm, rows=None, cols=None, packed=None, d=None):
-    """Run the HIP path on the whole case, compare the chosen rows/columns."""
+def device_cus(torch):
+    return torch.cuda.get_device_properties(0).multi_processor_count
+
+
+def run_linear(q, bits, op, x, packed, K, N, G, cus=0, route=0, y=None, torch=None):
+    """One call of the linear op (q.TF_OP_*) through the C ABI: the product
+    entry point when cus == 0 and route == 0 (automatic), else
+    tf_linear_planned with those plan inputs (cus 0: the device's count)."""
+    if cus == 0 and route == 0:
+        fn = {q.TF_OP_GEMV: linear_fn(q, bits, False), q.TF_OP_GEMM: linear_fn(q, bits, True),
+              q.TF_OP_GEMV_SILU_MUL: q.tf_gemv_w4a16_silu_mul if bits == 4 else q.tf_gemv_w8a16_silu_mul,
+              q.TF_OP_GEMM_SILU_MUL: q.tf_gemm_w4a16_silu_mul if bits == 4 else q.tf_gemm_w8a16_silu_mul}[op]
+        return fn(x, packed, K, N, G, y=y)
+    if cus == 0:
+        import torch as _torch
+
+        cus = device_cus(torch or _torch)
+    return q.tf_linear_planned(bits, op, x, packed, K, N, G, cus, route, y=y)
+
+
+def check_linear(case, torch, q, gemm, rows=None, cols=None, packed=None, d=None, cus=0, route=0):
+    """Run the HIP path on the whole case, compare the chosen rows/columns.
+    cus / route: the plan inputs (0, 0: the product call as routed)."""
     d = d or to_device(case, torch)
     packed = packed if packed is not None else repack(case, d, q)
-    y = linear_fn(q, case.bits, gemm)(d["x"], packed, case.K, case.N, case.G)
+    op = q.TF_OP_GEMM if gemm else q.TF_OP_GEMV
+    y = run_linear(q, case.bits, op, d["x"], packed, case.K, case.N, case.G, cus=cus, route=route, torch=torch)
     torch.cuda.synchronize()
     yh = bf16_to_f64(y)
     ref = oracle.awq_linear(case, cols=cols, rows=rows)
@@ -90,49 +112,21 @@ def check_linear(case, torch, q, gemm, rows=None, cols=None, packed=None, d=None
     return ok, ratio, y
 
 
-class planning_cus:
-    """Within the block, GEMM calls plan their launches for n compute units
-    (n = 1: one launch of 128-column tiles; see tf_gemm_plan)."""
-
-    def __init__(self, q, n):
-        self.q, self.n = q, n
-
-    def __enter__(self):
-        self.q.tf_gemm_set_planning_cus(self.n)
-
-    def __exit__(self, *exc):
-        self.q.tf_gemm_set_planning_cus(0)
-
-
-class gemm_route:
-    """Within the block, GEMM calls with M <= 64 run the given kernel
-    (1 the tiled GEMM, 2 the GEMV kernel; see tf_gemm_set_route)."""
-
-    def __init__(self, q, route):
-        self.q, self.route = q, route
-
-    def __enter__(self):
-        self.q.tf_gemm_set_route(self.route)
-
-    def __exit__(self, *exc):
-        self.q.tf_gemm_set_route(0)
-
-
 def split_cus(q, bits, M, K, N, G):
-    """A compute-unit count for which the GEMM plan has both 128- and
+    """A compute-unit count for which the tiled GEMM's plan has both 128- and
     64-column tiles and does not split K, or None if no count gives one."""
     mt = -(-M // 256)
     tiles = mt * -(-N // 128)
     for cus in range(2, tiles + 1):
-        _, wide, narrow, splits, _, _, _ = q.tf_gemm_plan(bits, M, K, N, G, cus)
+        _, wide, narrow, splits, _, _, _ = q.tf_gemm_plan(bits, M, K, N, G, cus, q.TF_ROUTE_TILED)
         if wide and narrow and splits == 1:
             return cus
     return None
 
 
 def splitk_cus(q, bits, M, K, N, G):
-    """A compute-unit count for which the GEMM plan splits K, or None."""
+    """A compute-unit count for which the tiled GEMM's plan splits K, or None."""
     for cus in (256, 1024, 4096, 1 << 20):
-        if q.tf_gemm_plan(bits, M, K, N, G, cus)[3] > 1:
+        if q.tf_gemm_plan(bits, M, K, N, G, cus, q.TF_ROUTE_TILED)[3] > 1:
             return cus
     return None

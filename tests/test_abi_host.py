@@ -88,15 +88,11 @@ def test_packed_bytes_invalid_shapes_are_zero(lib, K, N, G):
     assert lib.tf_packed_bytes_w4(K, N, G) == 0
 
 
-@pytest.fixture
-def tiled_route(lib):
-    """GEMM calls and plans with M <= 64 use the tiled GEMM within the test."""
-    lib.tf_gemm_set_route(1)
-    yield
-    lib.tf_gemm_set_route(0)
+ROUTE_AUTO, ROUTE_TILED, ROUTE_GEMV = 0, 1, 2
+OP_GEMV, OP_GEMM, OP_GEMV_SILU, OP_GEMM_SILU = 0, 1, 2, 3
 
 
-@pytest.mark.parametrize("route", [0, 1])
+@pytest.mark.parametrize("route", [ROUTE_AUTO, ROUTE_TILED])
 @pytest.mark.parametrize("M,K,N,G", [(1, 4096, 4096, 128), (8, 14336, 4096, 128), (16, 4096, 1024, 128),
                                      (1, 8192, 8192, 8192), (512, 8192, 8192, 8192), (2048, 4096, 14336, 128),
                                      (64, 4096, 4096, 128), (33, 14336, 4096, 128), (64, 256, 1024, 128)])
@@ -104,51 +100,60 @@ def test_workspace_cannot_hold_bf16_weights(lib, route, M, K, N, G):
     # The layer never materialises full-precision weights: its only scratch is
     # fp32 partial outputs of a K split (at most 16 x M x N, and at most one
     # range per two k-tiles), smaller than a bf16 copy of W for every shape.
-    lib.tf_gemm_set_route(route)
-    try:
-        for bits in (4, 8):
-            for gemm in (0, 1):
-                if not gemm and M > 16:
-                    continue
-                ws = lib.tf_workspace_bytes(bits, gemm, M, K, N, G)
+    for bits in (4, 8):
+        for op in (OP_GEMV, OP_GEMM):
+            if op == OP_GEMV and M > 16:
+                continue
+            for cus in (1, 80, 256, 304):  # devices of up to 304 compute units
+                ws = lib.tf_workspace_bytes_planned(bits, op, M, K, N, G, cus, route)
                 assert ws <= 16 * M * N * 4
                 assert ws < K * N * 2
-    finally:
-        lib.tf_gemm_set_route(0)
 
 
-def _plan(lib, M, N, cus, K=4096, G=128, bits=4):
+def _plan(lib, M, N, cus, K=4096, G=128, bits=4, route=ROUTE_AUTO):
     out = (ctypes.c_int64 * 7)()
-    st = lib.tf_gemm_plan(bits, M, K, N, G, cus, out)
+    st = lib.tf_gemm_plan(bits, M, K, N, G, cus, route, out)
     return st, tuple(out)
 
 
-@pytest.mark.parametrize("route", [0, 1])
+@pytest.mark.parametrize("route", [ROUTE_AUTO, ROUTE_TILED])
 def test_workspace_only_for_split_k(lib, route):
     """A call needs S x M x N fp32 partial sums exactly when its plan splits
-    K, whichever kernel it runs; tf_gemv_* below 8 rows never does (this
-    host has no GPU, so plans assume the library's default of 256 compute
-    units)."""
-    lib.tf_gemm_set_route(route)
-    try:
-        assert lib.tf_workspace_bytes(4, 0, 1, 4096, 4096, 128) == 0
-        assert lib.tf_workspace_bytes(8, 0, 7, 8192, 8192, 8192) == 0
-        assert lib.tf_workspace_bytes(4, 0, 17, 4096, 4096, 128) == 0  # beyond the GEMV's M
-        # 16 rows, per-channel W8 8192 x 8192: the 16-row-chunk kernel in four K ranges
-        st, (_, _, _, splits, _, _, _) = _plan(lib, 16, 8192, 256, K=8192, G=8192, bits=8)
-        assert lib.tf_workspace_bytes(8, 0, 16, 8192, 8192, 8192) == (16 * 8192 * 4 * splits if splits > 1 else 0)
-        assert lib.tf_workspace_bytes(5, 1, 1, 4096, 4096, 128) == 0
-        for bits, M, K, N, G in [(8, 512, 8192, 8192, 8192), (4, 1, 4096, 4096, 128), (4, 2048, 4096, 14336, 128),
-                                 (4, 100, 1024, 200, 64), (4, 64, 384, 64, 128), (4, 48, 4096, 4096, 128),
-                                 (8, 20, 8192, 1024, 8192), (4, 64, 4096, 28672, 128)]:
-            st, (_, _, _, splits, _, _, _) = _plan(lib, M, N, 256, K=K, G=G, bits=bits)
-            assert st == TF_OK
-            want = splits * M * N * 4 if splits > 1 else 0
-            assert lib.tf_workspace_bytes(bits, 1, M, K, N, G) == want
-        assert _plan(lib, 512, 8192, 256, K=8192, G=8192, bits=8)[1][3] == 2   # W8 M=512: two K ranges
-        assert _plan(lib, 2048, 14336, 256)[1][3] == 1                         # prefill: no split
-    finally:
-        lib.tf_gemm_set_route(0)
+    K, whichever kernel it runs; tf_gemv_* below 8 rows never does.  The
+    SiLU-product calls need what the plain call of their shape needs."""
+    ws = lambda bits, op, M, K, N, G, cus=256: lib.tf_workspace_bytes_planned(bits, op, M, K, N, G, cus, route)
+    assert ws(4, OP_GEMV, 1, 4096, 4096, 128) == 0
+    assert ws(8, OP_GEMV, 7, 8192, 8192, 8192) == 0
+    assert ws(4, OP_GEMV, 17, 4096, 4096, 128) == 0  # beyond the GEMV's M
+    # 16 rows, per-channel W8 8192 x 8192: the 16-row-chunk kernel in four K ranges
+    st, (_, _, _, splits, _, _, _) = _plan(lib, 16, 8192, 256, K=8192, G=8192, bits=8)
+    assert ws(8, OP_GEMV, 16, 8192, 8192, 8192) == (16 * 8192 * 4 * splits if splits > 1 else 0)
+    assert ws(8, OP_GEMV_SILU, 16, 8192, 8192, 8192) == ws(8, OP_GEMV, 16, 8192, 8192, 8192)
+    assert lib.tf_workspace_bytes_planned(5, OP_GEMM, 1, 4096, 4096, 128, 256, route) == 0
+    for bits, M, K, N, G in [(8, 512, 8192, 8192, 8192), (4, 1, 4096, 4096, 128), (4, 2048, 4096, 14336, 128),
+                             (4, 100, 1024, 200, 64), (4, 64, 384, 64, 128), (4, 48, 4096, 4096, 128),
+                             (8, 20, 8192, 1024, 8192), (4, 64, 4096, 28672, 128)]:
+        st, (_, _, _, splits, _, _, _) = _plan(lib, M, N, 256, K=K, G=G, bits=bits, route=route)
+        assert st == TF_OK
+        want = splits * M * N * 4 if splits > 1 else 0
+        assert ws(bits, OP_GEMM, M, K, N, G) == want
+        assert ws(bits, OP_GEMM_SILU, M, K, N, G) == want
+    assert _plan(lib, 512, 8192, 256, K=8192, G=8192, bits=8)[1][3] == 2   # W8 M=512: two K ranges
+    assert _plan(lib, 2048, 14336, 256)[1][3] == 1                         # prefill: no split
+
+
+def test_plan_hooks_keep_no_state(lib):
+    """The plan inputs are per call: a query with one route or compute-unit
+    count leaves every later query unchanged (no process-wide setting)."""
+    before = [_plan(lib, M, 4096, 256) for M in (1, 40, 64, 65, 2048)]
+    ws_before = lib.tf_workspace_bytes(4, 1, 40, 4096, 4096, 128)
+    for cus, route in ((1, ROUTE_TILED), (4096, ROUTE_GEMV), (7, ROUTE_TILED)):
+        _plan(lib, 40, 4096, cus, route=route)
+        lib.tf_workspace_bytes_planned(4, OP_GEMM, 40, 4096, 4096, 128, cus, route)
+    assert [_plan(lib, M, 4096, 256) for M in (1, 40, 64, 65, 2048)] == before
+    assert lib.tf_workspace_bytes(4, 1, 40, 4096, 4096, 128) == ws_before
+    assert not hasattr(ctypes.CDLL(LIB), "tf_gemm_set_route")
+    assert not hasattr(ctypes.CDLL(LIB), "tf_gemm_set_planning_cus")
 
 
 def test_gemm_route_by_m(lib):
@@ -158,18 +163,11 @@ def test_gemm_route_by_m(lib):
         assert _plan(lib, M, 4096, 256)[1][5] == 1
     for M in (65, 256, 2048):
         assert _plan(lib, M, 4096, 256)[1][5] == 0
-    lib.tf_gemm_set_route(1)
-    try:
-        assert _plan(lib, 1, 4096, 256)[1][5] == 0
-        assert _plan(lib, 64, 4096, 256)[1][5] == 0
-    finally:
-        lib.tf_gemm_set_route(0)
-    lib.tf_gemm_set_route(2)
-    try:
-        assert _plan(lib, 64, 4096, 256)[1][5] == 1
-        assert _plan(lib, 65, 4096, 256)[1][5] == 0
-    finally:
-        lib.tf_gemm_set_route(0)
+    assert _plan(lib, 1, 4096, 256, route=ROUTE_TILED)[1][5] == 0
+    assert _plan(lib, 64, 4096, 256, route=ROUTE_TILED)[1][5] == 0
+    assert _plan(lib, 64, 4096, 256, route=ROUTE_GEMV)[1][5] == 1
+    assert _plan(lib, 65, 4096, 256, route=ROUTE_GEMV)[1][5] == 0
+    assert _plan(lib, 64, 4096, 256, route=9)[0] == 6  # TF_ERR_UNSUPPORTED
 
 
 def test_gemv_route_plan_covers_k_once(lib):
@@ -218,7 +216,7 @@ def test_gemv_route_plan_covers_k_once(lib):
         assert cost(splits) == best, (M, N, cus, K, G, splits)
 
 
-def test_gemm_plan_covers_every_column_once(lib, tiled_route):
+def test_gemm_plan_covers_every_column_once(lib):
     """The launch plan: 128-column tiles from column 0, then 64-column tiles,
     covering [0, N) with no tile wholly past N; the narrow launch exists only
     when the wide tiles miss a whole number of rounds and fits one round.
@@ -234,7 +232,7 @@ def test_gemm_plan_covers_every_column_once(lib, tiled_route):
         cases.append((rng.randint(1, 9000), 8 * rng.randint(1, 5000), rng.choice([1, 2, 3, 7, 64, 80, 256, 304]),
                       K, rng.choice([G, K])))
     for M, N, cus, K, G in cases:
-        st, (mt, wide, narrow, splits, st_tiles, route, rows) = _plan(lib, M, N, cus, K=K, G=G)
+        st, (mt, wide, narrow, splits, st_tiles, route, rows) = _plan(lib, M, N, cus, K=K, G=G, route=ROUTE_TILED)
         assert st == TF_OK and route == 0, (M, N, cus, K, G)
         n_wide = -(-N // 128)
         tiles = mt * n_wide
@@ -271,8 +269,8 @@ def test_gemm_plan_rejects_bad_input(lib):
     assert _plan(lib, 64, 64, 0)[0] == TF_ERR_SHAPE
     assert _plan(lib, 64, 64, 256, K=4096, G=96)[0] == TF_ERR_GROUP
     out = (ctypes.c_int64 * 7)()
-    assert lib.tf_gemm_plan(4, 64, 4096, 64, 128, 256, None) == TF_ERR_NULL
-    assert lib.tf_gemm_plan(5, 64, 4096, 64, 128, 256, out) == 6  # TF_ERR_UNSUPPORTED
+    assert lib.tf_gemm_plan(4, 64, 4096, 64, 128, 256, 0, None) == TF_ERR_NULL
+    assert lib.tf_gemm_plan(5, 64, 4096, 64, 128, 256, 0, out) == 6  # TF_ERR_UNSUPPORTED
 
 
 FAKE = 0x10000  # a 64 KiB-aligned fake device address; never dereferenced

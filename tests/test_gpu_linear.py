@@ -6,8 +6,8 @@ import pytest
 
 import oracle
 import synth
-from gpu_harness import (bf16_bits, bf16_to_f64, check_linear, gemm_route, gpu_or_skip, linear_fn, planning_cus,
-                         repack, split_cus, splitk_cus, to_device)
+from gpu_harness import (bf16_bits, bf16_to_f64, check_linear, gpu_or_skip, linear_fn, repack, run_linear, split_cus,
+                         splitk_cus, to_device, within_tolerance)
 
 pytestmark = pytest.mark.gpu
 
@@ -37,6 +37,13 @@ GEMM_SHAPES = [
     (4, 96, 4096, 256, 512), (8, 64, 3072, 128, 3072), (4, 40, 2080, 128, 32), (4, 16, 2048, 136, 64),
     # between the GEMV kernels' 64 rows and one 256-row tile
     (4, 100, 768, 136, 256), (8, 77, 2080, 40, 32), (8, 128, 512, 64, 32),
+    # 256-row tiles whose plan can run 128- and 64-column tiles in two
+    # launches, W4 and W8, every group rule
+    (4, 600, 1024, 1000, 128), (8, 520, 1024, 456, 128), (8, 384, 2048, 264, 2048), (4, 300, 256, 264, 32),
+    (8, 513, 1024, 392, 32), (4, 700, 512, 1000, 64),
+    # K ranges of 32 rows: K = 32 on the tiled route, and a split whose last
+    # range is one k-tile of 32 rows
+    (4, 300, 32, 64, 32), (4, 100, 2592, 128, 32), (8, 140, 32, 40, 32),
 ]
 
 # GEMM calls with 17 <= M <= 64 run the GEMV kernel with two or four 16-row
@@ -70,8 +77,7 @@ def _plan_cus(q, plan, shape):
         return 0
     if plan == "wide":
         return 1
-    with gemm_route(q, 1):
-        cus = split_cus(q, *shape) if plan == "split" else splitk_cus(q, *shape)
+    cus = split_cus(q, *shape) if plan == "split" else splitk_cus(q, *shape)
     if cus is None:
         pytest.skip(f"no compute-unit count gives a '{plan}' plan for this grid")
     return cus
@@ -86,13 +92,44 @@ def test_gemm_within_tolerance(shape, plan):
     if plan == "tiled" and shape[1] > 64:
         pytest.skip("above 64 rows the automatic route is the tiled GEMM")
     cus = _plan_cus(q, plan, shape)
-    route = 0 if plan == "auto" else 1
-    with gemm_route(q, route):
-        print(f"gemm {shape} plan={plan} cus={cus} {q.tf_gemm_plan(*shape, cus or 256)}", flush=True)
-        c = _case(*shape, seed=2)
-        with planning_cus(q, cus):
-            ok, ratio, _ = check_linear(c, torch, q, gemm=True)
+    route = q.TF_ROUTE_AUTO if plan == "auto" else q.TF_ROUTE_TILED
+    print(f"gemm {shape} plan={plan} cus={cus} {q.tf_gemm_plan(*shape, cus or 256, route)}", flush=True)
+    c = _case(*shape, seed=2)
+    ok, ratio, _ = check_linear(c, torch, q, gemm=True, cus=cus, route=route)
     assert ok, f"worst error / bound = {ratio:.3f}"
+
+
+def test_split_plans_exist_for_both_widths():
+    """The wide + narrow plan is reachable for W4 and W8 shapes of the list
+    above (so the 'split' parametrisations are not all skipped)."""
+    _, q = gpu_or_skip()
+    for bits in (4, 8):
+        assert any(split_cus(q, *s) for s in GEMM_SHAPES if s[0] == bits), bits
+
+
+@pytest.mark.parametrize("shape", [(4, 300, 32, 64, 32), (4, 100, 2592, 128, 32), (8, 140, 32, 40, 32),
+                                   (4, 257, 64, 128, 64)])
+def test_gemm_short_k_ranges_stay_inside_x(shape):
+    """K ranges of 32 or 64 rows: the activation loads of a stage that runs
+    past K are clamped inside each row.  x sits at the start of a buffer
+    whose remainder is NaN, so a load past the last row would reach the
+    output (NaN times a zero weight is NaN)."""
+    torch, q = gpu_or_skip()
+    bits, M, K, N, G = shape
+    cus = splitk_cus(q, *shape) if K > 128 else 0
+    print(f"short-k {shape} cus={cus} {q.tf_gemm_plan(*shape, cus or 256, q.TF_ROUTE_TILED)}", flush=True)
+    c = _case(*shape, seed=8)
+    d = to_device(c, torch)
+    p = repack(c, d, q)
+    big = torch.full((M * K + 4096,), float("nan"), dtype=torch.bfloat16, device="cuda:0")
+    big[:M * K] = d["x"].reshape(-1)
+    x = big[:M * K].view(M, K)
+    y = run_linear(q, bits, q.TF_OP_GEMM, x, p, K, N, G, cus=cus, route=q.TF_ROUTE_TILED, torch=torch)
+    torch.cuda.synchronize()
+    yh = bf16_to_f64(y)
+    assert not np.isnan(yh).any()
+    ok, ratio = within_tolerance(yh, oracle.awq_linear(c))
+    assert ok, ratio
 
 
 @pytest.mark.parametrize("cus", [0, 1, 4096])
@@ -104,33 +141,31 @@ def test_gemm_mid_m_gemv_kernel(shape, cus):
     torch, q = gpu_or_skip()
     print(f"mid {shape} cus={cus} {q.tf_gemm_plan(*shape, cus or 256)}", flush=True)
     c = _case(*shape, seed=6)
-    with planning_cus(q, cus):
-        ok, ratio, _ = check_linear(c, torch, q, gemm=True)
+    ok, ratio, _ = check_linear(c, torch, q, gemm=True, cus=cus)
     assert ok, f"worst error / bound = {ratio:.3f}"
 
 
-@pytest.mark.parametrize("bits,M,K,N,G", [(4, 600, 1024, 1000, 128), (8, 300, 512, 456, 64), (4, 257, 256, 200, 32),
-                                          (8, 40, 1024, 328, 1024)])
+@pytest.mark.parametrize("bits,M,K,N,G", [(4, 600, 1024, 1000, 128), (8, 300, 512, 456, 64), (4, 300, 256, 264, 32),
+                                          (8, 600, 512, 520, 512)])
 def test_gemm_plans_agree_bitwise(bits, M, K, N, G):
     """Every tile width computes each output with the same operations in the
-    same order: all launch plans that do not split K give identical bits."""
+    same order: the single wide launch and the wide + narrow plan (which each
+    of these shapes has) give identical bits."""
     torch, q = gpu_or_skip()
     c = _case(bits, M, K, N, G, seed=5)
     d = to_device(c, torch)
     pk = repack(c, d, q)
-    f = linear_fn(q, bits, True)
+    split = split_cus(q, bits, M, K, N, G)
+    assert split is not None, "the shape must have a wide + narrow plan"
     outs = {}
-    with gemm_route(q, 1):
-        for cus in (1, split_cus(q, bits, M, K, N, G)):
-            if cus is None:
-                continue
-            print(f"plans W{bits} M={M} K={K} N={N} G={G} cus={cus} {q.tf_gemm_plan(bits, M, K, N, G, cus)}",
-                  flush=True)
-            with planning_cus(q, cus):
-                outs[cus] = bf16_bits(f(d["x"], pk, K, N, G))
-    ref = outs[1]
-    for cus, y in outs.items():
-        assert np.array_equal(y, ref), f"plan for {cus} CUs differs from the single wide launch"
+    for cus in (1, split):
+        plan = q.tf_gemm_plan(bits, M, K, N, G, cus, q.TF_ROUTE_TILED)
+        print(f"plans W{bits} M={M} K={K} N={N} G={G} cus={cus} {plan}", flush=True)
+        assert plan[3] == 1
+        outs[cus] = bf16_bits(run_linear(q, bits, q.TF_OP_GEMM, d["x"], pk, K, N, G, cus=cus,
+                                         route=q.TF_ROUTE_TILED, torch=torch))
+    assert q.tf_gemm_plan(bits, M, K, N, G, split, q.TF_ROUTE_TILED)[2] > 0
+    assert np.array_equal(outs[split], outs[1]), "the wide + narrow plan differs from the single wide launch"
 
 
 def _integer_case(bits, M, K, N, G, seed):
@@ -159,8 +194,9 @@ def test_integer_case_is_bit_exact(gemm, bits, M, K, N, G):
     print(f"integer gemm={gemm} W{bits} M={M} K={K} N={N} G={G}", flush=True)
     c, exact = _integer_case(bits, M, K, N, G, seed=K + N)
     d = to_device(c, torch)
-    with gemm_route(q, 1 if gemm == "tiled" else 0), planning_cus(q, 4096 if M > 16 else 0):
-        y = linear_fn(q, bits, bool(gemm))(d["x"], repack(c, d, q), K, N, G)
+    op = q.TF_OP_GEMM if gemm else q.TF_OP_GEMV
+    y = run_linear(q, bits, op, d["x"], repack(c, d, q), K, N, G, cus=4096 if M > 16 else 0,
+                   route=q.TF_ROUTE_TILED if gemm == "tiled" else q.TF_ROUTE_AUTO, torch=torch)
     torch.cuda.synchronize()
     # every partial sum is an integer below 2^24, so fp32 holds it exactly and
     # the only rounding is the final one to bf16
@@ -176,8 +212,9 @@ def test_q_equal_zero_point_gives_zero(gemm, M, bits):
     codes = c0.zeros[np.arange(c0.K) // c0.G]
     c = synth.gen.pack_case(bits, codes, c0.zeros, c0.scales, c0.x, c0.G)
     d = to_device(c, torch)
-    with gemm_route(q, 1 if gemm == "tiled" else 0), planning_cus(q, 4096 if M > 16 else 0):
-        y = linear_fn(q, bits, bool(gemm))(d["x"], repack(c, d, q), c.K, c.N, c.G)
+    op = q.TF_OP_GEMM if gemm else q.TF_OP_GEMV
+    y = run_linear(q, bits, op, d["x"], repack(c, d, q), c.K, c.N, c.G, cus=4096 if M > 16 else 0,
+                   route=q.TF_ROUTE_TILED if gemm == "tiled" else q.TF_ROUTE_AUTO, torch=torch)
     torch.cuda.synchronize()
     assert np.all(bf16_to_f64(y) == 0.0)
 

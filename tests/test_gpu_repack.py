@@ -41,13 +41,48 @@ def test_repack_matches_oracle_bytes_full_size(config, shape_id):
     assert np.array_equal(packed.cpu().numpy(), want)
 
 
-@pytest.mark.parametrize("bits,K,N,G", SMALL + [(4, 4096, 4096, 128), (8, 8192, 512, 8192)])
-def test_dequant_f32_bit_exact(bits, K, N, G):
+@pytest.mark.parametrize("hook", ["gemm", "gemv"])
+@pytest.mark.parametrize("bits,K,N,G", SMALL + [(4, 4096, 4096, 128), (8, 8192, 512, 8192), (8, 4096, 512, 32)])
+def test_dequant_f32_bit_exact(bits, K, N, G, hook):
+    """The fp32 weights decoded by each kernel's own operand builder (the
+    GEMM's exact bf16 q - z, the GEMV's 128 + q and 128 + z) equal the
+    oracle's (q - z) * s bit for bit."""
     torch, q = gpu_or_skip()
-    print(f"dequant W{bits} K={K} N={N} G={G}", flush=True)
+    print(f"dequant {hook} W{bits} K={K} N={N} G={G}", flush=True)
     c = synth.make_inputs(bits, 1, K, N, G, seed=(42, bits, K, N))
     packed = repack(c, to_device(c, torch), q)
-    fn = q.tf_dequant_w4_f32 if bits == 4 else q.tf_dequant_w8_f32
+    fn = {("gemm", 4): q.tf_dequant_w4_f32, ("gemm", 8): q.tf_dequant_w8_f32,
+          ("gemv", 4): q.tf_dequant_gemv_w4_f32, ("gemv", 8): q.tf_dequant_gemv_w8_f32}[(hook, bits)]
+    w = fn(packed, K, N, G)
+    torch.cuda.synchronize()
+    want = oracle.dequant(bits, c.qweight, c.qzeros, c.scales, K, N, G)
+    assert np.array_equal(w.cpu().numpy().view(np.uint32), want.view(np.uint32))
+
+
+@pytest.mark.parametrize("hook", ["gemm", "gemv"])
+@pytest.mark.parametrize("bits", [4, 8])
+def test_dequant_every_code_and_zero_point(bits, hook):
+    """Every (q, z) pair of the bit width, with scales of both signs and
+    exponents from 2^-100 to 2^100: still the oracle's value bit for bit."""
+    torch, q = gpu_or_skip()
+    levels = 1 << bits
+    G = 32
+    K = G * levels                      # group g has zero point (g + n) % levels
+    N = 16 if bits == 4 else 64
+    k = np.arange(K)
+    codes = ((k[:, None] + 7 * np.arange(N)[None, :]) % levels).astype(np.uint8)
+    if bits == 8:                       # 32 rows per group: column n holds q in 32 (n % 8) .. + 31
+        codes = ((k[:, None] % G) + G * (np.arange(N)[None, :] % 8)).astype(np.uint8)
+    zeros = ((np.arange(K // G)[:, None] + np.arange(N)[None, :]) % levels).astype(np.uint8)
+    rng = np.random.default_rng(44)
+    exps = rng.integers(-100, 101, size=(K // G, N))
+    mant = rng.uniform(1.0, 2.0, size=(K // G, N)) * rng.choice([-1.0, 1.0], size=(K // G, N))
+    scales = synth.f32_to_bf16_bits((mant * np.exp2(exps)).astype(np.float32))
+    x = synth.f32_to_bf16_bits(np.zeros((1, K), np.float32))
+    c = synth.gen.pack_case(bits, codes, zeros, scales, x, G)
+    packed = repack(c, to_device(c, torch), q)
+    fn = {("gemm", 4): q.tf_dequant_w4_f32, ("gemm", 8): q.tf_dequant_w8_f32,
+          ("gemv", 4): q.tf_dequant_gemv_w4_f32, ("gemv", 8): q.tf_dequant_gemv_w8_f32}[(hook, bits)]
     w = fn(packed, K, N, G)
     torch.cuda.synchronize()
     want = oracle.dequant(bits, c.qweight, c.qzeros, c.scales, K, N, G)

@@ -7,8 +7,7 @@ import pytest
 
 import oracle
 import synth
-from gpu_harness import (bf16_bits, bf16_to_f64, gpu_or_skip, planning_cus, sample_indices, to_device,
-                         within_tolerance)
+from gpu_harness import bf16_bits, bf16_to_f64, gpu_or_skip, run_linear, sample_indices, to_device, within_tolerance
 
 pytestmark = pytest.mark.gpu
 
@@ -31,10 +30,13 @@ def repack_gate_up(case, d, q):
     return fn(d["qweight"], d["qzeros"], d["scales"], case.K, case.N, case.G)
 
 
-def _run(case, torch, q, d=None, p=None, y=None):
+def _run(case, torch, q, d=None, p=None, y=None, cus=0):
+    """The GEMV SiLU-product call, planned for `cus` compute units (0: the
+    device's, through the product entry point)."""
     d = d or to_device(case, torch)
     p = p if p is not None else repack_gate_up(case, d, q)
-    out = _fn(q, case.bits)(d["x"], p, case.K, case.N, case.G, y=y)
+    out = run_linear(q, case.bits, q.TF_OP_GEMV_SILU_MUL, d["x"], p, case.K, case.N, case.G, cus=cus, y=y,
+                     torch=torch)
     torch.cuda.synchronize()
     return out
 
@@ -72,10 +74,12 @@ def test_silu_mul_routes(shape, cus):
     bits, M, K, N, G = shape
     print(f"silu_mul route shape={shape} cus={cus}", flush=True)
     c = synth.make_inputs(bits, M, K, N, G, seed=(69, bits, M, K), keep_codes=False)
-    with planning_cus(q, cus):
-        splits = ROUTE_SHAPES[shape][(1, 256, 4096).index(cus)]
-        assert q.tf_workspace_bytes(bits, False, M, K, N, G) == (4 * splits * M * N if splits > 1 else 0)
-        y = _run(c, torch, q)
+    splits = ROUTE_SHAPES[shape][(1, 256, 4096).index(cus)]
+    assert q.tf_workspace_bytes_planned(bits, q.TF_OP_GEMV_SILU_MUL, M, K, N, G, cus) == \
+        (4 * splits * M * N if splits > 1 else 0)
+    assert q.tf_workspace_bytes_planned(bits, q.TF_OP_GEMV, M, K, N, G, cus) == \
+        q.tf_workspace_bytes_planned(bits, q.TF_OP_GEMV_SILU_MUL, M, K, N, G, cus)
+    y = _run(c, torch, q, cus=cus)
     cols = sample_indices(N // 2, 512, seed=70)
     ok, ratio = within_tolerance(bf16_to_f64(y)[:, cols], oracle.awq_linear_silu_mul(c, cols=cols))
     assert ok, f"worst error / bound = {ratio:.3f}"
@@ -109,9 +113,8 @@ def test_zero_half_gives_exact_zero(bits, M, cus, half):
     cols = slice(0, N // 2) if half == "gate" else slice(N // 2, N)
     codes[:, cols] = c0.zeros[np.arange(K) // G][:, cols]
     c = synth.gen.pack_case(bits, codes, c0.zeros, c0.scales, c0.x, G)
-    with planning_cus(q, cus):
-        assert (q.tf_workspace_bytes(bits, False, M, K, N, G) > 0) == (cus == 256)
-        y = _run(c, torch, q)
+    assert (q.tf_workspace_bytes_planned(bits, q.TF_OP_GEMV, M, K, N, G, cus or 256) > 0) == (cus == 256)
+    y = _run(c, torch, q, cus=cus)
     assert np.all(bf16_to_f64(y) == 0.0)
 
 
@@ -188,16 +191,12 @@ GEMM_SILU = [
 @pytest.mark.parametrize("shape", GEMM_SILU, ids=[str(s) for s in GEMM_SILU])
 def test_gemm_silu_mul_routes(shape):
     torch, q = gpu_or_skip()
-    from gpu_harness import gemm_route
-
     bits, M, K, N, G, cus, route = shape
     print(f"gemm silu_mul shape={shape}", flush=True)
     c = synth.make_inputs(bits, M, K, N, G, seed=(73, bits, M, K), keep_codes=False)
     d = to_device(c, torch)
     p = repack_gate_up(c, d, q)
-    fn = q.tf_gemm_w4a16_silu_mul if bits == 4 else q.tf_gemm_w8a16_silu_mul
-    with planning_cus(q, cus), gemm_route(q, route):
-        y = fn(d["x"], p, K, N, G)
+    y = run_linear(q, bits, q.TF_OP_GEMM_SILU_MUL, d["x"], p, K, N, G, cus=cus, route=route, torch=torch)
     torch.cuda.synchronize()
     assert tuple(y.shape) == (M, N // 2)
     rows = sample_indices(M, 48, seed=74)
@@ -242,7 +241,6 @@ def test_gemm_silu_mul_zero_gate_gives_zero(M, cus):
     codes[:, : N // 2] = c0.zeros[np.arange(K) // G][:, : N // 2]
     c = synth.gen.pack_case(4, codes, c0.zeros, c0.scales, c0.x, G)
     d = to_device(c, torch)
-    with planning_cus(q, cus):
-        y = q.tf_gemm_w4a16_silu_mul(d["x"], repack_gate_up(c, d, q), K, N, G)
+    y = run_linear(q, 4, q.TF_OP_GEMM_SILU_MUL, d["x"], repack_gate_up(c, d, q), K, N, G, cus=cus, torch=torch)
     torch.cuda.synchronize()
     assert np.all(bf16_to_f64(y) == 0.0)
