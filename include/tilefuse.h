@@ -21,7 +21,8 @@
  *  - `stream` is a hipStream_t (NULL = the legacy default stream).  Calls are
  *    asynchronous on it; faults inside kernels surface at the caller's next
  *    synchronisation, as usual for HIP.
- *  - Arguments are validated on the host before any HIP call.  A call that
+ *  - Arguments are validated on the host before any HIP work is queued (the
+ *    only HIP calls before are device-property queries).  A call that
  *    returns anything but TF_OK has launched nothing and written nothing.
  *  - M == 0 is a valid empty problem: TF_OK, nothing launched.
  *  - Outputs must not alias inputs, the packed buffer or the workspace.
@@ -206,6 +207,27 @@ int tf_gemm_w4a16(const uint16_t *x, const void *packed, size_t packed_bytes, ui
 int tf_gemm_w8a16(const uint16_t *x, const void *packed, size_t packed_bytes, uint16_t *y,
                   int64_t M, int64_t K, int64_t N, int64_t G,
                   void *workspace, size_t ws_bytes, void *stream);
+
+/* tf_gemm_w4a16 for callers that cannot allocate device memory: code under
+ * HIP-graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, kernels, plan and results as tf_gemm_w4a16 (bit for bit),
+ * but no workspace argument: when the plan splits K, the fp32 partial sums go
+ * to a fixed device array of 32 MiB inside the library, one per GPU, held
+ * from the first such call on that GPU until the process ends.  The call
+ * itself allocates nothing (no hipMalloc, no allocating library routine).
+ *   - Every plan on a device of up to 256 compute units fits the array.  A
+ *     plan whose partial sums exceed it (tf_workspace_bytes(4, 1, M, K, N,
+ *     G) > 32 MiB, possible on larger devices) is refused with
+ *     TF_ERR_UNSUPPORTED before any HIP work; other errors as
+ *     tf_gemm_w4a16.
+ *   - Every call on a GPU shares that GPU's array, which keeps the last
+ *     call's contents (each call writes every partial it reads, so nothing
+ *     needs clearing).  Calls that overlap on one GPU -- on different streams,
+ *     or from several threads without ordering -- race on the array and may
+ *     return wrong results; order them on one stream.
+ *   - TF_ERR_HIP if the array's address cannot be obtained on the device. */
+int tf_gemm_w4a16_noalloc(const uint16_t *x, const void *packed, size_t packed_bytes, uint16_t *y,
+                          int64_t M, int64_t K, int64_t N, int64_t G, void *stream);
 
 /* Test hooks, not on the hot path: the dequantized weights w[K][N] as fp32
  * ((q - z) * s is exact in fp32), decoded from a packed buffer by the

@@ -29,6 +29,7 @@ from ._binding import (  # noqa: F401
     tf_gemm_plan,
     tf_gemv_plan,
     tf_gemm_w4a16,
+    tf_gemm_w4a16_noalloc,
     tf_gemm_w4a16_silu_mul,
     tf_gemm_w8a16,
     tf_gemm_w8a16_silu_mul,

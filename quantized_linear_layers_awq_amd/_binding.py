@@ -69,6 +69,8 @@ def load_library():
         for n in ("tf_dequant_w4_f32", "tf_dequant_w8_f32", "tf_dequant_gemv_w4_f32", "tf_dequant_gemv_w8_f32"):
             getattr(L, n).argtypes = [P, SZ, P, I64, I64, I64, P]
             getattr(L, n).restype = I
+        L.tf_gemm_w4a16_noalloc.argtypes = [P, P, SZ, P, I64, I64, I64, I64, P]
+        L.tf_gemm_w4a16_noalloc.restype = I
         L.tf_linear_planned.argtypes = [I, I, P, P, SZ, P, I64, I64, I64, I64, P, SZ, I, I, P]
         L.tf_linear_planned.restype = I
         L.tf_workspace_bytes_planned.argtypes = [I, I, I64, I64, I64, I64, I, I]
@@ -249,6 +251,26 @@ def tf_gemv_w8a16(x, packed, K, N, G, y=None, workspace=None, stream=None):
 def tf_gemm_w4a16(x, packed, K, N, G, y=None, workspace=None, stream=None):
     """y[M][N] (bf16) for x [M][K] bf16, any M, W4 packed weights."""
     return _linear(4, True, "tf_gemm_w4a16", x, packed, K, N, G, y, workspace, stream)
+
+
+def tf_gemm_w4a16_noalloc(x, packed, K, N, G, y=None, stream=None):
+    """tf_gemm_w4a16 without a workspace: split-K partial sums go to the
+    library's fixed per-GPU device array (calls that overlap on one GPU race
+    on it).  Allocates nothing but y when y is None."""
+    L = load_library()
+    _need(x, "x", 2)
+    _need(packed, "packed", 1)
+    if x.dim() != 2 or x.shape[1] != K:
+        raise ValueError(f"tf_gemm_w4a16_noalloc: x must be [M][K] with K={K}")
+    M = x.shape[0]
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    _need(y, "y", 2)
+    if y.numel() < M * N:
+        raise ValueError("tf_gemm_w4a16_noalloc: y holds fewer than M*N elements")
+    _check(L.tf_gemm_w4a16_noalloc(_ptr(x), _ptr(packed), packed.numel(), _ptr(y), M, K, N, G, _stream(x, stream)),
+           "tf_gemm_w4a16_noalloc")
+    return y
 
 
 def tf_gemm_w8a16(x, packed, K, N, G, y=None, workspace=None, stream=None):

@@ -3,7 +3,21 @@
 // The declarations and their documentation live in include/tilefuse.h.
 #include "tilefuse.h"
 
+#include <atomic>
+#include <mutex>
+
 #include "tf_launch.h"
+
+// Split-K partial sums of tf_gemm_w4a16_noalloc: a fixed device array, one
+// copy per GPU the library runs on, held until the process ends.  Host code
+// never uses this name as an address (on the host it is a stand-in for the
+// symbol); it uses the device address hipGetSymbolAddress returns for the
+// current device.  32 MiB holds every split plan on a device of up to 256
+// compute units: the tiled GEMM splits K only while its tiles fill at most
+// half the units, so S ranges of M x N fp32 partials stay within
+// cus x 256 x 128 x 4 bytes, and the GEMV kernels' splits stay below that.
+constexpr size_t kNoallocScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) uint8_t scratch[kNoallocScratchBytes];
 
 namespace {
 
@@ -79,11 +93,11 @@ size_t workspace_bytes(int bits, int op, int64_t M, int64_t K, int64_t N, int64_
     return (size_t)tf::gemm_workspace_bytes(M, N, K, G, cus);
 }
 
-// One linear call: validation on the host, then the launches.  cus and
-// route are the plan's inputs: the device's compute units and the automatic
-// route for every product entry point.
-int linear(int bits, int op, const uint16_t *x, const void *packed, size_t nbytes, uint16_t *y, int64_t M, int64_t K,
-           int64_t N, int64_t G, void *ws, size_t ws_bytes, int cus, int route, void *stream)
+// Validation of one linear call on the host (no HIP call): TF_OK, or the
+// error the call returns.  ws_known: the workspace is the library's own (its
+// pointer and size are checked by the caller), so only the size rule holds.
+int validate(int bits, int op, const uint16_t *x, const void *packed, size_t nbytes, uint16_t *y, int64_t M,
+             int64_t K, int64_t N, int64_t G, void *ws, size_t ws_bytes, int cus, int route)
 {
     if (M < 0 || M > op_max_m(op))
         return TF_ERR_SHAPE;
@@ -114,6 +128,14 @@ int linear(int bits, int op, const uint16_t *x, const void *packed, size_t nbyte
         if (ws_bytes < need)
             return TF_ERR_BUFFER_TOO_SMALL;
     }
+    return TF_OK;
+}
+
+// The launches of a validated call (M > 0).
+int launch(int bits, int op, const uint16_t *x, const void *packed, uint16_t *y, int64_t M, int64_t K, int64_t N,
+           int64_t G, void *ws, int cus, int route, void *stream)
+{
+    const Layout lay = Layout::make(bits, K, N, G);
     const hipStream_t st = static_cast<hipStream_t>(stream);
     const bool tiled = op_is_gemm(op) && !tf::gemm_uses_gemv(M, route);
     hipError_t e;
@@ -124,6 +146,19 @@ int linear(int bits, int op, const uint16_t *x, const void *packed, size_t nbyte
     else
         e = tf::launch_gemv(bits, x, packed, y, M, lay, ws, st, cus);
     return e == hipSuccess ? TF_OK : TF_ERR_HIP;
+}
+
+// One linear call: validation on the host, then the launches.  cus and
+// route are the plan's inputs: the device's compute units and the automatic
+// route for every product entry point.
+int linear(int bits, int op, const uint16_t *x, const void *packed, size_t nbytes, uint16_t *y, int64_t M, int64_t K,
+           int64_t N, int64_t G, void *ws, size_t ws_bytes, int cus, int route, void *stream)
+{
+    if (int st = validate(bits, op, x, packed, nbytes, y, M, K, N, G, ws, ws_bytes, cus, route))
+        return st;
+    if (M == 0)
+        return TF_OK;
+    return launch(bits, op, x, packed, y, M, K, N, G, ws, cus, route, stream);
 }
 
 int dequant(int bits, const void *packed, size_t nbytes, float *w, int64_t K, int64_t N, int64_t G, void *stream,
@@ -141,6 +176,29 @@ int dequant(int bits, const void *packed, size_t nbytes, float *w, int64_t K, in
     if (tf::launch_dequant_f32(bits, packed, lay, w, static_cast<hipStream_t>(stream), gemv) != hipSuccess)
         return TF_ERR_HIP;
     return TF_OK;
+}
+
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept; NULL if the lookup fails.
+constexpr int kMaxDevices = 64;
+std::atomic<void *> g_scratch[kMaxDevices];
+std::mutex g_scratch_lock;
+
+void *device_scratch()
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return nullptr;
+    if (void *p = g_scratch[dev].load(std::memory_order_acquire))
+        return p;
+    std::lock_guard<std::mutex> hold(g_scratch_lock);
+    if (void *p = g_scratch[dev].load(std::memory_order_relaxed))
+        return p;
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p)
+        return nullptr;
+    g_scratch[dev].store(p, std::memory_order_release);
+    return p;
 }
 
 bool plan_inputs_ok(int bits, int op, int cus, int route)
@@ -220,6 +278,30 @@ TF_LINEAR(tf_gemv_w8a16_silu_mul, 8, kOpGemvSiluMul)
 TF_LINEAR(tf_gemm_w4a16_silu_mul, 4, kOpGemmSiluMul)
 TF_LINEAR(tf_gemm_w8a16_silu_mul, 8, kOpGemmSiluMul)
 #undef TF_LINEAR
+
+int tf_gemm_w4a16_noalloc(const uint16_t *x, const void *packed, size_t nbytes, uint16_t *y, int64_t M, int64_t K,
+                          int64_t N, int64_t G, void *stream)
+{
+    const int cus = tf::device_cus();
+    // the size rule, then every check of tf_gemm_w4a16 (the workspace stands
+    // in as a valid 256-byte-aligned buffer of the array's size): no HIP
+    // call for a request that will be refused
+    if (workspace_bytes(4, kOpGemm, M, K, N, G, cus, tf::kRouteAuto) > kNoallocScratchBytes)
+        return TF_ERR_UNSUPPORTED;
+    void *const stand_in = reinterpret_cast<void *>(uintptr_t(256));
+    if (int st = validate(4, kOpGemm, x, packed, nbytes, y, M, K, N, G, stand_in, kNoallocScratchBytes, cus,
+                          tf::kRouteAuto))
+        return st;
+    if (M == 0)
+        return TF_OK;
+    void *ws = nullptr;
+    if (workspace_bytes(4, kOpGemm, M, K, N, G, cus, tf::kRouteAuto) > 0) {
+        ws = device_scratch();
+        if (!ws)
+            return TF_ERR_HIP;
+    }
+    return launch(4, kOpGemm, x, packed, y, M, K, N, G, ws, cus, tf::kRouteAuto, stream);
+}
 
 int tf_dequant_w4_f32(const void *packed, size_t nbytes, float *w, int64_t K, int64_t N, int64_t G, void *stream)
 {

@@ -380,6 +380,24 @@ class TestValidation:
         assert lib.tf_probe_mfma(256, 10, None, ctypes.byref(flops), None) == TF_ERR_NULL
         assert lib.tf_probe_mfma(256, 10, FAKE + 2, ctypes.byref(flops), None) == TF_ERR_ALIGN
 
+    def test_noalloc_validation(self, lib):
+        f = lib.tf_gemm_w4a16_noalloc
+        call = lambda M=2048, K=4096, N=4096, G=128, x=FAKE, p=FAKE, y=FAKE, nb=1 << 30: f(x, p, nb, y, M, K, N, G, None)
+        assert call(K=33) == TF_ERR_SHAPE
+        assert call(N=12) == TF_ERR_SHAPE
+        assert call(G=48) == TF_ERR_GROUP
+        assert call(x=None) == TF_ERR_NULL
+        assert call(y=FAKE + 1) == TF_ERR_ALIGN
+        assert call(p=FAKE + 8) == TF_ERR_ALIGN
+        assert call(nb=10) == TF_ERR_BUFFER_TOO_SMALL
+        assert call(M=0, x=None, y=None, p=None) == TF_OK
+        assert call(M=-1) == TF_ERR_SHAPE
+        # a split plan with bad pointers is refused before the array is looked up
+        assert lib.tf_workspace_bytes(4, 1, 48, 14336, 4096, 128) > 0
+        assert call(M=48, K=14336, x=FAKE + 2) == TF_ERR_ALIGN
+
     def test_dequant_validation(self, lib):
         assert lib.tf_dequant_w4_f32(FAKE, 1, FAKE, 256, 128, 128, None) == TF_ERR_BUFFER_TOO_SMALL
         assert lib.tf_dequant_w8_f32(FAKE, 1 << 30, FAKE + 2, 256, 128, 128, None) == TF_ERR_ALIGN
+        assert lib.tf_dequant_gemv_w4_f32(None, 1 << 30, FAKE, 256, 128, 128, None) == TF_ERR_NULL
+        assert lib.tf_dequant_gemv_w8_f32(FAKE, 1 << 30, FAKE, 256, 128, 96, None) == TF_ERR_GROUP

@@ -127,3 +127,21 @@ def test_gemv_plan_rejects_bad_input(lib):
     assert lib.tf_gemv_plan(4, 1, 4096, 64, 96, 256, out) == 3
     assert lib.tf_gemv_plan(5, 1, 4096, 64, 128, 256, out) == 6
     assert lib.tf_gemv_plan(4, 1, 4096, 64, 128, 256, None) == 1
+
+
+def test_every_split_plan_fits_the_noalloc_array(lib):
+    """tf_gemm_w4a16_noalloc holds its split-K partials in a 32 MiB array:
+    on 256 compute units no GEMM plan needs more (the bound is 256 x 256 x 128
+    fp32 values: a split runs only while the tiles fill at most half the
+    units)."""
+    cap = 32 << 20
+    worst = 0
+    Ms = list(range(1, 65)) + [65, 96, 128, 129, 160, 200, 256, 300, 384, 512, 768, 1024]
+    Ns = [128 * i for i in (1, 2, 4, 8, 16, 32, 48, 64, 128, 256)] + [1000, 5000]
+    for M in Ms:
+        for N in Ns:
+            for K in (128, 1024, 4096, 14336, 28672):
+                for G in (32, 128, K):
+                    w = lib.tf_workspace_bytes_planned(4, 1, M, K, N, G, 256, 0)
+                    worst = max(worst, w)
+    assert 0 < worst <= cap
