@@ -212,12 +212,12 @@ int tf_gemm_w8a16(const uint16_t *x, const void *packed, size_t packed_bytes, ui
  * HIP-graph capture, tight serving loops, harnesses that forbid hipMalloc.
  * Same arguments, kernels, plan and results as tf_gemm_w4a16 (bit for bit),
  * but no workspace argument: when the plan splits K, the fp32 partial sums go
- * to a fixed device array of 32 MiB inside the library, one per GPU, held
+ * to a fixed device array of 64 MiB inside the library, one per GPU, held
  * from the first such call on that GPU until the process ends.  The call
  * itself allocates nothing (no hipMalloc, no allocating library routine).
  *   - Every plan on a device of up to 256 compute units fits the array.  A
  *     plan whose partial sums exceed it (tf_workspace_bytes(4, 1, M, K, N,
- *     G) > 32 MiB, possible on larger devices) is refused with
+ *     G) > 64 MiB, possible on larger devices) is refused with
  *     TF_ERR_UNSUPPORTED before any HIP work; other errors as
  *     tf_gemm_w4a16.
  *   - Every call on a GPU shares that GPU's array, which keeps the last
@@ -260,11 +260,12 @@ int tf_dequant_gemv_w8_f32(const void *packed, size_t packed_bytes, float *w,
 /*   cus    compute units to plan for, 1 .. 2^20                            */
 /*   route  TF_ROUTE_AUTO (the product calls' choice), TF_ROUTE_TILED (GEMM */
 /*          calls run the tiled GEMM at any M), TF_ROUTE_GEMV (the GEMV     */
-/*          kernels up to 64 rows, as AUTO)                                 */
+/*          kernels up to 64 rows, as AUTO), TF_ROUTE_TILED128 (the tiled   */
+/*          GEMM at any M with 256 x 128 tiles only)                        */
 /* Other values: TF_ERR_UNSUPPORTED (the size query returns 0).             */
 /* ------------------------------------------------------------------------ */
 enum { TF_OP_GEMV = 0, TF_OP_GEMM = 1, TF_OP_GEMV_SILU_MUL = 2, TF_OP_GEMM_SILU_MUL = 3 };
-enum { TF_ROUTE_AUTO = 0, TF_ROUTE_TILED = 1, TF_ROUTE_GEMV = 2 };
+enum { TF_ROUTE_AUTO = 0, TF_ROUTE_TILED = 1, TF_ROUTE_GEMV = 2, TF_ROUTE_TILED128 = 3 };
 
 /* The call `op` on (bits, M, K, N, G) as planned for (cus, route): the same
  * validation, kernels and results as the product entry point it names when
@@ -277,20 +278,23 @@ size_t tf_workspace_bytes_planned(int bits, int op, int64_t M, int64_t K, int64_
                                   int cus, int route);
 
 /* Launch plan of a GEMM call (host only, no GPU work).
- * The GEMM covers y with 256-row x 128-column tiles (128 x 128 up to 128
- * rows).  When 256-row tiles are not a whole number of rounds over the
- * compute units, it runs the columns of the last partial round as 256 x 64
- * tiles in a second launch.  When the tiles fill less than half the compute
- * units (small M), it splits K into ranges that run in the same launch, each
- * writing fp32 partial sums to the workspace, and a second kernel adds them
- * in range order.  The plan never changes the result's bits except through
- * that split (the order of the split sums).
- * Writes seven values: out[5] = 1 when the call runs the GEMV kernels (then
- * out[0..2] = out[6] = 0 and out[3], out[4] are their K split), 0 for the
- * tiled GEMM; out[0] = row tiles of out[6] rows (256 or 128), out[1] =
- * 128-column tiles, out[2] = 64-column tiles, out[3] = K ranges, out[4] =
- * k-tiles of 128 rows per range.  TF_ERR_NULL / TF_ERR_SHAPE / TF_ERR_GROUP /
- * TF_ERR_UNSUPPORTED on bad input. */
+ * Above 128 rows, W4 weights whose groups are whole 128-row k-tiles (G a
+ * multiple of 128, or G == K) run on 256 x 256 output tiles.  Otherwise the
+ * GEMM covers y with 256-row x 128-column tiles (128 x 128 up to 128 rows);
+ * when those 256-row tiles are not a whole number of rounds over the compute
+ * units, it runs the columns of the last partial round as 256 x 64 tiles in
+ * a second launch.  When the tiles fill less than half the compute units
+ * (small M), either kernel splits K into ranges that run in the same launch,
+ * each writing fp32 partial sums to the workspace, and a second kernel adds
+ * them in range order.  Within one kernel the plan never changes the
+ * result's bits except through that split (the order of the split sums).
+ * Writes eight values: out[5] = 1 when the call runs the GEMV kernels (then
+ * out[0..2] = out[6] = out[7] = 0 and out[3], out[4] are their K split), 0
+ * for the tiled GEMM; out[0] = row tiles of out[6] rows (256 or 128),
+ * out[1] = wide column tiles of out[7] columns (256 or 128), out[2] =
+ * 64-column tiles, out[3] = K ranges, out[4] = k-tiles of 128 rows per
+ * range.  TF_ERR_NULL / TF_ERR_SHAPE / TF_ERR_GROUP / TF_ERR_UNSUPPORTED on
+ * bad input. */
 int tf_gemm_plan(int bits, int64_t M, int64_t K, int64_t N, int64_t G, int cus, int route, int64_t *out);
 
 /* Launch plan of the GEMV kernels for M <= 64 rows (host only), for checks of

@@ -21,6 +21,7 @@ from ._binding import (  # noqa: F401
     TF_ROUTE_AUTO,
     TF_ROUTE_GEMV,
     TF_ROUTE_TILED,
+    TF_ROUTE_TILED128,
     tf_dequant_gemv_w4_f32,
     tf_dequant_gemv_w8_f32,
     tf_dequant_w4_f32,

@@ -200,7 +200,7 @@ def _workspace(device: torch.device, stream_handle: int, nbytes: int):
 
 
 TF_OP_GEMV, TF_OP_GEMM, TF_OP_GEMV_SILU_MUL, TF_OP_GEMM_SILU_MUL = 0, 1, 2, 3
-TF_ROUTE_AUTO, TF_ROUTE_TILED, TF_ROUTE_GEMV = 0, 1, 2
+TF_ROUTE_AUTO, TF_ROUTE_TILED, TF_ROUTE_GEMV, TF_ROUTE_TILED128 = 0, 1, 2, 3
 
 
 def _call(bits, op, fn, x, packed, K, N, G, y, workspace, stream, plan=None):
@@ -352,12 +352,13 @@ def tf_workspace_bytes_planned(bits, op, M, K, N, G, cus, route=TF_ROUTE_AUTO) -
 
 
 def tf_gemm_plan(bits: int, M: int, K: int, N: int, G: int, cus: int, route: int = TF_ROUTE_AUTO) -> tuple[int, ...]:
-    """Test hook: (row tiles, 128-column tiles, 64-column tiles, K ranges,
+    """Test hook: (row tiles, wide column tiles, 64-column tiles, K ranges,
     k-tiles per range, 1 if the call runs the GEMV kernels else 0, rows per
-    row tile) of a GEMM call's launch plan on a device of `cus` compute
-    units with kernel route `route` (host only)."""
+    row tile, columns per wide tile (256 or 128)) of a GEMM call's launch
+    plan on a device of `cus` compute units with kernel route `route` (host
+    only)."""
     L = load_library()
-    out = (ctypes.c_int64 * 7)()
+    out = (ctypes.c_int64 * 8)()
     _check(L.tf_gemm_plan(bits, M, K, N, G, cus, route, out), "tf_gemm_plan")
     return tuple(int(v) for v in out)
 

@@ -17,7 +17,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(HERE, "libtilefuse.so")
-SOURCES = ("api.hip", "repack.hip", "gemv.hip", "gemm.hip", "probe.hip")
+SOURCES = ("api.hip", "repack.hip", "gemv.hip", "gemm.hip", "gemm256.hip", "probe.hip")
 ARCH = "gfx950"
 
 

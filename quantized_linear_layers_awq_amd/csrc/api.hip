@@ -12,11 +12,11 @@
 // copy per GPU the library runs on, held until the process ends.  Host code
 // never uses this name as an address (on the host it is a stand-in for the
 // symbol); it uses the device address hipGetSymbolAddress returns for the
-// current device.  32 MiB holds every split plan on a device of up to 256
+// current device.  64 MiB holds every split plan on a device of up to 256
 // compute units: the tiled GEMM splits K only while its tiles fill at most
 // half the units, so S ranges of M x N fp32 partials stay within
-// cus x 256 x 128 x 4 bytes, and the GEMV kernels' splits stay below that.
-constexpr size_t kNoallocScratchBytes = size_t(32) << 20;
+// cus x 256 x 256 x 4 bytes, and the GEMV kernels' splits stay below that.
+constexpr size_t kNoallocScratchBytes = size_t(64) << 20;
 static __device__ __align__(256) uint8_t scratch[kNoallocScratchBytes];
 
 namespace {
@@ -90,7 +90,7 @@ size_t workspace_bytes(int bits, int op, int64_t M, int64_t K, int64_t N, int64_
     const Layout lay = Layout::make(bits, K, N, G);
     if (!op_is_gemm(op) || tf::gemm_uses_gemv(M, route))
         return (size_t)tf::gemv_workspace_bytes(lay, M, cus);
-    return (size_t)tf::gemm_workspace_bytes(M, N, K, G, cus);
+    return (size_t)tf::gemm_workspace_bytes(bits, M, N, K, G, cus, route);
 }
 
 // Validation of one linear call on the host (no HIP call): TF_OK, or the
@@ -140,7 +140,8 @@ int launch(int bits, int op, const uint16_t *x, const void *packed, uint16_t *y,
     const bool tiled = op_is_gemm(op) && !tf::gemm_uses_gemv(M, route);
     hipError_t e;
     if (tiled)
-        e = tf::launch_gemm(bits, x, packed, y, M, lay, ws, st, cus, op_is_silu(op) ? tf::kActSiluMul : tf::kActNone);
+        e = tf::launch_gemm(bits, x, packed, y, M, lay, ws, st, cus, op_is_silu(op) ? tf::kActSiluMul : tf::kActNone,
+                            route);
     else if (op_is_silu(op))
         e = tf::launch_gemv_silu_mul(bits, x, packed, y, M, lay, ws, st, cus);
     else
@@ -204,7 +205,8 @@ void *device_scratch()
 bool plan_inputs_ok(int bits, int op, int cus, int route)
 {
     return (bits == 4 || bits == 8) && op >= kOpGemv && op <= kOpGemmSiluMul && cus >= 1 && cus <= (1 << 20) &&
-           (route == tf::kRouteAuto || route == tf::kRouteTiled || route == tf::kRouteGemv);
+           (route == tf::kRouteAuto || route == tf::kRouteTiled || route == tf::kRouteGemv ||
+            route == tf::kRouteTiled128);
 }
 
 } // namespace
@@ -360,9 +362,10 @@ int tf_gemm_plan(int bits, int64_t M, int64_t K, int64_t N, int64_t G, int cus, 
         out[4] = st;
         out[5] = 1;
         out[6] = 0;
+        out[7] = 0;
         return TF_OK;
     }
-    const tf::GemmPlan p = tf::plan_gemm(M, N, K, G, cus);
+    const tf::GemmPlan p = tf::plan_gemm(bits, M, N, K, G, cus, route != tf::kRouteTiled128);
     out[0] = p.m_tiles;
     out[1] = p.wide_cols;
     out[2] = p.narrow_cols;
@@ -370,6 +373,7 @@ int tf_gemm_plan(int bits, int64_t M, int64_t K, int64_t N, int64_t G, int cus, 
     out[4] = p.split_tiles;
     out[5] = 0;
     out[6] = p.rows;
+    out[7] = p.col_tile;
     return TF_OK;
 }
 

@@ -48,18 +48,12 @@
 #include "tf_common.h"
 #include "tf_launch.h"
 #include "tf_operands.h"
+#include "tf_gemm_common.h"
 
 namespace tf {
 
-typedef float f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
-
 constexpr int kGBM = 256;                        // rows per workgroup tile
-constexpr int kStage = 64;                       // k rows per pipeline stage
 constexpr int kAStages = 3;
-// Row tiles per band of the tile order: with two, the 32 workgroups an XCD runs
-// at once cover 2 activation panels x 16 weight column tiles (measured best of
-// 1, 2, 4 and all).
-constexpr int kBand = 2;
 constexpr int a_stage_bytes(int bm) { return bm * kStage * 2; } // 32 / 16 KiB
 constexpr int kGWaves = 8;                       // waves per workgroup
 constexpr int kGThreads = 64 * kGWaves;
@@ -85,77 +79,6 @@ constexpr int gemm_lds(int bits, int wn, int bm)
     return off_meta(bits, wn, bm) + kMetaBufs * metabuf_bytes(wn); // <= 158 KiB
 }
 static_assert(gemm_lds(8, 2, kGBM) <= 160 * 1024, "LDS of one CU");
-
-// 16-byte unit (row, c) of a [rows][64] bf16 tile, c = 0..7.  Rows are 128
-// bytes, so two share a 256-byte bank line; the XOR with (row / 2) % 8 puts
-// the 16 rows that 16 consecutive lanes read at one c into 16 distinct bank
-// groups.
-__device__ __forceinline__ int swz(int row, int c) { return (row << 3) + (c ^ ((row >> 1) & 7)); }
-
-// s_waitcnt immediates (gfx9 encoding): vmcnt in bits 3:0 and 15:14, expcnt
-// 6:4, lgkmcnt 11:8; counters not named stay at their maximum (no wait).
-template <int N> __device__ __forceinline__ void wait_vmcnt()
-{
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4)); }
-
-// Workgroup barrier for LDS filled by LDS-DMA: each wave has already waited
-// for its own loads; the empty asm statements keep the compiler from moving
-// memory operations across the barrier.
-__device__ __forceinline__ void lds_barrier()
-{
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
-
-// LDS-DMA: lane i's 16 (or 4) bytes land at lds + 16 i (or 4 i).
-// LDS-DMA loads go through buffer instructions (buffer_load_dword[x4] ...
-// lds) on a raw buffer resource whose base is wave-uniform: lane L's bytes
-// land at lds + size * L.  The buffer form matters: the compiler treats the
-// global-segment form as a flat access that may touch LDS and then drains
-// every outstanding LDS read before it and after it, which would serialise
-// the fragment reads with the MFMAs.
-typedef __amdgpu_buffer_rsrc_t Rsrc;
-__device__ __forceinline__ Rsrc make_rsrc(const void *base)
-{
-    // stride 0, no range limit below 4 GiB (offsets are built in bounds),
-    // dword data format (required for the resource to be valid on gfx9)
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, -1, 0x00020000);
-}
-__device__ __forceinline__ void dma16(Rsrc r, uint32_t voff, uint32_t soff, void *lds)
-{
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 16, (int)voff,
-                                             (int)soff, 0, 0);
-}
-__device__ __forceinline__ void dma4(Rsrc r, uint32_t voff, uint32_t soff, void *lds)
-{
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 4, (int)voff,
-                                             (int)soff, 0, 0);
-}
-
-__device__ __forceinline__ f32x16 mfma32x32x16(const u32x4 &a, const u32x4 &b, const f32x16 &c)
-{
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
-                                                   0, 0, 0);
-}
-
-// How groups map onto the 16-row slices of the k loop.  kGSplit32/64 and
-// kGOneTile are the slices per group (G = 32, 64, 128); kGWhole covers groups
-// of whole k-tiles (G a multiple of 256, or G == K).
-enum GemmGroups { kGWhole = 0, kGSplit32 = 2, kGSplit64 = 4, kGOneTile = 8 };
-
-template <int V> using ic = std::integral_constant<int, V>;
-
-// f(ic<I>{}), ..., f(ic<N - 1>{}): loop indices usable as constants
-template <int I, int N, typename F> __device__ __forceinline__ void static_for(F &&f)
-{
-    if constexpr (I < N) {
-        f(ic<I>{});
-        static_for<I + 1, N>(f);
-    }
-}
 
 // The workgroup grid covers `splits` ranges of split_tiles k-tiles each, and
 // per range m_tiles row tiles x (gridDim.x / splits / m_tiles) column tiles of
@@ -801,41 +724,65 @@ int device_cus()
     return n;
 }
 
-bool gemm_uses_gemv(int64_t M, int route) { return M <= kGemvKernelMaxM && route != kRouteTiled; }
+bool gemm_uses_gemv(int64_t M, int route)
+{
+    return M <= kGemvKernelMaxM && route != kRouteTiled && route != kRouteTiled128;
+}
 
-GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, int64_t G, int cus)
+// K split for a grid of `tiles` output tiles that fills less than half the
+// compute units: 2 to 8 ranges of at least 4 k-tiles, each starting on a
+// group boundary, so that the chip fills; each range writes fp32 partial
+// sums that a second kernel adds in range order.  Returns false (no split)
+// when no split of at least two ranges fits those rules.
+static bool plan_split(GemmPlan &p, int64_t tiles, int64_t K, int64_t G, int cus)
+{
+    const int64_t ktiles = (K + kTileRows - 1) / kTileRows;
+    if (2 * tiles > cus || ktiles < 8)
+        return false;
+    const int64_t unit = (G % kTileRows == 0 && G != K) ? G / kTileRows : 1; // k-tiles per boundary step
+    int64_t s = cus / tiles;
+    s = s < 8 ? s : 8;
+    s = s < ktiles / 4 ? s : ktiles / 4;
+    if (s < 2)
+        return false;
+    int64_t st = (ktiles + s - 1) / s;
+    st = (st + unit - 1) / unit * unit;
+    s = (ktiles + st - 1) / st;
+    if (s < 2)
+        return false;
+    p.splits = s;
+    p.split_tiles = st;
+    return true;
+}
+
+GemmPlan plan_gemm(int bits, int64_t M, int64_t N, int64_t K, int64_t G, int cus, bool allow256)
 {
     GemmPlan p;
+    const int64_t ktiles = (K + kTileRows - 1) / kTileRows;
+    p.splits = 1;
+    p.split_tiles = ktiles;
+    p.narrow_cols = 0;
+    // W4 with groups of whole k-tiles above 128 rows: 256 x 256 tiles (its
+    // epilogue's 32-bit offsets hold rows of fewer than 2^22 columns)
+    const bool whole = G % kTileRows == 0 || G == K;
+    if (allow256 && bits == 4 && whole && M > kShortTileMaxM && N < (int64_t(1) << 22)) {
+        p.rows = kGBM;
+        p.col_tile = 256;
+        p.m_tiles = (M + kGBM - 1) / kGBM;
+        p.wide_cols = (N + 255) / 256;
+        plan_split(p, p.m_tiles * p.wide_cols, K, G, cus);
+        return p;
+    }
     // up to 128 rows, 128-row tiles: a 256-row tile would compute at least
     // as many padding rows as real ones
+    p.col_tile = tile_cols(2);
     p.rows = M <= kShortTileMaxM ? kShortTileRows : kGBM;
     p.m_tiles = (M + p.rows - 1) / p.rows;
     const int64_t n_wide = (N + tile_cols(2) - 1) / tile_cols(2);
     const int64_t tiles = p.m_tiles * n_wide;
-    const int64_t ktiles = (K + kTileRows - 1) / kTileRows;
     p.wide_cols = n_wide; // default: one launch of 128-column tiles over all of K
-    p.narrow_cols = 0;
-    p.splits = 1;
-    p.split_tiles = ktiles;
-    // Few output tiles (small M): split K so that the chip fills.  A range
-    // holds at least 4 k-tiles and starts on a group boundary; each range
-    // writes fp32 partial sums that a second kernel adds in range order.
-    if (2 * tiles <= cus && ktiles >= 8) {
-        const int64_t unit = (G % kTileRows == 0 && G != K) ? G / kTileRows : 1; // k-tiles per boundary step
-        int64_t s = cus / tiles;
-        s = s < 8 ? s : 8;
-        s = s < ktiles / 4 ? s : ktiles / 4;
-        if (s >= 2) {
-            int64_t st = (ktiles + s - 1) / s;
-            st = (st + unit - 1) / unit * unit;
-            s = (ktiles + st - 1) / st;
-            if (s >= 2) {
-                p.splits = s;
-                p.split_tiles = st;
-                return p;
-            }
-        }
-    }
+    if (plan_split(p, tiles, K, G, cus))
+        return p;
     if (tiles % cus == 0 || p.rows != kGBM)
         return p;
     // the whole rounds with 128-column tiles, the columns left over as
@@ -852,19 +799,30 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, int64_t G, int cus)
     return p;
 }
 
-int64_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t G, int cus)
+int64_t gemm_workspace_bytes(int bits, int64_t M, int64_t N, int64_t K, int64_t G, int cus, int route)
 {
-    const GemmPlan p = plan_gemm(M, N, K, G, cus);
+    const GemmPlan p = plan_gemm(bits, M, N, K, G, cus, route != kRouteTiled128);
     return p.splits > 1 ? p.splits * M * N * (int64_t)sizeof(float) : 0;
 }
 
 hipError_t launch_gemm(int bits, const uint16_t *x, const void *packed, uint16_t *y, int64_t M, const Layout &lay,
-                       void *workspace, hipStream_t stream, int cus, int act)
+                       void *workspace, hipStream_t stream, int cus, int act, int route)
 {
     if (act != kActNone && lay.N % kBlockCols)
         return hipErrorInvalidValue;
-    const GemmPlan plan = plan_gemm(M, lay.N, lay.K, lay.G, cus);
+    const GemmPlan plan = plan_gemm(bits, M, lay.N, lay.K, lay.G, cus, route != kRouteTiled128);
     float *ws = plan.splits > 1 ? static_cast<float *>(workspace) : nullptr;
+    if (plan.col_tile == 256) {
+        if (hipError_t e = launch_gemm256(x, packed, y, M, lay, plan, ws, stream, act))
+            return e;
+        if (plan.splits > 1) {
+            if (act == kActSiluMul)
+                launch_splitk_sum_silu(ws, (int)plan.splits, M, lay.N, y, stream);
+            else
+                launch_splitk_sum(ws, (int)plan.splits, M * lay.N, y, stream);
+        }
+        return hipGetLastError();
+    }
     const uint8_t *pk = static_cast<const uint8_t *>(packed);
     const int mode = lay.tiles_per_group == 1 ? kGOneTile
                      : lay.whole_tiles()      ? kGWhole

@@ -66,34 +66,42 @@ void launch_splitk_sum_silu(const float *ws, int splits, int64_t M, int64_t N, u
 // 2 <= splits <= 16 (both plans stay within that).
 void launch_splitk_sum(const float *ws, int splits, int64_t mn, uint16_t *y, hipStream_t stream);
 // How the GEMM covers the output: m_tiles row tiles of `rows` rows (256, or
-// 128 up to kShortTileMaxM rows), then wide_cols column tiles of 128 columns
-// from column 0 in one launch and (256-row tiles only) narrow_cols tiles of
-// 64 columns after them in a second one.  With splits > 1 (small M), K is
-// cut into ranges of split_tiles k-tiles that run in the same launch and
-// write fp32 partial sums to the workspace.
+// 128 up to kShortTileMaxM rows), then wide_cols column tiles of col_tile
+// columns from column 0 in one launch and (256 x 128 tiles only)
+// narrow_cols tiles of 64 columns after them in a second one.  col_tile is
+// 256 (the 256 x 256 kernel, gemm256.hip: W4 with groups of whole k-tiles,
+// above kShortTileMaxM rows) or 128 (the kernel of gemm.hip).  With
+// splits > 1 (small M), K is cut into ranges of split_tiles k-tiles that run
+// in the same launch and write fp32 partial sums to the workspace.
 constexpr int64_t kShortTileRows = 128;
 constexpr int64_t kShortTileMaxM = 128;
 struct GemmPlan {
-    int64_t m_tiles, wide_cols, narrow_cols, splits, split_tiles, rows;
+    int64_t m_tiles, wide_cols, narrow_cols, splits, split_tiles, rows, col_tile;
 };
-GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, int64_t G, int cus);
+// allow256 = false keeps the 256 x 128 kernel (a test route)
+GemmPlan plan_gemm(int bits, int64_t M, int64_t N, int64_t K, int64_t G, int cus, bool allow256 = true);
 // Compute units of the current device (queried once per device and kept:
 // the library's only process-wide state).
 int device_cus();
 // Workspace bytes of the tiled GEMM planned for `cus` compute units (0
 // unless it splits K).
-int64_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t G, int cus);
+int64_t gemm_workspace_bytes(int bits, int64_t M, int64_t N, int64_t K, int64_t G, int cus, int route);
 // Which kernel a GEMM call of M rows runs: the GEMV kernels (M <= 64: the
 // tiled GEMM would compute 128- or 256-row tiles) or the tiled GEMM.  The
 // route is an argument: kRouteAuto in every product call; the test hooks
-// may pass kRouteTiled (the tiled GEMM at any M) or kRouteGemv (the GEMV
-// kernels up to 64 rows).
-constexpr int kRouteAuto = 0, kRouteTiled = 1, kRouteGemv = 2;
+// may pass kRouteTiled (the tiled GEMM at any M), kRouteGemv (the GEMV
+// kernels up to 64 rows) or kRouteTiled128 (the tiled GEMM at any M, with
+// 256 x 128 tiles only).
+constexpr int kRouteAuto = 0, kRouteTiled = 1, kRouteGemv = 2, kRouteTiled128 = 3;
 bool gemm_uses_gemv(int64_t M, int route);
 // act = kActSiluMul: a [gate | up] layer packed with pair_half = N/2, y is
 // [M][N/2] = silu(gate) * up (as launch_gemv_silu_mul).
 hipError_t launch_gemm(int bits, const uint16_t *x, const void *packed, uint16_t *y, int64_t M, const Layout &lay,
-                       void *workspace, hipStream_t stream, int cus, int act = kActNone);
+                       void *workspace, hipStream_t stream, int cus, int act = kActNone, int route = kRouteAuto);
+// The 256 x 256 kernel for a plan with col_tile 256 (W4, groups of whole
+// k-tiles); ws holds the split partials when plan.splits > 1.
+hipError_t launch_gemm256(const uint16_t *x, const void *packed, uint16_t *y, int64_t M, const Layout &lay,
+                          const GemmPlan &plan, float *ws, hipStream_t stream, int act);
 
 // Measurement probes (not on the hot path).
 hipError_t launch_probe_read(const void *buf, uint64_t bytes, uint32_t *sink, hipStream_t stream);

@@ -113,20 +113,23 @@ def check_linear(case, torch, q, gemm, rows=None, cols=None, packed=None, d=None
 
 
 def split_cus(q, bits, M, K, N, G):
-    """A compute-unit count for which the tiled GEMM's plan has both 128- and
-    64-column tiles and does not split K, or None if no count gives one."""
+    """A compute-unit count for which the 256 x 128 tiled GEMM's plan has
+    both 128- and 64-column tiles and does not split K, or None if no count
+    gives one (run it with route TF_ROUTE_TILED128)."""
     mt = -(-M // 256)
     tiles = mt * -(-N // 128)
     for cus in range(2, tiles + 1):
-        _, wide, narrow, splits, _, _, _ = q.tf_gemm_plan(bits, M, K, N, G, cus, q.TF_ROUTE_TILED)
+        _, wide, narrow, splits, _, _, _, _ = q.tf_gemm_plan(bits, M, K, N, G, cus, q.TF_ROUTE_TILED128)
         if wide and narrow and splits == 1:
             return cus
     return None
 
 
-def splitk_cus(q, bits, M, K, N, G):
-    """A compute-unit count for which the tiled GEMM's plan splits K, or None."""
+def splitk_cus(q, bits, M, K, N, G, route=None):
+    """A compute-unit count for which the tiled GEMM's plan (route: default
+    TF_ROUTE_TILED) splits K, or None."""
+    route = q.TF_ROUTE_TILED if route is None else route
     for cus in (256, 1024, 4096, 1 << 20):
-        if q.tf_gemm_plan(bits, M, K, N, G, cus, q.TF_ROUTE_TILED)[3] > 1:
+        if q.tf_gemm_plan(bits, M, K, N, G, cus, route)[3] > 1:
             return cus
     return None

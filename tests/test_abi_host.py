@@ -88,7 +88,7 @@ def test_packed_bytes_invalid_shapes_are_zero(lib, K, N, G):
     assert lib.tf_packed_bytes_w4(K, N, G) == 0
 
 
-ROUTE_AUTO, ROUTE_TILED, ROUTE_GEMV = 0, 1, 2
+ROUTE_AUTO, ROUTE_TILED, ROUTE_GEMV, ROUTE_TILED128 = 0, 1, 2, 3
 OP_GEMV, OP_GEMM, OP_GEMV_SILU, OP_GEMM_SILU = 0, 1, 2, 3
 
 
@@ -111,7 +111,7 @@ def test_workspace_cannot_hold_bf16_weights(lib, route, M, K, N, G):
 
 
 def _plan(lib, M, N, cus, K=4096, G=128, bits=4, route=ROUTE_AUTO):
-    out = (ctypes.c_int64 * 7)()
+    out = (ctypes.c_int64 * 8)()
     st = lib.tf_gemm_plan(bits, M, K, N, G, cus, route, out)
     return st, tuple(out)
 
@@ -126,20 +126,21 @@ def test_workspace_only_for_split_k(lib, route):
     assert ws(8, OP_GEMV, 7, 8192, 8192, 8192) == 0
     assert ws(4, OP_GEMV, 17, 4096, 4096, 128) == 0  # beyond the GEMV's M
     # 16 rows, per-channel W8 8192 x 8192: the 16-row-chunk kernel in four K ranges
-    st, (_, _, _, splits, _, _, _) = _plan(lib, 16, 8192, 256, K=8192, G=8192, bits=8)
+    st, (_, _, _, splits, _, _, _, _) = _plan(lib, 16, 8192, 256, K=8192, G=8192, bits=8)
     assert ws(8, OP_GEMV, 16, 8192, 8192, 8192) == (16 * 8192 * 4 * splits if splits > 1 else 0)
     assert ws(8, OP_GEMV_SILU, 16, 8192, 8192, 8192) == ws(8, OP_GEMV, 16, 8192, 8192, 8192)
     assert lib.tf_workspace_bytes_planned(5, OP_GEMM, 1, 4096, 4096, 128, 256, route) == 0
     for bits, M, K, N, G in [(8, 512, 8192, 8192, 8192), (4, 1, 4096, 4096, 128), (4, 2048, 4096, 14336, 128),
                              (4, 100, 1024, 200, 64), (4, 64, 384, 64, 128), (4, 48, 4096, 4096, 128),
                              (8, 20, 8192, 1024, 8192), (4, 64, 4096, 28672, 128)]:
-        st, (_, _, _, splits, _, _, _) = _plan(lib, M, N, 256, K=K, G=G, bits=bits, route=route)
+        st, (_, _, _, splits, _, _, _, _) = _plan(lib, M, N, 256, K=K, G=G, bits=bits, route=route)
         assert st == TF_OK
         want = splits * M * N * 4 if splits > 1 else 0
         assert ws(bits, OP_GEMM, M, K, N, G) == want
         assert ws(bits, OP_GEMM_SILU, M, K, N, G) == want
     assert _plan(lib, 512, 8192, 256, K=8192, G=8192, bits=8)[1][3] == 2   # W8 M=512: two K ranges
     assert _plan(lib, 2048, 14336, 256)[1][3] == 1                         # prefill: no split
+    assert _plan(lib, 2048, 14336, 256, route=ROUTE_TILED128)[1][3] == 1
 
 
 def test_plan_hooks_keep_no_state(lib):
@@ -188,8 +189,8 @@ def test_gemv_route_plan_covers_k_once(lib):
         cases.append((rng.randint(1, 64), 8 * rng.randint(1, 5000), rng.choice([1, 2, 3, 7, 64, 80, 256, 304]),
                       K, rng.choice([G, K])))
     for M, N, cus, K, G in cases:
-        st, (mt, wide, narrow, splits, st_tiles, route, rows) = _plan(lib, M, N, cus, K=K, G=G)
-        assert st == TF_OK and route == 1 and mt == wide == narrow == rows == 0, (M, N, cus, K, G)
+        st, (mt, wide, narrow, splits, st_tiles, route, rows, cols) = _plan(lib, M, N, cus, K=K, G=G)
+        assert st == TF_OK and route == 1 and mt == wide == narrow == rows == cols == 0, (M, N, cus, K, G)
         ktiles = -(-K // 128)
         groups = -(-N // 128)
         assert (splits - 1) * st_tiles < ktiles <= splits * st_tiles
@@ -216,11 +217,14 @@ def test_gemv_route_plan_covers_k_once(lib):
         assert cost(splits) == best, (M, N, cus, K, G, splits)
 
 
-def test_gemm_plan_covers_every_column_once(lib):
-    """The launch plan: 128-column tiles from column 0, then 64-column tiles,
-    covering [0, N) with no tile wholly past N; the narrow launch exists only
-    when the wide tiles miss a whole number of rounds and fits one round.
-    A K split uses wide tiles only, fits one round, and its ranges of whole
+@pytest.mark.parametrize("route", [ROUTE_TILED, ROUTE_TILED128])
+def test_gemm_plan_covers_every_column_once(lib, route):
+    """The launch plan: wide tiles from column 0, then 64-column tiles,
+    covering [0, N) with no tile wholly past N; 256-column tiles for W4 with
+    groups of whole k-tiles above 128 rows (not on the 256 x 128 route), with
+    no narrow launch; otherwise 128-column tiles and a narrow launch only when
+    the wide tiles miss a whole number of rounds and it fits one round.  A K
+    split uses wide tiles only, fits one round, and its ranges of whole
     groups cover the k-tiles exactly once."""
     rng = __import__("random").Random(7)
     cases = [(2048, 14336, 256, 4096, 128), (2048, 4096, 256, 14336, 128), (512, 8192, 256, 8192, 8192),
@@ -231,36 +235,46 @@ def test_gemm_plan_covers_every_column_once(lib):
         K = G * rng.randint(1, 40) if G >= 128 else 128 * rng.randint(1, 40)
         cases.append((rng.randint(1, 9000), 8 * rng.randint(1, 5000), rng.choice([1, 2, 3, 7, 64, 80, 256, 304]),
                       K, rng.choice([G, K])))
-    for M, N, cus, K, G in cases:
-        st, (mt, wide, narrow, splits, st_tiles, route, rows) = _plan(lib, M, N, cus, K=K, G=G, route=ROUTE_TILED)
-        assert st == TF_OK and route == 0, (M, N, cus, K, G)
-        n_wide = -(-N // 128)
-        tiles = mt * n_wide
-        ktiles = -(-K // 128)
-        assert rows == (128 if M <= 128 else 256)
-        assert mt == -(-M // rows)
-        if rows == 128:
-            assert narrow == 0  # short tiles come in one width
-        if splits > 1:
-            assert wide == n_wide and narrow == 0
-            assert splits * tiles <= cus
-            assert (splits - 1) * st_tiles < ktiles <= splits * st_tiles
-            unit = G // 128 if G % 128 == 0 and G != K else 1
-            assert st_tiles % unit == 0 and st_tiles >= 4
-            continue
-        assert st_tiles == ktiles
-        if narrow == 0:
-            assert wide == n_wide
-        else:
-            assert tiles % cus != 0
-            assert wide * 128 < N <= wide * 128 + narrow * 64 < N + 64
-            assert mt * narrow <= cus
-            assert mt * wide <= (tiles // cus) * cus
-    # the headline prefill shape: 3 whole rounds of wide tiles, one of narrow
-    assert _plan(lib, 2048, 14336, 256)[1] == (8, 96, 32, 1, 32, 0, 256)
-    assert _plan(lib, 2048, 4096, 256, K=14336)[1] == (8, 32, 0, 1, 112, 0, 256)
+    for bits in (4, 8):
+        for M, N, cus, K, G in cases:
+            st, (mt, wide, narrow, splits, st_tiles, gemv, rows, cols) = _plan(lib, M, N, cus, K=K, G=G, bits=bits,
+                                                                             route=route)
+            assert st == TF_OK and gemv == 0, (M, N, cus, K, G)
+            big = route == ROUTE_TILED and bits == 4 and (G % 128 == 0 or G == K) and M > 128
+            assert cols == (256 if big else 128), (bits, M, N, cus, K, G)
+            n_wide = -(-N // cols)
+            tiles = mt * n_wide
+            ktiles = -(-K // 128)
+            assert rows == (128 if M <= 128 else 256)
+            assert mt == -(-M // rows)
+            if rows == 128 or big:
+                assert narrow == 0  # short tiles and 256-column tiles come in one width
+            if splits > 1:
+                assert wide == n_wide and narrow == 0
+                assert splits * tiles <= cus
+                assert (splits - 1) * st_tiles < ktiles <= splits * st_tiles
+                unit = G // 128 if G % 128 == 0 and G != K else 1
+                assert st_tiles % unit == 0 and st_tiles >= 4
+                continue
+            assert st_tiles == ktiles
+            if narrow == 0:
+                assert wide == n_wide
+            else:
+                assert tiles % cus != 0
+                assert wide * 128 < N <= wide * 128 + narrow * 64 < N + 64
+                assert mt * narrow <= cus
+                assert mt * wide <= (tiles // cus) * cus
+    if route == ROUTE_TILED:
+        # the headline prefill shapes on 256 x 256 tiles; the narrower one
+        # splits K in two to fill the chip
+        assert _plan(lib, 2048, 14336, 256)[1] == (8, 56, 0, 1, 32, 0, 256, 256)
+        assert _plan(lib, 2048, 4096, 256, K=14336)[1] == (8, 16, 0, 2, 56, 0, 256, 256)
+    else:
+        # 3 whole rounds of 256 x 128 tiles, one of 256 x 64
+        assert _plan(lib, 2048, 14336, 256, route=route)[1] == (8, 96, 32, 1, 32, 0, 256, 128)
+        assert _plan(lib, 2048, 4096, 256, K=14336, route=route)[1] == (8, 32, 0, 1, 112, 0, 256, 128)
     # 65..128 rows: one 128-row tile per column tile
-    assert _plan(lib, 100, 28672, 256)[1] == (1, 224, 0, 1, 32, 0, 128)
+    assert _plan(lib, 100, 28672, 256, route=route)[1] == (1, 224, 0, 1, 32, 0, 128, 128)
 
 
 def test_gemm_plan_rejects_bad_input(lib):
@@ -268,7 +282,7 @@ def test_gemm_plan_rejects_bad_input(lib):
     assert _plan(lib, 64, 0, 256)[0] == TF_ERR_SHAPE
     assert _plan(lib, 64, 64, 0)[0] == TF_ERR_SHAPE
     assert _plan(lib, 64, 64, 256, K=4096, G=96)[0] == TF_ERR_GROUP
-    out = (ctypes.c_int64 * 7)()
+    out = (ctypes.c_int64 * 8)()
     assert lib.tf_gemm_plan(4, 64, 4096, 64, 128, 256, 0, None) == TF_ERR_NULL
     assert lib.tf_gemm_plan(5, 64, 4096, 64, 128, 256, 0, out) == 6  # TF_ERR_UNSUPPORTED
 

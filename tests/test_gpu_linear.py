@@ -44,6 +44,12 @@ GEMM_SHAPES = [
     # K ranges of 32 rows: K = 32 on the tiled route, and a split whose last
     # range is one k-tile of 32 rows
     (4, 300, 32, 64, 32), (4, 100, 2592, 128, 32), (8, 140, 32, 40, 32),
+    # 256 x 256 tiles (W4, groups of whole k-tiles, above 128 rows): ragged N
+    # (a partial last tile and half a block), ragged M, groups of two and four
+    # k-tiles, per channel with a ragged last k-tile, one row tile with K
+    # split, one block of columns, K of one k-tile
+    (4, 600, 2048, 1000, 128), (4, 260, 1024, 264, 256), (4, 513, 4128, 520, 4128), (4, 200, 8192, 512, 512),
+    (4, 129, 1024, 8, 128), (4, 300, 128, 264, 128), (4, 1024, 4096, 2048, 128),
 ]
 
 # GEMM calls with 17 <= M <= 64 run the GEMV kernel with two or four 16-row
@@ -70,29 +76,39 @@ def test_gemv_within_tolerance(shape):
 
 
 def _plan_cus(q, plan, shape):
-    """Compute units to plan the tiled GEMM for: the device's (auto, tiled),
-    one (128-column tiles only), a count that splits the columns between both
-    tile widths, or one that splits K."""
-    if plan in ("auto", "tiled"):
+    """Compute units to plan the tiled GEMM for: the device's (auto, tiled,
+    tiled128), one (one launch of wide tiles, no split), a count that splits
+    the columns between 128- and 64-column tiles (with 256 x 128 tiles), or
+    one that splits K."""
+    if plan in ("auto", "tiled", "tiled128"):
         return 0
     if plan == "wide":
         return 1
-    cus = split_cus(q, *shape) if plan == "split" else splitk_cus(q, *shape)
+    if plan == "split":
+        cus = split_cus(q, *shape)
+    else:
+        cus = splitk_cus(q, *shape, route=q.TF_ROUTE_TILED128 if plan == "splitk128" else q.TF_ROUTE_TILED)
     if cus is None:
         pytest.skip(f"no compute-unit count gives a '{plan}' plan for this grid")
     return cus
 
 
-@pytest.mark.parametrize("plan", ["auto", "tiled", "wide", "split", "splitk"])
+PLAN_ROUTE = {"auto": 0, "tiled": 1, "tiled128": 3, "wide": 1, "split": 3, "splitk": 1, "splitk128": 3}
+
+
+@pytest.mark.parametrize("plan", list(PLAN_ROUTE))
 @pytest.mark.parametrize("shape", GEMM_SHAPES)
 def test_gemm_within_tolerance(shape, plan):
     """auto: the kernel the call picks (the GEMV kernel for M <= 64); the
-    other plans force the tiled GEMM."""
+    other plans force a tiled GEMM: the route's choice of tile (tiled, wide,
+    splitk) or 256 x 128 tiles (tiled128, split, splitk128)."""
     torch, q = gpu_or_skip()
     if plan == "tiled" and shape[1] > 64:
         pytest.skip("above 64 rows the automatic route is the tiled GEMM")
+    route = PLAN_ROUTE[plan]
+    if plan in ("tiled128", "splitk128") and q.tf_gemm_plan(*shape, 256, q.TF_ROUTE_TILED)[7] != 256:
+        pytest.skip("the shape runs 256 x 128 tiles on every tiled route")
     cus = _plan_cus(q, plan, shape)
-    route = q.TF_ROUTE_AUTO if plan == "auto" else q.TF_ROUTE_TILED
     print(f"gemm {shape} plan={plan} cus={cus} {q.tf_gemm_plan(*shape, cus or 256, route)}", flush=True)
     c = _case(*shape, seed=2)
     ok, ratio, _ = check_linear(c, torch, q, gemm=True, cus=cus, route=route)
@@ -105,6 +121,10 @@ def test_split_plans_exist_for_both_widths():
     _, q = gpu_or_skip()
     for bits in (4, 8):
         assert any(split_cus(q, *s) for s in GEMM_SHAPES if s[0] == bits), bits
+    # and the 256 x 256 tiles, with and without a K split
+    wide256 = [s for s in GEMM_SHAPES if q.tf_gemm_plan(*s, 256, q.TF_ROUTE_TILED)[7] == 256]
+    assert any(q.tf_gemm_plan(*s, 256, q.TF_ROUTE_TILED)[3] > 1 for s in wide256)
+    assert any(q.tf_gemm_plan(*s, 256, q.TF_ROUTE_TILED)[3] == 1 for s in wide256)
 
 
 @pytest.mark.parametrize("shape", [(4, 300, 32, 64, 32), (4, 100, 2592, 128, 32), (8, 140, 32, 40, 32),
@@ -159,12 +179,12 @@ def test_gemm_plans_agree_bitwise(bits, M, K, N, G):
     assert split is not None, "the shape must have a wide + narrow plan"
     outs = {}
     for cus in (1, split):
-        plan = q.tf_gemm_plan(bits, M, K, N, G, cus, q.TF_ROUTE_TILED)
+        plan = q.tf_gemm_plan(bits, M, K, N, G, cus, q.TF_ROUTE_TILED128)
         print(f"plans W{bits} M={M} K={K} N={N} G={G} cus={cus} {plan}", flush=True)
         assert plan[3] == 1
         outs[cus] = bf16_bits(run_linear(q, bits, q.TF_OP_GEMM, d["x"], pk, K, N, G, cus=cus,
-                                         route=q.TF_ROUTE_TILED, torch=torch))
-    assert q.tf_gemm_plan(bits, M, K, N, G, split, q.TF_ROUTE_TILED)[2] > 0
+                                         route=q.TF_ROUTE_TILED128, torch=torch))
+    assert q.tf_gemm_plan(bits, M, K, N, G, split, q.TF_ROUTE_TILED128)[2] > 0
     assert np.array_equal(outs[split], outs[1]), "the wide + narrow plan differs from the single wide launch"
 
 
@@ -186,7 +206,8 @@ def _integer_case(bits, M, K, N, G, seed):
 @pytest.mark.parametrize("gemm", [False, "auto", "tiled"])
 @pytest.mark.parametrize("bits,M,K,N,G", [(4, 1, 1024, 128, 128), (4, 7, 2048, 200, 64), (8, 4, 1024, 72, 1024),
                                           (4, 16, 14336, 64, 128), (8, 3, 512, 64, 32), (4, 40, 2048, 200, 64),
-                                          (8, 64, 1024, 72, 1024), (4, 33, 4096, 128, 128)])
+                                          (8, 64, 1024, 72, 1024), (4, 33, 4096, 128, 128),
+                                          (4, 300, 2048, 520, 128), (4, 260, 1024, 264, 512)])
 def test_integer_case_is_bit_exact(gemm, bits, M, K, N, G):
     torch, q = gpu_or_skip()
     if not gemm and M > 16:
@@ -204,7 +225,7 @@ def test_integer_case_is_bit_exact(gemm, bits, M, K, N, G):
     assert np.array_equal(bf16_bits(y), oracle.f64_to_bf16(exact.astype(np.float64)))
 
 
-@pytest.mark.parametrize("gemm,M", [(False, 5), ("auto", 5), ("tiled", 5), ("auto", 40), ("tiled", 40)])
+@pytest.mark.parametrize("gemm,M", [(False, 5), ("auto", 5), ("tiled", 5), ("auto", 40), ("tiled", 40), ("auto", 300)])
 @pytest.mark.parametrize("bits", [4, 8])
 def test_q_equal_zero_point_gives_zero(gemm, M, bits):
     torch, q = gpu_or_skip()

@@ -130,11 +130,11 @@ def test_gemv_plan_rejects_bad_input(lib):
 
 
 def test_every_split_plan_fits_the_noalloc_array(lib):
-    """tf_gemm_w4a16_noalloc holds its split-K partials in a 32 MiB array:
-    on 256 compute units no GEMM plan needs more (the bound is 256 x 256 x 128
-    fp32 values: a split runs only while the tiles fill at most half the
-    units)."""
-    cap = 32 << 20
+    """tf_gemm_w4a16_noalloc holds its split-K partials in a 64 MiB array:
+    on 256 compute units no GEMM plan needs more (the bound is 256 x 256 x 256
+    fp32 values: a split runs only while the tiles of at most 256 x 256 fill
+    at most half the units)."""
+    cap = 64 << 20
     worst = 0
     Ms = list(range(1, 65)) + [65, 96, 128, 129, 160, 200, 256, 300, 384, 512, 768, 1024]
     Ns = [128 * i for i in (1, 2, 4, 8, 16, 32, 48, 64, 128, 256)] + [1000, 5000]

@@ -15,7 +15,7 @@ from gpu_harness import bf16_bits, bf16_to_f64, gpu_or_skip, repack, to_device, 
 
 pytestmark = pytest.mark.gpu
 
-SCRATCH_BYTES = 32 << 20
+SCRATCH_BYTES = 64 << 20
 
 # (M, K, N): the 16-row-chunk GEMV kernel with K split (M <= 64), and the
 # tiled GEMM with K split (128-row tiles); each pair runs larger then smaller
@@ -53,11 +53,11 @@ def test_noalloc_matches_workspace_call(pair):
 
 
 def test_noalloc_largest_split_fits_the_array():
-    """The largest split plan on this device (256-row tiles filling half the
-    compute units, G = 32) runs from the array, and matches the workspace
-    call bit for bit."""
+    """The largest split plan on this device (256 x 256 tiles filling half
+    the compute units, K in two ranges) runs from the array, and matches the
+    workspace call bit for bit."""
     torch, q = gpu_or_skip()
-    M, K, N, G = 256, 4096, 4096, 32
+    M, K, N, G = 2048, 4096, 4096, 128
     need = q.tf_workspace_bytes(4, True, M, K, N, G)
     print(f"noalloc largest split: {need} bytes", flush=True)
     assert 0 < need <= SCRATCH_BYTES
@@ -73,7 +73,7 @@ def test_noalloc_largest_split_fits_the_array():
 
 def test_noalloc_without_split_and_empty():
     torch, q = gpu_or_skip()
-    M, K, N, G = 2048, 4096, 4096, 128  # 256 output tiles: no K split
+    M, K, N, G = 2048, 4096, 8192, 128  # 256 output tiles: no K split
     assert q.tf_workspace_bytes(4, True, M, K, N, G) == 0
     c = synth.make_inputs(4, M, K, N, G, seed=(92,), keep_codes=False)
     d = to_device(c, torch)
