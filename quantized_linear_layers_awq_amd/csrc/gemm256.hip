@@ -298,13 +298,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm256_kernel(const uint16_t *__
     wait_lgkmcnt0();
     lds_barrier();
 
-    // ---- one stage (k-tile t, half h): four 16-row slices.  Loads for later
-    //      stages first (the activations of the next stage; at a k-tile's
-    //      first stage the next k-tile's codes and records), all waited for
-    //      at the stage's end.  At a group's first stage each accumulator
-    //      tile is rescaled right before its first MFMA of the group.  The
-    //      next stage is unpacked in slices 2 and 3 (its codes read in slice
-    //      1 when it starts a new k-tile). ----
     // Fold of group boundary t (between k-tiles t - 1 and t): ratios from
     // the scales of k-tile t's group (ratio exactly 1 where no group starts
     // at t), applied to the row tiles i0 .. i0 + 1 (both columns j).
@@ -336,36 +329,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm256_kernel(const uint16_t *__
     //      last MFMAs of k-tile t (the last slice of its second stage), row
     //      tiles 2 and 3 in the first slice of k-tile t + 1, before their
     //      MFMAs.  Each half overlaps the other tiles' MFMAs.  The next stage
-    //      is unpacked in slices 1 and 2 (its codes read in slice 1 when it
-    //      starts a new k-tile). ----
-    // The instruction order inside a slice: each MFMA followed by a share of
-    // the slice's VALU work (unpack or fold), its LDS stores and its loads,
-    // so that both waves of a SIMD keep the matrix core fed while the other
-    // computes (the default schedule puts all VALU work ahead of the MFMAs).
-    auto interleave = [&](auto nv_c) {
-        constexpr int NV = decltype(nv_c)::value; // VALU instructions per MFMA
-        static_for<0, 8>([&](auto) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0); // one MFMA
-            if constexpr (NV > 0)
-                __builtin_amdgcn_sched_group_barrier(0x002, NV, 0); // VALU
-            __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);      // an LDS store
-            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);      // a global load
-            __builtin_amdgcn_sched_group_barrier(0x004, 2, 0);      // scalar work
-        });
-    };
-
-    // ---- one stage (k-tile t, half h): four 16-row slices.  Loads for later
-    //      stages first (the activations of the next stage; at a k-tile's
-    //      first stage the next k-tile's codes and records), all waited for
-    //      at the stage's end.  The scale fold of the group boundary before
-    //      k-tile t + 1 is split in two: row tiles 0 and 1 right after their
-    //      last MFMAs of k-tile t (the last slice of its second stage), row
-    //      tiles 2 and 3 in the first slice of k-tile t + 1, before their
-    //      MFMAs.  Each half overlaps the other tiles' MFMAs.  The next stage
     //      is unpacked in slices 1 and 2 (its codes read in slice 0 when it
-    //      starts a new k-tile).  No step depends on a branch: after the last
-    //      stage the loads re-read in-bounds data (clamped) into buffers no
-    //      one reads, and the unpack writes the idle B buffer. ----
+    //      starts a new k-tile); within a slice the compiler's own schedule
+    //      spreads that VALU work between the MFMAs (measured faster than
+    //      forcing an MFMA/VALU pattern).  No step depends on a branch: after
+    //      the last stage the loads re-read in-bounds data (clamped) into
+    //      buffers no one reads, and the unpack writes the idle B buffer. ----
     auto stage = [&](int t, auto h_c) {
         constexpr int h = decltype(h_c)::value;
         constexpr int hn = h ^ 1; // parity of the next stage
@@ -409,12 +378,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm256_kernel(const uint16_t *__
                 fold_ratios(t + 1); // the boundary before k-tile t + 1
                 fold_rows(0);
             }
-            if constexpr ((sl == 0 && h == 0) || (sl == 3 && h == 1))
-                interleave(ic<9>{});
-            else if constexpr (sl == 1 || sl == 2)
-                interleave(ic<6>{});
-            else
-                interleave(ic<1>{});
         });
         wait_vmcnt<0>();
         wait_lgkmcnt0();
