@@ -42,6 +42,9 @@ HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
 BF16_DENSE_PEAK_TFS = 2500.0  # MI355X dense bf16 MFMA, published
 INFINITY_CACHE_BYTES = 256 * 2**20
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "gemv_w4a16_layer_m1_counters.json")
+GEMM_COUNTERS_FILE = os.path.join(ROOT, "profiles", "gemm_w4a16_m2048_counters.json")
+GEMM_SOURCES = ("gemm256.hip", "gemm.hip", "tf_gemm_common.h", "tf_common.h", "tf_launch.h", "tf_operands.h")
+GEMM_TRACE_NAME = "gemm256_kernel"
 
 
 def algorithmic_bytes(bits, M, K, N, G):
@@ -55,12 +58,12 @@ GEMV_SOURCES = ("gemv.hip", "tf_common.h", "tf_launch.h", "tf_operands.h")
 GEMV_TRACE_NAME = "gemv_kernel<4, 2, {depth}, {bpw}, 0>"
 
 
-def kernel_source_hash():
-    """Hash of the GEMV kernel's sources: stored counters are used only while
-    the kernel they were taken on is unchanged."""
+def kernel_source_hash(sources=GEMV_SOURCES):
+    """Hash of a kernel's sources: stored counters are used only while the
+    kernel they were taken on is unchanged."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "quantized_linear_layers_awq_amd", "csrc")
-    for name in GEMV_SOURCES:
+    for name in sources:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
@@ -80,6 +83,11 @@ def parse():
     p.add_argument("--counters-from", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
                    help="no GPU: read four rocprofv3 --pmc output directories (FETCH_SIZE and WRITE_SIZE over "
                         "'--only gemv', then over '--only copy') and write the per-launch HBM traffic file")
+    p.add_argument("--gemm-counters-from", nargs=6,
+                   metavar=("TRACE", "BUSY", "FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
+                   help="no GPU: read a --kernel-trace directory and five --pmc directories over '--only gemm' "
+                        "(SQ_VALU_MFMA_BUSY_CYCLES with GRBM_GUI_ACTIVE, FETCH_SIZE, WRITE_SIZE) and "
+                        "'--only copy' (FETCH_SIZE, WRITE_SIZE), and write the GEMM counter file")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--no-energy", action="store_true", help="skip the energy-per-call leg")
     p.add_argument("--no-configs", action="store_true", help="skip the per-config throughput table")
@@ -175,7 +183,8 @@ def _pmc_rows(path):
     for fn in files:
         with open(fn, newline="") as f:
             for r in csv.DictReader(f):
-                rows.append((r["Kernel_Name"], r["Counter_Name"], float(r["Counter_Value"]), r.get("Dispatch_Id")))
+                rows.append((r["Kernel_Name"], r["Counter_Name"], float(r["Counter_Value"]), r.get("Dispatch_Id"),
+                             int(r.get("Grid_Size") or r.get("Grid_Size_X") or 0)))
     return rows
 
 
@@ -183,8 +192,8 @@ def _per_dispatch_kib(path, counter, match):
     """Mean over matching dispatches of one counter (summed over its
     instances within a dispatch), in the counter's own unit (KiB)."""
     per = {}
-    for name, cname, v, did in _pmc_rows(path):
-        if cname == counter and match(name):
+    for name, cname, v, did, grid in _pmc_rows(path):
+        if cname == counter and match(name, grid):
             per[did] = per.get(did, 0.0) + v
     if not per:
         raise SystemExit(f"no {counter} dispatches matched in {path}")
@@ -196,8 +205,8 @@ def write_counters(dirs, kernel):
     the layer step) from two --pmc passes, each scaled by the same counter's
     reading on the plain copy kernel."""
     fetch_dir, write_dir, cfetch_dir, cwrite_dir = dirs
-    is_gemv = lambda n: kernel in n
-    is_copy = lambda n: "copy" in n.lower() and "gemv" not in n
+    is_gemv = lambda n, grid: kernel in n
+    is_copy = lambda n, grid: "copy" in n.lower() and "gemv" not in n
     f_kib, nf = _per_dispatch_kib(fetch_dir, "FETCH_SIZE", is_gemv)
     w_kib, nw = _per_dispatch_kib(write_dir, "WRITE_SIZE", is_gemv)
     cf_kib, _ = _per_dispatch_kib(cfetch_dir, "FETCH_SIZE", is_copy)
@@ -213,6 +222,83 @@ def write_counters(dirs, kernel):
                                      fetch_scale=round(fetch_scale, 4), write_scale=round(write_scale, 4)),
                hbm_bytes_per_launch=round(hbm))
     with open(COUNTERS_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out))
+
+
+def _trace_us(path, match):
+    """Mean duration (us) and count of the matching dispatches of a rocprofv3
+    kernel trace (a file, or a directory searched for *kernel_trace.csv)."""
+    import csv
+    import glob
+
+    files = [path] if os.path.isfile(path) else sorted(
+        glob.glob(os.path.join(path, "**", "*kernel_trace.csv"), recursive=True))
+    if not files:
+        raise SystemExit(f"no kernel_trace.csv under {path}")
+    d = []
+    for fn in files:
+        with open(fn, newline="") as f:
+            for r in csv.DictReader(f):
+                grid = int(r.get("Grid_Size") or r.get("Grid_Size_X") or 0)
+                if match(r["Kernel_Name"], grid):
+                    d.append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    if not d:
+        raise SystemExit(f"no dispatch matched in {path}")
+    return sum(d) / len(d), len(d)
+
+
+def gemm_bench_shapes():
+    """(M, K, N, G) of the two prefill shapes the GEMM leg times."""
+    return [(2048, 4096, 14336, 128), (2048, 14336, 4096, 128)]
+
+
+def gemm_grid_threads(q, M, K, N, G):
+    """Threads in the 256 x 256 GEMM kernel's grid for a shape (its launch
+    plan from tf_gemm_plan; no GPU needed)."""
+    m_tiles, wide, narrow, splits, _, _, rows, col_tile = q.tf_gemm_plan(4, M, K, N, G, cus=256)
+    if col_tile != 256:
+        raise SystemExit(f"shape {M}x{K}x{N} does not run the 256 x 256 kernel")
+    return m_tiles * wide * splits * 512
+
+
+def write_gemm_counters(dirs):
+    """MFMA busy, clock and HBM traffic per launch of the 256 x 256 GEMM
+    kernel on each prefill shape, from a kernel trace and five --pmc passes
+    (the traffic counters scaled by their readings on the plain copy kernel)."""
+    import quantized_linear_layers_awq_amd as q
+
+    trace_dir, busy_dir, fetch_dir, write_dir, cfetch_dir, cwrite_dir = dirs
+    is_copy = lambda n, grid: "copy" in n.lower() and "gemm" not in n
+    cf_kib, _ = _per_dispatch_kib(cfetch_dir, "FETCH_SIZE", is_copy)
+    cw_kib, _ = _per_dispatch_kib(cwrite_dir, "WRITE_SIZE", is_copy)
+    fetch_scale = COPY_BYTES / (cf_kib * 1024)
+    write_scale = COPY_BYTES / (cw_kib * 1024)
+    shapes = []
+    for M, K, N, G in gemm_bench_shapes():
+        threads = gemm_grid_threads(q, M, K, N, G)
+        match = lambda n, grid, t=threads: GEMM_TRACE_NAME in n and grid == t
+        us, n_trace = _trace_us(trace_dir, match)
+        busy, nb = _per_dispatch_kib(busy_dir, "SQ_VALU_MFMA_BUSY_CYCLES", match)
+        grbm, _ = _per_dispatch_kib(busy_dir, "GRBM_GUI_ACTIVE", match)
+        f_kib, nf = _per_dispatch_kib(fetch_dir, "FETCH_SIZE", match)
+        w_kib, nw = _per_dispatch_kib(write_dir, "WRITE_SIZE", match)
+        simd_cycles = grbm / 8 * 1024  # GRBM_GUI_ACTIVE sums the 8 XCDs; 256 CUs x 4 SIMDs
+        flops = 2.0 * M * K * N
+        alg = 2 * M * K + algorithmic_bytes(4, 0, K, N, G) + 2 * M * N
+        shapes.append(dict(M=M, K=K, N=N, G=G, grid_threads=threads, trace_us=round(us, 2),
+                           trace_tflops=round(flops / (us * 1e-6) / 1e12, 1),
+                           clock_ghz=round(grbm / 8 / (us * 1e3), 3), mfma_busy=round(busy / simd_cycles, 4),
+                           fetch_kib_per_launch=round(f_kib, 1), write_kib_per_launch=round(w_kib, 1),
+                           hbm_bytes_per_launch=round(f_kib * 1024 * fetch_scale + w_kib * 1024 * write_scale),
+                           algorithmic_bytes=int(alg), dispatches=dict(trace=n_trace, busy=nb, fetch=nf, write=nw)))
+    out = dict(kernel_source_hash=kernel_source_hash(GEMM_SOURCES), kernel_trace_name=GEMM_TRACE_NAME,
+               kernel=f"{GEMM_TRACE_NAME} (tf_gemm_w4a16), M=2048 prefill shapes",
+               shapes=shapes,
+               copy_calibration=dict(bytes=COPY_BYTES, fetch_kib=round(cf_kib, 1), write_kib=round(cw_kib, 1),
+                                     fetch_scale=round(fetch_scale, 4), write_scale=round(write_scale, 4)))
+    with open(GEMM_COUNTERS_FILE, "w") as f:
         json.dump(out, f, indent=1)
         f.write("\n")
     print(json.dumps(out))
@@ -572,12 +658,36 @@ def bench_gemm(torch, q, args):
     e1.record()
     torch.cuda.synchronize()
     mfma_roof = fl / (e0.elapsed_time(e1) * 1e-3) / 1e12
+
+    # counters of the same kernel build (MFMA busy, clock, HBM bytes per
+    # launch), taken by rocprofv3 passes over this leg and stored with the
+    # hash of the kernel's sources; unused once the sources have changed
+    counters = None
+    if os.path.exists(GEMM_COUNTERS_FILE):
+        with open(GEMM_COUNTERS_FILE) as f:
+            cnt = json.load(f)
+        if cnt.get("kernel_source_hash") == kernel_source_hash(GEMM_SOURCES):
+            counters = cnt
+    traffic = mfma_busy = clock = None
+    if counters:
+        sh = counters["shapes"]
+        traffic = round(sum(c["hbm_bytes_per_launch"] for c in sh) / len(sh))
+        wsum = sum(c["trace_us"] for c in sh)
+        mfma_busy = round(sum(c["mfma_busy"] * c["trace_us"] for c in sh) / wsum, 4)
+        clock = round(sum(c["clock_ghz"] * c["trace_us"] for c in sh) / wsum, 3)
     return dict(
         metric="W4A16 GEMM M=2048 TFLOP/s", value=round(tfs, 1), unit="TFLOP/s",
         frac_of_peak=round(tfs / BF16_DENSE_PEAK_TFS, 4), shapes=out,
         roofline=dict(bound="mfma", achieved=round(tfs, 1), peak=BF16_DENSE_PEAK_TFS, unit="TFLOP/s",
-                      frac=round(tfs / BF16_DENSE_PEAK_TFS, 4), traffic=None,
+                      frac=round(tfs / BF16_DENSE_PEAK_TFS, 4), traffic=traffic,
                       kernel="gemm256_kernel (tf_gemm_w4a16; per call, the split-K sum included)",
+                      mfma_busy=mfma_busy, clock_ghz=clock,
+                      counters=None if counters is None else dict(
+                          source=os.path.relpath(GEMM_COUNTERS_FILE, ROOT),
+                          what="time-weighted over both shapes; traffic = mean HBM bytes per launch of the kernel",
+                          shapes=[dict(K=c["K"], N=c["N"], trace_us=c["trace_us"], mfma_busy=c["mfma_busy"],
+                                       clock_ghz=c["clock_ghz"], hbm_bytes_per_launch=c["hbm_bytes_per_launch"],
+                                       algorithmic_bytes=c["algorithmic_bytes"]) for c in counters["shapes"]]),
                       measured_roof=round(mfma_roof, 1), frac_of_measured_roof=round(tfs / mfma_roof, 4),
                       measured_roof_kind="back-to-back bf16 32x32x16 MFMAs, 8 waves per CU, sustained "
                                          "as long as the GEMM launches"),
@@ -912,6 +1022,9 @@ def main():
     args = parse()
     if args.counters_from:
         write_counters(args.counters_from, args.counters_kernel)
+        return
+    if args.gemm_counters_from:
+        write_gemm_counters(args.gemm_counters_from)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the library has no multi-GPU path.",
