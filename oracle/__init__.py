@@ -52,9 +52,14 @@ def lib():
         L.oracle_f64_to_bf16.argtypes = [ctypes.c_double]
         L.oracle_f64_to_bf16.restype = ctypes.c_uint16
         L.oracle_round_bf16.argtypes = [P, I64, P]
-        L.oracle_dequant_w4.argtypes = [P, P, P, I64, I64, I64, P, I64, P]
-        L.oracle_dequant_w8.argtypes = [P, P, P, I64, I64, I64, P, I64, P]
-        L.oracle_linear.argtypes = [P, I64, I64, P, I64, P]
+        L.oracle_f16_to_f32.argtypes = [ctypes.c_uint16]
+        L.oracle_f16_to_f32.restype = ctypes.c_float
+        L.oracle_f64_to_f16.argtypes = [ctypes.c_double]
+        L.oracle_f64_to_f16.restype = ctypes.c_uint16
+        L.oracle_round_f16.argtypes = [P, I64, P]
+        L.oracle_dequant_w4.argtypes = [P, P, P, ctypes.c_int, I64, I64, I64, P, I64, P]
+        L.oracle_dequant_w8.argtypes = [P, P, P, ctypes.c_int, I64, I64, I64, P, I64, P]
+        L.oracle_linear.argtypes = [P, ctypes.c_int, I64, I64, P, I64, P]
         L.oracle_silu_mul.argtypes = [P, P, I64, P]
         L.oracle_num_threads.restype = ctypes.c_int
         L.oracle_set_num_threads.argtypes = [ctypes.c_int]
@@ -118,8 +123,35 @@ def f64_to_bf16(y) -> np.ndarray:
     return out
 
 
-def dequant(bits, qweight, qzeros, scales, K, N, G, cols=None) -> np.ndarray:
-    """Dequantized fp32 weights w[K][len(cols)] (all N columns when cols is None)."""
+FORMATS = {"bf16": 0, "f16": 1}
+
+
+def _fmt(dtype: str) -> int:
+    if dtype not in FORMATS:
+        raise ValueError(f"dtype must be one of {sorted(FORMATS)}")
+    return FORMATS[dtype]
+
+
+def f16_to_f32(bits) -> np.ndarray:
+    """Widen fp16 bit patterns to float32 (exact)."""
+    bits = _c(bits, np.uint16)
+    f = np.vectorize(lambda b: lib().oracle_f16_to_f32(int(b)), otypes=[np.float32])
+    return f(bits) if bits.size else bits.astype(np.float32)
+
+
+def f64_to_f16(y) -> np.ndarray:
+    """Round fp64 values to fp16 bits (nearest, ties to even, overflow to
+    infinity) in one step."""
+    y = _c(y, np.float64)
+    out = np.empty(y.shape, dtype=np.uint16)
+    lib().oracle_round_f16(_p(y), y.size, _p(out))
+    return out
+
+
+def dequant(bits, qweight, qzeros, scales, K, N, G, cols=None, dtype="bf16") -> np.ndarray:
+    """Dequantized fp32 weights w[K][len(cols)] (all N columns when cols is
+    None); scales are bf16 or fp16 bit patterns (dtype)."""
+    fmt = _fmt(dtype)
     sc = _c(scales, np.uint16)
     if cols is None:
         cp, ncols = None, N
@@ -132,34 +164,38 @@ def dequant(bits, qweight, qzeros, scales, K, N, G, cols=None) -> np.ndarray:
     if bits == 4:
         qw, qz = _c(qweight, np.uint32), _c(qzeros, np.uint32)
         assert qw.shape == (K, N // 8) and qz.shape == (K // G, N // 8)
-        lib().oracle_dequant_w4(_p(qw), _p(qz), _p(sc), K, N, G, cp, ncols, _p(w))
+        lib().oracle_dequant_w4(_p(qw), _p(qz), _p(sc), fmt, K, N, G, cp, ncols, _p(w))
     elif bits == 8:
         qw, qz = _c(qweight, np.uint8), _c(qzeros, np.uint8)
         assert qw.shape == (K, N) and qz.shape == (K // G, N)
-        lib().oracle_dequant_w8(_p(qw), _p(qz), _p(sc), K, N, G, cp, ncols, _p(w))
+        lib().oracle_dequant_w8(_p(qw), _p(qz), _p(sc), fmt, K, N, G, cp, ncols, _p(w))
     else:
         raise ValueError("bits must be 4 or 8")
     assert sc.shape == (K // G, N)
     return w
 
 
-def linear(x_bits, w) -> np.ndarray:
-    """y64[M][N] = sum_k x[m][k] * w[k][n] in fp64, k ascending."""
+def linear(x_bits, w, dtype="bf16") -> np.ndarray:
+    """y64[M][N] = sum_k x[m][k] * w[k][n] in fp64, k ascending; x holds bf16
+    or fp16 bit patterns (dtype)."""
+    fmt = _fmt(dtype)
     x = _c(x_bits, np.uint16)
     w = _c(w, np.float32)
     M, K = x.shape
     assert w.shape[0] == K
     N = w.shape[1]
     y = np.empty((M, N), dtype=np.float64)
-    lib().oracle_linear(_p(x), M, K, _p(w), N, _p(y))
+    lib().oracle_linear(_p(x), fmt, M, K, _p(w), N, _p(y))
     return y
 
 
 def awq_linear(case, cols=None, rows=None) -> np.ndarray:
-    """Reference output of a synth.Case: fp64 y for the chosen rows/columns."""
-    w = dequant(case.bits, case.qweight, case.qzeros, case.scales, case.K, case.N, case.G, cols)
+    """Reference output of a synth.Case: fp64 y for the chosen rows/columns
+    (x and scales in the case's dtype, bf16 or fp16)."""
+    dtype = getattr(case, "dtype", "bf16")
+    w = dequant(case.bits, case.qweight, case.qzeros, case.scales, case.K, case.N, case.G, cols, dtype=dtype)
     x = case.x if rows is None else case.x[np.asarray(rows)]
-    return linear(x, w)
+    return linear(x, w, dtype=dtype)
 
 
 def silu_mul(g, u) -> np.ndarray:

@@ -21,6 +21,12 @@
  * and the k-ascending sum in fp64, one rounding to bf16 at the end, straight
  * from fp64 (round to nearest, ties to even).
  *
+ * Half-precision variant: many AWQ checkpoints store fp16 scales and run on
+ * fp16 activations.  With fmt = 1 the scales and x are IEEE binary16 and the
+ * output is rounded once to binary16 (nearest, ties to even, overflow to
+ * infinity).  The dequant stays exact in fp32: 8 bits of (q - z) times 11
+ * significant bits of an fp16 scale is at most 19 < 24 bits.
+ *
  * The repack/unrepack routines implement the interleaved pre-tiled layout
  * (TileFuse summary, Methodology section 2, "Interleaved pre-tiling":
  * scales and zero points packed into the weight tiles, tiles one consumer
@@ -121,12 +127,69 @@ void oracle_round_bf16(const double *y, int64_t n, uint16_t *out)
 }
 
 /* ------------------------------------------------------------------ */
+/* IEEE binary16 (fp16) <-> binary floating point                      */
+/* Sign bit, 5 exponent bits (bias 15), 10 fraction bits: 11           */
+/* significant bits, normal exponents -14..15, subnormal quantum 2^-24, */
+/* largest finite value 65504.                                         */
+/* ------------------------------------------------------------------ */
+float oracle_f16_to_f32(uint16_t h)
+{
+    int sign = h >> 15, e = (h >> 10) & 0x1F, f = h & 0x3FF;
+    double v;
+    if (e == 0x1F)
+        v = f ? NAN : INFINITY;
+    else if (e == 0)
+        v = ldexp((double)f, -24);            /* subnormal: f * 2^-24 */
+    else
+        v = ldexp((double)(f | 0x400), e - 25); /* (1024 + f) * 2^(e - 15 - 10) */
+    return (float)(sign ? -v : v);
+}
+
+/* Round a double to the nearest fp16 value, ties to even, in one step;
+ * magnitudes that round past 65504 become infinity. */
+uint16_t oracle_f64_to_f16(double v)
+{
+    if (isnan(v))
+        return 0x7E00;
+    uint16_t sign = signbit(v) ? 0x8000 : 0;
+    double a = fabs(v);
+    if (isinf(a))
+        return sign | 0x7C00;
+    if (a == 0.0)
+        return sign;
+    int e;
+    (void)frexp(a, &e);             /* 2^(e-1) <= a < 2^e */
+    int quantum_exp = (e - 1) - 10; /* spacing of 11-significant-bit values in that binade */
+    if (quantum_exp < -24)
+        quantum_exp = -24;          /* subnormal range */
+    double r = ldexp(nearbyint(ldexp(a, -quantum_exp)), quantum_exp);
+    if (r >= 65536.0)
+        return sign | 0x7C00;
+    if (r < 0x1p-14)                /* subnormal (or the smallest normal, reached below) */
+        return sign | (uint16_t)ldexp(r, 24);
+    int e2;
+    double f2 = frexp(r, &e2);      /* r = f2 * 2^e2, f2 in [0.5, 1) */
+    uint16_t frac = (uint16_t)ldexp(f2 * 2.0 - 1.0, 10); /* exact: r has <= 11 significant bits */
+    return sign | (uint16_t)((e2 - 1 + 15) << 10) | frac;
+}
+
+void oracle_round_f16(const double *y, int64_t n, uint16_t *out)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = oracle_f64_to_f16(y[i]);
+}
+
+/* A 16-bit scale or activation in format fmt: 0 = bf16, 1 = fp16. */
+static inline float half_to_f32(uint16_t b, int fmt) { return fmt ? oracle_f16_to_f32(b) : oracle_bf16_to_f32(b); }
+
+/* ------------------------------------------------------------------ */
 /* Dequantization: w[k][j] = (q - z) * s for output column cols[j]     */
-/* (all columns when cols == NULL).  fp32, exact.                      */
+/* (all columns when cols == NULL).  fp32, exact.  Scales in format    */
+/* fmt (0 = bf16, 1 = fp16).                                          */
 /* ------------------------------------------------------------------ */
 static inline int64_t col_of(const int64_t *cols, int64_t j) { return cols ? cols[j] : j; }
 
-void oracle_dequant_w4(const uint32_t *qweight, const uint32_t *qzeros, const uint16_t *scales,
+void oracle_dequant_w4(const uint32_t *qweight, const uint32_t *qzeros, const uint16_t *scales, int fmt,
                        int64_t K, int64_t N, int64_t G, const int64_t *cols, int64_t ncols, float *w)
 {
 #pragma omp parallel for schedule(static)
@@ -136,13 +199,13 @@ void oracle_dequant_w4(const uint32_t *qweight, const uint32_t *qzeros, const ui
             int64_t n = col_of(cols, j);
             int q = (int)awq_code(qweight, N, k, n);
             int z = (int)awq_code(qzeros, N, g, n);
-            float s = oracle_bf16_to_f32(scales[g * N + n]);
+            float s = half_to_f32(scales[g * N + n], fmt);
             w[k * ncols + j] = (float)(q - z) * s;
         }
     }
 }
 
-void oracle_dequant_w8(const uint8_t *qweight, const uint8_t *zeros, const uint16_t *scales,
+void oracle_dequant_w8(const uint8_t *qweight, const uint8_t *zeros, const uint16_t *scales, int fmt,
                        int64_t K, int64_t N, int64_t G, const int64_t *cols, int64_t ncols, float *w)
 {
 #pragma omp parallel for schedule(static)
@@ -152,20 +215,21 @@ void oracle_dequant_w8(const uint8_t *qweight, const uint8_t *zeros, const uint1
             int64_t n = col_of(cols, j);
             int q = qweight[k * N + n];
             int z = zeros[g * N + n];
-            float s = oracle_bf16_to_f32(scales[g * N + n]);
+            float s = half_to_f32(scales[g * N + n], fmt);
             w[k * ncols + j] = (float)(q - z) * s;
         }
     }
 }
 
 /* ------------------------------------------------------------------ */
-/* Linear: y[m][n] = sum_{k ascending} x[m][k] * w[k][n], in fp64.     */
+/* Linear: y[m][n] = sum_{k ascending} x[m][k] * w[k][n], in fp64;    */
+/* x in format fmt (0 = bf16, 1 = fp16).                              */
 /* Each thread owns a (row, column range) block and walks k outermost, */
 /* so every output element still sums in k order.                     */
 /* ------------------------------------------------------------------ */
 #define ORACLE_COL_CHUNK 512
 
-void oracle_linear(const uint16_t *x, int64_t M, int64_t K, const float *w, int64_t N, double *y)
+void oracle_linear(const uint16_t *x, int fmt, int64_t M, int64_t K, const float *w, int64_t N, double *y)
 {
     int64_t nchunks = (N + ORACLE_COL_CHUNK - 1) / ORACLE_COL_CHUNK;
 #pragma omp parallel for schedule(dynamic, 1)
@@ -177,7 +241,7 @@ void oracle_linear(const uint16_t *x, int64_t M, int64_t K, const float *w, int6
         for (int64_t n = n0; n < n1; ++n)
             yr[n] = 0.0;
         for (int64_t k = 0; k < K; ++k) {
-            double xv = (double)oracle_bf16_to_f32(x[m * K + k]);
+            double xv = (double)half_to_f32(x[m * K + k], fmt);
             const float *wr = w + k * N;
             for (int64_t n = n0; n < n1; ++n)
                 yr[n] += xv * (double)wr[n];

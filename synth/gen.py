@@ -19,6 +19,10 @@ Storage formats produced (the inputs of the linear layer):
 * scales: bf16 bit patterns (uint16) ``[K/G][N]``; group ``g`` covers rows
   ``g*G .. g*G+G-1`` of one output column (per-channel metadata is G = K).
 * activations x: bf16 bit patterns (uint16) ``[M][K]``.
+
+With ``dtype="f16"`` the scales and activations are drawn from the same
+distributions and stored as IEEE fp16 bit patterns instead (the format of
+many AWQ checkpoints); ``Case.dtype`` records which.
 """
 
 from __future__ import annotations
@@ -46,6 +50,21 @@ def f32_to_bf16_bits(a) -> np.ndarray:
     if nan.any():
         out[nan] = 0x7FC0
     return out
+
+
+def f32_to_f16_bits(a) -> np.ndarray:
+    """Round float32 values to IEEE fp16 (numpy's conversion: nearest, ties
+    to even); return uint16 bits."""
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float32)).astype(np.float16).view(np.uint16)
+
+
+def to_half_bits(a, dtype) -> np.ndarray:
+    """float32 values -> bit patterns of the 16-bit format dtype ("bf16" or "f16")."""
+    if dtype == "bf16":
+        return f32_to_bf16_bits(a)
+    if dtype == "f16":
+        return f32_to_f16_bits(a)
+    raise ValueError("dtype must be 'bf16' or 'f16'")
 
 
 def bf16_bits_to_f32(b) -> np.ndarray:
@@ -86,9 +105,10 @@ class Case:
     zeros: np.ndarray | None = None
     name: str = ""
     meta: dict = field(default_factory=dict)
+    dtype: str = "bf16"  # format of scales and x: "bf16" or "f16"
 
 
-def pack_case(bits, codes, zeros, scales_bits, x_bits, G, name="", keep_codes=True) -> Case:
+def pack_case(bits, codes, zeros, scales_bits, x_bits, G, name="", keep_codes=True, dtype="bf16") -> Case:
     """Wrap drawn (or hand-made) codes/zeros/scales/x into a :class:`Case`."""
     codes = np.ascontiguousarray(codes, dtype=np.uint8)
     zeros = np.ascontiguousarray(zeros, dtype=np.uint8)
@@ -106,7 +126,7 @@ def pack_case(bits, codes, zeros, scales_bits, x_bits, G, name="", keep_codes=Tr
     return Case(bits=bits, M=M, K=K, N=N, G=G, qweight=qweight, qzeros=qzeros,
                 scales=np.ascontiguousarray(scales_bits, dtype=np.uint16), x=x_bits,
                 codes=codes if keep_codes else None, zeros=zeros if keep_codes else None,
-                name=name)
+                name=name, dtype=dtype)
 
 
 # Value distributions per weight width: code range, zero range (inclusive),
@@ -117,27 +137,28 @@ DIST = {
 }
 
 
-def draw_weights(rng, bits, K, N, G):
-    """Draw codes [K][N], zeros [K/G][N] and bf16 scales [K/G][N], in that order."""
+def draw_weights(rng, bits, K, N, G, dtype="bf16"):
+    """Draw codes [K][N], zeros [K/G][N] and scales [K/G][N] (bit patterns of
+    dtype), in that order."""
     d = DIST[bits]
     codes = rng.integers(0, 1 << bits, size=(K, N), dtype=np.uint8)
     zeros = rng.integers(d["zero_lo"], d["zero_hi"] + 1, size=(K // G, N), dtype=np.uint8)
     z = rng.standard_normal(size=(K // G, N), dtype=np.float32)
     scales = np.float32(d["scale_a"]) + np.float32(d["scale_c"]) * np.abs(z)
-    return codes, zeros, f32_to_bf16_bits(scales)
+    return codes, zeros, to_half_bits(scales, dtype)
 
 
-def draw_x(rng, M, K, outlier_frac=0.0, outlier_gain=20.0):
+def draw_x(rng, M, K, outlier_frac=0.0, outlier_gain=20.0, dtype="bf16"):
     """Draw activations N(0,1); optionally scale round(frac*K) channels by gain."""
     x = rng.standard_normal(size=(M, K), dtype=np.float32)
     if outlier_frac > 0:
         n_out = int(round(outlier_frac * K))
         ch = rng.choice(K, size=n_out, replace=False)
         x[:, ch] *= np.float32(outlier_gain)
-    return f32_to_bf16_bits(x)
+    return to_half_bits(x, dtype)
 
 
-def make_inputs(bits, M, K, N, G, seed, outlier_frac=0.0, keep_codes=True, name="") -> Case:
+def make_inputs(bits, M, K, N, G, seed, outlier_frac=0.0, keep_codes=True, name="", dtype="bf16") -> Case:
     """Draw a full case from ``seed`` (a tuple of ints).
 
     Weights come from ``SeedSequence(seed)`` and activations from
@@ -145,10 +166,10 @@ def make_inputs(bits, M, K, N, G, seed, outlier_frac=0.0, keep_codes=True, name=
     """
     seed = tuple(int(s) for s in seed)
     wrng = np.random.default_rng(np.random.SeedSequence(list(seed)))
-    codes, zeros, scales = draw_weights(wrng, bits, K, N, G)
+    codes, zeros, scales = draw_weights(wrng, bits, K, N, G, dtype=dtype)
     xrng = np.random.default_rng(np.random.SeedSequence(list(seed) + [M]))
-    x = draw_x(xrng, M, K, outlier_frac)
-    return pack_case(bits, codes, zeros, scales, x, G, name=name, keep_codes=keep_codes)
+    x = draw_x(xrng, M, K, outlier_frac, dtype=dtype)
+    return pack_case(bits, codes, zeros, scales, x, G, name=name, keep_codes=keep_codes, dtype=dtype)
 
 
 # Llama-style decoder layer linears: (name, K, N).
@@ -185,12 +206,13 @@ CONFIGS = {
 }
 
 
-def make_case(config: int, shape_id: int, M: int, keep_codes=True, replica: int | None = None) -> Case:
+def make_case(config: int, shape_id: int, M: int, keep_codes=True, replica: int | None = None,
+              dtype: str = "bf16") -> Case:
     """Inputs of one workload shape, seeded by (root, config, shape_id[, replica])."""
     cfg = CONFIGS[config]
     name, bits, K, N, G = cfg["shapes"][shape_id]
     seed = (SEED_ROOT, config, shape_id) + (() if replica is None else (replica,))
     c = make_inputs(bits, M, K, N, G, seed, outlier_frac=cfg["outlier"], keep_codes=keep_codes,
-                    name=f"c{config}_{name}_M{M}")
+                    name=f"c{config}_{name}_M{M}" + ("" if dtype == "bf16" else f"_{dtype}"), dtype=dtype)
     c.meta.update(config=config, shape_id=shape_id)
     return c

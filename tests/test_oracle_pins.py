@@ -103,6 +103,113 @@ def test_bf16_rounding_matches_torch_on_fp32_inputs():
 
 
 # ----------------------------------------------------------------------------
+# fp16 (IEEE binary16): the format of the scales and activations of many AWQ
+# checkpoints
+# ----------------------------------------------------------------------------
+
+
+def test_f16_decode_exhaustive_matches_numpy():
+    # every one of the 65536 bit patterns against numpy's own float16
+    b = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    got = oracle.f16_to_f32(b)
+    want = b.view(np.float16).astype(np.float32)
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan].view(np.uint32), want[~nan].view(np.uint32))  # signed zeros too
+
+
+def test_f16_rounding_hand_worked_values():
+    rows = read_golden("f16_rne.txt")
+    vals = np.array([float.fromhex(r[0]) for r in rows])
+    expect = np.array([int(r[1], 16) for r in rows], dtype=np.uint16)
+    got = oracle.f64_to_f16(vals)
+    assert [hex(v) for v in got] == [hex(v) for v in expect]
+
+
+def _rne_f16_exact(v: float) -> int:
+    """Round with exact rationals to the nearest fp16 value (ties to even);
+    encode it with numpy (exact, the value has <= 11 significant bits)."""
+    fr = Fraction(v)
+    neg = v < 0 or (v == 0 and np.signbit(v))
+    a = abs(fr)
+    if a == 0:
+        return 0x8000 if neg else 0
+    e = 0
+    while a >= 2 ** (e + 1):
+        e += 1
+    while a < 2 ** e:
+        e -= 1
+    q = Fraction(2) ** max(e - 10, -24)
+    n = a / q
+    lo = n.numerator // n.denominator
+    rem = n - lo
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and lo % 2 == 1):
+        lo += 1
+    r = lo * q
+    if r >= 2**16:
+        return 0xFC00 if neg else 0x7C00
+    h = np.array([float(r)], dtype=np.float64).astype(np.float16).view(np.uint16)[0]
+    return int(h) | (0x8000 if neg else 0)
+
+
+def test_f16_rounding_against_exact_rationals():
+    rng = np.random.default_rng(33)
+    base = rng.integers(0, 2**11, size=400) * 2 + 1                 # odd: exact ties at 12 bits
+    exps = rng.integers(-30, 16, size=400)
+    ties = np.ldexp(base.astype(np.float64) + 2**11 * 2, exps - 12)  # 12-significant-bit values
+    nudged = ties * (1 + rng.choice([-1, 1], size=400) * 2.0**-40)
+    randoms = rng.standard_normal(400) * np.exp2(rng.integers(-28, 17, size=400))
+    vals = np.concatenate([ties, nudged, randoms, -ties])
+    got = oracle.f64_to_f16(vals)
+    want = np.array([_rne_f16_exact(float(v)) for v in vals], dtype=np.uint16)
+    assert np.array_equal(got, want)
+
+
+def test_f16_rounding_matches_numpy_on_doubles():
+    rng = np.random.default_rng(34)
+    v = rng.standard_normal(50000) * np.exp2(rng.integers(-30, 18, 50000))
+    assert np.array_equal(oracle.f64_to_f16(v), v.astype(np.float16).view(np.uint16))
+
+
+def _all_finite_f16_patterns():
+    b = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    return b[np.isfinite(b.view(np.float16))]
+
+
+def test_dequant_w8_f16_scales_exhaustive_exactness():
+    # Every finite fp16 scale times every difference q - z in [-255, 255]:
+    # 8 + 11 significant bits fit fp32's 24, so the fp32 product is exact.
+    sb = _all_finite_f16_patterns()
+    d = np.arange(-255, 256)
+    K, N, G = d.size, sb.size, 1
+    q = np.maximum(d, 0).astype(np.uint8)
+    z = np.maximum(-d, 0).astype(np.uint8)
+    qweight = np.repeat(q[:, None], N, axis=1)
+    zeros = np.repeat(z[:, None], N, axis=1)
+    scales = np.repeat(sb[None, :], K, axis=0)
+    w = oracle.dequant(8, qweight, zeros, scales, K, N, G, dtype="f16")
+    exact = d[:, None].astype(np.float64) * sb.view(np.float16).astype(np.float64)[None, :]
+    assert np.array_equal(w.astype(np.float64), exact)
+
+
+def test_dequant_w4_f16_scales_exhaustive_exactness():
+    sb = _all_finite_f16_patterns()
+    qz = np.array([(q, z) for q in range(16) for z in range(16)])
+    K, N = qz.shape[0], 64
+    sbs = sb[: (sb.size // N) * N].reshape(-1, N)
+    for chunk in np.array_split(np.arange(sbs.shape[0]), 8):
+        s = sbs[chunk]
+        R = s.shape[0]
+        codes = np.tile(np.repeat(qz[:, 0:1], N, axis=1), (R, 1)).astype(np.uint8)
+        zeros = np.tile(np.repeat(qz[:, 1:2], N, axis=1), (R, 1)).astype(np.uint8)
+        scales = np.repeat(s, K, axis=0)
+        w = oracle.dequant(4, synth.pack_awq_w4(codes), synth.pack_awq_w4(zeros), scales, R * K, N, 1,
+                           dtype="f16")
+        exact = (codes.astype(np.float64) - zeros) * scales.view(np.float16).astype(np.float64)
+        assert np.array_equal(w.astype(np.float64), exact)
+
+
+# ----------------------------------------------------------------------------
 # Dequantization: (q - z) * s in fp32 is exact
 # ----------------------------------------------------------------------------
 
@@ -224,6 +331,54 @@ def test_linear_unit_scale_reduces_to_integer_gemm(bits, K):
     y = oracle.awq_linear(c)
     want = xi.astype(np.int64) @ (codes.astype(np.int64) - zval)
     assert np.array_equal(y, want.astype(np.float64))
+
+
+@pytest.mark.parametrize("bits,K", [(4, 1024), (8, 512)])
+def test_linear_f16_unit_scale_reduces_to_integer_gemm(bits, K):
+    rng = np.random.default_rng(27)
+    M, N, G = 5, 64, 128
+    codes = rng.integers(0, 1 << bits, size=(K, N), dtype=np.uint8)
+    zval = 8 if bits == 4 else 128
+    zeros = np.full((K // G, N), zval, dtype=np.uint8)
+    scales = np.full((K // G, N), 0x3C00, dtype=np.uint16)       # fp16 1.0
+    xi = rng.integers(-2, 3, size=(M, K))
+    x = xi.astype(np.float16).view(np.uint16)
+    c = synth.gen.pack_case(bits, codes, zeros, scales, x, G, dtype="f16")
+    y = oracle.awq_linear(c)
+    want = xi.astype(np.int64) @ (codes.astype(np.int64) - zval)
+    assert np.array_equal(y, want.astype(np.float64))
+
+
+@pytest.mark.parametrize("bits,M,K,N,G,seed", [(4, 2, 64, 16, 32, 41), (8, 3, 64, 8, 64, 42)])
+def test_linear_f16_tiny_against_exact_rationals(bits, M, K, N, G, seed):
+    c = synth.make_inputs(bits, M, K, N, G, seed=(seed,), dtype="f16")
+    y64 = oracle.awq_linear(c)
+    xs = [[Fraction(float(v)) for v in row] for row in c.x.view(np.float16)]
+    q = c.codes.astype(int)
+    z = c.zeros.astype(int)
+    s = c.scales.view(np.float16)
+    for m in range(M):
+        for n in range(N):
+            e = sum(xs[m][k] * (q[k, n] - z[k // G, n]) * Fraction(float(s[k // G, n])) for k in range(K))
+            assert Fraction(float(y64[m, n])) == e
+            assert int(oracle.f64_to_f16(np.array([y64[m, n]]))[0]) == _rne_f16_exact(float(e))
+
+
+def test_linear_f16_and_bf16_agree_where_the_values_coincide():
+    # x and scales with at most 8 significant bits inside fp16's normal range
+    # are the same numbers in both formats: the two decodings must give the
+    # same fp64 sums, bit for bit.
+    rng = np.random.default_rng(43)
+    M, K, N, G = 3, 256, 40, 64
+    codes = rng.integers(0, 16, size=(K, N), dtype=np.uint8)
+    zeros = rng.integers(0, 16, size=(K // G, N), dtype=np.uint8)
+    xv = np.ldexp(rng.integers(-255, 256, size=(M, K)).astype(np.float64), rng.integers(-12, 0, size=(M, K)))
+    sv = np.ldexp(rng.integers(128, 256, size=(K // G, N)).astype(np.float64), rng.integers(-14, -6, size=(K // G, N)))
+    cb = synth.gen.pack_case(4, codes, zeros, synth.f32_to_bf16_bits(sv), synth.f32_to_bf16_bits(xv), G)
+    ch = synth.gen.pack_case(4, codes, zeros, synth.f32_to_f16_bits(sv), synth.f32_to_f16_bits(xv), G, dtype="f16")
+    assert np.array_equal(synth.bf16_bits_to_f32(cb.x), ch.x.view(np.float16).astype(np.float32))
+    yb, yh = oracle.awq_linear(cb), oracle.awq_linear(ch)
+    assert np.any(yb != 0) and np.array_equal(yb, yh)
 
 
 def test_per_channel_equals_repeated_group_metadata():
