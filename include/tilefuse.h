@@ -103,14 +103,16 @@ size_t tf_packed_bytes_w8(int64_t K, int64_t N, int64_t G);
  *            symmetric quantization: every zero point is 8 (Methodology
  *            section 1 names zero points; this is their common special
  *            case), packed exactly as an explicit tensor of 8s would be.
- *   scales   bf16 [K/G][N].  2-byte aligned.
+ *   scales   bf16 [K/G][N] (fp16 for the *_f16 calls: the 16-bit scale
+ *            bits are copied into the records unchanged).  2-byte aligned.
  *   packed   output, packed_bytes >= tf_packed_bytes_w4(K, N, G); 16-byte
  *            aligned.  Every byte of the layout is written. */
 int tf_repack_w4(const uint32_t *qweight, const uint32_t *qzeros, const uint16_t *scales,
                  int64_t K, int64_t N, int64_t G, void *packed, size_t packed_bytes, void *stream);
 
 /* Re-lay out a W8 checkpoint: qweight uint8 [K][N], zeros uint8 [K/G][N]
- * (unsigned codes, zero points stored as bytes), scales bf16 [K/G][N].
+ * (unsigned codes, zero points stored as bytes), scales bf16 (or fp16, as
+ * for tf_repack_w4) [K/G][N].
  * zeros NULL: symmetric quantization, every zero point 128. */
 int tf_repack_w8(const uint8_t *qweight, const uint8_t *zeros, const uint16_t *scales,
                  int64_t K, int64_t N, int64_t G, void *packed, size_t packed_bytes, void *stream);
@@ -208,6 +210,33 @@ int tf_gemm_w8a16(const uint16_t *x, const void *packed, size_t packed_bytes, ui
                   int64_t M, int64_t K, int64_t N, int64_t G,
                   void *workspace, size_t ws_bytes, void *stream);
 
+/* The same four calls for checkpoints in IEEE fp16 (the 16-bit format of
+ * many AWQ checkpoints; the summary's Contribution 1 consumes AWQ-style
+ * checkpoints directly, its Methodology section 1 names the BF16 form):
+ * x is fp16 [M][K], the packed buffer was written by tf_repack_w4 / _w8
+ * from fp16 scales [K/G][N] (repacking copies scale bits unchanged, so the
+ * same repack serves both formats), and y is fp16 [M][N], one rounding of
+ * the fp32 sum to nearest-even, magnitudes past 65504 becoming infinity.
+ * The weights are still exact: (q - z) is an integer of at most 9 bits and
+ * the MFMAs take fp16 operands; each group's fp16 scale, widened exactly,
+ * is applied in fp32 as in the bf16 calls.  Kernels, launch plans,
+ * workspace sizes (tf_workspace_bytes with is_gemm 0 or 1), shape rules
+ * and errors are those of the bf16 call of the same name.  A buffer
+ * repacked from bf16 scales gives wrong results here, and one from fp16
+ * scales wrong results in the bf16 calls (not detectable). */
+int tf_gemv_w4a16_f16(const uint16_t *x, const void *packed, size_t packed_bytes, uint16_t *y,
+                      int64_t M, int64_t K, int64_t N, int64_t G,
+                      void *workspace, size_t ws_bytes, void *stream);
+int tf_gemv_w8a16_f16(const uint16_t *x, const void *packed, size_t packed_bytes, uint16_t *y,
+                      int64_t M, int64_t K, int64_t N, int64_t G,
+                      void *workspace, size_t ws_bytes, void *stream);
+int tf_gemm_w4a16_f16(const uint16_t *x, const void *packed, size_t packed_bytes, uint16_t *y,
+                      int64_t M, int64_t K, int64_t N, int64_t G,
+                      void *workspace, size_t ws_bytes, void *stream);
+int tf_gemm_w8a16_f16(const uint16_t *x, const void *packed, size_t packed_bytes, uint16_t *y,
+                      int64_t M, int64_t K, int64_t N, int64_t G,
+                      void *workspace, size_t ws_bytes, void *stream);
+
 /* tf_gemm_w4a16 for callers that cannot allocate device memory: code under
  * HIP-graph capture, tight serving loops, harnesses that forbid hipMalloc.
  * Same arguments, kernels, plan and results as tf_gemm_w4a16 (bit for bit),
@@ -256,7 +285,8 @@ int tf_dequant_gemv_w8_f32(const void *packed, size_t packed_bytes, float *w,
 /* state is the per-device compute-unit count, queried once).               */
 /*                                                                          */
 /*   op     TF_OP_GEMV (tf_gemv_*), TF_OP_GEMM (tf_gemm_*),                 */
-/*          TF_OP_GEMV_SILU_MUL, TF_OP_GEMM_SILU_MUL (the *_silu_mul calls)  */
+/*          TF_OP_GEMV_SILU_MUL, TF_OP_GEMM_SILU_MUL (the *_silu_mul calls), */
+/*          TF_OP_GEMV_F16, TF_OP_GEMM_F16 (the *_f16 calls)                 */
 /*   cus    compute units to plan for, 1 .. 2^20                            */
 /*   route  TF_ROUTE_AUTO (the product calls' choice), TF_ROUTE_TILED (GEMM */
 /*          calls run the tiled GEMM at any M), TF_ROUTE_GEMV (the GEMV     */
@@ -264,7 +294,8 @@ int tf_dequant_gemv_w8_f32(const void *packed, size_t packed_bytes, float *w,
 /*          GEMM at any M with 256 x 128 tiles only)                        */
 /* Other values: TF_ERR_UNSUPPORTED (the size query returns 0).             */
 /* ------------------------------------------------------------------------ */
-enum { TF_OP_GEMV = 0, TF_OP_GEMM = 1, TF_OP_GEMV_SILU_MUL = 2, TF_OP_GEMM_SILU_MUL = 3 };
+enum { TF_OP_GEMV = 0, TF_OP_GEMM = 1, TF_OP_GEMV_SILU_MUL = 2, TF_OP_GEMM_SILU_MUL = 3,
+       TF_OP_GEMV_F16 = 4, TF_OP_GEMM_F16 = 5 };
 enum { TF_ROUTE_AUTO = 0, TF_ROUTE_TILED = 1, TF_ROUTE_GEMV = 2, TF_ROUTE_TILED128 = 3 };
 
 /* The call `op` on (bits, M, K, N, G) as planned for (cus, route): the same

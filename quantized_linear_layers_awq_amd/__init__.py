@@ -15,8 +15,10 @@ from ._binding import (  # noqa: F401
     library_path,
     load_library,
     TF_OP_GEMM,
+    TF_OP_GEMM_F16,
     TF_OP_GEMM_SILU_MUL,
     TF_OP_GEMV,
+    TF_OP_GEMV_F16,
     TF_OP_GEMV_SILU_MUL,
     TF_ROUTE_AUTO,
     TF_ROUTE_GEMV,
@@ -30,13 +32,17 @@ from ._binding import (  # noqa: F401
     tf_gemm_plan,
     tf_gemv_plan,
     tf_gemm_w4a16,
+    tf_gemm_w4a16_f16,
     tf_gemm_w4a16_noalloc,
     tf_gemm_w4a16_silu_mul,
     tf_gemm_w8a16,
+    tf_gemm_w8a16_f16,
     tf_gemm_w8a16_silu_mul,
     tf_gemv_w4a16,
+    tf_gemv_w4a16_f16,
     tf_gemv_w4a16_silu_mul,
     tf_gemv_w8a16,
+    tf_gemv_w8a16_f16,
     tf_gemv_w8a16_silu_mul,
     tf_linear_planned,
     tf_packed_bytes_w4,

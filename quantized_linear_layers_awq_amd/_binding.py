@@ -60,7 +60,8 @@ def load_library():
             getattr(L, n).restype = I
         L.tf_workspace_bytes.argtypes = [I, I, I64, I64, I64, I64]
         L.tf_workspace_bytes.restype = SZ
-        for n in ("tf_gemv_w4a16", "tf_gemv_w8a16", "tf_gemm_w4a16", "tf_gemm_w8a16"):
+        for n in ("tf_gemv_w4a16", "tf_gemv_w8a16", "tf_gemm_w4a16", "tf_gemm_w8a16",
+                  "tf_gemv_w4a16_f16", "tf_gemv_w8a16_f16", "tf_gemm_w4a16_f16", "tf_gemm_w8a16_f16"):
             getattr(L, n).argtypes = [P, P, SZ, P, I64, I64, I64, I64, P, SZ, P]
             getattr(L, n).restype = I
         for n in ("tf_gemv_w4a16_silu_mul", "tf_gemv_w8a16_silu_mul", "tf_gemm_w4a16_silu_mul", "tf_gemm_w8a16_silu_mul"):
@@ -199,7 +200,9 @@ def _workspace(device: torch.device, stream_handle: int, nbytes: int):
     return ws
 
 
-TF_OP_GEMV, TF_OP_GEMM, TF_OP_GEMV_SILU_MUL, TF_OP_GEMM_SILU_MUL = 0, 1, 2, 3
+TF_OP_GEMV, TF_OP_GEMM, TF_OP_GEMV_SILU_MUL, TF_OP_GEMM_SILU_MUL, TF_OP_GEMV_F16, TF_OP_GEMM_F16 = 0, 1, 2, 3, 4, 5
+_GEMM_OPS = (TF_OP_GEMM, TF_OP_GEMM_SILU_MUL, TF_OP_GEMM_F16)
+_F16_OPS = (TF_OP_GEMV_F16, TF_OP_GEMM_F16)
 TF_ROUTE_AUTO, TF_ROUTE_TILED, TF_ROUTE_GEMV, TF_ROUTE_TILED128 = 0, 1, 2, 3
 
 
@@ -214,13 +217,13 @@ def _call(bits, op, fn, x, packed, K, N, G, y, workspace, stream, plan=None):
     M = x.shape[0]
     n_out = N // 2 if op in (TF_OP_GEMV_SILU_MUL, TF_OP_GEMM_SILU_MUL) else N
     if y is None:
-        y = torch.empty((M, n_out), dtype=torch.bfloat16, device=x.device)
+        y = torch.empty((M, n_out), dtype=torch.float16 if op in _F16_OPS else torch.bfloat16, device=x.device)
     _need(y, "y", 2)
     if y.numel() < M * n_out:
         raise ValueError(f"{fn}: y holds fewer than {M * n_out} elements")
     sh = _stream(x, stream)
     if plan is None:
-        need = int(L.tf_workspace_bytes(bits, int(op in (TF_OP_GEMM, TF_OP_GEMM_SILU_MUL)), M, K, N, G))
+        need = int(L.tf_workspace_bytes(bits, int(op in _GEMM_OPS), M, K, N, G))
     else:
         need = int(L.tf_workspace_bytes_planned(bits, op, M, K, N, G, int(plan[0]), int(plan[1])))
     if workspace is None:
@@ -275,6 +278,26 @@ def tf_gemm_w4a16_noalloc(x, packed, K, N, G, y=None, stream=None):
 
 def tf_gemm_w8a16(x, packed, K, N, G, y=None, workspace=None, stream=None):
     return _linear(8, True, "tf_gemm_w8a16", x, packed, K, N, G, y, workspace, stream)
+
+
+def tf_gemv_w4a16_f16(x, packed, K, N, G, y=None, workspace=None, stream=None):
+    """tf_gemv_w4a16 for fp16 checkpoints: x [M][K] fp16, packed from fp16
+    scales, y [M][N] fp16."""
+    return _call(4, TF_OP_GEMV_F16, "tf_gemv_w4a16_f16", x, packed, K, N, G, y, workspace, stream)
+
+
+def tf_gemv_w8a16_f16(x, packed, K, N, G, y=None, workspace=None, stream=None):
+    return _call(8, TF_OP_GEMV_F16, "tf_gemv_w8a16_f16", x, packed, K, N, G, y, workspace, stream)
+
+
+def tf_gemm_w4a16_f16(x, packed, K, N, G, y=None, workspace=None, stream=None):
+    """tf_gemm_w4a16 for fp16 checkpoints: x [M][K] fp16, packed from fp16
+    scales, y [M][N] fp16."""
+    return _call(4, TF_OP_GEMM_F16, "tf_gemm_w4a16_f16", x, packed, K, N, G, y, workspace, stream)
+
+
+def tf_gemm_w8a16_f16(x, packed, K, N, G, y=None, workspace=None, stream=None):
+    return _call(8, TF_OP_GEMM_F16, "tf_gemm_w8a16_f16", x, packed, K, N, G, y, workspace, stream)
 
 
 def _silu_mul(bits, fn, x, packed, K, N, G, y, workspace, stream, is_gemm=False):
@@ -337,7 +360,9 @@ def tf_dequant_gemv_w8_f32(packed, K, N, G, w=None, stream=None):
 _OP_FN = {(4, TF_OP_GEMV): "tf_gemv_w4a16", (8, TF_OP_GEMV): "tf_gemv_w8a16", (4, TF_OP_GEMM): "tf_gemm_w4a16",
           (8, TF_OP_GEMM): "tf_gemm_w8a16", (4, TF_OP_GEMV_SILU_MUL): "tf_gemv_w4a16_silu_mul",
           (8, TF_OP_GEMV_SILU_MUL): "tf_gemv_w8a16_silu_mul", (4, TF_OP_GEMM_SILU_MUL): "tf_gemm_w4a16_silu_mul",
-          (8, TF_OP_GEMM_SILU_MUL): "tf_gemm_w8a16_silu_mul"}
+          (8, TF_OP_GEMM_SILU_MUL): "tf_gemm_w8a16_silu_mul", (4, TF_OP_GEMV_F16): "tf_gemv_w4a16_f16",
+          (8, TF_OP_GEMV_F16): "tf_gemv_w8a16_f16", (4, TF_OP_GEMM_F16): "tf_gemm_w4a16_f16",
+          (8, TF_OP_GEMM_F16): "tf_gemm_w8a16_f16"}
 
 
 def tf_linear_planned(bits, op, x, packed, K, N, G, cus, route=TF_ROUTE_AUTO, y=None, workspace=None, stream=None):

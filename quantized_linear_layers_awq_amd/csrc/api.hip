@@ -71,10 +71,11 @@ int repack(int bits, const void *qweight, const void *qzeros, const uint16_t *sc
     return TF_OK;
 }
 
-// The four kinds of linear call (the TF_OP_* values of the header).
-constexpr int kOpGemv = 0, kOpGemm = 1, kOpGemvSiluMul = 2, kOpGemmSiluMul = 3;
-bool op_is_gemm(int op) { return op == kOpGemm || op == kOpGemmSiluMul; }
+// The six kinds of linear call (the TF_OP_* values of the header).
+constexpr int kOpGemv = 0, kOpGemm = 1, kOpGemvSiluMul = 2, kOpGemmSiluMul = 3, kOpGemvF16 = 4, kOpGemmF16 = 5;
+bool op_is_gemm(int op) { return op == kOpGemm || op == kOpGemmSiluMul || op == kOpGemmF16; }
 bool op_is_silu(int op) { return op == kOpGemvSiluMul || op == kOpGemmSiluMul; }
+bool op_is_f16(int op) { return op == kOpGemvF16 || op == kOpGemmF16; }
 int64_t op_max_m(int op) { return op_is_gemm(op) ? (int64_t(1) << 30) : 16; }
 
 // fp32 partial sums, S x M x N floats, when a call splits K over workgroups:
@@ -139,13 +140,13 @@ int launch(int bits, int op, const uint16_t *x, const void *packed, uint16_t *y,
     const hipStream_t st = static_cast<hipStream_t>(stream);
     const bool tiled = op_is_gemm(op) && !tf::gemm_uses_gemv(M, route);
     hipError_t e;
+    const int act = op_is_silu(op) ? tf::kActSiluMul : op_is_f16(op) ? tf::kActF16 : tf::kActNone;
     if (tiled)
-        e = tf::launch_gemm(bits, x, packed, y, M, lay, ws, st, cus, op_is_silu(op) ? tf::kActSiluMul : tf::kActNone,
-                            route);
+        e = tf::launch_gemm(bits, x, packed, y, M, lay, ws, st, cus, act, route);
     else if (op_is_silu(op))
         e = tf::launch_gemv_silu_mul(bits, x, packed, y, M, lay, ws, st, cus);
     else
-        e = tf::launch_gemv(bits, x, packed, y, M, lay, ws, st, cus);
+        e = tf::launch_gemv(bits, x, packed, y, M, lay, ws, st, cus, op_is_f16(op));
     return e == hipSuccess ? TF_OK : TF_ERR_HIP;
 }
 
@@ -204,7 +205,7 @@ void *device_scratch()
 
 bool plan_inputs_ok(int bits, int op, int cus, int route)
 {
-    return (bits == 4 || bits == 8) && op >= kOpGemv && op <= kOpGemmSiluMul && cus >= 1 && cus <= (1 << 20) &&
+    return (bits == 4 || bits == 8) && op >= kOpGemv && op <= kOpGemmF16 && cus >= 1 && cus <= (1 << 20) &&
            (route == tf::kRouteAuto || route == tf::kRouteTiled || route == tf::kRouteGemv ||
             route == tf::kRouteTiled128);
 }
@@ -279,6 +280,10 @@ TF_LINEAR(tf_gemv_w4a16_silu_mul, 4, kOpGemvSiluMul)
 TF_LINEAR(tf_gemv_w8a16_silu_mul, 8, kOpGemvSiluMul)
 TF_LINEAR(tf_gemm_w4a16_silu_mul, 4, kOpGemmSiluMul)
 TF_LINEAR(tf_gemm_w8a16_silu_mul, 8, kOpGemmSiluMul)
+TF_LINEAR(tf_gemv_w4a16_f16, 4, kOpGemvF16)
+TF_LINEAR(tf_gemv_w8a16_f16, 8, kOpGemvF16)
+TF_LINEAR(tf_gemm_w4a16_f16, 4, kOpGemmF16)
+TF_LINEAR(tf_gemm_w8a16_f16, 8, kOpGemmF16)
 #undef TF_LINEAR
 
 int tf_gemm_w4a16_noalloc(const uint16_t *x, const void *packed, size_t nbytes, uint16_t *y, int64_t M, int64_t K,

@@ -93,6 +93,7 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_kernel(const uint16_t *__re
                                                             int split_tiles, float *__restrict__ ws)
 {
     constexpr int kGBN = tile_cols(WN), kGBlocks = tile_blocks(WN);
+    constexpr bool F16 = ACT == kActF16; // fp16 x, scales and y (else bf16)
     constexpr int kBStageBytes = bstage_bytes(WN), kCodeBufBytes = codebuf_bytes(WN);
     constexpr int kMetaBufBytes = metabuf_bytes(WN);
     constexpr int kBOct = kGBN * 16; // bytes per k-octet row of a dequantized B stage
@@ -316,9 +317,10 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_kernel(const uint16_t *__re
         const float nz = -(float)zero_of(in.zb[kk]) * live;
         u32x4 v;
         if constexpr (kW8)
-            v = kk == 0 ? unpack_w8(in.cw[0], in.cw[1], live, nz) : unpack_w8(in.cw8[0], in.cw8[1], live, nz);
+            v = kk == 0 ? unpack_w8<F16>(in.cw[0], in.cw[1], live, nz)
+                        : unpack_w8<F16>(in.cw8[0], in.cw8[1], live, nz);
         else
-            v = unpack_w4(in.cw[kk], live, nz);
+            v = unpack_w4<F16>(in.cw[kk], live, nz);
         *reinterpret_cast<u32x4 *>(fill_lane + (sd & 1) * kBStageBytes + kk * 4 * kBOct) = v;
     };
 
@@ -328,7 +330,7 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_kernel(const uint16_t *__re
     auto scales_of = [&](int64_t g, int t, float (&sc)[2]) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            const float v = record_scale<BITS>(meta_rec(4 * wn + 2 * j + (l32 >> 4), t, g), r);
+            const float v = record_scale<BITS, F16>(meta_rec(4 * wn + 2 * j + (l32 >> 4), t, g), r);
             sc[j] = g < L.ngroups ? v : 0.f;
         }
     };
@@ -341,7 +343,7 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_kernel(const uint16_t *__re
     auto scales_decode = [&](int64_t g, const uint32_t (&sb)[2], float (&sc)[2]) {
 #pragma unroll
         for (int j = 0; j < 2; ++j)
-            sc[j] = g < L.ngroups ? __uint_as_float(sb[j] << 16) : 0.f;
+            sc[j] = g < L.ngroups ? half_bits_to_f32<F16>(sb[j]) : 0.f;
     };
 
     // ---- accumulator chains (even / odd groups) and their current scales ----
@@ -532,7 +534,7 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_kernel(const uint16_t *__re
                     for (int i = 0; i < MI; ++i)
 #pragma unroll
                         for (int j = 0; j < 2; ++j)
-                            acc[0][i][j] = mfma32x32x16(af[cur][i], bf[cur][j], acc[0][i][j]);
+                            acc[0][i][j] = mfma32x32x16<F16>(af[cur][i], bf[cur][j], acc[0][i][j]);
                     if (sig == 7 && (t + 1) % (int)L.tiles_per_group == 0 && t + 1 < ktiles) {
                         start_fold(ic<0>{}, (int64_t)(t + 1) / L.tiles_per_group, t + 1, true);
                         fold_chunk(ic<0>{}, ic<0>{}, ic<1>{});
@@ -549,7 +551,7 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_kernel(const uint16_t *__re
                     for (int i = 0; i < MI; ++i)
 #pragma unroll
                         for (int j = 0; j < 2; ++j)
-                            acc[C][i][j] = mfma32x32x16(af[cur][i], bf[cur][j], acc[C][i][j]);
+                            acc[C][i][j] = mfma32x32x16<F16>(af[cur][i], bf[cur][j], acc[C][i][j]);
                     fold_chunk(ic<F>{}, ic<pos>{}, ic<kSpg>{});
                 }
             });
@@ -599,12 +601,12 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_kernel(const uint16_t *__re
                 const int64_t row = m0 + 32 * MI * wm + 32 * i + 8 * (e >> 2) + 4 * h32 + (e & 3);
                 const float v = kMode == kGWhole ? acc[0][i][j][e] * s_last[0][j]
                                                  : fmaf(acc[0][i][j][e], s_last[0][j], acc[1][i][j][e] * s_last[1][j]);
-                if constexpr (ACT == kActNone) {
+                if constexpr (ACT != kActSiluMul) {
                     if (row < M) {
                         if (splits > 1)
                             __builtin_nontemporal_store(v, ws + ((int64_t)split * M + row) * L.N + col);
                         else
-                            y[row * L.N + col] = f32_to_bf16_bits(v);
+                            y[row * L.N + col] = f32_to_half_bits<F16>(v);
                     }
                 } else {
                     // [gate | up] packed by tf_repack_*_gate_up (N % 16 == 0):
@@ -641,11 +643,12 @@ static void launch_mode(int64_t wgs, int m_tiles, int64_t col0, const GemmPlan &
         x, pk, y, lay, M, m_tiles, col0, (int)plan.splits, (int)plan.split_tiles, ws);
 }
 
-// y = bf16(sum over s of ws[s]) for the M x N outputs, in split order.  The
+// y = bf16 (fp16 when F16) of the sum over s of ws[s] for the M x N outputs,
+// in split order.  The
 // split count is a template parameter so that a thread issues all S loads
 // at once (one round trip) and then adds them in order.  The partials were
 // stored non-temporally on other XCDs and are read the same way.
-template <int S>
+template <int S, bool F16>
 __global__ __launch_bounds__(256) void splitk_sum_kernel(const float *__restrict__ ws, int64_t mn,
                                                          uint16_t *__restrict__ y)
 {
@@ -662,8 +665,8 @@ __global__ __launch_bounds__(256) void splitk_sum_kernel(const float *__restrict
         for (int s = 1; s < S; ++s)
             v = v + p[s];
         u32x2 o;
-        o[0] = pack_bf16x2(v[0], v[1]);
-        o[1] = pack_bf16x2(v[2], v[3]);
+        o[0] = pack_half_x2<F16>(v[0], v[1]);
+        o[1] = pack_half_x2<F16>(v[2], v[3]);
         *reinterpret_cast<u32x2 *>(y + i) = o;
     } else {
         for (int64_t e = i; e < mn; ++e) {
@@ -671,35 +674,38 @@ __global__ __launch_bounds__(256) void splitk_sum_kernel(const float *__restrict
 #pragma unroll
             for (int s = 1; s < S; ++s)
                 v += ws[s * mn + e];
-            y[e] = f32_to_bf16_bits(v);
+            y[e] = f32_to_half_bits<F16>(v);
         }
     }
 }
 
-template <int S> static void launch_sum(const float *ws, int64_t mn, uint16_t *y, hipStream_t stream)
+template <int S> static void launch_sum(const float *ws, int64_t mn, uint16_t *y, hipStream_t stream, bool f16)
 {
     const int64_t grid = (mn + 4 * 256 - 1) / (4 * 256);
-    splitk_sum_kernel<S><<<dim3((unsigned)grid), 256, 0, stream>>>(ws, mn, y);
+    if (f16)
+        splitk_sum_kernel<S, true><<<dim3((unsigned)grid), 256, 0, stream>>>(ws, mn, y);
+    else
+        splitk_sum_kernel<S, false><<<dim3((unsigned)grid), 256, 0, stream>>>(ws, mn, y);
 }
 
-void launch_splitk_sum(const float *ws, int splits, int64_t mn, uint16_t *y, hipStream_t stream)
+void launch_splitk_sum(const float *ws, int splits, int64_t mn, uint16_t *y, hipStream_t stream, bool f16)
 {
     switch (splits) {
-    case 2: launch_sum<2>(ws, mn, y, stream); break;
-    case 3: launch_sum<3>(ws, mn, y, stream); break;
-    case 4: launch_sum<4>(ws, mn, y, stream); break;
-    case 5: launch_sum<5>(ws, mn, y, stream); break;
-    case 6: launch_sum<6>(ws, mn, y, stream); break;
-    case 7: launch_sum<7>(ws, mn, y, stream); break;
-    case 8: launch_sum<8>(ws, mn, y, stream); break;
-    case 9: launch_sum<9>(ws, mn, y, stream); break;
-    case 10: launch_sum<10>(ws, mn, y, stream); break;
-    case 11: launch_sum<11>(ws, mn, y, stream); break;
-    case 12: launch_sum<12>(ws, mn, y, stream); break;
-    case 13: launch_sum<13>(ws, mn, y, stream); break;
-    case 14: launch_sum<14>(ws, mn, y, stream); break;
-    case 15: launch_sum<15>(ws, mn, y, stream); break;
-    default: launch_sum<16>(ws, mn, y, stream); break;
+    case 2: launch_sum<2>(ws, mn, y, stream, f16); break;
+    case 3: launch_sum<3>(ws, mn, y, stream, f16); break;
+    case 4: launch_sum<4>(ws, mn, y, stream, f16); break;
+    case 5: launch_sum<5>(ws, mn, y, stream, f16); break;
+    case 6: launch_sum<6>(ws, mn, y, stream, f16); break;
+    case 7: launch_sum<7>(ws, mn, y, stream, f16); break;
+    case 8: launch_sum<8>(ws, mn, y, stream, f16); break;
+    case 9: launch_sum<9>(ws, mn, y, stream, f16); break;
+    case 10: launch_sum<10>(ws, mn, y, stream, f16); break;
+    case 11: launch_sum<11>(ws, mn, y, stream, f16); break;
+    case 12: launch_sum<12>(ws, mn, y, stream, f16); break;
+    case 13: launch_sum<13>(ws, mn, y, stream, f16); break;
+    case 14: launch_sum<14>(ws, mn, y, stream, f16); break;
+    case 15: launch_sum<15>(ws, mn, y, stream, f16); break;
+    default: launch_sum<16>(ws, mn, y, stream, f16); break;
     }
 }
 
@@ -808,7 +814,7 @@ int64_t gemm_workspace_bytes(int bits, int64_t M, int64_t N, int64_t K, int64_t 
 hipError_t launch_gemm(int bits, const uint16_t *x, const void *packed, uint16_t *y, int64_t M, const Layout &lay,
                        void *workspace, hipStream_t stream, int cus, int act, int route)
 {
-    if (act != kActNone && lay.N % kBlockCols)
+    if (act == kActSiluMul && lay.N % kBlockCols)
         return hipErrorInvalidValue;
     const GemmPlan plan = plan_gemm(bits, M, lay.N, lay.K, lay.G, cus, route != kRouteTiled128);
     float *ws = plan.splits > 1 ? static_cast<float *>(workspace) : nullptr;
@@ -819,7 +825,7 @@ hipError_t launch_gemm(int bits, const uint16_t *x, const void *packed, uint16_t
             if (act == kActSiluMul)
                 launch_splitk_sum_silu(ws, (int)plan.splits, M, lay.N, y, stream);
             else
-                launch_splitk_sum(ws, (int)plan.splits, M * lay.N, y, stream);
+                launch_splitk_sum(ws, (int)plan.splits, M * lay.N, y, stream, act == kActF16);
         }
         return hipGetLastError();
     }
@@ -843,6 +849,8 @@ hipError_t launch_gemm(int bits, const uint16_t *x, const void *packed, uint16_t
     auto go = [&](auto bits_c, auto wn_c, auto bm_c, int64_t n_cols, int64_t col0) {
         if (act == kActSiluMul)
             go_act(bits_c, wn_c, bm_c, ic<kActSiluMul>{}, n_cols, col0);
+        else if (act == kActF16)
+            go_act(bits_c, wn_c, bm_c, ic<kActF16>{}, n_cols, col0);
         else
             go_act(bits_c, wn_c, bm_c, ic<kActNone>{}, n_cols, col0);
     };
@@ -864,7 +872,7 @@ hipError_t launch_gemm(int bits, const uint16_t *x, const void *packed, uint16_t
         if (act == kActSiluMul)
             launch_splitk_sum_silu(ws, (int)plan.splits, M, lay.N, y, stream);
         else
-            launch_splitk_sum(ws, (int)plan.splits, M * lay.N, y, stream);
+            launch_splitk_sum(ws, (int)plan.splits, M * lay.N, y, stream, act == kActF16);
     }
     return hipGetLastError();
 }

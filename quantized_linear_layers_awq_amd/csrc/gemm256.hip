@@ -74,6 +74,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm256_kernel(const uint16_t *__
 {
     static_assert(kMode == kGOneTile || kMode == kGWhole, "groups of whole k-tiles");
     constexpr int RB = record_bytes(4);
+    constexpr bool F16 = ACT == kActF16; // fp16 x, scales and y (else bf16)
     constexpr bool one_tile = kMode == kGOneTile;
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
@@ -227,7 +228,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm256_kernel(const uint16_t *__
         for (int bb = 0; bb < 2; ++bb) {
             const float live = (step < steps && (in.sb[bb] & 0x7FFFu) != 0) ? 1.f : 0.f;
             const float nz = -(float)((in.zb[bb] >> (4 * (r & 1))) & 0xFu) * live;
-            const u32x4 v = unpack_w4(cw[bb][u], live, nz);
+            const u32x4 v = unpack_w4<F16>(cw[bb][u], live, nz);
             *reinterpret_cast<u32x4 *>(fill_lane + hd * kBStageB + uu * 4 * kBOct + bb * 256) = v;
         }
     };
@@ -291,7 +292,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm256_kernel(const uint16_t *__
         unpack_store(ic<0>{}, 0, in, 1);
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            const float sv = bf16_bits_to_f32(fold_scale_bits(0, j));
+            const float sv = half_bits_to_f32<F16>(fold_scale_bits(0, j));
             s_last[j] = sv != 0.f ? sv : 1.f;
         }
     }
@@ -305,7 +306,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm256_kernel(const uint16_t *__
         const bool starts = t > 0 && t < ktiles && (one_tile || group_of(t) != group_of(t - 1));
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            const float sv = bf16_bits_to_f32(fold_scale_bits(t < ktiles ? t : ktiles - 1, j));
+            const float sv = half_bits_to_f32<F16>(fold_scale_bits(t < ktiles ? t : ktiles - 1, j));
             const float se = starts && sv != 0.f ? sv : s_last[j];
             ratio[j] = starts ? s_last[j] * __builtin_amdgcn_rcpf(se) : 1.f;
             s_last[j] = se;
@@ -373,7 +374,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm256_kernel(const uint16_t *__
             for (int i = 0; i < 4; ++i)
 #pragma unroll
                 for (int j = 0; j < 2; ++j)
-                    acc[i][j] = mfma32x32x16(af[cur][i], bf[cur][j], acc[i][j]);
+                    acc[i][j] = mfma32x32x16<F16>(af[cur][i], bf[cur][j], acc[i][j]);
             if constexpr (sl == 3 && h == 1) {
                 fold_ratios(t + 1); // the boundary before k-tile t + 1
                 fold_rows(0);
@@ -436,7 +437,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm256_kernel(const uint16_t *__
                 if (splits > 1)
                     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), out_rsrc, (int)(lane_off + roff), 0, 0);
                 else
-                    __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_bits(v), out_rsrc, (int)(lane_off + roff), 0, 0);
+                    __builtin_amdgcn_raw_buffer_store_b16(f32_to_half_bits<F16>(v), out_rsrc, (int)(lane_off + roff), 0, 0);
             }
     }
 }
@@ -469,6 +470,11 @@ hipError_t launch_gemm256(const uint16_t *x, const void *packed, uint16_t *y, in
             launch_256<kGOneTile, kActSiluMul>(wgs, mt, plan, stream, x, pk, y, lay, M, ws);
         else
             launch_256<kGWhole, kActSiluMul>(wgs, mt, plan, stream, x, pk, y, lay, M, ws);
+    } else if (act == kActF16) {
+        if (one)
+            launch_256<kGOneTile, kActF16>(wgs, mt, plan, stream, x, pk, y, lay, M, ws);
+        else
+            launch_256<kGWhole, kActF16>(wgs, mt, plan, stream, x, pk, y, lay, M, ws);
     } else {
         if (one)
             launch_256<kGOneTile, kActNone>(wgs, mt, plan, stream, x, pk, y, lay, M, ws);

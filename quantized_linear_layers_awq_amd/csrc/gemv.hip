@@ -46,12 +46,13 @@ template <int BITS> struct TileCodes {
     u32x4 w[BITS == 4 ? 1 : 2];
 };
 
-template <int BITS> __device__ __forceinline__ u32x4 code_operand(const TileCodes<BITS> &c, int u, uint32_t magic)
+template <int BITS, bool F16>
+__device__ __forceinline__ u32x4 code_operand(const TileCodes<BITS> &c, int u, uint32_t magic)
 {
     if constexpr (BITS == 4)
-        return w4_operand(c.w[0][u], magic);
+        return w4_operand<F16>(c.w[0][u], magic);
     else
-        return w8_operand(c.w[u >> 1][2 * (u & 1)], c.w[u >> 1][2 * (u & 1) + 1]);
+        return w8_operand<F16>(c.w[u >> 1][2 * (u & 1)], c.w[u >> 1][2 * (u & 1) + 1]);
 }
 
 template <int BITS>
@@ -106,6 +107,7 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const uint16_t *__restrict__
 {
     // D: k-tiles of codes in flight per wave
     constexpr uint32_t TB = tile_bytes(BITS), RB = record_bytes(BITS);
+    constexpr bool F16 = ACT == kActF16; // fp16 x, scales and y (else bf16)
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     uint16_t *sx = reinterpret_cast<uint16_t *>(smem + BPW * ch.meta_cap);
     float *red = reinterpret_cast<float *>(smem); // reused after the last chunk
@@ -126,7 +128,7 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const uint16_t *__restrict__
     // MFMA rows >= M are never stored, so their lanes read row 0 instead of
     // being masked off.
     const int xr = r < M ? r : 0;
-    const uint32_t magic = magic_in_vgpr();
+    const uint32_t magic = magic_in_vgpr<F16>();
     const int ktiles = (int)lay.ktiles;
     const f32x4 zf = {0.f, 0.f, 0.f, 0.f};
 
@@ -231,7 +233,7 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const uint16_t *__restrict__
                 u32x4 ops[4];
 #pragma unroll
                 for (int u = 0; u < 4; ++u)
-                    ops[u] = code_operand<BITS>(ring[j], u, magic);
+                    ops[u] = code_operand<BITS, F16>(ring[j], u, magic);
                 load_codes<BITS>(ring[j], tiles + (uint32_t)(ti + D < n ? t + D : b - 1) * TB);
                 if (ti < n) {
                     u32x4 xa[4];
@@ -240,28 +242,28 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const uint16_t *__restrict__
                         xa[u] = *reinterpret_cast<const u32x4 *>(xl + t * kTileRows + kStepRows * u);
                     if constexpr (kMode == kOneTile) {
                         const uint8_t *rg = smeta + (t - (int)g0) * RB;
-                        const u32x4 zop = zero_operand<BITS>(record_zero<BITS>(rg, r));
-                        f32x4 ga4 = mfma16x16x32(xa[0], ops[0], zf);
-                        f32x4 za4 = mfma16x16x32(xa[0], zop, zf);
+                        const u32x4 zop = zero_operand<BITS, F16>(record_zero<BITS>(rg, r));
+                        f32x4 ga4 = mfma16x16x32<F16>(xa[0], ops[0], zf);
+                        f32x4 za4 = mfma16x16x32<F16>(xa[0], zop, zf);
 #pragma unroll
                         for (int u = 1; u < 4; ++u) {
-                            ga4 = mfma16x16x32(xa[u], ops[u], ga4);
-                            za4 = mfma16x16x32(xa[u], zop, za4);
+                            ga4 = mfma16x16x32<F16>(xa[u], ops[u], ga4);
+                            za4 = mfma16x16x32<F16>(xa[u], zop, za4);
                         }
-                        const float sc = record_scale<BITS>(rg, r);
+                        const float sc = record_scale<BITS, F16>(rg, r);
 #pragma unroll
                         for (int e = 0; e < 4; ++e)
                             yacc[e] = fmaf(sc, ga4[e] - za4[e], yacc[e]);
                     } else if constexpr (kMode == kMultiTile) {
-                        const u32x4 zop = zero_operand<BITS>(record_zero<BITS>(rec, r));
+                        const u32x4 zop = zero_operand<BITS, F16>(record_zero<BITS>(rec, r));
 #pragma unroll
                         for (int u = 0; u < 4; ++u) {
-                            gacc = mfma16x16x32(xa[u], ops[u], gacc);
-                            zacc = mfma16x16x32(xa[u], zop, zacc);
+                            gacc = mfma16x16x32<F16>(xa[u], ops[u], gacc);
+                            zacc = mfma16x16x32<F16>(xa[u], zop, zacc);
                         }
                         --tg_left;
                         if (tg_left == 0 || ti + 1 == n)
-                            fold(yacc, gacc, zacc, record_scale<BITS>(rec, r));
+                            fold(yacc, gacc, zacc, record_scale<BITS, F16>(rec, r));
                         if (tg_left == 0) {
                             tg_left = tpg;
                             rec += RB;
@@ -272,13 +274,13 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const uint16_t *__restrict__
                             const int64_t st = 4 * (int64_t)t + u;
                             if (st < lay.steps) {
                                 const uint8_t *rg = smeta + ((st >> sh) - g0) * RB;
-                                const f32x4 ga4 = mfma16x16x32(xa[u], ops[u], zf);
+                                const f32x4 ga4 = mfma16x16x32<F16>(xa[u], ops[u], zf);
                                 const f32x4 za4 =
-                                    mfma16x16x32(xa[u], zero_operand<BITS>(record_zero<BITS>(rg, r)), zf);
+                                    mfma16x16x32<F16>(xa[u], zero_operand<BITS, F16>(record_zero<BITS>(rg, r)), zf);
                                 gacc += ga4;
                                 zacc += za4;
                                 if (((st + 1) & ((1 << sh) - 1)) == 0)
-                                    fold(yacc, gacc, zacc, record_scale<BITS>(rg, r));
+                                    fold(yacc, gacc, zacc, record_scale<BITS, F16>(rg, r));
                             }
                         }
                     }
@@ -294,7 +296,7 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const uint16_t *__restrict__
         red[(wave * 16 + 4 * o + e) * kBlockCols + r] = yacc[e];
     __syncthreads();
     // each block sums its own waves, in wave order
-    if constexpr (ACT == kActNone) {
+    if constexpr (ACT != kActSiluMul) {
 #pragma unroll
         for (int eb = 0; eb < BPW; ++eb) {
             for (int e = tid; e < M * kBlockCols; e += blockDim.x) {
@@ -304,7 +306,7 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const uint16_t *__restrict__
                     v += red[(w * 16 + row) * kBlockCols + col];
                 const int64_t nn = (blk0 + eb) * kBlockCols + col;
                 if (nn < lay.N)
-                    y[(int64_t)row * lay.N + nn] = f32_to_bf16_bits(v);
+                    y[(int64_t)row * lay.N + nn] = f32_to_half_bits<F16>(v);
             }
         }
     } else {
@@ -368,6 +370,7 @@ __global__ __launch_bounds__(64 * kMidWaves) void gemv_mid_kernel(const uint16_t
                                                                  MidChunks ch, float *__restrict__ ws)
 {
     constexpr uint32_t TB = tile_bytes(BITS), RB = record_bytes(BITS);
+    constexpr bool F16 = ACT == kActF16; // fp16 x, scales and y (else bf16)
     constexpr int kThreads = 64 * kMidWaves;
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int meta_buf_bytes = kMidWaves * ch.meta_cap;
@@ -391,7 +394,7 @@ __global__ __launch_bounds__(64 * kMidWaves) void gemv_mid_kernel(const uint16_t
 #pragma unroll
     for (int c = 0; c < MT; ++c)
         xoff[c] = c == 0 ? 0 : ((16 * c + r < M ? 16 * c + r : 0) - xr) * ch.xpitch;
-    const uint32_t magic = magic_in_vgpr();
+    const uint32_t magic = magic_in_vgpr<F16>();
     const f32x4 zf = {0.f, 0.f, 0.f, 0.f};
 
     // ---- staging of chunk cc: activations x[0:M][chunk] (zero past K) and
@@ -510,46 +513,46 @@ __global__ __launch_bounds__(64 * kMidWaves) void gemv_mid_kernel(const uint16_t
                         u32x4 ops[4];
 #pragma unroll
                         for (int u = 0; u < 4; ++u)
-                            ops[u] = code_operand<BITS>(ring[j], u, magic);
+                            ops[u] = code_operand<BITS, F16>(ring[j], u, magic);
                         auto xfrag = [&](int c, int u) {
                             return *reinterpret_cast<const u32x4 *>(xl + xoff[c] + t * kTileRows + kStepRows * u);
                         };
                         if constexpr (kMode == kOneTile) {
                             const uint8_t *rg = smeta + (t - (int)g0) * RB;
-                            const u32x4 zop = zero_operand<BITS>(record_zero<BITS>(rg, r));
+                            const u32x4 zop = zero_operand<BITS, F16>(record_zero<BITS>(rg, r));
 #pragma unroll
                             for (int c = 0; c < MT; ++c) {
                                 u32x4 xa[4];
 #pragma unroll
                                 for (int u = 0; u < 4; ++u)
                                     xa[u] = xfrag(c, u);
-                                f32x4 ga4 = mfma16x16x32(xa[0], ops[0], zf);
-                                f32x4 za4 = mfma16x16x32(xa[0], zop, zf);
+                                f32x4 ga4 = mfma16x16x32<F16>(xa[0], ops[0], zf);
+                                f32x4 za4 = mfma16x16x32<F16>(xa[0], zop, zf);
 #pragma unroll
                                 for (int u = 1; u < 4; ++u) {
-                                    ga4 = mfma16x16x32(xa[u], ops[u], ga4);
-                                    za4 = mfma16x16x32(xa[u], zop, za4);
+                                    ga4 = mfma16x16x32<F16>(xa[u], ops[u], ga4);
+                                    za4 = mfma16x16x32<F16>(xa[u], zop, za4);
                                 }
-                                const float sc = record_scale<BITS>(rg, r);
+                                const float sc = record_scale<BITS, F16>(rg, r);
 #pragma unroll
                                 for (int e = 0; e < 4; ++e)
                                     yacc[c][e] = fmaf(sc, ga4[e] - za4[e], yacc[c][e]);
                             }
                         } else if constexpr (kMode == kMultiTile) {
                             const uint8_t *rec = smeta + (gcur - g0) * RB;
-                            const u32x4 zop = zero_operand<BITS>(record_zero<BITS>(rec, r));
+                            const u32x4 zop = zero_operand<BITS, F16>(record_zero<BITS>(rec, r));
 #pragma unroll
                             for (int c = 0; c < MT; ++c) {
 #pragma unroll
                                 for (int u = 0; u < 4; ++u) {
                                     const u32x4 xa = xfrag(c, u);
-                                    gacc[c] = mfma16x16x32(xa, ops[u], gacc[c]);
-                                    zacc[c] = mfma16x16x32(xa, zop, zacc[c]);
+                                    gacc[c] = mfma16x16x32<F16>(xa, ops[u], gacc[c]);
+                                    zacc[c] = mfma16x16x32<F16>(xa, zop, zacc[c]);
                                 }
                             }
                             --tg_left;
                             if (tg_left == 0 || t + 1 == kt_end) {
-                                const float sc = record_scale<BITS>(rec, r);
+                                const float sc = record_scale<BITS, F16>(rec, r);
 #pragma unroll
                                 for (int c = 0; c < MT; ++c)
                                     fold(yacc[c], gacc[c], zacc[c], sc);
@@ -564,16 +567,16 @@ __global__ __launch_bounds__(64 * kMidWaves) void gemv_mid_kernel(const uint16_t
                                 const int64_t st = 4 * (int64_t)t + u;
                                 if (st < lay.steps) {
                                     const uint8_t *rg = smeta + ((st >> sh) - g0) * RB;
-                                    const u32x4 zop = zero_operand<BITS>(record_zero<BITS>(rg, r));
+                                    const u32x4 zop = zero_operand<BITS, F16>(record_zero<BITS>(rg, r));
                                     const bool last = ((st + 1) & ((1 << sh) - 1)) == 0;
 #pragma unroll
                                     for (int c = 0; c < MT; ++c) {
                                         const u32x4 xa = xfrag(c, u);
-                                        gacc[c] += mfma16x16x32(xa, ops[u], zf);
-                                        zacc[c] += mfma16x16x32(xa, zop, zf);
+                                        gacc[c] += mfma16x16x32<F16>(xa, ops[u], zf);
+                                        zacc[c] += mfma16x16x32<F16>(xa, zop, zf);
                                     }
                                     if (last) {
-                                        const float sc = record_scale<BITS>(rg, r);
+                                        const float sc = record_scale<BITS, F16>(rg, r);
 #pragma unroll
                                         for (int c = 0; c < MT; ++c)
                                             fold(yacc[c], gacc[c], zacc[c], sc);
@@ -603,7 +606,7 @@ __global__ __launch_bounds__(64 * kMidWaves) void gemv_mid_kernel(const uint16_t
     //      16 c + 4 o + e of column r); with K split, fp32 partials, stored
     //      non-temporally: the summing kernel reads them on other XCDs, so
     //      they need not stay in this XCD's L2
-    if constexpr (ACT == kActNone) {
+    if constexpr (ACT != kActSiluMul) {
         if (blk_ok) {
             const int64_t nn = blk * kBlockCols + r;
             if (nn < lay.N) {
@@ -616,7 +619,7 @@ __global__ __launch_bounds__(64 * kMidWaves) void gemv_mid_kernel(const uint16_t
                             if (gridDim.y > 1)
                                 __builtin_nontemporal_store(yacc[c][e], ws + ((int64_t)split * M + row) * lay.N + nn);
                             else
-                                y[(int64_t)row * lay.N + nn] = f32_to_bf16_bits(yacc[c][e]);
+                                y[(int64_t)row * lay.N + nn] = f32_to_half_bits<F16>(yacc[c][e]);
                         }
                     }
             }
@@ -936,8 +939,8 @@ static hipError_t launch_gemv_mid(int bits, const uint16_t *x, const uint8_t *pk
     else
         launch_mid_bits<8, ACT>(grid, ch, stream, x, pk, y, lay, (int)M, ws);
     if (splits > 1) {
-        if constexpr (ACT == kActNone)
-            launch_splitk_sum(ws, (int)splits, M * lay.N, y, stream);
+        if constexpr (ACT != kActSiluMul)
+            launch_splitk_sum(ws, (int)splits, M * lay.N, y, stream, ACT == kActF16);
         else
             launch_splitk_sum_silu(ws, (int)splits, M, lay.N, y, stream);
     }
@@ -985,12 +988,13 @@ GemvPlanInfo gemv_plan_info(int bits, const Layout &lay, int64_t M, int cus)
     return p;
 }
 
-hipError_t launch_gemv(int bits, const uint16_t *x, const void *packed, uint16_t *y, int64_t M, const Layout &lay,
-                       void *workspace, hipStream_t stream, int cus)
+template <int ACT>
+static hipError_t launch_gemv_plain(int bits, const uint16_t *x, const void *packed, uint16_t *y, int64_t M,
+                                    const Layout &lay, void *workspace, hipStream_t stream, int cus)
 {
     const uint8_t *pk = static_cast<const uint8_t *>(packed);
     if (use_mid(lay, M, cus))
-        return launch_gemv_mid(bits, x, pk, y, M, lay, workspace, stream, cus);
+        return launch_gemv_mid<ACT>(bits, x, pk, y, M, lay, workspace, stream, cus);
     const int W = gemv_waves(lay, M);
     const int bpw = gemv_bpw(lay, M);
     const GemvChunks ch = plan_chunks(bits, lay, M, W, bpw);
@@ -998,10 +1002,18 @@ hipError_t launch_gemv(int bits, const uint16_t *x, const void *packed, uint16_t
         return hipErrorInvalidValue;
     const dim3 grid((unsigned)((lay.nblocks + bpw - 1) / bpw)), block(64 * W);
     if (bits == 4)
-        launch_gemv_bits<4>(lay, grid, block, ch, stream, x, pk, y, (int)M);
+        launch_gemv_bits<4, ACT>(lay, grid, block, ch, stream, x, pk, y, (int)M);
     else
-        launch_gemv_bits<8>(lay, grid, block, ch, stream, x, pk, y, (int)M);
+        launch_gemv_bits<8, ACT>(lay, grid, block, ch, stream, x, pk, y, (int)M);
     return hipGetLastError();
+}
+
+hipError_t launch_gemv(int bits, const uint16_t *x, const void *packed, uint16_t *y, int64_t M, const Layout &lay,
+                       void *workspace, hipStream_t stream, int cus, bool f16)
+{
+    if (f16)
+        return launch_gemv_plain<kActF16>(bits, x, packed, y, M, lay, workspace, stream, cus);
+    return launch_gemv_plain<kActNone>(bits, x, packed, y, M, lay, workspace, stream, cus);
 }
 
 void launch_splitk_sum_silu(const float *ws, int splits, int64_t M, int64_t N, uint16_t *y, hipStream_t stream)

@@ -1,5 +1,7 @@
 // Shared device/host definitions of the fused W4A16 / W8A16 linear layer:
-// vector types, the packed (pre-tiled) layout geometry, bf16 helpers.
+// vector types, the packed (pre-tiled) layout geometry, helpers for the two
+// 16-bit formats of activations, scales and outputs (bf16, and the IEEE fp16
+// of many AWQ checkpoints; F16 selects it).
 //
 // The packed layout implements the interleaved pre-tiling of the TileFuse
 // summary (Methodology section 2): scales and zero points packed next to the
@@ -17,12 +19,20 @@ namespace tf {
 
 typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((__vector_size__(8 * sizeof(_Float16))));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kFormatVersion = 2;
+
+// Epilogue and 16-bit format of a linear launch (a template argument of the
+// kernels): a plain store with x, scales and y in bf16; silu(gate) * up over
+// a [gate | up] layer (bf16); or a plain store with x, scales and y in IEEE
+// fp16.
+constexpr int kActNone = 0, kActSiluMul = 1, kActF16 = 2;
 constexpr int kBlockCols = 16;  // output columns per packed block (one MFMA column tile)
 constexpr int kTileRows = 128;  // rows per k-tile of codes
 constexpr int kStepRows = 32;   // rows per MFMA (k depth of 16x16x32)
@@ -77,10 +87,20 @@ struct Layout {
     }
 };
 
-// Metadata of one column inside a record: scale (bf16 bits) and zero point.
-template <int BITS> __device__ __forceinline__ float record_scale(const uint8_t *rec, int c)
+// A 16-bit value (bf16, or fp16 when F16) widened to fp32, exactly.
+template <bool F16> __device__ __forceinline__ float half_bits_to_f32(uint32_t b)
 {
-    return __uint_as_float((uint32_t)(*reinterpret_cast<const uint16_t *>(rec + 2 * c)) << 16);
+    if constexpr (F16)
+        return (float)__builtin_bit_cast(_Float16, (uint16_t)b);
+    else
+        return __uint_as_float(b << 16);
+}
+
+// Metadata of one column inside a record: scale (16-bit bits in the
+// format of the call: bf16, or fp16 when F16) and zero point.
+template <int BITS, bool F16 = false> __device__ __forceinline__ float record_scale(const uint8_t *rec, int c)
+{
+    return half_bits_to_f32<F16>(*reinterpret_cast<const uint16_t *>(rec + 2 * c));
 }
 template <int BITS> __device__ __forceinline__ uint32_t record_zero(const uint8_t *rec, int c)
 {
@@ -114,10 +134,43 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
 
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float v) { return (uint16_t)(pack_bf16x2(v, 0.f) & 0xFFFFu); }
 
-__device__ __forceinline__ f32x4 mfma16x16x32(const u32x4 &a, const u32x4 &b, const f32x4 &c)
+// Output rounding: fp32 -> bf16 or fp16 (F16), nearest even; an fp16 value
+// past 65504 rounds to infinity (v_cvt_f16_f32 in the default mode).
+template <bool F16> __device__ __forceinline__ uint16_t f32_to_half_bits(float v)
 {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
-                                                   0, 0, 0);
+    if constexpr (F16)
+        return __builtin_bit_cast(uint16_t, (_Float16)v);
+    else
+        return f32_to_bf16_bits(v);
+}
+template <bool F16> __device__ __forceinline__ uint32_t pack_half_x2(float lo, float hi)
+{
+    if constexpr (F16) {
+        f32x2 f = {lo, hi};
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, f16x2));
+    } else {
+        return pack_bf16x2(lo, hi);
+    }
+}
+// Operand building: two small integers (|v| <= 2^8, exact in either
+// format) packed as 16-bit values; for fp16 the round-toward-zero pack
+// (v_cvt_pkrtz_f16_f32) is exact and costs one instruction.
+template <bool F16> __device__ __forceinline__ uint32_t pack_int_x2(float lo, float hi)
+{
+    if constexpr (F16)
+        return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
+    else
+        return pack_bf16x2(lo, hi);
+}
+
+template <bool F16 = false> __device__ __forceinline__ f32x4 mfma16x16x32(const u32x4 &a, const u32x4 &b, const f32x4 &c)
+{
+    if constexpr (F16)
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c,
+                                                      0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                                                       c, 0, 0, 0);
 }
 
 __device__ __forceinline__ u32x4 load16(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }

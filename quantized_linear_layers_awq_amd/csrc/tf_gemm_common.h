@@ -66,10 +66,15 @@ __device__ __forceinline__ void dma4(Rsrc r, uint32_t voff, uint32_t soff, void 
                                              (int)soff, 0, 0);
 }
 
-__device__ __forceinline__ f32x16 mfma32x32x16(const u32x4 &a, const u32x4 &b, const f32x16 &c)
+// bf16 operands, or fp16 (F16)
+template <bool F16 = false> __device__ __forceinline__ f32x16 mfma32x32x16(const u32x4 &a, const u32x4 &b, const f32x16 &c)
 {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
-                                                   0, 0, 0);
+    if constexpr (F16)
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c,
+                                                      0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                                                       c, 0, 0, 0);
 }
 
 // How groups map onto the 16-row slices of the k loop.  kGSplit32/64 and

@@ -48,11 +48,9 @@ GemvPlanInfo gemv_plan_info(int bits, const Layout &lay, int64_t M, int cus);
 int64_t gemv_workspace_bytes(const Layout &lay, int64_t M, int cus);
 // Largest M the GEMV kernel takes (16-row chunks, up to four per wave).
 constexpr int64_t kGemvKernelMaxM = 64;
+// f16: x, the scales in the packed records and y are IEEE fp16 (else bf16).
 hipError_t launch_gemv(int bits, const uint16_t *x, const void *packed, uint16_t *y, int64_t M, const Layout &lay,
-                       void *workspace, hipStream_t stream, int cus);
-// Epilogue of the GEMV kernel: none, or silu(gate) * up over a [gate | up]
-// layer (launch_gemv_silu_mul).
-constexpr int kActNone = 0, kActSiluMul = 1;
+                       void *workspace, hipStream_t stream, int cus, bool f16 = false);
 // y[m][8 j + c] = silu(g) * u with g, u the fp32 sums of columns c and c + 8
 // of block j of a [gate | up] layer packed with pair_half = N/2 (N % 16 ==
 // 0), 1 <= M <= kGemvKernelMaxM; y is [M][N/2].  Same kernel choice, and so
@@ -62,9 +60,10 @@ hipError_t launch_gemv_silu_mul(int bits, const uint16_t *x, const void *packed,
 // Sum of a SiLU-product launch's K ranges: y[m][8 j + c] = silu(g) * u from
 // the in-order sums of the partials ws[s][m][16 j + c] and ws[s][m][16 j + c + 8].
 void launch_splitk_sum_silu(const float *ws, int splits, int64_t M, int64_t N, uint16_t *y, hipStream_t stream);
-// y = bf16(sum of the splits' fp32 partials ws[s][mn]), added in split order;
-// 2 <= splits <= 16 (both plans stay within that).
-void launch_splitk_sum(const float *ws, int splits, int64_t mn, uint16_t *y, hipStream_t stream);
+// y = bf16 (fp16 when f16) of the sum of the splits' fp32 partials
+// ws[s][mn], added in split order; 2 <= splits <= 16 (both plans stay within
+// that).
+void launch_splitk_sum(const float *ws, int splits, int64_t mn, uint16_t *y, hipStream_t stream, bool f16 = false);
 // How the GEMM covers the output: m_tiles row tiles of `rows` rows (256, or
 // 128 up to kShortTileMaxM rows), then wide_cols column tiles of col_tile
 // columns from column 0 in one launch and (256 x 128 tiles only)
@@ -95,7 +94,8 @@ int64_t gemm_workspace_bytes(int bits, int64_t M, int64_t N, int64_t K, int64_t 
 constexpr int kRouteAuto = 0, kRouteTiled = 1, kRouteGemv = 2, kRouteTiled128 = 3;
 bool gemm_uses_gemv(int64_t M, int route);
 // act = kActSiluMul: a [gate | up] layer packed with pair_half = N/2, y is
-// [M][N/2] = silu(gate) * up (as launch_gemv_silu_mul).
+// [M][N/2] = silu(gate) * up (as launch_gemv_silu_mul); act = kActF16: x, the
+// scales and y are fp16.
 hipError_t launch_gemm(int bits, const uint16_t *x, const void *packed, uint16_t *y, int64_t M, const Layout &lay,
                        void *workspace, hipStream_t stream, int cus, int act = kActNone, int route = kRouteAuto);
 // The 256 x 256 kernel for a plan with col_tile 256 (W4, groups of whole

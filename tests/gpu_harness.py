@@ -1,8 +1,9 @@
 """Helpers of the GPU parity tests: move a synth.Case to the device, run the
 HIP path through the binding, and compare with the oracle.
 
-Tolerance (fp32 accumulation, bf16 output):
+Tolerance (fp32 accumulation, bf16 or fp16 output):
     |y - y_ref| <= 1e-2 * max(|y_ref|, rms(y_ref row))  for every element.
+A case whose dtype is "f16" (fp16 x and scales) runs the *_f16 entry points.
 """
 
 from __future__ import annotations
@@ -30,7 +31,8 @@ def to_device(case, torch, dev="cuda:0"):
         qweight=torch.from_numpy(np.ascontiguousarray(qw)).to(dev),
         qzeros=torch.from_numpy(np.ascontiguousarray(qz)).to(dev),
         scales=torch.from_numpy(case.scales.view(np.int16)).to(dev),
-        x=torch.from_numpy(case.x.view(np.int16)).to(dev).view(torch.bfloat16),
+        x=torch.from_numpy(case.x.view(np.int16)).to(dev).view(
+            torch.float16 if getattr(case, "dtype", "bf16") == "f16" else torch.bfloat16),
     )
 
 
@@ -45,7 +47,7 @@ def linear_fn(q, bits, gemm):
 
 
 def bf16_to_f64(t):
-    """bf16 device tensor -> float64 numpy (exact)."""
+    """bf16 or fp16 device tensor -> float64 numpy (exact)."""
     return t.float().cpu().numpy().astype(np.float64)
 
 
@@ -87,7 +89,9 @@ def run_linear(q, bits, op, x, packed, K, N, G, cus=0, route=0, y=None, torch=No
     if cus == 0 and route == 0:
         fn = {q.TF_OP_GEMV: linear_fn(q, bits, False), q.TF_OP_GEMM: linear_fn(q, bits, True),
               q.TF_OP_GEMV_SILU_MUL: q.tf_gemv_w4a16_silu_mul if bits == 4 else q.tf_gemv_w8a16_silu_mul,
-              q.TF_OP_GEMM_SILU_MUL: q.tf_gemm_w4a16_silu_mul if bits == 4 else q.tf_gemm_w8a16_silu_mul}[op]
+              q.TF_OP_GEMM_SILU_MUL: q.tf_gemm_w4a16_silu_mul if bits == 4 else q.tf_gemm_w8a16_silu_mul,
+              q.TF_OP_GEMV_F16: q.tf_gemv_w4a16_f16 if bits == 4 else q.tf_gemv_w8a16_f16,
+              q.TF_OP_GEMM_F16: q.tf_gemm_w4a16_f16 if bits == 4 else q.tf_gemm_w8a16_f16}[op]
         return fn(x, packed, K, N, G, y=y)
     if cus == 0:
         import torch as _torch
@@ -96,12 +100,20 @@ def run_linear(q, bits, op, x, packed, K, N, G, cus=0, route=0, y=None, torch=No
     return q.tf_linear_planned(bits, op, x, packed, K, N, G, cus, route, y=y)
 
 
+def linear_op(q, case, gemm):
+    """The TF_OP_* of a plain linear call on the case (its dtype picks the
+    bf16 or the fp16 entry points)."""
+    if getattr(case, "dtype", "bf16") == "f16":
+        return q.TF_OP_GEMM_F16 if gemm else q.TF_OP_GEMV_F16
+    return q.TF_OP_GEMM if gemm else q.TF_OP_GEMV
+
+
 def check_linear(case, torch, q, gemm, rows=None, cols=None, packed=None, d=None, cus=0, route=0):
     """Run the HIP path on the whole case, compare the chosen rows/columns.
     cus / route: the plan inputs (0, 0: the product call as routed)."""
     d = d or to_device(case, torch)
     packed = packed if packed is not None else repack(case, d, q)
-    op = q.TF_OP_GEMM if gemm else q.TF_OP_GEMV
+    op = linear_op(q, case, gemm)
     y = run_linear(q, case.bits, op, d["x"], packed, case.K, case.N, case.G, cus=cus, route=route, torch=torch)
     torch.cuda.synchronize()
     yh = bf16_to_f64(y)

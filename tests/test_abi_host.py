@@ -89,7 +89,28 @@ def test_packed_bytes_invalid_shapes_are_zero(lib, K, N, G):
 
 
 ROUTE_AUTO, ROUTE_TILED, ROUTE_GEMV, ROUTE_TILED128 = 0, 1, 2, 3
-OP_GEMV, OP_GEMM, OP_GEMV_SILU, OP_GEMM_SILU = 0, 1, 2, 3
+OP_GEMV, OP_GEMM, OP_GEMV_SILU, OP_GEMM_SILU, OP_GEMV_F16, OP_GEMM_F16 = 0, 1, 2, 3, 4, 5
+
+
+def test_f16_ops_plan_as_their_bf16_ops(lib):
+    """The fp16 calls run the kernels and launch plans of the bf16 calls of
+    the same name: every planned workspace size agrees; an op past the last
+    is refused (size 0)."""
+    n = 0
+    for bits in (4, 8):
+        for K, N, G in ((4096, 4096, 128), (14336, 4096, 128), (4096, 1024, 32), (8192, 8192, 8192), (4096, 28672, 128)):
+            for M in (1, 4, 8, 16, 24, 40, 64, 65, 129, 300, 2048):
+                for cus in (80, 256, 4096):
+                    for route in (ROUTE_AUTO, ROUTE_TILED, ROUTE_GEMV, ROUTE_TILED128):
+                        a = lib.tf_workspace_bytes_planned(bits, OP_GEMM, M, K, N, G, cus, route)
+                        assert a == lib.tf_workspace_bytes_planned(bits, OP_GEMM_F16, M, K, N, G, cus, route)
+                        if M <= 16:
+                            g = lib.tf_workspace_bytes_planned(bits, OP_GEMV, M, K, N, G, cus, route)
+                            assert g == lib.tf_workspace_bytes_planned(bits, OP_GEMV_F16, M, K, N, G, cus, route)
+                        n += 1
+    assert n > 1000
+    assert lib.tf_workspace_bytes_planned(4, 6, 8, 4096, 4096, 128, 256, ROUTE_AUTO) == 0
+    assert lib.tf_workspace_bytes_planned(4, OP_GEMV_F16, 17, 4096, 4096, 128, 256, ROUTE_AUTO) == 0
 
 
 @pytest.mark.parametrize("route", [ROUTE_AUTO, ROUTE_TILED])
@@ -309,6 +330,18 @@ class TestValidation:
         assert self._gemv(lib, M=-1) == TF_ERR_SHAPE
         assert self._gemv(lib, K=0) == TF_ERR_SHAPE
         assert self._gemv(lib, M=2**30 + 1, fn="tf_gemm_w4a16") == TF_ERR_SHAPE
+
+    @pytest.mark.parametrize("fn", ["tf_gemv_w4a16_f16", "tf_gemv_w8a16_f16", "tf_gemm_w4a16_f16",
+                                    "tf_gemm_w8a16_f16"])
+    def test_f16_entries_validate_like_bf16(self, lib, fn):
+        gemm = "gemm" in fn
+        assert self._gemv(lib, K=33, fn=fn) == TF_ERR_SHAPE
+        assert self._gemv(lib, M=17 if not gemm else 2**30 + 1, fn=fn) == TF_ERR_SHAPE
+        assert self._gemv(lib, G=48, fn=fn) == TF_ERR_GROUP
+        assert self._gemv(lib, x=None, fn=fn) == TF_ERR_NULL
+        assert self._gemv(lib, y=FAKE + 1, fn=fn) == TF_ERR_ALIGN
+        assert self._gemv(lib, nbytes=10, fn=fn) == TF_ERR_BUFFER_TOO_SMALL
+        assert self._gemv(lib, M=0, fn=fn) == TF_OK
 
     def test_group_errors(self, lib):
         assert self._gemv(lib, G=48) == TF_ERR_GROUP
