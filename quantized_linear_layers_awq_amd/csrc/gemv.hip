@@ -131,6 +131,11 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const uint16_t *__restrict__
     const uint32_t magic = magic_in_vgpr<F16>();
     const int ktiles = (int)lay.ktiles;
     const f32x4 zf = {0.f, 0.f, 0.f, 0.f};
+    // One block per workgroup with one group per k-tile: the waves' k-tile
+    // ranges, and so the x columns and the records each reads, are disjoint.
+    // Each wave then stages only its own part, and no workgroup barrier
+    // separates the staging from the loop.
+    constexpr bool kPerWave = kMode == kOneTile && BPW == 1;
 
     f32x4 yacc = zf, gacc = zf, zacc = zf;
     TileCodes<BITS> ring[D];
@@ -140,82 +145,141 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const uint16_t *__restrict__
         const int nct = c1 - c0;
         const int a = c0 + nct * ws / Wb, b = c0 + nct * (ws + 1) / Wb; // this wave's k-tiles
         const int n = blk_ok ? b - a : 0;
-        // ---- x[m][k0 .. k0 + 128 nct) (zero past K) and the chunk's records
-        //      are loaded first, into registers: they come from L2 and are
-        //      stored to LDS before the barrier, and vector-memory loads
-        //      retire in order, so loads issued after the codes would wait for
-        //      the codes' HBM latency before the barrier ----
         const int64_t k0 = (int64_t)c0 * kTileRows;
-        const int units_per_row = nct * (kTileRows / 8);
-        const int x_units = M * units_per_row;
-        // unit e is row e / units_per_row: a multiply-high by a per-chunk
-        // constant instead of a division, exact since e * units_per_row <
-        // 2^32 (the chunk fits LDS: units_per_row < 10^4, e < 16 of them)
-        const uint32_t upr_m = 0xFFFFFFFFu / (uint32_t)units_per_row + 1u;
-        constexpr int XR = 4; // x units per thread held in registers
-        u32x4 xv[XR];
-#pragma unroll
-        for (int i = 0; i < XR; ++i) {
-            const int e = tid + i * (int)blockDim.x;
-            xv[i] = u32x4{0u, 0u, 0u, 0u};
-            if (e < x_units) {
-                const int m = (int)__umulhi((uint32_t)e, upr_m), u8 = e - m * units_per_row;
-                const int64_t k = k0 + 8 * u8;
-                if (k < lay.K)
-                    xv[i] = load16(x + (int64_t)m * lay.K + k);
-            }
-        }
         const int64_t k1 = (int64_t)c1 * kTileRows < lay.K ? (int64_t)c1 * kTileRows : lay.K;
         const int64_t g0 = (uint32_t)k0 / (uint32_t)lay.G, g1 = (uint32_t)(k1 - 1) / (uint32_t)lay.G;
-        const int rec_words = (int)((g1 - g0 + 1) * RB / 8);
-        u32x2 mv[BPW];
+        if constexpr (kPerWave) {
+            // ---- this wave's k-tiles a .. b - 1 only: x[m][128 a .. 128 b)
+            //      (zero past K) and the records of groups a .. b - 1, loaded
+            //      before the codes, then stored to the same LDS places the
+            //      shared staging uses; LDS operations of one wave complete in
+            //      order, so the loop's reads see them without a barrier ----
+            const int wupr = n * (kTileRows / 8); // 16-byte units per row of x
+            const int wx_units = M * wupr;
+            const uint32_t wupr_m = 0xFFFFFFFFu / (uint32_t)(wupr > 0 ? wupr : 1) + 1u;
+            constexpr int XR = 4;
+            u32x4 xv[XR];
 #pragma unroll
-        for (int eb = 0; eb < BPW; ++eb) {
-            mv[eb] = u32x2{0u, 0u};
-            if (tid < rec_words && blk0 + eb < lay.nblocks)
-                mv[eb] = *reinterpret_cast<const u32x2 *>(packed + (blk0 + eb) * lay.block_bytes + g0 * RB + 8 * tid);
-        }
-        // ---- then the codes.  Ring loads past the wave's range re-read its
-        //      last tile (in bounds, never used). ----
-        if (n > 0) {
+            for (int i = 0; i < XR; ++i) {
+                const int e = lane + 64 * i;
+                xv[i] = u32x4{0u, 0u, 0u, 0u};
+                if (e < wx_units) {
+                    const int m = (int)__umulhi((uint32_t)e, wupr_m), u8 = (a - c0) * 16 + e - m * wupr;
+                    const int64_t k = k0 + 8 * u8;
+                    if (k < lay.K)
+                        xv[i] = load16(x + (int64_t)m * lay.K + k);
+                }
+            }
+            const int rec_words = n * (int)RB / 8;
+            u32x2 mv = {0u, 0u};
+            if (lane < rec_words)
+                mv = *reinterpret_cast<const u32x2 *>(meta + (int64_t)a * RB + 8 * lane);
+            if (n > 0) {
 #pragma unroll
-            for (int j = 0; j < D; ++j)
-                load_codes<BITS>(ring[j], tiles + (uint32_t)(a + (j < n ? j : n - 1)) * TB);
-        }
+                for (int j = 0; j < D; ++j)
+                    load_codes<BITS>(ring[j], tiles + (uint32_t)(a + (j < n ? j : n - 1)) * TB);
+            }
+            // the waves' ranges move between chunks: another wave may still
+            // read the previous chunk where this one stores
+            if (c0 > 0)
+                __syncthreads();
+#pragma unroll
+            for (int i = 0; i < XR; ++i) {
+                const int e = lane + 64 * i;
+                if (e < wx_units) {
+                    const int m = (int)__umulhi((uint32_t)e, wupr_m), u8 = (a - c0) * 16 + e - m * wupr;
+                    *reinterpret_cast<u32x4 *>(sx + m * ch.xpitch + 8 * u8) = xv[i];
+                }
+            }
+            for (int e = lane + 64 * XR; e < wx_units; e += 64) { // more than XR per lane
+                const int m = (int)__umulhi((uint32_t)e, wupr_m), u8 = (a - c0) * 16 + e - m * wupr;
+                const int64_t k = k0 + 8 * u8;
+                u32x4 v = {0u, 0u, 0u, 0u};
+                if (k < lay.K)
+                    v = load16(x + (int64_t)m * lay.K + k);
+                *reinterpret_cast<u32x4 *>(sx + m * ch.xpitch + 8 * u8) = v;
+            }
+            uint8_t *const srec = smeta + (a - c0) * RB;
+            if (lane < rec_words)
+                *reinterpret_cast<u32x2 *>(srec + 8 * lane) = mv;
+            for (int e = lane + 64; e < rec_words; e += 64) // more than one per lane
+                *reinterpret_cast<u32x2 *>(srec + 8 * e) =
+                    *reinterpret_cast<const u32x2 *>(meta + (int64_t)a * RB + 8 * e);
+            __builtin_amdgcn_wave_barrier();
+        } else {
+            // ---- x[m][k0 .. k0 + 128 nct) (zero past K) and the chunk's records
+            //      are loaded first, into registers: they come from L2 and are
+            //      stored to LDS before the barrier, and vector-memory loads
+            //      retire in order, so loads issued after the codes would wait for
+            //      the codes' HBM latency before the barrier ----
+            const int units_per_row = nct * (kTileRows / 8);
+            const int x_units = M * units_per_row;
+            // unit e is row e / units_per_row: a multiply-high by a per-chunk
+            // constant instead of a division, exact since e * units_per_row <
+            // 2^32 (the chunk fits LDS: units_per_row < 10^4, e < 16 of them)
+            const uint32_t upr_m = 0xFFFFFFFFu / (uint32_t)units_per_row + 1u;
+            constexpr int XR = 4; // x units per thread held in registers
+            u32x4 xv[XR];
+#pragma unroll
+            for (int i = 0; i < XR; ++i) {
+                const int e = tid + i * (int)blockDim.x;
+                xv[i] = u32x4{0u, 0u, 0u, 0u};
+                if (e < x_units) {
+                    const int m = (int)__umulhi((uint32_t)e, upr_m), u8 = e - m * units_per_row;
+                    const int64_t k = k0 + 8 * u8;
+                    if (k < lay.K)
+                        xv[i] = load16(x + (int64_t)m * lay.K + k);
+                }
+            }
+            const int rec_words = (int)((g1 - g0 + 1) * RB / 8);
+            u32x2 mv[BPW];
+#pragma unroll
+            for (int eb = 0; eb < BPW; ++eb) {
+                mv[eb] = u32x2{0u, 0u};
+                if (tid < rec_words && blk0 + eb < lay.nblocks)
+                    mv[eb] = *reinterpret_cast<const u32x2 *>(packed + (blk0 + eb) * lay.block_bytes + g0 * RB + 8 * tid);
+            }
+            // ---- then the codes.  Ring loads past the wave's range re-read its
+            //      last tile (in bounds, never used). ----
+            if (n > 0) {
+#pragma unroll
+                for (int j = 0; j < D; ++j)
+                    load_codes<BITS>(ring[j], tiles + (uint32_t)(a + (j < n ? j : n - 1)) * TB);
+            }
 
-        if (c0 > 0)
-            __syncthreads(); // the previous chunk's LDS is no longer read
+            if (c0 > 0)
+                __syncthreads(); // the previous chunk's LDS is no longer read
 #pragma unroll
-        for (int i = 0; i < XR; ++i) {
-            const int e = tid + i * (int)blockDim.x;
-            if (e < x_units) {
+            for (int i = 0; i < XR; ++i) {
+                const int e = tid + i * (int)blockDim.x;
+                if (e < x_units) {
+                    const int m = (int)__umulhi((uint32_t)e, upr_m), u8 = e - m * units_per_row;
+                    *reinterpret_cast<u32x4 *>(sx + m * ch.xpitch + 8 * u8) = xv[i];
+                }
+            }
+            for (int e = tid + XR * (int)blockDim.x; e < x_units; e += blockDim.x) { // more than XR per thread
                 const int m = (int)__umulhi((uint32_t)e, upr_m), u8 = e - m * units_per_row;
-                *reinterpret_cast<u32x4 *>(sx + m * ch.xpitch + 8 * u8) = xv[i];
+                const int64_t k = k0 + 8 * u8;
+                u32x4 v = {0u, 0u, 0u, 0u};
+                if (k < lay.K)
+                    v = load16(x + (int64_t)m * lay.K + k);
+                *reinterpret_cast<u32x4 *>(sx + m * ch.xpitch + 8 * u8) = v;
             }
-        }
-        for (int e = tid + XR * (int)blockDim.x; e < x_units; e += blockDim.x) { // more than XR per thread
-            const int m = (int)__umulhi((uint32_t)e, upr_m), u8 = e - m * units_per_row;
-            const int64_t k = k0 + 8 * u8;
-            u32x4 v = {0u, 0u, 0u, 0u};
-            if (k < lay.K)
-                v = load16(x + (int64_t)m * lay.K + k);
-            *reinterpret_cast<u32x4 *>(sx + m * ch.xpitch + 8 * u8) = v;
-        }
 #pragma unroll
-        for (int eb = 0; eb < BPW; ++eb) {
-            if (blk0 + eb < lay.nblocks) {
-                if (tid < rec_words)
-                    *reinterpret_cast<u32x2 *>(smem + eb * ch.meta_cap + 8 * tid) = mv[eb];
-                const uint8_t *src = packed + (blk0 + eb) * lay.block_bytes + g0 * RB;
-                for (int e = tid + (int)blockDim.x; e < rec_words; e += blockDim.x) // more than one per thread
-                    *reinterpret_cast<u32x2 *>(smem + eb * ch.meta_cap + 8 * e) =
-                        *reinterpret_cast<const u32x2 *>(src + 8 * e);
+            for (int eb = 0; eb < BPW; ++eb) {
+                if (blk0 + eb < lay.nblocks) {
+                    if (tid < rec_words)
+                        *reinterpret_cast<u32x2 *>(smem + eb * ch.meta_cap + 8 * tid) = mv[eb];
+                    const uint8_t *src = packed + (blk0 + eb) * lay.block_bytes + g0 * RB;
+                    for (int e = tid + (int)blockDim.x; e < rec_words; e += blockDim.x) // more than one per thread
+                        *reinterpret_cast<u32x2 *>(smem + eb * ch.meta_cap + 8 * e) =
+                            *reinterpret_cast<const u32x2 *>(src + 8 * e);
+                }
             }
+            __syncthreads();
         }
-        __syncthreads();
         if (n <= 0)
             continue;
-
         const uint16_t *xl = sx + xr * ch.xpitch + 8 * o - c0 * kTileRows;
         // kMultiTile: tiles left in the current group and the group's record
         const int tpg = kMode == kMultiTile ? (int)lay.tiles_per_group : 1;
