@@ -267,10 +267,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm256_kernel(const uint16_t *__
     for (int sl = 0; sl < 4; ++sl)
         a_rd[sl] = 16 * swz(128 * wm + l32, 2 * sl + h32);
     const int b_rd = kOffB + h32 * kBOct + (64 * wn + l32) * 16;
-    auto read_frags = [&](auto h_c, int sl, u32x4 (&af)[4], u32x4 (&bf)[2]) {
-        constexpr int hb = decltype(h_c)::value;
+    auto read_frags = [&](auto h_c, auto live_c, int sl, u32x4 (&af)[4], u32x4 (&bf)[2]) {
+        constexpr int hb = decltype(h_c)::value, LIVE = decltype(live_c)::value;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < LIVE; ++i)
             af[i] = *reinterpret_cast<const u32x4 *>(lds + hb * kAStageB + a_rd[sl] + 4096 * i);
 #pragma unroll
         for (int j = 0; j < 2; ++j)
@@ -312,9 +312,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm256_kernel(const uint16_t *__
             s_last[j] = se;
         }
     };
-    auto fold_rows = [&](int i0) {
+    auto fold_rows = [&](int i0, auto live_c) {
+        constexpr int LIVE = decltype(live_c)::value;
 #pragma unroll
-        for (int i = i0; i < i0 + 2; ++i)
+        for (int i = i0; i < (i0 + 2 < LIVE ? i0 + 2 : LIVE); ++i)
 #pragma unroll
             for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -336,14 +337,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm256_kernel(const uint16_t *__
     //      forcing an MFMA/VALU pattern).  No step depends on a branch: after
     //      the last stage the loads re-read in-bounds data (clamped) into
     //      buffers no one reads, and the unpack writes the idle B buffer. ----
-    auto stage = [&](int t, auto h_c) {
-        constexpr int h = decltype(h_c)::value;
+    auto stage = [&](int t, auto h_c, auto live_c) {
+        constexpr int h = decltype(h_c)::value, LIVE = decltype(live_c)::value;
         constexpr int hn = h ^ 1; // parity of the next stage
         const int s = 2 * t + h;
         const int tn = h == 0 ? t : (t + 1 < ktiles ? t + 1 : t); // k-tile of the next stage (clamped)
         const int tc = t + 1 < ktiles ? t + 1 : t;                 // next k-tile's loads (clamped)
         u32x4 af[2][4], bf[2][2];
-        read_frags(h_c, 0, af[0], bf[0]);
+        read_frags(h_c, live_c, 0, af[0], bf[0]);
         UnpackIn uin;
         static_for<0, 4>([&](auto sl_c) {
             constexpr int sl = decltype(sl_c)::value;
@@ -354,7 +355,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm256_kernel(const uint16_t *__
                 unpack_load(tn, uin);
             }
             if constexpr (sl + 1 < 4)
-                read_frags(h_c, sl + 1, af[cur ^ 1], bf[cur ^ 1]);
+                read_frags(h_c, live_c, sl + 1, af[cur ^ 1], bf[cur ^ 1]);
             __builtin_amdgcn_sched_barrier(0);
             if constexpr (sl == 0) {
                 dma_a(s + 1, 0, kAJ / 2);
@@ -369,24 +370,40 @@ __global__ __launch_bounds__(kThreads, 1) void gemm256_kernel(const uint16_t *__
                 unpack_store(ic<hn>{}, tn, uin, 1);
             }
             if constexpr (sl == 0 && h == 0)
-                fold_rows(2); // second half of the fold before k-tile t
+                fold_rows(2, live_c); // second half of the fold before k-tile t
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < LIVE; ++i)
 #pragma unroll
                 for (int j = 0; j < 2; ++j)
                     acc[i][j] = mfma32x32x16<F16>(af[cur][i], bf[cur][j], acc[i][j]);
             if constexpr (sl == 3 && h == 1) {
                 fold_ratios(t + 1); // the boundary before k-tile t + 1
-                fold_rows(0);
+                fold_rows(0, live_c);
             }
         });
         wait_vmcnt<0>();
         wait_lgkmcnt0();
         lds_barrier();
     };
-    for (int t = 0; t < ktiles; ++t) {
-        stage(t, ic<0>{});
-        stage(t, ic<1>{});
+    // Row tiles of the wave below M: a last row tile with fewer than 256
+    // rows leaves some waves' 32-row MFMA tiles entirely past M.  Their
+    // MFMAs, fragment reads and folds are skipped (their outputs are never
+    // stored); the wave still does its share of the loads, unpacking and
+    // barriers.  One copy of the k loop per count, chosen once.
+    const int64_t wave_rows = M - m0 - 128 * wm;
+    const int live = wave_rows >= 128 ? 4 : wave_rows <= 0 ? 0 : (int)((wave_rows + 31) / 32);
+    auto k_loop = [&](auto live_c) {
+        for (int t = 0; t < ktiles; ++t) {
+            stage(t, ic<0>{}, live_c);
+            stage(t, ic<1>{}, live_c);
+        }
+    };
+    switch (__builtin_amdgcn_readfirstlane(live)) {
+    case 4: k_loop(ic<4>{}); break;
+    case 3: k_loop(ic<3>{}); break;
+    case 2: k_loop(ic<2>{}); break;
+    case 1: k_loop(ic<1>{}); break;
+    default: k_loop(ic<0>{}); break;
     }
 
     // ---- epilogue: y = chain * s_last, fp32 -> bf16 (nearest even).
