@@ -289,9 +289,11 @@ int tf_dequant_gemv_w8_f32(const void *packed, size_t packed_bytes, float *w,
 /*          TF_OP_GEMV_F16, TF_OP_GEMM_F16 (the *_f16 calls)                 */
 /*   cus    compute units to plan for, 1 .. 2^20                            */
 /*   route  TF_ROUTE_AUTO (the product calls' choice), TF_ROUTE_TILED (GEMM */
-/*          calls run the tiled GEMM at any M), TF_ROUTE_GEMV (the GEMV     */
-/*          kernels up to 64 rows, as AUTO), TF_ROUTE_TILED128 (the tiled   */
-/*          GEMM at any M with 256 x 128 tiles only)                        */
+/*          calls run the tiled GEMM at any M, with 256 x 256 tiles wherever */
+/*          they apply; AUTO drops them where a K split of theirs would     */
+/*          still fill less than 85 % of the compute units), TF_ROUTE_GEMV  */
+/*          (the GEMV kernels up to 64 rows, as AUTO), TF_ROUTE_TILED128    */
+/*          (the tiled GEMM at any M with 256 x 128 tiles only)             */
 /* Other values: TF_ERR_UNSUPPORTED (the size query returns 0).             */
 /* ------------------------------------------------------------------------ */
 enum { TF_OP_GEMV = 0, TF_OP_GEMM = 1, TF_OP_GEMV_SILU_MUL = 2, TF_OP_GEMM_SILU_MUL = 3,

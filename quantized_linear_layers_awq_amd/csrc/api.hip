@@ -370,7 +370,7 @@ int tf_gemm_plan(int bits, int64_t M, int64_t K, int64_t N, int64_t G, int cus, 
         out[7] = 0;
         return TF_OK;
     }
-    const tf::GemmPlan p = tf::plan_gemm(bits, M, N, K, G, cus, route != tf::kRouteTiled128);
+    const tf::GemmPlan p = tf::plan_gemm(bits, M, N, K, G, cus, route);
     out[0] = p.m_tiles;
     out[1] = p.wide_cols;
     out[2] = p.narrow_cols;

@@ -761,8 +761,9 @@ static bool plan_split(GemmPlan &p, int64_t tiles, int64_t K, int64_t G, int cus
     return true;
 }
 
-GemmPlan plan_gemm(int bits, int64_t M, int64_t N, int64_t K, int64_t G, int cus, bool allow256)
+GemmPlan plan_gemm(int bits, int64_t M, int64_t N, int64_t K, int64_t G, int cus, int route)
 {
+    const bool allow256 = route != kRouteTiled128;
     GemmPlan p;
     const int64_t ktiles = (K + kTileRows - 1) / kTileRows;
     p.splits = 1;
@@ -777,7 +778,21 @@ GemmPlan plan_gemm(int bits, int64_t M, int64_t N, int64_t K, int64_t G, int cus
         p.m_tiles = (M + kGBM - 1) / kGBM;
         p.wide_cols = (N + 255) / 256;
         plan_split(p, p.m_tiles * p.wide_cols, K, G, cus);
-        return p;
+        // The automatic choice drops these tiles only where K had to be
+        // split and the split launch still fills less than 85 % of the
+        // compute units: the split is capped at 8 ranges (often of only a few
+        // k-tiles each), and twice as many 256 x 128 tiles fill the chip
+        // better.  On the decoder layer's q/k/v, o and down projections at
+        // M = 129-256 they took 28-46 us against 30-56.  Without a split a
+        // partial round of these tiles still beats the 256 x 128 tiles' one
+        // and a half (q/k/v at M = 2048).  The test route kRouteTiled keeps
+        // these tiles wherever they apply.
+        if (route == kRouteTiled || p.splits == 1 || p.m_tiles * p.wide_cols * p.splits * 20 >= 17 * (int64_t)cus)
+            return p;
+        p = GemmPlan{};
+        p.splits = 1;
+        p.split_tiles = ktiles;
+        p.narrow_cols = 0;
     }
     // up to 128 rows, 128-row tiles: a 256-row tile would compute at least
     // as many padding rows as real ones
@@ -807,7 +822,7 @@ GemmPlan plan_gemm(int bits, int64_t M, int64_t N, int64_t K, int64_t G, int cus
 
 int64_t gemm_workspace_bytes(int bits, int64_t M, int64_t N, int64_t K, int64_t G, int cus, int route)
 {
-    const GemmPlan p = plan_gemm(bits, M, N, K, G, cus, route != kRouteTiled128);
+    const GemmPlan p = plan_gemm(bits, M, N, K, G, cus, route);
     return p.splits > 1 ? p.splits * M * N * (int64_t)sizeof(float) : 0;
 }
 
@@ -816,7 +831,7 @@ hipError_t launch_gemm(int bits, const uint16_t *x, const void *packed, uint16_t
 {
     if (act == kActSiluMul && lay.N % kBlockCols)
         return hipErrorInvalidValue;
-    const GemmPlan plan = plan_gemm(bits, M, lay.N, lay.K, lay.G, cus, route != kRouteTiled128);
+    const GemmPlan plan = plan_gemm(bits, M, lay.N, lay.K, lay.G, cus, route);
     float *ws = plan.splits > 1 ? static_cast<float *>(workspace) : nullptr;
     if (plan.col_tile == 256) {
         if (hipError_t e = launch_gemm256(x, packed, y, M, lay, plan, ws, stream, act))

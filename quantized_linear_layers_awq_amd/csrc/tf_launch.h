@@ -77,8 +77,10 @@ constexpr int64_t kShortTileMaxM = 128;
 struct GemmPlan {
     int64_t m_tiles, wide_cols, narrow_cols, splits, split_tiles, rows, col_tile;
 };
-// allow256 = false keeps the 256 x 128 kernel (a test route)
-GemmPlan plan_gemm(int bits, int64_t M, int64_t N, int64_t K, int64_t G, int cus, bool allow256 = true);
+// route: the automatic choice (kRouteAuto; kRouteGemv plans the same),
+// kRouteTiled (256 x 256 tiles wherever they apply) or kRouteTiled128
+// (256 x 128 tiles only)
+GemmPlan plan_gemm(int bits, int64_t M, int64_t N, int64_t K, int64_t G, int cus, int route);
 // Compute units of the current device (queried once per device and kept:
 // the library's only process-wide state).
 int device_cus();
