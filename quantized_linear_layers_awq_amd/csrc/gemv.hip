@@ -55,12 +55,25 @@ __device__ __forceinline__ u32x4 code_operand(const TileCodes<BITS> &c, int u, u
         return w8_operand<F16>(c.w[u >> 1][2 * (u & 1)], c.w[u >> 1][2 * (u & 1) + 1]);
 }
 
-template <int BITS>
-__device__ __forceinline__ void load_codes(TileCodes<BITS> &c, const uint8_t *tile_lane)
+// A wave's code tiles are read through a buffer resource whose range ends
+// at the wave's last k-tile.  The ring's look-ahead loads past that end
+// return zero without a memory access, so every slot can be refilled
+// unconditionally (the wait counts stay exact) and no tile is read twice.
+typedef __amdgpu_buffer_rsrc_t CodeRange;
+__device__ __forceinline__ CodeRange code_range(const uint8_t *tiles, uint32_t bytes)
 {
-    c.w[0] = load16_stream(tile_lane);
+    // stride 0, range [0, bytes), dword data format (required on gfx9)
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(tiles), 0, (int)bytes, 0x00020000);
+}
+
+// The codes of tile byte offset off (lane offset included), non-temporal.
+template <int BITS>
+__device__ __forceinline__ void load_codes(TileCodes<BITS> &c, CodeRange cr, uint32_t off)
+{
+    constexpr int kNonTemporal = 2;
+    c.w[0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(cr, (int)off, 0, kNonTemporal));
     if constexpr (BITS == 8)
-        c.w[1] = load16_stream(tile_lane + 1024);
+        c.w[1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(cr, (int)off + 1024, 0, kNonTemporal));
 }
 
 __device__ __forceinline__ void fold(f32x4 &yacc, f32x4 &gacc, f32x4 &zacc, float s)
@@ -123,7 +136,8 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const uint16_t *__restrict__
     const int64_t blk = blk0 + bi;
     const bool blk_ok = blk < lay.nblocks;                // a last workgroup may be partial
     const uint8_t *meta = packed + (blk_ok ? blk : 0) * lay.block_bytes;
-    const uint8_t *tiles = meta + lay.meta_bytes + 16 * lane;
+    const uint8_t *tiles = meta + lay.meta_bytes;
+    const uint32_t lane_off = 16 * lane;
     uint8_t *smeta = smem + bi * ch.meta_cap;             // this block's staged records
     // MFMA rows >= M are never stored, so their lanes read row 0 instead of
     // being masked off.
@@ -148,6 +162,7 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const uint16_t *__restrict__
         const int64_t k0 = (int64_t)c0 * kTileRows;
         const int64_t k1 = (int64_t)c1 * kTileRows < lay.K ? (int64_t)c1 * kTileRows : lay.K;
         const int64_t g0 = (uint32_t)k0 / (uint32_t)lay.G, g1 = (uint32_t)(k1 - 1) / (uint32_t)lay.G;
+        const CodeRange cr = code_range(tiles, (uint32_t)(n > 0 ? b : 0) * TB);
         if constexpr (kPerWave) {
             // ---- this wave's k-tiles a .. b - 1 only: x[m][128 a .. 128 b)
             //      (zero past K) and the records of groups a .. b - 1, loaded
@@ -177,7 +192,7 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const uint16_t *__restrict__
             if (n > 0) {
 #pragma unroll
                 for (int j = 0; j < D; ++j)
-                    load_codes<BITS>(ring[j], tiles + (uint32_t)(a + (j < n ? j : n - 1)) * TB);
+                    load_codes<BITS>(ring[j], cr, lane_off + (uint32_t)(a + j) * TB);
             }
             // the waves' ranges move between chunks: another wave may still
             // read the previous chunk where this one stores
@@ -239,12 +254,11 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const uint16_t *__restrict__
                 if (tid < rec_words && blk0 + eb < lay.nblocks)
                     mv[eb] = *reinterpret_cast<const u32x2 *>(packed + (blk0 + eb) * lay.block_bytes + g0 * RB + 8 * tid);
             }
-            // ---- then the codes.  Ring loads past the wave's range re-read its
-            //      last tile (in bounds, never used). ----
+            // ---- then the codes (loads past the wave's range are dropped) ----
             if (n > 0) {
 #pragma unroll
                 for (int j = 0; j < D; ++j)
-                    load_codes<BITS>(ring[j], tiles + (uint32_t)(a + (j < n ? j : n - 1)) * TB);
+                    load_codes<BITS>(ring[j], cr, lane_off + (uint32_t)(a + j) * TB);
             }
 
             if (c0 > 0)
@@ -298,7 +312,7 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const uint16_t *__restrict__
 #pragma unroll
                 for (int u = 0; u < 4; ++u)
                     ops[u] = code_operand<BITS, F16>(ring[j], u, magic);
-                load_codes<BITS>(ring[j], tiles + (uint32_t)(ti + D < n ? t + D : b - 1) * TB);
+                load_codes<BITS>(ring[j], cr, lane_off + (uint32_t)(t + D) * TB);
                 if (ti < n) {
                     u32x4 xa[4];
 #pragma unroll
@@ -446,11 +460,14 @@ __global__ __launch_bounds__(64 * kMidWaves) void gemv_mid_kernel(const uint16_t
     const int64_t blk0 = (int64_t)blockIdx.x * kMidWaves;
     const int64_t blk = blk0 + wave;
     const bool blk_ok = blk < lay.nblocks;
-    const uint8_t *tiles = packed + (blk_ok ? blk : 0) * lay.block_bytes + lay.meta_bytes + 16 * lane;
     const int ktiles = (int)lay.ktiles;
     const int split = blockIdx.y;
     const int kt_begin = split * ch.split_tiles;
     const int kt_end = kt_begin + ch.split_tiles < ktiles ? kt_begin + ch.split_tiles : ktiles;
+    // the wave's k range of its block; a wave past the last block loads nothing
+    const CodeRange cr = code_range(packed + (blk_ok ? blk : 0) * lay.block_bytes + lay.meta_bytes,
+                                    (uint32_t)(blk_ok ? kt_end : 0) * TB);
+    const uint32_t lane_off = 16 * lane;
     const int nchunks = (kt_end - kt_begin + ch.tiles - 1) / ch.tiles;
     // rows >= M are never stored; their lanes read row 0
     const int xr = r < M ? r : 0;
@@ -542,12 +559,12 @@ __global__ __launch_bounds__(64 * kMidWaves) void gemv_mid_kernel(const uint16_t
     TileCodes<BITS> ring[D];
 
     // ---- prologue: chunk 0 staged, the ring filled with the first D tiles.
-    //      A wave past the last block streams block 0 and stores nothing.
+    //      A wave past the last block computes on zeros and stores nothing.
     Chunk cur = chunk_info(0);
     stage_load(cur);
 #pragma unroll
     for (int j = 0; j < D; ++j)
-        load_codes<BITS>(ring[j], tiles + (uint32_t)(kt_begin + j < kt_end ? kt_begin + j : kt_end - 1) * TB);
+        load_codes<BITS>(ring[j], cr, lane_off + (uint32_t)(kt_begin + j) * TB);
     stage_store(cur, 0);
     __syncthreads();
 
@@ -652,9 +669,9 @@ __global__ __launch_bounds__(64 * kMidWaves) void gemv_mid_kernel(const uint16_t
                     if (first && j == 0 && more)
                         stage_load(nxt);
                     // refill the slot with the tile D ahead, across chunk
-                    // boundaries (past the range: its last tile again, never
-                    // used); issued on every path
-                    load_codes<BITS>(ring[j], tiles + (uint32_t)(t + D < kt_end ? t + D : kt_end - 1) * TB);
+                    // boundaries (past the range: dropped, never used);
+                    // issued on every path
+                    load_codes<BITS>(ring[j], cr, lane_off + (uint32_t)(t + D) * TB);
                 }
         };
         group(c0, true);
