@@ -437,9 +437,42 @@ def time_graphs(torch, q, lins, args, R):
             q.tf_probe_stream_read(p, sink)
 
     read_ms = time_queued(torch, lambda i: read_pass(i % R), args.steps, enqueue_us=host_us_per_step(read_pass, R))
+
+    # the GEMV's own code stream without its arithmetic (same blocks, waves,
+    # ring depth and closing exchange), per launch and as a queued step
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    plans = [q.tf_gemv_plan(4, 1, l["K"], l["N"], l["G"], cus) for l in lins]
+
+    def block_read(j, p):
+        l, pl = lins[j], plans[j]
+        q.tf_probe_block_read(4, p, l["K"], l["N"], l["G"], pl["waves"], pl["depth"], sink)
+
+    def block_pass(r):
+        for j, p in enumerate(replicas[r]):
+            block_read(j, p)
+
+    block_ms = time_queued(torch, lambda i: block_pass(i % R), args.steps,
+                           enqueue_us=host_us_per_step(block_pass, R))
+    keep = queue_filler(torch, ms=0.02 * n_prof * len(lins) * 2 + 5)
+    evs = []
+    for j in range(len(lins)):
+        for probe in ("read", "block"):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for i in range(n_prof):
+                if probe == "read":
+                    q.tf_probe_stream_read(replicas[i % R][j], sink)
+                else:
+                    block_read(j, replicas[i % R][j])
+            e1.record()
+            evs.append((e0, e1))
+    torch.cuda.synchronize()
+    del keep
+    probe_us = [1e3 * e0.elapsed_time(e1) / n_prof for e0, e1 in evs]
     del replicas, graphs
     return dict(graph_ms=ms_step, host_eager_ms=eager_ms, queued_ms=queued_ms, read_roof_ms=read_ms,
-                mean_us=mean_us, step_pct_us=step_pct)
+                block_read_ms=block_ms, mean_us=mean_us, read_us=probe_us[0::2], block_us=probe_us[1::2],
+                step_pct_us=step_pct)
 
 
 def host_us_per_step(step, R, n=20):
@@ -557,9 +590,12 @@ def bench_gemv(torch, q, args):
         if cnt.get("kernel_source_hash") == kernel_source_hash() and cnt.get("kernel_trace_name") == trace_name:
             traffic = cnt.get("hbm_bytes_per_launch")
 
-    def rows(ls, us):
+    def rows(ls, t):
         return [dict(name=l["name"].replace("c1_layer_", "").replace("_M1", ""), K=l["K"], N=l["N"],
-                     us=round(u, 3), gbs=round(l["bytes"] / (u * 1e-6) / 1e9, 1)) for l, u in zip(ls, us)]
+                     us=round(u, 3), gbs=round(l["bytes"] / (u * 1e-6) / 1e9, 1),
+                     read_probe_us=round(ru, 3), block_probe_us=round(bu, 3),
+                     vs_read_probe=round(u / ru, 3), vs_block_probe=round(u / bu, 3))
+                for l, u, ru, bu in zip(ls, t["mean_us"], t["read_us"], t["block_us"])]
 
     value = layer_bytes / (ms_f * 1e-3) / 1e9
     gbs = lambda ms: round(layer_bytes / (ms * 1e-3) / 1e9, 1)
@@ -568,11 +604,12 @@ def bench_gemv(torch, q, args):
         graph_ms=tf_["graph_ms"], graph_gbs=gbs(tf_["graph_ms"]), host_eager_ms=tf_["host_eager_ms"],
         step_pct_us=tf_["step_pct_us"],
         read_roof_gbs=round(read_roof, 1),
-        per_launch=rows(fused, us_f),
+        block_probe_gbs=gbs(tf_["block_read_ms"]),
+        per_launch=rows(fused, tf_),
         separate=None if args.no_separate else dict(
             ms_per_step=round(ts_["queued_ms"], 5), gbs=gbs(ts_["queued_ms"]),
             graph_ms_per_step=round(ts_["graph_ms"], 5), graph_gbs=gbs(ts_["graph_ms"]),
-            per_linear=rows(lins, ts_["mean_us"])),
+            per_linear=rows(lins, ts_)),
         roofline=dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                       frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic,
                       kernel=f"{trace_name} ({' and '.join(dom['names'])} launches)",
@@ -1065,6 +1102,8 @@ def main():
                                    frac_of_hbm_peak=round(gv["value"] / HBM_PEAK_GBS, 4),
                                    read_roof_gbs=gv["read_roof_gbs"],
                                    frac_of_read_roof=round(gv["value"] / gv["read_roof_gbs"], 4),
+                                   block_probe_gbs=gv["block_probe_gbs"],
+                                   frac_of_block_probe=round(gv["value"] / gv["block_probe_gbs"], 4),
                                    graph_replay=dict(ms_per_step=round(gv["graph_ms"], 5), gbs=gv["graph_gbs"]),
                                    host_eager_ms_per_step=round(gv["host_eager_ms"], 4),
                                    step_percentiles_us=gv["step_pct_us"],

@@ -352,10 +352,23 @@ int tf_gemv_plan(int bits, int64_t M, int64_t K, int64_t N, int64_t G, int cus, 
  *   tf_probe_mfma: one launch of `workgroups` workgroups of 8 waves, each wave
  *     issuing `iters` x 4 independent bf16 32x32x16 MFMAs; *flops (host) gets
  *     the launch's flop count.  sink is a device float it may write.
- * Both return TF_ERR_NULL / TF_ERR_SHAPE / TF_ERR_ALIGN on bad arguments,
- * TF_ERR_HIP on a launch error. */
+ *   tf_probe_block_read: the GEMV's code stream over a packed buffer of
+ *     (bits, K, N, G) (layout as tf_packed_bytes_*; device pointer, 16-byte
+ *     aligned, `nbytes` at least the packed size, else
+ *     TF_ERR_BUFFER_TOO_SMALL) without its arithmetic: one workgroup per 16-column block,
+ *     `waves` waves (1..16, at most ceil(K / 128)) splitting the block's
+ *     k-tiles into contiguous ranges, `depth` (2, 4 or 8) 16-byte
+ *     non-temporal tile loads in flight per wave, and a closing exchange
+ *     through LDS with two barriers.  Pass the waves and depth tf_gemv_plan
+ *     reports to mirror a GEMV launch.  Reads only the code tiles, never the
+ *     records; K < 2^25.  sink is a device uint32 it may write.
+ * All return TF_ERR_NULL / TF_ERR_SHAPE / TF_ERR_GROUP / TF_ERR_ALIGN on bad
+ * arguments (TF_ERR_UNSUPPORTED for bits other than 4 and 8), TF_ERR_HIP on
+ * a launch error. */
 int tf_probe_stream_read(const void *buf, size_t bytes, uint32_t *sink, void *stream);
 int tf_probe_mfma(int workgroups, int iters, float *sink, int64_t *flops, void *stream);
+int tf_probe_block_read(int bits, const void *packed, size_t nbytes, int64_t K, int64_t N, int64_t G, int waves,
+                        int depth, uint32_t *sink, void *stream);
 
 #ifdef __cplusplus
 }

@@ -47,6 +47,7 @@ from ._binding import (  # noqa: F401
     tf_linear_planned,
     tf_packed_bytes_w4,
     tf_packed_bytes_w8,
+    tf_probe_block_read,
     tf_probe_mfma,
     tf_probe_stream_read,
     tf_repack_w4,

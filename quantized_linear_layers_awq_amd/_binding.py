@@ -84,6 +84,8 @@ def load_library():
         L.tf_probe_stream_read.restype = I
         L.tf_probe_mfma.argtypes = [I, I, P, ctypes.POINTER(I64), P]
         L.tf_probe_mfma.restype = I
+        L.tf_probe_block_read.argtypes = [I, P, SZ, I64, I64, I64, I, I, P, P]
+        L.tf_probe_block_read.restype = I
         _lib = L
         return _lib
 
@@ -408,6 +410,18 @@ def tf_probe_stream_read(buf, sink, stream=None):
     L = load_library()
     nbytes = buf.numel() * buf.element_size()
     _check(L.tf_probe_stream_read(_ptr(buf), nbytes, _ptr(sink), _stream(buf, stream)), "tf_probe_stream_read")
+
+
+def tf_probe_block_read(bits, packed, K, N, G, waves, depth, sink, stream=None):
+    """Measurement probe: the GEMV's code stream over `packed` (a CUDA uint8
+    tensor in the pre-tiled layout of (bits, K, N, G)) without its
+    arithmetic, `waves` waves per 16-column block and `depth` tiles in
+    flight per wave; `sink` is a small int32 CUDA tensor the kernel may
+    write."""
+    L = load_library()
+    nbytes = packed.numel() * packed.element_size()
+    _check(L.tf_probe_block_read(int(bits), _ptr(packed), nbytes, int(K), int(N), int(G), int(waves), int(depth),
+                                 _ptr(sink), _stream(packed, stream)), "tf_probe_block_read")
 
 
 def tf_probe_mfma(workgroups, iters, sink, stream=None) -> int:

@@ -24,6 +24,9 @@ namespace {
 using tf::Layout;
 
 constexpr int64_t kDimLimit = int64_t(1) << 31;
+// 32-bit offsets: a row of x in the GEMM, and a code tile within a
+// 16-column block (K / 128 tiles of up to 2 KiB) in the GEMV kernels
+constexpr int64_t kKernelKLimit = int64_t(1) << 25;
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -107,9 +110,7 @@ int validate(int bits, int op, const uint16_t *x, const void *packed, size_t nby
     // the [gate | up] halves are whole 8-column runs
     if (op_is_silu(op) && N % (2 * 8))
         return TF_ERR_SHAPE;
-    // 32-bit offsets: a row of x in the GEMM, and a code tile within a
-    // 16-column block (K / 128 tiles of up to 2 KiB) in the GEMV kernels
-    if (K >= (int64_t(1) << 25))
+    if (K >= kKernelKLimit)
         return TF_ERR_SHAPE;
     if (M == 0)
         return TF_OK;
@@ -410,6 +411,28 @@ int tf_probe_stream_read(const void *buf, size_t bytes, uint32_t *sink, void *st
         return TF_ERR_ALIGN;
     return tf::launch_probe_read(buf, bytes, sink, static_cast<hipStream_t>(stream)) == hipSuccess ? TF_OK
                                                                                                   : TF_ERR_HIP;
+}
+
+int tf_probe_block_read(int bits, const void *packed, size_t nbytes, int64_t K, int64_t N, int64_t G, int waves,
+                        int depth, uint32_t *sink, void *stream)
+{
+    if (!packed || !sink)
+        return TF_ERR_NULL;
+    if (bits != 4 && bits != 8)
+        return TF_ERR_UNSUPPORTED;
+    if (int st = check_kng(bits, K, N, G))
+        return st;
+    const Layout lay = Layout::make(bits, K, N, G);
+    if (K >= kKernelKLimit || waves < 1 || waves > 16 || waves > lay.ktiles || (depth != 2 && depth != 4 && depth != 8))
+        return TF_ERR_SHAPE;
+    if (nbytes < packed_bytes(bits, K, N, G))
+        return TF_ERR_BUFFER_TOO_SMALL;
+    if (!aligned(packed, 16) || !aligned(sink, 4))
+        return TF_ERR_ALIGN;
+    return tf::launch_probe_block_read(bits, packed, lay, waves, depth, sink, static_cast<hipStream_t>(stream)) ==
+                   hipSuccess
+               ? TF_OK
+               : TF_ERR_HIP;
 }
 
 int tf_probe_mfma(int workgroups, int iters, float *sink, int64_t *flops, void *stream)

@@ -1,7 +1,11 @@
 // Measurement probes: the practical roofs the fused kernels are compared
 // against on the same machine, in the same launch pattern.
 //  - stream read: a plain kernel that reads a buffer once with 16-byte
-//    non-temporal loads (the GEMV's access pattern without its arithmetic);
+//    non-temporal loads (the bytes of a GEMV launch with no structure at all);
+//  - block read: the GEMV's own code stream without its arithmetic: one
+//    workgroup per 16-column block, the same waves splitting the block's
+//    k-tiles, the same ring of 16-byte non-temporal loads, and a closing
+//    LDS exchange with two barriers like the GEMV's reduction;
 //  - MFMA: back-to-back independent bf16 32x32x16 MFMAs on every SIMD (the
 //    GEMM's instruction without its loads), for the clock the chip holds
 //    under sustained matrix load.
@@ -33,6 +37,56 @@ __global__ __launch_bounds__(kReadThreads) void stream_read_kernel(const u32x4 *
         acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
     if (acc == 0x9E3779B9u) // practically never; keeps the loads
         sink[0] = acc;
+}
+
+// One workgroup per block, W waves (blockDim.x / 64): wave w reads k-tiles
+// [ktiles w / W, ktiles (w + 1) / W) of the block, D tiles in flight, through
+// a buffer resource that ends at its last tile (look-ahead loads past it are
+// dropped, as in the GEMV).  W8 tiles are two 1 KiB halves.
+template <int BITS, int D>
+__global__ __launch_bounds__(1024) void block_read_kernel(const uint8_t *__restrict__ packed, uint64_t block_bytes,
+                                                          uint32_t meta_bytes, int ktiles, uint32_t *__restrict__ sink)
+{
+    constexpr uint32_t TB = BITS == 4 ? 1024 : 2048;
+    __shared__ uint32_t red[1024];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int W = blockDim.x >> 6;
+    const uint8_t *tiles = packed + (uint64_t)blockIdx.x * block_bytes + meta_bytes;
+    const int a = ktiles * wave / W, b = ktiles * (wave + 1) / W;
+    const auto range = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(tiles), 0, (int)((uint32_t)b * TB),
+                                                         0x00020000);
+    constexpr int kNonTemporal = 2;
+    auto load = [&](uint32_t t, u32x4 *v) {
+        v[0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(range, (int)(16 * lane + t * TB), 0,
+                                                                               kNonTemporal));
+        if constexpr (BITS == 8)
+            v[1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(range, (int)(16 * lane + t * TB + 1024),
+                                                                                   0, kNonTemporal));
+    };
+    u32x4 ring[D][BITS == 4 ? 1 : 2];
+#pragma unroll
+    for (int j = 0; j < D; ++j)
+        load((uint32_t)(a + j), ring[j]);
+    uint32_t acc = 0;
+    for (int i = a; i < b; i += D) {
+#pragma unroll
+        for (int j = 0; j < D; ++j) {
+#pragma unroll
+            for (int h = 0; h < (BITS == 4 ? 1 : 2); ++h)
+                acc ^= ring[j][h][0] ^ ring[j][h][1] ^ ring[j][h][2] ^ ring[j][h][3];
+            load((uint32_t)(i + j + D), ring[j]);
+        }
+    }
+    __syncthreads();
+    red[threadIdx.x] = acc;
+    __syncthreads();
+    if (threadIdx.x < 16) {
+        for (int w = 1; w < W; ++w)
+            acc ^= red[64 * w + threadIdx.x];
+        if (acc == 0x9E3779B9u) // practically never; keeps the loads
+            sink[0] = acc;
+    }
 }
 
 typedef float f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
@@ -71,6 +125,32 @@ hipError_t launch_probe_read(const void *buf, uint64_t bytes, uint32_t *sink, hi
     const uint64_t per_block = (uint64_t)kReadThreads * kReadUnroll;
     const uint64_t grid = (n16 + per_block - 1) / per_block;
     stream_read_kernel<<<dim3((unsigned)grid), kReadThreads, 0, stream>>>(static_cast<const u32x4 *>(buf), n16, sink);
+    return hipGetLastError();
+}
+
+hipError_t launch_probe_block_read(int bits, const void *packed, const Layout &lay, int waves, int depth,
+                                  uint32_t *sink, hipStream_t stream)
+{
+    const uint8_t *pk = static_cast<const uint8_t *>(packed);
+    const dim3 grid((unsigned)lay.nblocks), block(64 * waves);
+    const int kt = (int)lay.ktiles;
+    const uint32_t mb = (uint32_t)lay.meta_bytes;
+    const uint64_t bb = (uint64_t)lay.block_bytes;
+    if (bits == 4) {
+        if (depth == 2)
+            block_read_kernel<4, 2><<<grid, block, 0, stream>>>(pk, bb, mb, kt, sink);
+        else if (depth == 4)
+            block_read_kernel<4, 4><<<grid, block, 0, stream>>>(pk, bb, mb, kt, sink);
+        else
+            block_read_kernel<4, 8><<<grid, block, 0, stream>>>(pk, bb, mb, kt, sink);
+    } else {
+        if (depth == 2)
+            block_read_kernel<8, 2><<<grid, block, 0, stream>>>(pk, bb, mb, kt, sink);
+        else if (depth == 4)
+            block_read_kernel<8, 4><<<grid, block, 0, stream>>>(pk, bb, mb, kt, sink);
+        else
+            block_read_kernel<8, 8><<<grid, block, 0, stream>>>(pk, bb, mb, kt, sink);
+    }
     return hipGetLastError();
 }
 

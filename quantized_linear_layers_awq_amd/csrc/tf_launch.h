@@ -108,6 +108,8 @@ hipError_t launch_gemm256(const uint16_t *x, const void *packed, uint16_t *y, in
 // Measurement probes (not on the hot path).
 hipError_t launch_probe_read(const void *buf, uint64_t bytes, uint32_t *sink, hipStream_t stream);
 hipError_t launch_probe_mfma(int workgroups, int iters, float *sink, hipStream_t stream);
+hipError_t launch_probe_block_read(int bits, const void *packed, const Layout &lay, int waves, int depth,
+                                  uint32_t *sink, hipStream_t stream);
 int64_t probe_mfma_flops(int workgroups, int iters);
 
 } // namespace tf

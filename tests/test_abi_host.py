@@ -427,6 +427,29 @@ class TestValidation:
         assert lib.tf_probe_mfma(256, 10, None, ctypes.byref(flops), None) == TF_ERR_NULL
         assert lib.tf_probe_mfma(256, 10, FAKE + 2, ctypes.byref(flops), None) == TF_ERR_ALIGN
 
+    def test_block_read_probe_validation(self, lib):
+        f = lib.tf_probe_block_read
+        big = ctypes.c_size_t(1 << 30)
+
+        def call(bits=4, p=FAKE, nb=big, K=4096, N=4096, G=128, waves=16, depth=2, sink=FAKE):
+            return f(bits, ctypes.c_void_p(p), nb, ctypes.c_int64(K), ctypes.c_int64(N), ctypes.c_int64(G), waves,
+                     depth, ctypes.c_void_p(sink), None)
+
+        assert call(p=None) == TF_ERR_NULL
+        assert call(sink=None) == TF_ERR_NULL
+        assert call(bits=5) == 6  # TF_ERR_UNSUPPORTED
+        assert call(N=12) == TF_ERR_SHAPE
+        assert call(G=96) == TF_ERR_GROUP
+        assert call(nb=ctypes.c_size_t(lib.tf_packed_bytes_w4(4096, 4096, 128) - 16)) == TF_ERR_BUFFER_TOO_SMALL
+        assert call(waves=0) == TF_ERR_SHAPE
+        assert call(waves=17) == TF_ERR_SHAPE
+        assert call(K=256, waves=3) == TF_ERR_SHAPE  # more waves than k-tiles
+        assert call(depth=3) == TF_ERR_SHAPE
+        assert call(depth=16) == TF_ERR_SHAPE
+        assert call(K=1 << 25) == TF_ERR_SHAPE
+        assert call(p=FAKE + 8) == TF_ERR_ALIGN
+        assert call(sink=FAKE + 2) == TF_ERR_ALIGN
+
     def test_noalloc_validation(self, lib):
         f = lib.tf_gemm_w4a16_noalloc
         call = lambda M=2048, K=4096, N=4096, G=128, x=FAKE, p=FAKE, y=FAKE, nb=1 << 30: f(x, p, nb, y, M, K, N, G, None)

@@ -297,3 +297,26 @@ def test_errors_raise_before_launch():
     with pytest.raises(q.TileFuseError) as e:
         q.tf_gemv_w4a16(x17, p, c.K, c.N, c.G)
     assert e.value.name == "TF_ERR_SHAPE"
+
+
+@pytest.mark.parametrize("bits,K,N,G", [(4, 4096, 6144, 128), (4, 14336, 4096, 128), (8, 8192, 264, 8192),
+                                        (4, 160, 40, 32)])
+def test_block_read_probe_runs_on_packed_buffers(bits, K, N, G):
+    """The measurement probe that mirrors a GEMV launch's code stream runs on
+    exactly-sized packed buffers for every ring depth and the GEMV plan's wave
+    count (a probe: it computes nothing to compare; it must launch cleanly,
+    leave the packed buffer unchanged and not touch its sink in practice)."""
+    torch, q = gpu_or_skip()
+    case = synth.make_inputs(bits, 1, K, N, G, seed=(55, bits, K, N))
+    d = to_device(case, torch)
+    packed = repack(case, d, q)
+    before = packed.clone()
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda:0")
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    waves = q.tf_gemv_plan(bits, 1, K, N, G, cus)["waves"]
+    for w in sorted({1, waves, min(16, -(-K // 128))}):
+        for depth in (2, 4, 8):
+            q.tf_probe_block_read(bits, packed, K, N, G, w, depth, sink)
+    torch.cuda.synchronize()
+    assert torch.equal(packed, before)
+    assert int(sink.abs().sum()) == 0
