@@ -202,7 +202,22 @@ int tf_gemm_w8a16_silu_mul(const uint16_t *x, const void *packed, size_t packed_
  * compute padding, so the call runs the GEMV kernels instead (as tf_gemv_*
  * does up to 16 rows; above, up to four 16-row chunks of x per wave, K split
  * over workgroups on narrow layers); the result meets the same tolerance,
- * not the tiled kernel's bits. */
+ * not the tiled kernel's bits.
+ *
+ * Scale domain of the tiled kernels (above 64 rows).  They carry each
+ * column's running sum divided by the scale of its latest group and
+ * multiply it by s_prev / s_next at each group start (256 x 256 tiles: one
+ * chain over the call's K range; 256 x 128 and narrower tiles: two chains,
+ * over the even and the odd groups; each K range of a split plan starts its
+ * own chains).  Every nonzero scale must be at least 2^-126 in magnitude,
+ * and every quotient the chain holds (the partial output sum x (q - z) s up
+ * to a group, divided by that group's scale) and every ratio of consecutive
+ * nonzero scales in a chain must stay below 2^127 in magnitude; otherwise
+ * the output overflows to +-inf or NaN.  A column whose nonzero scales lie
+ * within a factor of 2^60 of each other, with |x| <= 2^32, always meets
+ * this (K < 2^25).  Zero scales are exact: the chain keeps its previous
+ * scale and the group adds nothing.  The GEMV kernels multiply each group's
+ * sum by its own scale and have no such limit. */
 int tf_gemm_w4a16(const uint16_t *x, const void *packed, size_t packed_bytes, uint16_t *y,
                   int64_t M, int64_t K, int64_t N, int64_t G,
                   void *workspace, size_t ws_bytes, void *stream);

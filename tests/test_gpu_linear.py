@@ -320,3 +320,47 @@ def test_block_read_probe_runs_on_packed_buffers(bits, K, N, G):
     torch.cuda.synchronize()
     assert torch.equal(packed, before)
     assert int(sink.abs().sum()) == 0
+
+
+def _swing_case(bits, M, K, N, G, seed):
+    """A case whose nonzero scales swing across groups by 2^60: 2^30 (1 + u)
+    for groups 0, 1, 4, 5, ... and 2^-30 (1 + u) for groups 2, 3, 6, 7, ...,
+    so the 256 x 256 tiles' one chain and each of the 256 x 128 tiles' two
+    chains (even and odd groups) rescale by about 2^60 at every other step."""
+    c = synth.make_inputs(bits, M, K, N, G, seed=(93, seed, bits, M, K, N, G))
+    ng = K // G
+    rng = np.random.default_rng(seed)
+    e = np.where((np.arange(ng) // 2) % 2 == 0, 30.0, -30.0).astype(np.float32)[:, None]
+    s = (np.float32(1.0) + rng.random((ng, N), dtype=np.float32)) * np.exp2(e)
+    return synth.pack_case(bits, c.codes, c.zeros, synth.f32_to_bf16_bits(s), c.x, G)
+
+
+# (bits, M, K, N, G, route name): 256 x 256 tiles (one chain), 256 x 128 tiles
+# (two chains), a K split on each, groups of two k-tiles, W8, and the GEMV
+SWING_CASES = [(4, 300, 1024, 320, 128, "wide"), (4, 300, 1024, 320, 128, "tiled"),
+               (4, 300, 1024, 320, 128, "tiled128"),
+               (4, 130, 4096, 256, 128, "splitk"), (4, 130, 4096, 256, 128, "splitk128"),
+               (4, 257, 2048, 256, 256, "tiled"), (8, 200, 1024, 192, 128, "tiled128"),
+               (4, 4, 2048, 256, 128, "gemv")]
+
+
+@pytest.mark.parametrize("case", SWING_CASES)
+def test_scales_swinging_by_2_pow_60_inside_the_fold_domain(case):
+    """The GEMM carries each column's running sum divided by the scale of its
+    latest group; the header bounds that quotient.  Scales that swing by 2^60
+    between groups (normal activations) stay inside the bound and match the
+    oracle, which takes every scale as given."""
+    torch, q = gpu_or_skip()
+    bits, M, K, N, G, plan = case
+    c = _swing_case(bits, M, K, N, G, seed=4)
+    if plan == "gemv":
+        ok, ratio, _ = check_linear(c, torch, q, gemm=False)
+    else:
+        route = PLAN_ROUTE[plan]
+        cus = _plan_cus(q, plan, (bits, M, K, N, G))
+        pl = q.tf_gemm_plan(bits, M, K, N, G, cus or 256, route)
+        print(f"swing {case} cus={cus} plan={pl}", flush=True)
+        if plan.startswith("splitk"):
+            assert pl[3] > 1, "the plan splits K"
+        ok, ratio, _ = check_linear(c, torch, q, gemm=True, cus=cus, route=route)
+    assert ok, f"worst error / bound = {ratio:.3f}"
