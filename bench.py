@@ -678,6 +678,30 @@ def bench_gemm(torch, q, args):
     tot_us = sum(o["us"] for o in out)
     tfs = tot_fl / (tot_us * 1e-6) / 1e12
 
+    # the vendor library's dense bf16 GEMM (hipBLASLt through
+    # torch.nn.functional.linear, weights [N][K] in bf16, nothing to
+    # dequantize) on the same shapes, warmed up and timed the same way: what a
+    # tuned dense kernel reaches on this GPU at its board power limit
+    lib = []
+    for s in shapes:
+        w = torch.empty((s["N"], s["K"]), dtype=torch.bfloat16, device="cuda:0").normal_(0.0, 0.02)
+        t_end = _time.perf_counter() + 0.3
+        while _time.perf_counter() < t_end:
+            for _ in range(4):
+                torch.nn.functional.linear(s["x"], w)
+            torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.gemm_iters):
+            torch.nn.functional.linear(s["x"], w)
+        e1.record()
+        torch.cuda.synchronize()
+        us = 1e3 * e0.elapsed_time(e1) / args.gemm_iters
+        lib.append(dict(K=s["K"], N=s["N"], us=round(us, 2),
+                        tflops=round(2.0 * s["M"] * s["K"] * s["N"] / (us * 1e-6) / 1e12, 1)))
+        del w
+    lib_tfs = tot_fl / (sum(o["us"] for o in lib) * 1e-6) / 1e12
+
     # practical roof: back-to-back bf16 MFMAs on every SIMD (two waves each),
     # sustained for about as long as the GEMM launches above
     props = torch.cuda.get_device_properties(0)
@@ -727,7 +751,12 @@ def bench_gemm(torch, q, args):
                                        algorithmic_bytes=c["algorithmic_bytes"]) for c in counters["shapes"]]),
                       measured_roof=round(mfma_roof, 1), frac_of_measured_roof=round(tfs / mfma_roof, 4),
                       measured_roof_kind="back-to-back bf16 32x32x16 MFMAs, 8 waves per CU, sustained "
-                                         "as long as the GEMM launches"),
+                                         "as long as the GEMM launches",
+                      library_dense_bf16=dict(
+                          value=round(lib_tfs, 1), unit="TFLOP/s", frac_of_library=round(tfs / lib_tfs, 4),
+                          shapes=lib,
+                          what="hipBLASLt dense bf16 GEMM (torch.nn.functional.linear, weights [N][K] bf16, no "
+                               "dequantization) on the same shapes, warmed up and timed the same way")),
     )
 
 
@@ -947,7 +976,8 @@ def bench_energy(torch, q, args, seconds=1.0):
     decoder layer's GEMV pass at M=1 as HIP-graph replays of 32 passes each
     (over weight replicas larger than twice the Infinity Cache; eager
     launches from the host would leave the GPU idle between them), and the
-    prefill GEMM at M=2048 launched back to back.  HIP events around the
+    prefill GEMM at M=2048 launched back to back, and for scale the vendor
+    library's dense bf16 GEMM of that shape.  HIP events around the
     window give the GPU-busy fraction.  Beside them the idle draw over the
     same time.  The accumulator updates about once a millisecond, so each
     window is long; the figures are board energy, idle included."""
@@ -965,6 +995,17 @@ def bench_energy(torch, q, args, seconds=1.0):
         e = amdsmi.amdsmi_get_energy_count(handle)
         return e["energy_accumulator"] * e["counter_resolution"] * 1e-6
 
+    try:  # the board power limit, in microwatts
+        cap_w = round(amdsmi.amdsmi_get_power_cap_info(handle)["power_cap"] * 1e-6, 1)
+    except Exception:
+        cap_w = None
+
+    def clock_mhz():
+        try:
+            return amdsmi.amdsmi_get_clock_info(handle, amdsmi.AmdSmiClkType.GFX)["clk"]
+        except Exception:
+            return None
+
     def window(run_one, calls_per_run, gpu_ms_per_run):
         run_one(0)
         torch.cuda.synchronize()
@@ -977,8 +1018,9 @@ def bench_energy(torch, q, args, seconds=1.0):
         # keep about 20 ms of work queued: the host never lets the GPU drain
         ahead = max(2, int(20.0 / gpu_ms_per_run))
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        marks = []
+        marks, clocks = [], []
         j0, t0 = joules(), time.perf_counter()
+        t_clk = t0
         e0.record()
         n = 0
         while time.perf_counter() - t0 < seconds:
@@ -989,6 +1031,11 @@ def bench_energy(torch, q, args, seconds=1.0):
             marks.append(ev)
             if len(marks) > ahead:
                 marks.pop(0).synchronize()
+            if time.perf_counter() - t_clk > 0.005:  # the GFX clock, sampled every 5 ms
+                t_clk = time.perf_counter()
+                mhz = clock_mhz()
+                if mhz is not None:
+                    clocks.append(mhz)
         e1.record()
         torch.cuda.synchronize()
         j1, t1 = joules(), time.perf_counter()
@@ -996,7 +1043,8 @@ def bench_energy(torch, q, args, seconds=1.0):
         busy = e0.elapsed_time(e1) * 1e-3 / (t1 - t0)
         return dict(calls=calls, seconds=round(t1 - t0, 3), joules=round(j1 - j0, 3),
                     watts=round((j1 - j0) / (t1 - t0), 1), mj_per_call=round((j1 - j0) / calls * 1e3, 4),
-                    gpu_busy_frac=round(min(busy, 1.0), 3))
+                    gpu_busy_frac=round(min(busy, 1.0), 3),
+                    gfx_clock_mhz_median=float(sorted(clocks)[len(clocks) // 2]) if clocks else None)
 
     torch.cuda.synchronize()
     j0, t0 = joules(), time.perf_counter()
@@ -1047,11 +1095,20 @@ def bench_energy(torch, q, args, seconds=1.0):
     gemm = window(lambda i: q.tf_gemm_w4a16(x, packed, c.K, c.N, c.G, y=y), 1, 0.3)
     gemm.update(kernel=f"gemm W4A16 M={c.M} K={c.K} N={c.N}", unit="mJ per GEMM call",
                 tflop_per_joule=round(2.0 * c.M * c.K * c.N * gemm["calls"] / 1e12 / gemm["joules"], 3))
+    # the same shape as a dense bf16 GEMM in the vendor library, for scale
+    del packed
+    w = torch.empty((c.N, c.K), dtype=torch.bfloat16, device=dev).normal_(0.0, 0.02)
+    lib = window(lambda i: torch.nn.functional.linear(x, w), 1, 0.3)
+    lib.update(kernel=f"hipBLASLt dense bf16 GEMM (torch.nn.functional.linear) M={c.M} K={c.K} N={c.N}",
+               unit="mJ per GEMM call",
+               tflop_per_joule=round(2.0 * c.M * c.K * c.N * lib["calls"] / 1e12 / lib["joules"], 3))
+    del w
     try:
         amdsmi.amdsmi_shut_down()
     except Exception:
         pass
-    return dict(available=True, idle_watts=round(idle_w, 1), gemv=gemv, gemm=gemm,
+    return dict(available=True, idle_watts=round(idle_w, 1), power_cap_watts=cap_w, gemv=gemv, gemm=gemm,
+                library_dense_bf16_gemm=lib,
                 note="board energy from the amdsmi accumulator, idle draw included")
 
 
