@@ -364,3 +364,35 @@ def test_scales_swinging_by_2_pow_60_inside_the_fold_domain(case):
             assert pl[3] > 1, "the plan splits K"
         ok, ratio, _ = check_linear(c, torch, q, gemm=True, cus=cus, route=route)
     assert ok, f"worst error / bound = {ratio:.3f}"
+
+
+# The 256 x 256 tile kernel without a K split writes its outputs from LDS in
+# 16-byte units when y is 16-byte aligned, else element by element from the
+# same units.  (bits, M, K, N, G): a partial last row tile and a last column
+# tile of one 8-column unit; K of four k-tiles, so no split.
+@pytest.mark.parametrize("op", ["plain", "f16", "silu_mul"])
+def test_gemm256_unaligned_y_matches_aligned(op):
+    torch, q = gpu_or_skip()
+    bits, M, K, N, G = 4, 300, 512, 264 if op != "silu_mul" else 272, 128
+    plan = q.tf_gemm_plan(bits, M, K, N, G, torch.cuda.get_device_properties(0).multi_processor_count)
+    assert plan[7] == 256 and plan[3] == 1, f"not the unsplit 256 x 256 kernel: {plan}"
+    print(f"gemm256 unaligned y op={op} M={M} K={K} N={N}", flush=True)
+    c = synth.make_inputs(bits, M, K, N, G, seed=(81, M, K, N), dtype="f16" if op == "f16" else "bf16")
+    d = to_device(c, torch)
+    if op == "silu_mul":
+        p = q.tf_repack_w4_gate_up(d["qweight"], d["qzeros"], d["scales"], K, N, G)
+        fn, n_out, dt = q.tf_gemm_w4a16_silu_mul, N // 2, torch.bfloat16
+    else:
+        p = repack(c, d, q)
+        fn = q.tf_gemm_w4a16_f16 if op == "f16" else q.tf_gemm_w4a16
+        n_out, dt = N, torch.float16 if op == "f16" else torch.bfloat16
+    want = fn(d["x"], p, K, N, G)
+    pad = 4097  # odd: y starts 2 bytes past a 16-byte boundary
+    big = torch.full((M * n_out + 2 * pad,), -7.25, dtype=dt, device="cuda:0")
+    y = big[pad:pad + M * n_out].view(M, n_out)
+    assert y.data_ptr() % 16 != 0
+    fn(d["x"], p, K, N, G, y=y)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), want.view(torch.int16))
+    host = big.float().cpu().numpy()
+    assert np.all(host[:pad] == -7.25) and np.all(host[-pad:] == -7.25)
