@@ -589,6 +589,69 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_kernel(const uint16_t *__re
     //      (nearest even).  Element e of a 32x32 accumulator is row
     //      8 (e / 4) + 4 h32 + e % 4, column l32. ----
     const int64_t n0 = col0 + (int64_t)nt * kGBN;
+    if (splits == 1) {
+        // The tile's outputs go through LDS as [BM rows][TC] 16-bit values
+        // (TC = the tile's columns, half of them with the SiLU product) and
+        // leave in 16-byte units, consecutive lanes on consecutive units of a
+        // row, where y and its rows are 16-byte aligned; otherwise per
+        // element from the same units.  (Per-element two-byte stores wrote
+        // about 1.4 times the output's bytes to HBM.)
+        constexpr bool kSilu = ACT == kActSiluMul;
+        constexpr int TC = kSilu ? kGBN / 2 : kGBN;
+        static_assert(BM * TC * 2 <= off_codes(WN, BM), "the output tile fits the A and B stages");
+        uint16_t *const st = reinterpret_cast<uint16_t *>(lds);
+        lds_barrier(); // every wave is done with the k loop's LDS
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int ct = 64 * wn + 32 * j + l32; // column within the tile
+            // [gate | up] packed by tf_repack_*_gate_up (N % 16 == 0):
+            // column c < 8 of a 16-column block is gate, c + 8 (lane l32 ^ 8,
+            // same rows) the matching up column; output column 8 (ct / 16) + c
+            const int oc = kSilu ? ((ct >> 4) << 3) + (ct & 7) : ct;
+            const bool writer = !kSilu || (ct & 8) == 0;
+#pragma unroll
+            for (int i = 0; i < MI; ++i)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    float v = kMode == kGWhole ? acc[0][i][j][e] * s_last[0][j]
+                                               : fmaf(acc[0][i][j][e], s_last[0][j], acc[1][i][j][e] * s_last[1][j]);
+                    if constexpr (kSilu) {
+                        // SiLU as in the GEMV epilogue: v / (1 + e^-v), -0
+                        // where e^-v overflows
+                        const float u = __shfl_xor(v, 8);
+                        v = v / (1.f + expf(-v)) * u;
+                    }
+                    const int rt = 32 * MI * wm + 32 * i + 8 * (e >> 2) + 4 * h32 + (e & 3);
+                    if (writer)
+                        st[rt * TC + oc] = f32_to_half_bits<F16>(v);
+                }
+        }
+        lds_barrier();
+        const int64_t out_n = kSilu ? (L.N >> 1) : L.N;
+        const int64_t oc0 = kSilu ? n0 / 2 : n0;
+        constexpr int UPR = TC / 8; // 16-byte units per tile row
+        const bool vec = (reinterpret_cast<uintptr_t>(y) & 15) == 0 && (out_n & 7) == 0;
+#pragma unroll 4
+        for (int u = tid; u < BM * UPR; u += kGThreads) {
+            const int rt = u / UPR, cu = u - rt * UPR;
+            const int64_t row = m0 + rt, col = oc0 + 8 * cu;
+            if (row >= M || col >= out_n)
+                continue;
+            const u32x4 v = *reinterpret_cast<const u32x4 *>(st + rt * TC + 8 * cu);
+            uint16_t *const dst = y + row * out_n + col;
+            if (vec) {
+                *reinterpret_cast<u32x4 *>(dst) = v;
+            } else {
+#pragma unroll
+                for (int h = 0; h < 8; ++h)
+                    if (col + h < out_n)
+                        dst[h] = (uint16_t)(v[h >> 1] >> (16 * (h & 1)));
+            }
+        }
+        return;
+    }
+    // K split: this range's fp32 partial sums, every column (the SiLU
+    // product, if any, is applied by the summing kernel)
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
         const int64_t col = n0 + 64 * wn + 32 * j + l32;
@@ -601,29 +664,8 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_kernel(const uint16_t *__re
                 const int64_t row = m0 + 32 * MI * wm + 32 * i + 8 * (e >> 2) + 4 * h32 + (e & 3);
                 const float v = kMode == kGWhole ? acc[0][i][j][e] * s_last[0][j]
                                                  : fmaf(acc[0][i][j][e], s_last[0][j], acc[1][i][j][e] * s_last[1][j]);
-                if constexpr (ACT != kActSiluMul) {
-                    if (row < M) {
-                        if (splits > 1)
-                            __builtin_nontemporal_store(v, ws + ((int64_t)split * M + row) * L.N + col);
-                        else
-                            y[row * L.N + col] = f32_to_half_bits<F16>(v);
-                    }
-                } else {
-                    // [gate | up] packed by tf_repack_*_gate_up (N % 16 == 0):
-                    // column c < 8 of a 16-column block is gate, c + 8 (lane
-                    // l32 ^ 8, same rows) the matching up column.  Lanes of
-                    // columns past N skip in whole 16-column groups.  SiLU as
-                    // in the GEMV epilogue: v / (1 + e^-v), -0 where e^-v
-                    // overflows.
-                    const float u = __shfl_xor(v, 8);
-                    if (row < M) {
-                        if (splits > 1)
-                            __builtin_nontemporal_store(v, ws + ((int64_t)split * M + row) * L.N + col);
-                        else if ((col & 8) == 0)
-                            y[row * (L.N >> 1) + ((col >> 4) << 3) + (col & 7)] =
-                                f32_to_bf16_bits(v / (1.f + expf(-v)) * u);
-                    }
-                }
+                if (row < M)
+                    __builtin_nontemporal_store(v, ws + ((int64_t)split * M + row) * L.N + col);
             }
     }
 }

@@ -366,26 +366,42 @@ def test_scales_swinging_by_2_pow_60_inside_the_fold_domain(case):
     assert ok, f"worst error / bound = {ratio:.3f}"
 
 
-# The 256 x 256 tile kernel without a K split writes its outputs from LDS in
-# 16-byte units when y is 16-byte aligned, else element by element from the
-# same units.  (bits, M, K, N, G): a partial last row tile and a last column
-# tile of one 8-column unit; K of four k-tiles, so no split.
+# Tiled GEMM launches without a K split write their outputs from LDS in
+# 16-byte units where y and its rows are 16-byte aligned, else element by
+# element from the same units.  (bits, M, K, N, G, column tile): K of four
+# k-tiles, so no split; a partial last row tile; a last column tile of one
+# 8-column unit (W4) or of a ragged width with rows that are not 16-byte
+# multiples (W8, N = 100); 128-row tiles below 129 rows.
+UNSPLIT_TILED = [(4, 300, 512, 264, 128, 256), (4, 300, 512, 272, 128, 256), (8, 300, 512, 100, 512, 128),
+                 (4, 100, 512, 264, 128, 128), (4, 100, 512, 272, 128, 128)]
+
+
 @pytest.mark.parametrize("op", ["plain", "f16", "silu_mul"])
-def test_gemm256_unaligned_y_matches_aligned(op):
+@pytest.mark.parametrize("shape", UNSPLIT_TILED, ids=[str(s) for s in UNSPLIT_TILED])
+def test_tiled_gemm_unaligned_y_matches_aligned(shape, op):
     torch, q = gpu_or_skip()
-    bits, M, K, N, G = 4, 300, 512, 264 if op != "silu_mul" else 272, 128
+    bits, M, K, N, G, width = shape
+    if op == "silu_mul" and N % 16:
+        pytest.skip("the SiLU product pairs 16-column blocks (N % 16 == 0)")
+    if op != "silu_mul" and bits == 4 and N % 16 == 0:
+        pytest.skip("the plain and fp16 calls take the shape with half a block")
     plan = q.tf_gemm_plan(bits, M, K, N, G, torch.cuda.get_device_properties(0).multi_processor_count)
-    assert plan[7] == 256 and plan[3] == 1, f"not the unsplit 256 x 256 kernel: {plan}"
-    print(f"gemm256 unaligned y op={op} M={M} K={K} N={N}", flush=True)
-    c = synth.make_inputs(bits, M, K, N, G, seed=(81, M, K, N), dtype="f16" if op == "f16" else "bf16")
+    assert plan[7] == width and plan[3] == 1 and plan[5] == 0, f"not an unsplit tiled launch: {plan}"
+    print(f"tiled gemm unaligned y op={op} shape={shape}", flush=True)
+    c = synth.make_inputs(bits, M, K, N, G, seed=(81, bits, M, K, N), dtype="f16" if op == "f16" else "bf16")
     d = to_device(c, torch)
     if op == "silu_mul":
-        p = q.tf_repack_w4_gate_up(d["qweight"], d["qzeros"], d["scales"], K, N, G)
-        fn, n_out, dt = q.tf_gemm_w4a16_silu_mul, N // 2, torch.bfloat16
+        p = (q.tf_repack_w4_gate_up if bits == 4 else q.tf_repack_w8_gate_up)(d["qweight"], d["qzeros"], d["scales"],
+                                                                              K, N, G)
+        fn = q.tf_gemm_w4a16_silu_mul if bits == 4 else q.tf_gemm_w8a16_silu_mul
+        n_out, dt = N // 2, torch.bfloat16
     else:
         p = repack(c, d, q)
-        fn = q.tf_gemm_w4a16_f16 if op == "f16" else q.tf_gemm_w4a16
-        n_out, dt = N, torch.float16 if op == "f16" else torch.bfloat16
+        if op == "f16":
+            fn, dt = (q.tf_gemm_w4a16_f16 if bits == 4 else q.tf_gemm_w8a16_f16), torch.float16
+        else:
+            fn, dt = linear_fn(q, bits, True), torch.bfloat16
+        n_out = N
     want = fn(d["x"], p, K, N, G)
     pad = 4097  # odd: y starts 2 bytes past a 16-byte boundary
     big = torch.full((M * n_out + 2 * pad,), -7.25, dtype=dt, device="cuda:0")
@@ -396,3 +412,6 @@ def test_gemm256_unaligned_y_matches_aligned(op):
     assert torch.equal(y.view(torch.int16), want.view(torch.int16))
     host = big.float().cpu().numpy()
     assert np.all(host[:pad] == -7.25) and np.all(host[-pad:] == -7.25)
+    ref = oracle.awq_linear_silu_mul(c) if op == "silu_mul" else oracle.awq_linear(c)
+    ok, ratio = within_tolerance(bf16_to_f64(want) if dt == torch.bfloat16 else want.double().cpu().numpy(), ref)
+    assert ok, f"worst error / bound = {ratio:.3f}"
