@@ -811,10 +811,10 @@ GemmPlan plan_gemm(int bits, int64_t M, int64_t N, int64_t K, int64_t G, int cus
     p.splits = 1;
     p.split_tiles = ktiles;
     p.narrow_cols = 0;
-    // W4 with groups of whole k-tiles above 128 rows: 256 x 256 tiles (its
+    // Groups of whole k-tiles above 128 rows: 256 x 256 tiles (their
     // epilogue's 32-bit offsets hold rows of fewer than 2^22 columns)
     const bool whole = G % kTileRows == 0 || G == K;
-    if (allow256 && bits == 4 && whole && M > kShortTileMaxM && N < (int64_t(1) << 22)) {
+    if (allow256 && whole && M > kShortTileMaxM && N < (int64_t(1) << 22)) {
         p.rows = kGBM;
         p.col_tile = 256;
         p.m_tiles = (M + kGBM - 1) / kGBM;
@@ -827,9 +827,14 @@ GemmPlan plan_gemm(int bits, int64_t M, int64_t N, int64_t K, int64_t G, int cus
         // better.  On the decoder layer's q/k/v, o and down projections at
         // M = 129-256 they took 28-46 us against 30-56.  Without a split a
         // partial round of these tiles still beats the 256 x 128 tiles' one
-        // and a half (q/k/v at M = 2048).  The test route kRouteTiled keeps
-        // these tiles wherever they apply.
-        if (route == kRouteTiled || p.splits == 1 || p.m_tiles * p.wide_cols * p.splits * 20 >= 17 * (int64_t)cus)
+        // and a half (q/k/v at M = 2048).  W8 keeps them only without a
+        // split: W8 per channel at M = 512, K = N = 8192 took 84 us as 64
+        // tiles x 4 K ranges against 79 as 128 tiles of 256 x 128 x 2
+        // ranges, while W8 at M = 2048, K = 4096, N = 14336, G = 128 took 240
+        // us against 273.  The test route kRouteTiled keeps these tiles
+        // wherever they apply.
+        if (route == kRouteTiled || p.splits == 1 ||
+            (bits == 4 && p.m_tiles * p.wide_cols * p.splits * 20 >= 17 * (int64_t)cus))
             return p;
         p = GemmPlan{};
         p.splits = 1;
@@ -876,7 +881,7 @@ hipError_t launch_gemm(int bits, const uint16_t *x, const void *packed, uint16_t
     const GemmPlan plan = plan_gemm(bits, M, lay.N, lay.K, lay.G, cus, route);
     float *ws = plan.splits > 1 ? static_cast<float *>(workspace) : nullptr;
     if (plan.col_tile == 256) {
-        if (hipError_t e = launch_gemm256(x, packed, y, M, lay, plan, ws, stream, act))
+        if (hipError_t e = launch_gemm256(bits, x, packed, y, M, lay, plan, ws, stream, act))
             return e;
         if (plan.splits > 1) {
             if (act == kActSiluMul)

@@ -1,6 +1,6 @@
 // Prefill GEMM with fused dequantization on 256 x 256 output tiles, for W4
-// weights whose groups are whole 128-row k-tiles (G a multiple of 128, or
-// G == K).  TileFuse summary, Methodology section 1: each weight tile is
+// and W8 weights whose groups are whole 128-row k-tiles (G a multiple of
+// 128, or G == K).  TileFuse summary, Methodology section 1: each weight tile is
 // unpacked and dequantized once, kept in core-local memory and reused by
 // every row of the output tile.
 //
@@ -16,10 +16,13 @@
 // K advances in stages of 64 rows:
 //   - activations: a ring of two [256][64] bf16 stages filled by LDS-DMA one
 //     stage ahead;
-//   - codes: one k-tile (16 blocks x 1 KiB) by LDS-DMA, a k-tile ahead; each
-//     unpacking lane reads its 16-byte unit of both blocks it unpacks one
-//     stage before the first use and keeps the second half in registers, so
-//     the buffer is free for the next k-tile after one stage;
+//   - codes: W4, one k-tile (16 blocks x 1 KiB) by LDS-DMA, a k-tile ahead;
+//     each unpacking lane reads its 16-byte unit of both blocks it unpacks
+//     one stage before the first use and keeps the second half in
+//     registers, so the buffer is free for the next k-tile after one stage.
+//     W8 (a k-tile is two 1 KiB halves per block, one per stage): the half
+//     of stage s + 2, fetched during stage s into the slots of the wave that
+//     unpacks it, once that wave has read stage s + 1's;
 //   - records: the k-tile's record of each block (2 x 4 KiB ring), a k-tile
 //     ahead.
 // Every load a stage issues is waited for at its end, before the one barrier
@@ -65,7 +68,7 @@ constexpr int kAJ = kBM * kStage * 2 / 16 / kThreads; // activation DMAs per lan
 // kMode: kGOneTile (G == 128, or G == K == 128) or kGWhole (groups of whole
 // k-tiles).  With one range the output is y (bf16); with several, each range
 // writes fp32 partial sums to ws[range][M][N].
-template <int kMode, int ACT>
+template <int BITS, int kMode, int ACT>
 __global__ __launch_bounds__(kThreads, 1) void gemm256_kernel(const uint16_t *__restrict__ x,
                                                               const uint8_t *__restrict__ packed,
                                                               uint16_t *__restrict__ y, Layout lay, int64_t M,
@@ -73,7 +76,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm256_kernel(const uint16_t *__
                                                               float *__restrict__ ws)
 {
     static_assert(kMode == kGOneTile || kMode == kGWhole, "groups of whole k-tiles");
-    constexpr int RB = record_bytes(4);
+    constexpr int RB = record_bytes(BITS);
     constexpr bool F16 = ACT == kActF16; // fp16 x, scales and y (else bf16)
     constexpr bool one_tile = kMode == kGOneTile;
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -122,7 +125,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm256_kernel(const uint16_t *__
         } else {
             L.ngroups = L.K / lay.G;
         }
-        L.meta_bytes = lay.meta_bytes - g_begin * RB + kt0 * tile_bytes(4);
+        L.meta_bytes = lay.meta_bytes - g_begin * RB + kt0 * tile_bytes(BITS);
     }
     const uint8_t *const pk = packed + g_begin * RB;
     const int ktiles = (int)L.ktiles;
@@ -171,11 +174,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm256_kernel(const uint16_t *__
         const int64_t b = blk0 + 2 * wave + bb;
         blk_rsrc[bb] = make_rsrc(pk + (b < L.nblocks ? b : 0) * L.block_bytes);
     }
+    // W4: k-tile t (1 KiB per block, both stages); W8: stage t, the half of
+    // k-tile t / 2 that holds its 64 rows (1 KiB per block).  Each wave
+    // fetches and reads only its own two blocks' slots.
     auto dma_codes = [&](int t) {
+        const uint32_t off = BITS == 4 ? (uint32_t)t * 1024u : (uint32_t)(t >> 1) * 2048u + (uint32_t)(t & 1) * 1024u;
 #pragma unroll
         for (int bb = 0; bb < 2; ++bb)
-            dma16(blk_rsrc[bb], 16 * lane, (uint32_t)L.meta_bytes + (uint32_t)t * 1024u,
-                  sCodes + (2 * wave + bb) * 1024);
+            dma16(blk_rsrc[bb], 16 * lane, (uint32_t)L.meta_bytes + off, sCodes + (2 * wave + bb) * 1024);
     };
     // group of k-tile t (a multiply-high by a per-launch constant for
     // multi-tile groups: exact while t * tpg < 2^32, else a division)
@@ -204,7 +210,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm256_kernel(const uint16_t *__
     //      as exact bf16 q - z, zero where the row is past K or the group's
     //      scale is 0.  Unit (k-octet 4 uu + o, column 32 w + 16 bb + r),
     //      u = 2 hd + uu. ----
-    u32x4 cw[2]; // the lane's code units of its two blocks for the current k-tile
+    u32x4 cw[2]; // the lane's code units of its two blocks: the k-tile's (W4), the stage's (W8)
     uint8_t *const fill_lane = sB + o * kBOct + (32 * wave + r) * 16;
     auto rec_buf = [&](int t) { return sRec + (t & 1) * kRecBufB; };
     struct UnpackIn {
@@ -217,7 +223,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm256_kernel(const uint16_t *__
         for (int bb = 0; bb < 2; ++bb) {
             const uint8_t *rec = rb + (2 * wave + bb) * kRecBlockB;
             in.sb[bb] = *reinterpret_cast<const uint16_t *>(rec + 2 * r);
-            in.zb[bb] = rec[32 + (r >> 1)];
+            in.zb[bb] = BITS == 4 ? rec[32 + (r >> 1)] : rec[32 + r];
         }
     };
     auto unpack_store = [&](auto hd_c, int td, const UnpackIn &in, int uu) {
@@ -227,8 +233,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm256_kernel(const uint16_t *__
 #pragma unroll
         for (int bb = 0; bb < 2; ++bb) {
             const float live = (step < steps && (in.sb[bb] & 0x7FFFu) != 0) ? 1.f : 0.f;
-            const float nz = -(float)((in.zb[bb] >> (4 * (r & 1))) & 0xFu) * live;
-            const u32x4 v = unpack_w4<F16>(cw[bb][u], live, nz);
+            const uint32_t z = BITS == 4 ? (in.zb[bb] >> (4 * (r & 1))) & 0xFu : in.zb[bb];
+            const float nz = -(float)z * live;
+            // W4: word u of the k-tile's unit; W8: words 2 uu, 2 uu + 1 of the stage's
+            const u32x4 v = BITS == 4 ? unpack_w4<F16>(cw[bb][u], live, nz)
+                                      : unpack_w8<F16>(cw[bb][2 * uu], cw[bb][2 * uu + 1], live, nz);
             *reinterpret_cast<u32x4 *>(fill_lane + hd * kBStageB + uu * 4 * kBOct + bb * 256) = v;
         }
     };
@@ -277,8 +286,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm256_kernel(const uint16_t *__
             bf[j] = *reinterpret_cast<const u32x4 *>(lds + b_rd + hb * kBStageB + sl * 2 * kBOct + 512 * j);
     };
 
-    // ---- prologue: k-tile 0's codes and records and stage 0's activations,
-    //      then stage 0 unpacked and the chain's first scale ----
+    // ---- prologue: k-tile 0's codes (W8: stage 0's) and records and stage
+    //      0's activations, then stage 0 unpacked and the chain's first scale
+    //      (W8: and stage 1's codes, fetched once this wave has read stage
+    //      0's from its slots) ----
     dma_codes(0);
     dma_rec(0, 0);
     dma_a(0, 0, kAJ);
@@ -297,6 +308,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm256_kernel(const uint16_t *__
         }
     }
     wait_lgkmcnt0();
+    if constexpr (BITS == 8) {
+        dma_codes(1);
+        wait_vmcnt<0>();
+    }
     lds_barrier();
 
     // Fold of group boundary t (between k-tiles t - 1 and t): ratios from
@@ -350,8 +365,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm256_kernel(const uint16_t *__
             constexpr int sl = decltype(sl_c)::value;
             constexpr int cur = sl & 1;
             if constexpr (sl == 0) {
-                if constexpr (h == 1)
-                    read_codes(); // k-tile t + 1, for its two stages
+                if constexpr (BITS == 8 || h == 1)
+                    read_codes(); // W4: k-tile t + 1, for its two stages; W8: stage s + 1
                 unpack_load(tn, uin);
             }
             if constexpr (sl + 1 < 4)
@@ -362,12 +377,17 @@ __global__ __launch_bounds__(kThreads, 1) void gemm256_kernel(const uint16_t *__
             } else if constexpr (sl == 1) {
                 dma_a(s + 1, kAJ / 2, kAJ);
                 if constexpr (h == 0) {
-                    dma_codes(tc);
+                    if constexpr (BITS == 4)
+                        dma_codes(tc);
                     dma_rec(tc, t + 1);
                 }
                 unpack_store(ic<hn>{}, tn, uin, 0);
             } else if constexpr (sl == 2) {
                 unpack_store(ic<hn>{}, tn, uin, 1);
+                // W8: stage s + 2's codes into this wave's slots, which its
+                // unpack above has finished reading (clamped past the end)
+                if constexpr (BITS == 8)
+                    dma_codes(s + 2 < 2 * ktiles ? s + 2 : 2 * ktiles - 1);
             }
             if constexpr (sl == 0 && h == 0)
                 fold_rows(2, live_c); // second half of the fold before k-tile t
@@ -416,8 +436,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm256_kernel(const uint16_t *__
         // SiLU product), and leave in 16-byte units, consecutive lanes on
         // consecutive units of a row: 16 stores per lane instead of 128
         // two-byte ones.  Measured 1-2 % faster on K = 4096, N = 14336 at
-        // M = 2048.  A y that is not 16-byte aligned is written per element
-        // from the same units.
+        // M = 2048.
         constexpr bool kSilu = ACT == kActSiluMul;
         constexpr int TC = kSilu ? kBN / 2 : kBN;
         uint16_t *const st = reinterpret_cast<uint16_t *>(lds);
@@ -444,12 +463,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm256_kernel(const uint16_t *__
                 }
         }
         lds_barrier();
-        // W4 rows are whole 8-column units (N % 8 == 0, N % 16 == 0 with the
-        // SiLU product), so a unit is either entirely inside y or past it
+        // 16-byte units where y and its rows are 16-byte aligned (every W4
+        // layer: N % 8 == 0); otherwise (W8 allows any N) per element, up to
+        // the row's last column
         const int64_t out_n = kSilu ? (L.N >> 1) : L.N;
         const int64_t oc0 = kSilu ? n0 / 2 : n0;
         constexpr int UPR = TC / 8; // 16-byte units per tile row
-        const bool al16 = (reinterpret_cast<uintptr_t>(y) & 15) == 0;
+        const bool vec = (reinterpret_cast<uintptr_t>(y) & 15) == 0 && (out_n & 7) == 0;
 #pragma unroll 4
         for (int u = tid; u < kBM * UPR; u += kThreads) {
             const int rt = u / UPR, cu = u - rt * UPR;
@@ -458,14 +478,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm256_kernel(const uint16_t *__
                 continue;
             const u32x4 v = *reinterpret_cast<const u32x4 *>(st + rt * TC + 8 * cu);
             uint16_t *const dst = y + row * out_n + col;
-            if (al16) {
+            if (vec) {
                 *reinterpret_cast<u32x4 *>(dst) = v;
             } else {
 #pragma unroll
-                for (int h = 0; h < 4; ++h) {
-                    dst[2 * h] = (uint16_t)(v[h] & 0xFFFFu);
-                    dst[2 * h + 1] = (uint16_t)(v[h] >> 16);
-                }
+                for (int h = 0; h < 8; ++h)
+                    if (col + h < out_n)
+                        dst[h] = (uint16_t)(v[h >> 1] >> (16 * (h & 1)));
             }
         }
         return;
@@ -501,11 +520,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm256_kernel(const uint16_t *__
     }
 }
 
-template <int kMode, int ACT>
+template <int BITS, int kMode, int ACT>
 static void launch_256(int64_t wgs, int m_tiles, const GemmPlan &plan, hipStream_t stream, const uint16_t *x,
                        const uint8_t *pk, uint16_t *y, const Layout &lay, int64_t M, float *ws)
 {
-    auto kern = &gemm256_kernel<kMode, ACT>;
+    auto kern = &gemm256_kernel<BITS, kMode, ACT>;
     static const hipError_t attr =
         hipFuncSetAttribute(reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
     (void)attr;
@@ -513,33 +532,43 @@ static void launch_256(int64_t wgs, int m_tiles, const GemmPlan &plan, hipStream
                                                          (int)plan.split_tiles, ws);
 }
 
-hipError_t launch_gemm256(const uint16_t *x, const void *packed, uint16_t *y, int64_t M, const Layout &lay,
+template <int BITS>
+static void launch_256_bits(int64_t wgs, int mt, const GemmPlan &plan, hipStream_t stream, const uint16_t *x,
+                            const uint8_t *pk, uint16_t *y, const Layout &lay, int64_t M, float *ws, int act)
+{
+    const bool one = lay.tiles_per_group == 1;
+    if (act == kActSiluMul) {
+        if (one)
+            launch_256<BITS, kGOneTile, kActSiluMul>(wgs, mt, plan, stream, x, pk, y, lay, M, ws);
+        else
+            launch_256<BITS, kGWhole, kActSiluMul>(wgs, mt, plan, stream, x, pk, y, lay, M, ws);
+    } else if (act == kActF16) {
+        if (one)
+            launch_256<BITS, kGOneTile, kActF16>(wgs, mt, plan, stream, x, pk, y, lay, M, ws);
+        else
+            launch_256<BITS, kGWhole, kActF16>(wgs, mt, plan, stream, x, pk, y, lay, M, ws);
+    } else {
+        if (one)
+            launch_256<BITS, kGOneTile, kActNone>(wgs, mt, plan, stream, x, pk, y, lay, M, ws);
+        else
+            launch_256<BITS, kGWhole, kActNone>(wgs, mt, plan, stream, x, pk, y, lay, M, ws);
+    }
+}
+
+hipError_t launch_gemm256(int bits, const uint16_t *x, const void *packed, uint16_t *y, int64_t M, const Layout &lay,
                           const GemmPlan &plan, float *ws, hipStream_t stream, int act)
 {
     // the epilogue's 32-bit offsets: 128 rows of fp32 partials below 2^32 bytes
-    if (!lay.whole_tiles() || plan.rows != kBM || plan.col_tile != kBN || plan.narrow_cols != 0 ||
-        lay.N >= (int64_t(1) << 22))
+    if ((bits != 4 && bits != 8) || !lay.whole_tiles() || plan.rows != kBM || plan.col_tile != kBN ||
+        plan.narrow_cols != 0 || lay.N >= (int64_t(1) << 22))
         return hipErrorInvalidValue;
     const uint8_t *pk = static_cast<const uint8_t *>(packed);
     const int64_t wgs = plan.m_tiles * plan.wide_cols * plan.splits;
     const int mt = (int)plan.m_tiles;
-    const bool one = lay.tiles_per_group == 1;
-    if (act == kActSiluMul) {
-        if (one)
-            launch_256<kGOneTile, kActSiluMul>(wgs, mt, plan, stream, x, pk, y, lay, M, ws);
-        else
-            launch_256<kGWhole, kActSiluMul>(wgs, mt, plan, stream, x, pk, y, lay, M, ws);
-    } else if (act == kActF16) {
-        if (one)
-            launch_256<kGOneTile, kActF16>(wgs, mt, plan, stream, x, pk, y, lay, M, ws);
-        else
-            launch_256<kGWhole, kActF16>(wgs, mt, plan, stream, x, pk, y, lay, M, ws);
-    } else {
-        if (one)
-            launch_256<kGOneTile, kActNone>(wgs, mt, plan, stream, x, pk, y, lay, M, ws);
-        else
-            launch_256<kGWhole, kActNone>(wgs, mt, plan, stream, x, pk, y, lay, M, ws);
-    }
+    if (bits == 4)
+        launch_256_bits<4>(wgs, mt, plan, stream, x, pk, y, lay, M, ws, act);
+    else
+        launch_256_bits<8>(wgs, mt, plan, stream, x, pk, y, lay, M, ws, act);
     return hipSuccess;
 }
 

@@ -100,9 +100,9 @@ bool gemm_uses_gemv(int64_t M, int route);
 // scales and y are fp16.
 hipError_t launch_gemm(int bits, const uint16_t *x, const void *packed, uint16_t *y, int64_t M, const Layout &lay,
                        void *workspace, hipStream_t stream, int cus, int act = kActNone, int route = kRouteAuto);
-// The 256 x 256 kernel for a plan with col_tile 256 (W4, groups of whole
-// k-tiles); ws holds the split partials when plan.splits > 1.
-hipError_t launch_gemm256(const uint16_t *x, const void *packed, uint16_t *y, int64_t M, const Layout &lay,
+// The 256 x 256 kernel for a plan with col_tile 256 (W4 or W8, groups of
+// whole k-tiles); ws holds the split partials when plan.splits > 1.
+hipError_t launch_gemm256(int bits, const uint16_t *x, const void *packed, uint16_t *y, int64_t M, const Layout &lay,
                           const GemmPlan &plan, float *ws, hipStream_t stream, int act);
 
 // Measurement probes (not on the hot path).

@@ -241,8 +241,8 @@ def test_gemv_route_plan_covers_k_once(lib):
 @pytest.mark.parametrize("route", [ROUTE_TILED, ROUTE_TILED128])
 def test_gemm_plan_covers_every_column_once(lib, route):
     """The launch plan: wide tiles from column 0, then 64-column tiles,
-    covering [0, N) with no tile wholly past N; 256-column tiles for W4 with
-    groups of whole k-tiles above 128 rows (not on the 256 x 128 route), with
+    covering [0, N) with no tile wholly past N; 256-column tiles for groups
+    of whole k-tiles above 128 rows (not on the 256 x 128 route), with
     no narrow launch; otherwise 128-column tiles and a narrow launch only when
     the wide tiles miss a whole number of rounds and it fits one round.  A K
     split uses wide tiles only, fits one round, and its ranges of whole
@@ -261,7 +261,7 @@ def test_gemm_plan_covers_every_column_once(lib, route):
             st, (mt, wide, narrow, splits, st_tiles, gemv, rows, cols) = _plan(lib, M, N, cus, K=K, G=G, bits=bits,
                                                                              route=route)
             assert st == TF_OK and gemv == 0, (M, N, cus, K, G)
-            big = route == ROUTE_TILED and bits == 4 and (G % 128 == 0 or G == K) and M > 128
+            big = route == ROUTE_TILED and (G % 128 == 0 or G == K) and M > 128
             assert cols == (256 if big else 128), (bits, M, N, cus, K, G)
             n_wide = -(-N // cols)
             tiles = mt * n_wide

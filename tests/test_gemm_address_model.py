@@ -139,7 +139,7 @@ def check_records(L, blks, g_first, ngroups_range, g_begin, lane_off, want_first
 
 def check_plan_256(q, bits, M, K, N, G, cus, route):
     m_tiles, wide, narrow, splits, split_tiles, gemv, rows, col_tile = q.tf_gemm_plan(bits, M, K, N, G, cus, route)
-    assert gemv == 0 and rows == 256 and col_tile == 256 and narrow == 0 and bits == 4
+    assert gemv == 0 and rows == 256 and col_tile == 256 and narrow == 0
     L = layout(bits, K, N, G)
     nwg = m_tiles * wide * splits
     n_tiles = tile_map(nwg, splits, m_tiles)
@@ -155,14 +155,22 @@ def check_plan_256(q, bits, M, K, N, G, cus, route):
             for wave in range(8):
                 check_x(M, K, k_begin, Kr, mt * 256, 32, 4, wave, stages, x_bytes, cover)
             assert cover.all()
-        # codes and records: k-tile 0 in the prologue, k-tile min(t + 1,
-        # last) during k-tile t; wave w fetches blocks 2 w and 2 w + 1 of the
-        # tile (a block past N: block 0)
-        ts = np.array(sorted({0} | {min(t + 1, kts - 1) for t in range(kts)}))
-        assert ts.tolist() == list(range(kts))
+        # codes: W4 k-tile 0 in the prologue, k-tile min(t + 1, last) during
+        # k-tile t; W8 the halves of stages 0 and 1 in the prologue, stage
+        # min(s + 2, last) during stage s.  Wave w fetches blocks 2 w and
+        # 2 w + 1 of the tile (a block past N: block 0)
         b = np.arange(n_tiles * 16)
         blks = np.where(b < L["nblocks"], b, 0)
-        check_codes(L, blks, kt0, ts, np.zeros_like(ts))
+        if bits == 4:
+            code_ts = np.array(sorted({0} | {min(t + 1, kts - 1) for t in range(kts)}))
+            hs = np.zeros_like(code_ts)
+        else:
+            st = np.array(sorted({0, 1} | {min(s + 2, nstages - 1) for s in range(nstages)}))
+            assert st.tolist() == list(range(nstages))
+            code_ts, hs = st >> 1, st & 1
+        assert sorted(set(code_ts.tolist())) == list(range(kts))
+        check_codes(L, blks, kt0, code_ts, hs)
+        ts = np.arange(kts)  # records: k-tile 0 in the prologue, min(t + 1, last) during k-tile t
         tpg = L["tpg"] if G != K else kts
         g_first = np.zeros_like(ts) if G == K else ts // tpg  # group_of(t), relative to the range
         ngroups_range = 1 if G == K else Kr // G
@@ -242,6 +250,9 @@ SHAPES = [
     (8, 140, 32, 40, 32), (4, 96, 4096, 256, 512), (8, 64, 3072, 128, 3072), (4, 40, 2080, 128, 32),
     (8, 520, 1024, 456, 128), (8, 384, 2048, 264, 2048), (4, 700, 512, 1000, 64), (8, 513, 1024, 392, 32),
     (4, 129, 4096, 28672, 128), (4, 256, 14336, 4096, 128), (8, 1000, 224, 40, 224),
+    # W8 on 256 x 256 tiles: the prefill shape, per channel with a ragged
+    # last k-tile, groups of two k-tiles split over K, a partial column tile
+    (8, 2048, 4096, 14336, 128), (8, 300, 4128, 520, 4128), (8, 200, 8192, 264, 256),
 ]
 
 

@@ -37,6 +37,9 @@ GEMM_SHAPES = [
     (4, 96, 4096, 256, 512), (8, 64, 3072, 128, 3072), (4, 40, 2080, 128, 32), (4, 16, 2048, 136, 64),
     # between the GEMV kernels' 64 rows and one 256-row tile
     (4, 100, 768, 136, 256), (8, 77, 2080, 40, 32), (8, 128, 512, 64, 32),
+    # W8 on 256 x 256 tiles: ragged N (rows not 16-byte multiples), per
+    # channel with a ragged last k-tile, groups of whole k-tiles
+    (8, 300, 1024, 100, 1024), (8, 600, 2080, 1000, 2080), (8, 513, 4096, 520, 256), (8, 600, 896, 1000, 128),
     # 256-row tiles whose plan can run 128- and 64-column tiles in two
     # launches, W4 and W8, every group rule
     (4, 600, 1024, 1000, 128), (8, 520, 1024, 456, 128), (8, 384, 2048, 264, 2048), (4, 300, 256, 264, 32),
@@ -207,7 +210,8 @@ def _integer_case(bits, M, K, N, G, seed):
 @pytest.mark.parametrize("bits,M,K,N,G", [(4, 1, 1024, 128, 128), (4, 7, 2048, 200, 64), (8, 4, 1024, 72, 1024),
                                           (4, 16, 14336, 64, 128), (8, 3, 512, 64, 32), (4, 40, 2048, 200, 64),
                                           (8, 64, 1024, 72, 1024), (4, 33, 4096, 128, 128),
-                                          (4, 300, 2048, 520, 128), (4, 260, 1024, 264, 512)])
+                                          (4, 300, 2048, 520, 128), (4, 260, 1024, 264, 512),
+                                          (8, 300, 2048, 520, 128), (8, 260, 1024, 100, 1024)])
 def test_integer_case_is_bit_exact(gemm, bits, M, K, N, G):
     torch, q = gpu_or_skip()
     if not gemm and M > 16:
@@ -371,9 +375,11 @@ def test_scales_swinging_by_2_pow_60_inside_the_fold_domain(case):
 # element from the same units.  (bits, M, K, N, G, column tile): K of four
 # k-tiles, so no split; a partial last row tile; a last column tile of one
 # 8-column unit (W4) or of a ragged width with rows that are not 16-byte
-# multiples (W8, N = 100); 128-row tiles below 129 rows.
-UNSPLIT_TILED = [(4, 300, 512, 264, 128, 256), (4, 300, 512, 272, 128, 256), (8, 300, 512, 100, 512, 128),
-                 (4, 100, 512, 264, 128, 128), (4, 100, 512, 272, 128, 128)]
+# multiples (W8, N = 100) on the 256 x 256 tiles, the 64-column tiles
+# (G = 32) and the 128-row tiles.
+UNSPLIT_TILED = [(4, 300, 512, 264, 128, 256), (4, 300, 512, 272, 128, 256), (8, 300, 512, 100, 512, 256),
+                 (8, 300, 512, 100, 32, 128), (8, 100, 512, 100, 512, 128), (4, 100, 512, 264, 128, 128),
+                 (4, 100, 512, 272, 128, 128)]
 
 
 @pytest.mark.parametrize("op", ["plain", "f16", "silu_mul"])

@@ -180,11 +180,12 @@ def test_silu_mul_large_sums(bits, M):
 # (bits, M, K, N, G, cus, route): the 16-row-chunk kernel at 17..64 rows (one
 # to four row chunks, K split or not), 128-row tiles (forced at 64 rows, and
 # at 96 and 100) with K split, 256-row tiles with K split, as wide + narrow
-# launches, and as narrow tiles only
+# launches, and as narrow tiles only; W8 on 256 x 256 tiles
 GEMM_SILU = [
     (4, 17, 1024, 1056, 128, 0, 0), (4, 40, 2048, 2080, 64, 0, 0), (8, 64, 1024, 528, 1024, 0, 0),
     (4, 64, 1024, 1056, 128, 0, 1), (4, 100, 4096, 1024, 128, 0, 0), (4, 96, 4096, 256, 512, 4096, 0),
-    (4, 300, 1024, 2080, 128, 0, 0), (4, 520, 512, 4096, 32, 40, 0), (8, 257, 384, 1040, 384, 0, 0),
+    (4, 300, 1024, 2080, 128, 0, 0), (4, 520, 512, 4096, 32, 40, 0), (8, 257, 384, 1040, 64, 0, 0),
+    (8, 257, 384, 1040, 384, 0, 0),
 ]
 
 
@@ -213,7 +214,8 @@ def test_gemm_silu_mul_plans_cover_the_routes():
     assert q.tf_gemm_plan(4, 300, 1024, 2080, 128, 256)[3] > 1              # K split, 256-row tiles
     wide, narrow = q.tf_gemm_plan(4, 520, 512, 4096, 32, 40)[1:3]
     assert wide > 0 and narrow > 0                                          # wide + narrow launches
-    assert q.tf_gemm_plan(8, 257, 384, 1040, 384, 256)[1:3] == (0, 17)      # narrow tiles only
+    assert q.tf_gemm_plan(8, 257, 384, 1040, 64, 256)[1:3] == (0, 17)       # narrow tiles only
+    assert q.tf_gemm_plan(8, 257, 384, 1040, 384, 256)[7] == 256            # W8, 256 x 256 tiles
     assert q.tf_gemm_plan(4, 100, 4096, 1024, 128, 256)[6] == 128           # 128-row tiles
     assert q.tf_gemm_plan(4, 40, 2048, 2080, 64, 256)[5] == 1               # the GEMV kernel
 
