@@ -827,14 +827,18 @@ GemmPlan plan_gemm(int bits, int64_t M, int64_t N, int64_t K, int64_t G, int cus
         // better.  On the decoder layer's q/k/v, o and down projections at
         // M = 129-256 they took 28-46 us against 30-56.  Without a split a
         // partial round of these tiles still beats the 256 x 128 tiles' one
-        // and a half (q/k/v at M = 2048).  W8 keeps them only without a
-        // split: W8 per channel at M = 512, K = N = 8192 took 84 us as 64
-        // tiles x 4 K ranges against 79 as 128 tiles of 256 x 128 x 2
-        // ranges, while W8 at M = 2048, K = 4096, N = 14336, G = 128 took 240
-        // us against 273.  The test route kRouteTiled keeps these tiles
-        // wherever they apply.
+        // and a half (q/k/v at M = 2048).  A split into ranges of fewer than
+        // 8 k-tiles also drops them (each range's fixed costs outweigh the
+        // wider tile): the layer's o projection (4096 x 4096) took 30-43 us
+        // on 256 x 128 tiles against 33-49 at M = 300-768, and the layer pass
+        // at M = 512 went from 270 to 258 us (at M = 300 from 208 to 212).
+        // W8 keeps them only without a split: W8 per channel at M = 512,
+        // K = N = 8192 took 84 us as 64 tiles x 4 K ranges against 79 as 128
+        // tiles of 256 x 128 x 2 ranges, while W8 at M = 2048, K = 4096,
+        // N = 14336, G = 128 took 240 us against 273.  The test route
+        // kRouteTiled keeps these tiles wherever they apply.
         if (route == kRouteTiled || p.splits == 1 ||
-            (bits == 4 && p.m_tiles * p.wide_cols * p.splits * 20 >= 17 * (int64_t)cus))
+            (bits == 4 && p.split_tiles >= 8 && p.m_tiles * p.wide_cols * p.splits * 20 >= 17 * (int64_t)cus))
             return p;
         p = GemmPlan{};
         p.splits = 1;
