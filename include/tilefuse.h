@@ -306,7 +306,8 @@ int tf_dequant_gemv_w8_f32(const void *packed, size_t packed_bytes, float *w,
 /*   route  TF_ROUTE_AUTO (the product calls' choice), TF_ROUTE_TILED (GEMM */
 /*          calls run the tiled GEMM at any M, with 256 x 256 tiles wherever */
 /*          they apply; AUTO drops them where a K split of theirs would     */
-/*          still fill less than 85 % of the compute units), TF_ROUTE_GEMV  */
+/*          fill less than 85 % of the compute units or leave ranges under  */
+/*          8 k-tiles, and for W8 wherever K is split), TF_ROUTE_GEMV        */
 /*          (the GEMV kernels up to 64 rows, as AUTO), TF_ROUTE_TILED128    */
 /*          (the tiled GEMM at any M with 256 x 128 tiles only)             */
 /* Other values: TF_ERR_UNSUPPORTED (the size query returns 0).             */
@@ -326,8 +327,10 @@ size_t tf_workspace_bytes_planned(int bits, int op, int64_t M, int64_t K, int64_
                                   int cus, int route);
 
 /* Launch plan of a GEMM call (host only, no GPU work).
- * Above 128 rows, W4 weights whose groups are whole 128-row k-tiles (G a
- * multiple of 128, or G == K) run on 256 x 256 output tiles.  Otherwise the
+ * Above 128 rows, weights whose groups are whole 128-row k-tiles (G a
+ * multiple of 128, or G == K) run on 256 x 256 output tiles, unless K has to
+ * be split and the split would leave the chip under-filled or its ranges
+ * short (W4), or K has to be split at all (W8).  Otherwise the
  * GEMM covers y with 256-row x 128-column tiles (128 x 128 up to 128 rows);
  * when those 256-row tiles are not a whole number of rounds over the compute
  * units, it runs the columns of the last partial round as 256 x 64 tiles in
