@@ -970,7 +970,7 @@ def bench_silu(torch, q, args):
     return out
 
 
-def bench_energy(torch, q, args, seconds=1.0):
+def bench_energy(torch, q, args, seconds=1.0, max_seconds=8.0):
     """Energy per call from the GPU's energy accumulator (amdsmi), read around
     about `seconds` of calls that keep the GPU busy the whole window: the
     decoder layer's GEMV pass at M=1 as HIP-graph replays of 32 passes each
@@ -979,8 +979,9 @@ def bench_energy(torch, q, args, seconds=1.0):
     prefill GEMM at M=2048 launched back to back, and for scale the vendor
     library's dense bf16 GEMM of that shape.  HIP events around the
     window give the GPU-busy fraction.  Beside them the idle draw over the
-    same time.  The accumulator updates about once a millisecond, so each
-    window is long; the figures are board energy, idle included."""
+    same time.  Each window lasts at least `seconds` and at least four
+    updates of the accumulator (at most `max_seconds`); the figures are board
+    energy, idle included."""
     try:
         import amdsmi
 
@@ -1006,6 +1007,27 @@ def bench_energy(torch, q, args, seconds=1.0):
         except Exception:
             return None
 
+    def sample(edges):
+        """Append (time, energy) when the accumulator has moved since the last edge."""
+        j = joules()
+        if j != edges[-1][1]:
+            edges.append((time.perf_counter(), j))
+
+    def edge_watts(edges, t0, t1, j0, j1):
+        """Power between the first and the last accumulator update seen.  The
+        accumulator moves in steps (about once a millisecond on some boards,
+        about once a second on others), so the two end readings of a window
+        can each lag by a whole step; between update edges the energy is
+        exact up to the sampling interval."""
+        if len(edges) >= 3:  # the start reading, then at least two updates
+            (ta, ja), (tb, jb) = edges[1], edges[-1]
+            return (jb - ja) / (tb - ta)
+        return (j1 - j0) / (t1 - t0)
+
+    def enough(edges, t0):
+        elapsed = time.perf_counter() - t0
+        return (elapsed >= seconds and len(edges) >= 5) or elapsed >= max_seconds
+
     def window(run_one, calls_per_run, gpu_ms_per_run):
         run_one(0)
         torch.cuda.synchronize()
@@ -1020,10 +1042,13 @@ def bench_energy(torch, q, args, seconds=1.0):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         marks, clocks = [], []
         j0, t0 = joules(), time.perf_counter()
-        t_clk = t0
+        edges = [(t0, j0)]
+        t_poll = t0
         e0.record()
         n = 0
-        while time.perf_counter() - t0 < seconds:
+        # run until `seconds` have passed and four accumulator updates were
+        # seen, so that the power comes from whole update periods
+        while not enough(edges, t0):
             run_one(n)
             n += 1
             ev = torch.cuda.Event()
@@ -1031,25 +1056,32 @@ def bench_energy(torch, q, args, seconds=1.0):
             marks.append(ev)
             if len(marks) > ahead:
                 marks.pop(0).synchronize()
-            if time.perf_counter() - t_clk > 0.005:  # the GFX clock, sampled every 5 ms
-                t_clk = time.perf_counter()
-                mhz = clock_mhz()
-                if mhz is not None:
-                    clocks.append(mhz)
+            if time.perf_counter() - t_poll > 0.002:  # energy every 2 ms, clock beside it
+                t_poll = time.perf_counter()
+                sample(edges)
+                if len(clocks) < 4000:
+                    mhz = clock_mhz()
+                    if mhz is not None:
+                        clocks.append(mhz)
         e1.record()
         torch.cuda.synchronize()
         j1, t1 = joules(), time.perf_counter()
         calls = n * calls_per_run
         busy = e0.elapsed_time(e1) * 1e-3 / (t1 - t0)
-        return dict(calls=calls, seconds=round(t1 - t0, 3), joules=round(j1 - j0, 3),
-                    watts=round((j1 - j0) / (t1 - t0), 1), mj_per_call=round((j1 - j0) / calls * 1e3, 4),
-                    gpu_busy_frac=round(min(busy, 1.0), 3),
+        watts = edge_watts(edges, t0, t1, j0, j1)
+        joules_window = watts * (t1 - t0)
+        return dict(calls=calls, seconds=round(t1 - t0, 3), joules=round(joules_window, 3),
+                    watts=round(watts, 1), mj_per_call=round(joules_window / calls * 1e3, 4),
+                    energy_updates=len(edges) - 1, gpu_busy_frac=round(min(busy, 1.0), 3),
                     gfx_clock_mhz_median=float(sorted(clocks)[len(clocks) // 2]) if clocks else None)
 
     torch.cuda.synchronize()
     j0, t0 = joules(), time.perf_counter()
-    time.sleep(seconds)
-    idle_w = (joules() - j0) / (time.perf_counter() - t0)
+    edges = [(t0, j0)]
+    while not enough(edges, t0):
+        time.sleep(0.002)
+        sample(edges)
+    idle_w = edge_watts(edges, t0, time.perf_counter(), j0, joules())
 
     lins = stage_layer(torch, q, synth, M=1)
     fused = fuse_layer(torch, q, lins)
