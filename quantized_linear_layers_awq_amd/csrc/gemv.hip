@@ -66,14 +66,14 @@ __device__ __forceinline__ CodeRange code_range(const uint8_t *tiles, uint32_t b
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(tiles), 0, (int)bytes, 0x00020000);
 }
 
-// The codes of tile byte offset off (lane offset included), non-temporal.
-template <int BITS>
+// The codes of tile byte offset off (lane offset included).  kPolicy is the
+// load's cache-policy field: 2 = non-temporal, 0 = the default policy.
+template <int BITS, int kPolicy = 2>
 __device__ __forceinline__ void load_codes(TileCodes<BITS> &c, CodeRange cr, uint32_t off)
 {
-    constexpr int kNonTemporal = 2;
-    c.w[0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(cr, (int)off, 0, kNonTemporal));
+    c.w[0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(cr, (int)off, 0, kPolicy));
     if constexpr (BITS == 8)
-        c.w[1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(cr, (int)off + 1024, 0, kNonTemporal));
+        c.w[1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(cr, (int)off + 1024, 0, kPolicy));
 }
 
 __device__ __forceinline__ void fold(f32x4 &yacc, f32x4 &gacc, f32x4 &zacc, float s)
@@ -118,6 +118,11 @@ template <int BITS, int kMode, int D, int BPW, int ACT = kActNone>
 __global__ __launch_bounds__(1024) void gemv_kernel(const uint16_t *__restrict__ x, const uint8_t *__restrict__ packed,
                                                     uint16_t *__restrict__ y, Layout lay, int M, GemvChunks ch)
 {
+    // Launches whose waves stream at most 3 k-tiles each (ring depth 2) ran
+    // faster with the default cache policy than with non-temporal loads;
+    // longer streams ran faster non-temporal (the decoder layer's launches,
+    // queued back to back).
+    constexpr int kCodePolicy = D == 2 ? 0 : 2;
     // D: k-tiles of codes in flight per wave
     constexpr uint32_t TB = tile_bytes(BITS), RB = record_bytes(BITS);
     constexpr bool F16 = ACT == kActF16; // fp16 x, scales and y (else bf16)
@@ -192,7 +197,7 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const uint16_t *__restrict__
             if (n > 0) {
 #pragma unroll
                 for (int j = 0; j < D; ++j)
-                    load_codes<BITS>(ring[j], cr, lane_off + (uint32_t)(a + j) * TB);
+                    load_codes<BITS, kCodePolicy>(ring[j], cr, lane_off + (uint32_t)(a + j) * TB);
             }
             // the waves' ranges move between chunks: another wave may still
             // read the previous chunk where this one stores
@@ -258,7 +263,7 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const uint16_t *__restrict__
             if (n > 0) {
 #pragma unroll
                 for (int j = 0; j < D; ++j)
-                    load_codes<BITS>(ring[j], cr, lane_off + (uint32_t)(a + j) * TB);
+                    load_codes<BITS, kCodePolicy>(ring[j], cr, lane_off + (uint32_t)(a + j) * TB);
             }
 
             if (c0 > 0)
@@ -312,7 +317,7 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const uint16_t *__restrict__
 #pragma unroll
                 for (int u = 0; u < 4; ++u)
                     ops[u] = code_operand<BITS, F16>(ring[j], u, magic);
-                load_codes<BITS>(ring[j], cr, lane_off + (uint32_t)(t + D) * TB);
+                load_codes<BITS, kCodePolicy>(ring[j], cr, lane_off + (uint32_t)(t + D) * TB);
                 if (ti < n) {
                     u32x4 xa[4];
 #pragma unroll
