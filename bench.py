@@ -1014,15 +1014,26 @@ def bench_energy(torch, q, args, seconds=1.0, max_seconds=8.0):
             edges.append((time.perf_counter(), j))
 
     def edge_watts(edges, t0, t1, j0, j1):
-        """Power between the first and the last accumulator update seen.  The
-        accumulator moves in steps (about once a millisecond on some boards,
-        about once a second on others), so the two end readings of a window
-        can each lag by a whole step; between update edges the energy is
-        exact up to the sampling interval."""
-        if len(edges) >= 3:  # the start reading, then at least two updates
-            (ta, ja), (tb, jb) = edges[1], edges[-1]
-            return (jb - ja) / (tb - ta)
-        return (j1 - j0) / (t1 - t0)
+        """Power between the first and the last accumulator update seen, and
+        the number of intervals left out.  The accumulator moves in steps
+        (about once a millisecond on some boards, about once a second on
+        others), so the two end readings of a window can each lag by a whole
+        step; between update edges the energy is exact up to the sampling
+        interval.  An interval between successive updates whose power is
+        negative or above three times the board limit comes from a bad
+        reading (one such reading spoils the intervals on both sides of it)
+        and is left out of both sums."""
+        ups = edges[1:]
+        limit = 3.0 * (cap_w or 1400.0)
+        good, dropped = [], 0
+        for (ta, ja), (tb, jb) in zip(ups, ups[1:]):
+            if tb > ta and 0.0 <= (jb - ja) / (tb - ta) <= limit:
+                good.append((jb - ja, tb - ta))
+            else:
+                dropped += 1
+        if good:
+            return sum(g[0] for g in good) / sum(g[1] for g in good), dropped
+        return (j1 - j0) / (t1 - t0), dropped
 
     def enough(edges, t0):
         elapsed = time.perf_counter() - t0
@@ -1068,11 +1079,11 @@ def bench_energy(torch, q, args, seconds=1.0, max_seconds=8.0):
         j1, t1 = joules(), time.perf_counter()
         calls = n * calls_per_run
         busy = e0.elapsed_time(e1) * 1e-3 / (t1 - t0)
-        watts = edge_watts(edges, t0, t1, j0, j1)
+        watts, dropped = edge_watts(edges, t0, t1, j0, j1)
         joules_window = watts * (t1 - t0)
         return dict(calls=calls, seconds=round(t1 - t0, 3), joules=round(joules_window, 3),
                     watts=round(watts, 1), mj_per_call=round(joules_window / calls * 1e3, 4),
-                    energy_updates=len(edges) - 1, gpu_busy_frac=round(min(busy, 1.0), 3),
+                    energy_updates=len(edges) - 1, intervals_dropped=dropped, gpu_busy_frac=round(min(busy, 1.0), 3),
                     gfx_clock_mhz_median=float(sorted(clocks)[len(clocks) // 2]) if clocks else None)
 
     torch.cuda.synchronize()
@@ -1081,7 +1092,7 @@ def bench_energy(torch, q, args, seconds=1.0, max_seconds=8.0):
     while not enough(edges, t0):
         time.sleep(0.002)
         sample(edges)
-    idle_w = edge_watts(edges, t0, time.perf_counter(), j0, joules())
+    idle_w, _ = edge_watts(edges, t0, time.perf_counter(), j0, joules())
 
     lins = stage_layer(torch, q, synth, M=1)
     fused = fuse_layer(torch, q, lins)
